@@ -1,0 +1,184 @@
+"""Synthetic long-context attention inputs.
+
+The five named workloads are stand-ins for the long-context LLM prefill
+workloads the MInference pages measure on (LLaMA-3-8B-1M-style layers, 128K to
+1M tokens; "MInference 1.0 README", section "TL;DR"; talk slides
+"System-Algorithm Co-design", slide "Dynamic sparsity in attention").  No
+model weights or datasets are used: Q, K and V are Gaussian, rotated with
+rotary position embedding (base 500000, rotate-half form) and given planted
+structure so that vertical lines (attention sinks, heavy columns) and slash
+lines (equidistant diagonals) exist for the estimator to find.
+
+Everything here is input shaping; none of it is the method's arithmetic.
+
+Generation:
+  * CPU (small cases, tests): Q/K/V drawn in float64, rotated and planted in
+    float64, then rounded to float32 (round-to-nearest-even) and from there to
+    bfloat16, so the float32 and bfloat16 copies share one draw.
+  * GPU (the 128K-1M workloads): same recipe in float32 on the device, with the
+    rotary angles computed in float64 and chunked over positions.
+Each (workload, seed, device) triple is deterministic.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field, replace
+
+import torch
+
+HEAD_DIM = 128
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    n_q_heads: int
+    n_kv_heads: int
+    seq_len: int
+    head_dim: int = HEAD_DIM
+    dtypes: tuple = ("bf16",)
+    vertical_topk: int = 1000
+    slash_topk: int = 6096
+    last_q: int = 64
+    block: int = 64
+    rope_base: float = 500000.0
+    n_planted: int = 16          # planted vertical columns per kv head, key 0 included
+    plant_gain: float = 3.0      # K[col] += gain * mean(q)
+    slash_period: int = 0        # >0: keys at offset multiples of this are biased toward q
+    head_patterns: tuple = field(default_factory=tuple)  # per q head: "vs" | "a" | "bs"
+    sink: int = 128              # A-shape: leading columns kept
+    window: int = 4096           # A-shape: local diagonals kept
+    bs_topk: int = 100           # block-sparse: key blocks kept per query block
+    seed: int = 0
+
+    @property
+    def group(self) -> int:
+        return self.n_q_heads // self.n_kv_heads
+
+    @property
+    def n_blocks(self) -> int:
+        return self.seq_len // self.block
+
+    def pattern(self, h: int) -> str:
+        return self.head_patterns[h] if self.head_patterns else "vs"
+
+    def heads_with(self, pat: str) -> list:
+        return [h for h in range(self.n_q_heads) if self.pattern(h) == pat]
+
+
+def _mixed_patterns(n: int = 32) -> tuple:
+    return tuple("a" if h < 8 else ("vs" if h < 24 else "bs") for h in range(n))
+
+
+WORKLOADS = {
+    # single head, 4K tokens, float32 and bfloat16 copies of one draw
+    "single_head_4k": Workload("single_head_4k", 1, 1, 4096, dtypes=("fp32", "bf16"),
+                               vertical_topk=64, slash_topk=256, n_planted=9, seed=1001),
+    # LLaMA-3-8B attention layer shape (32 q / 8 kv heads, GQA 4:1)
+    "llama3_8b_128k": Workload("llama3_8b_128k", 32, 8, 131072, seed=1002),
+    "llama3_8b_512k": Workload("llama3_8b_512k", 32, 8, 524288, slash_period=512, seed=1003),
+    "llama3_8b_1m": Workload("llama3_8b_1m", 32, 8, 1048576, slash_period=512, seed=1004),
+    # heads 0-7 A-shape, 8-23 vertical-slash, 24-31 block-sparse
+    "mixed_256k": Workload("mixed_256k", 32, 8, 262144, head_patterns=_mixed_patterns(), seed=1005),
+}
+
+
+def small_workload(name: str = "small", **kw) -> Workload:
+    """A test-sized workload (same recipe, smaller shapes)."""
+    base = dict(n_q_heads=4, n_kv_heads=1, seq_len=1024, vertical_topk=64, slash_topk=128,
+                n_planted=5, seed=7)
+    base.update(kw)
+    return Workload(name, **base)
+
+
+def rope_tables(positions: torch.Tensor, head_dim: int, base: float, dtype: torch.dtype):
+    """cos/sin tables [len(positions), head_dim/2] for rotate-half rotary embedding.
+
+    Angles are formed in float64 (position * base^(-2i/head_dim)) and cast once.
+    """
+    half = head_dim // 2
+    inv_freq = base ** (-(torch.arange(half, dtype=torch.float64, device=positions.device) * 2.0)
+                        / head_dim)
+    ang = positions.to(torch.float64)[:, None] * inv_freq[None, :]
+    return torch.cos(ang).to(dtype), torch.sin(ang).to(dtype)
+
+
+def _rotate_(x: torch.Tensor, base: float, chunk: int) -> None:
+    """In-place rotate-half rotary embedding over positions 0..N-1 of x [H, N, D]."""
+    H, N, D = x.shape
+    half = D // 2
+    for p0 in range(0, N, chunk):
+        p1 = min(N, p0 + chunk)
+        cos, sin = rope_tables(torch.arange(p0, p1, device=x.device), D, base, x.dtype)
+        x1 = x[:, p0:p1, :half].clone()
+        x2 = x[:, p0:p1, half:].clone()
+        x[:, p0:p1, :half] = x1 * cos - x2 * sin
+        x[:, p0:p1, half:] = x2 * cos + x1 * sin
+
+
+def _planted_columns(w: Workload, seed: int) -> torch.Tensor:
+    """Per kv head: key 0 plus (n_planted-1) distinct random keys in [1, N)."""
+    g = torch.Generator(device="cpu").manual_seed(seed * 7919 + 17)
+    cols = []
+    for _ in range(w.n_kv_heads):
+        extra = torch.randperm(w.seq_len - 1, generator=g)[: w.n_planted - 1] + 1
+        cols.append(torch.cat([torch.zeros(1, dtype=torch.long), torch.sort(extra).values]))
+    return torch.stack(cols)
+
+
+def _plant_(w: Workload, q: torch.Tensor, k: torch.Tensor, planted: torch.Tensor) -> None:
+    G, N, D = w.group, w.seq_len, w.head_dim
+    for g in range(w.n_kv_heads):
+        qg = q[g * G:(g + 1) * G]
+        if w.n_planted > 0:
+            qbar = qg.mean(dim=(0, 1))                       # mean over positions and group heads
+            cols = planted[g].to(k.device)
+            k[g, cols] += w.plant_gain * qbar
+        if w.slash_period > 0:
+            P = w.slash_period
+            assert N % P == 0
+            qpos = qg.mean(dim=0).reshape(N // P, P, D)      # per-position group mean
+            incl = torch.flip(torch.cumsum(torch.flip(qpos, [0]), 0), [0])
+            excl = incl - qpos                               # sum over later positions j+P*m, m>=1
+            cnt = (N // P - 1 - torch.arange(N // P, device=q.device, dtype=q.dtype))
+            boost = torch.where(cnt[:, None, None] > 0,
+                                excl / cnt.clamp(min=1)[:, None, None],
+                                torch.zeros((), dtype=q.dtype, device=q.device))
+            k[g] += w.plant_gain * boost.reshape(N, D)
+
+
+def make_inputs(w: Workload, seed: int | None = None, device: str = "cpu") -> dict:
+    """Draw Q [Hq,N,D], K and V [Hkv,N,D] for workload w.
+
+    Returns a dict with 'q','k','v' in bfloat16 (when "bf16" is in w.dtypes),
+    'q32','k32','v32' in float32 (when "fp32" is in w.dtypes), and 'planted'
+    (the planted vertical columns, [Hkv, n_planted]).
+    """
+    seed = w.seed if seed is None else seed
+    dev = torch.device(device)
+    work = torch.float64 if dev.type == "cpu" else torch.float32
+    gen = torch.Generator(device=dev).manual_seed(int(seed))
+    Hq, Hkv, N, D = w.n_q_heads, w.n_kv_heads, w.seq_len, w.head_dim
+    q = torch.randn((Hq, N, D), generator=gen, dtype=work, device=dev)
+    k = torch.randn((Hkv, N, D), generator=gen, dtype=work, device=dev)
+    v = torch.randn((Hkv, N, D), generator=gen, dtype=work, device=dev)
+    chunk = 1 << 16
+    _rotate_(q, w.rope_base, chunk)
+    _rotate_(k, w.rope_base, chunk)
+    planted = _planted_columns(w, seed) if w.n_planted > 0 else torch.zeros((Hkv, 0), dtype=torch.long)
+    _plant_(w, q, k, planted)
+    out = {"planted": planted}
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        t32 = t.to(torch.float32)
+        del t
+        if "fp32" in w.dtypes:
+            out[name + "32"] = t32.contiguous()
+        if "bf16" in w.dtypes:
+            out[name] = t32.to(torch.bfloat16).contiguous()
+        del t32
+    return out
+
+
+def with_seq_len(w: Workload, n: int) -> Workload:
+    return replace(w, seq_len=n)

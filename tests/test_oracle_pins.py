@@ -1,0 +1,386 @@
+"""Pins for the CPU oracle: each check ties an oracle function to something other
+than itself (a closed form, an invariant, a library routine, or a brute-force
+evaluation of the definition on tiny inputs)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.index import index_caps
+
+RNG = np.random.default_rng(12345)
+
+
+def rand_qkv(hq, hkv, n, d, seed=0, scale=1.0):
+    r = np.random.default_rng(seed)
+    return (r.standard_normal((hq, n, d)) * scale, r.standard_normal((hkv, n, d)) * scale,
+            r.standard_normal((hkv, n, d)))
+
+
+def random_sets(h, n, kv, ks, seed=0):
+    r = np.random.default_rng(seed)
+    v = np.stack([np.sort(r.choice(n, size=kv, replace=False)) for _ in range(h)]).astype(np.int32)
+    s = np.stack([np.sort(r.choice(n, size=ks, replace=False)) for _ in range(h)]).astype(np.int32)
+    return v, s
+
+
+# ---------------------------------------------------------------- estimator
+
+def brute_estimate(q, k, L, G, scale):
+    """Per-entry loops straight from the definition (pure Python, tiny sizes)."""
+    Hq, N, D = q.shape
+    v = [[0.0] * N for _ in range(Hq)]
+    s = [[0.0] * N for _ in range(Hq)]
+    for h in range(Hq):
+        g = h // G
+        for r in range(L):
+            p = N - L + r
+            z = [scale * sum(q[h, p, d] * k[g, j, d] for d in range(D)) for j in range(p + 1)]
+            m = max(z)
+            w = [math.exp(x - m) for x in z]
+            tot = math.fsum(w)
+            for j in range(p + 1):
+                v[h][j] += w[j] / tot
+                s[h][p - j] += w[j] / tot
+    return np.array(v), np.array(s)
+
+
+@pytest.mark.parametrize("hq,hkv,n,d,L", [(4, 2, 24, 3, 4), (2, 1, 40, 5, 7), (1, 1, 9, 2, 9)])
+def test_estimate_matches_brute_force(hq, hkv, n, d, L):
+    q, k, _ = rand_qkv(hq, hkv, n, d, seed=n)
+    scale = 1.0 / math.sqrt(d)
+    v, s = oracle.estimate_vs(q, k, last_q=L)
+    bv, bs = brute_estimate(q, k, L, hq // hkv, scale)
+    np.testing.assert_allclose(v, bv, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(s, bs, rtol=0, atol=1e-12)
+
+
+def test_estimate_geometric_closed_form():
+    """q = (c, 0, ...), k_j = (j, 0, ...), scale 1: row p has weights
+    x^j / sum_{t<=p} x^t with x = e^c, so v and s have closed forms that fix the
+    direction of the diagonal index (o = i - j)."""
+    N, L, D, c = 12, 3, 4, 0.3
+    q = np.zeros((1, N, D))
+    q[0, :, 0] = c
+    k = np.zeros((1, N, D))
+    k[0, :, 0] = np.arange(N)
+    v, s = oracle.estimate_vs(q, k, last_q=L, scale=1.0)
+    x = math.exp(c)
+    ev = np.zeros(N)
+    es = np.zeros(N)
+    for r in range(L):
+        p = N - L + r
+        S = (x ** (p + 1) - 1) / (x - 1)
+        for j in range(p + 1):
+            ev[j] += x ** j / S
+            es[p - j] += x ** j / S
+    np.testing.assert_allclose(v[0], ev, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(s[0], es, rtol=1e-13, atol=1e-15)
+    # every row puts its largest weight on its own diagonal, so s falls with o
+    assert np.all(np.diff(s[0]) < 0)
+
+
+def test_estimate_zero_query_uniform():
+    """q = 0: every allowed key of row p has weight 1/(p+1)."""
+    N, L, D = 50, 6, 8
+    q = np.zeros((2, N, D))
+    k = RNG.standard_normal((1, N, D))
+    v, s = oracle.estimate_vs(q, k, last_q=L)
+    for j in range(N):
+        want = sum(1.0 / (p + 1) for p in range(N - L, N) if p >= j)
+        assert abs(v[0, j] - want) < 1e-13 and abs(s[1, j] - want) < 1e-13
+
+
+def test_estimate_mass_and_last_row_symmetry():
+    """Each softmax row sums to one: sum v = sum s = L.  With L = 1 the only row
+    is p = N-1, so s[o] = v[N-1-o] exactly."""
+    q, k, _ = rand_qkv(4, 1, 300, 16, seed=3)
+    v, s = oracle.estimate_vs(q, k, last_q=64)
+    np.testing.assert_allclose(v.sum(1), 64.0, rtol=1e-12)
+    np.testing.assert_allclose(s.sum(1), 64.0, rtol=1e-12)
+    v1, s1 = oracle.estimate_vs(q, k, last_q=1)
+    np.testing.assert_array_equal(s1, v1[:, ::-1])
+
+
+def test_estimate_gqa_mapping():
+    """q head h reads kv head h // G: duplicating a kv head changes nothing."""
+    q, k, _ = rand_qkv(4, 2, 80, 8, seed=5)
+    v, s = oracle.estimate_vs(q, k, last_q=8)
+    k4 = np.repeat(k, 2, axis=0)
+    v4, s4 = oracle.estimate_vs(q, k4, last_q=8)
+    np.testing.assert_array_equal(v, v4)
+    np.testing.assert_array_equal(s, s4)
+
+
+# ---------------------------------------------------------------- top-k
+
+@pytest.mark.parametrize("seed", range(5))
+def test_top_k_definition(seed):
+    """Every chosen score beats every unchosen one, ties go to the lower index,
+    output ascending -- checked pairwise."""
+    r = np.random.default_rng(seed)
+    x = r.integers(0, 6, size=40).astype(float)      # many exact ties
+    k = 13
+    sel = oracle.top_k_indices(x, k)
+    assert len(sel) == k and np.all(np.diff(sel) > 0)
+    chosen = set(sel.tolist())
+    for i in chosen:
+        for j in range(len(x)):
+            if j not in chosen:
+                assert x[i] > x[j] or (x[i] == x[j] and i < j)
+
+
+# ---------------------------------------------------------------- index builder
+
+def union_points(s_set, r0, r1):
+    U = set()
+    for o in s_set:
+        if o <= r1:
+            U.update(range(max(0, r0 - o), r1 - o + 1))
+    return U
+
+
+def leftmost_cover(U, w=64):
+    """Blocks placed at the leftmost point of U not yet covered (set form)."""
+    pts = sorted(U)
+    out, cov = [], -1
+    for u in pts:
+        if u > cov:
+            out.append(u)
+            cov = u + w - 1
+    return out
+
+
+def min_cover_dp(U, w=64):
+    """Minimum number of width-w integer intervals covering U, by exhaustive DP
+    over every start that covers the leftmost remaining point."""
+    pts = sorted(U)
+    f = [0] * (len(pts) + 1)            # f[i]: blocks needed for pts[i:]
+    for i in range(len(pts) - 1, -1, -1):
+        best = None
+        for st in range(pts[i] - w + 1, pts[i] + 1):
+            j = i
+            while j < len(pts) and pts[j] <= st + w - 1:
+                j += 1
+            c = 1 + f[j]
+            best = c if best is None else min(best, c)
+        f[i] = best
+    return f[0]
+
+
+@pytest.mark.parametrize("n,kv,ks,seed", [(320, 7, 9, 0), (256, 3, 40, 1), (640, 20, 30, 2),
+                                          (100, 5, 17, 3), (192, 1, 1, 4)])
+def test_index_characterisation(n, kv, ks, seed):
+    v_idx, s_idx = random_sets(2, n, kv, ks, seed)
+    idx = oracle.build_index(v_idx, s_idx, n)
+    nqb = (n + 63) // 64
+    for h in range(2):
+        for b in range(nqb):
+            r0, r1 = 64 * b, min(64 * b + 63, n - 1)
+            cnt = idx.block_count[h, b]
+            blocks = idx.block_offset[h, b, :cnt].tolist()
+            U = union_points(s_idx[h].tolist(), r0, r1)
+            assert blocks == leftmost_cover(U)
+            assert cnt == min_cover_dp(U)
+            assert cnt <= min(ks, b + 1)
+            assert all(blocks[i] + 64 <= blocks[i + 1] for i in range(len(blocks) - 1))
+            covered = set()
+            for st in blocks:
+                covered.update(range(st, st + 64))
+            assert U <= covered
+            cols = idx.column_index[h, b, : idx.column_count[h, b]].tolist()
+            want = [j for j in v_idx[h].tolist() if j <= r1 and j not in covered]
+            assert cols == want
+
+
+def test_index_mask_contains_exact_union():
+    n = 384
+    v_idx, s_idx = random_sets(3, n, 11, 23, seed=9)
+    idx = oracle.build_index(v_idx, s_idx, n)
+    M = oracle.index_mask(idx, n)
+    Mx = oracle.exact_union_mask(v_idx, s_idx, n)
+    assert np.all(M >= Mx)
+    assert np.all(~np.triu(np.ones((n, n), bool), 1)[None] | ~M)   # causal
+
+
+def test_index_all_selected_is_causal():
+    n = 320
+    all_ = np.arange(n, dtype=np.int32)[None]
+    idx = oracle.build_index(all_, all_, n)
+    for b in range((n + 63) // 64):
+        assert idx.block_offset[0, b, : idx.block_count[0, b]].tolist() == list(range(0, 64 * b + 1, 64))
+        assert idx.column_count[0, b] == 0
+    M = oracle.index_mask(idx, n)
+    np.testing.assert_array_equal(M[0], np.tril(np.ones((n, n), bool)))
+
+
+def test_index_a_shape_closed_form():
+    """Sink 128 + window 4096: for r0 >= 4095 + 128 the blocks start at
+    r0 - 4095 + 64 t, t < 65, and all 128 sink columns are leftovers."""
+    n = 64 * 80
+    v, s = oracle.a_shape_sets(n, 128, 4096)
+    idx = oracle.build_index(v[None], s[None], n)
+    for b in range(66, 80):
+        r0 = 64 * b
+        assert idx.block_offset[0, b, : idx.block_count[0, b]].tolist() == \
+            [r0 - 4095 + 64 * t for t in range(65)]
+        assert idx.column_index[0, b, : idx.column_count[0, b]].tolist() == list(range(128))
+    # early blocks: the window reaches key 0, so it tiles [0, r1] and no column is left over
+    for b in range(0, 60):
+        assert idx.block_offset[0, b, : idx.block_count[0, b]].tolist() == list(range(0, 64 * b + 1, 64))
+        assert idx.column_count[0, b] == 0
+
+
+def test_index_capacity_error():
+    v_idx, s_idx = random_sets(1, 256, 4, 40, seed=1)
+    with pytest.raises(ValueError):
+        oracle.build_index(v_idx, s_idx, 256, cap_b=1)
+
+
+# ---------------------------------------------------------------- attention
+
+def brute_masked_attention(q, k, v, idx, n, G, scale):
+    """Per-entry membership straight from the index lists, pure Python."""
+    Hq, N, D = q.shape
+    O = np.zeros((Hq, N, D))
+    for h in range(Hq):
+        g = h // G
+        for i in range(N):
+            b = i // 64
+            blocks = idx.block_offset[h, b, : idx.block_count[h, b]].tolist()
+            cols = set(idx.column_index[h, b, : idx.column_count[h, b]].tolist())
+            allowed = [j for j in range(i + 1)
+                       if any(st <= j <= st + 63 for st in blocks) or j in cols]
+            if not allowed:
+                continue
+            z = [scale * sum(q[h, i, d] * k[g, j, d] for d in range(D)) for j in allowed]
+            m = max(z)
+            w = [math.exp(t - m) for t in z]
+            tot = math.fsum(w)
+            for d in range(D):
+                O[h, i, d] = math.fsum(w[t] * v[g, allowed[t], d] for t in range(len(allowed))) / tot
+    return O
+
+
+@pytest.mark.parametrize("n,kv,ks", [(64, 3, 5), (128, 4, 9), (320, 6, 11)])
+def test_masked_attention_brute_force(n, kv, ks):
+    hq, hkv, d = 4, 2, 6
+    q, k, v = rand_qkv(hq, hkv, n, d, seed=n)
+    v_idx, s_idx = random_sets(hq, n, kv, ks, seed=n + 1)
+    idx = oracle.build_index(v_idx, s_idx, n)
+    M = oracle.index_mask(idx, n)
+    O, lse, probs = oracle.attention_with_mask(q, k, v, M, return_probs=True)
+    B = brute_masked_attention(q, k, v, idx, n, hq // hkv, 1.0 / math.sqrt(d))
+    np.testing.assert_allclose(O, B, rtol=0, atol=1e-12)
+    # softmax rows sum to one on non-empty rows, and empty rows give 0 / -inf
+    for h in range(hq):
+        rows = M[h].any(axis=1)
+        np.testing.assert_allclose(probs[h][rows].sum(1), 1.0, atol=1e-12)
+        assert np.all(O[h][~rows] == 0) and np.all(np.isneginf(lse[h][~rows]))
+    # the row-sampled evaluation is the same mask
+    items = [(h, b) for h in range(hq) for b in range(n // 64)]
+    blk = oracle.masked_attention_blocks(q, k, v, idx, items)
+    for (h, b), (o, l) in blk.items():
+        np.testing.assert_allclose(o, O[h, 64 * b: 64 * b + 64], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(l, lse[h, 64 * b: 64 * b + 64], rtol=0, atol=1e-13)
+
+
+def test_all_selected_equals_dense_and_sdpa():
+    n, d = 256, 32
+    q, k, v = rand_qkv(4, 2, n, d, seed=11)
+    all_ = np.tile(np.arange(n, dtype=np.int32), (4, 1))
+    idx = oracle.build_index(all_, all_, n)
+    O, lse = oracle.attention_with_mask(q, k, v, oracle.index_mask(idx, n))
+    Od, lsed = oracle.dense_attention(q, k, v)
+    np.testing.assert_allclose(O, Od, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, lsed, rtol=0, atol=1e-12)
+    tq = torch.from_numpy(q)[None]
+    tk = torch.from_numpy(np.repeat(k, 2, axis=0))[None]
+    tv = torch.from_numpy(np.repeat(v, 2, axis=0))[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True)[0].numpy()
+    np.testing.assert_allclose(O, ref, rtol=0, atol=1e-12)
+    blk = oracle.dense_attention_blocks(q, k, v, [(1, 2), (3, 0)])
+    np.testing.assert_allclose(blk[(1, 2)][0], ref[1, 128:192], atol=1e-12)
+    np.testing.assert_allclose(blk[(3, 0)][0], ref[3, 0:64], atol=1e-12)
+
+
+def test_single_allowed_key_returns_value_row():
+    n, d = 128, 8
+    q, k, v = rand_qkv(1, 1, n, d, seed=2)
+    v_idx = np.array([[5]], np.int32)
+    s_idx = np.array([[n - 1]], np.int32)       # diagonal offset only reachable from the last row
+    idx = oracle.build_index(v_idx, s_idx, n)
+    M = oracle.index_mask(idx, n)
+    O, lse = oracle.attention_with_mask(q, k, v, M)
+    rows = [i for i in range(5, 64) if M[0, i].sum() == 1]
+    assert rows, "expected rows whose only key is column 5"
+    for i in rows:
+        np.testing.assert_array_equal(O[0, i], v[0, 5])
+
+
+def test_linearity_and_zero_query():
+    n, d = 192, 16
+    q, k, v = rand_qkv(2, 1, n, d, seed=4)
+    v_idx, s_idx = random_sets(2, n, 5, 12, seed=6)
+    idx = oracle.build_index(v_idx, s_idx, n)
+    M = oracle.index_mask(idx, n)
+    O, _ = oracle.attention_with_mask(q, k, v, M)
+    O3, _ = oracle.attention_with_mask(q, k, -2.5 * v, M)
+    np.testing.assert_allclose(O3, -2.5 * O, atol=1e-12)
+    Oz, lz = oracle.attention_with_mask(np.zeros_like(q), k, v, M)
+    for h in range(2):
+        for i in range(n):
+            allowed = np.nonzero(M[h, i])[0]
+            if len(allowed):
+                np.testing.assert_allclose(Oz[h, i], v[0, allowed].mean(0), atol=1e-12)
+                assert abs(lz[h, i] - math.log(len(allowed))) < 1e-12
+
+
+# ---------------------------------------------------------------- block-sparse
+
+def test_block_scores_brute_force():
+    n, d = 256, 5
+    q, k, _ = rand_qkv(2, 1, n, d, seed=8)
+    u = oracle.block_scores(q, k, 1, block=64)
+    for b in range(4):
+        for c in range(4):
+            if c > b:
+                assert u[b, c] == -np.inf
+                continue
+            qm = [sum(q[1, 64 * b + t, e] for t in range(64)) / 64 for e in range(d)]
+            km = [sum(k[0, 64 * c + t, e] for t in range(64)) / 64 for e in range(d)]
+            want = sum(qm[e] * km[e] for e in range(d)) / math.sqrt(d)
+            assert abs(u[b, c] - want) < 1e-12
+
+
+def test_block_sparse_full_topk_is_dense():
+    n, d = 320, 16
+    q, k, v = rand_qkv(2, 1, n, d, seed=10)
+    cnt, offs, _ = oracle.block_sparse_select(q, k, [0, 1], topk=100)
+    nb = n // 64
+    for b in range(nb):
+        assert cnt[0, b] == b + 1 and offs[0, b, : b + 1].tolist() == [64 * c for c in range(b + 1)]
+    idx = oracle.IndexArrays(cnt, offs, np.zeros_like(cnt), np.zeros((2, nb, 0), np.int32))
+    O, _ = oracle.attention_with_mask(q, k, v, oracle.index_mask(idx, n))
+    Od, _ = oracle.dense_attention(q, k, v)
+    np.testing.assert_allclose(O, Od, atol=1e-13)
+
+
+def test_block_sparse_topk_picks_best_blocks():
+    n, d = 64 * 12, 8
+    q, k, _ = rand_qkv(1, 1, n, d, seed=12)
+    cnt, offs, scores = oracle.block_sparse_select(q, k, [0], topk=3)
+    for b in range(12):
+        chosen = set((offs[0, b, : cnt[0, b]] // 64).tolist())
+        assert len(chosen) == min(3, b + 1)
+        for c in range(b + 1):
+            if c not in chosen:
+                assert all(scores[0, b, x] >= scores[0, b, c] for x in chosen)
+
+
+def test_index_caps():
+    assert index_caps(1 << 20, 1000, 6096) == (6096, 1000)
+    assert index_caps(4096, 64, 256) == (64, 64)
