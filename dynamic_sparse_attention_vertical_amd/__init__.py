@@ -1,0 +1,15 @@
+"""MI355X-native vertical-slash dynamic sparse prefill attention.
+
+The computation lives in libmsa.so (hand-written HIP kernels for gfx950 behind
+the C ABI declared in include/msa.h); this package is a thin ctypes binding
+over it.  PyTorch provides device memory and streams only.
+"""
+
+from .msa import (MsaError, IndexTensors, Problem, alloc_index, build_index, dense_prefill,
+                  estimate_bs, estimate_vs, estimate_vs_workspace_bytes, index_caps, lib_path, load,
+                  problem, sparse_prefill)
+from .layer import vertical_slash_layer, mixed_layer
+
+__all__ = ["MsaError", "IndexTensors", "Problem", "alloc_index", "build_index", "dense_prefill",
+           "estimate_bs", "estimate_vs", "estimate_vs_workspace_bytes", "index_caps", "lib_path",
+           "load", "problem", "sparse_prefill", "vertical_slash_layer", "mixed_layer"]

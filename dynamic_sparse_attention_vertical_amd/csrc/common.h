@@ -1,0 +1,110 @@
+// Shared device helpers for the gfx950 kernels: element types, 16-byte
+// vector access, and the 32x32 MFMA step used by every contraction here.
+//
+// MFMA operand convention used throughout (one 32x32 output tile, K chunk 16):
+//   A fragment: lane l holds A[row = l%32][k = (l/32)*8 + e], e = 0..7
+//   B fragment: lane l holds B[k = (l/32)*8 + e][col = l%32], e = 0..7
+//   C/D:        lane l holds C[row = jj*8 + (l/32)*4 + i][col = l%32] in
+//               acc[jj*4 + i], jj, i = 0..3.
+// Only the row/column placement matters for correctness: A and B use the same
+// (lane, e) -> k labelling, so any hardware permutation of k cancels out.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct bf16 { uint16_t x; };
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// round-to-nearest-even float -> bfloat16 (inputs here are finite)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// Element traits: an MFMA fragment holds 8 consecutive k values.
+template <typename T> struct Elem;
+
+template <> struct Elem<bf16> {
+    typedef bf16x8 frag;                          // 16 bytes
+    static constexpr int kBytes = 2;
+    __device__ static __forceinline__ frag load_frag(const void *p) {
+        u32x4 r = *reinterpret_cast<const u32x4 *>(p);
+        return __builtin_bit_cast(frag, r);
+    }
+    __device__ static __forceinline__ frag zero_frag() {
+        u32x4 z = {0u, 0u, 0u, 0u};
+        return __builtin_bit_cast(frag, z);
+    }
+    // C += A * B over one K chunk of 16
+    __device__ static __forceinline__ void mma(f32x16 &c, const frag &a, const frag &b) {
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ frag from_f32(const float *x) {
+        u32x4 r;
+        r[0] = pack_bf16x2(x[0], x[1]);
+        r[1] = pack_bf16x2(x[2], x[3]);
+        r[2] = pack_bf16x2(x[4], x[5]);
+        r[3] = pack_bf16x2(x[6], x[7]);
+        return __builtin_bit_cast(frag, r);
+    }
+    __device__ static __forceinline__ float to_f32(uint16_t v) { return bf16_to_f32(v); }
+};
+
+template <> struct Elem<float> {
+    typedef f32x8 frag;                           // 32 bytes
+    static constexpr int kBytes = 4;
+    __device__ static __forceinline__ frag load_frag(const void *p) {
+        const f32x4 *q = reinterpret_cast<const f32x4 *>(p);
+        f32x4 a = q[0], b = q[1];
+        frag r;
+        r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+        r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+        return r;
+    }
+    __device__ static __forceinline__ frag zero_frag() {
+        frag r;
+        for (int i = 0; i < 8; ++i) r[i] = 0.f;
+        return r;
+    }
+    // Eight K=2 steps: step e contracts k = e (lanes 0-31) and k = 8+e (lanes 32-63).
+    __device__ static __forceinline__ void mma(f32x16 &c, const frag &a, const frag &b) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], b[e], c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ frag from_f32(const float *x) {
+        frag r;
+        for (int i = 0; i < 8; ++i) r[i] = x[i];
+        return r;
+    }
+};
+
+__device__ __forceinline__ float wave_shfl_xor(float v, int mask) {
+    return __shfl_xor(v, mask, 64);
+}
+
+// Number of XCDs on MI355X; consecutive workgroup ids are spread round-robin
+// over them, and each XCD has its own L2.
+constexpr int kNumXcd = 8;
+
+}  // namespace msa

@@ -1,0 +1,81 @@
+// Launch interfaces between the C-ABI layer (msa_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+struct AttnArgs {
+    const void *q, *k, *v;
+    const int32_t *block_count, *block_offset, *column_count, *column_index;
+    int32_t cap_b, cap_c;
+    void *out;
+    float *lse;
+    int32_t hq, hkv;
+    int64_t n;
+    float scale_log2;    // sm_scale * log2(e)
+    float scale;         // sm_scale
+};
+
+// dtype: 0 = bf16, 1 = fp32
+hipError_t launch_sparse_prefill(const AttnArgs &a, int dtype, hipStream_t s);
+hipError_t launch_dense_prefill(const AttnArgs &a, int dtype, hipStream_t s);
+
+struct EstArgs {
+    const void *q, *k;
+    int64_t n;
+    int32_t hq, hkv;
+    float scale_log2;
+    int64_t range_keys;  // keys per workgroup range (multiple of 64)
+    int32_t nranges;
+    float *part_m, *part_l;      // [hq][64][nranges]
+    float *row_m, *row_il;       // [hq][64]
+    float *v_score, *s_score;    // [hq][n]
+    float *diag_hi, *diag_lo;    // [hq][nranges][64]
+};
+
+hipError_t launch_estimate_scores(const EstArgs &a, int dtype, hipStream_t s);
+
+struct TopkArgs {
+    const float *src0, *src1;    // [hq][n] each
+    int32_t *dst0, *dst1;        // [hq][k0], [hq][k1]
+    int32_t k0, k1;
+    int32_t hq;
+    int64_t n;
+    int32_t nslices;
+    uint32_t *hist;              // [2*hq][2048]
+    uint32_t *state;             // [2*hq][4]
+    uint32_t *cnt;               // [2*hq][nslices][2]
+    uint32_t *off;               // [2*hq][nslices][2]
+};
+
+constexpr int kTopkSlice = 4096;   // elements per top-k workgroup slice
+
+hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
+
+struct IndexArgs {
+    const int32_t *v_idx, *s_idx;
+    int32_t kv, ks;
+    int64_t n;
+    int32_t hq;
+    int32_t *block_count, *block_offset, *column_count, *column_index;
+    int32_t cap_b, cap_c;
+};
+
+hipError_t launch_build_index(const IndexArgs &a, hipStream_t s);
+
+struct BsArgs {
+    const void *q, *k;
+    int64_t n;
+    int32_t hq, hkv;
+    float scale;
+    int32_t topk;
+    float *qm, *km;              // pooled means [hq][nb][128], [hkv][nb][128]
+    int32_t *block_count, *block_offset, *column_count;
+    int32_t cap_b;
+};
+
+hipError_t launch_estimate_bs(const BsArgs &a, int dtype, hipStream_t s);
+
+}  // namespace msa

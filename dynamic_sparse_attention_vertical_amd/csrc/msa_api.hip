@@ -1,0 +1,314 @@
+// C-ABI entry points: host-side validation, workspace layout and launches.
+// Every argument is checked before anything is enqueued; no C++ exception
+// leaves this file.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "msa.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_err[0] = 0;
+    return MSA_OK;
+}
+
+int launch_status(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(MSA_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+int check_problem(const msa_problem *p) {
+    if (!p) return fail(MSA_ERR_NULL, "problem descriptor is NULL");
+    if (p->head_dim != 128) return fail(MSA_ERR_SHAPE, "head_dim must be 128 (got %d)", p->head_dim);
+    if (p->n_q_heads <= 0 || p->n_kv_heads <= 0 || p->n_q_heads % p->n_kv_heads != 0)
+        return fail(MSA_ERR_SHAPE, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)",
+                    p->n_q_heads, p->n_kv_heads);
+    if (p->seq_len <= 0 || p->seq_len % 64 != 0 || p->seq_len >= (int64_t(1) << 31))
+        return fail(MSA_ERR_SHAPE, "seq_len must be a positive multiple of 64 below 2^31 (got %lld)",
+                    (long long)p->seq_len);
+    if (p->dtype != MSA_BF16 && p->dtype != MSA_F32)
+        return fail(MSA_ERR_DTYPE, "unknown dtype %d", p->dtype);
+    if (!(p->sm_scale >= 0.f) || isinf(p->sm_scale))
+        return fail(MSA_ERR_RANGE, "sm_scale must be finite and >= 0");
+    return MSA_OK;
+}
+
+float scale_of(const msa_problem *p) {
+    return p->sm_scale > 0.f ? p->sm_scale : 1.0f / sqrtf((float)p->head_dim);
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Estimator work split: contiguous key ranges per workgroup, sized so the grid
+// has about 2048 workgroups.
+struct EstLayout {
+    int64_t range_keys;
+    int32_t nranges;
+    int32_t nslices;
+    size_t off_part_m, off_part_l, off_row_m, off_row_il, off_hi, off_lo, off_v, off_s;
+    size_t off_hist, off_state, off_cnt, off_off, total;
+};
+
+EstLayout est_layout(const msa_problem *p) {
+    EstLayout L;
+    const int64_t n = p->seq_len;
+    int64_t rk = (n * p->n_kv_heads + 2047) / 2048;
+    rk = ((rk + 63) / 64) * 64;
+    if (rk < 256) rk = 256;
+    if (rk > 8192) rk = 8192;
+    if (rk > n) rk = n;
+    L.range_keys = rk;
+    L.nranges = (int32_t)((n + rk - 1) / rk);
+    L.nslices = (int32_t)((n + msa::kTopkSlice - 1) / msa::kTopkSlice);
+    const size_t hq = (size_t)p->n_q_heads;
+    size_t o = 0;
+    L.off_part_m = o; o = align_up(o + hq * 64 * L.nranges * 4);
+    L.off_part_l = o; o = align_up(o + hq * 64 * L.nranges * 4);
+    L.off_row_m = o;  o = align_up(o + hq * 64 * 4);
+    L.off_row_il = o; o = align_up(o + hq * 64 * 4);
+    L.off_hi = o;     o = align_up(o + hq * L.nranges * 64 * 4);
+    L.off_lo = o;     o = align_up(o + hq * L.nranges * 64 * 4);
+    L.off_v = o;      o = align_up(o + hq * (size_t)n * 4);
+    L.off_s = o;      o = align_up(o + hq * (size_t)n * 4);
+    L.off_hist = o;   o = align_up(o + 2 * hq * 2048 * 4);
+    L.off_state = o;  o = align_up(o + 2 * hq * 4 * 4);
+    L.off_cnt = o;    o = align_up(o + 2 * hq * (size_t)L.nslices * 2 * 4);
+    L.off_off = o;    o = align_up(o + 2 * hq * (size_t)L.nslices * 2 * 4);
+    L.total = o;
+    return L;
+}
+
+template <typename T> T *at(void *ws, size_t off) {
+    return reinterpret_cast<T *>(reinterpret_cast<char *>(ws) + off);
+}
+
+constexpr int64_t kBsMaxBlocks = 15360;   // LDS holds one score key per key block
+
+}  // namespace
+
+extern "C" {
+
+const char *msa_status_str(int status) {
+    switch (status) {
+        case MSA_OK: return "MSA_OK";
+        case MSA_ERR_NULL: return "MSA_ERR_NULL";
+        case MSA_ERR_SHAPE: return "MSA_ERR_SHAPE";
+        case MSA_ERR_DTYPE: return "MSA_ERR_DTYPE";
+        case MSA_ERR_RANGE: return "MSA_ERR_RANGE";
+        case MSA_ERR_CAPACITY: return "MSA_ERR_CAPACITY";
+        case MSA_ERR_WORKSPACE: return "MSA_ERR_WORKSPACE";
+        case MSA_ERR_LAUNCH: return "MSA_ERR_LAUNCH";
+        default: return "MSA_ERR_UNKNOWN";
+    }
+}
+
+const char *msa_last_error(void) { return g_err; }
+
+int msa_index_caps(const msa_problem *p, int32_t vertical_topk, int32_t slash_topk, int32_t block,
+                   int32_t *cap_blocks, int32_t *cap_cols) {
+    int st = check_problem(p);
+    if (st) return st;
+    if (!cap_blocks || !cap_cols) return fail(MSA_ERR_NULL, "cap outputs are NULL");
+    if (block != 64) return fail(MSA_ERR_RANGE, "block must be 64 (got %d)", block);
+    if (vertical_topk < 0 || vertical_topk > p->seq_len || slash_topk < 0 || slash_topk > p->seq_len)
+        return fail(MSA_ERR_RANGE, "top-k values must lie in [0, seq_len]");
+    const int64_t nqb = p->seq_len / 64;
+    *cap_blocks = (int32_t)(slash_topk < nqb ? slash_topk : nqb);
+    *cap_cols = vertical_topk;
+    return ok();
+}
+
+size_t msa_estimate_vs_workspace(const msa_problem *p, int32_t last_q, int32_t vertical_topk,
+                                 int32_t slash_topk) {
+    (void)vertical_topk;
+    (void)slash_topk;
+    if (check_problem(p) != MSA_OK || last_q != 64) return 0;
+    return est_layout(p).total;
+}
+
+int msa_estimate_vs(const msa_problem *p, const void *q, const void *k, int32_t last_q,
+                    int32_t vertical_topk, int32_t slash_topk, int32_t *v_idx, int32_t *s_idx,
+                    float *v_score, float *s_score, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+    int st = check_problem(p);
+    if (st) return st;
+    if (!q || !k || !v_idx || !s_idx || !workspace) return fail(MSA_ERR_NULL, "a required pointer is NULL");
+    if (last_q != 64) return fail(MSA_ERR_RANGE, "last_q must be 64 (got %d)", last_q);
+    if (vertical_topk < 1 || vertical_topk > p->seq_len || slash_topk < 1 || slash_topk > p->seq_len)
+        return fail(MSA_ERR_RANGE, "top-k values must lie in [1, seq_len]");
+    const EstLayout L = est_layout(p);
+    if (workspace_bytes < L.total)
+        return fail(MSA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, L.total);
+    msa::EstArgs e;
+    e.q = q;
+    e.k = k;
+    e.n = p->seq_len;
+    e.hq = p->n_q_heads;
+    e.hkv = p->n_kv_heads;
+    e.scale_log2 = scale_of(p) * msa::kLog2e;
+    e.range_keys = L.range_keys;
+    e.nranges = L.nranges;
+    e.part_m = at<float>(workspace, L.off_part_m);
+    e.part_l = at<float>(workspace, L.off_part_l);
+    e.row_m = at<float>(workspace, L.off_row_m);
+    e.row_il = at<float>(workspace, L.off_row_il);
+    e.diag_hi = at<float>(workspace, L.off_hi);
+    e.diag_lo = at<float>(workspace, L.off_lo);
+    e.v_score = v_score ? v_score : at<float>(workspace, L.off_v);
+    e.s_score = s_score ? s_score : at<float>(workspace, L.off_s);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    st = launch_status(msa::launch_estimate_scores(e, p->dtype, s), "estimate");
+    if (st) return st;
+    msa::TopkArgs t;
+    t.src0 = e.v_score;
+    t.src1 = e.s_score;
+    t.dst0 = v_idx;
+    t.dst1 = s_idx;
+    t.k0 = vertical_topk;
+    t.k1 = slash_topk;
+    t.hq = p->n_q_heads;
+    t.n = p->seq_len;
+    t.nslices = L.nslices;
+    t.hist = at<uint32_t>(workspace, L.off_hist);
+    t.state = at<uint32_t>(workspace, L.off_state);
+    t.cnt = at<uint32_t>(workspace, L.off_cnt);
+    t.off = at<uint32_t>(workspace, L.off_off);
+    return launch_status(msa::launch_topk(t, s), "top-k");
+}
+
+int msa_build_index(const msa_problem *p, const int32_t *v_idx, int32_t vertical_topk,
+                    const int32_t *s_idx, int32_t slash_topk, int32_t block,
+                    int32_t *block_count, int32_t *block_offset, int32_t cap_blocks,
+                    int32_t *column_count, int32_t *column_index, int32_t cap_cols, void *stream) {
+    int32_t need_b, need_c;
+    int st = msa_index_caps(p, vertical_topk, slash_topk, block, &need_b, &need_c);
+    if (st) return st;
+    if ((vertical_topk > 0 && !v_idx) || (slash_topk > 0 && !s_idx) || !block_count || !column_count ||
+        (cap_blocks > 0 && !block_offset) || (cap_cols > 0 && !column_index))
+        return fail(MSA_ERR_NULL, "a required pointer is NULL");
+    if (cap_blocks < need_b || cap_cols < need_c)
+        return fail(MSA_ERR_CAPACITY, "capacities (%d, %d) below required (%d, %d)", cap_blocks, cap_cols,
+                    need_b, need_c);
+    msa::IndexArgs a;
+    a.v_idx = v_idx;
+    a.s_idx = s_idx;
+    a.kv = vertical_topk;
+    a.ks = slash_topk;
+    a.n = p->seq_len;
+    a.hq = p->n_q_heads;
+    a.block_count = block_count;
+    a.block_offset = block_offset;
+    a.column_count = column_count;
+    a.column_index = column_index;
+    a.cap_b = cap_blocks;
+    a.cap_c = cap_cols;
+    return launch_status(msa::launch_build_index(a, reinterpret_cast<hipStream_t>(stream)), "build_index");
+}
+
+static int attn_common(const msa_problem *p, const void *q, const void *k, const void *v, void *out,
+                       msa::AttnArgs &a) {
+    int st = check_problem(p);
+    if (st) return st;
+    if (!q || !k || !v || !out) return fail(MSA_ERR_NULL, "a required pointer is NULL");
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.hq = p->n_q_heads;
+    a.hkv = p->n_kv_heads;
+    a.n = p->seq_len;
+    a.scale = scale_of(p);
+    a.scale_log2 = a.scale * msa::kLog2e;
+    return MSA_OK;
+}
+
+int msa_sparse_prefill(const msa_problem *p, const void *q, const void *k, const void *v,
+                       const int32_t *block_count, const int32_t *block_offset, int32_t cap_blocks,
+                       const int32_t *column_count, const int32_t *column_index, int32_t cap_cols,
+                       void *out, float *lse, void *stream) {
+    msa::AttnArgs a;
+    int st = attn_common(p, q, k, v, out, a);
+    if (st) return st;
+    if (!block_count || !column_count || (cap_blocks > 0 && !block_offset) || (cap_cols > 0 && !column_index))
+        return fail(MSA_ERR_NULL, "an index pointer is NULL");
+    if (cap_blocks < 0 || cap_cols < 0) return fail(MSA_ERR_CAPACITY, "negative capacity");
+    a.block_count = block_count;
+    a.block_offset = block_offset;
+    a.column_count = column_count;
+    a.column_index = column_index;
+    a.cap_b = cap_blocks;
+    a.cap_c = cap_cols;
+    a.lse = lse;
+    return launch_status(msa::launch_sparse_prefill(a, p->dtype, reinterpret_cast<hipStream_t>(stream)),
+                         "sparse_prefill");
+}
+
+int msa_dense_prefill(const msa_problem *p, const void *q, const void *k, const void *v, void *out,
+                      float *lse, void *stream) {
+    msa::AttnArgs a;
+    int st = attn_common(p, q, k, v, out, a);
+    if (st) return st;
+    a.block_count = a.block_offset = a.column_count = a.column_index = nullptr;
+    a.cap_b = a.cap_c = 0;
+    a.lse = lse;
+    return launch_status(msa::launch_dense_prefill(a, p->dtype, reinterpret_cast<hipStream_t>(stream)),
+                         "dense_prefill");
+}
+
+size_t msa_estimate_bs_workspace(const msa_problem *p, int32_t block) {
+    if (check_problem(p) != MSA_OK || block != 64) return 0;
+    const size_t nb = (size_t)(p->seq_len / 64);
+    return align_up((size_t)p->n_q_heads * nb * 128 * 4) + align_up((size_t)p->n_kv_heads * nb * 128 * 4);
+}
+
+int msa_estimate_bs(const msa_problem *p, const void *q, const void *k, int32_t block, int32_t topk_blocks,
+                    int32_t *block_count, int32_t *block_offset, int32_t cap_blocks, int32_t *column_count,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+    int st = check_problem(p);
+    if (st) return st;
+    if (!q || !k || !block_count || !block_offset || !column_count || !workspace)
+        return fail(MSA_ERR_NULL, "a required pointer is NULL");
+    if (block != 64) return fail(MSA_ERR_RANGE, "block must be 64 (got %d)", block);
+    const int64_t nb = p->seq_len / 64;
+    if (nb > kBsMaxBlocks)
+        return fail(MSA_ERR_SHAPE, "block-sparse estimation supports at most %lld key blocks",
+                    (long long)kBsMaxBlocks);
+    if (topk_blocks < 1) return fail(MSA_ERR_RANGE, "topk_blocks must be >= 1");
+    const int64_t need = topk_blocks < nb ? topk_blocks : nb;
+    if (cap_blocks < need) return fail(MSA_ERR_CAPACITY, "cap_blocks %d below %lld", cap_blocks, (long long)need);
+    const size_t ws = msa_estimate_bs_workspace(p, block);
+    if (workspace_bytes < ws) return fail(MSA_ERR_WORKSPACE, "workspace too small: %zu < %zu", workspace_bytes, ws);
+    msa::BsArgs a;
+    a.q = q;
+    a.k = k;
+    a.n = p->seq_len;
+    a.hq = p->n_q_heads;
+    a.hkv = p->n_kv_heads;
+    a.scale = scale_of(p);
+    a.topk = topk_blocks;
+    a.qm = at<float>(workspace, 0);
+    a.km = at<float>(workspace, align_up((size_t)p->n_q_heads * nb * 128 * 4));
+    a.block_count = block_count;
+    a.block_offset = block_offset;
+    a.column_count = column_count;
+    a.cap_b = cap_blocks;
+    return launch_status(msa::launch_estimate_bs(a, p->dtype, reinterpret_cast<hipStream_t>(stream)),
+                         "estimate_bs");
+}
+
+}  // extern "C"

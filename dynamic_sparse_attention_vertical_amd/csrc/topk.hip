@@ -1,0 +1,268 @@
+// Exact top-k of the vertical and slash scores, per head, for gfx950.
+//
+// The pages warn that per-query top-k on a GPU is not kernel friendly ("How to
+// optimise the TTFT of an 8B LLM with 1M tokens to 20 seconds", section on
+// co-designing algorithm and system); here it is one selection per head over
+// N scores, done as a radix select on the scores' bit patterns.  Scores are
+// non-negative floats, so their IEEE bit patterns order like unsigned
+// integers.  Three histogram passes (11 + 11 + 10 bits) find the k-th largest
+// pattern T and how many entries equal to T are needed; a count / scan / write
+// sequence then emits, in ascending index order, every entry above T and the
+// lowest-index entries equal to T.  Ties therefore go to the lower index and
+// the result is exact and deterministic (integer atomics only).
+//
+// Rows: 2*hq of them -- rows [0, hq) select vertical columns (k0 each),
+// rows [hq, 2hq) select slash diagonals (k1 each).
+#include "common.h"
+#include "kernels.h"
+
+namespace msa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kPer = kTopkSlice / kThreads;     // 16 consecutive elements per thread
+
+struct RowView {
+    const float *src;
+    int32_t *dst;
+    int32_t k;
+};
+
+__device__ __forceinline__ RowView row_view(const TopkArgs &a, int row) {
+    RowView r;
+    if (row < a.hq) {
+        r.src = a.src0 + (int64_t)row * a.n;
+        r.dst = a.dst0 + (int64_t)row * a.k0;
+        r.k = a.k0;
+    } else {
+        r.src = a.src1 + (int64_t)(row - a.hq) * a.n;
+        r.dst = a.dst1 + (int64_t)(row - a.hq) * a.k1;
+        r.k = a.k1;
+    }
+    return r;
+}
+
+// pass p: bucket bits and the prefix the element must match
+__device__ __forceinline__ int pass_shift(int p) { return p == 0 ? 21 : (p == 1 ? 10 : 0); }
+__device__ __forceinline__ int pass_bits(int p) { return p == 2 ? 10 : 11; }
+
+__global__ __launch_bounds__(kThreads) void topk_init_kernel(TopkArgs a) {
+    const int row = blockIdx.x;
+    for (int i = threadIdx.x; i < 2048; i += kThreads) a.hist[(int64_t)row * 2048 + i] = 0u;
+    if (threadIdx.x == 0) {
+        RowView r = row_view(a, row);
+        a.state[row * 4 + 0] = 0u;                 // prefix of the threshold found so far
+        a.state[row * 4 + 1] = (uint32_t)r.k;      // entries still to take at or below it
+    }
+}
+
+__device__ __forceinline__ void load_slice(const float *src, int64_t n, int64_t e0, uint32_t (&x)[kPer],
+                                           bool (&valid)[kPer]) {
+    if (e0 + kPer <= n) {
+#pragma unroll
+        for (int c = 0; c < kPer / 4; ++c) {
+            u32x4 w = *reinterpret_cast<const u32x4 *>(src + e0 + 4 * c);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { x[4 * c + i] = w[i]; valid[4 * c + i] = true; }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            valid[i] = e0 + i < n;
+            x[i] = valid[i] ? __float_as_uint(src[e0 + i]) : 0u;
+        }
+    }
+}
+
+template <int P>
+__global__ __launch_bounds__(kThreads) void topk_hist_kernel(TopkArgs a) {
+    __shared__ uint32_t h[2048];
+    const int row = blockIdx.y;
+    const int64_t e0 = (int64_t)blockIdx.x * kTopkSlice + threadIdx.x * kPer;
+    constexpr int nb = (P == 2) ? 1024 : 2048;
+    for (int i = threadIdx.x; i < nb; i += kThreads) h[i] = 0u;
+    __syncthreads();
+    RowView r = row_view(a, row);
+    const uint32_t prefix = a.state[row * 4 + 0];
+    uint32_t x[kPer];
+    bool valid[kPer];
+    load_slice(r.src, a.n, e0, x, valid);
+    const int sh = pass_shift(P);
+    const int hi_sh = sh + pass_bits(P);         // bits above the bucket must equal prefix
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        if (!valid[i]) continue;
+        const bool match = (P == 0) ? true : ((x[i] >> hi_sh) == prefix);
+        if (match) atomicAdd(&h[(x[i] >> sh) & (nb - 1)], 1u);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nb; i += kThreads)
+        if (h[i]) atomicAdd(&a.hist[(int64_t)row * 2048 + i], h[i]);
+}
+
+// exclusive prefix sum over the 256 threads of a workgroup
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *tmp, uint32_t *total) {
+    const int t = threadIdx.x;
+    tmp[t] = v;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+        uint32_t add = t >= off ? tmp[t - off] : 0u;
+        __syncthreads();
+        tmp[t] += add;
+        __syncthreads();
+    }
+    const uint32_t incl = tmp[t];
+    if (total) *total = tmp[kThreads - 1];
+    __syncthreads();
+    return incl - v;
+}
+
+template <int P>
+__global__ __launch_bounds__(kThreads) void topk_pick_kernel(TopkArgs a) {
+    __shared__ uint32_t tmp[kThreads];
+    const int row = blockIdx.x;
+    constexpr int nb = (P == 2) ? 1024 : 2048;
+    constexpr int per = nb / kThreads;
+    uint32_t *hist = a.hist + (int64_t)row * 2048;
+    const uint32_t krem = a.state[row * 4 + 1];
+    // thread t owns buckets nb-1-t*per ... nb-per-t*per (top down)
+    uint32_t c[per];
+    uint32_t sum = 0;
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+        c[i] = hist[nb - 1 - (threadIdx.x * per + i)];
+        sum += c[i];
+    }
+    __syncthreads();
+    const uint32_t above = block_exclusive_scan(sum, tmp, nullptr);
+#pragma unroll
+    for (int i = 0; i < per; ++i) hist[nb - 1 - (threadIdx.x * per + i)] = 0u;   // ready for next pass
+    if (above < krem && krem <= above + sum) {
+        uint32_t acc = above;
+#pragma unroll
+        for (int i = 0; i < per; ++i) {
+            if (acc < krem && krem <= acc + c[i]) {
+                const uint32_t bucket = (uint32_t)(nb - 1 - (threadIdx.x * per + i));
+                const uint32_t prefix = a.state[row * 4 + 0];
+                a.state[row * 4 + 0] = (prefix << pass_bits(P)) | bucket;
+                a.state[row * 4 + 1] = krem - acc;
+            }
+            acc += c[i];
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void topk_count_kernel(TopkArgs a) {
+    __shared__ uint32_t red[2][kThreads / 64];
+    const int row = blockIdx.y;
+    const int64_t e0 = (int64_t)blockIdx.x * kTopkSlice + threadIdx.x * kPer;
+    RowView r = row_view(a, row);
+    const uint32_t T = a.state[row * 4 + 0];
+    uint32_t x[kPer];
+    bool valid[kPer];
+    load_slice(r.src, a.n, e0, x, valid);
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        gt += (valid[i] && x[i] > T) ? 1u : 0u;
+        eq += (valid[i] && x[i] == T) ? 1u : 0u;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        gt += __shfl_xor(gt, off, 64);
+        eq += __shfl_xor(eq, off, 64);
+    }
+    if ((threadIdx.x & 63) == 0) { red[0][threadIdx.x >> 6] = gt; red[1][threadIdx.x >> 6] = eq; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t G = 0, Q = 0;
+        for (int w = 0; w < kThreads / 64; ++w) { G += red[0][w]; Q += red[1][w]; }
+        const int64_t o = ((int64_t)row * a.nslices + blockIdx.x) * 2;
+        a.cnt[o] = G;
+        a.cnt[o + 1] = Q;
+    }
+}
+
+// per row: slice output offsets and equal-entries-before counts
+__global__ __launch_bounds__(kThreads) void topk_scan_kernel(TopkArgs a) {
+    __shared__ uint32_t tmp[kThreads];
+    const int row = blockIdx.x;
+    const uint32_t krem = a.state[row * 4 + 1];
+    uint32_t eq_run = 0, sel_run = 0;
+    for (int s0 = 0; s0 < a.nslices; s0 += kThreads) {
+        const int s = s0 + threadIdx.x;
+        const int64_t o = ((int64_t)row * a.nslices + s) * 2;
+        const uint32_t gt = s < a.nslices ? a.cnt[o] : 0u;
+        const uint32_t eq = s < a.nslices ? a.cnt[o + 1] : 0u;
+        uint32_t eq_tot;
+        const uint32_t eq_before = eq_run + block_exclusive_scan(eq, tmp, &eq_tot);
+        const uint32_t chosen = eq_before >= krem ? 0u : min(eq, krem - eq_before);
+        uint32_t sel_tot;
+        const uint32_t sel_before = sel_run + block_exclusive_scan(gt + chosen, tmp, &sel_tot);
+        if (s < a.nslices) {
+            a.off[o] = sel_before;
+            a.off[o + 1] = eq_before;
+        }
+        eq_run += eq_tot;
+        sel_run += sel_tot;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void topk_write_kernel(TopkArgs a) {
+    __shared__ uint32_t tmp[kThreads];
+    const int row = blockIdx.y;
+    const int64_t e0 = (int64_t)blockIdx.x * kTopkSlice + threadIdx.x * kPer;
+    RowView r = row_view(a, row);
+    const uint32_t T = a.state[row * 4 + 0];
+    const uint32_t krem = a.state[row * 4 + 1];
+    const int64_t o = ((int64_t)row * a.nslices + blockIdx.x) * 2;
+    const uint32_t slice_off = a.off[o], slice_eq = a.off[o + 1];
+    uint32_t x[kPer];
+    bool valid[kPer];
+    load_slice(r.src, a.n, e0, x, valid);
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        gt += (valid[i] && x[i] > T) ? 1u : 0u;
+        eq += (valid[i] && x[i] == T) ? 1u : 0u;
+    }
+    const uint32_t eq_before = slice_eq + block_exclusive_scan(eq, tmp, nullptr);
+    const uint32_t chosen = eq_before >= krem ? 0u : min(eq, krem - eq_before);
+    uint32_t pos = slice_off + block_exclusive_scan(gt + chosen, tmp, nullptr);
+    uint32_t eq_seen = eq_before;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        if (!valid[i]) continue;
+        bool take = x[i] > T;
+        if (x[i] == T) {
+            take = eq_seen < krem;
+            ++eq_seen;
+        }
+        if (take) {
+            if (pos < (uint32_t)r.k) r.dst[pos] = (int32_t)(e0 + i);
+            ++pos;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
+    const int rows = 2 * a.hq;
+    hipError_t e;
+    hipLaunchKernelGGL(topk_init_kernel, dim3(rows), dim3(kThreads), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const dim3 grid(a.nslices, rows);
+    hipLaunchKernelGGL(topk_hist_kernel<0>, grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(topk_pick_kernel<0>, dim3(rows), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(topk_hist_kernel<1>, grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(topk_pick_kernel<1>, dim3(rows), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(topk_hist_kernel<2>, grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(topk_pick_kernel<2>, dim3(rows), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(topk_count_kernel, grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(topk_scan_kernel, dim3(rows), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(topk_write_kernel, grid, dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace msa

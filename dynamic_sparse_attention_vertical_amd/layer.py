@@ -1,0 +1,149 @@
+"""One attention layer's sparse prefill, composed from the C-ABI steps.
+
+vertical_slash_layer is the composition the MInference README exposes as one
+kernel-only call, vertical_slash_sparse_attention(q, k, v, vertical_topk,
+slash) ("MInference 1.0 README", section "How to use MInference", kernel-only
+usage): estimate the index online, build the work lists, run the sparse
+kernel.  mixed_layer runs heads with different patterns in one layer (A-shape,
+vertical-slash and block-sparse heads, the three patterns of talk slides
+"System-Algorithm Co-design", patterns slide), sharing one sparse-attention
+launch.  Buffers can be preallocated once (LayerPlan) so repeated calls
+allocate nothing.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+from . import msa
+
+
+@dataclass
+class LayerPlan:
+    """Preallocated device buffers for one layer shape."""
+    n_q_heads: int
+    n_kv_heads: int
+    seq_len: int
+    vertical_topk: int
+    slash_topk: int
+    device: str = "cuda"
+    dtype: torch.dtype = torch.bfloat16
+    index: msa.IndexTensors = field(init=False)
+    workspace: torch.Tensor = field(init=False)
+    v_idx: torch.Tensor = field(init=False)
+    s_idx: torch.Tensor = field(init=False)
+
+    def __post_init__(self):
+        cb, cc = msa.index_caps(self.seq_len, self.vertical_topk, self.slash_topk, self.n_q_heads)
+        self.index = msa.alloc_index(self.n_q_heads, self.seq_len, cb, cc, self.device)
+        ws = msa.estimate_vs_workspace_bytes(self.n_q_heads, self.n_kv_heads, self.seq_len, self.dtype)
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=self.device)
+        i32 = dict(dtype=torch.int32, device=self.device)
+        self.v_idx = torch.empty((self.n_q_heads, self.vertical_topk), **i32)
+        self.s_idx = torch.empty((self.n_q_heads, self.slash_topk), **i32)
+
+
+def vertical_slash_layer(q, k, v, vertical_topk: int, slash_topk: int, *, plan: LayerPlan | None = None,
+                         out: torch.Tensor | None = None, lse=None, stream=None):
+    """Estimate + build index + sparse prefill for every head of q.
+
+    Returns (out, plan); plan.v_idx / plan.s_idx / plan.index hold the index."""
+    hq, n = q.shape[0], q.shape[1]
+    if plan is None:
+        plan = LayerPlan(hq, k.shape[0], n, vertical_topk, slash_topk, str(q.device), q.dtype)
+    msa.estimate_vs(q, k, vertical_topk, slash_topk, workspace=plan.workspace, v_idx=plan.v_idx,
+                    s_idx=plan.s_idx, stream=stream)
+    msa.build_index(plan.v_idx, plan.s_idx, n, out=plan.index, stream=stream)
+    res = msa.sparse_prefill(q, k, v, plan.index, out=out, lse=lse, stream=stream)
+    return res, plan
+
+
+def _slice_index(idx: msa.IndexTensors, h0: int, h1: int) -> msa.IndexTensors:
+    return msa.IndexTensors(idx.block_count[h0:h1], idx.block_offset[h0:h1],
+                            idx.column_count[h0:h1], idx.column_index[h0:h1])
+
+
+def _runs(patterns, pat):
+    """Contiguous head ranges [h0, h1) with pattern pat."""
+    out, h = [], 0
+    while h < len(patterns):
+        if patterns[h] == pat:
+            h1 = h
+            while h1 < len(patterns) and patterns[h1] == pat:
+                h1 += 1
+            out.append((h, h1))
+            h = h1
+        else:
+            h += 1
+    return out
+
+
+@dataclass
+class MixedPlan:
+    patterns: tuple
+    n_kv_heads: int
+    seq_len: int
+    vertical_topk: int
+    slash_topk: int
+    sink: int
+    window: int
+    bs_topk: int
+    device: str = "cuda"
+    dtype: torch.dtype = torch.bfloat16
+    index: msa.IndexTensors = field(init=False)
+
+    def __post_init__(self):
+        n, hq = self.seq_len, len(self.patterns)
+        nqb = n // msa.BLOCK
+        caps = [(0, 0)]
+        if "vs" in self.patterns:
+            caps.append(msa.index_caps(n, self.vertical_topk, self.slash_topk, 1))
+        if "a" in self.patterns:
+            caps.append(msa.index_caps(n, min(self.sink, n), min(self.window, n), 1))
+        if "bs" in self.patterns:
+            caps.append((min(self.bs_topk, nqb), 0))
+        cb = max(c[0] for c in caps)
+        cc = max(c[1] for c in caps)
+        self.index = msa.alloc_index(hq, n, cb, cc, self.device)
+        i32 = dict(dtype=torch.int32, device=self.device)
+        na = max(sum(p == "a" for p in self.patterns), 1)
+        self.a_v = torch.arange(min(self.sink, n), **i32).expand(na, -1).contiguous()
+        self.a_s = torch.arange(min(self.window, n), **i32).expand(na, -1).contiguous()
+        nvs = sum(p == "vs" for p in self.patterns)
+        self.v_idx = torch.empty((max(nvs, 1), self.vertical_topk), **i32)
+        self.s_idx = torch.empty((max(nvs, 1), self.slash_topk), **i32)
+        G = hq // self.n_kv_heads
+        ws_vs = max([msa.estimate_vs_workspace_bytes(h1 - h0, (h1 - h0) // G, n, self.dtype)
+                     for h0, h1 in _runs(self.patterns, "vs")] or [0])
+        self.workspace = torch.empty(max(ws_vs, 1), dtype=torch.uint8, device=self.device)
+
+
+def mixed_layer(q, k, v, plan: MixedPlan, *, out: torch.Tensor | None = None, lse=None, stream=None):
+    """Per-head patterns in one layer: 'a' (static sink + window index), 'vs'
+    (online vertical-slash estimate) and 'bs' (online block-sparse estimate);
+    then a single sparse prefill over all heads.  Head runs must align with kv
+    groups."""
+    hq, n = q.shape[0], q.shape[1]
+    G = hq // k.shape[0]
+    vs_row = 0
+    for pat in ("a", "vs", "bs"):
+        for h0, h1 in _runs(plan.patterns, pat):
+            if h0 % G or h1 % G:
+                raise msa.MsaError("pattern runs must align with kv-head groups")
+            qs, ks_ = q[h0:h1], k[h0 // G: h1 // G]
+            sub = _slice_index(plan.index, h0, h1)
+            if pat == "a":
+                nh = h1 - h0
+                msa.build_index(plan.a_v[:nh], plan.a_s[:nh], n, out=sub, stream=stream)
+            elif pat == "vs":
+                nh = h1 - h0
+                vi, si = plan.v_idx[vs_row: vs_row + nh], plan.s_idx[vs_row: vs_row + nh]
+                vs_row += nh
+                msa.estimate_vs(qs, ks_, plan.vertical_topk, plan.slash_topk, workspace=plan.workspace,
+                                v_idx=vi, s_idx=si, stream=stream)
+                msa.build_index(vi, si, n, out=sub, stream=stream)
+            else:
+                msa.estimate_bs(qs, ks_, plan.bs_topk, out=sub, stream=stream)
+    return msa.sparse_prefill(q, k, v, plan.index, out=out, lse=lse, stream=stream)

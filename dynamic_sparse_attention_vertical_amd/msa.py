@@ -1,0 +1,275 @@
+"""ctypes binding for libmsa.so.
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, their data pointers and the current HIP stream are handed to the C
+entry points, and a non-zero status raises MsaError with the library's message.
+Every step of the computation runs in the HIP kernels; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsa.so")
+_lib = None
+
+MSA_BF16, MSA_F32 = 0, 1
+HEAD_DIM = 128
+BLOCK = 64
+LAST_Q = 64
+
+
+class MsaError(RuntimeError):
+    pass
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("seq_len", ctypes.c_int64), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("sm_scale", ctypes.c_float)]
+
+
+_VP = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_SIGS = {
+    "msa_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "msa_last_error": (ctypes.c_char_p, []),
+    "msa_index_caps": (ctypes.c_int, [_VP, _I32, _I32, _I32, _VP, _VP]),
+    "msa_estimate_vs_workspace": (ctypes.c_size_t, [_VP, _I32, _I32, _I32]),
+    "msa_estimate_vs": (ctypes.c_int, [_VP, _VP, _VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP,
+                                       ctypes.c_size_t, _VP]),
+    "msa_build_index": (ctypes.c_int, [_VP, _VP, _I32, _VP, _I32, _I32, _VP, _VP, _I32, _VP, _VP,
+                                       _I32, _VP]),
+    "msa_sparse_prefill": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _I32, _VP,
+                                          _VP, _VP]),
+    "msa_dense_prefill": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "msa_estimate_bs_workspace": (ctypes.c_size_t, [_VP, _I32]),
+    "msa_estimate_bs": (ctypes.c_int, [_VP, _VP, _VP, _I32, _I32, _VP, _VP, _I32, _VP, _VP,
+                                       ctypes.c_size_t, _VP]),
+}
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Load libmsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise MsaError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -m dynamic_sparse_attention_vertical_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        lib = load()
+        raise MsaError(f"{what}: {lib.msa_status_str(status).decode()}: "
+                       f"{lib.msa_last_error().decode()}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MSA_BF16
+    if t.dtype == torch.float32:
+        return MSA_F32
+    raise MsaError(f"unsupported dtype {t.dtype}")
+
+
+def problem(n_q_heads: int, n_kv_heads: int, seq_len: int, dtype: int, sm_scale: float = 0.0) -> Problem:
+    return Problem(n_q_heads, n_kv_heads, seq_len, HEAD_DIM, dtype, sm_scale)
+
+
+def _problem_of(q: torch.Tensor, k: torch.Tensor, sm_scale: float) -> Problem:
+    if q.dim() != 3 or k.dim() != 3:
+        raise MsaError("q and k must be [heads, seq_len, head_dim]")
+    return problem(q.shape[0], k.shape[0], q.shape[1], _dtype_code(q), sm_scale)
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not t.is_cuda:
+        raise MsaError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise MsaError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+@dataclass
+class IndexTensors:
+    """Per-query-block work lists on the GPU (int32)."""
+    block_count: torch.Tensor      # [H, nQB]
+    block_offset: torch.Tensor     # [H, nQB, cap_blocks]
+    column_count: torch.Tensor     # [H, nQB]
+    column_index: torch.Tensor     # [H, nQB, cap_cols]
+
+    @property
+    def cap_blocks(self) -> int:
+        return self.block_offset.shape[2]
+
+    @property
+    def cap_cols(self) -> int:
+        return self.column_index.shape[2]
+
+
+def index_caps(seq_len: int, vertical_topk: int, slash_topk: int, n_q_heads: int = 1):
+    cb, cc = ctypes.c_int32(), ctypes.c_int32()
+    p = problem(n_q_heads, 1, seq_len, MSA_BF16)
+    _check(load().msa_index_caps(ctypes.byref(p), vertical_topk, slash_topk, BLOCK,
+                                 ctypes.byref(cb), ctypes.byref(cc)), "msa_index_caps")
+    return cb.value, cc.value
+
+
+def alloc_index(n_q_heads: int, seq_len: int, cap_blocks: int, cap_cols: int, device="cuda") -> IndexTensors:
+    nqb = seq_len // BLOCK
+    i32 = dict(dtype=torch.int32, device=device)
+    return IndexTensors(torch.empty((n_q_heads, nqb), **i32),
+                        torch.empty((n_q_heads, nqb, max(cap_blocks, 1)), **i32)[:, :, :cap_blocks],
+                        torch.empty((n_q_heads, nqb), **i32),
+                        torch.empty((n_q_heads, nqb, max(cap_cols, 1)), **i32)[:, :, :cap_cols])
+
+
+def estimate_vs_workspace_bytes(n_q_heads: int, n_kv_heads: int, seq_len: int, dtype=torch.bfloat16) -> int:
+    p = problem(n_q_heads, n_kv_heads, seq_len, MSA_BF16 if dtype == torch.bfloat16 else MSA_F32)
+    return int(load().msa_estimate_vs_workspace(ctypes.byref(p), LAST_Q, 1, 1))
+
+
+def estimate_vs(q: torch.Tensor, k: torch.Tensor, vertical_topk: int, slash_topk: int, *,
+                last_q: int = LAST_Q, v_score: torch.Tensor | None = None,
+                s_score: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                v_idx: torch.Tensor | None = None, s_idx: torch.Tensor | None = None,
+                sm_scale: float = 0.0, stream=None):
+    """Vertical and slash index sets, each [Hq, k] int32 ascending."""
+    lib = load()
+    p = _problem_of(q, k, sm_scale)
+    hq, n = q.shape[0], q.shape[1]
+    ws_bytes = int(lib.msa_estimate_vs_workspace(ctypes.byref(p), last_q, vertical_topk, slash_topk))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    if v_idx is None:
+        v_idx = torch.empty((hq, vertical_topk), dtype=torch.int32, device=q.device)
+    if s_idx is None:
+        s_idx = torch.empty((hq, slash_topk), dtype=torch.int32, device=q.device)
+    for t, name in ((v_score, "v_score"), (s_score, "s_score")):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (hq, n)):
+            raise MsaError(f"{name} must be float32 [{hq}, {n}]")
+    _check(lib.msa_estimate_vs(ctypes.byref(p), _dev(q, "q"), _dev(k, "k"), last_q, vertical_topk,
+                               slash_topk, _dev(v_idx, "v_idx"), _dev(s_idx, "s_idx"),
+                               _dev(v_score, "v_score") if v_score is not None else None,
+                               _dev(s_score, "s_score") if s_score is not None else None,
+                               _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                               _stream(stream)), "msa_estimate_vs")
+    return v_idx, s_idx
+
+
+def build_index(v_idx: torch.Tensor, s_idx: torch.Tensor, seq_len: int, *,
+                out: IndexTensors | None = None, stream=None) -> IndexTensors:
+    lib = load()
+    hq, kv = v_idx.shape
+    ks = s_idx.shape[1]
+    p = problem(hq, 1, seq_len, MSA_BF16)
+    if out is None:
+        cb, cc = index_caps(seq_len, kv, ks, hq)
+        out = alloc_index(hq, seq_len, cb, cc, v_idx.device)
+    for t in (v_idx, s_idx):
+        if t.dtype != torch.int32:
+            raise MsaError("index sets must be int32")
+    _check(lib.msa_build_index(ctypes.byref(p), _dev(v_idx, "v_idx") if kv else None, kv,
+                               _dev(s_idx, "s_idx") if ks else None, ks, BLOCK,
+                               _dev(out.block_count, "block_count"), out.block_offset.data_ptr(),
+                               out.cap_blocks, _dev(out.column_count, "column_count"),
+                               out.column_index.data_ptr(), out.cap_cols, _stream(stream)),
+           "msa_build_index")
+    return out
+
+
+def _index_ptrs(idx: IndexTensors, hq: int, n: int):
+    nqb = n // BLOCK
+    for name in ("block_count", "column_count"):
+        t = getattr(idx, name)
+        if t.dtype != torch.int32 or tuple(t.shape) != (hq, nqb) or not t.is_contiguous():
+            raise MsaError(f"{name} must be contiguous int32 [{hq}, {nqb}]")
+    for name in ("block_offset", "column_index"):
+        t = getattr(idx, name)
+        if t.dtype != torch.int32 or t.shape[0] != hq or t.shape[1] != nqb or \
+                t.stride(2) != 1 or t.stride(1) != t.shape[2] or t.stride(0) != nqb * t.shape[2]:
+            if t.shape[2] > 0:
+                raise MsaError(f"{name} must be a dense int32 [{hq}, {nqb}, cap] array")
+    return (idx.block_count.data_ptr(), idx.block_offset.data_ptr(), idx.cap_blocks,
+            idx.column_count.data_ptr(), idx.column_index.data_ptr(), idx.cap_cols)
+
+
+def sparse_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: IndexTensors, *,
+                   out: torch.Tensor | None = None, lse: torch.Tensor | bool | None = None,
+                   sm_scale: float = 0.0, stream=None):
+    """Causal attention restricted to the work lists.  Returns out (and lse if requested)."""
+    lib = load()
+    p = _problem_of(q, k, sm_scale)
+    hq, n = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    want_lse = lse is not None and lse is not False
+    if lse is True:
+        lse = torch.empty((hq, n), dtype=torch.float32, device=q.device)
+    bc, bo, cb, cc, ci, ccap = _index_ptrs(index, hq, n)
+    _check(lib.msa_sparse_prefill(ctypes.byref(p), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
+                                  bc, bo, cb, cc, ci, ccap, _dev(out, "out"),
+                                  _dev(lse, "lse") if want_lse else None, _stream(stream)),
+           "msa_sparse_prefill")
+    return (out, lse) if want_lse else out
+
+
+def dense_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, out: torch.Tensor | None = None,
+                  lse: torch.Tensor | bool | None = None, sm_scale: float = 0.0, stream=None):
+    """Dense causal attention.  Returns out (and lse if requested)."""
+    lib = load()
+    p = _problem_of(q, k, sm_scale)
+    hq, n = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    want_lse = lse is not None and lse is not False
+    if lse is True:
+        lse = torch.empty((hq, n), dtype=torch.float32, device=q.device)
+    _check(lib.msa_dense_prefill(ctypes.byref(p), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
+                                 _dev(out, "out"), _dev(lse, "lse") if want_lse else None,
+                                 _stream(stream)), "msa_dense_prefill")
+    return (out, lse) if want_lse else out
+
+
+def estimate_bs(q: torch.Tensor, k: torch.Tensor, topk_blocks: int, *, cap_blocks: int | None = None,
+                out: IndexTensors | None = None, workspace: torch.Tensor | None = None,
+                sm_scale: float = 0.0, stream=None) -> IndexTensors:
+    """Block-sparse work lists (no columns)."""
+    lib = load()
+    p = _problem_of(q, k, sm_scale)
+    hq, n = q.shape[0], q.shape[1]
+    nqb = n // BLOCK
+    if out is None:
+        cap = cap_blocks if cap_blocks is not None else min(topk_blocks, nqb)
+        out = alloc_index(hq, n, cap, 0, q.device)
+    ws_bytes = int(lib.msa_estimate_bs_workspace(ctypes.byref(p), BLOCK))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.msa_estimate_bs(ctypes.byref(p), _dev(q, "q"), _dev(k, "k"), BLOCK, topk_blocks,
+                               _dev(out.block_count, "block_count"), out.block_offset.data_ptr(),
+                               out.cap_blocks, _dev(out.column_count, "column_count"),
+                               _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                               _stream(stream)), "msa_estimate_bs")
+    return out

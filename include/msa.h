@@ -1,0 +1,175 @@
+/*
+ * msa.h -- vertical-slash dynamic sparse prefill attention for MI355X (gfx950).
+ *
+ * The method (MInference): each attention head follows a sparse pattern; at
+ * prefill time the head's sparse index is estimated online from the input and
+ * attention is computed only over the selected entries ("MInference 1.0
+ * README", section "TL;DR"; talk slides "System-Algorithm Co-design", slide
+ * "MInference", steps 1-2).  For vertical-slash heads the index is a set of key
+ * columns (vertical lines) and a set of diagonals (slash lines) (same slides,
+ * slide "Dynamic sparsity in attention").  The README's kernel-only interface
+ * is one fused call per pattern returning the attention output
+ * (vertical_slash_sparse_attention(q, k, v, vertical_topk, slash),
+ * block_sparse_attention(q, k, v, topk), section "How to use MInference",
+ * kernel-only usage).  This library splits that call into its steps:
+ *
+ *   msa_estimate_vs      -> vertical and slash index sets (top-k)
+ *   msa_build_index      -> per-query-block work lists (64-wide key blocks
+ *                           covering the diagonals, plus leftover columns)
+ *   msa_sparse_prefill   -> causal attention over the work lists
+ *   msa_dense_prefill    -> dense causal attention (the speedup denominator)
+ *   msa_estimate_bs      -> block-sparse work lists (mean-pooled block scores)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  * Tensors are device memory owned by the caller, batch 1, contiguous
+ *    [heads, seq_len, head_dim] row-major.  Q has n_q_heads heads; K and V have
+ *    n_kv_heads; q head h reads kv head h / (n_q_heads / n_kv_heads).
+ *  * head_dim must be 128; seq_len must be a positive multiple of 64 and below
+ *    2^31; n_q_heads must be a multiple of n_kv_heads.
+ *  * A subset of heads is selected by offsetting the pointers (q by h0 heads,
+ *    k/v by h0/G heads) and passing the subset's head counts.
+ *  * The library never allocates or frees device memory.  Scratch memory comes
+ *    from a caller-provided workspace whose size the *_workspace call returns.
+ *  * `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Work is enqueued asynchronously; nothing is copied to the host.
+ *  * Every call validates its arguments on the host before touching the
+ *    device, and returns MSA_OK or an error status without enqueuing anything.
+ *    msa_last_error() then gives a message (thread-local).  Launch failures
+ *    return MSA_ERR_LAUNCH.  Faults inside kernels surface at the caller's next
+ *    synchronisation.  No C++ exception crosses this interface.
+ *  * Calls keep no state between them; concurrent calls on different streams
+ *    with disjoint outputs and workspaces are safe.
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MSA_OK = 0,
+    MSA_ERR_NULL = 1,       /* a required pointer is NULL */
+    MSA_ERR_SHAPE = 2,      /* unsupported head counts, seq_len or head_dim */
+    MSA_ERR_DTYPE = 3,      /* unknown element type */
+    MSA_ERR_RANGE = 4,      /* a scalar argument is out of range (top-k, block, last_q) */
+    MSA_ERR_CAPACITY = 5,   /* an index capacity is smaller than msa_index_caps returns */
+    MSA_ERR_WORKSPACE = 6,  /* workspace smaller than the *_workspace size */
+    MSA_ERR_LAUNCH = 7      /* the HIP runtime refused a launch */
+} msa_status;
+
+typedef enum {
+    MSA_BF16 = 0,           /* bfloat16 Q/K/V/out, fp32 accumulation */
+    MSA_F32 = 1             /* float32 Q/K/V/out, fp32 accumulation */
+} msa_dtype;
+
+typedef struct {
+    int32_t n_q_heads;
+    int32_t n_kv_heads;
+    int64_t seq_len;
+    int32_t head_dim;       /* must be 128 */
+    int32_t dtype;          /* msa_dtype */
+    float sm_scale;         /* softmax scale; 0 selects 1/sqrt(head_dim) */
+} msa_problem;
+
+/* Human-readable name of a status code (static storage). */
+const char *msa_status_str(int status);
+
+/* Detail of the last error returned on this thread ("" if none). */
+const char *msa_last_error(void);
+
+/* Capacities of the work lists for one query block (block = 64):
+ *   cap_blocks = min(slash_topk, seq_len / 64)   (blocks are disjoint and start
+ *                at or before the block's last row, so at most b+1 of them)
+ *   cap_cols   = min(vertical_topk, seq_len).                               */
+int msa_index_caps(const msa_problem *p, int32_t vertical_topk, int32_t slash_topk, int32_t block,
+                   int32_t *cap_blocks, int32_t *cap_cols);
+
+/* Workspace bytes msa_estimate_vs needs for these arguments. */
+size_t msa_estimate_vs_workspace(const msa_problem *p, int32_t last_q, int32_t vertical_topk,
+                                 int32_t slash_topk);
+
+/* Online vertical-slash index estimation.
+ * For every q head h (kv head g = h / G) and the last L = last_q query rows
+ * p_r = N - L + r (the pages: the index is approximated online per head,
+ * "MInference 1.0 README", "TL;DR"; talk slides "System-Algorithm
+ * Co-design", slide "MInference", online estimation of sparsity indices):
+ *     z[r, j]  = sm_scale * <q[h, p_r], k[g, j]>  for j <= p_r   (causal)
+ *     P[r, :]  = softmax over j
+ *     v[j]     = sum_r P[r, j]                  (vertical score)
+ *     s[o]     = sum_r P[r, p_r - o], o = i - j (slash score)
+ * then v_idx[h] = the vertical_topk largest v, s_idx[h] = the slash_topk
+ * largest s, exact ties going to the lower index, each written in ascending
+ * order.  last_q must be 64.  1 <= vertical_topk, slash_topk <= seq_len.
+ *   q [n_q_heads, N, 128], k [n_kv_heads, N, 128]      (dtype of p)
+ *   v_idx [n_q_heads, vertical_topk] int32, s_idx [n_q_heads, slash_topk] int32
+ *   v_score, s_score [n_q_heads, N] float32: optional outputs of the scores
+ *   (NULL: kept in the workspace).                                          */
+int msa_estimate_vs(const msa_problem *p, const void *q, const void *k, int32_t last_q,
+                    int32_t vertical_topk, int32_t slash_topk, int32_t *v_idx, int32_t *s_idx,
+                    float *v_score, float *s_score, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/* Work lists from index sets (block = 64).  For query block b (rows r0 = 64b to
+ * r1 = 64b+63), each selected offset o <= r1 needs keys [max(0, r0-o), r1-o];
+ * visiting those ranges by descending o, a range not yet covered emits a
+ * 64-wide block starting at max(range start, end of the previous block).
+ * Columns: every selected j <= r1 outside all emitted blocks, ascending.
+ * The pages ask for sparse work in large contiguous blocks suited to the matrix
+ * units, built online at small cost ("How to optimise the TTFT of an 8B LLM
+ * with 1M tokens to 20 seconds", section on co-designing algorithm and system,
+ * principles 1-2); the covering rule itself is this library's reading.
+ *   v_idx [n_q_heads, vertical_topk], s_idx [n_q_heads, slash_topk]: ascending,
+ *     distinct, in [0, N); out-of-range entries are ignored.
+ *   block_count, column_count [n_q_heads, N/64] int32
+ *   block_offset [n_q_heads, N/64, cap_blocks] int32 (key start of each block)
+ *   column_index [n_q_heads, N/64, cap_cols] int32
+ * Entries past each count are unspecified.                                  */
+int msa_build_index(const msa_problem *p, const int32_t *v_idx, int32_t vertical_topk,
+                    const int32_t *s_idx, int32_t slash_topk, int32_t block,
+                    int32_t *block_count, int32_t *block_offset, int32_t cap_blocks,
+                    int32_t *column_count, int32_t *column_index, int32_t cap_cols, void *stream);
+
+/* Sparse causal attention over the work lists (talk slides "System-Algorithm
+ * Co-design", slide "MInference": dynamic sparse attention calculation).  Row i
+ * of query block b attends to key j iff j <= i and j lies in one of b's blocks
+ * [st, st+63] or in b's column list:
+ *     out[h, i] = sum_j softmax_j(sm_scale <q_i, k_j>) v_j,
+ *     lse[h, i] = log sum_j exp(sm_scale <q_i, k_j>)   (natural log)
+ * A row with no allowed key gives out = 0 and lse = -inf.  Counts above the
+ * capacities are clamped; keys outside [0, N) are ignored.
+ *   out [n_q_heads, N, 128] (dtype of p); lse [n_q_heads, N] float32 or NULL. */
+int msa_sparse_prefill(const msa_problem *p, const void *q, const void *k, const void *v,
+                       const int32_t *block_count, const int32_t *block_offset, int32_t cap_blocks,
+                       const int32_t *column_count, const int32_t *column_index, int32_t cap_cols,
+                       void *out, float *lse, void *stream);
+
+/* Dense causal attention (every j <= i), same layouts as msa_sparse_prefill. */
+int msa_dense_prefill(const msa_problem *p, const void *q, const void *k, const void *v,
+                      void *out, float *lse, void *stream);
+
+/* Workspace bytes msa_estimate_bs needs. */
+size_t msa_estimate_bs_workspace(const msa_problem *p, int32_t block);
+
+/* Block-sparse work lists (talk slides "System-Algorithm Co-design", patterns
+ * slide: block-sparse heads; "MInference 1.0 README", kernel-only
+ * block_sparse_attention(q, k, v, topk)).  Reading: with qm[b] and km[c] the
+ * means of 64-row blocks of q and k, u[b, c] = sm_scale <qm[b], km[c]> for
+ * c <= b; query block b keeps its min(topk_blocks, b+1) highest-scoring key
+ * blocks (exact ties to the lower c), written as ascending key starts 64c.
+ * column_count is set to 0.  block must be 64; cap_blocks >= min(topk_blocks,
+ * N/64).                                                                    */
+int msa_estimate_bs(const msa_problem *p, const void *q, const void *k, int32_t block,
+                    int32_t topk_blocks, int32_t *block_count, int32_t *block_offset,
+                    int32_t cap_blocks, int32_t *column_count, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H */

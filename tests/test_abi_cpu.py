@@ -1,0 +1,115 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before touching the
+device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import dynamic_sparse_attention_vertical_amd as m
+from dynamic_sparse_attention_vertical_amd import msa as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+OK, NULL, SHAPE, DTYPE, RANGE, CAP, WS = 0, 1, 2, 3, 4, 5, 6
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return m.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) == 10, names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def P(hq=32, hkv=8, n=4096, d=128, dtype=0, scale=0.0):
+    return ctypes.byref(B.Problem(hq, hkv, n, d, dtype, scale))
+
+
+FAKE = ctypes.c_void_p(0x1000)       # never dereferenced: every case fails validation first
+
+
+def status_of(lib, fn, *args):
+    return getattr(lib, fn)(*args)
+
+
+def test_problem_validation(lib):
+    for prob, want in [(P(d=64), SHAPE), (P(hq=6, hkv=4), SHAPE), (P(n=100), SHAPE), (P(n=0), SHAPE),
+                       (P(n=1 << 31), SHAPE), (P(dtype=7), DTYPE), (P(scale=-1.0), RANGE),
+                       (P(hkv=0), SHAPE)]:
+        assert lib.msa_dense_prefill(prob, FAKE, FAKE, FAKE, FAKE, None, None) == want
+        assert lib.msa_last_error()
+    assert lib.msa_dense_prefill(None, FAKE, FAKE, FAKE, FAKE, None, None) == NULL
+    assert lib.msa_dense_prefill(P(), None, FAKE, FAKE, FAKE, None, None) == NULL
+    assert lib.msa_status_str(SHAPE) == b"MSA_ERR_SHAPE"
+
+
+def test_index_caps(lib):
+    cb, cc = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.msa_index_caps(P(n=1 << 20), 1000, 6096, 64, ctypes.byref(cb), ctypes.byref(cc)) == OK
+    assert (cb.value, cc.value) == (6096, 1000)
+    assert lib.msa_index_caps(P(n=4096), 64, 256, 64, ctypes.byref(cb), ctypes.byref(cc)) == OK
+    assert (cb.value, cc.value) == (64, 64)
+    assert lib.msa_index_caps(P(n=4096), 64, 256, 32, ctypes.byref(cb), ctypes.byref(cc)) == RANGE
+    assert lib.msa_index_caps(P(n=4096), 5000, 256, 64, ctypes.byref(cb), ctypes.byref(cc)) == RANGE
+
+
+def test_build_index_validation(lib):
+    args = lambda cb, cc, blk=64: (P(n=4096), FAKE, 64, FAKE, 256, blk, FAKE, FAKE, cb, FAKE, FAKE, cc, None)
+    assert lib.msa_build_index(*args(63, 64)) == CAP
+    assert lib.msa_build_index(*args(64, 63)) == CAP
+    assert lib.msa_build_index(*args(64, 64, blk=128)) == RANGE
+    a = list(args(64, 64))
+    a[6] = None
+    assert lib.msa_build_index(*a) == NULL
+
+
+def test_estimate_validation(lib):
+    prob = P(n=4096)
+    ws = lib.msa_estimate_vs_workspace(prob, 64, 64, 256)
+    assert ws > 0 and lib.msa_estimate_vs_workspace(prob, 32, 64, 256) == 0
+    call = lambda lq, kv, ks, wsb: lib.msa_estimate_vs(prob, FAKE, FAKE, lq, kv, ks, FAKE, FAKE, None, None,
+                                                       FAKE, wsb, None)
+    assert call(32, 64, 256, ws) == RANGE
+    assert call(64, 0, 256, ws) == RANGE
+    assert call(64, 64, 5000, ws) == RANGE
+    assert call(64, 64, 256, ws - 1) == WS
+
+
+def test_estimate_bs_validation(lib):
+    prob = P(n=4096)
+    ws = lib.msa_estimate_bs_workspace(prob, 64)
+    assert ws == 32 * 64 * 128 * 4 + 8 * 64 * 128 * 4
+    call = lambda blk, k, cap, wsb: lib.msa_estimate_bs(prob, FAKE, FAKE, blk, k, FAKE, FAKE, cap, FAKE, FAKE,
+                                                        wsb, None)
+    assert call(32, 10, 10, ws) == RANGE
+    assert call(64, 0, 10, ws) == RANGE
+    assert call(64, 10, 9, ws) == CAP
+    assert call(64, 10, 10, ws - 1) == WS
+
+
+def test_sparse_prefill_validation(lib):
+    call = lambda bc, cb: lib.msa_sparse_prefill(P(), FAKE, FAKE, FAKE, bc, FAKE, cb, FAKE, FAKE, 4, FAKE,
+                                                 None, None)
+    assert call(None, 4) == NULL
+    assert call(FAKE, -1) == CAP
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros((4, 256, 128), dtype=torch.bfloat16)
+    with pytest.raises(m.MsaError):
+        m.dense_prefill(q, q[:1], q[:1])
