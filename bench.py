@@ -1,0 +1,242 @@
+"""Benchmark: one vertical-slash sparse prefill layer on one MI355X.
+
+A step is one pass of the whole hot path over one layer's synthetic input
+already resident in HBM: online estimation (scores + top-k), index build, and
+the sparse prefill kernel.  Prints one JSON line:
+
+  value      = executed sparse-attention TFLOP per layer / layer time
+               (effective TFLOP/s; executed FLOP counts every issued 64x64
+               tile: 4 * 128 * 64 * 64 per block and per 64-column chunk)
+  roofline   = the sparse prefill kernel against the bf16 MFMA peak, timed
+               with HIP events on its own stream over the timed steps
+  cpu_baseline = the float64 CPU oracle on a bounded sample, extrapolated to
+               the layer
+
+usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse prefill ms/layer & eff. TFLOP/s (fraction of MFMA peak), 128K-1M tokens"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+TILE_FLOP = 4 * 128 * 64 * 64  # QK^T + PV for one 64x64 tile, head_dim 128
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def executed_tiles(idx):
+    import torch
+    bc = idx.block_count.to(torch.int64)
+    cc = idx.column_count.to(torch.int64)
+    return int(bc.sum().item() + ((cc + 63) // 64).sum().item())
+
+
+def useful_pairs(idx, n):
+    """Number of (i, j) pairs the mask allows (j <= i, j listed for i's block)."""
+    import torch
+    H, nqb, cap = idx.block_offset.shape
+    dev = idx.block_count.device
+    # a block starting a = st - r0 keys after the query block's first row covers
+    # sum_t clamp(t - a + 1, 0, 64) pairs over its 64 rows t
+    a = torch.arange(-63, 64, device=dev, dtype=torch.int64)
+    t = torch.arange(64, device=dev, dtype=torch.int64)
+    table = (t[None, :] - a[:, None] + 1).clamp(0, 64).sum(1)
+    r0 = torch.arange(nqb, device=dev, dtype=torch.int64) * 64
+    total = 0
+    for h in range(H):
+        st = idx.block_offset[h].to(torch.int64)
+        valid = torch.arange(cap, device=dev)[None, :] < idx.block_count[h][:, None]
+        off = (st - r0[:, None]).clamp(-63, 63) + 63
+        total += int((table[off] * valid).sum().item())
+        ci = idx.column_index[h].to(torch.int64)
+        cvalid = torch.arange(ci.shape[1], device=dev)[None, :] < idx.column_count[h][:, None]
+        rows = (r0[:, None] + 63 - ci + 1).clamp(min=0, max=64)
+        total += int((rows * cvalid).sum().item())
+    return total
+
+
+def cpu_baseline(x, plan, w, target_s=20.0):
+    """Time the float64 oracle on a bounded sample and extrapolate to the layer."""
+    import numpy as np
+    import oracle
+    n, hq, G = w.seq_len, w.n_q_heads, w.group
+    nqb = n // 64
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    q, k, v = x["q"].cpu(), x["k"].cpu(), x["v"].cpu()
+    v_idx, s_idx = plan.v_idx.cpu().numpy(), plan.s_idx.cpu().numpy()
+    # estimator for one head
+    t0 = time.perf_counter()
+    oracle.estimate_vs(q, k, last_q=64, heads=[0])
+    t_est = (time.perf_counter() - t0) * hq
+    # index build, all heads (plain C)
+    t0 = time.perf_counter()
+    ridx = oracle.build_index(v_idx, s_idx, n)
+    t_idx = time.perf_counter() - t0
+    # masked attention on sampled query blocks of head 0 until ~target_s
+    rng = np.random.default_rng(0)
+    order = [nqb - 1, 0, 1] + rng.permutation(np.arange(2, nqb - 1)).tolist()
+    done, keys_done, t_att = [], 0, 0.0
+    for b in order:
+        t0 = time.perf_counter()
+        oracle.masked_attention_blocks(q, k, v, ridx, [(0, b)])
+        t_att += time.perf_counter() - t0
+        done.append(b)
+        keys_done += 64 * b + 64
+        if t_est / hq + t_idx + t_att > target_s or len(done) >= 64:
+            break
+    keys_total = hq * sum(64 * b + 64 for b in range(nqb))
+    t_layer = t_est + t_idx + t_att * keys_total / keys_done
+    tiles = int(ridx.block_count.sum() + ((ridx.column_count + 63) // 64).sum())
+    return {
+        "value": round(tiles * TILE_FLOP / t_layer / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"float64 oracle: estimator on 1 of {hq} heads, index build on all heads, masked "
+                   f"attention on {len(done)} of {nqb} query blocks of head 0; layer time extrapolated "
+                   f"by heads and by keys scanned ({t_layer:.1f} s/layer, {t_est / hq:.2f} s estimator "
+                   f"per head, {t_idx:.2f} s index, {t_att:.2f} s attention measured)"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="llama3_8b_128k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the sparse prefill path has no multi-GPU mode "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dynamic_sparse_attention_vertical_amd as msa
+    from dynamic_sparse_attention_vertical_amd.layer import LayerPlan
+    from synth import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    if w.head_patterns:
+        raise SystemExit("bench.py times vertical-slash layers; use a vertical-slash workload")
+    n, hq, hkv = w.seq_len, w.n_q_heads, w.n_kv_heads
+    log(f"[bench] workload {w.name}: {hq}q/{hkv}kv heads, N={n}, k={w.vertical_topk}/{w.slash_topk}")
+    t0 = time.perf_counter()
+    x = make_inputs(w, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] inputs generated on the GPU in {time.perf_counter() - t0:.1f} s")
+    q, k, v = x["q"], x["k"], x["v"]
+    plan = LayerPlan(hq, hkv, n, w.vertical_topk, w.slash_topk, "cuda", q.dtype)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        msa.estimate_vs(q, k, w.vertical_topk, w.slash_topk, workspace=plan.workspace, v_idx=plan.v_idx,
+                        s_idx=plan.s_idx, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        msa.build_index(plan.v_idx, plan.s_idx, n, out=plan.index, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        msa.sparse_prefill(q, k, v, plan.index, out=out, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"[bench] warmup {i + 1}/{args.warmup} done")
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in events]
+    ms_est = sum(p[0] for p in per) / len(per)
+    ms_idx = sum(p[1] for p in per) / len(per)
+    ms_att = sum(p[2] for p in per) / len(per)
+    ms_step = wall * 1e3 / args.steps
+    log(f"[bench] timed {args.steps} steps: {ms_step:.2f} ms/layer (estimate {ms_est:.3f}, index {ms_idx:.3f}, "
+        f"sparse prefill {ms_att:.3f})")
+
+    tiles = executed_tiles(plan.index)
+    nqb = n // 64
+    causal_tiles = hq * nqb * (nqb + 1) // 2
+    exec_flop = tiles * TILE_FLOP
+    pairs = useful_pairs(plan.index, n)
+    causal_pairs = hq * n * (n + 1) // 2
+    att_tflops = exec_flop / (ms_att * 1e-3) / 1e12
+
+    breakdown = {
+        "ms_estimate": round(ms_est, 4), "ms_build_index": round(ms_idx, 4),
+        "ms_sparse_prefill": round(ms_att, 4),
+        "executed_tiles": tiles, "causal_tiles": causal_tiles,
+        "executed_density": round(tiles / causal_tiles, 5),
+        "useful_density": round(pairs / causal_pairs, 5),
+        "executed_tflop": round(exec_flop / 1e12, 4),
+        "sparse_prefill_tflops": round(att_tflops, 2),
+    }
+    if not args.no_dense:
+        dense_out = torch.empty_like(q)
+        msa.dense_prefill(q, k, v, out=dense_out, stream=stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        msa.dense_prefill(q, k, v, out=dense_out, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_dense = e0.elapsed_time(e1)
+        dense_flop = causal_tiles * TILE_FLOP
+        breakdown.update({"ms_dense_prefill": round(ms_dense, 3),
+                          "dense_prefill_tflops": round(dense_flop / (ms_dense * 1e-3) / 1e12, 2),
+                          "speedup_vs_dense": round(ms_dense / ms_step, 3)})
+        del dense_out
+        log(f"[bench] dense prefill {ms_dense:.2f} ms")
+
+    res = {
+        "metric": METRIC,
+        "value": round(exec_flop / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "seq_len": n, "q_heads": hq, "kv_heads": hkv, "head_dim": 128,
+                   "vertical_topk": w.vertical_topk, "slash_topk": w.slash_topk, "last_q": 64, "block": 64},
+        "breakdown": breakdown,
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel<bf16, sparse>",
+                     "achieved": round(att_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        res["cpu_baseline"] = cpu_baseline(x, plan, w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

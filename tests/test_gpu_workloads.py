@@ -1,0 +1,214 @@
+"""GPU parity at the five named workloads' full sizes, in the launch
+configuration bench.py times (LayerPlan buffers, one call per step on the
+current stream).  The oracle checks sampled heads and query blocks one by
+one; index counts are checked for every head."""
+
+import numpy as np
+import pytest
+import torch
+
+import dynamic_sparse_attention_vertical_amd as msa
+import oracle
+from dynamic_sparse_attention_vertical_amd.layer import LayerPlan, MixedPlan, mixed_layer
+from parity import (SCORE_RTOL, check_band, compare_index, compare_lse, compare_out,
+                    to_oracle_index)
+from synth import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def sample_blocks(nqb, k, seed):
+    r = np.random.default_rng(seed)
+    extra = r.choice(np.arange(2, nqb - 1), size=min(k, nqb - 3), replace=False).tolist()
+    return sorted(set([0, 1, nqb - 1] + extra))
+
+
+def check_vs_heads(x, w, plan, heads):
+    """Scores and index sets of sampled heads against the oracle."""
+    q, k = x["q"], x["k"]
+    n = w.seq_len
+    G = w.group
+    for h in heads:
+        g = h // G
+        vsc = torch.empty((G, n), dtype=torch.float32, device="cuda")
+        ssc = torch.empty((G, n), dtype=torch.float32, device="cuda")
+        vi, si = msa.estimate_vs(q[g * G:(g + 1) * G], k[g:g + 1], w.vertical_topk, w.slash_topk,
+                                 v_score=vsc, s_score=ssc)
+        hh = h - g * G
+        # the group-local call selects the same sets as the full-layer call
+        assert torch.equal(vi[hh], plan.v_idx[h]) and torch.equal(si[hh], plan.s_idx[h])
+        qc = q[h:h + 1, n - 64:].cpu()
+        qfull = torch.zeros((1, n, 128), dtype=q.dtype)
+        qfull[0, n - 64:] = qc[0]
+        rv, rs = oracle.estimate_vs(qfull, k[g:g + 1].cpu(), last_q=64)
+        for gs, r, name in ((vsc[hh], rv[0], "v"), (ssc[hh], rs[0], "s")):
+            gg = gs.cpu().numpy().astype(np.float64)
+            bad = np.abs(gg - r) > SCORE_RTOL * r + 1e-6
+            assert not bad.any(), f"head {h} {name}: {bad.sum()} scores off (max {np.abs(gg - r).max():.3e})"
+        check_band(plan.v_idx[h].cpu().numpy(), rv[0], w.vertical_topk, f"head {h} v_idx")
+        check_band(plan.s_idx[h].cpu().numpy(), rs[0], w.slash_topk, f"head {h} s_idx")
+        log(f"  head {h}: scores and sets within tolerance")
+
+
+def check_index_heads(plan_idx, v_idx, s_idx, n, heads, full_arrays=True):
+    vi = v_idx.cpu().numpy()
+    si = s_idx.cpu().numpy()
+    ridx = oracle.build_index(vi[heads], si[heads], n)
+    sub = msa.IndexTensors(plan_idx.block_count[heads], plan_idx.block_offset[heads],
+                           plan_idx.column_count[heads], plan_idx.column_index[heads])
+    compare_index(sub, ridx, "index")
+    return ridx
+
+
+def check_attention(x, out, lse, idx_rows, items, what):
+    q, k, v = x["q"].cpu(), x["k"].cpu(), x["v"].cpu()
+    ref = oracle.masked_attention_blocks(q, k, v, idx_rows[0], items, head_rows=idx_rows[1])
+    for (h, b), (o, l) in ref.items():
+        compare_out(out[h, 64 * b: 64 * b + 64].float().cpu().numpy(), o, False, f"{what} h{h} b{b}")
+        compare_lse(lse[h, 64 * b: 64 * b + 64].cpu().numpy(), l, f"{what} h{h} b{b}")
+    log(f"  {what}: {len(items)} sampled query blocks within tolerance")
+
+
+def check_dense(x, n, items):
+    q, k, v = x["q"], x["k"], x["v"]
+    out, lse = msa.dense_prefill(q, k, v, lse=True)
+    torch.cuda.synchronize()
+    ref = oracle.dense_attention_blocks(q.cpu(), k.cpu(), v.cpu(), items)
+    for (h, b), (o, l) in ref.items():
+        compare_out(out[h, 64 * b: 64 * b + 64].float().cpu().numpy(), o, False, f"dense h{h} b{b}")
+        compare_lse(lse[h, 64 * b: 64 * b + 64].cpu().numpy(), l, f"dense h{h} b{b}")
+    log(f"  dense: {len(items)} sampled query blocks within tolerance")
+
+
+def run_vs_workload(name, heads, n_blocks, dense=True):
+    w = WORKLOADS[name]
+    n, hq = w.seq_len, w.n_q_heads
+    log(f"[{name}] generating inputs")
+    x = make_inputs(w, device="cuda")
+    q, k, v = x["q"], x["k"], x["v"]
+    plan = LayerPlan(hq, w.n_kv_heads, n, w.vertical_topk, w.slash_topk, "cuda", q.dtype)
+    lse = torch.empty((hq, n), dtype=torch.float32, device="cuda")
+    out, plan = msa.vertical_slash_layer(q, k, v, w.vertical_topk, w.slash_topk, plan=plan, lse=lse)
+    out = out[0]
+    torch.cuda.synchronize()
+    log(f"[{name}] layer done")
+    check_vs_heads(x, w, plan, heads)
+    # counts: every head; arrays: sampled heads
+    bc = plan.index.block_count.cpu().numpy()
+    assert bc.min() >= 0 and bc.max() <= plan.index.cap_blocks
+    ridx = check_index_heads(plan.index, plan.v_idx, plan.s_idx, n, heads)
+    log(f"[{name}] index arrays of heads {heads} exact")
+    nqb = n // 64
+    blocks = sample_blocks(nqb, n_blocks, seed=n)
+    items = [(h, b) for h in heads for b in blocks]
+    check_attention(x, out, lse, (ridx, {h: i for i, h in enumerate(heads)}), items, "sparse")
+    if dense:
+        check_dense(x, n, [(heads[0], b) for b in blocks[:6]])
+    return plan
+
+
+def test_single_head_4k_full_parity():
+    """Whole-array parity at the single-head 4K workload, float32 and bfloat16."""
+    w = WORKLOADS["single_head_4k"]
+    n = w.seq_len
+    x = make_inputs(w)
+    for fp32 in (True, False):
+        sfx = "32" if fp32 else ""
+        q, k, v = x["q" + sfx], x["k" + sfx], x["v" + sfx]
+        qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+        vsc = torch.empty((1, n), dtype=torch.float32, device="cuda")
+        ssc = torch.empty((1, n), dtype=torch.float32, device="cuda")
+        vi, si = msa.estimate_vs(qd, kd, w.vertical_topk, w.slash_topk, v_score=vsc, s_score=ssc)
+        rv, rs = oracle.estimate_vs(q, k, last_q=64)
+        for gs, r in ((vsc, rv), (ssc, rs)):
+            gg = gs.cpu().numpy().astype(np.float64)
+            assert np.all(np.abs(gg - r) <= SCORE_RTOL * r + 1e-6)
+        check_band(vi[0].cpu().numpy(), rv[0], w.vertical_topk, "v")
+        check_band(si[0].cpu().numpy(), rs[0], w.slash_topk, "s")
+        idx = msa.build_index(vi, si, n)
+        ridx = oracle.build_index(vi.cpu().numpy(), si.cpu().numpy(), n)
+        compare_index(idx, ridx, "index")
+        out, lse = msa.sparse_prefill(qd, kd, vd, idx, lse=True)
+        ref, rlse = oracle.attention_with_mask(q, k, v, oracle.index_mask(ridx, n))
+        compare_out(out.float().cpu().numpy(), ref, fp32, "sparse")
+        compare_lse(lse.cpu().numpy(), rlse, "sparse")
+        dout, dlse = msa.dense_prefill(qd, kd, vd, lse=True)
+        dref, drlse = oracle.dense_attention(q, k, v)
+        compare_out(dout.float().cpu().numpy(), dref, fp32, "dense")
+        compare_lse(dlse.cpu().numpy(), drlse, "dense")
+        log(f"single_head_4k {'fp32' if fp32 else 'bf16'}: full parity")
+
+
+def test_llama3_8b_128k():
+    plan = run_vs_workload("llama3_8b_128k", heads=[0, 13, 31], n_blocks=10)
+    # whole index arrays of every head at this size
+    ridx = oracle.build_index(plan.v_idx.cpu().numpy(), plan.s_idx.cpu().numpy(), 131072)
+    compare_index(plan.index, ridx, "index (all heads)")
+
+
+def test_llama3_8b_512k():
+    run_vs_workload("llama3_8b_512k", heads=[0, 22], n_blocks=8)
+
+
+def test_llama3_8b_1m():
+    run_vs_workload("llama3_8b_1m", heads=[5, 31], n_blocks=6, dense=False)
+
+
+def test_mixed_256k():
+    w = WORKLOADS["mixed_256k"]
+    n, hq = w.seq_len, w.n_q_heads
+    x = make_inputs(w, device="cuda")
+    q, k, v = x["q"], x["k"], x["v"]
+    plan = MixedPlan(w.head_patterns, w.n_kv_heads, n, w.vertical_topk, w.slash_topk, w.sink, w.window,
+                     w.bs_topk, "cuda", q.dtype)
+    lse = torch.empty((hq, n), dtype=torch.float32, device="cuda")
+    out, lse = mixed_layer(q, k, v, plan, lse=lse)
+    torch.cuda.synchronize()
+    log("[mixed_256k] layer done")
+    nqb = n // 64
+    a_heads, vs_heads, bs_heads = w.heads_with("a"), w.heads_with("vs"), w.heads_with("bs")
+    # A-shape heads: static index, exact
+    av, as_ = oracle.a_shape_sets(n, w.sink, w.window)
+    ra = oracle.build_index(av[None], as_[None], n)
+    for h in (a_heads[0], a_heads[-1]):
+        compare_index(msa.IndexTensors(plan.index.block_count[h:h + 1], plan.index.block_offset[h:h + 1],
+                                       plan.index.column_count[h:h + 1], plan.index.column_index[h:h + 1]),
+                      ra, f"a-shape head {h}")
+    # vertical-slash heads: sets within the band, arrays exact
+    vs_rows = {h: i for i, h in enumerate(vs_heads)}
+    sample_vs = [vs_heads[0], vs_heads[-1]]
+    for h in sample_vs:
+        r = vs_rows[h]
+        qfull = torch.zeros((1, n, 128), dtype=q.dtype)
+        qfull[0, n - 64:] = q[h, n - 64:].cpu()
+        rv, rs = oracle.estimate_vs(qfull, k[h // w.group: h // w.group + 1].cpu(), last_q=64)
+        check_band(plan.v_idx[r].cpu().numpy(), rv[0], w.vertical_topk, f"vs head {h} v")
+        check_band(plan.s_idx[r].cpu().numpy(), rs[0], w.slash_topk, f"vs head {h} s")
+        ridx = oracle.build_index(plan.v_idx[r:r + 1].cpu().numpy(), plan.s_idx[r:r + 1].cpu().numpy(), n)
+        compare_index(msa.IndexTensors(plan.index.block_count[h:h + 1], plan.index.block_offset[h:h + 1],
+                                       plan.index.column_count[h:h + 1], plan.index.column_index[h:h + 1]),
+                      ridx, f"vs head {h}")
+    # block-sparse heads: chosen blocks within the band of the row softmax of the block scores
+    for h in (bs_heads[0], bs_heads[-1]):
+        u = oracle.block_scores(q.cpu(), k.cpu(), h)
+        bc = plan.index.block_count[h].cpu().numpy()
+        bo = plan.index.block_offset[h].cpu().numpy()
+        assert np.all(plan.index.column_count[h].cpu().numpy() == 0)
+        for b in sample_blocks(nqb, 40, seed=h):
+            kk = min(w.bs_topk, b + 1)
+            assert bc[b] == kk
+            row = u[b, : b + 1]
+            pr = np.exp(row - row.max())
+            check_band(bo[b, :kk] // 64, pr / pr.sum(), kk, f"bs head {h} block {b}")
+    log("[mixed_256k] index checks passed")
+    # attention on sampled blocks of every pattern, with the GPU's (validated) index
+    heads = [a_heads[0], sample_vs[0], bs_heads[-1]]
+    gi = to_oracle_index(msa.IndexTensors(plan.index.block_count[heads], plan.index.block_offset[heads],
+                                          plan.index.column_count[heads], plan.index.column_index[heads]))
+    blocks = sample_blocks(nqb, 5, seed=7)
+    items = [(h, b) for h in heads for b in blocks]
+    check_attention(x, out, lse, (gi, {h: i for i, h in enumerate(heads)}), items, "mixed")
