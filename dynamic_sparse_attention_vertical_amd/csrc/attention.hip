@@ -165,7 +165,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
-    float m_i = -INFINITY, l_i = 0.f;
+    // running row max kept in scaled log2 units as a stored fp32 value, so an
+    // unchanged max gives a rescale factor of exactly 1
+    float mb_i = -INFINITY, l_i = 0.f;
 
     for (int it = 0; it < nblk + nchunk; ++it) {
         const bool is_col = it >= nblk;
@@ -223,27 +225,27 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
                     }
         }
 
-        // online softmax (raw-score max; exp2 with the folded scale)
+        // online softmax: p = 2^(s*c - mb), c = scale*log2(e)
         float mx = -INFINITY;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
         mx = fmaxf(mx, wave_shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_i, mx);
-        const float mb = (m_new == -INFINITY) ? 0.f : m_new * a.scale_log2;
-        const float alpha = exp2f(m_i * a.scale_log2 - mb);
+        const float mb_new = fmaxf(mb_i, mx * a.scale_log2);
+        const float ref = (mb_new == -INFINITY) ? 0.f : mb_new;
+        const float alpha = exp2f(mb_i - ref);
         float rs = 0.f;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float p = exp2f(s[kt][i] * a.scale_log2 - mb);
+                const float p = exp2f(fmaf(s[kt][i], a.scale_log2, -ref));
                 s[kt][i] = p;
                 rs += p;
             }
         l_i = l_i * alpha + rs;
-        m_i = m_new;
+        mb_i = mb_new;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -284,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
                            o[dt][jj * 4 + 2] * inv, o[dt][jj * 4 + 3] * inv);
         }
     if (a.lse != nullptr && hl == 0)
-        a.lse[(int64_t)h * n + qrow] = l_tot > 0.f ? (m_i * a.scale + logf(l_tot)) : -INFINITY;
+        a.lse[(int64_t)h * n + qrow] = l_tot > 0.f ? (mb_i * kLn2 + logf(l_tot)) : -INFINITY;
 }
 
 template <typename T, bool kDense> hipError_t launch(const AttnArgs &a, hipStream_t s) {

@@ -14,7 +14,8 @@
 // serving q head g*G + w (+4, ...).  The K tile (64 keys) is staged in LDS
 // once and shared by the G q heads of the group.  Scores are computed with
 // MFMA as S^T = K Q^T (lane = one query row, 16 keys per 32-key sub-tile).
-//   pass 1: per-row running max and sum of exp over the range -> partials
+//   pass 1: per-row running max (kept as scale*log2(e)*z) and sum of exp2
+//           over the range -> partials
 //   combine: partials -> row max m_r and 1 / sum
 //   pass 2: recompute S, p = exp(z - m_r) / l_r, written to a per-wave LDS
 //           tile; column sums give v directly, diagonal sums are read along
@@ -123,13 +124,15 @@ __global__ __launch_bounds__(kThreads) void est_pass1_kernel(EstArgs a) {
                 for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
-                const float mn = fmaxf(m[half], mx);
-                const float mb = (mn == -INFINITY) ? 0.f : mn * a.scale_log2;
-                float acc = l[half] * __builtin_amdgcn_exp2f(m[half] * a.scale_log2 - mb);
+                // running max in scaled log2 units (stored value: an unchanged
+                // max rescales by exactly 1)
+                const float mn = fmaxf(m[half], mx * a.scale_log2);
+                const float ref = (mn == -INFINITY) ? 0.f : mn;
+                float acc = l[half] * exp2f(m[half] - ref);
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) acc += __builtin_amdgcn_exp2f(s[kt][i] * a.scale_log2 - mb);
+                    for (int i = 0; i < 16; ++i) acc += exp2f(fmaf(s[kt][i], a.scale_log2, -ref));
                 m[half] = mn;
                 l[half] = acc;
             }
@@ -139,9 +142,8 @@ __global__ __launch_bounds__(kThreads) void est_pass1_kernel(EstArgs a) {
             for (int half = 0; half < 2; ++half) {
                 const float mo = wave_shfl_xor(m[half], 32), lo = wave_shfl_xor(l[half], 32);
                 const float mn = fmaxf(m[half], mo);
-                const float mb = (mn == -INFINITY) ? 0.f : mn * a.scale_log2;
-                const float lt = l[half] * __builtin_amdgcn_exp2f(m[half] * a.scale_log2 - mb) +
-                                 lo * __builtin_amdgcn_exp2f(mo * a.scale_log2 - mb);
+                const float ref = (mn == -INFINITY) ? 0.f : mn;
+                const float lt = l[half] * exp2f(m[half] - ref) + lo * exp2f(mo - ref);
                 if (hl == 0) {
                     const int64_t o = ((int64_t)h * kL + half * 32 + l32) * a.nranges + range;
                     a.part_m[o] = mn;
@@ -163,16 +165,16 @@ __global__ __launch_bounds__(256) void est_combine_kernel(EstArgs a) {
     for (int i = lane; i < a.nranges; i += 64) {
         const float mi = pm[i], li = pl[i];
         const float mn = fmaxf(m, mi);
-        const float mb = (mn == -INFINITY) ? 0.f : mn * a.scale_log2;
-        l = l * __builtin_amdgcn_exp2f(m * a.scale_log2 - mb) + li * __builtin_amdgcn_exp2f(mi * a.scale_log2 - mb);
+        const float base = (mn == -INFINITY) ? 0.f : mn;
+        l = l * exp2f(m - base) + li * exp2f(mi - base);
         m = mn;
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
         const float mo = wave_shfl_xor(m, off), lo = wave_shfl_xor(l, off);
         const float mn = fmaxf(m, mo);
-        const float mb = (mn == -INFINITY) ? 0.f : mn * a.scale_log2;
-        l = l * __builtin_amdgcn_exp2f(m * a.scale_log2 - mb) + lo * __builtin_amdgcn_exp2f(mo * a.scale_log2 - mb);
+        const float base = (mn == -INFINITY) ? 0.f : mn;
+        l = l * exp2f(m - base) + lo * exp2f(mo - base);
         m = mn;
     }
     if (lane == 0) {
@@ -209,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void est_pass2_kernel(EstArgs a) {
                 qf[half][dk] = active ? E::load_frag(qp + (half * 32 + l32) * kD + dk * 16 + hl * 8)
                                       : E::zero_frag();
             const int64_t ri = (int64_t)h * kL + half * 32 + l32;
-            mrow[half] = active ? a.row_m[ri] * a.scale_log2 : 0.f;
+            mrow[half] = active ? a.row_m[ri] : 0.f;          // scaled log2 units
             il[half] = active ? a.row_il[ri] : 0.f;
         }
         float *vout = a.v_score + (int64_t)h * n;
@@ -233,7 +235,7 @@ __global__ __launch_bounds__(kThreads) void est_pass2_kernel(EstArgs a) {
 #pragma unroll
                         for (int i = 0; i < 16; ++i) {
                             const int e = kt * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
-                            float p = __builtin_amdgcn_exp2f(s[kt][i] * a.scale_log2 - mrow[half]) * il[half];
+                            float p = exp2f(fmaf(s[kt][i], a.scale_log2, -mrow[half])) * il[half];
                             if (last && base + e > prow) p = 0.f;
                             pw[l32 * kPP + e] = p;
                         }

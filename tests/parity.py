@@ -74,13 +74,15 @@ def compare_index(gpu_idx, ref_idx, what: str = ""):
     cc = gpu_idx.column_count.cpu().numpy()
     assert np.array_equal(bc, ref_idx.block_count), f"{what}: block counts differ"
     assert np.array_equal(cc, ref_idx.column_count), f"{what}: column counts differ"
-    bo = gpu_idx.block_offset.cpu().numpy()
-    ci = gpu_idx.column_index.cpu().numpy()
-    H, nqb = bc.shape
-    mb = np.arange(bo.shape[2])[None, None, :] < bc[:, :, None]
-    mc = np.arange(ci.shape[2])[None, None, :] < cc[:, :, None]
-    assert np.array_equal(bo[mb], ref_idx.block_offset[:, :, :bo.shape[2]][mb]), f"{what}: block offsets differ"
-    assert np.array_equal(ci[mc], ref_idx.column_index[:, :, :ci.shape[2]][mc]), f"{what}: columns differ"
+    # the two sides may use different capacities; counts fit in both
+    wb = int(bc.max()) if bc.size else 0
+    wc = int(cc.max()) if cc.size else 0
+    bo = gpu_idx.block_offset[:, :, :wb].cpu().numpy()
+    ci = gpu_idx.column_index[:, :, :wc].cpu().numpy()
+    mb = np.arange(wb)[None, None, :] < bc[:, :, None]
+    mc = np.arange(wc)[None, None, :] < cc[:, :, None]
+    assert np.array_equal(bo[mb], ref_idx.block_offset[:, :, :wb][mb]), f"{what}: block offsets differ"
+    assert np.array_equal(ci[mc], ref_idx.column_index[:, :, :wc][mc]), f"{what}: columns differ"
 
 
 def to_oracle_index(gpu_idx):
