@@ -5,18 +5,17 @@
 // kernel, first the item's 64-wide key blocks (arbitrary start), then its
 // leftover vertical columns gathered 64 at a time; for the dense kernel, the
 // aligned tiles 0..b.  Per tile:
-//   S^T = K Q^T        (MFMA 32x32x16 bf16; K tile from LDS, Q in registers)
+//   S^T = K Q^T        (MFMA 32x32x16; K tile from LDS, Q in registers)
 //   online softmax in fp32 (exp2 with the log2(e)-folded scale)
-//   O^T += V^T P^T     (P stays in registers as the B operand; V^T from LDS)
+//   O^T += V^T P^T     (P stays in registers as the B operand; V^T read from
+//                       the row-major V tile with the LDS transpose read)
 // Computing S transposed leaves each lane holding one query's scores for 16
 // keys, so a row max needs only one cross-lane exchange (lane l with l^32), and
-// those scores already sit in the B-operand layout of the PV product up to a
-// fixed key permutation, which the V^T tile is written in.
+// those scores are already the B operand of the PV product.
 //
-// Tiles are double-buffered in LDS.  bf16: while a tile is being computed,
-// the next tile's K and V rows are already in flight from HBM into registers;
-// after the compute they are written (V transposed) to the other stage.  fp32
-// (a checking path) loads after the compute.  One barrier per tile.
+// K and V rows move from HBM straight into LDS (global_load_lds, 16 bytes per
+// lane, no registers), 16-byte chunks XOR-swizzled per row so that the MFMA
+// operand reads are free of bank conflicts.
 //
 // The pages: causal attention computed only over the selected entries, in
 // FlashAttention style (talk slides "System-Algorithm Co-design", slide
@@ -35,24 +34,25 @@ constexpr int kBQ = 64;          // query rows per work item
 constexpr int kBK = 64;          // keys per tile
 constexpr int kThreads = 128;    // two waves
 
-template <typename T> struct AttnStage {
-    static constexpr int kEpv = 16 / Elem<T>::kBytes;        // elements per 16-byte vector
-    static constexpr int kKPitch = kD + kEpv;                 // K row pitch (+16 B: conflict-free reads)
-    T k[kBK * kKPitch];
-    T vt[kD * kBK];                                           // V^T, chunk-swizzled rows
-    int32_t kidx[kBK];                                        // key of each tile row (-1: none)
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
+
+template <typename T> struct Geo {
+    static constexpr int kRowBytes = kD * (int)sizeof(T);      // 256 (bf16) / 512 (fp32)
+    static constexpr int kChunks = kRowBytes / 16;             // 16-byte chunks per row
+    static constexpr int kTileBytes = kBK * kRowBytes;         // 16 KB / 32 KB
+    static constexpr int kSlots = kTileBytes / 1024;           // 1 KB direct-load slots per tile
+    static constexpr int kRowsPerSlot = 1024 / kRowBytes;
+    // chunk swizzles (bf16 only; the fp32 checking path keeps plain rows)
+    __device__ static __forceinline__ int k_swz(int row) { return sizeof(T) == 2 ? (row & 7) : 0; }
+    __device__ static __forceinline__ int v_swz(int row) { return sizeof(T) == 2 ? 2 * (row & 3) : 0; }
 };
 
-// Position of tile key e in the V^T row: inside each group of 16 keys the two
-// middle quads are swapped, matching where the S^T accumulator keeps them.
-__device__ __forceinline__ int vt_pos(int e) {
-    int q = (e >> 2) & 3;
-    int qn = (q == 1) ? 2 : (q == 2 ? 1 : q);
-    return (e & ~15) | (qn << 2) | (e & 3);
-}
-
-// 8-element chunk swizzle of V^T row d (conflict-free reads and writes).
-__device__ __forceinline__ int vt_swz(int d) { return (d & 7) ^ ((d >> 3) & 7); }
+template <typename T> struct AttnStage {
+    alignas(16) unsigned char k[Geo<T>::kTileBytes];
+    alignas(16) unsigned char v[Geo<T>::kTileBytes];
+    int32_t kidx[kBK];                                        // key of each tile row (-1: none)
+};
 
 __device__ __forceinline__ int64_t item_of_block(int64_t bid, int64_t total) {
     // Consecutive workgroup ids land on different XCDs; give each XCD a
@@ -68,6 +68,8 @@ __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
     f32x2_t v = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <typename T> struct Out;
 template <> struct Out<bf16> {
@@ -102,102 +104,106 @@ struct TileSrc {
     int c0;
 };
 
-// Global -> registers -> LDS staging of one K/V tile.  Thread t moves K rows
-// (t>>4) + 8i (16-byte column t&15) and V key quads (t>>4) + 8j (d-octet t&15).
-template <typename T> struct Loader {
-    static constexpr int kEpv = AttnStage<T>::kEpv;
-    static constexpr int kVpr = kD / kEpv;                        // 16-byte vectors per row
-    static constexpr int kKVec = kBK * kVpr / kThreads;            // K vectors per thread
-    static constexpr int kVVec = 8 * Elem<T>::kBytes / 16;         // 16-byte vectors per V row piece
-    u32x4 kr[kKVec];
-    u32x4 vr[2][4][kVVec];
-    int32_t key_lo;                                                // key of tile row tid (tid < 64)
-
-    __device__ __forceinline__ static int64_t key_of(const TileSrc &s, int row, const int32_t *clist,
-                                                     int ncol) {
-        if (!s.is_col) return s.base + row;
-        const int c = s.c0 + row;
-        return c < ncol ? (int64_t)clist[c] : -1;
+// Start the HBM -> LDS copy of one tile's K and V rows.  Wave w moves the 1 KB
+// slots w*S/2 .. w*S/2 + S/2 - 1 of each tile; in a slot, lane l writes the
+// 16-byte physical chunk l % kChunks of row slot*kRowsPerSlot + l / kChunks,
+// and so loads the logical chunk that the swizzle puts there.  A row whose key
+// does not exist (past the end of the sequence, or column padding) reads a
+// clamped existing row: the softmax mask gives it weight zero and its values
+// are finite, so no zero fill is needed.
+template <typename T>
+__device__ __forceinline__ void load_tile(AttnStage<T> &st, const T *kp, const T *vp, const TileSrc &src,
+                                          int64_t n, const int32_t *clist, int ncol, int tid) {
+    using Gm = Geo<T>;
+    const int wave = tid >> 6, lane = tid & 63;
+    constexpr int kHalf = Gm::kSlots / 2;
+    const int sub = lane / Gm::kChunks, phys = lane % Gm::kChunks;
+    const char *kb = reinterpret_cast<const char *>(kp);
+    const char *vb = reinterpret_cast<const char *>(vp);
+#pragma unroll
+    for (int i = 0; i < kHalf; ++i) {
+        const int slot = wave * kHalf + i;
+        const int row = slot * Gm::kRowsPerSlot + sub;
+        int64_t key;
+        if (src.is_col) {
+            const int c = min(src.c0 + row, ncol - 1);
+            key = clist[c];
+        } else {
+            key = src.base + row;
+        }
+        key = min(max(key, (int64_t)0), n - 1);
+        const int64_t rb = key * Gm::kRowBytes;
+        __builtin_amdgcn_global_load_lds(kb + rb + ((phys ^ Gm::k_swz(row)) << 4),
+                                         (LDS_AS void *)(LDS_AS unsigned char *)(st.k + slot * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vb + rb + ((phys ^ Gm::v_swz(row)) << 4),
+                                         (LDS_AS void *)(LDS_AS unsigned char *)(st.v + slot * 1024), 16, 0, 0);
     }
-
-    __device__ __forceinline__ void issue(const TileSrc &s, const T *kp, const T *vp, int64_t n,
-                                          const int32_t *clist, int ncol, int tid) {
-        const int col = tid & 15;
-#pragma unroll
-        for (int i = 0; i < kKVec; ++i) {
-            const int v = tid + kThreads * i;
-            const int row = v / kVpr, cv = v % kVpr;
-            const int64_t key = key_of(s, row, clist, ncol);
-            u32x4 z = {0u, 0u, 0u, 0u};
-            kr[i] = (key >= 0 && key < n) ? *reinterpret_cast<const u32x4 *>(kp + key * kD + cv * kEpv) : z;
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int kq = (tid >> 4) + 8 * j;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t key = key_of(s, kq * 4 + r, clist, ncol);
-                const bool ok = key >= 0 && key < n;
-#pragma unroll
-                for (int c = 0; c < kVVec; ++c) {
-                    u32x4 z = {0u, 0u, 0u, 0u};
-                    vr[j][r][c] = ok ? *reinterpret_cast<const u32x4 *>(vp + key * kD + col * 8 + c * kEpv) : z;
-                }
-            }
-        }
-        if (tid < kBK) key_lo = (int32_t)key_of(s, tid, clist, ncol);
+    if (src.is_col && tid < kBK) {
+        const int c = src.c0 + tid;
+        st.kidx[tid] = c < ncol ? clist[c] : -1;
     }
+}
 
-    __device__ __forceinline__ void commit(AttnStage<T> &st, int tid) {
-        const int col = tid & 15;
-#pragma unroll
-        for (int i = 0; i < kKVec; ++i) {
-            const int v = tid + kThreads * i;
-            const int row = v / kVpr, cv = v % kVpr;
-            *reinterpret_cast<u32x4 *>(&st.k[row * AttnStage<T>::kKPitch + cv * kEpv]) = kr[i];
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int kq = (tid >> 4) + 8 * j;
-            const int p = vt_pos(kq * 4);                             // multiple of 4
-            const int chunk = p >> 3, within = p & 7;
-#pragma unroll
-            for (int dd = 0; dd < 8; ++dd) {
-                const int d = col * 8 + dd;
-                T *dst = &st.vt[d * kBK + ((chunk ^ vt_swz(d)) << 3) + within];
-                if constexpr (sizeof(T) == 2) {
-                    // element dd of each of the 4 rows: 16-bit half (dd&1) of word dd>>1
-                    const int w = dd >> 1;
-                    const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
-                    u32x2 out;
-                    out[0] = __builtin_amdgcn_perm(vr[j][1][0][w], vr[j][0][0][w], sel);
-                    out[1] = __builtin_amdgcn_perm(vr[j][3][0][w], vr[j][2][0][w], sel);
-                    *reinterpret_cast<u32x2 *>(dst) = out;
-                } else {
-                    const int c = dd >> 2, w = dd & 3;
-                    u32x4 out;
-                    out[0] = vr[j][0][c][w];
-                    out[1] = vr[j][1][c][w];
-                    out[2] = vr[j][2][c][w];
-                    out[3] = vr[j][3][c][w];
-                    *reinterpret_cast<u32x4 *>(dst) = out;
-                }
-            }
-        }
-        if (tid < kBK) st.kidx[tid] = key_lo;
+// K fragment (A operand of S^T = K Q^T): row kt*32 + l32, d = dk*16 + hl*8 .. +7
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::frag k_frag(const AttnStage<T> &st, int kt, int dk, int l32, int hl) {
+    using Gm = Geo<T>;
+    const int row = kt * 32 + l32;
+    if constexpr (sizeof(T) == 2) {
+        const int c = dk * 2 + hl;
+        return Elem<T>::load_frag(st.k + row * Gm::kRowBytes + ((c ^ Gm::k_swz(row)) << 4));
+    } else {
+        return Elem<T>::load_frag(st.k + row * Gm::kRowBytes + (dk * 16 + hl * 8) * 4);
     }
-};
+}
 
-template <typename T, bool kDense>
-__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
+// V^T fragment (A operand of O^T = V^T P^T) for d-tile dt and key step kk:
+// lane l needs V[key][d = dt*32 + l%32] for keys kk*16 + (e/4)*8 + hl*4 + e%4,
+// e = 0..7 -- the order the S^T accumulator holds P in.
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::frag v_frag(const AttnStage<T> &st, int dt, int kk, int lane) {
+    using Gm = Geo<T>;
+    const int hl = lane >> 5;
+    if constexpr (sizeof(T) == 2) {
+        // LDS transpose read: in each 16-lane group, source lane 4i+q reads 4
+        // consecutive d (d0 + 4q ..) of key row kb+i; output lane j then holds
+        // keys kb..kb+3 of d = d0 + j.
+        const int g = lane >> 4, j = lane & 15, i = j >> 2, q = j & 3;
+        const int d = dt * 32 + (g & 1) * 16 + 4 * q;
+        u32x4 r;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int row = kk * 16 + half * 8 + hl * 4 + i;
+            const int c = d >> 3;
+            const int off = row * Gm::kRowBytes + ((c ^ Gm::v_swz(row)) << 4) + ((d >> 2) & 1) * 8;
+            const v4i16 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (LDS_AS v4i16 *)(LDS_AS unsigned char *)(st.v + off));
+            const u32x2 w = __builtin_bit_cast(u32x2, x);
+            r[2 * half] = w[0];
+            r[2 * half + 1] = w[1];
+        }
+        return __builtin_bit_cast(bf16x8, r);
+    } else {
+        const int d = dt * 32 + (lane & 31);
+        f32x8 r;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int row = kk * 16 + (e >> 2) * 8 + hl * 4 + (e & 3);
+            r[e] = *reinterpret_cast<const float *>(st.v + row * Gm::kRowBytes + d * 4);
+        }
+        return r;
+    }
+}
+
+// bf16: one 33 KB LDS stage and two waves per SIMD (four workgroups per CU hide
+// each other's load latency; measured faster than two stages at one wave per
+// SIMD).  fp32 (a checking path): two stages, one wave per SIMD.
+template <typename T, bool kDense, int kStages>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1, sizeof(T) == 2 ? 2 : 1)))
+void attn_fwd_kernel(AttnArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)   // the body uses gfx950-only LDS builtins
     using E = Elem<T>;
     using frag = typename E::frag;
-    constexpr int kKPitch = AttnStage<T>::kKPitch;
-    constexpr bool kPipe = sizeof(T) == 2;    // prefetch the next tile into registers during compute
-    // Two LDS stages (68 KB for bf16: two workgroups, one wave per SIMD).  A
-    // single 34 KB stage would allow two waves per SIMD, but then the register
-    // prefetch no longer fits in 256 registers and spills; measured slower.
-    constexpr int kStages = 2;
     __shared__ AttnStage<T> stage[kStages];
 
     const int tid = threadIdx.x;
@@ -255,18 +261,22 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
     // unchanged max gives a rescale factor of exactly 1
     float mb_i = -INFINITY, l_i = 0.f;
 
-    Loader<T> ld;
-    if (ntile > 0) {
-        ld.issue(src_of(0), kp, vp, n, clist, ncol, tid);
-        ld.commit(stage[0], tid);
+    if (kStages == 2 && ntile > 0) {
+        load_tile<T>(stage[0], kp, vp, src_of(0), n, clist, ncol, tid);
+        wait_vmem();
+        __syncthreads();
     }
-    __syncthreads();
 
     for (int it = 0; it < ntile; ++it) {
         const TileSrc cur = src_of(it);
-        const bool more = it + 1 < ntile;
-        if (kPipe && more) ld.issue(src_of(it + 1), kp, vp, n, clist, ncol, tid);
-        const AttnStage<T> &st = stage[it % kStages];
+        if (kStages == 1) {
+            load_tile<T>(stage[0], kp, vp, cur, n, clist, ncol, tid);
+            wait_vmem();
+            __syncthreads();
+        } else if (it + 1 < ntile) {
+            load_tile<T>(stage[(it + 1) & 1], kp, vp, src_of(it + 1), n, clist, ncol, tid);
+        }
+        const AttnStage<T> &st = stage[kStages == 1 ? 0 : (it & 1)];
 
         // S^T for this wave's 32 queries: two 32-key sub-tiles
         f32x16 s[2];
@@ -275,15 +285,26 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
 #pragma unroll
-            for (int dk = 0; dk < 8; ++dk) {
-                frag kf = E::load_frag(&st.k[(kt * 32 + l32) * kKPitch + dk * 16 + hl * 8]);
-                E::mma(s[kt], kf, qf[dk]);
-            }
+            for (int dk = 0; dk < 8; ++dk) E::mma(s[kt], k_frag<T>(st, kt, dk, l32, hl), qf[dk]);
         }
 
-        // mask: the key must exist and satisfy j <= i
-        const bool need_mask = cur.is_col || (cur.base + kBK - 1 > r0) || cur.base < 0;
-        if (need_mask) {
+        // mask: the key must exist and satisfy j <= i (keys past the end of the
+        // sequence are > i, column padding is -1)
+        if (cur.is_col) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int4 kk = *reinterpret_cast<const int4 *>(&st.kidx[kt * 32 + jj * 8 + hl * 4]);
+                    const int kx[4] = {kk.x, kk.y, kk.z, kk.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (!(kx[i] >= 0 && (int64_t)kx[i] <= qrow)) s[kt][jj * 4 + i] = -INFINITY;
+                }
+        } else if (cur.base + kBK - 1 > r0 || cur.base < 0) {
+            // e allowed iff 0 <= base + e <= qrow
+            const int hi = (int)min(max(qrow - cur.base, (int64_t)-1), (int64_t)kBK);
+            const int lo = (int)min(max(-cur.base, (int64_t)0), (int64_t)kBK);
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -291,8 +312,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int e = kt * 32 + jj * 8 + hl * 4 + i;
-                        const int64_t key = cur.is_col ? (int64_t)st.kidx[e] : cur.base + e;
-                        if (!(key >= 0 && key <= qrow)) s[kt][jj * 4 + i] = -INFINITY;
+                        if (e > hi || e < lo) s[kt][jj * 4 + i] = -INFINITY;
                     }
         }
 
@@ -337,20 +357,11 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
         }
         // O^T += V^T P^T
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-            const int d = dt * 32 + l32;
-            const int sw = vt_swz(d);
+        for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                frag vf = E::load_frag(&st.vt[d * kBK + (((kk * 2 + hl) ^ sw) << 3)]);
-                E::mma(o[dt], vf, pf[kk]);
-            }
-        }
+            for (int kk = 0; kk < 4; ++kk) E::mma(o[dt], v_frag<T>(st, dt, kk, lane), pf[kk]);
 
-        if (more) {
-            if (!kPipe) ld.issue(src_of(it + 1), kp, vp, n, clist, ncol, tid);
-            ld.commit(stage[(it + 1) % kStages], tid);
-        }
+        if (kStages == 2) wait_vmem();              // the next tile has landed
         __syncthreads();
     }
 
@@ -368,12 +379,14 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
         }
     if (a.lse != nullptr && hl == 0)
         a.lse[(int64_t)h * n + qrow] = l_tot > 0.f ? (mb_i * kLn2 + logf(l_tot)) : -INFINITY;
+#endif
 }
 
 template <typename T, bool kDense> hipError_t launch(const AttnArgs &a, hipStream_t s) {
     const int64_t total = (int64_t)a.hq * (a.n / kBQ);
     if (total == 0) return hipSuccess;
-    hipLaunchKernelGGL((attn_fwd_kernel<T, kDense>), dim3((unsigned)total), dim3(kThreads), 0, s, a);
+    constexpr int kStages = sizeof(T) == 2 ? 1 : 2;
+    hipLaunchKernelGGL((attn_fwd_kernel<T, kDense, kStages>), dim3((unsigned)total), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
