@@ -32,8 +32,44 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 TILE_FLOP = 4 * 128 * 64 * 64  # QK^T + PV for one 64x64 tile, head_dim 128
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_sparse_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "dynamic_sparse_attention_vertical_amd", "csrc", "attention.hip")
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def attn_src_sha():
+    import hashlib
+    return hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per sparse-prefill launch from the committed rocprofv3 counter
+    runs (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter's reading
+    for a plain copy of known size), or None if absent or taken on a different
+    kernel source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    entry = rec.get("workloads", {}).get(workload)
+    if not entry or rec.get("attention_src_sha") != attn_src_sha():
+        return None
+    return entry["fetch_kib"] * 1024 * rec["fetch_calib"] + entry["write_kib"] * 1024 * rec["write_calib"]
+
+
+def copy_calibration(gib):
+    """A plain device copy of a known size, for calibrating HBM byte counters."""
+    import torch
+    n = int(gib * (1 << 30)) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4}), flush=True)
 
 
 def executed_tiles(idx):
@@ -120,7 +156,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--copy-calib", type=float, default=0.0,
+                    help="only run a plain copy of this many GiB (counter calibration) and exit")
     args = ap.parse_args()
+    if args.copy_calib > 0:
+        copy_calibration(args.copy_calib)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the sparse prefill path has no multi-GPU mode "
               f"(--gpus {args.gpus} requested)", file=sys.stderr)
@@ -230,7 +271,8 @@ def main():
         "breakdown": breakdown,
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel<bf16, sparse>",
                      "achieved": round(att_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(w.name)},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")

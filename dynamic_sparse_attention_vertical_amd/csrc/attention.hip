@@ -43,9 +43,14 @@ template <typename T> struct Geo {
     static constexpr int kTileBytes = kBK * kRowBytes;         // 16 KB / 32 KB
     static constexpr int kSlots = kTileBytes / 1024;           // 1 KB direct-load slots per tile
     static constexpr int kRowsPerSlot = 1024 / kRowBytes;
-    // chunk swizzles (bf16 only; the fp32 checking path keeps plain rows)
-    __device__ static __forceinline__ int k_swz(int row) { return sizeof(T) == 2 ? (row & 7) : 0; }
-    __device__ static __forceinline__ int v_swz(int row) { return sizeof(T) == 2 ? 2 * (row & 3) : 0; }
+    // 16-byte chunk swizzles (bf16 only; the fp32 checking path keeps plain
+    // rows).  Conflict-free whether the LDS serves 128 B or 256 B per clock:
+    // K (ds_read_b128, rows r..r+15 at one logical chunk): phys = c ^ (row & 15);
+    // V (transpose reads, 4 rows x 4 chunks per 32 lanes): phys = c ^ {0,4,10,14}[row & 3].
+    __device__ static __forceinline__ int k_swz(int row) { return sizeof(T) == 2 ? (row & 15) : 0; }
+    __device__ static __forceinline__ int v_swz(int row) {
+        return sizeof(T) == 2 ? (4 * (row & 3) + 2 * ((row >> 1) & 1)) : 0;
+    }
 };
 
 template <typename T> struct AttnStage {
@@ -54,12 +59,16 @@ template <typename T> struct AttnStage {
     int32_t kidx[kBK];                                        // key of each tile row (-1: none)
 };
 
-__device__ __forceinline__ int64_t item_of_block(int64_t bid, int64_t total) {
-    // Consecutive workgroup ids land on different XCDs; give each XCD a
-    // contiguous run of work items (kv-group major) so one XCD's L2 serves the
-    // q heads that share K/V.
-    if (total % kNumXcd == 0) return (bid % kNumXcd) * (total / kNumXcd) + bid / kNumXcd;
-    return bid;
+// Work item (q head h, query block b) of workgroup bid: kv group by kv group,
+// heavy (late) query blocks first, the G q heads of a block next to each
+// other.  Consecutive ids are dispatched round-robin over the XCDs, so all
+// XCDs stream the same kv head at once through the shared last-level cache
+// (measured: as fast as or faster than pinning kv heads to XCDs).
+__device__ __forceinline__ void item_of_block(int64_t bid, int64_t nqb, int G, int &h, int64_t &b) {
+    const int64_t per_g = (int64_t)G * nqb;
+    const int64_t g = bid / per_g, rem = bid % per_g;
+    b = nqb - 1 - rem / G;
+    h = (int)(g * G + rem % G);
 }
 
 __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
@@ -107,36 +116,51 @@ struct TileSrc {
 // Start the HBM -> LDS copy of one tile's K and V rows.  Wave w moves the 1 KB
 // slots w*S/2 .. w*S/2 + S/2 - 1 of each tile; in a slot, lane l writes the
 // 16-byte physical chunk l % kChunks of row slot*kRowsPerSlot + l / kChunks,
-// and so loads the logical chunk that the swizzle puts there.  A row whose key
-// does not exist (past the end of the sequence, or column padding) reads a
-// clamped existing row: the softmax mask gives it weight zero and its values
-// are finite, so no zero fill is needed.
+// and so loads the logical chunk that the swizzle puts there.
+//
+// Fast path (64 consecutive keys inside the sequence): one uniform row address
+// plus per-lane offsets that depend only on the lane and the slot.  Otherwise
+// each row's key is looked up (column list) and clamped into the sequence: a
+// row whose key does not exist (past the end, or column padding) reads an
+// existing row, which the softmax mask gives weight zero (its values are
+// finite), so no zero fill is needed.
 template <typename T>
 __device__ __forceinline__ void load_tile(AttnStage<T> &st, const T *kp, const T *vp, const TileSrc &src,
                                           int64_t n, const int32_t *clist, int ncol, int tid) {
     using Gm = Geo<T>;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
     constexpr int kHalf = Gm::kSlots / 2;
     const int sub = lane / Gm::kChunks, phys = lane % Gm::kChunks;
     const char *kb = reinterpret_cast<const char *>(kp);
     const char *vb = reinterpret_cast<const char *>(vp);
+    LDS_AS unsigned char *kl = (LDS_AS unsigned char *)st.k + wave * kHalf * 1024;
+    LDS_AS unsigned char *vl = (LDS_AS unsigned char *)st.v + wave * kHalf * 1024;
+    const int row0 = wave * kHalf * Gm::kRowsPerSlot;                 // first row of this wave
+    if (!src.is_col && src.base >= 0 && src.base + kBK <= n) {
+        const char *kt = kb + (src.base + row0) * Gm::kRowBytes;     // uniform
+        const char *vt = vb + (src.base + row0) * Gm::kRowBytes;
+#pragma unroll
+        for (int i = 0; i < kHalf; ++i) {
+            const int row = row0 + i * Gm::kRowsPerSlot + sub;
+            const uint32_t rel = (uint32_t)((i * Gm::kRowsPerSlot + sub) * Gm::kRowBytes);
+            __builtin_amdgcn_global_load_lds(kt + rel + ((phys ^ Gm::k_swz(row)) << 4),
+                                             (LDS_AS void *)(kl + i * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vt + rel + ((phys ^ Gm::v_swz(row)) << 4),
+                                             (LDS_AS void *)(vl + i * 1024), 16, 0, 0);
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < kHalf; ++i) {
-        const int slot = wave * kHalf + i;
-        const int row = slot * Gm::kRowsPerSlot + sub;
-        int64_t key;
-        if (src.is_col) {
-            const int c = min(src.c0 + row, ncol - 1);
-            key = clist[c];
-        } else {
-            key = src.base + row;
-        }
+        const int row = row0 + i * Gm::kRowsPerSlot + sub;
+        int64_t key = src.is_col ? (int64_t)clist[min(src.c0 + row, ncol - 1)] : src.base + row;
         key = min(max(key, (int64_t)0), n - 1);
         const int64_t rb = key * Gm::kRowBytes;
         __builtin_amdgcn_global_load_lds(kb + rb + ((phys ^ Gm::k_swz(row)) << 4),
-                                         (LDS_AS void *)(LDS_AS unsigned char *)(st.k + slot * 1024), 16, 0, 0);
+                                         (LDS_AS void *)(kl + i * 1024), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(vb + rb + ((phys ^ Gm::v_swz(row)) << 4),
-                                         (LDS_AS void *)(LDS_AS unsigned char *)(st.v + slot * 1024), 16, 0, 0);
+                                         (LDS_AS void *)(vl + i * 1024), 16, 0, 0);
     }
     if (src.is_col && tid < kBK) {
         const int c = src.c0 + tid;
@@ -211,13 +235,10 @@ void attn_fwd_kernel(AttnArgs a) {
     const int64_t n = a.n;
     const int64_t nqb = n / kBQ;
     const int G = a.hq / a.hkv;
-    const int64_t total = (int64_t)a.hq * nqb;
-    const int64_t t = item_of_block(blockIdx.x, total);
-    const int64_t per_g = (int64_t)G * nqb;
-    const int g = (int)(t / per_g);
-    const int64_t rem = t % per_g;
-    const int64_t b = nqb - 1 - rem / G;           // heavy (late) query blocks first
-    const int h = g * G + (int)(rem % G);
+    int h;
+    int64_t b;
+    item_of_block(blockIdx.x, nqb, G, h, b);
+    const int g = h / G;
     const int64_t r0 = b * kBQ;
     const int64_t qrow = r0 + wave * 32 + l32;
 
@@ -299,7 +320,7 @@ void attn_fwd_kernel(AttnArgs a) {
                     const int kx[4] = {kk.x, kk.y, kk.z, kk.w};
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        if (!(kx[i] >= 0 && (int64_t)kx[i] <= qrow)) s[kt][jj * 4 + i] = -INFINITY;
+                        if (!(kx[i] >= 0 && kx[i] <= (int)qrow)) s[kt][jj * 4 + i] = -INFINITY;
                 }
         } else if (cur.base + kBK - 1 > r0 || cur.base < 0) {
             // e allowed iff 0 <= base + e <= qrow
