@@ -56,7 +56,7 @@ template <typename T> struct Geo {
 template <typename T> struct AttnStage {
     alignas(16) unsigned char k[Geo<T>::kTileBytes];
     alignas(16) unsigned char v[Geo<T>::kTileBytes];
-    int32_t kidx[kBK];                                        // key of each tile row (-1: none)
+    int32_t kidx[2][kBK];                                     // key of each column-tile row (-1: none), by tile parity
 };
 
 // Work item (q head h, query block b) of workgroup bid: kv group by kv group,
@@ -113,61 +113,89 @@ struct TileSrc {
     int c0;
 };
 
-// Start the HBM -> LDS copy of one tile's K and V rows.  Wave w moves the 1 KB
-// slots w*S/2 .. w*S/2 + S/2 - 1 of each tile; in a slot, lane l writes the
-// 16-byte physical chunk l % kChunks of row slot*kRowsPerSlot + l / kChunks,
-// and so loads the logical chunk that the swizzle puts there.
+// HBM -> LDS copies of 16 bytes per lane (lane l's bytes land at lds + 16 l),
+// issued from inline assembly: the compiler does not track these copies, so
+// it never waits for them on its own (it would otherwise wait for all of them
+// before any LDS read it cannot prove disjoint).  Completion is awaited with
+// vm_wait<N>() (every copy but the last N issued has landed), then a barrier.
+__device__ __forceinline__ void dma16(const void *gaddr, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "s"(lds) : "memory", "m0");
+}
+// same, with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit offset
+__device__ __forceinline__ void dma16_sbase(const void *sbase, uint32_t voff, uint32_t lds) {
+    const uint64_t u = (uint64_t)(uintptr_t)sbase;     // wave-uniform: move it to SGPRs
+    sbase = (const void *)(uintptr_t)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(u >> 32)) << 32) |
+                                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)u));
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds) : "memory", "m0");
+}
+// s_waitcnt immediate for vmcnt(0) with the other counters unconstrained
+// (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
+constexpr int kVmcnt0 = 0x0F70;
+template <int N> __device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+// Read a wave-uniform int32 through the constant address space: a scalar load,
+// counted by lgkmcnt.  A plain load of kernel-argument memory is a vector load
+// (the compiler cannot prove the kernel never writes it), and its vmcnt wait
+// would also wait for every HBM -> LDS copy in flight.
+__device__ __forceinline__ int32_t load_uniform(const int32_t *p) {
+    return *(const __attribute__((address_space(4))) int32_t *)(uintptr_t)p;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(LDS_AS const unsigned char *)p;
+}
+
+// Start the HBM -> LDS copy of one tile's K rows (kIsV false) or V rows.  Wave
+// w moves the 1 KB slots w*S/2 .. w*S/2 + S/2 - 1 of the tile (S/2 copies per
+// lane); in a slot, lane l writes the 16-byte physical chunk l % kChunks of row
+// slot*kRowsPerSlot + l / kChunks, and so loads the logical chunk that the
+// swizzle puts there.
 //
-// Fast path (64 consecutive keys inside the sequence): one uniform row address
-// plus per-lane offsets that depend only on the lane and the slot.  Otherwise
-// each row's key is looked up (column list) and clamped into the sequence: a
-// row whose key does not exist (past the end, or column padding) reads an
-// existing row, which the softmax mask gives weight zero (its values are
-// finite), so no zero fill is needed.
-template <typename T>
-__device__ __forceinline__ void load_tile(AttnStage<T> &st, const T *kp, const T *vp, const TileSrc &src,
-                                          int64_t n, const int32_t *clist, int ncol, int tid) {
+// Fast path (64 consecutive keys inside the sequence): a uniform base plus
+// per-lane offsets that depend only on the lane and the slot.  Otherwise each
+// row's key is looked up (column list) and clamped into the sequence: a row
+// whose key does not exist (past the end, or column padding) reads an existing
+// row, which the softmax mask gives weight zero (its values are finite).
+template <typename T, bool kIsV>
+__device__ __forceinline__ void load_half(unsigned char *dst, const T *src_rows, const TileSrc &src, int64_t n,
+                                          const int32_t *clist, int ncol, int tid) {
     using Gm = Geo<T>;
+    constexpr int kHalf = Gm::kSlots / 2;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
-    constexpr int kHalf = Gm::kSlots / 2;
     const int sub = lane / Gm::kChunks, phys = lane % Gm::kChunks;
-    const char *kb = reinterpret_cast<const char *>(kp);
-    const char *vb = reinterpret_cast<const char *>(vp);
-    LDS_AS unsigned char *kl = (LDS_AS unsigned char *)st.k + wave * kHalf * 1024;
-    LDS_AS unsigned char *vl = (LDS_AS unsigned char *)st.v + wave * kHalf * 1024;
+    const char *rows = reinterpret_cast<const char *>(src_rows);
+    const uint32_t l0 = lds_addr(dst) + wave * kHalf * 1024;
     const int row0 = wave * kHalf * Gm::kRowsPerSlot;                 // first row of this wave
     if (!src.is_col && src.base >= 0 && src.base + kBK <= n) {
-        const char *kt = kb + (src.base + row0) * Gm::kRowBytes;     // uniform
-        const char *vt = vb + (src.base + row0) * Gm::kRowBytes;
+        const char *tb = rows + (src.base + row0) * Gm::kRowBytes;     // uniform
 #pragma unroll
         for (int i = 0; i < kHalf; ++i) {
-            const int row = row0 + i * Gm::kRowsPerSlot + sub;
-            const uint32_t rel = (uint32_t)((i * Gm::kRowsPerSlot + sub) * Gm::kRowBytes);
-            __builtin_amdgcn_global_load_lds(kt + rel + ((phys ^ Gm::k_swz(row)) << 4),
-                                             (LDS_AS void *)(kl + i * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(vt + rel + ((phys ^ Gm::v_swz(row)) << 4),
-                                             (LDS_AS void *)(vl + i * 1024), 16, 0, 0);
+            const int r = i * Gm::kRowsPerSlot + sub;                    // row - row0
+            const int swz = kIsV ? Gm::v_swz(row0 + r) : Gm::k_swz(row0 + r);
+            dma16_sbase(tb, (uint32_t)(r * Gm::kRowBytes + ((phys ^ swz) << 4)), l0 + i * 1024);
         }
         return;
+    }
+    // all key lookups first: each copy below is a compiler barrier for memory
+    // operations, so a lookup placed after one would wait for every copy
+    int64_t key[kHalf];
+    if (src.is_col) {
+#pragma unroll
+        for (int i = 0; i < kHalf; ++i)
+            key[i] = clist[min(src.c0 + row0 + i * Gm::kRowsPerSlot + sub, ncol - 1)];
+    } else {
+#pragma unroll
+        for (int i = 0; i < kHalf; ++i) key[i] = src.base + row0 + i * Gm::kRowsPerSlot + sub;
     }
 #pragma unroll
     for (int i = 0; i < kHalf; ++i) {
         const int row = row0 + i * Gm::kRowsPerSlot + sub;
-        int64_t key = src.is_col ? (int64_t)clist[min(src.c0 + row, ncol - 1)] : src.base + row;
-        key = min(max(key, (int64_t)0), n - 1);
-        const int64_t rb = key * Gm::kRowBytes;
-        __builtin_amdgcn_global_load_lds(kb + rb + ((phys ^ Gm::k_swz(row)) << 4),
-                                         (LDS_AS void *)(kl + i * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vb + rb + ((phys ^ Gm::v_swz(row)) << 4),
-                                         (LDS_AS void *)(vl + i * 1024), 16, 0, 0);
-    }
-    if (src.is_col && tid < kBK) {
-        const int c = src.c0 + tid;
-        st.kidx[tid] = c < ncol ? clist[c] : -1;
+        const int64_t kc = min(max(key[i], (int64_t)0), n - 1);
+        const int swz = kIsV ? Gm::v_swz(row) : Gm::k_swz(row);
+        dma16(rows + kc * Gm::kRowBytes + ((phys ^ swz) << 4), l0 + i * 1024);
     }
 }
-
 // K fragment (A operand of S^T = K Q^T): row kt*32 + l32, d = dk*16 + hl*8 .. +7
 template <typename T>
 __device__ __forceinline__ typename Elem<T>::frag k_frag(const AttnStage<T> &st, int kt, int dk, int l32, int hl) {
@@ -219,16 +247,26 @@ __device__ __forceinline__ typename Elem<T>::frag v_frag(const AttnStage<T> &st,
     }
 }
 
-// bf16: one 33 KB LDS stage and two waves per SIMD (four workgroups per CU hide
-// each other's load latency; measured faster than two stages at one wave per
-// SIMD).  fp32 (a checking path): two stages, one wave per SIMD.
-template <typename T, bool kDense, int kStages>
+
+// One 64-key tile of K and one of V in LDS (33 KB for bf16: four workgroups
+// and two waves per SIMD), loaded out of phase so that every copy overlaps
+// compute of the same workgroup:
+//   top of tile t:  wait K[t]; barrier; start V[t]
+//   S^T = K Q^T;    barrier; start K[t+1]
+//   mask, online softmax, P
+//   wait V[t];      barrier
+//   O^T += V^T P^T
+// V[t] has QK and softmax of tile t to land, K[t+1] has softmax and PV.  The
+// per-row key list of a column tile is double buffered by tile parity.
+// fp32 (a checking path) uses the same scheme with 64 KB of LDS.
+template <typename T, bool kDense>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1, sizeof(T) == 2 ? 2 : 1)))
 void attn_fwd_kernel(AttnArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the body uses gfx950-only LDS builtins
     using E = Elem<T>;
     using frag = typename E::frag;
-    __shared__ AttnStage<T> stage[kStages];
+    constexpr int kHalf = Geo<T>::kSlots / 2;     // copies per lane per K or V tile
+    __shared__ AttnStage<T> st;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
@@ -263,9 +301,14 @@ void attn_fwd_kernel(AttnArgs a) {
     auto src_of = [&](int it) {
         TileSrc s;
         s.is_col = it >= nblk;
-        s.base = s.is_col ? 0 : (kDense ? (int64_t)it * kBK : (int64_t)blist[it]);
+        s.base = s.is_col ? 0 : (kDense ? (int64_t)it * kBK : (int64_t)load_uniform(blist + it));
         s.c0 = s.is_col ? (it - nblk) * kBK : 0;
         return s;
+    };
+    // start K of tile it (and record a column tile's keys for its mask)
+    auto start_k = [&](int it, const TileSrc &s) {
+        if (s.is_col && tid < kBK) st.kidx[it & 1][tid] = s.c0 + tid < ncol ? clist[s.c0 + tid] : -1;
+        load_half<T, false>(st.k, kp, s, n, clist, ncol, tid);
     };
 
     // Q fragments (B operand of S^T = K Q^T): query qrow, d = dk*16 + hl*8 + e
@@ -281,23 +324,18 @@ void attn_fwd_kernel(AttnArgs a) {
     // running row max kept in scaled log2 units as a stored fp32 value, so an
     // unchanged max gives a rescale factor of exactly 1
     float mb_i = -INFINITY, l_i = 0.f;
+    // Q has landed.  A compiler-visible wait: otherwise the compiler places its
+    // waits for these loads inside the tile loop, where they would also wait
+    // for the K/V copies in flight.
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
 
-    if (kStages == 2 && ntile > 0) {
-        load_tile<T>(stage[0], kp, vp, src_of(0), n, clist, ncol, tid);
-        wait_vmem();
-        __syncthreads();
-    }
+    if (ntile > 0) start_k(0, src_of(0));
 
     for (int it = 0; it < ntile; ++it) {
         const TileSrc cur = src_of(it);
-        if (kStages == 1) {
-            load_tile<T>(stage[0], kp, vp, cur, n, clist, ncol, tid);
-            wait_vmem();
-            __syncthreads();
-        } else if (it + 1 < ntile) {
-            load_tile<T>(stage[(it + 1) & 1], kp, vp, src_of(it + 1), n, clist, ncol, tid);
-        }
-        const AttnStage<T> &st = stage[kStages == 1 ? 0 : (it & 1)];
+        vm_wait<0>();                                   // K[it] has landed (this wave's part)
+        __syncthreads();                                // ... all parts; V is free
+        load_half<T, true>(st.v, vp, cur, n, clist, ncol, tid);
 
         // S^T for this wave's 32 queries: two 32-key sub-tiles
         f32x16 s[2];
@@ -308,6 +346,9 @@ void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
             for (int dk = 0; dk < 8; ++dk) E::mma(s[kt], k_frag<T>(st, kt, dk, l32, hl), qf[dk]);
         }
+        __syncthreads();                                // every wave is done with K
+        const bool more = it + 1 < ntile;
+        if (more) start_k(it + 1, src_of(it + 1));
 
         // mask: the key must exist and satisfy j <= i (keys past the end of the
         // sequence are > i, column padding is -1)
@@ -316,7 +357,7 @@ void attn_fwd_kernel(AttnArgs a) {
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
-                    const int4 kk = *reinterpret_cast<const int4 *>(&st.kidx[kt * 32 + jj * 8 + hl * 4]);
+                    const int4 kk = *reinterpret_cast<const int4 *>(&st.kidx[it & 1][kt * 32 + jj * 8 + hl * 4]);
                     const int kx[4] = {kk.x, kk.y, kk.z, kk.w};
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
@@ -343,7 +384,7 @@ void attn_fwd_kernel(AttnArgs a) {
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
-        mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+        mx = pair32_max(mx);
         const float mb_new = fmaxf(mb_i, mx * a.scale_log2);
         const float ref = (mb_new == -INFINITY) ? 0.f : mb_new;
         float rs = 0.f;
@@ -376,18 +417,18 @@ void attn_fwd_kernel(AttnArgs a) {
             for (int e = 0; e < 8; ++e) tmp[e] = s[kk >> 1][8 * (kk & 1) + e];
             pf[kk] = Out<T>::frag(tmp);
         }
+
+        if (more) vm_wait<kHalf>(); else vm_wait<0>();  // V[it] has landed (K[it+1] may not)
+        __syncthreads();
         // O^T += V^T P^T
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) E::mma(o[dt], v_frag<T>(st, dt, kk, lane), pf[kk]);
-
-        if (kStages == 2) wait_vmem();              // the next tile has landed
-        __syncthreads();
     }
 
     // finalise: lanes l and l^32 hold halves of the same row's sum
-    const float l_tot = l_i + wave_shfl_xor(l_i, 32);
+    const float l_tot = pair32_sum(l_i);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     T *op = reinterpret_cast<T *>(a.out) + ((int64_t)h * n + qrow) * kD;
 #pragma unroll
@@ -406,8 +447,7 @@ void attn_fwd_kernel(AttnArgs a) {
 template <typename T, bool kDense> hipError_t launch(const AttnArgs &a, hipStream_t s) {
     const int64_t total = (int64_t)a.hq * (a.n / kBQ);
     if (total == 0) return hipSuccess;
-    constexpr int kStages = sizeof(T) == 2 ? 1 : 2;
-    hipLaunchKernelGGL((attn_fwd_kernel<T, kDense, kStages>), dim3((unsigned)total), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, kDense>), dim3((unsigned)total), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

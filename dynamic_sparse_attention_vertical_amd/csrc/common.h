@@ -103,6 +103,21 @@ __device__ __forceinline__ float wave_shfl_xor(float v, int mask) {
     return __shfl_xor(v, mask, 64);
 }
 
+// Max / sum of a value over the lane pair (l, l ^ 32) in one VALU permute,
+// v_permlane32_swap, instead of an LDS permute.  With both operands v, the
+// swap returns, in every lane, its own value in one result and its partner's
+// in the other, so a symmetric operation over the two results is the pair's.
+__device__ __forceinline__ float pair32_max(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_sum(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Number of XCDs on MI355X; consecutive workgroup ids are spread round-robin
 // over them, and each XCD has its own L2.
 constexpr int kNumXcd = 8;
