@@ -1,17 +1,21 @@
 // Sparse and dense causal prefill attention for gfx950.
 //
 // One workgroup = one (q head, 64-row query block) work item, two waves of 32
-// query rows each.  The work item walks a list of 64-key tiles: for the sparse
-// kernel, first the item's 64-wide key blocks (arbitrary start), then its
-// leftover vertical columns gathered 64 at a time; for the dense kernel, the
-// aligned tiles 0..b.  Per tile:
-//   S^T = K Q^T        (MFMA 32x32x16; K tile from LDS, Q in registers)
+// query rows each.  The work item walks a list of keys in 32-key chunks: for
+// the sparse kernel, first the item's 64-wide key blocks (arbitrary start, two
+// chunks each), then its leftover vertical columns gathered 32 at a time; for
+// the dense kernel, the aligned tiles 0..b.  Per chunk:
+//   S^T = K Q^T        (MFMA 32x32x16; K rows from LDS, Q in registers)
 //   online softmax in fp32 (exp2 with the log2(e)-folded scale)
 //   O^T += V^T P^T     (P stays in registers as the B operand; V^T read from
-//                       the row-major V tile with the LDS transpose read)
+//                       the row-major V rows with the LDS transpose read)
 // Computing S transposed leaves each lane holding one query's scores for 16
 // keys, so a row max needs only one cross-lane exchange (lane l with l^32), and
 // those scores are already the B operand of the PV product.
+//
+// The three stages are software pipelined across chunks: while a wave's VALU
+// runs the softmax of chunk c, its matrix unit works on S of chunk c+1 and on
+// O += V^T P^T of chunk c-1.
 //
 // K and V rows move from HBM straight into LDS (global_load_lds, 16 bytes per
 // lane, no registers), 16-byte chunks XOR-swizzled per row so that the MFMA
@@ -25,6 +29,8 @@
 // co-designing algorithm and system, principle 1).
 #include "common.h"
 #include "kernels.h"
+
+#include <type_traits>
 
 namespace msa {
 namespace {
@@ -56,7 +62,7 @@ template <typename T> struct Geo {
 template <typename T> struct AttnStage {
     alignas(16) unsigned char k[Geo<T>::kTileBytes];
     alignas(16) unsigned char v[Geo<T>::kTileBytes];
-    int32_t kidx[2][kBK];                                     // key of each column-tile row (-1: none), by tile parity
+    int32_t kidx[4][32];                                      // key of each column-chunk row (-1: none), by chunk % 4
 };
 
 // Work item (q head h, query block b) of workgroup bid: kv group by kv group,
@@ -77,8 +83,6 @@ __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
     f32x2_t v = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
-
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <typename T> struct Out;
 template <> struct Out<bf16> {
@@ -105,29 +109,17 @@ template <> struct Out<float> {
     __device__ static __forceinline__ f32x8 frag(const float *x) { return Elem<float>::from_f32(x); }
 };
 
-// Where a tile's keys come from: 64 consecutive keys from `base`, or 64
-// entries of a column list starting at `c0` (entries past `ncol` are empty).
-struct TileSrc {
+// Where a chunk's 32 keys come from: consecutive keys from `base`, or entries
+// c0 .. c0+31 of the column list (entries past `ncol` are empty).  Key
+// arithmetic is 32-bit: sequence lengths are below 2^31.
+struct ChunkSrc {
     bool is_col;
-    int64_t base;
+    bool fast;      // 32 consecutive keys inside the sequence (both chunks of the tile)
+    bool masked;    // some score of the tile needs the mask
+    int base;
     int c0;
 };
 
-// HBM -> LDS copies of 16 bytes per lane (lane l's bytes land at lds + 16 l),
-// issued from inline assembly: the compiler does not track these copies, so
-// it never waits for them on its own (it would otherwise wait for all of them
-// before any LDS read it cannot prove disjoint).  Completion is awaited with
-// vm_wait<N>() (every copy but the last N issued has landed), then a barrier.
-__device__ __forceinline__ void dma16(const void *gaddr, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "s"(lds) : "memory", "m0");
-}
-// same, with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit offset
-__device__ __forceinline__ void dma16_sbase(const void *sbase, uint32_t voff, uint32_t lds) {
-    const uint64_t u = (uint64_t)(uintptr_t)sbase;     // wave-uniform: move it to SGPRs
-    sbase = (const void *)(uintptr_t)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(u >> 32)) << 32) |
-                                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)u));
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds) : "memory", "m0");
-}
 // s_waitcnt immediate for vmcnt(0) with the other counters unconstrained
 // (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
 constexpr int kVmcnt0 = 0x0F70;
@@ -145,57 +137,119 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)(LDS_AS const unsigned char *)p;
 }
 
-// Start the HBM -> LDS copy of one tile's K rows (kIsV false) or V rows.  Wave
-// w moves the 1 KB slots w*S/2 .. w*S/2 + S/2 - 1 of the tile (S/2 copies per
-// lane); in a slot, lane l writes the 16-byte physical chunk l % kChunks of row
-// slot*kRowsPerSlot + l / kChunks, and so loads the logical chunk that the
-// swizzle puts there.
-//
-// Fast path (64 consecutive keys inside the sequence): a uniform base plus
-// per-lane offsets that depend only on the lane and the slot.  Otherwise each
-// row's key is looked up (column list) and clamped into the sequence: a row
-// whose key does not exist (past the end, or column padding) reads an existing
-// row, which the softmax mask gives weight zero (its values are finite).
-template <typename T, bool kIsV>
-__device__ __forceinline__ void load_half(unsigned char *dst, const T *src_rows, const TileSrc &src, int64_t n,
-                                          const int32_t *clist, int ncol, int tid) {
-    using Gm = Geo<T>;
-    constexpr int kHalf = Gm::kSlots / 2;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63;
-    const int sub = lane / Gm::kChunks, phys = lane % Gm::kChunks;
-    const char *rows = reinterpret_cast<const char *>(src_rows);
-    const uint32_t l0 = lds_addr(dst) + wave * kHalf * 1024;
-    const int row0 = wave * kHalf * Gm::kRowsPerSlot;                 // first row of this wave
-    if (!src.is_col && src.base >= 0 && src.base + kBK <= n) {
-        const char *tb = rows + (src.base + row0) * Gm::kRowBytes;     // uniform
+__device__ __forceinline__ const void *to_sgpr(const void *p) {   // p is wave-uniform
+    const uint64_t u = (uint64_t)(uintptr_t)p;
+    return (const void *)(uintptr_t)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(u >> 32)) << 32) |
+                                     (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)u));
+}
+
+// HBM -> LDS copies, 16 bytes per lane (lane l's bytes land at M0 + 16 l), four
+// 1 KB copies into consecutive LDS slots from `lds` on.  Issued from inline
+// assembly: the compiler does not track these copies, so it never waits for
+// them on its own (it would otherwise wait for all of them before any LDS read
+// it cannot prove disjoint).  Completion is awaited with vm_wait<N>() (every
+// copy but the last N issued has landed), then a barrier.
+// Uniform 64-bit base in SGPRs plus a per-lane 32-bit offset per copy:
+__device__ __forceinline__ void dma_x4(const void *sbase, uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3,
+                                       uint32_t lds) {
+    asm volatile(
+        "s_mov_b32 m0, %5\n\t"
+        "global_load_lds_dwordx4 %0, %4\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "global_load_lds_dwordx4 %1, %4\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "global_load_lds_dwordx4 %2, %4\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "global_load_lds_dwordx4 %3, %4" ::"v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(to_sgpr(sbase)), "s"(lds)
+        : "memory", "m0", "scc");
+}
+// Per-lane 64-bit addresses:
+__device__ __forceinline__ void dma_x4(const void *a0, const void *a1, const void *a2, const void *a3, uint32_t lds) {
+    asm volatile(
+        "s_mov_b32 m0, %4\n\t"
+        "global_load_lds_dwordx4 %0, off\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "global_load_lds_dwordx4 %2, off\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "global_load_lds_dwordx4 %3, off" ::"v"(a0), "v"(a1), "v"(a2), "v"(a3), "s"(lds)
+        : "memory", "m0", "scc");
+}
+
+// Per-lane constants of the chunk copies.  A chunk (32 rows) is moved as
+// kPer 1 KB slots per wave: wave w moves chunk rows 16w .. 16w+15; in slot i,
+// lane l writes the 16-byte physical chunk l % kChunks of row i*kRowsPerSlot +
+// l / kChunks and so reads the logical chunk that the swizzle puts there.
+// Rows 16w + r of either half of a tile have the swizzle of r (16 | row0), so
+// the fast-path offsets are the same for every chunk.
+template <typename T> struct CopyLanes {
+    static constexpr int kPer = 16 * Geo<T>::kRowBytes / 1024;        // 4 (bf16) / 8 (fp32)
+    uint32_t k[kPer], v[kPer];      // fast path: byte offset from the wave's first row
+    int sub, phys;
+    __device__ __forceinline__ void init(int lane) {
+        using Gm = Geo<T>;
+        sub = lane / Gm::kChunks;
+        phys = lane % Gm::kChunks;
 #pragma unroll
-        for (int i = 0; i < kHalf; ++i) {
-            const int r = i * Gm::kRowsPerSlot + sub;                    // row - row0
-            const int swz = kIsV ? Gm::v_swz(row0 + r) : Gm::k_swz(row0 + r);
-            dma16_sbase(tb, (uint32_t)(r * Gm::kRowBytes + ((phys ^ swz) << 4)), l0 + i * 1024);
+        for (int i = 0; i < kPer; ++i) {
+            const int r = i * Gm::kRowsPerSlot + sub;
+            k[i] = (uint32_t)(r * Gm::kRowBytes + ((phys ^ Gm::k_swz(r)) << 4));
+            v[i] = (uint32_t)(r * Gm::kRowBytes + ((phys ^ Gm::v_swz(r)) << 4));
         }
+    }
+};
+
+// Start the HBM -> LDS copy of one chunk's K rows (kIsV false) or V rows into
+// rows 32*half .. 32*half+31 of the K or V tile (this wave's 16 of them).
+//
+// Fast path (32 consecutive keys inside the sequence): one uniform base.
+// Otherwise each row's key is looked up and clamped into the sequence: a row
+// whose key does not exist (past the end, or column padding) reads an existing
+// row, which the softmax mask gives weight zero (its values are finite).  The
+// keys of a column chunk come from the list for K, and from LDS for V (recorded
+// when its K was started).
+template <typename T, bool kIsV>
+__device__ __forceinline__ void load_chunk(const CopyLanes<T> &cl, uint32_t lds_wave, const T *src_rows,
+                                           const ChunkSrc &src, int half, int wave, int n, const int32_t *clist,
+                                           int ncol, const int32_t *keys_lds) {
+    using Gm = Geo<T>;
+    constexpr int kPer = CopyLanes<T>::kPer;
+    const char *rows = reinterpret_cast<const char *>(src_rows);
+    const uint32_t l0 = lds_wave + half * 32 * Gm::kRowBytes;
+    const uint32_t *off = kIsV ? cl.v : cl.k;
+    if (src.fast) {
+        const char *tb = rows + (int64_t)(src.base + wave * 16) * Gm::kRowBytes;
+#pragma unroll
+        for (int i = 0; i < kPer; i += 4) dma_x4(tb, off[i], off[i + 1], off[i + 2], off[i + 3], l0 + i * 1024);
         return;
     }
     // all key lookups first: each copy below is a compiler barrier for memory
     // operations, so a lookup placed after one would wait for every copy
-    int64_t key[kHalf];
-    if (src.is_col) {
+    int key[kPer];
+    if (src.is_col && kIsV) {
 #pragma unroll
-        for (int i = 0; i < kHalf; ++i)
-            key[i] = clist[min(src.c0 + row0 + i * Gm::kRowsPerSlot + sub, ncol - 1)];
+        for (int i = 0; i < kPer; ++i) key[i] = keys_lds[wave * 16 + i * Gm::kRowsPerSlot + cl.sub];
+    } else if (src.is_col) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+            key[i] = clist[min(src.c0 + wave * 16 + i * Gm::kRowsPerSlot + cl.sub, ncol - 1)];
     } else {
 #pragma unroll
-        for (int i = 0; i < kHalf; ++i) key[i] = src.base + row0 + i * Gm::kRowsPerSlot + sub;
+        for (int i = 0; i < kPer; ++i) key[i] = src.base + wave * 16 + i * Gm::kRowsPerSlot + cl.sub;
+    }
+    const char *a[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int r = i * Gm::kRowsPerSlot + cl.sub;
+        const int kc = min(max(key[i], 0), n - 1);
+        const int swz = kIsV ? Gm::v_swz(r) : Gm::k_swz(r);
+        a[i] = rows + (int64_t)kc * Gm::kRowBytes + ((cl.phys ^ swz) << 4);
     }
 #pragma unroll
-    for (int i = 0; i < kHalf; ++i) {
-        const int row = row0 + i * Gm::kRowsPerSlot + sub;
-        const int64_t kc = min(max(key[i], (int64_t)0), n - 1);
-        const int swz = kIsV ? Gm::v_swz(row) : Gm::k_swz(row);
-        dma16(rows + kc * Gm::kRowBytes + ((phys ^ swz) << 4), l0 + i * 1024);
-    }
+    for (int i = 0; i < kPer; i += 4) dma_x4(a[i], a[i + 1], a[i + 2], a[i + 3], l0 + i * 1024);
 }
+
 // K fragment (A operand of S^T = K Q^T): row kt*32 + l32, d = dk*16 + hl*8 .. +7
 template <typename T>
 __device__ __forceinline__ typename Elem<T>::frag k_frag(const AttnStage<T> &st, int kt, int dk, int l32, int hl) {
@@ -249,15 +303,16 @@ __device__ __forceinline__ typename Elem<T>::frag v_frag(const AttnStage<T> &st,
 
 
 // One 64-key tile of K and one of V in LDS (33 KB for bf16: four workgroups
-// and two waves per SIMD), loaded out of phase so that every copy overlaps
-// compute of the same workgroup:
-//   top of tile t:  wait K[t]; barrier; start V[t]
-//   S^T = K Q^T;    barrier; start K[t+1]
-//   mask, online softmax, P
-//   wait V[t];      barrier
-//   O^T += V^T P^T
-// V[t] has QK and softmax of tile t to land, K[t+1] has softmax and PV.  The
-// per-row key list of a column tile is double buffered by tile parity.
+// and two waves per SIMD), each holding two 32-key chunks; chunk c lives in
+// half c % 2.  Step c of the pipeline (after a wait and a barrier):
+//   start the copies of K of chunk c+2 and V of chunk c
+//   mask S(c) where needed
+//   MFMA: S(c+1) = K(c+1) Q^T,  O^T += V(c-1)^T P(c-1)
+//   VALU: online softmax of S(c) -> P(c)
+//   rescale O if a row maximum moved (after PV(c-1), before PV(c))
+// K of chunk c+1 and V of chunk c-1 were started one step earlier.  The last
+// step computes an S that is never used (from K rows still in LDS), which
+// keeps the step free of branches around the matrix work.
 // fp32 (a checking path) uses the same scheme with 64 KB of LDS.
 template <typename T, bool kDense>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1, sizeof(T) == 2 ? 2 : 1)))
@@ -265,20 +320,21 @@ void attn_fwd_kernel(AttnArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the body uses gfx950-only LDS builtins
     using E = Elem<T>;
     using frag = typename E::frag;
-    constexpr int kHalf = Geo<T>::kSlots / 2;     // copies per lane per K or V tile
     __shared__ AttnStage<T> st;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
     const int64_t n = a.n;
+    const int n32 = (int)n;                          // below 2^31
     const int64_t nqb = n / kBQ;
     const int G = a.hq / a.hkv;
     int h;
     int64_t b;
     item_of_block(blockIdx.x, nqb, G, h, b);
     const int g = h / G;
-    const int64_t r0 = b * kBQ;
-    const int64_t qrow = r0 + wave * 32 + l32;
+    const int r0 = (int)b * kBQ;
+    const int qrow = r0 + wave * 32 + l32;
 
     const T *qp = reinterpret_cast<const T *>(a.q) + ((int64_t)h * n) * kD;
     const T *kp = reinterpret_cast<const T *>(a.k) + ((int64_t)g * n) * kD;
@@ -296,25 +352,43 @@ void attn_fwd_kernel(AttnArgs a) {
         blist = a.block_offset + item * a.cap_b;
         clist = a.column_index + item * a.cap_c;
     }
-    const int ntile = nblk + (ncol + kBK - 1) / kBK;
+    // an even number of chunks (column chunks padded with an empty one), so
+    // that the steps come in pairs
+    const int nchunk = 2 * (nblk + (ncol + kBK - 1) / kBK);
 
-    auto src_of = [&](int it) {
-        TileSrc s;
-        s.is_col = it >= nblk;
-        s.base = s.is_col ? 0 : (kDense ? (int64_t)it * kBK : (int64_t)load_uniform(blist + it));
-        s.c0 = s.is_col ? (it - nblk) * kBK : 0;
+    // where tile t's keys come from (one scalar load per block tile), and the
+    // chunk of it in half hf
+    auto tile_of = [&](int t) {
+        ChunkSrc s;
+        s.is_col = t >= nblk;
+        s.base = s.is_col ? 0 : (kDense ? t * kBK : load_uniform(blist + t));
+        s.c0 = s.is_col ? (t - nblk) * kBK : 0;
+        s.fast = !s.is_col && s.base >= 0 && s.base <= n32 - kBK;
+        s.masked = !s.fast || s.base + kBK - 1 > r0;
         return s;
     };
-    // start K of tile it (and record a column tile's keys for its mask)
-    auto start_k = [&](int it, const TileSrc &s) {
-        if (s.is_col && tid < kBK) st.kidx[it & 1][tid] = s.c0 + tid < ncol ? clist[s.c0 + tid] : -1;
-        load_half<T, false>(st.k, kp, s, n, clist, ncol, tid);
+    auto half_of = [](ChunkSrc s, int hf) {
+        s.base += 32 * hf;
+        s.c0 += 32 * hf;
+        return s;
+    };
+    // start K of chunk c (and record a column chunk's keys for its mask)
+    CopyLanes<T> cl;
+    cl.init(lane);
+    const uint32_t lds_k = lds_addr(st.k) + wave * 16 * Geo<T>::kRowBytes;
+    const uint32_t lds_v = lds_addr(st.v) + wave * 16 * Geo<T>::kRowBytes;
+    auto start_k = [&](int c, const ChunkSrc &s) {
+        if (!s.fast && s.is_col && tid < 32) st.kidx[c & 3][tid] = s.c0 + tid < ncol ? clist[s.c0 + tid] : -1;
+        load_chunk<T, false>(cl, lds_k, kp, s, c & 1, wave, n32, clist, ncol, nullptr);
+    };
+    auto start_v = [&](int c, const ChunkSrc &s) {
+        load_chunk<T, true>(cl, lds_v, vp, s, c & 1, wave, n32, clist, ncol, st.kidx[c & 3]);
     };
 
     // Q fragments (B operand of S^T = K Q^T): query qrow, d = dk*16 + hl*8 + e
     frag qf[8];
 #pragma unroll
-    for (int dk = 0; dk < 8; ++dk) qf[dk] = E::load_frag(qp + qrow * kD + dk * 16 + hl * 8);
+    for (int dk = 0; dk < 8; ++dk) qf[dk] = E::load_frag(qp + (int64_t)qrow * kD + dk * 16 + hl * 8);
 
     f32x16 o[4];
 #pragma unroll
@@ -325,106 +399,133 @@ void attn_fwd_kernel(AttnArgs a) {
     // unchanged max gives a rescale factor of exactly 1
     float mb_i = -INFINITY, l_i = 0.f;
     // Q has landed.  A compiler-visible wait: otherwise the compiler places its
-    // waits for these loads inside the tile loop, where they would also wait
+    // waits for these loads inside the chunk loop, where they would also wait
     // for the K/V copies in flight.
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
 
-    if (ntile > 0) start_k(0, src_of(0));
-
-    for (int it = 0; it < ntile; ++it) {
-        const TileSrc cur = src_of(it);
-        vm_wait<0>();                                   // K[it] has landed (this wave's part)
-        __syncthreads();                                // ... all parts; V is free
-        load_half<T, true>(st.v, vp, cur, n, clist, ncol, tid);
-
-        // S^T for this wave's 32 queries: two 32-key sub-tiles
-        f32x16 s[2];
+    // S(c) = K(c) Q^T for the 32 keys of the chunk in K half c % 2
+    auto qk = [&](int c, f32x16 &s) {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
+        for (int dk = 0; dk < 8; ++dk) E::mma(s, k_frag<T>(st, c & 1, dk, l32, hl), qf[dk]);
+    };
+    // O^T += V(c)^T P(c) for the chunk in V half c % 2
+    auto pv = [&](int c, const frag (&p)[2]) {
 #pragma unroll
-            for (int dk = 0; dk < 8; ++dk) E::mma(s[kt], k_frag<T>(st, kt, dk, l32, hl), qf[dk]);
-        }
-        __syncthreads();                                // every wave is done with K
-        const bool more = it + 1 < ntile;
-        if (more) start_k(it + 1, src_of(it + 1));
-
-        // mask: the key must exist and satisfy j <= i (keys past the end of the
-        // sequence are > i, column padding is -1)
-        if (cur.is_col) {
+        for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int kk = 0; kk < 2; ++kk) E::mma(o[dt], v_frag<T>(st, dt, 2 * (c & 1) + kk, lane), p[kk]);
+    };
+    // mask: the key must exist and satisfy j <= i (keys past the end of the
+    // sequence are > i, column padding is -1).  Lane value jj*4+i of S^T is
+    // chunk key jj*8 + hl*4 + i.
+    auto mask = [&](int c, const ChunkSrc &cs, f32x16 &s) {
+        if (!cs.masked) return;
+        if (cs.is_col) {
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int4 kk = *reinterpret_cast<const int4 *>(&st.kidx[it & 1][kt * 32 + jj * 8 + hl * 4]);
-                    const int kx[4] = {kk.x, kk.y, kk.z, kk.w};
+            for (int jj = 0; jj < 4; ++jj) {
+                const int4 kk = *reinterpret_cast<const int4 *>(&st.kidx[c & 3][jj * 8 + hl * 4]);
+                const int kx[4] = {kk.x, kk.y, kk.z, kk.w};
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (!(kx[i] >= 0 && kx[i] <= (int)qrow)) s[kt][jj * 4 + i] = -INFINITY;
-                }
-        } else if (cur.base + kBK - 1 > r0 || cur.base < 0) {
+                for (int i = 0; i < 4; ++i)
+                    if (!(kx[i] >= 0 && kx[i] <= qrow)) s[jj * 4 + i] = -INFINITY;
+            }
+        } else {
             // e allowed iff 0 <= base + e <= qrow
-            const int hi = (int)min(max(qrow - cur.base, (int64_t)-1), (int64_t)kBK);
-            const int lo = (int)min(max(-cur.base, (int64_t)0), (int64_t)kBK);
+            const int hi = min(max(qrow - cs.base, -1), 32);
+            const int lo = min(max(-cs.base, 0), 32);
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int e = kt * 32 + jj * 8 + hl * 4 + i;
-                        if (e > hi || e < lo) s[kt][jj * 4 + i] = -INFINITY;
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    const int e = jj * 8 + hl * 4 + i;
+                    if (e > hi || e < lo) s[jj * 4 + i] = -INFINITY;
+                }
         }
-
-        // online softmax: p = 2^(s*c - mb), c = scale*log2(e)
+    };
+    // online softmax of S(c) -> P(c); returns the factor for O (1 if no row
+    // maximum moved in this wave)
+    auto softmax = [&](f32x16 &s, frag (&p)[2], float &alpha, bool &moved) {
         float mx = -INFINITY;
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
         mx = pair32_max(mx);
         const float mb_new = fmaxf(mb_i, mx * a.scale_log2);
         const float ref = (mb_new == -INFINITY) ? 0.f : mb_new;
         float rs = 0.f;
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int i = 0; i < 16; ++i) {
+            const float e = __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -ref));
+            s[i] = e;
+            rs += e;
+        }
+        moved = __builtin_amdgcn_ballot_w64(mb_new != mb_i) != 0;
+        alpha = moved ? __builtin_amdgcn_exp2f(mb_i - ref) : 1.f;
+        l_i = l_i * alpha + rs;
+        mb_i = mb_new;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][i], a.scale_log2, -ref));
-                s[kt][i] = p;
-                rs += p;
-            }
-        // rescale only when some row's max moved (alpha is exactly 1 otherwise)
-        if (__builtin_amdgcn_ballot_w64(mb_new != mb_i) != 0) {
-            const float alpha = __builtin_amdgcn_exp2f(mb_i - ref);
-            l_i *= alpha;
+        for (int kk = 0; kk < 2; ++kk) {
+            float tmp[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) tmp[e] = s[8 * kk + e];
+            p[kk] = Out<T>::frag(tmp);
+        }
+    };
+    // one pipeline step for chunk c (source cs); kn is the source of chunk c+2
+    auto step = [&](int c, const ChunkSrc &cs, const ChunkSrc &kn, f32x16 &s_cur, f32x16 &s_next,
+                    frag (&p_cur)[2], const frag (&p_prev)[2], auto with_pv) {
+        vm_wait<0>();                                   // K(c+1), V(c-1) have landed (this wave's part)
+        __syncthreads();                                // ... all parts; K(c) and V(c-2) are free
+        start_k(c + 2, kn);     // past the end: a copy of the last tile's K, never read
+        start_v(c, cs);
+        mask(c, cs, s_cur);
+        qk(c + 1, s_next);
+        float alpha;
+        bool moved;
+        softmax(s_cur, p_cur, alpha, moved);
+        if constexpr (decltype(with_pv)::value) pv(c - 1, p_prev);
+        // keep P(c) and the row sum computed here, next to the matrix work of
+        // this step (the compiler would otherwise sink them to their use in
+        // the next step)
+        asm volatile("" ::"v"(p_cur[0]), "v"(p_cur[1]), "v"(l_i));
+        if (moved) {
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
         }
-        l_i += rs;
-        mb_i = mb_new;
+    };
 
-        // P fragments: k-step kk uses accumulator s[kk/2], elements 8*(kk%2)..+7
-        frag pf[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            float tmp[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) tmp[e] = s[kk >> 1][8 * (kk & 1) + e];
-            pf[kk] = Out<T>::frag(tmp);
-        }
-
-        if (more) vm_wait<kHalf>(); else vm_wait<0>();  // V[it] has landed (K[it+1] may not)
+    if (nchunk > 0) {
+        const int ntile = nchunk / 2;
+        f32x16 sa, sb;
+        frag pa[2], pb[2];
+        ChunkSrc cur = tile_of(0);
+        ChunkSrc nxt = tile_of(min(1, ntile - 1));
+        start_k(0, half_of(cur, 0));
+        start_k(1, half_of(cur, 1));
+        vm_wait<0>();
         __syncthreads();
-        // O^T += V^T P^T
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) E::mma(o[dt], v_frag<T>(st, dt, kk, lane), pf[kk]);
+        qk(0, sa);
+        // tile 0: no PV yet in its first step
+        {
+            const ChunkSrc after = tile_of(min(2, ntile - 1));
+            step(0, half_of(cur, 0), half_of(nxt, 0), sa, sb, pa, pb, std::false_type{});
+            step(1, half_of(cur, 1), half_of(nxt, 1), sb, sa, pb, pa, std::true_type{});
+            cur = nxt;
+            nxt = after;
+        }
+        for (int t = 1; t < ntile; ++t) {
+            const ChunkSrc after = tile_of(min(t + 2, ntile - 1));     // needed one pair later
+            step(2 * t, half_of(cur, 0), half_of(nxt, 0), sa, sb, pa, pb, std::true_type{});
+            step(2 * t + 1, half_of(cur, 1), half_of(nxt, 1), sb, sa, pb, pa, std::true_type{});
+            cur = nxt;
+            nxt = after;
+        }
+        vm_wait<0>();                                   // V of the last chunk
+        __syncthreads();
+        pv(nchunk - 1, pb);
     }
 
     // finalise: lanes l and l^32 hold halves of the same row's sum
