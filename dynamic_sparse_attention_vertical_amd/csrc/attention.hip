@@ -41,7 +41,7 @@ constexpr int kBK = 64;          // keys per tile
 constexpr int kThreads = 128;    // two waves
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
-#define LDS_AS __attribute__((address_space(3)))
+
 
 template <typename T> struct Geo {
     static constexpr int kRowBytes = kD * (int)sizeof(T);      // 256 (bf16) / 512 (fp32)
@@ -119,63 +119,6 @@ struct ChunkSrc {
     int base;
     int c0;
 };
-
-// s_waitcnt immediate for vmcnt(0) with the other counters unconstrained
-// (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
-constexpr int kVmcnt0 = 0x0F70;
-template <int N> __device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
-
-// Read a wave-uniform int32 through the constant address space: a scalar load,
-// counted by lgkmcnt.  A plain load of kernel-argument memory is a vector load
-// (the compiler cannot prove the kernel never writes it), and its vmcnt wait
-// would also wait for every HBM -> LDS copy in flight.
-__device__ __forceinline__ int32_t load_uniform(const int32_t *p) {
-    return *(const __attribute__((address_space(4))) int32_t *)(uintptr_t)p;
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-    return (uint32_t)(uintptr_t)(LDS_AS const unsigned char *)p;
-}
-
-__device__ __forceinline__ const void *to_sgpr(const void *p) {   // p is wave-uniform
-    const uint64_t u = (uint64_t)(uintptr_t)p;
-    return (const void *)(uintptr_t)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(u >> 32)) << 32) |
-                                     (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)u));
-}
-
-// HBM -> LDS copies, 16 bytes per lane (lane l's bytes land at M0 + 16 l), four
-// 1 KB copies into consecutive LDS slots from `lds` on.  Issued from inline
-// assembly: the compiler does not track these copies, so it never waits for
-// them on its own (it would otherwise wait for all of them before any LDS read
-// it cannot prove disjoint).  Completion is awaited with vm_wait<N>() (every
-// copy but the last N issued has landed), then a barrier.
-// Uniform 64-bit base in SGPRs plus a per-lane 32-bit offset per copy:
-__device__ __forceinline__ void dma_x4(const void *sbase, uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3,
-                                       uint32_t lds) {
-    asm volatile(
-        "s_mov_b32 m0, %5\n\t"
-        "global_load_lds_dwordx4 %0, %4\n\t"
-        "s_add_u32 m0, m0, 0x400\n\t"
-        "global_load_lds_dwordx4 %1, %4\n\t"
-        "s_add_u32 m0, m0, 0x400\n\t"
-        "global_load_lds_dwordx4 %2, %4\n\t"
-        "s_add_u32 m0, m0, 0x400\n\t"
-        "global_load_lds_dwordx4 %3, %4" ::"v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(to_sgpr(sbase)), "s"(lds)
-        : "memory", "m0", "scc");
-}
-// Per-lane 64-bit addresses:
-__device__ __forceinline__ void dma_x4(const void *a0, const void *a1, const void *a2, const void *a3, uint32_t lds) {
-    asm volatile(
-        "s_mov_b32 m0, %4\n\t"
-        "global_load_lds_dwordx4 %0, off\n\t"
-        "s_add_u32 m0, m0, 0x400\n\t"
-        "global_load_lds_dwordx4 %1, off\n\t"
-        "s_add_u32 m0, m0, 0x400\n\t"
-        "global_load_lds_dwordx4 %2, off\n\t"
-        "s_add_u32 m0, m0, 0x400\n\t"
-        "global_load_lds_dwordx4 %3, off" ::"v"(a0), "v"(a1), "v"(a2), "v"(a3), "s"(lds)
-        : "memory", "m0", "scc");
-}
 
 // Per-lane constants of the chunk copies.  A chunk (32 rows) is moved as
 // kPer 1 KB slots per wave: wave w moves chunk rows 16w .. 16w+15; in slot i,

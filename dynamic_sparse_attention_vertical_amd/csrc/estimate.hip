@@ -11,21 +11,26 @@
 // token long-sequence QA on a single 4090D", section 3.2, is v / 64).
 //
 // Work split: workgroup = (kv head g, contiguous key range), four waves, wave w
-// serving q head g*G + w (+4, ...).  The K tile (64 keys) is staged in LDS
-// once and shared by the G q heads of the group.  Scores are computed with
-// MFMA as S^T = K Q^T (lane = one query row, 16 keys per 32-key sub-tile).
-//   pass 1: per-row running max (kept as scale*log2(e)*z) and sum of exp2
+// serving q head g*G + w (+4, ...).  K tiles (64 keys) stream HBM -> LDS with
+// direct copies, double buffered, and are shared by the G q heads of the group.
+//   pass 1 (S^T = K Q^T, lane = query row, 16 keys per lane and sub-tile):
+//           per-row running max (kept as scale*log2(e)*z) and sum of exp2
 //           over the range -> partials
-//   combine: partials -> row max m_r and 1 / sum
-//   pass 2: recompute S, p = exp(z - m_r) / l_r, written to a per-wave LDS
-//           tile; column sums give v directly, diagonal sums are read along
-//           diagonals of that tile.  A diagonal spans at most two adjacent
-//           tiles; inside a range the carry is kept in a register, across
-//           ranges the two partial sums go to the workspace and a fix-up
-//           kernel adds them.  No floating-point atomics: results are
-//           deterministic.
+//   combine: partials -> per-row log2 normaliser  m_r + log2(l_r)
+//   pass 2 (S = Q K^T, lane = key, 16 query rows per lane and sub-tile):
+//           p = exp2(scale*log2(e)*z - normaliser).  Column sums v stay in
+//           registers.  For the diagonal sums, each wave writes its 32 x 64
+//           block of p into LDS skewed, row r shifted by -r, so that a diagonal
+//           becomes a column; cells outside the written parallelogram are zero
+//           from the start and never written, so the column reads need no
+//           bounds tests.  A diagonal spans at most two adjacent tiles: inside
+//           a range the carry is kept in a register, across ranges the two
+//           partial sums go to the workspace and a fix-up kernel adds them.
+//           No floating-point atomics: results are deterministic.
 #include "common.h"
 #include "kernels.h"
+
+#include <type_traits>
 
 namespace msa {
 namespace {
@@ -34,59 +39,81 @@ constexpr int kD = 128;
 constexpr int kL = 64;           // last_q
 constexpr int kTK = 64;          // keys per tile
 constexpr int kThreads = 256;    // four waves
-constexpr int kPP = 65;          // per-wave P tile pitch (floats)
+constexpr int kSkew = 95;        // skewed p block: 32 rows x 95 columns (row pitch)
 
-template <typename T> struct EstSmem {
-    static constexpr int kEpv = 16 / Elem<T>::kBytes;
-    static constexpr int kKPitch = kD + kEpv;
-    T k[kTK * kKPitch];
+// K tile geometry: rows of kRowBytes, 1 KB copy slots, 16-byte chunks XOR
+// swizzled per row (bf16) so that the MFMA operand reads (rows r..r+15 at one
+// logical chunk) are free of bank conflicts.
+template <typename T> struct KGeo {
+    static constexpr int kRowBytes = kD * (int)sizeof(T);
+    static constexpr int kChunks = kRowBytes / 16;
+    static constexpr int kTileBytes = kTK * kRowBytes;
+    static constexpr int kRowsPerSlot = 1024 / kRowBytes;
+    static constexpr int kPer = kTileBytes / 1024 / 4;           // copies per lane (4 waves)
+    __device__ static __forceinline__ int swz(int row) { return sizeof(T) == 2 ? (row & 15) : 0; }
 };
 
-template <typename T>
-__device__ __forceinline__ void load_k_tile(T *ks, const T *kp, int64_t base, int tid) {
-    constexpr int kEpv = EstSmem<T>::kEpv;
-    constexpr int kKPitch = EstSmem<T>::kKPitch;
-    constexpr int kVpr = kD / kEpv;
-#pragma unroll
-    for (int c = tid; c < kTK * kVpr; c += kThreads) {
-        const int row = c / kVpr, cv = c % kVpr;
-        u32x4 val = *reinterpret_cast<const u32x4 *>(kp + (base + row) * kD + cv * kEpv);
-        *reinterpret_cast<u32x4 *>(&ks[row * kKPitch + cv * kEpv]) = val;
-    }
-}
+template <typename T> struct EstSmem {
+    alignas(16) unsigned char k[2][KGeo<T>::kTileBytes];
+};
 
-// S^T for 32 query rows (half) against the 64-key tile: s[kt][jj*4+i] is
-// the score of key kt*32 + jj*8 + hl*4 + i for query row half*32 + lane%32.
+// Start the copy of the 64-key tile at `base` into LDS buffer `buf`: wave w
+// moves rows 16w .. 16w+15 (kPer 1 KB slots).
 template <typename T>
-__device__ __forceinline__ void tile_scores(f32x16 (&s)[2], const T *ks, const typename Elem<T>::frag *qf,
-                                            int l32, int hl) {
-    using E = Elem<T>;
-    constexpr int kKPitch = EstSmem<T>::kKPitch;
+__device__ __forceinline__ void start_tile(unsigned char *buf, const T *kp, int64_t base, int wave,
+                                           const uint32_t (&off)[KGeo<T>::kPer]) {
+    using Gm = KGeo<T>;
+    const char *tb = reinterpret_cast<const char *>(kp) + (base + wave * 16) * Gm::kRowBytes;
+    const uint32_t l0 = lds_addr(buf) + wave * 16 * Gm::kRowBytes;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
-#pragma unroll
-        for (int dk = 0; dk < 8; ++dk) {
-            typename E::frag kf = E::load_frag(&ks[(kt * 32 + l32) * kKPitch + dk * 16 + hl * 8]);
-            E::mma(s[kt], kf, qf[dk]);
-        }
-    }
+    for (int i = 0; i < Gm::kPer; i += 4) dma_x4(tb, off[i], off[i + 1], off[i + 2], off[i + 3], l0 + i * 1024);
 }
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void est_pass1_kernel(EstArgs a) {
+__device__ __forceinline__ void copy_offsets(uint32_t (&off)[KGeo<T>::kPer], int lane) {
+    using Gm = KGeo<T>;
+    const int sub = lane / Gm::kChunks, phys = lane % Gm::kChunks;
+#pragma unroll
+    for (int i = 0; i < Gm::kPer; ++i) {
+        const int r = i * Gm::kRowsPerSlot + sub;          // rows 16w + r share the swizzle of r
+        off[i] = (uint32_t)(r * Gm::kRowBytes + ((phys ^ Gm::swz(r)) << 4));
+    }
+}
+
+// K fragment of tile rows kt*32 + l32, d = dk*16 + hl*8 .. +7
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::frag k_frag(const unsigned char *buf, int kt, int dk, int l32, int hl) {
+    using Gm = KGeo<T>;
+    const int row = kt * 32 + l32;
+    const int c = (dk * 16 + hl * 8) * (int)sizeof(T) / 16;
+    if constexpr (sizeof(T) == 2) {
+        return Elem<T>::load_frag(buf + row * Gm::kRowBytes + ((c ^ Gm::swz(row)) << 4));
+    } else {
+        return Elem<T>::load_frag(buf + row * Gm::kRowBytes + c * 16);
+    }
+}
+
+// Number of q heads waves serve per pass over the key range.
+__device__ __forceinline__ int n_slots(int G) { return (G + 3) / 4; }
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void est_pass1_kernel(EstArgs a) {
     using E = Elem<T>;
+    using Gm = KGeo<T>;
     __shared__ EstSmem<T> sm;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int range = blockIdx.x, g = blockIdx.y;
     const int G = a.hq / a.hkv;
     const int64_t n = a.n;
     const int64_t k0 = (int64_t)range * a.range_keys;
     const int64_t k1 = min(n, k0 + a.range_keys);
+    const int ntile = (int)((k1 - k0) / kTK);
     const T *kp = reinterpret_cast<const T *>(a.k) + (int64_t)g * n * kD;
-    const int nslot = (G + 3) / 4;
-    for (int slot = 0; slot < nslot; ++slot) {
+    uint32_t off[Gm::kPer];
+    copy_offsets<T>(off, lane);
+    for (int slot = 0; slot < n_slots(G); ++slot) {
         const int hw = wave + 4 * slot;
         const bool active = hw < G;
         const int h = g * G + (active ? hw : 0);
@@ -96,28 +123,36 @@ __global__ __launch_bounds__(kThreads) void est_pass1_kernel(EstArgs a) {
         for (int half = 0; half < 2; ++half)
 #pragma unroll
             for (int dk = 0; dk < 8; ++dk)
-                qf[half][dk] = active ? E::load_frag(qp + (half * 32 + l32) * kD + dk * 16 + hl * 8)
-                                      : E::zero_frag();
+                qf[half][dk] = E::load_frag(qp + (half * 32 + l32) * kD + dk * 16 + hl * 8);
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);        // Q has landed (compiler-visible wait)
         float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
-        for (int64_t base = k0; base < k1; base += kTK) {
-            __syncthreads();
-            load_k_tile<T>(sm.k, kp, base, tid);
-            __syncthreads();
+        __syncthreads();                            // the previous slot is done with both buffers
+        start_tile<T>(sm.k[0], kp, k0, wave, off);
+        for (int t = 0; t < ntile; ++t) {
+            const int64_t base = k0 + (int64_t)t * kTK;
+            vm_wait<0>();
+            __syncthreads();                        // tile t visible; tile t-1's buffer is free
+            if (t + 1 < ntile) start_tile<T>(sm.k[(t + 1) & 1], kp, base + kTK, wave, off);
             if (!active) continue;
-            const bool last = base + kTK > n - kL;       // keys past some p_r
+            const unsigned char *buf = sm.k[t & 1];
+            const bool last = base + kTK > n - kL;  // keys past some p_r
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 f32x16 s[2];
-                tile_scores<T>(s, sm.k, qf[half], l32, hl);
-                const int64_t prow = n - kL + half * 32 + l32;
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
+#pragma unroll
+                    for (int dk = 0; dk < 8; ++dk) E::mma(s[kt], k_frag<T>(buf, kt, dk, l32, hl), qf[half][dk]);
+                }
                 if (last) {
+                    const int64_t prow = n - kL + half * 32 + l32;
 #pragma unroll
                     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            const int64_t key = base + kt * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
-                            if (key > prow) s[kt][i] = -INFINITY;
-                        }
+                        for (int i = 0; i < 16; ++i)
+                            if (base + kt * 32 + (i >> 2) * 8 + hl * 4 + (i & 3) > prow) s[kt][i] = -INFINITY;
                 }
                 float mx = -INFINITY;
 #pragma unroll
@@ -128,11 +163,11 @@ __global__ __launch_bounds__(kThreads) void est_pass1_kernel(EstArgs a) {
                 // max rescales by exactly 1)
                 const float mn = fmaxf(m[half], mx * a.scale_log2);
                 const float ref = (mn == -INFINITY) ? 0.f : mn;
-                float acc = l[half] * exp2f(m[half] - ref);
+                float acc = l[half] * __builtin_amdgcn_exp2f(m[half] - ref);
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) acc += exp2f(fmaf(s[kt][i], a.scale_log2, -ref));
+                    for (int i = 0; i < 16; ++i) acc += __builtin_amdgcn_exp2f(fmaf(s[kt][i], a.scale_log2, -ref));
                 m[half] = mn;
                 l[half] = acc;
             }
@@ -143,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void est_pass1_kernel(EstArgs a) {
                 const float mo = wave_shfl_xor(m[half], 32), lo = wave_shfl_xor(l[half], 32);
                 const float mn = fmaxf(m[half], mo);
                 const float ref = (mn == -INFINITY) ? 0.f : mn;
-                const float lt = l[half] * exp2f(m[half] - ref) + lo * exp2f(mo - ref);
+                const float lt = l[half] * __builtin_amdgcn_exp2f(m[half] - ref) + lo * __builtin_amdgcn_exp2f(mo - ref);
                 if (hl == 0) {
                     const int64_t o = ((int64_t)h * kL + half * 32 + l32) * a.nranges + range;
                     a.part_m[o] = mn;
@@ -154,7 +189,9 @@ __global__ __launch_bounds__(kThreads) void est_pass1_kernel(EstArgs a) {
     }
 }
 
-// One wave per (q head, row): merge the per-range (max, sum) partials.
+// One wave per (q head, row): merge the per-range (max, sum) partials into the
+// row's log2 normaliser m + log2(l) (scaled log2 units), so that
+// p = exp2(scale*log2(e)*z - normaliser).
 __global__ __launch_bounds__(256) void est_combine_kernel(EstArgs a) {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -177,104 +214,161 @@ __global__ __launch_bounds__(256) void est_combine_kernel(EstArgs a) {
         l = l * exp2f(m - base) + lo * exp2f(mo - base);
         m = mn;
     }
-    if (lane == 0) {
-        a.row_m[row] = m;
-        a.row_il[row] = l > 0.f ? 1.f / l : 0.f;
-    }
+    // every last-window row has at least one key, so l > 0
+    if (lane == 0) a.row_norm[row] = m + log2f(l);
 }
 
+// Pass 2: eight waves, two per q head; wave 2k + hf holds query rows 32 hf ..
+// 32 hf + 31 of head slot k (a wave's Q fragments and normalisers then fit in
+// half the registers, which gives two waves per SIMD).  The half-1 wave passes
+// its column and diagonal partials of tile t to the half-0 wave through LDS
+// (double buffered by tile parity); the half-0 wave adds them after the next
+// tile's barrier and writes the scores.
+constexpr int kThreads2 = 512;
+template <typename T> struct Pass2Smem {
+    static constexpr int kKBuf = sizeof(T) == 2 ? 2 : 1;     // fp32 tiles: single buffer (LDS size)
+    alignas(16) unsigned char k[kKBuf][KGeo<T>::kTileBytes];
+    float p[8][32 * kSkew];                                    // per-wave skewed p block
+    float x[2][4][3][64];                                      // half-1 partials: v, D1, D2
+};
+
 template <typename T>
-__global__ __launch_bounds__(kThreads) void est_pass2_kernel(EstArgs a) {
+__global__ __launch_bounds__(kThreads2) void est_pass2_kernel(EstArgs a) {
     using E = Elem<T>;
-    __shared__ EstSmem<T> sm;
-    __shared__ float pbuf[4][32 * kPP];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+    using Gm = KGeo<T>;
+    using Sm = Pass2Smem<T>;
+    __shared__ Sm sm;
+    const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hs = wave >> 1, hf = wave & 1;                    // head slot, row half
     const int range = blockIdx.x, g = blockIdx.y;
     const int G = a.hq / a.hkv;
     const int64_t n = a.n;
     const int64_t k0 = (int64_t)range * a.range_keys;
     const int64_t k1 = min(n, k0 + a.range_keys);
+    const int ntile = (int)((k1 - k0) / kTK);
     const T *kp = reinterpret_cast<const T *>(a.k) + (int64_t)g * n * kD;
-    float *pw = pbuf[wave];
-    const int nslot = (G + 3) / 4;
-    for (int slot = 0; slot < nslot; ++slot) {
-        const int hw = wave + 4 * slot;
+    const bool loader = wave < 4;                               // waves 0-3 copy the K tiles
+    uint32_t off[Gm::kPer];
+    copy_offsets<T>(off, lane);
+    float *pw = sm.p[wave];
+    // Skewed block: p of (row r, key e) at pw[r*kSkew + e - r + 31]; the cells
+    // never written (outside the parallelogram) stay zero.
+    for (int i = lane; i < 32 * kSkew; i += 64) pw[i] = 0.f;
+    // Lane t owns the tile diagonals D1 = t - 63 and D2 = t + 1 (D = R - e for
+    // global row R = 32 hf + r).  Diagonal D is column 32 hf + 31 - D; a column
+    // outside [0, 94] holds no element of this half.
+    const int c1 = hf * 32 + 94 - lane, c2 = hf * 32 + 30 - lane;
+    const float use1 = (c1 >= 0 && c1 <= 94) ? 1.f : 0.f, use2 = (c2 >= 0 && c2 <= 94) ? 1.f : 0.f;
+    const int col1 = min(max(c1, 0), 94), col2 = min(max(c2, 0), 94);
+    for (int slot = 0; slot < n_slots(G); ++slot) {
+        const int hw = hs + 4 * slot;
         const bool active = hw < G;
         const int h = g * G + (active ? hw : 0);
         const T *qp = reinterpret_cast<const T *>(a.q) + ((int64_t)h * n + (n - kL)) * kD;
-        typename E::frag qf[2][8];
-        float mrow[2], il[2];
+        // A operand of S = Q K^T: query 32 hf + l32, d = dk*16 + hl*8 + e
+        typename E::frag qf[8];
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
+        for (int dk = 0; dk < 8; ++dk) qf[dk] = E::load_frag(qp + (hf * 32 + l32) * kD + dk * 16 + hl * 8);
+        // normaliser of the 16 rows this lane holds: row 32 hf + jj*8 + hl*4 + i at jj*4 + i
+        float nrm[16];
 #pragma unroll
-            for (int dk = 0; dk < 8; ++dk)
-                qf[half][dk] = active ? E::load_frag(qp + (half * 32 + l32) * kD + dk * 16 + hl * 8)
-                                      : E::zero_frag();
-            const int64_t ri = (int64_t)h * kL + half * 32 + l32;
-            mrow[half] = active ? a.row_m[ri] : 0.f;          // scaled log2 units
-            il[half] = active ? a.row_il[ri] : 0.f;
-        }
+        for (int x = 0; x < 16; ++x) nrm[x] = a.row_norm[(int64_t)h * kL + hf * 32 + (x >> 2) * 8 + hl * 4 + (x & 3)];
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);        // Q and the normalisers have landed
         float *vout = a.v_score + (int64_t)h * n;
         float *sout = a.s_score + (int64_t)h * n;
         float carry = 0.f;
-        bool first = true;
-        for (int64_t base = k0; base < k1; base += kTK) {
-            __syncthreads();
-            load_k_tile<T>(sm.k, kp, base, tid);
-            __syncthreads();
-            const bool last = base + kTK > n - kL;
-            float col = 0.f, dg1 = 0.f, dg2 = 0.f;
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                if (active) {
-                    f32x16 s[2];
-                    tile_scores<T>(s, sm.k, qf[half], l32, hl);
-                    const int64_t prow = n - kL + half * 32 + l32;
-#pragma unroll
-                    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            const int e = kt * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
-                            float p = exp2f(fmaf(s[kt][i], a.scale_log2, -mrow[half])) * il[half];
-                            if (last && base + e > prow) p = 0.f;
-                            pw[l32 * kPP + e] = p;
-                        }
-                }
-                __syncthreads();
-                if (active) {
-                    // rows R = half*32 + r of the head's 64; diagonal d = R - e
-#pragma unroll 8
-                    for (int r = 0; r < 32; ++r) {
-                        col += pw[r * kPP + lane];
-                        const int e1 = half * 32 + r + 63 - lane;   // d = lane - 63
-                        if (e1 >= 0 && e1 < kTK) dg1 += pw[r * kPP + e1];
-                        const int e2 = half * 32 + r - lane - 1;    // d = lane + 1
-                        if (e2 >= 0 && e2 < kTK) dg2 += pw[r * kPP + e2];
-                    }
-                }
-                __syncthreads();
-            }
-            if (active) {
-                vout[base + lane] = col;
-                const int64_t A = n - kL - base;                 // offset of diagonal d = 0
-                if (lane == 63) {
-                    sout[A] = dg1;                               // d = 0 lies in this tile only
+        float v_own = 0.f, d1_own = 0.f, d2_own = 0.f;          // half-0 partials of the pending tile
+        // tile t's scores (half-0 wave): add the half-1 partials, write, carry
+        auto finish = [&](int t) {
+            const float *xs = &sm.x[t & 1][hs][0][0];
+            const float vt = v_own + xs[lane];
+            const float dg1 = d1_own + xs[64 + lane], dg2 = d2_own + xs[128 + lane];
+            const int64_t base = k0 + (int64_t)t * kTK;
+            vout[base + lane] = vt;
+            const int64_t A = n - kL - base;                     // offset of diagonal D = 0
+            if (lane == 63) {
+                sout[A] = dg1;                                   // D = 0 lies in this tile only
+            } else {
+                const int64_t o2 = A + lane + 1;                 // D = lane + 1
+                if (t > 0) {
+                    sout[o2] = dg2 + carry;
+                } else if (range == 0) {
+                    sout[o2] = dg2;                              // keys below 0 do not exist
                 } else {
-                    const int64_t o2 = A + lane + 1;             // d = lane + 1
-                    if (!first) {
-                        sout[o2] = dg2 + carry;
-                    } else if (range == 0) {
-                        sout[o2] = dg2;                          // keys below 0 do not exist
-                    } else {
-                        a.diag_hi[((int64_t)h * a.nranges + range) * 64 + lane] = dg2;
-                    }
-                    carry = dg1;                                 // d = lane - 63, finished by the next tile
+                    a.diag_hi[((int64_t)h * a.nranges + range) * 64 + lane] = dg2;
+                }
+                carry = dg1;                                     // D = lane - 63, finished by the next tile
+            }
+        };
+        // scores of tile t for this wave's 32 rows: p into the skewed block, the
+        // column sums (lane t: key t) and the two diagonal partials
+        auto tile = [&](const unsigned char *buf, int64_t base, auto masked) {
+            float vk[2] = {0.f, 0.f};
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                f32x16 sc;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sc[i] = 0.f;
+#pragma unroll
+                for (int dk = 0; dk < 8; ++dk) E::mma(sc, qf[dk], k_frag<T>(buf, kt, dk, l32, hl));
+                const int e = kt * 32 + l32;                      // key of this lane in the tile
+#pragma unroll
+                for (int x = 0; x < 16; ++x) {
+                    const int r = (x >> 2) * 8 + hl * 4 + (x & 3);
+                    float p = __builtin_amdgcn_exp2f(fmaf(sc[x], a.scale_log2, -nrm[x]));
+                    if constexpr (decltype(masked)::value)
+                        if (base + e > n - kL + hf * 32 + r) p = 0.f;
+                    vk[kt] += p;
+                    pw[r * kSkew + e - r + 31] = p;
                 }
             }
-            first = false;
+            float d1 = 0.f, d2 = 0.f;
+#pragma unroll 8
+            for (int r = 0; r < 32; ++r) {
+                d1 += pw[r * kSkew + col1];
+                d2 += pw[r * kSkew + col2];
+            }
+            // lanes l and l^32 hold the two 16-row halves of each key:
+            // v_permlane32_swap(old = vk[0], src = vk[1]) returns lanes 0-31 of
+            // vk[0] and of vk[1] in the first result and lanes 32-63 in the
+            // second, so lane t gets the 32-row sum of key t
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(vk[0]), __float_as_uint(vk[1]), false, false);
+            return f32x4{__uint_as_float(sw[0]) + __uint_as_float(sw[1]), d1 * use1, d2 * use2, 0.f};
+        };
+        __syncthreads();                            // the previous slot is done with every buffer
+        if (loader) start_tile<T>(sm.k[0], kp, k0, wave, off);
+        for (int t = 0; t < ntile; ++t) {
+            const int64_t base = k0 + (int64_t)t * kTK;
+            vm_wait<0>();
+            __syncthreads();                        // tile t visible; half-1 partials of t-1 visible
+            if (Sm::kKBuf == 2 && loader && t + 1 < ntile) start_tile<T>(sm.k[(t + 1) & 1], kp, base + kTK, wave, off);
+            if (active && hf == 0 && t > 0) finish(t - 1);
+            if (active) {
+                const unsigned char *buf = sm.k[Sm::kKBuf == 2 ? (t & 1) : 0];
+                const f32x4 r = base + kTK > n - kL ? tile(buf, base, std::true_type{}) : tile(buf, base, std::false_type{});
+                if (hf == 0) {
+                    v_own = r[0];
+                    d1_own = r[1];
+                    d2_own = r[2];
+                } else {
+                    float *xs = &sm.x[t & 1][hs][0][0];
+                    xs[lane] = r[0];
+                    xs[64 + lane] = r[1];
+                    xs[128 + lane] = r[2];
+                }
+            }
+            if (Sm::kKBuf == 1) {
+                __syncthreads();                    // every wave is done with the single tile buffer
+                if (loader && t + 1 < ntile) start_tile<T>(sm.k[0], kp, base + kTK, wave, off);
+            }
         }
-        if (active && lane < 63 && range != a.nranges - 1)
-            a.diag_lo[((int64_t)h * a.nranges + range) * 64 + lane] = carry;
+        __syncthreads();                            // half-1 partials of the last tile
+        if (active && hf == 0 && ntile > 0) {
+            finish(ntile - 1);
+            if (lane < 63 && range != a.nranges - 1)
+                a.diag_lo[((int64_t)h * a.nranges + range) * 64 + lane] = carry;
+        }
     }
 }
 
@@ -301,7 +395,7 @@ template <typename T> hipError_t launch_t(const EstArgs &a, hipStream_t s) {
     const int64_t rows = (int64_t)a.hq * kL;
     hipLaunchKernelGGL(est_combine_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(est_pass2_kernel<T>, grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(est_pass2_kernel<T>, grid, dim3(kThreads2), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t fix = (int64_t)(a.nranges - 1) * 63 * a.hq;
     if (fix > 0) {

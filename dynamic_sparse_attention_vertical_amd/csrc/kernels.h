@@ -30,7 +30,7 @@ struct EstArgs {
     int64_t range_keys;  // keys per workgroup range (multiple of 64)
     int32_t nranges;
     float *part_m, *part_l;      // [hq][64][nranges]
-    float *row_m, *row_il;       // [hq][64]
+    float *row_norm;             // [hq][64] per-row log2 normaliser (scaled max + log2 sum)
     float *v_score, *s_score;    // [hq][n]
     float *diag_hi, *diag_lo;    // [hq][nranges][64]
 };

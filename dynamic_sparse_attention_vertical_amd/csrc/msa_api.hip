@@ -54,20 +54,21 @@ float scale_of(const msa_problem *p) {
 
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Estimator work split: contiguous key ranges per workgroup, sized so the grid
-// has about 2048 workgroups.
+// Estimator work split: contiguous key ranges (256 .. 8192 keys) per workgroup,
+// about 512 workgroups over the kv heads: long enough ranges to amortise each
+// workgroup's set-up, enough workgroups for every CU.
 struct EstLayout {
     int64_t range_keys;
     int32_t nranges;
     int32_t nslices;
-    size_t off_part_m, off_part_l, off_row_m, off_row_il, off_hi, off_lo, off_v, off_s;
+    size_t off_part_m, off_part_l, off_row_norm, off_hi, off_lo, off_v, off_s;
     size_t off_hist, off_state, off_cnt, off_off, total;
 };
 
 EstLayout est_layout(const msa_problem *p) {
     EstLayout L;
     const int64_t n = p->seq_len;
-    int64_t rk = (n * p->n_kv_heads + 2047) / 2048;
+    int64_t rk = (n * p->n_kv_heads + 511) / 512;
     rk = ((rk + 63) / 64) * 64;
     if (rk < 256) rk = 256;
     if (rk > 8192) rk = 8192;
@@ -79,8 +80,7 @@ EstLayout est_layout(const msa_problem *p) {
     size_t o = 0;
     L.off_part_m = o; o = align_up(o + hq * 64 * L.nranges * 4);
     L.off_part_l = o; o = align_up(o + hq * 64 * L.nranges * 4);
-    L.off_row_m = o;  o = align_up(o + hq * 64 * 4);
-    L.off_row_il = o; o = align_up(o + hq * 64 * 4);
+    L.off_row_norm = o; o = align_up(o + hq * 64 * 4);
     L.off_hi = o;     o = align_up(o + hq * L.nranges * 64 * 4);
     L.off_lo = o;     o = align_up(o + hq * L.nranges * 64 * 4);
     L.off_v = o;      o = align_up(o + hq * (size_t)n * 4);
@@ -165,8 +165,7 @@ int msa_estimate_vs(const msa_problem *p, const void *q, const void *k, int32_t 
     e.nranges = L.nranges;
     e.part_m = at<float>(workspace, L.off_part_m);
     e.part_l = at<float>(workspace, L.off_part_l);
-    e.row_m = at<float>(workspace, L.off_row_m);
-    e.row_il = at<float>(workspace, L.off_row_il);
+    e.row_norm = at<float>(workspace, L.off_row_norm);
     e.diag_hi = at<float>(workspace, L.off_hi);
     e.diag_lo = at<float>(workspace, L.off_lo);
     e.v_score = v_score ? v_score : at<float>(workspace, L.off_v);
