@@ -1,20 +1,23 @@
 // Work-list construction for vertical-slash heads, gfx950.
 //
-// One thread per (q head, 64-row query block b): rows r0 = 64b .. r1 = 64b+63.
+// One lane per (q head, 64-row query block b): rows r0 = 64b .. r1 = 64b+63.
 // Each selected diagonal offset o <= r1 needs keys [max(0, r0-o), r1-o].
 // Visiting those ranges by descending o (so ascending start), with cov the end
 // of the last emitted block (initially 0): a range ending below cov is already
 // covered; otherwise emit a 64-wide block at max(start, cov).  Once cov passes
-// r1 every remaining range is covered, so the walk stops.  Then every selected
-// column j <= r1 outside the emitted blocks is listed, ascending (merge walk:
-// blocks and columns are both ascending).
+// r1 every remaining range is covered.  Every selected column j <= r1 outside
+// the emitted blocks is listed too, ascending.
+//
+// The offsets of a head are the same for every lane, so a wave walks them in
+// lock step (scalar loads, four at a time) and each lane applies the step to
+// its own cover.  Columns are merged into the same walk: when a block starts at
+// st, the columns in [cov, st) are exactly the ones no block covers.
 //
 // The pages ask that sparse work come in large contiguous blocks for the
 // matrix units and that the index be built online at small cost ("How to
 // optimise the TTFT of an 8B LLM with 1M tokens to 20 seconds", section on
 // co-designing algorithm and system, principles 1-2); the covering rule is
-// this library's reading of that.  The head's offsets and columns are staged
-// in LDS, shared by the 256 query blocks of the workgroup.
+// this library's reading of that.
 #include "common.h"
 #include "kernels.h"
 
@@ -22,63 +25,115 @@ namespace msa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kStageMax = 12288;     // int32 entries staged in LDS (48 KB)
+constexpr int kStageMax = 4096;      // columns staged in LDS (16 KB)
+
+__device__ __forceinline__ int4 load_uniform4(const int32_t *p) {   // p 16-byte aligned, wave-uniform
+    typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+    const i32x4 v = *(const __attribute__((address_space(4))) i32x4 *)(uintptr_t)p;
+    return make_int4(v.x, v.y, v.z, v.w);
+}
+
+constexpr int kRing = 32;            // per-lane LDS ring of block starts (two 16-entry lines)
 
 template <bool kStaged>
 __global__ __launch_bounds__(kThreads) void build_index_kernel(IndexArgs a) {
-    __shared__ int32_t st_s[kStaged ? kStageMax : 1];
+    __shared__ int32_t stage[kStaged ? kStageMax : 1];
+    __shared__ int32_t ring_all[kThreads * kRing];
     const int h = blockIdx.y;
-    const int64_t nqb = a.n / 64;
-    const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int nqb = (int)(a.n / 64);                 // sequence lengths are below 2^31
+    const int b = blockIdx.x * kThreads + threadIdx.x;
     const int32_t *S = a.s_idx + (int64_t)h * a.ks;
     const int32_t *V = a.v_idx + (int64_t)h * a.kv;
     if constexpr (kStaged) {
-        for (int i = threadIdx.x; i < a.ks; i += kThreads) st_s[i] = S[i];
+        for (int i = threadIdx.x; i < a.kv; i += kThreads) stage[i] = V[i];
         __syncthreads();
-        S = st_s;
+        V = stage;
     }
     if (b >= nqb) return;
-    const int64_t r0 = b * 64, r1 = r0 + 63;
-    // number of offsets <= r1 (offsets ascending)
+    const int r0 = b * 64, r1 = r0 + 63;
+    const int64_t item = (int64_t)h * nqb + b;
+    int32_t *blk = a.block_offset + item * a.cap_b;
+    int32_t *col = a.column_index + item * a.cap_c;
+
+    // offsets that matter to some lane of the wave: those <= r1 of its last item
+    const int wave_first = b - (int)(threadIdx.x & 63);
+    const int r1_max = min(wave_first + 63, nqb - 1) * 64 + 63;
     int lo = 0, hi = a.ks;
     while (lo < hi) {
         const int mid = (lo + hi) >> 1;
-        if ((int64_t)S[mid] <= r1) lo = mid + 1; else hi = mid;
+        if (load_uniform(S + mid) <= r1_max) lo = mid + 1; else hi = mid;
     }
-    const int64_t item = (int64_t)h * nqb + b;
-    int32_t *blk = a.block_offset + item * a.cap_b;
-    int64_t cov = 0;
-    int cnt = 0;
-    for (int i = lo - 1; i >= 0; --i) {
-        const int64_t o = S[i];
-        if (o < 0) continue;                       // out-of-range entries are ignored
-        const int64_t e = r1 - o;
-        if (e < cov) continue;
-        const int64_t s0 = r0 - o;
-        const int64_t st = s0 > cov ? s0 : cov;    // s0 may be negative: cov >= 0 covers it
-        if (cnt < a.cap_b) blk[cnt] = (int32_t)st;
+
+    // Block starts go to a per-lane LDS ring; a lane writes a completed,
+    // 16-entry-aligned run of its list as one 64-byte line (four 16-byte
+    // stores) instead of 16 scattered 4-byte stores.
+    int32_t *ring = ring_all + threadIdx.x * kRing;
+    const bool vec = (a.cap_b & 3) == 0;              // rows 16-byte aligned
+    int flushed = 0;                                  // entries of blk already written
+    auto flush_line = [&]() {                         // entries flushed .. flushed+15, all emitted
+        const int32_t *rl = ring + (flushed & (kRing - 1));
+        if (vec && flushed + 16 <= a.cap_b) {
+#pragma unroll
+            for (int k = 0; k < 16; k += 4)
+                *reinterpret_cast<int4 *>(blk + flushed + k) = make_int4(rl[k], rl[k + 1], rl[k + 2], rl[k + 3]);
+        } else {
+            for (int k = 0; k < 16; ++k)
+                if (flushed + k < a.cap_b) blk[flushed + k] = rl[k];
+        }
+        flushed += 16;
+    };
+    int cov = 0, cnt = 0, vp = 0, cc = 0;
+    // columns below `upto` (exclusive): the ones at or past cov are uncovered
+    auto columns_below = [&](int upto) {
+        while (vp < a.kv) {
+            const int j = V[vp];
+            if (j >= upto) break;
+            if (j >= cov) {
+                if (cc < a.cap_c) col[cc] = j;
+                ++cc;
+            }
+            ++vp;
+        }
+    };
+    auto step = [&](int o) {
+        if (o < 0 || o > r1 || cov > r1) return;     // not this lane's offset, or done
+        if (r1 - o < cov) return;                    // range already covered
+        const int st = max(r0 - o, cov);             // r0 - o may be negative: cov >= 0 covers it
+        columns_below(st);
+        ring[cnt & (kRing - 1)] = st;
         ++cnt;
         cov = st + 64;
-        if (cov > r1) break;
-    }
-    cnt = min(cnt, a.cap_b);
-    a.block_count[item] = cnt;
-
-    int32_t *col = a.column_index + item * a.cap_c;
-    int p = 0, cc = 0;
-    int64_t cur_end = cnt > 0 ? (int64_t)blk[0] + 63 : -1;
-    for (int i = 0; i < a.kv; ++i) {
-        const int64_t j = V[i];
-        if (j > r1) break;
-        if (j < 0) continue;
-        while (p < cnt && cur_end < j) {
-            ++p;
-            cur_end = p < cnt ? (int64_t)blk[p] + 63 : -1;
+    };
+    int i = lo - 1;
+    // unaligned head of the walk, one offset at a time, down to a multiple of 4
+    for (; i >= 0 && (i & 3) != 3; --i) step(load_uniform(S + i));
+    const bool aligned = ((uintptr_t)S & 15) == 0;
+    for (; i >= 3; i -= 4) {
+        int4 q;
+        if (aligned) {
+            q = load_uniform4(S + i - 3);
+        } else {
+            q = make_int4(load_uniform(S + i - 3), load_uniform(S + i - 2), load_uniform(S + i - 1), load_uniform(S + i));
         }
-        if (p < cnt && (int64_t)blk[p] <= j) continue;   // inside block p
-        if (cc < a.cap_c) col[cc] = (int32_t)j;
-        ++cc;
+        step(q.w);
+        step(q.z);
+        step(q.y);
+        step(q.x);
+        if ((i & 15) == 3) {
+            // at most 16 emissions since the last check: at most one line completed
+            if (cnt - flushed >= 16) flush_line();
+            if ((i & 63) == 3 && __builtin_amdgcn_ballot_w64(cov <= r1) == 0) break;   // every lane is done
+        }
     }
+    for (; i >= 0; --i) {
+        step(load_uniform(S + i));
+        if (cnt - flushed >= 16) flush_line();
+    }
+    // the unfinished line
+    for (int k = flushed; k < cnt; ++k)
+        if (k < a.cap_b) blk[k] = ring[k & (kRing - 1)];
+    columns_below(r1 + 1);
+    a.block_count[item] = min(cnt, a.cap_b);
     a.column_count[item] = min(cc, a.cap_c);
 }
 
@@ -87,7 +142,7 @@ __global__ __launch_bounds__(kThreads) void build_index_kernel(IndexArgs a) {
 hipError_t launch_build_index(const IndexArgs &a, hipStream_t s) {
     const int64_t nqb = a.n / 64;
     dim3 grid((unsigned)((nqb + kThreads - 1) / kThreads), a.hq);
-    if (a.ks <= kStageMax)
+    if (a.kv <= kStageMax)
         hipLaunchKernelGGL(build_index_kernel<true>, grid, dim3(kThreads), 0, s, a);
     else
         hipLaunchKernelGGL(build_index_kernel<false>, grid, dim3(kThreads), 0, s, a);
