@@ -227,8 +227,18 @@ def main():
     causal_pairs = hq * n * (n + 1) // 2
     att_tflops = exec_flop / (ms_att * 1e-3) / 1e12
 
+    # HBM-bound steps: algorithmic bytes over the measured time.  Estimator: K
+    # read by both passes plus the two score arrays written (the top-k
+    # selection inside the same call is timed with it).  Index builder: the
+    # entries and counts written.
+    est_bytes = 2 * hkv * n * 128 * 2 + 2 * hq * n * 4
+    idx_bytes = 4 * (int(plan.index.block_count.sum()) + int(plan.index.column_count.sum())) + 8 * hq * nqb
+    est_gbs = est_bytes / (ms_est * 1e-3) / 1e9
+    idx_gbs = idx_bytes / (ms_idx * 1e-3) / 1e9
     breakdown = {
         "ms_estimate": round(ms_est, 4), "ms_build_index": round(ms_idx, 4),
+        "estimate_gbs": round(est_gbs, 1), "estimate_hbm_frac": round(est_gbs / PEAK_HBM_GBS, 4),
+        "build_index_gbs": round(idx_gbs, 1), "build_index_hbm_frac": round(idx_gbs / PEAK_HBM_GBS, 4),
         "ms_sparse_prefill": round(ms_att, 4),
         "executed_tiles": tiles, "causal_tiles": causal_tiles,
         "executed_density": round(tiles / causal_tiles, 5),

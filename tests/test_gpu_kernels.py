@@ -97,6 +97,28 @@ def test_build_index_exact(hq, n, kv, ks, seed):
     compare_index(gidx, ridx, "build_index")
 
 
+@pytest.mark.parametrize("hq,n,kv,ks,cap_b,cap_c,seed", [
+    (2, 448, 5, 10, None, None, 5),       # minimal caps 7 and 5: rows not 16-byte aligned
+    (3, 1024, 40, 200, 37, 53, 6),        # caller caps above the minimum, odd
+    (2, 2048, 30, 2000, 33, 30, 7),       # many blocks per item, odd row pitch
+])
+def test_build_index_odd_capacities(hq, n, kv, ks, cap_b, cap_c, seed):
+    vi, si = random_sets(hq, n, kv, ks, seed)
+    ridx = oracle.build_index(vi, si, n)
+    mb, mc = msa.index_caps(n, kv, ks)
+    out = msa.alloc_index(hq, n, cap_b or mb, cap_c or mc)
+    gidx = msa.build_index(*cuda(torch.from_numpy(vi), torch.from_numpy(si)), n, out=out)
+    compare_index(gidx, ridx, "build_index odd caps")
+
+
+def test_build_index_many_columns():
+    # more selected columns than the kernel stages in LDS
+    vi, si = random_sets(2, 8192, 5000, 120, 8)
+    ridx = oracle.build_index(vi, si, 8192)
+    gidx = msa.build_index(*cuda(torch.from_numpy(vi), torch.from_numpy(si)), 8192)
+    compare_index(gidx, ridx, "build_index many columns")
+
+
 def test_build_index_a_shape():
     n = 64 * 120
     av, as_ = oracle.a_shape_sets(n, 128, 4096)
