@@ -70,6 +70,8 @@ template <typename T> struct AttnStage {
 // other.  Consecutive ids are dispatched round-robin over the XCDs, so all
 // XCDs stream the same kv head at once through the shared last-level cache
 // (measured: as fast as or faster than pinning kv heads to XCDs).
+// With kH q heads per workgroup, the workgroup's "head" is a group of kH
+// consecutive q heads (G / kH such groups per kv head).
 __device__ __forceinline__ void item_of_block(int64_t bid, int64_t nqb, int G, int &h, int64_t &b) {
     const int64_t per_g = (int64_t)G * nqb;
     const int64_t g = bid / per_g, rem = bid % per_g;
@@ -120,25 +122,28 @@ struct ChunkSrc {
     int c0;
 };
 
-// Per-lane constants of the chunk copies.  A chunk (32 rows) is moved as
-// kPer 1 KB slots per wave: wave w moves chunk rows 16w .. 16w+15; in slot i,
-// lane l writes the 16-byte physical chunk l % kChunks of row i*kRowsPerSlot +
-// l / kChunks and so reads the logical chunk that the swizzle puts there.
-// Rows 16w + r of either half of a tile have the swizzle of r (16 | row0), so
-// the fast-path offsets are the same for every chunk.
-template <typename T> struct CopyLanes {
-    static constexpr int kPer = 16 * Geo<T>::kRowBytes / 1024;        // 4 (bf16) / 8 (fp32)
+// Per-lane constants of the chunk copies.  A chunk (32 rows) is moved by the
+// 2 kH waves of the workgroup, kRpw = 16 / kH rows each (wave w: chunk rows
+// w kRpw .. w kRpw + kRpw - 1) as kPer 1 KB slots; in slot i, lane l writes the
+// 16-byte physical chunk l % kChunks of row i*kRowsPerSlot + l / kChunks and so
+// reads the logical chunk that the swizzle puts there.  The swizzles depend on
+// row & 15 and row & 3, and 16 divides 32 half, so the fast-path offsets of a
+// wave are the same for every chunk.
+template <typename T, int kH> struct CopyLanes {
+    static constexpr int kRpw = 16 / kH;                                // rows per wave and chunk
+    static constexpr int kPer = kRpw * Geo<T>::kRowBytes / 1024;        // 1 KB copies per wave and chunk
     uint32_t k[kPer], v[kPer];      // fast path: byte offset from the wave's first row
     int sub, phys;
-    __device__ __forceinline__ void init(int lane) {
+    __device__ __forceinline__ void init(int lane, int wave) {
         using Gm = Geo<T>;
         sub = lane / Gm::kChunks;
         phys = lane % Gm::kChunks;
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int r = i * Gm::kRowsPerSlot + sub;
-            k[i] = (uint32_t)(r * Gm::kRowBytes + ((phys ^ Gm::k_swz(r)) << 4));
-            v[i] = (uint32_t)(r * Gm::kRowBytes + ((phys ^ Gm::v_swz(r)) << 4));
+            const int row = wave * kRpw + r;                            // row in the chunk
+            k[i] = (uint32_t)(r * Gm::kRowBytes + ((phys ^ Gm::k_swz(row)) << 4));
+            v[i] = (uint32_t)(r * Gm::kRowBytes + ((phys ^ Gm::v_swz(row)) << 4));
         }
     }
 };
@@ -152,19 +157,25 @@ template <typename T> struct CopyLanes {
 // row, which the softmax mask gives weight zero (its values are finite).  The
 // keys of a column chunk come from the list for K, and from LDS for V (recorded
 // when its K was started).
-template <typename T, bool kIsV>
-__device__ __forceinline__ void load_chunk(const CopyLanes<T> &cl, uint32_t lds_wave, const T *src_rows,
+template <typename T, int kH, bool kIsV>
+__device__ __forceinline__ void load_chunk(const CopyLanes<T, kH> &cl, uint32_t lds_wave, const T *src_rows,
                                            const ChunkSrc &src, int half, int wave, int n, const int32_t *clist,
                                            int ncol, const int32_t *keys_lds) {
     using Gm = Geo<T>;
-    constexpr int kPer = CopyLanes<T>::kPer;
+    constexpr int kPer = CopyLanes<T, kH>::kPer;
+    constexpr int kRpw = CopyLanes<T, kH>::kRpw;
     const char *rows = reinterpret_cast<const char *>(src_rows);
     const uint32_t l0 = lds_wave + half * 32 * Gm::kRowBytes;
     const uint32_t *off = kIsV ? cl.v : cl.k;
     if (src.fast) {
-        const char *tb = rows + (int64_t)(src.base + wave * 16) * Gm::kRowBytes;
+        const char *tb = rows + (int64_t)(src.base + wave * kRpw) * Gm::kRowBytes;
+        if constexpr (kPer % 4 == 0) {
 #pragma unroll
-        for (int i = 0; i < kPer; i += 4) dma_x4(tb, off[i], off[i + 1], off[i + 2], off[i + 3], l0 + i * 1024);
+            for (int i = 0; i < kPer; i += 4) dma_x4(tb, off[i], off[i + 1], off[i + 2], off[i + 3], l0 + i * 1024);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) dma_x1(tb, off[i], l0 + i * 1024);
+        }
         return;
     }
     // all key lookups first: each copy below is a compiler barrier for memory
@@ -172,25 +183,30 @@ __device__ __forceinline__ void load_chunk(const CopyLanes<T> &cl, uint32_t lds_
     int key[kPer];
     if (src.is_col && kIsV) {
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) key[i] = keys_lds[wave * 16 + i * Gm::kRowsPerSlot + cl.sub];
+        for (int i = 0; i < kPer; ++i) key[i] = keys_lds[wave * kRpw + i * Gm::kRowsPerSlot + cl.sub];
     } else if (src.is_col) {
 #pragma unroll
         for (int i = 0; i < kPer; ++i)
-            key[i] = clist[min(src.c0 + wave * 16 + i * Gm::kRowsPerSlot + cl.sub, ncol - 1)];
+            key[i] = clist[min(src.c0 + wave * kRpw + i * Gm::kRowsPerSlot + cl.sub, ncol - 1)];
     } else {
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) key[i] = src.base + wave * 16 + i * Gm::kRowsPerSlot + cl.sub;
+        for (int i = 0; i < kPer; ++i) key[i] = src.base + wave * kRpw + i * Gm::kRowsPerSlot + cl.sub;
     }
     const char *a[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-        const int r = i * Gm::kRowsPerSlot + cl.sub;
+        const int row = wave * kRpw + i * Gm::kRowsPerSlot + cl.sub;    // row in the chunk
         const int kc = min(max(key[i], 0), n - 1);
-        const int swz = kIsV ? Gm::v_swz(r) : Gm::k_swz(r);
+        const int swz = kIsV ? Gm::v_swz(row) : Gm::k_swz(row);
         a[i] = rows + (int64_t)kc * Gm::kRowBytes + ((cl.phys ^ swz) << 4);
     }
+    if constexpr (kPer % 4 == 0) {
 #pragma unroll
-    for (int i = 0; i < kPer; i += 4) dma_x4(a[i], a[i + 1], a[i + 2], a[i + 3], l0 + i * 1024);
+        for (int i = 0; i < kPer; i += 4) dma_x4(a[i], a[i + 1], a[i + 2], a[i + 3], l0 + i * 1024);
+    } else {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) dma_x1(a[i], l0 + i * 1024);
+    }
 }
 
 // K fragment (A operand of S^T = K Q^T): row kt*32 + l32, d = dk*16 + hl*8 .. +7
@@ -257,8 +273,10 @@ __device__ __forceinline__ typename Elem<T>::frag v_frag(const AttnStage<T> &st,
 // step computes an S that is never used (from K rows still in LDS), which
 // keeps the step free of branches around the matrix work.
 // fp32 (a checking path) uses the same scheme with 64 KB of LDS.
-template <typename T, bool kDense>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1, sizeof(T) == 2 ? 2 : 1)))
+// kH q heads of one kv group per workgroup (2 kH waves) share every K/V copy;
+// used by the dense kernel, whose heads all walk the same tiles.
+template <typename T, bool kDense, int kH>
+__global__ __launch_bounds__(kThreads * kH) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1, sizeof(T) == 2 ? 2 : 1)))
 void attn_fwd_kernel(AttnArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the body uses gfx950-only LDS builtins
     using E = Elem<T>;
@@ -272,12 +290,13 @@ void attn_fwd_kernel(AttnArgs a) {
     const int n32 = (int)n;                          // below 2^31
     const int64_t nqb = n / kBQ;
     const int G = a.hq / a.hkv;
-    int h;
+    int hgrp;
     int64_t b;
-    item_of_block(blockIdx.x, nqb, G, h, b);
+    item_of_block(blockIdx.x, nqb, G / kH, hgrp, b);
+    const int h = hgrp * kH + (wave >> 1);           // this wave's q head
     const int g = h / G;
     const int r0 = (int)b * kBQ;
-    const int qrow = r0 + wave * 32 + l32;
+    const int qrow = r0 + (wave & 1) * 32 + l32;
 
     const T *qp = reinterpret_cast<const T *>(a.q) + ((int64_t)h * n) * kD;
     const T *kp = reinterpret_cast<const T *>(a.k) + ((int64_t)g * n) * kD;
@@ -316,16 +335,16 @@ void attn_fwd_kernel(AttnArgs a) {
         return s;
     };
     // start K of chunk c (and record a column chunk's keys for its mask)
-    CopyLanes<T> cl;
-    cl.init(lane);
-    const uint32_t lds_k = lds_addr(st.k) + wave * 16 * Geo<T>::kRowBytes;
-    const uint32_t lds_v = lds_addr(st.v) + wave * 16 * Geo<T>::kRowBytes;
+    CopyLanes<T, kH> cl;
+    cl.init(lane, wave);
+    const uint32_t lds_k = lds_addr(st.k) + wave * CopyLanes<T, kH>::kRpw * Geo<T>::kRowBytes;
+    const uint32_t lds_v = lds_addr(st.v) + wave * CopyLanes<T, kH>::kRpw * Geo<T>::kRowBytes;
     auto start_k = [&](int c, const ChunkSrc &s) {
         if (!s.fast && s.is_col && tid < 32) st.kidx[c & 3][tid] = s.c0 + tid < ncol ? clist[s.c0 + tid] : -1;
-        load_chunk<T, false>(cl, lds_k, kp, s, c & 1, wave, n32, clist, ncol, nullptr);
+        load_chunk<T, kH, false>(cl, lds_k, kp, s, c & 1, wave, n32, clist, ncol, nullptr);
     };
     auto start_v = [&](int c, const ChunkSrc &s) {
-        load_chunk<T, true>(cl, lds_v, vp, s, c & 1, wave, n32, clist, ncol, st.kidx[c & 3]);
+        load_chunk<T, kH, true>(cl, lds_v, vp, s, c & 1, wave, n32, clist, ncol, st.kidx[c & 3]);
     };
 
     // Q fragments (B operand of S^T = K Q^T): query qrow, d = dk*16 + hl*8 + e
@@ -488,11 +507,22 @@ void attn_fwd_kernel(AttnArgs a) {
 #endif
 }
 
-template <typename T, bool kDense> hipError_t launch(const AttnArgs &a, hipStream_t s) {
-    const int64_t total = (int64_t)a.hq * (a.n / kBQ);
+template <typename T, bool kDense, int kH> hipError_t launch_h(const AttnArgs &a, hipStream_t s) {
+    const int64_t total = (int64_t)(a.hq / kH) * (a.n / kBQ);
     if (total == 0) return hipSuccess;
-    hipLaunchKernelGGL((attn_fwd_kernel<T, kDense>), dim3((unsigned)total), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, kDense, kH>), dim3((unsigned)total), dim3(kThreads * kH), 0, s, a);
     return hipGetLastError();
+}
+
+// Sparse: one q head per workgroup (each head has its own work lists).  Dense:
+// up to four q heads of a kv group per workgroup, sharing every K/V tile.
+template <typename T, bool kDense> hipError_t launch(const AttnArgs &a, hipStream_t s) {
+    if constexpr (kDense) {
+        const int G = a.hq / a.hkv;
+        if (G % 4 == 0) return launch_h<T, true, 4>(a, s);
+        if (G % 2 == 0) return launch_h<T, true, 2>(a, s);
+    }
+    return launch_h<T, kDense, 1>(a, s);
 }
 
 }  // namespace

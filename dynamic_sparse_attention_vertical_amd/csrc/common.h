@@ -165,6 +165,20 @@ __device__ __forceinline__ void dma_x4(const void *sbase, uint32_t v0, uint32_t 
         "global_load_lds_dwordx4 %3, %4" ::"v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(to_sgpr(sbase)), "s"(lds)
         : "memory", "m0", "scc");
 }
+// One 1 KB copy (uniform base in SGPRs plus a per-lane offset):
+__device__ __forceinline__ void dma_x1(const void *sbase, uint32_t v0, uint32_t lds) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %0, %1" ::"v"(v0), "s"(to_sgpr(sbase)), "s"(lds)
+        : "memory", "m0");
+}
+// One 1 KB copy from per-lane 64-bit addresses:
+__device__ __forceinline__ void dma_x1(const void *a0, uint32_t lds) {
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "global_load_lds_dwordx4 %0, off" ::"v"(a0), "s"(lds)
+        : "memory", "m0");
+}
 // Per-lane 64-bit addresses:
 __device__ __forceinline__ void dma_x4(const void *a0, const void *a1, const void *a2, const void *a3, uint32_t lds) {
     asm volatile(
