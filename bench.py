@@ -169,12 +169,11 @@ def main():
 
     import torch
     import dynamic_sparse_attention_vertical_amd as msa
-    from dynamic_sparse_attention_vertical_amd.layer import LayerPlan
+    from dynamic_sparse_attention_vertical_amd.layer import LayerPlan, MixedPlan, mixed_index
     from synth import WORKLOADS, make_inputs
 
     w = WORKLOADS[args.workload]
-    if w.head_patterns:
-        raise SystemExit("bench.py times vertical-slash layers; use a vertical-slash workload")
+    mixed = bool(w.head_patterns)
     n, hq, hkv = w.seq_len, w.n_q_heads, w.n_kv_heads
     log(f"[bench] workload {w.name}: {hq}q/{hkv}kv heads, N={n}, k={w.vertical_topk}/{w.slash_topk}")
     t0 = time.perf_counter()
@@ -182,20 +181,32 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] inputs generated on the GPU in {time.perf_counter() - t0:.1f} s")
     q, k, v = x["q"], x["k"], x["v"]
-    plan = LayerPlan(hq, hkv, n, w.vertical_topk, w.slash_topk, "cuda", q.dtype)
+    if mixed:
+        # heads with three patterns (A-shape, vertical-slash, block-sparse): all
+        # work lists are built in one stage (timed as "estimate"), then one
+        # sparse prefill over all heads
+        plan = MixedPlan(w.head_patterns, hkv, n, w.vertical_topk, w.slash_topk, w.sink, w.window, w.bs_topk)
+    else:
+        plan = LayerPlan(hq, hkv, n, w.vertical_topk, w.slash_topk, "cuda", q.dtype)
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        msa.estimate_vs(q, k, w.vertical_topk, w.slash_topk, workspace=plan.workspace, v_idx=plan.v_idx,
-                        s_idx=plan.s_idx, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-        msa.build_index(plan.v_idx, plan.s_idx, n, out=plan.index, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
+        if mixed:
+            mixed_index(q, k, plan, stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+                ev[2].record(stream)
+        else:
+            msa.estimate_vs(q, k, w.vertical_topk, w.slash_topk, workspace=plan.workspace, v_idx=plan.v_idx,
+                            s_idx=plan.s_idx, stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+            msa.build_index(plan.v_idx, plan.s_idx, n, out=plan.index, stream=stream)
+            if ev is not None:
+                ev[2].record(stream)
         msa.sparse_prefill(q, k, v, plan.index, out=out, stream=stream)
         if ev is not None:
             ev[3].record(stream)
@@ -231,21 +242,26 @@ def main():
     # read by both passes plus the two score arrays written (the top-k
     # selection inside the same call is timed with it).  Index builder: the
     # entries and counts written.
-    est_bytes = 2 * hkv * n * 128 * 2 + 2 * hq * n * 4
-    idx_bytes = 4 * (int(plan.index.block_count.sum()) + int(plan.index.column_count.sum())) + 8 * hq * nqb
-    est_gbs = est_bytes / (ms_est * 1e-3) / 1e9
-    idx_gbs = idx_bytes / (ms_idx * 1e-3) / 1e9
-    breakdown = {
-        "ms_estimate": round(ms_est, 4), "ms_build_index": round(ms_idx, 4),
-        "estimate_gbs": round(est_gbs, 1), "estimate_hbm_frac": round(est_gbs / PEAK_HBM_GBS, 4),
-        "build_index_gbs": round(idx_gbs, 1), "build_index_hbm_frac": round(idx_gbs / PEAK_HBM_GBS, 4),
+    if mixed:
+        breakdown = {"ms_work_lists": round(ms_est + ms_idx, 4),
+                     "head_patterns": {p: sum(x == p for x in w.head_patterns) for p in ("a", "vs", "bs")}}
+    else:
+        est_bytes = 2 * hkv * n * 128 * 2 + 2 * hq * n * 4
+        idx_bytes = 4 * (int(plan.index.block_count.sum()) + int(plan.index.column_count.sum())) + 8 * hq * nqb
+        est_gbs = est_bytes / (ms_est * 1e-3) / 1e9
+        idx_gbs = idx_bytes / (ms_idx * 1e-3) / 1e9
+        breakdown = {
+            "ms_estimate": round(ms_est, 4), "ms_build_index": round(ms_idx, 4),
+            "estimate_gbs": round(est_gbs, 1), "estimate_hbm_frac": round(est_gbs / PEAK_HBM_GBS, 4),
+            "build_index_gbs": round(idx_gbs, 1), "build_index_hbm_frac": round(idx_gbs / PEAK_HBM_GBS, 4)}
+    breakdown.update({
         "ms_sparse_prefill": round(ms_att, 4),
         "executed_tiles": tiles, "causal_tiles": causal_tiles,
         "executed_density": round(tiles / causal_tiles, 5),
         "useful_density": round(pairs / causal_pairs, 5),
         "executed_tflop": round(exec_flop / 1e12, 4),
         "sparse_prefill_tflops": round(att_tflops, 2),
-    }
+    })
     if not args.no_dense:
         dense_out = torch.empty_like(q)
         msa.dense_prefill(q, k, v, out=dense_out, stream=stream)
@@ -284,7 +300,9 @@ def main():
                      "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(w.name)},
     }
-    if not args.no_cpu_baseline:
+    if mixed:
+        log("[bench] the CPU oracle baseline is sampled on vertical-slash layers only")
+    elif not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
         res["cpu_baseline"] = cpu_baseline(x, plan, w, args.cpu_seconds)
     print(json.dumps(res), flush=True)

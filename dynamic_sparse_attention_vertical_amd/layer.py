@@ -118,13 +118,16 @@ class MixedPlan:
         ws_vs = max([msa.estimate_vs_workspace_bytes(h1 - h0, (h1 - h0) // G, n, self.dtype)
                      for h0, h1 in _runs(self.patterns, "vs")] or [0])
         self.workspace = torch.empty(max(ws_vs, 1), dtype=torch.uint8, device=self.device)
+        ws_bs = max([msa.estimate_bs_workspace_bytes(h1 - h0, (h1 - h0) // G, n, self.dtype)
+                     for h0, h1 in _runs(self.patterns, "bs")] or [0])
+        self.bs_workspace = torch.empty(max(ws_bs, 1), dtype=torch.uint8, device=self.device)
 
 
-def mixed_layer(q, k, v, plan: MixedPlan, *, out: torch.Tensor | None = None, lse=None, stream=None):
-    """Per-head patterns in one layer: 'a' (static sink + window index), 'vs'
-    (online vertical-slash estimate) and 'bs' (online block-sparse estimate);
-    then a single sparse prefill over all heads.  Head runs must align with kv
-    groups."""
+def mixed_index(q, k, plan: MixedPlan, *, stream=None) -> msa.IndexTensors:
+    """Work lists of every head of a mixed layer: 'a' (static sink + window
+    index), 'vs' (online vertical-slash estimate) and 'bs' (online
+    block-sparse estimate), written into plan.index.  Head runs must align
+    with kv groups."""
     hq, n = q.shape[0], q.shape[1]
     G = hq // k.shape[0]
     vs_row = 0
@@ -145,5 +148,12 @@ def mixed_layer(q, k, v, plan: MixedPlan, *, out: torch.Tensor | None = None, ls
                                 v_idx=vi, s_idx=si, stream=stream)
                 msa.build_index(vi, si, n, out=sub, stream=stream)
             else:
-                msa.estimate_bs(qs, ks_, plan.bs_topk, out=sub, stream=stream)
+                msa.estimate_bs(qs, ks_, plan.bs_topk, out=sub, workspace=plan.bs_workspace, stream=stream)
+    return plan.index
+
+
+def mixed_layer(q, k, v, plan: MixedPlan, *, out: torch.Tensor | None = None, lse=None, stream=None):
+    """Per-head patterns in one layer (see mixed_index), then a single sparse
+    prefill over all heads."""
+    mixed_index(q, k, plan, stream=stream)
     return msa.sparse_prefill(q, k, v, plan.index, out=out, lse=lse, stream=stream)

@@ -151,6 +151,11 @@ def estimate_vs_workspace_bytes(n_q_heads: int, n_kv_heads: int, seq_len: int, d
     return int(load().msa_estimate_vs_workspace(ctypes.byref(p), LAST_Q, 1, 1))
 
 
+def estimate_bs_workspace_bytes(n_q_heads: int, n_kv_heads: int, seq_len: int, dtype=torch.bfloat16) -> int:
+    p = problem(n_q_heads, n_kv_heads, seq_len, MSA_BF16 if dtype == torch.bfloat16 else MSA_F32)
+    return int(load().msa_estimate_bs_workspace(ctypes.byref(p), BLOCK))
+
+
 def estimate_vs(q: torch.Tensor, k: torch.Tensor, vertical_topk: int, slash_topk: int, *,
                 last_q: int = LAST_Q, v_score: torch.Tensor | None = None,
                 s_score: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
