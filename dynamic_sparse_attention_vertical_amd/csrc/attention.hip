@@ -38,10 +38,9 @@ namespace {
 constexpr int kD = 128;          // head_dim
 constexpr int kBQ = 64;          // query rows per work item
 constexpr int kBK = 64;          // keys per tile
-constexpr int kThreads = 128;    // two waves
+constexpr int kThreads = 128;    // two waves per q head of a workgroup
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
-
 
 template <typename T> struct Geo {
     static constexpr int kRowBytes = kD * (int)sizeof(T);      // 256 (bf16) / 512 (fp32)
@@ -69,9 +68,9 @@ template <typename T> struct AttnStage {
 // heavy (late) query blocks first, the G q heads of a block next to each
 // other.  Consecutive ids are dispatched round-robin over the XCDs, so all
 // XCDs stream the same kv head at once through the shared last-level cache
-// (measured: as fast as or faster than pinning kv heads to XCDs).
-// With kH q heads per workgroup, the workgroup's "head" is a group of kH
-// consecutive q heads (G / kH such groups per kv head).
+// (measured: as fast as or faster than pinning kv heads to XCDs).  For a
+// workgroup serving kH q heads, G here is the number of kH-head groups per kv
+// head and h indexes those groups.
 __device__ __forceinline__ void item_of_block(int64_t bid, int64_t nqb, int G, int &h, int64_t &b) {
     const int64_t per_g = (int64_t)G * nqb;
     const int64_t g = bid / per_g, rem = bid % per_g;
