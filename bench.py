@@ -46,10 +46,10 @@ def attn_src_sha():
 
 
 def measured_traffic(workload):
-    """HBM bytes per sparse-prefill launch from the committed rocprofv3 counter
-    runs (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter's reading
-    for a plain copy of known size), or None if absent or taken on a different
-    kernel source."""
+    """HBM bytes of one step's sparse prefill (the sum over its key-phase
+    launches) from the committed rocprofv3 counter runs (FETCH_SIZE and
+    WRITE_SIZE, each scaled by the same counter's reading for a plain copy of
+    known size), or None if absent or taken on a different kernel source."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
@@ -57,7 +57,14 @@ def measured_traffic(workload):
     entry = rec.get("workloads", {}).get(workload)
     if not entry or rec.get("attention_src_sha") != attn_src_sha():
         return None
-    return entry["fetch_kib"] * 1024 * rec["fetch_calib"] + entry["write_kib"] * 1024 * rec["write_calib"]
+    return entry["fetch_kib_per_step"] * 1024 * rec["fetch_calib"] + \
+        entry["write_kib_per_step"] * 1024 * rec["write_calib"]
+
+
+def phase_launches(n):
+    """Launches of one sparse prefill at the default phase length."""
+    from dynamic_sparse_attention_vertical_amd.msa import DEFAULT_PHASE_KEYS
+    return max(1, -(-n // DEFAULT_PHASE_KEYS))
 
 
 def copy_calibration(gib):
@@ -207,7 +214,7 @@ def main():
             msa.build_index(plan.v_idx, plan.s_idx, n, out=plan.index, stream=stream)
             if ev is not None:
                 ev[2].record(stream)
-        msa.sparse_prefill(q, k, v, plan.index, out=out, stream=stream)
+        msa.sparse_prefill(q, k, v, plan.index, out=out, workspace=plan.attn_workspace, stream=stream)
         if ev is not None:
             ev[3].record(stream)
 
@@ -295,7 +302,10 @@ def main():
         "config": {"workload": w.name, "seq_len": n, "q_heads": hq, "kv_heads": hkv, "head_dim": 128,
                    "vertical_topk": w.vertical_topk, "slash_topk": w.slash_topk, "last_q": 64, "block": 64},
         "breakdown": breakdown,
+        # the step's sparse prefill is n / phase_keys launches of one kernel
+        # (key phases): achieved = the step's executed FLOPs over their summed time
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel<bf16, sparse>",
+                     "launches_per_step": phase_launches(n),
                      "achieved": round(att_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(w.name)},

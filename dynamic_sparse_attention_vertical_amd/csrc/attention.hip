@@ -30,6 +30,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <climits>
+
 #include <type_traits>
 
 namespace msa {
@@ -39,6 +41,7 @@ constexpr int kD = 128;          // head_dim
 constexpr int kBQ = 64;          // query rows per work item
 constexpr int kBK = 64;          // keys per tile
 constexpr int kThreads = 128;    // two waves per q head of a workgroup
+constexpr int kStateFloats = 64 * 64 + 2 * 64;   // sparse phase state of one wave: O, max, sum
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
@@ -260,6 +263,29 @@ __device__ __forceinline__ typename Elem<T>::frag v_frag(const AttnStage<T> &st,
 }
 
 
+// First index i in [0, cnt) with list[i] >= key (cnt if none) in an ascending
+// list.  The 64 lanes of the wave probe 64 evenly spaced entries per round and
+// the ballot of the comparisons narrows the range 64-fold, so a list of up to
+// 4096 entries takes two rounds of loads.
+__device__ __forceinline__ int lower_bound_wave(const int32_t *list, int cnt, int key, int lane) {
+    int lo = 0, hi = cnt;
+    while (lo < hi) {
+        const int step = (hi - lo + 63) >> 6;
+        const int pos = lo + lane * step;
+        const bool ge = pos < hi && list[pos] >= key;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(ge);
+        if (m != 0) {
+            const int f = __builtin_ctzll(m);
+            const int nhi = lo + f * step;
+            lo = f > 0 ? lo + (f - 1) * step + 1 : nhi;
+            hi = nhi;
+        } else {
+            lo += ((hi - 1 - lo) / step) * step + 1;    // past the last probe
+        }
+    }
+    return lo;
+}
+
 // One 64-key tile of K and one of V in LDS (33 KB for bf16: four workgroups
 // and two waves per SIMD), each holding two 32-key chunks; chunk c lives in
 // half c % 2.  Step c of the pipeline (after a wait and a barrier):
@@ -291,7 +317,9 @@ void attn_fwd_kernel(AttnArgs a) {
     const int G = a.hq / a.hkv;
     int hgrp;
     int64_t b;
-    item_of_block(blockIdx.x, nqb, G / kH, hgrp, b);
+    const int64_t qb0 = kDense ? 0 : a.qb_lo;         // first query block of this launch
+    item_of_block(blockIdx.x, nqb - qb0, G / kH, hgrp, b);
+    b += qb0;
     const int h = hgrp * kH + (wave >> 1);           // this wave's q head
     const int g = h / G;
     const int r0 = (int)b * kBQ;
@@ -312,7 +340,30 @@ void attn_fwd_kernel(AttnArgs a) {
         ncol = min(max(a.column_count[item], 0), a.cap_c);
         blist = a.block_offset + item * a.cap_b;
         clist = a.column_index + item * a.cap_c;
+        if (a.ws != nullptr) {
+            // one phase of several: the block tiles starting in [k_lo, k_hi)
+            // and the columns in it (the lists are ascending); the first phase
+            // also takes everything below, the last everything above
+            const int b0 = a.k_lo == INT_MIN ? 0 : lower_bound_wave(blist, nblk, a.k_lo, lane);
+            const int b1 = a.k_hi == INT_MAX ? nblk : lower_bound_wave(blist, nblk, a.k_hi, lane);
+            const int c0 = a.k_lo == INT_MIN ? 0 : lower_bound_wave(clist, ncol, a.k_lo, lane);
+            const int c1 = a.k_hi == INT_MAX ? ncol : lower_bound_wave(clist, ncol, a.k_hi, lane);
+            blist += b0;
+            nblk = max(b1 - b0, 0);
+            clist += c0;
+            ncol = max(c1 - c0, 0);
+        }
     }
+    // phases: the first starts from an empty state, and the query block's
+    // output is written in the phase holding its own rows (no later key is
+    // visible to it); other phases keep the state in ws
+    const bool first = kDense || a.ws == nullptr || a.k_lo == INT_MIN;
+    const bool final_ = kDense || a.ws == nullptr || (int64_t)r0 + kBQ - 1 < (int64_t)a.k_hi;
+    if (!first && !final_ && nblk == 0 && ncol == 0) return;    // nothing in this phase
+    // this wave's state: 16 float4 of O per lane, then the lane's max and sum
+    float *sw = nullptr;
+    if constexpr (!kDense)
+        if (a.ws != nullptr) sw = a.ws + ((int64_t)h * nqb + b) * (2 * kStateFloats) + wave * kStateFloats;
     // an even number of chunks (column chunks padded with an empty one), so
     // that the steps come in pairs
     const int nchunk = 2 * (nblk + (ncol + kBK - 1) / kBK);
@@ -359,6 +410,18 @@ void attn_fwd_kernel(AttnArgs a) {
     // running row max kept in scaled log2 units as a stored fp32 value, so an
     // unchanged max gives a rescale factor of exactly 1
     float mb_i = -INFINITY, l_i = 0.f;
+    if (!first) {
+#pragma unroll
+        for (int v4 = 0; v4 < 16; ++v4) {
+            const float4 x = *reinterpret_cast<const float4 *>(sw + (v4 * 64 + lane) * 4);
+            o[v4 >> 2][(v4 & 3) * 4 + 0] = x.x;
+            o[v4 >> 2][(v4 & 3) * 4 + 1] = x.y;
+            o[v4 >> 2][(v4 & 3) * 4 + 2] = x.z;
+            o[v4 >> 2][(v4 & 3) * 4 + 3] = x.w;
+        }
+        mb_i = sw[4096 + lane];
+        l_i = sw[4096 + 64 + lane];
+    }
     // Q has landed.  A compiler-visible wait: otherwise the compiler places its
     // waits for these loads inside the chunk loop, where they would also wait
     // for the K/V copies in flight.
@@ -489,6 +552,16 @@ void attn_fwd_kernel(AttnArgs a) {
         pv(nchunk - 1, pb);
     }
 
+    if (!final_) {
+#pragma unroll
+        for (int v4 = 0; v4 < 16; ++v4)
+            *reinterpret_cast<float4 *>(sw + (v4 * 64 + lane) * 4) =
+                make_float4(o[v4 >> 2][(v4 & 3) * 4 + 0], o[v4 >> 2][(v4 & 3) * 4 + 1],
+                            o[v4 >> 2][(v4 & 3) * 4 + 2], o[v4 >> 2][(v4 & 3) * 4 + 3]);
+        sw[4096 + lane] = mb_i;
+        sw[4096 + 64 + lane] = l_i;
+        return;
+    }
     // finalise: lanes l and l^32 hold halves of the same row's sum
     const float l_tot = pair32_sum(l_i);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -507,7 +580,7 @@ void attn_fwd_kernel(AttnArgs a) {
 }
 
 template <typename T, bool kDense, int kH> hipError_t launch_h(const AttnArgs &a, hipStream_t s) {
-    const int64_t total = (int64_t)(a.hq / kH) * (a.n / kBQ);
+    const int64_t total = (int64_t)(a.hq / kH) * (a.n / kBQ - (kDense ? 0 : a.qb_lo));
     if (total == 0) return hipSuccess;
     hipLaunchKernelGGL((attn_fwd_kernel<T, kDense, kH>), dim3((unsigned)total), dim3(kThreads * kH), 0, s, a);
     return hipGetLastError();
@@ -515,16 +588,43 @@ template <typename T, bool kDense, int kH> hipError_t launch_h(const AttnArgs &a
 
 // Sparse: one q head per workgroup (each head has its own work lists).  Dense:
 // up to four q heads of a kv group per workgroup, sharing every K/V tile.
-template <typename T, bool kDense> hipError_t launch(const AttnArgs &a, hipStream_t s) {
+// Sparse in phases: launch j covers the keys [j R, (j+1) R) for the query
+// blocks from j R / 64 on, so the workgroups in flight read K/V from one
+// R-key range of a kv head (a working set the last-level cache holds) rather
+// than from the whole sequence.
+template <typename T, bool kDense> hipError_t launch(AttnArgs a, hipStream_t s) {
     if constexpr (kDense) {
         const int G = a.hq / a.hkv;
         if (G % 4 == 0) return launch_h<T, true, 4>(a, s);
         if (G % 2 == 0) return launch_h<T, true, 2>(a, s);
+        return launch_h<T, true, 1>(a, s);
+    } else {
+        const int64_t R = a.phase_keys;
+        if (a.ws == nullptr || R <= 0 || R >= a.n) {
+            a.ws = nullptr;
+            a.k_lo = INT_MIN;
+            a.k_hi = INT_MAX;
+            a.qb_lo = 0;
+            return launch_h<T, false, 1>(a, s);
+        }
+        const int64_t np = (a.n + R - 1) / R;
+        for (int64_t j = 0; j < np; ++j) {
+            a.k_lo = j == 0 ? INT_MIN : (int32_t)(j * R);
+            a.k_hi = j == np - 1 ? INT_MAX : (int32_t)((j + 1) * R);
+            a.qb_lo = j * R / kBQ;
+            const hipError_t e = launch_h<T, false, 1>(a, s);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
     }
-    return launch_h<T, kDense, 1>(a, s);
 }
 
 }  // namespace
+
+size_t sparse_state_bytes(int64_t hq, int64_t n, int64_t phase_keys) {
+    if (phase_keys <= 0 || phase_keys >= n) return 0;
+    return (size_t)hq * (size_t)(n / kBQ) * 2 * kStateFloats * sizeof(float);
+}
 
 hipError_t launch_sparse_prefill(const AttnArgs &a, int dtype, hipStream_t s) {
     return dtype == 0 ? launch<bf16, false>(a, s) : launch<float, false>(a, s);

@@ -16,7 +16,19 @@ struct AttnArgs {
     int64_t n;
     float scale_log2;    // sm_scale * log2(e)
     float scale;         // sm_scale
+    // key phases of the sparse kernel (one launch each): block tiles whose
+    // start and columns that lie in [k_lo, k_hi), for the query blocks
+    // b >= qb_lo; the running softmax state of a query block that is not
+    // finished in a phase goes to ws (NULL: a single phase over all keys)
+    int32_t phase_keys;  // keys per phase (multiple of 64); >= n: one phase
+    int32_t k_lo, k_hi;
+    int64_t qb_lo;
+    float *ws;
 };
+
+// Bytes of sparse-prefill state for hq heads and n keys in phases of
+// phase_keys keys (0 when one phase covers all keys).
+size_t sparse_state_bytes(int64_t hq, int64_t n, int64_t phase_keys);
 
 // dtype: 0 = bf16, 1 = fp32
 hipError_t launch_sparse_prefill(const AttnArgs &a, int dtype, hipStream_t s);

@@ -233,13 +233,28 @@ static int attn_common(const msa_problem *p, const void *q, const void *k, const
     a.n = p->seq_len;
     a.scale = scale_of(p);
     a.scale_log2 = a.scale * msa::kLog2e;
+    a.phase_keys = 0;
+    a.k_lo = INT32_MIN;
+    a.k_hi = INT32_MAX;
+    a.qb_lo = 0;
+    a.ws = nullptr;
     return MSA_OK;
+}
+
+static int64_t phase_keys_of(int32_t phase_keys) {
+    return phase_keys == 0 ? MSA_DEFAULT_PHASE_KEYS : phase_keys;
+}
+
+size_t msa_sparse_prefill_workspace(const msa_problem *p, int32_t phase_keys) {
+    if (check_problem(p) != MSA_OK || phase_keys < 0 || phase_keys % 64 != 0) return 0;
+    return msa::sparse_state_bytes(p->n_q_heads, p->seq_len, phase_keys_of(phase_keys));
 }
 
 int msa_sparse_prefill(const msa_problem *p, const void *q, const void *k, const void *v,
                        const int32_t *block_count, const int32_t *block_offset, int32_t cap_blocks,
                        const int32_t *column_count, const int32_t *column_index, int32_t cap_cols,
-                       void *out, float *lse, void *stream) {
+                       int32_t phase_keys, void *workspace, size_t workspace_bytes, void *out, float *lse,
+                       void *stream) {
     msa::AttnArgs a;
     int st = attn_common(p, q, k, v, out, a);
     if (st) return st;
@@ -253,6 +268,18 @@ int msa_sparse_prefill(const msa_problem *p, const void *q, const void *k, const
     a.cap_b = cap_blocks;
     a.cap_c = cap_cols;
     a.lse = lse;
+    if (phase_keys < 0 || phase_keys % 64 != 0)
+        return fail(MSA_ERR_RANGE, "phase_keys %d is not a non-negative multiple of 64", phase_keys);
+    a.phase_keys = (int32_t)phase_keys_of(phase_keys);
+    const size_t need = msa::sparse_state_bytes(p->n_q_heads, p->seq_len, a.phase_keys);
+    if (need > 0) {
+        if (!workspace) return fail(MSA_ERR_NULL, "workspace is NULL (%zu bytes needed)", need);
+        if (workspace_bytes < need)
+            return fail(MSA_ERR_WORKSPACE, "workspace %zu bytes, %zu needed", workspace_bytes, need);
+        if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+            return fail(MSA_ERR_RANGE, "workspace is not 16-byte aligned");
+        a.ws = static_cast<float *>(workspace);
+    }
     return launch_status(msa::launch_sparse_prefill(a, p->dtype, reinterpret_cast<hipStream_t>(stream)),
                          "sparse_prefill");
 }

@@ -32,6 +32,7 @@ class LayerPlan:
     dtype: torch.dtype = torch.bfloat16
     index: msa.IndexTensors = field(init=False)
     workspace: torch.Tensor = field(init=False)
+    attn_workspace: torch.Tensor | None = field(init=False)
     v_idx: torch.Tensor = field(init=False)
     s_idx: torch.Tensor = field(init=False)
 
@@ -40,6 +41,8 @@ class LayerPlan:
         self.index = msa.alloc_index(self.n_q_heads, self.seq_len, cb, cc, self.device)
         ws = msa.estimate_vs_workspace_bytes(self.n_q_heads, self.n_kv_heads, self.seq_len, self.dtype)
         self.workspace = torch.empty(ws, dtype=torch.uint8, device=self.device)
+        aws = msa.sparse_prefill_workspace_bytes(self.n_q_heads, self.n_kv_heads, self.seq_len, self.dtype)
+        self.attn_workspace = torch.empty(aws, dtype=torch.uint8, device=self.device) if aws else None
         i32 = dict(dtype=torch.int32, device=self.device)
         self.v_idx = torch.empty((self.n_q_heads, self.vertical_topk), **i32)
         self.s_idx = torch.empty((self.n_q_heads, self.slash_topk), **i32)
@@ -56,7 +59,8 @@ def vertical_slash_layer(q, k, v, vertical_topk: int, slash_topk: int, *, plan: 
     msa.estimate_vs(q, k, vertical_topk, slash_topk, workspace=plan.workspace, v_idx=plan.v_idx,
                     s_idx=plan.s_idx, stream=stream)
     msa.build_index(plan.v_idx, plan.s_idx, n, out=plan.index, stream=stream)
-    res = msa.sparse_prefill(q, k, v, plan.index, out=out, lse=lse, stream=stream)
+    res = msa.sparse_prefill(q, k, v, plan.index, out=out, lse=lse, workspace=plan.attn_workspace,
+                             stream=stream)
     return res, plan
 
 
@@ -121,6 +125,8 @@ class MixedPlan:
         ws_bs = max([msa.estimate_bs_workspace_bytes(h1 - h0, (h1 - h0) // G, n, self.dtype)
                      for h0, h1 in _runs(self.patterns, "bs")] or [0])
         self.bs_workspace = torch.empty(max(ws_bs, 1), dtype=torch.uint8, device=self.device)
+        aws = msa.sparse_prefill_workspace_bytes(hq, self.n_kv_heads, n, self.dtype)
+        self.attn_workspace = torch.empty(aws, dtype=torch.uint8, device=self.device) if aws else None
 
 
 def mixed_index(q, k, plan: MixedPlan, *, stream=None) -> msa.IndexTensors:
@@ -156,4 +162,5 @@ def mixed_layer(q, k, v, plan: MixedPlan, *, out: torch.Tensor | None = None, ls
     """Per-head patterns in one layer (see mixed_index), then a single sparse
     prefill over all heads."""
     mixed_index(q, k, plan, stream=stream)
-    return msa.sparse_prefill(q, k, v, plan.index, out=out, lse=lse, stream=stream)
+    return msa.sparse_prefill(q, k, v, plan.index, out=out, lse=lse, workspace=plan.attn_workspace,
+                              stream=stream)

@@ -20,6 +20,7 @@ _lib = None
 MSA_BF16, MSA_F32 = 0, 1
 HEAD_DIM = 128
 BLOCK = 64
+DEFAULT_PHASE_KEYS = 16384    # MSA_DEFAULT_PHASE_KEYS: keys per sparse-prefill phase when phase_keys is 0
 LAST_Q = 64
 
 
@@ -44,8 +45,9 @@ _SIGS = {
                                        ctypes.c_size_t, _VP]),
     "msa_build_index": (ctypes.c_int, [_VP, _VP, _I32, _VP, _I32, _I32, _VP, _VP, _I32, _VP, _VP,
                                        _I32, _VP]),
-    "msa_sparse_prefill": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _I32, _VP,
-                                          _VP, _VP]),
+    "msa_sparse_prefill": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32,
+                                          _VP, ctypes.c_size_t, _VP, _VP, _VP]),
+    "msa_sparse_prefill_workspace": (ctypes.c_size_t, [_VP, _I32]),
     "msa_dense_prefill": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "msa_estimate_bs_workspace": (ctypes.c_size_t, [_VP, _I32]),
     "msa_estimate_bs": (ctypes.c_int, [_VP, _VP, _VP, _I32, _I32, _VP, _VP, _I32, _VP, _VP,
@@ -221,10 +223,22 @@ def _index_ptrs(idx: IndexTensors, hq: int, n: int):
             idx.column_count.data_ptr(), idx.column_index.data_ptr(), idx.cap_cols)
 
 
+def sparse_prefill_workspace_bytes(n_q_heads: int, n_kv_heads: int, seq_len: int, dtype=torch.bfloat16,
+                                   phase_keys: int = 0) -> int:
+    """Workspace bytes of sparse_prefill (0: one key phase, none needed)."""
+    p = problem(n_q_heads, n_kv_heads, seq_len, MSA_BF16 if dtype == torch.bfloat16 else MSA_F32)
+    return int(load().msa_sparse_prefill_workspace(ctypes.byref(p), phase_keys))
+
+
 def sparse_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: IndexTensors, *,
                    out: torch.Tensor | None = None, lse: torch.Tensor | bool | None = None,
-                   sm_scale: float = 0.0, stream=None):
-    """Causal attention restricted to the work lists.  Returns out (and lse if requested)."""
+                   sm_scale: float = 0.0, phase_keys: int = 0, workspace: torch.Tensor | None = None,
+                   stream=None):
+    """Causal attention restricted to the work lists.  Returns out (and lse if requested).
+
+    phase_keys: keys per phase (0: the library default); workspace: a device
+    uint8 buffer of sparse_prefill_workspace_bytes(...) bytes, allocated here
+    when None and needed."""
     lib = load()
     p = _problem_of(q, k, sm_scale)
     hq, n = q.shape[0], q.shape[1]
@@ -234,8 +248,14 @@ def sparse_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: Ind
     if lse is True:
         lse = torch.empty((hq, n), dtype=torch.float32, device=q.device)
     bc, bo, cb, cc, ci, ccap = _index_ptrs(index, hq, n)
+    need = int(lib.msa_sparse_prefill_workspace(ctypes.byref(p), phase_keys))
+    ws_ptr, ws_bytes = None, 0
+    if need > 0:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
     _check(lib.msa_sparse_prefill(ctypes.byref(p), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
-                                  bc, bo, cb, cc, ci, ccap, _dev(out, "out"),
+                                  bc, bo, cb, cc, ci, ccap, phase_keys, ws_ptr, ws_bytes, _dev(out, "out"),
                                   _dev(lse, "lse") if want_lse else None, _stream(stream)),
            "msa_sparse_prefill")
     return (out, lse) if want_lse else out

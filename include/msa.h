@@ -142,11 +142,35 @@ int msa_build_index(const msa_problem *p, const int32_t *v_idx, int32_t vertical
  *     lse[h, i] = log sum_j exp(sm_scale <q_i, k_j>)   (natural log)
  * A row with no allowed key gives out = 0 and lse = -inf.  Counts above the
  * capacities are clamped; keys outside [0, N) are ignored.
+ *
+ * Key phases.  With R = phase_keys (0 selects MSA_DEFAULT_PHASE_KEYS) below
+ * seq_len, the work runs as ceil(N / R) launches in order on `stream`; launch
+ * j takes the block tiles whose start, and the columns that, lie in
+ * [jR, (j+1)R) (the first also everything below 0, the last everything from
+ * its start on), so the K/V read at any time come from one R-key range of a kv
+ * head.  The running softmax state of each query block (fp32) passes between
+ * launches through `workspace`.  This path needs every block list and column
+ * list ascending, as msa_build_index writes them; the result is then the same
+ * up to fp32 rounding order.  With R >= seq_len there is one launch over the
+ * lists in their given order and no workspace is used (it may be NULL).
+ *   phase_keys: 0 or a positive multiple of 64, else MSA_ERR_RANGE.
+ *   workspace: msa_sparse_prefill_workspace() bytes, 16-byte aligned, owned by
+ *     the caller, no initial contents; calls sharing one must not overlap.
  *   out [n_q_heads, N, 128] (dtype of p); lse [n_q_heads, N] float32 or NULL. */
 int msa_sparse_prefill(const msa_problem *p, const void *q, const void *k, const void *v,
                        const int32_t *block_count, const int32_t *block_offset, int32_t cap_blocks,
                        const int32_t *column_count, const int32_t *column_index, int32_t cap_cols,
-                       void *out, float *lse, void *stream);
+                       int32_t phase_keys, void *workspace, size_t workspace_bytes, void *out, float *lse,
+                       void *stream);
+
+/* Keys per phase of msa_sparse_prefill when phase_keys is 0 (K+V of one kv
+ * head over this many keys: 8 MB in bf16). */
+#define MSA_DEFAULT_PHASE_KEYS 16384
+
+/* Workspace bytes msa_sparse_prefill needs (0 when one phase covers seq_len;
+ * 0 for invalid arguments):
+ *   n_q_heads * (seq_len / 64) * 2 * (64 * 64 + 2 * 64) * 4. */
+size_t msa_sparse_prefill_workspace(const msa_problem *p, int32_t phase_keys);
 
 /* Dense causal attention (every j <= i), same layouts as msa_sparse_prefill. */
 int msa_dense_prefill(const msa_problem *p, const void *q, const void *k, const void *v,

@@ -30,7 +30,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -102,10 +102,37 @@ def test_estimate_bs_validation(lib):
 
 
 def test_sparse_prefill_validation(lib):
-    call = lambda bc, cb: lib.msa_sparse_prefill(P(), FAKE, FAKE, FAKE, bc, FAKE, cb, FAKE, FAKE, 4, FAKE,
-                                                 None, None)
+    # n = 4096 fits one default phase: no workspace needed
+    call = lambda bc, cb: lib.msa_sparse_prefill(P(), FAKE, FAKE, FAKE, bc, FAKE, cb, FAKE, FAKE, 4, 0, None, 0,
+                                                 FAKE, None, None)
     assert call(None, 4) == NULL
     assert call(FAKE, -1) == CAP
+    phased = lambda pk, ws, wsb: lib.msa_sparse_prefill(P(), FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 4, pk,
+                                                        ws, wsb, FAKE, None, None)
+    need = lib.msa_sparse_prefill_workspace(P(), 1024)
+    assert phased(-64, FAKE, need) == RANGE
+    assert phased(100, FAKE, need) == RANGE
+    assert phased(1024, None, need) == NULL
+    assert phased(1024, FAKE, need - 1) == WS
+    assert phased(1024, ctypes.c_void_p(0x1004), need) == RANGE      # not 16-byte aligned
+
+
+def test_default_phase_keys_matches_header():
+    text = open(HEADER).read()
+    assert int(re.search(r"#define MSA_DEFAULT_PHASE_KEYS (\d+)", text).group(1)) == B.DEFAULT_PHASE_KEYS
+
+
+def test_sparse_prefill_workspace_size(lib):
+    # one phase (default 65536 keys, or phase_keys >= seq_len): none
+    assert lib.msa_sparse_prefill_workspace(P(), 0) == 0
+    assert lib.msa_sparse_prefill_workspace(P(), 4096) == 0
+    assert lib.msa_sparse_prefill_workspace(P(n=1 << 17), 1 << 17) == 0
+    # per q head and query block: two waves x (64 x 64 O + 64 max + 64 sum) fp32
+    per_item = 2 * (64 * 64 + 2 * 64) * 4
+    assert lib.msa_sparse_prefill_workspace(P(), 1024) == 32 * 64 * per_item
+    assert lib.msa_sparse_prefill_workspace(P(n=1 << 17), 0) == 32 * 2048 * per_item
+    assert lib.msa_sparse_prefill_workspace(P(), 100) == 0          # invalid: not a multiple of 64
+    assert lib.msa_sparse_prefill_workspace(P(d=64), 1024) == 0     # invalid problem
 
 
 def test_binding_rejects_cpu_tensors():

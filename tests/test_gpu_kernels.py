@@ -63,6 +63,38 @@ def test_sparse_prefill_given_index(hq, hkv, n, kv, ks, fp32):
     compare_lse(lse.cpu().numpy(), rlse, "sparse")
 
 
+@pytest.mark.parametrize("hq,hkv,n,kv,ks,phase,fp32", [
+    (4, 2, 1216, 40, 60, 64, False),      # one phase per query block, ragged lists
+    (2, 1, 1216, 100, 300, 320, False),   # phase edges inside block tiles (unaligned starts)
+    (2, 1, 2048, 7, 2048, 512, False),    # every diagonal: blocks in every phase
+    (2, 1, 640, 9, 13, 192, True),        # fp32; most phases hold nothing for most blocks
+    (1, 1, 256, 1, 1, 64, False),         # a single diagonal and column
+])
+def test_sparse_prefill_phases(hq, hkv, n, kv, ks, phase, fp32):
+    """Key phases (one launch per phase, state in the workspace) against the
+    oracle and against one phase over the same lists."""
+    w, q, k, v = inputs(hq, hkv, n, seed=n + phase, fp32=fp32)
+    vi, si = random_sets(hq, n, kv, ks, seed=n + phase + 1)
+    ridx = oracle.build_index(vi, si, n)
+    gidx = msa.alloc_index(hq, n, ridx.block_offset.shape[2], ridx.column_index.shape[2])
+    gidx.block_count.copy_(torch.from_numpy(ridx.block_count))
+    gidx.block_offset.copy_(torch.from_numpy(ridx.block_offset))
+    gidx.column_count.copy_(torch.from_numpy(ridx.column_count))
+    gidx.column_index.copy_(torch.from_numpy(ridx.column_index))
+    dt = torch.float32 if fp32 else torch.bfloat16
+    need = msa.sparse_prefill_workspace_bytes(hq, hkv, n, dt, phase_keys=phase)
+    assert need == hq * (n // 64) * 2 * (64 * 64 + 128) * 4
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")     # no initial contents assumed
+    qs, ks_, vs = cuda(q, k, v)
+    out, lse = msa.sparse_prefill(qs, ks_, vs, gidx, lse=True, phase_keys=phase, workspace=ws)
+    ref, rlse = oracle.attention_with_mask(q, k, v, oracle.index_mask(ridx, n))
+    compare_out(out.float().cpu().numpy(), ref, fp32, "sparse phases")
+    compare_lse(lse.cpu().numpy(), rlse, "sparse phases")
+    one, one_lse = msa.sparse_prefill(qs, ks_, vs, gidx, lse=True, phase_keys=n)
+    compare_out(out.float().cpu().numpy(), one.float().cpu().numpy(), fp32, "phases vs one phase")
+    compare_lse(lse.cpu().numpy(), one_lse.cpu().numpy(), "phases vs one phase")
+
+
 def test_sparse_all_selected_equals_dense():
     n = 512
     w, q, k, v = inputs(4, 2, n, seed=3)
