@@ -117,9 +117,13 @@ def test_sparse_prefill_validation(lib):
     assert phased(1024, ctypes.c_void_p(0x1004), need) == RANGE      # not 16-byte aligned
 
 
-def test_default_phase_keys_matches_header():
+def test_default_phase_keys_matches_header(lib):
     text = open(HEADER).read()
     assert int(re.search(r"#define MSA_DEFAULT_PHASE_KEYS (\d+)", text).group(1)) == B.DEFAULT_PHASE_KEYS
+    # the built library resolves phase_keys = 0 to the same length
+    dk = B.DEFAULT_PHASE_KEYS
+    assert lib.msa_sparse_prefill_workspace(P(n=dk), 0) == 0
+    assert lib.msa_sparse_prefill_workspace(P(n=dk + 64), 0) > 0
 
 
 def test_sparse_prefill_workspace_size(lib):
