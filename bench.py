@@ -271,14 +271,26 @@ def main():
     })
     if not args.no_dense:
         dense_out = torch.empty_like(q)
+        lse_d = torch.empty((hq, n), dtype=torch.float32, device=q.device)
         msa.dense_prefill(q, k, v, out=dense_out, stream=stream)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        msa.dense_prefill(q, k, v, out=dense_out, stream=stream)
+        msa.dense_prefill(q, k, v, out=dense_out, lse=lse_d, stream=stream)
         e1.record(stream)
         torch.cuda.synchronize()
         ms_dense = e0.elapsed_time(e1)
+        # attention recall: the share of each row's dense softmax mass that the
+        # sparse index keeps, exp(lse_sparse - lse_dense), from one more
+        # (untimed) sparse call
+        lse_s = torch.empty_like(lse_d)
+        msa.sparse_prefill(q, k, v, plan.index, out=dense_out, lse=lse_s, workspace=plan.attn_workspace,
+                           stream=stream)
+        rec = torch.exp(lse_s - lse_d).flatten()
+        breakdown["attention_recall"] = {
+            "mean": round(float(rec.mean()), 4), "p05": round(float(torch.quantile(rec[::max(1, rec.numel() // 1000000)], 0.05)), 4),
+            "min": round(float(rec.min()), 4), "rows": "every row of every head"}
+        del lse_s, lse_d, rec
         dense_flop = causal_tiles * TILE_FLOP
         breakdown.update({"ms_dense_prefill": round(ms_dense, 3),
                           "dense_prefill_tflops": round(dense_flop / (ms_dense * 1e-3) / 1e12, 2),

@@ -331,6 +331,12 @@ void attn_fwd_kernel(AttnArgs a) {
 
     int nblk, ncol;
     const int32_t *blist = nullptr, *clist = nullptr;
+    // key phases (sparse, ws set): the first starts from an empty state, and
+    // the query block's output is written in the phase holding its own rows
+    // (no later key is visible to it); in between the state lives in ws
+    bool first = true, final_ = true, have_state = false;
+    float *sw = nullptr;                             // this wave's state: 16 float4 of O per lane, max, sum
+    int *state_flag = nullptr;                       // nonzero: ws holds a state for this query block
     if constexpr (kDense) {
         nblk = (int)b + 1;
         ncol = 0;
@@ -341,29 +347,28 @@ void attn_fwd_kernel(AttnArgs a) {
         blist = a.block_offset + item * a.cap_b;
         clist = a.column_index + item * a.cap_c;
         if (a.ws != nullptr) {
-            // one phase of several: the block tiles starting in [k_lo, k_hi)
-            // and the columns in it (the lists are ascending); the first phase
-            // also takes everything below, the last everything above
-            const int b0 = a.k_lo == INT_MIN ? 0 : lower_bound_wave(blist, nblk, a.k_lo, lane);
+            // this phase's part: the block tiles starting in [k_lo, k_hi) (the
+            // lists are ascending; the first phase also takes starts below, the
+            // last those above).  The columns all go to the final phase: every
+            // block of a head draws them from the same few keys, so they need no
+            // splitting for locality.
+            first = a.k_lo == INT_MIN;
+            final_ = (int64_t)r0 + kBQ - 1 < (int64_t)a.k_hi;
+            const int b0 = first ? 0 : lower_bound_wave(blist, nblk, a.k_lo, lane);
             const int b1 = a.k_hi == INT_MAX ? nblk : lower_bound_wave(blist, nblk, a.k_hi, lane);
-            const int c0 = a.k_lo == INT_MIN ? 0 : lower_bound_wave(clist, ncol, a.k_lo, lane);
-            const int c1 = a.k_hi == INT_MAX ? ncol : lower_bound_wave(clist, ncol, a.k_hi, lane);
             blist += b0;
             nblk = max(b1 - b0, 0);
-            clist += c0;
-            ncol = max(c1 - c0, 0);
+            if (!final_) ncol = 0;
+            sw = a.ws + item * (2 * kStateFloats) + wave * kStateFloats;
+            // every query block passes the first phase, which sets its flag
+            state_flag = reinterpret_cast<int *>(a.ws + (int64_t)a.hq * nqb * 2 * kStateFloats) + item;
+            have_state = !first && __builtin_amdgcn_readfirstlane(*state_flag) != 0;
+            if (!final_ && nblk == 0) {                 // nothing in this phase
+                if (first && tid == 0) *state_flag = 0;
+                return;
+            }
         }
     }
-    // phases: the first starts from an empty state, and the query block's
-    // output is written in the phase holding its own rows (no later key is
-    // visible to it); other phases keep the state in ws
-    const bool first = kDense || a.ws == nullptr || a.k_lo == INT_MIN;
-    const bool final_ = kDense || a.ws == nullptr || (int64_t)r0 + kBQ - 1 < (int64_t)a.k_hi;
-    if (!first && !final_ && nblk == 0 && ncol == 0) return;    // nothing in this phase
-    // this wave's state: 16 float4 of O per lane, then the lane's max and sum
-    float *sw = nullptr;
-    if constexpr (!kDense)
-        if (a.ws != nullptr) sw = a.ws + ((int64_t)h * nqb + b) * (2 * kStateFloats) + wave * kStateFloats;
     // an even number of chunks (column chunks padded with an empty one), so
     // that the steps come in pairs
     const int nchunk = 2 * (nblk + (ncol + kBK - 1) / kBK);
@@ -410,7 +415,7 @@ void attn_fwd_kernel(AttnArgs a) {
     // running row max kept in scaled log2 units as a stored fp32 value, so an
     // unchanged max gives a rescale factor of exactly 1
     float mb_i = -INFINITY, l_i = 0.f;
-    if (!first) {
+    if (have_state) {
 #pragma unroll
         for (int v4 = 0; v4 < 16; ++v4) {
             const float4 x = *reinterpret_cast<const float4 *>(sw + (v4 * 64 + lane) * 4);
@@ -560,6 +565,7 @@ void attn_fwd_kernel(AttnArgs a) {
                             o[v4 >> 2][(v4 & 3) * 4 + 2], o[v4 >> 2][(v4 & 3) * 4 + 3]);
         sw[4096 + lane] = mb_i;
         sw[4096 + 64 + lane] = l_i;
+        if (tid == 0) *state_flag = 1;
         return;
     }
     // finalise: lanes l and l^32 hold halves of the same row's sum
@@ -623,7 +629,7 @@ template <typename T, bool kDense> hipError_t launch(AttnArgs a, hipStream_t s) 
 
 size_t sparse_state_bytes(int64_t hq, int64_t n, int64_t phase_keys) {
     if (phase_keys <= 0 || phase_keys >= n) return 0;
-    return (size_t)hq * (size_t)(n / kBQ) * 2 * kStateFloats * sizeof(float);
+    return (size_t)hq * (size_t)(n / kBQ) * (2 * kStateFloats * sizeof(float) + sizeof(int));
 }
 
 hipError_t launch_sparse_prefill(const AttnArgs &a, int dtype, hipStream_t s) {

@@ -145,14 +145,15 @@ int msa_build_index(const msa_problem *p, const int32_t *v_idx, int32_t vertical
  *
  * Key phases.  With R = phase_keys (0 selects MSA_DEFAULT_PHASE_KEYS) below
  * seq_len, the work runs as ceil(N / R) launches in order on `stream`; launch
- * j takes the block tiles whose start, and the columns that, lie in
- * [jR, (j+1)R) (the first also everything below 0, the last everything from
- * its start on), so the K/V read at any time come from one R-key range of a kv
- * head.  The running softmax state of each query block (fp32) passes between
- * launches through `workspace`.  This path needs every block list and column
- * list ascending, as msa_build_index writes them; the result is then the same
- * up to fp32 rounding order.  With R >= seq_len there is one launch over the
- * lists in their given order and no workspace is used (it may be NULL).
+ * j takes the block tiles whose start lies in [jR, (j+1)R) (the first also
+ * starts below 0, the last every start from jR on), so the K/V read at any
+ * time come from one R-key range of a kv head; each query block's columns go
+ * to the launch that holds its own rows.  The running softmax state of each
+ * query block (fp32) passes between launches through `workspace`.  This path
+ * needs every block list ascending, as msa_build_index and msa_estimate_bs
+ * write them; the result is then the same up to fp32 rounding order.  With
+ * R >= seq_len there is one launch over the lists in their given order and no
+ * workspace is used (it may be NULL).
  *   phase_keys: 0 or a positive multiple of 64, else MSA_ERR_RANGE.
  *   workspace: msa_sparse_prefill_workspace() bytes, 16-byte aligned, owned by
  *     the caller, no initial contents; calls sharing one must not overlap.
@@ -169,7 +170,7 @@ int msa_sparse_prefill(const msa_problem *p, const void *q, const void *k, const
 
 /* Workspace bytes msa_sparse_prefill needs (0 when one phase covers seq_len;
  * 0 for invalid arguments):
- *   n_q_heads * (seq_len / 64) * 2 * (64 * 64 + 2 * 64) * 4. */
+ *   n_q_heads * (seq_len / 64) * (2 * (64 * 64 + 2 * 64) * 4 + 4). */
 size_t msa_sparse_prefill_workspace(const msa_problem *p, int32_t phase_keys);
 
 /* Dense causal attention (every j <= i), same layouts as msa_sparse_prefill. */

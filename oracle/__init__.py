@@ -27,7 +27,8 @@ state):
                            (plain C helper, see csrc/index_ref.c).
   attention.*              softmax attention restricted to an explicit boolean
                            mask (dense causal when every column and diagonal is
-                           selected).
+                           selected); attention_recall, the share of each
+                           row's dense attention that a mask keeps.
 
 Pins that tie each function to something other than itself live in
 tests/test_oracle_pins.py.
@@ -37,7 +38,7 @@ from .estimate import estimate_vs, top_k_indices, block_sparse_select, block_sco
 from .index import (build_index, a_shape_sets, index_mask, exact_union_mask, block_key_sets,
                     IndexArrays)
 from .attention import (attention_with_mask, masked_attention_blocks, dense_attention_blocks,
-                        dense_attention)
+                        dense_attention, attention_recall)
 
 __all__ = [
     "estimate_vs", "top_k_indices", "block_sparse_select", "block_scores",

@@ -114,3 +114,27 @@ def dense_attention_blocks(q, k, v, items, block: int = 64, scale: float | None 
                                              mask, scale)
             out[(h, b)] = (o, lse)
     return out
+
+
+def attention_recall(q, k, mask, scale: float | None = None, heads=None):
+    """Share of each row's dense causal attention that the mask keeps, [H, N].
+
+    The pages judge a sparse selection by how much of the attention scores it
+    recovers (talk slides "System-Algorithm Co-design", slide "Dynamic
+    sparsity in attention", figure panels (a)-(c): coverage and recovery of
+    top-k selections).  Written as that definition:
+        p[i, :] = softmax_j(scale * <q_i, k_j>) over j <= i
+        recall[i] = sum_{j <= i, M[i, j]} p[i, j]
+    mask: [H, N, N] (or [N, N] shared), as in attention_with_mask."""
+    Hq, N, D = q.shape
+    G = Hq // k.shape[0]
+    scale = (1.0 / np.sqrt(D)) if scale is None else scale
+    heads = list(range(Hq)) if heads is None else list(heads)
+    causal = np.tril(np.ones((N, N), dtype=bool))
+    out = np.zeros((len(heads), N))
+    for n, h in enumerate(heads):
+        g = h // G
+        mk = mask if mask.ndim == 2 else mask[n]
+        _, _, p = _masked_softmax_rows(as_f64(q[h]), as_f64(k[g]), np.zeros((N, 1)), causal, scale)
+        out[n] = np.where(mk & causal, p, 0.0).sum(axis=1)
+    return out

@@ -46,6 +46,8 @@ class Workload:
     n_planted: int = 16          # planted vertical columns per kv head, key 0 included
     plant_gain: float = 3.0      # K[col] += gain * mean(q)
     slash_period: int = 0        # >0: keys at offset multiples of this are biased toward q
+    band: float = 0.0            # >0: a content direction shared by all q and k of a kv group
+    band_pairs: int = 64         # rotary pairs (fastest first) the shared direction occupies
     head_patterns: tuple = field(default_factory=tuple)  # per q head: "vs" | "a" | "bs"
     sink: int = 128              # A-shape: leading columns kept
     window: int = 4096           # A-shape: local diagonals kept
@@ -81,6 +83,12 @@ WORKLOADS = {
     "llama3_8b_1m": Workload("llama3_8b_1m", 32, 8, 1048576, slash_period=512, seed=1004),
     # heads 0-7 A-shape, 8-23 vertical-slash, 24-31 block-sparse
     "mixed_256k": Workload("mixed_256k", 32, 8, 262144, head_patterns=_mixed_patterns(), seed=1005),
+    # clustered slashes ("local band"): the 1M layer plus a shared content
+    # direction on the 48 fastest rotary pairs, so that the selected diagonals
+    # gather near the main diagonal (a labelled extra workload, not one of the
+    # five above)
+    "llama3_8b_1m_band": Workload("llama3_8b_1m_band", 32, 8, 1048576, slash_period=512, band=12.0,
+                                  band_pairs=48, seed=1006),
 }
 
 
@@ -163,6 +171,19 @@ def make_inputs(w: Workload, seed: int | None = None, device: str = "cpu") -> di
     q = torch.randn((Hq, N, D), generator=gen, dtype=work, device=dev)
     k = torch.randn((Hkv, N, D), generator=gen, dtype=work, device=dev)
     v = torch.randn((Hkv, N, D), generator=gen, dtype=work, device=dev)
+    if w.band > 0:
+        # local band: every query and key of kv group g gets band * u_g (a
+        # random unit vector) before the rotation, so q_i . k_j carries
+        # band^2 * sum_f |u_g,f|^2 cos((i - j) theta_f): largest near the
+        # diagonal and decaying with the offset, as rotary embeddings do
+        # (faster the fewer and faster the rotary pairs u occupies)
+        u = torch.randn((Hkv, D), generator=gen, dtype=work, device=dev)
+        keep = (torch.arange(D, device=dev) % (D // 2)) < w.band_pairs
+        u = torch.where(keep, u, torch.zeros((), dtype=work, device=dev))
+        u = u / u.norm(dim=1, keepdim=True)
+        G = Hq // Hkv
+        q += w.band * u.repeat_interleave(G, dim=0)[:, None, :]
+        k += w.band * u[:, None, :]
     chunk = 1 << 16
     _rotate_(q, w.rope_base, chunk)
     _rotate_(k, w.rope_base, chunk)

@@ -131,8 +131,9 @@ def test_sparse_prefill_workspace_size(lib):
     assert lib.msa_sparse_prefill_workspace(P(), 0) == 0
     assert lib.msa_sparse_prefill_workspace(P(), 4096) == 0
     assert lib.msa_sparse_prefill_workspace(P(n=1 << 17), 1 << 17) == 0
-    # per q head and query block: two waves x (64 x 64 O + 64 max + 64 sum) fp32
-    per_item = 2 * (64 * 64 + 2 * 64) * 4
+    # per q head and query block: two waves x (64 x 64 O + 64 max + 64 sum) fp32,
+    # and a 4-byte flag
+    per_item = 2 * (64 * 64 + 2 * 64) * 4 + 4
     assert lib.msa_sparse_prefill_workspace(P(), 1024) == 32 * 64 * per_item
     assert lib.msa_sparse_prefill_workspace(P(n=1 << 17), 0) == 32 * 2048 * per_item
     assert lib.msa_sparse_prefill_workspace(P(), 100) == 0          # invalid: not a multiple of 64

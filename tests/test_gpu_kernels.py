@@ -83,7 +83,7 @@ def test_sparse_prefill_phases(hq, hkv, n, kv, ks, phase, fp32):
     gidx.column_index.copy_(torch.from_numpy(ridx.column_index))
     dt = torch.float32 if fp32 else torch.bfloat16
     need = msa.sparse_prefill_workspace_bytes(hq, hkv, n, dt, phase_keys=phase)
-    assert need == hq * (n // 64) * 2 * (64 * 64 + 128) * 4
+    assert need == hq * (n // 64) * (2 * (64 * 64 + 128) * 4 + 4)
     ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")     # no initial contents assumed
     qs, ks_, vs = cuda(q, k, v)
     out, lse = msa.sparse_prefill(qs, ks_, vs, gidx, lse=True, phase_keys=phase, workspace=ws)
@@ -93,6 +93,21 @@ def test_sparse_prefill_phases(hq, hkv, n, kv, ks, phase, fp32):
     one, one_lse = msa.sparse_prefill(qs, ks_, vs, gidx, lse=True, phase_keys=n)
     compare_out(out.float().cpu().numpy(), one.float().cpu().numpy(), fp32, "phases vs one phase")
     compare_lse(lse.cpu().numpy(), one_lse.cpu().numpy(), "phases vs one phase")
+
+
+def test_recall_from_lse():
+    """Attention recall measured on the GPU as exp(lse_sparse - lse_dense)
+    against the oracle's share of the dense softmax mass under the mask."""
+    hq, hkv, n = 4, 2, 640
+    w, q, k, v = inputs(hq, hkv, n, seed=17)
+    vi, si = random_sets(hq, n, 12, 40, seed=18)
+    idx = msa.build_index(*cuda(torch.from_numpy(vi), torch.from_numpy(si)), n)
+    qs, ks_, vs = cuda(q, k, v)
+    _, lse_s = msa.sparse_prefill(qs, ks_, vs, idx, lse=True)
+    _, lse_d = msa.dense_prefill(qs, ks_, vs, lse=True)
+    got = torch.exp(lse_s - lse_d).cpu().numpy()
+    want = oracle.attention_recall(q, k, oracle.index_mask(to_oracle_index(idx), n))
+    assert np.abs(got - want).max() <= 3e-4
 
 
 def test_sparse_all_selected_equals_dense():

@@ -339,6 +339,49 @@ def test_linearity_and_zero_query():
                 assert abs(lz[h, i] - math.log(len(allowed))) < 1e-12
 
 
+# ---------------------------------------------------------------- attention recall
+
+@pytest.mark.parametrize("n,kv,ks", [(64, 3, 5), (192, 5, 9)])
+def test_recall_brute_force(n, kv, ks):
+    """Per-entry loop: share of the causal softmax mass on the masked keys."""
+    hq, hkv, d = 2, 1, 6
+    q, k, v = rand_qkv(hq, hkv, n, d, seed=n + 5)
+    v_idx, s_idx = random_sets(hq, n, kv, ks, seed=n + 6)
+    idx = oracle.build_index(v_idx, s_idx, n)
+    M = oracle.index_mask(idx, n)
+    R = oracle.attention_recall(q, k, M)
+    scale = 1.0 / math.sqrt(d)
+    for h in range(hq):
+        for i in range(0, n, 7):
+            z = [scale * sum(q[h, i, t] * k[0, j, t] for t in range(d)) for j in range(i + 1)]
+            m = max(z)
+            w = [math.exp(x - m) for x in z]
+            want = math.fsum(w[j] for j in range(i + 1) if M[h, i, j]) / math.fsum(w)
+            assert abs(R[h, i] - want) < 1e-12
+
+
+def test_recall_closed_forms_and_lse_identity():
+    n, d = 256, 16
+    q, k, v = rand_qkv(2, 1, n, d, seed=21)
+    v_idx, s_idx = random_sets(2, n, 6, 20, seed=22)
+    idx = oracle.build_index(v_idx, s_idx, n)
+    M = oracle.index_mask(idx, n)
+    causal = np.tril(np.ones((n, n), dtype=bool))
+    # the causal mask keeps everything
+    np.testing.assert_allclose(oracle.attention_recall(q, k, causal), 1.0, atol=1e-12)
+    # disjoint masks add up
+    R = oracle.attention_recall(q, k, M)
+    Rc = oracle.attention_recall(q, k, causal[None] & ~M)
+    np.testing.assert_allclose(R + Rc, 1.0, atol=1e-12)
+    # zero queries: uniform attention, recall = allowed keys / (i + 1)
+    Rz = oracle.attention_recall(np.zeros_like(q), k, M)
+    np.testing.assert_allclose(Rz, (M & causal[None]).sum(-1) / np.arange(1, n + 1)[None], atol=1e-12)
+    # the same quantity through the log-sum-exps of masked and dense attention
+    _, lse = oracle.attention_with_mask(q, k, v, M)
+    _, lsed = oracle.dense_attention(q, k, v)
+    np.testing.assert_allclose(R, np.exp(lse - lsed), atol=1e-12)
+
+
 # ---------------------------------------------------------------- block-sparse
 
 def test_block_scores_brute_force():
