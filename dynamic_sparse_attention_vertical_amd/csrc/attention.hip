@@ -21,6 +21,13 @@
 // lane, no registers), 16-byte chunks XOR-swizzled per row so that the MFMA
 // operand reads are free of bank conflicts.
 //
+// Long sparse sequences run in key phases, one launch per range of keys (16K
+// by default): each launch takes the block tiles starting in its range, so the
+// workgroups in flight read K/V from one cache-sized range of a kv head, and a
+// query block's fp32 softmax state (O, row max, row sum) waits in a caller
+// workspace between launches; its columns and its output go to the launch that
+// holds its own rows.
+//
 // The pages: causal attention computed only over the selected entries, in
 // FlashAttention style (talk slides "System-Algorithm Co-design", slide
 // "MInference": dynamic sparse attention calculation with PIT and
