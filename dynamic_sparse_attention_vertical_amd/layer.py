@@ -164,3 +164,68 @@ def mixed_layer(q, k, v, plan: MixedPlan, *, out: torch.Tensor | None = None, ls
     mixed_index(q, k, plan, stream=stream)
     return msa.sparse_prefill(q, k, v, plan.index, out=out, lse=lse, workspace=plan.attn_workspace,
                               stream=stream)
+
+
+# ---------------------------------------------------------------------------
+# The README's kernel-only calls ("MInference 1.0 README", section "How to use
+# MInference", kernel-only usage: vertical_slash_sparse_attention,
+# block_sparse_attention, streaming_forward), on [batch, heads, seq, dim] or
+# [heads, seq, dim] tensors.  Batch elements run one after another on the
+# stream through the same C-ABI steps, sharing one set of buffers.
+
+def _batched(q, k, v):
+    if q.dim() == 3:
+        return q[None], k[None], v[None], True
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or k.shape[0] != q.shape[0] or v.shape[0] != q.shape[0]:
+        raise msa.MsaError("q, k, v must all be [batch, heads, seq, dim] (or all [heads, seq, dim])")
+    return q, k, v, False
+
+
+def vertical_slash_sparse_attention(q, k, v, vertical_topk: int, slash_topk: int, *, stream=None):
+    """Vertical-slash sparse attention: per head, the vertical_topk key columns
+    and slash_topk diagonals the online estimate selects, then causal
+    attention over their 64-wide block cover.  Returns the attention output."""
+    q4, k4, v4, squeeze = _batched(q, k, v)
+    out = torch.empty_like(q4)
+    plan = LayerPlan(q4.shape[1], k4.shape[1], q4.shape[2], vertical_topk, slash_topk, str(q4.device), q4.dtype)
+    for bi in range(q4.shape[0]):
+        vertical_slash_layer(q4[bi], k4[bi], v4[bi], vertical_topk, slash_topk, plan=plan, out=out[bi],
+                             stream=stream)
+    return out[0] if squeeze else out
+
+
+def block_sparse_attention(q, k, v, topk: int, *, stream=None):
+    """Block-sparse attention: each 64-row query block attends to its topk
+    highest-scoring 64-key blocks (mean-pooled q and k block scores), causally."""
+    q4, k4, v4, squeeze = _batched(q, k, v)
+    out = torch.empty_like(q4)
+    hq, hkv, n = q4.shape[1], k4.shape[1], q4.shape[2]
+    idx = msa.alloc_index(hq, n, min(topk, n // msa.BLOCK), 0, q4.device)
+    ws = torch.empty(max(msa.estimate_bs_workspace_bytes(hq, hkv, n, q4.dtype), 1), dtype=torch.uint8,
+                     device=q4.device)
+    aws_bytes = msa.sparse_prefill_workspace_bytes(hq, hkv, n, q4.dtype)
+    aws = torch.empty(aws_bytes, dtype=torch.uint8, device=q4.device) if aws_bytes else None
+    for bi in range(q4.shape[0]):
+        msa.estimate_bs(q4[bi], k4[bi], topk, out=idx, workspace=ws, stream=stream)
+        msa.sparse_prefill(q4[bi], k4[bi], v4[bi], idx, out=out[bi], workspace=aws, stream=stream)
+    return out[0] if squeeze else out
+
+
+def streaming_forward(q, k, v, init_num: int, local_window_num: int, *, stream=None):
+    """A-shape (streaming) attention: every row attends to the first init_num
+    keys and to the local_window_num keys ending at itself (diagonal offsets
+    0 .. local_window_num - 1), causally, over their 64-wide block cover."""
+    q4, k4, v4, squeeze = _batched(q, k, v)
+    hq, hkv, n = q4.shape[1], k4.shape[1], q4.shape[2]
+    if not (1 <= init_num <= n and 1 <= local_window_num <= n):
+        raise msa.MsaError("init_num and local_window_num must be in [1, seq_len]")
+    i32 = dict(dtype=torch.int32, device=q4.device)
+    vi = torch.arange(init_num, **i32).expand(hq, -1).contiguous()
+    si = torch.arange(local_window_num, **i32).expand(hq, -1).contiguous()
+    idx = msa.build_index(vi, si, n, stream=stream)       # the same for every batch element
+    out = torch.empty_like(q4)
+    aws_bytes = msa.sparse_prefill_workspace_bytes(hq, hkv, n, q4.dtype)
+    aws = torch.empty(aws_bytes, dtype=torch.uint8, device=q4.device) if aws_bytes else None
+    for bi in range(q4.shape[0]):
+        msa.sparse_prefill(q4[bi], k4[bi], v4[bi], idx, out=out[bi], workspace=aws, stream=stream)
+    return out[0] if squeeze else out
