@@ -84,14 +84,17 @@ def top_k_indices(x, k: int) -> np.ndarray:
 
 def block_scores(q, k, h: int, block: int = 64, scale: float | None = None) -> np.ndarray:
     """Mean-pooled block scores of q head h: u[b, c] = scale * <mean q-block b,
-    mean k-block c>, for c <= b; -inf above the block diagonal."""
+    mean k-block c>, for c <= b; -inf above the block diagonal.  A last block
+    shorter than `block` rows (N not a multiple of it) is the mean of the rows
+    it has."""
     Hq, N, D = q.shape
     G = Hq // k.shape[0]
     g = h // G
     scale = (1.0 / np.sqrt(D)) if scale is None else scale
-    nb = N // block
-    qb = as_f64(q[h]).reshape(nb, block, D).mean(axis=1)
-    kb = as_f64(k[g]).reshape(nb, block, D).mean(axis=1)
+    nb = (N + block - 1) // block
+    qh, kh = as_f64(q[h]), as_f64(k[g])
+    qb = np.stack([qh[b * block: (b + 1) * block].mean(axis=0) for b in range(nb)])
+    kb = np.stack([kh[c * block: (c + 1) * block].mean(axis=0) for c in range(nb)])
     u = scale * (qb @ kb.T)
     u[np.triu_indices(nb, 1)] = -np.inf
     return u
@@ -103,7 +106,7 @@ def block_sparse_select(q, k, heads, topk: int = 100, block: int = 64, scale: fl
     starts 64*c.  Returns (block_count [H, nb], block_offset [H, nb, topk] with -1
     past the count, scores [H, nb, nb])."""
     Hq, N, D = q.shape
-    nb = N // block
+    nb = (N + block - 1) // block
     heads = list(heads)
     counts = np.zeros((len(heads), nb), dtype=np.int32)
     offs = np.full((len(heads), nb, topk), -1, dtype=np.int32)

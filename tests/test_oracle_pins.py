@@ -399,6 +399,37 @@ def test_block_scores_brute_force():
             assert abs(u[b, c] - want) < 1e-12
 
 
+def test_block_scores_ragged_last_block():
+    """N not a multiple of 64: the last block is the mean of its rows."""
+    n, d = 64 * 3 + 17, 4
+    q, k, _ = rand_qkv(1, 1, n, d, seed=9)
+    u = oracle.block_scores(q, k, 0, block=64)
+    assert u.shape == (4, 4)
+    qm = [sum(q[0, 192 + t, e] for t in range(17)) / 17 for e in range(d)]
+    for c in range(4):
+        rows = range(64 * c, min(64 * c + 64, n))
+        km = [sum(k[0, t, e] for t in rows) / len(rows) for e in range(d)]
+        want = sum(qm[e] * km[e] for e in range(d)) / math.sqrt(d)
+        assert abs(u[3, c] - want) < 1e-12
+
+
+def test_index_ragged_last_block():
+    """N not a multiple of 64: the last query block ends at row N-1, and its
+    blocks and columns stop there too."""
+    n = 64 * 5 + 23
+    v_idx, s_idx = random_sets(2, n, 9, 30, seed=12)
+    idx = oracle.build_index(v_idx, s_idx, n)
+    assert idx.block_count.shape == (2, 6)
+    M = oracle.index_mask(idx, n)
+    Mx = oracle.exact_union_mask(v_idx, s_idx, n)
+    assert np.all(M[Mx])                          # every selected entry is covered
+    for h in range(2):
+        for t in range(int(idx.column_count[h, 5])):
+            assert idx.column_index[h, 5, t] <= n - 1
+        # rows of the last block see no key past themselves
+        assert not np.any(np.triu(M[h], 1))
+
+
 def test_block_sparse_full_topk_is_dense():
     n, d = 320, 16
     q, k, v = rand_qkv(2, 1, n, d, seed=10)
