@@ -320,7 +320,7 @@ void attn_fwd_kernel(AttnArgs a) {
     const int lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
     const int64_t n = a.n;
     const int n32 = (int)n;                          // below 2^31
-    const int64_t nqb = n / kBQ;
+    const int64_t nqb = (n + kBQ - 1) / kBQ;        // the last query block may be short
     const int G = a.hq / a.hkv;
     int hgrp;
     int64_t b;
@@ -412,7 +412,7 @@ void attn_fwd_kernel(AttnArgs a) {
     // Q fragments (B operand of S^T = K Q^T): query qrow, d = dk*16 + hl*8 + e
     frag qf[8];
 #pragma unroll
-    for (int dk = 0; dk < 8; ++dk) qf[dk] = E::load_frag(qp + (int64_t)qrow * kD + dk * 16 + hl * 8);
+    for (int dk = 0; dk < 8; ++dk) qf[dk] = E::load_frag(qp + (int64_t)min(qrow, n32 - 1) * kD + dk * 16 + hl * 8);
 
     f32x16 o[4];
 #pragma unroll
@@ -578,6 +578,7 @@ void attn_fwd_kernel(AttnArgs a) {
     // finalise: lanes l and l^32 hold halves of the same row's sum
     const float l_tot = pair32_sum(l_i);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (qrow >= n32) return;                            // rows past the end of a short last block
     T *op = reinterpret_cast<T *>(a.out) + ((int64_t)h * n + qrow) * kD;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -593,7 +594,7 @@ void attn_fwd_kernel(AttnArgs a) {
 }
 
 template <typename T, bool kDense, int kH> hipError_t launch_h(const AttnArgs &a, hipStream_t s) {
-    const int64_t total = (int64_t)(a.hq / kH) * (a.n / kBQ - (kDense ? 0 : a.qb_lo));
+    const int64_t total = (int64_t)(a.hq / kH) * ((a.n + kBQ - 1) / kBQ - (kDense ? 0 : a.qb_lo));
     if (total == 0) return hipSuccess;
     hipLaunchKernelGGL((attn_fwd_kernel<T, kDense, kH>), dim3((unsigned)total), dim3(kThreads * kH), 0, s, a);
     return hipGetLastError();
@@ -636,7 +637,7 @@ template <typename T, bool kDense> hipError_t launch(AttnArgs a, hipStream_t s) 
 
 size_t sparse_state_bytes(int64_t hq, int64_t n, int64_t phase_keys) {
     if (phase_keys <= 0 || phase_keys >= n) return 0;
-    return (size_t)hq * (size_t)(n / kBQ) * (2 * kStateFloats * sizeof(float) + sizeof(int));
+    return (size_t)hq * (size_t)((n + kBQ - 1) / kBQ) * (2 * kStateFloats * sizeof(float) + sizeof(int));
 }
 
 hipError_t launch_sparse_prefill(const AttnArgs &a, int dtype, hipStream_t s) {

@@ -38,9 +38,8 @@ int check_problem(const msa_problem *p) {
     if (p->n_q_heads <= 0 || p->n_kv_heads <= 0 || p->n_q_heads % p->n_kv_heads != 0)
         return fail(MSA_ERR_SHAPE, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)",
                     p->n_q_heads, p->n_kv_heads);
-    if (p->seq_len <= 0 || p->seq_len % 64 != 0 || p->seq_len >= (int64_t(1) << 31))
-        return fail(MSA_ERR_SHAPE, "seq_len must be a positive multiple of 64 below 2^31 (got %lld)",
-                    (long long)p->seq_len);
+    if (p->seq_len <= 0 || p->seq_len >= (int64_t(1) << 31))
+        return fail(MSA_ERR_SHAPE, "seq_len must be positive and below 2^31 (got %lld)", (long long)p->seq_len);
     if (p->dtype != MSA_BF16 && p->dtype != MSA_F32)
         return fail(MSA_ERR_DTYPE, "unknown dtype %d", p->dtype);
     if (!(p->sm_scale >= 0.f) || isinf(p->sm_scale))
@@ -127,7 +126,7 @@ int msa_index_caps(const msa_problem *p, int32_t vertical_topk, int32_t slash_to
     if (block != 64) return fail(MSA_ERR_RANGE, "block must be 64 (got %d)", block);
     if (vertical_topk < 0 || vertical_topk > p->seq_len || slash_topk < 0 || slash_topk > p->seq_len)
         return fail(MSA_ERR_RANGE, "top-k values must lie in [0, seq_len]");
-    const int64_t nqb = p->seq_len / 64;
+    const int64_t nqb = (p->seq_len + 63) / 64;
     *cap_blocks = (int32_t)(slash_topk < nqb ? slash_topk : nqb);
     *cap_cols = vertical_topk;
     return ok();
@@ -149,6 +148,9 @@ int msa_estimate_vs(const msa_problem *p, const void *q, const void *k, int32_t 
     if (st) return st;
     if (!q || !k || !v_idx || !s_idx || !workspace) return fail(MSA_ERR_NULL, "a required pointer is NULL");
     if (last_q != 64) return fail(MSA_ERR_RANGE, "last_q must be 64 (got %d)", last_q);
+    if (p->seq_len % 64 != 0)
+        return fail(MSA_ERR_SHAPE, "seq_len must be a multiple of 64 for the estimate (got %lld)",
+                    (long long)p->seq_len);
     if (vertical_topk < 1 || vertical_topk > p->seq_len || slash_topk < 1 || slash_topk > p->seq_len)
         return fail(MSA_ERR_RANGE, "top-k values must lie in [1, seq_len]");
     const EstLayout L = est_layout(p);
@@ -310,6 +312,9 @@ int msa_estimate_bs(const msa_problem *p, const void *q, const void *k, int32_t 
     if (!q || !k || !block_count || !block_offset || !column_count || !workspace)
         return fail(MSA_ERR_NULL, "a required pointer is NULL");
     if (block != 64) return fail(MSA_ERR_RANGE, "block must be 64 (got %d)", block);
+    if (p->seq_len % 64 != 0)
+        return fail(MSA_ERR_SHAPE, "seq_len must be a multiple of 64 for the estimate (got %lld)",
+                    (long long)p->seq_len);
     const int64_t nb = p->seq_len / 64;
     if (nb > kBsMaxBlocks)
         return fail(MSA_ERR_SHAPE, "block-sparse estimation supports at most %lld key blocks",

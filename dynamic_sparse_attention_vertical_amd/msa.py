@@ -140,7 +140,7 @@ def index_caps(seq_len: int, vertical_topk: int, slash_topk: int, n_q_heads: int
 
 
 def alloc_index(n_q_heads: int, seq_len: int, cap_blocks: int, cap_cols: int, device="cuda") -> IndexTensors:
-    nqb = seq_len // BLOCK
+    nqb = (seq_len + BLOCK - 1) // BLOCK
     i32 = dict(dtype=torch.int32, device=device)
     return IndexTensors(torch.empty((n_q_heads, nqb), **i32),
                         torch.empty((n_q_heads, nqb, max(cap_blocks, 1)), **i32)[:, :, :cap_blocks],
@@ -208,7 +208,7 @@ def build_index(v_idx: torch.Tensor, s_idx: torch.Tensor, seq_len: int, *,
 
 
 def _index_ptrs(idx: IndexTensors, hq: int, n: int):
-    nqb = n // BLOCK
+    nqb = (n + BLOCK - 1) // BLOCK
     for name in ("block_count", "column_count"):
         t = getattr(idx, name)
         if t.dtype != torch.int32 or tuple(t.shape) != (hq, nqb) or not t.is_contiguous():

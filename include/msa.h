@@ -25,8 +25,11 @@
  *  * Tensors are device memory owned by the caller, batch 1, contiguous
  *    [heads, seq_len, head_dim] row-major.  Q has n_q_heads heads; K and V have
  *    n_kv_heads; q head h reads kv head h / (n_q_heads / n_kv_heads).
- *  * head_dim must be 128; seq_len must be a positive multiple of 64 and below
- *    2^31; n_q_heads must be a multiple of n_kv_heads.
+ *  * head_dim must be 128; seq_len must be positive and below 2^31 (the two
+ *    estimators need a multiple of 64); n_q_heads must be a multiple of
+ *    n_kv_heads.  Query blocks are 64 rows; when seq_len is not a multiple of
+ *    64 the last one is shorter (rows 64b .. seq_len-1), and per-block arrays
+ *    have ceil(seq_len / 64) entries per head.
  *  * A subset of heads is selected by offsetting the pointers (q by h0 heads,
  *    k/v by h0/G heads) and passing the subset's head counts.
  *  * The library never allocates or frees device memory.  Scratch memory comes
@@ -115,7 +118,7 @@ int msa_estimate_vs(const msa_problem *p, const void *q, const void *k, int32_t 
                     void *stream);
 
 /* Work lists from index sets (block = 64).  For query block b (rows r0 = 64b to
- * r1 = 64b+63), each selected offset o <= r1 needs keys [max(0, r0-o), r1-o];
+ * r1 = min(64b+63, N-1)), each selected offset o <= r1 needs keys [max(0, r0-o), r1-o];
  * visiting those ranges by descending o, a range not yet covered emits a
  * 64-wide block starting at max(range start, end of the previous block).
  * Columns: every selected j <= r1 outside all emitted blocks, ascending.
@@ -125,9 +128,9 @@ int msa_estimate_vs(const msa_problem *p, const void *q, const void *k, int32_t 
  * principles 1-2); the covering rule itself is this library's reading.
  *   v_idx [n_q_heads, vertical_topk], s_idx [n_q_heads, slash_topk]: ascending,
  *     distinct, in [0, N); out-of-range entries are ignored.
- *   block_count, column_count [n_q_heads, N/64] int32
- *   block_offset [n_q_heads, N/64, cap_blocks] int32 (key start of each block)
- *   column_index [n_q_heads, N/64, cap_cols] int32
+ *   block_count, column_count [n_q_heads, ceil(N/64)] int32
+ *   block_offset [n_q_heads, ceil(N/64), cap_blocks] int32 (key start of each block)
+ *   column_index [n_q_heads, ceil(N/64), cap_cols] int32
  * Entries past each count are unspecified.                                  */
 int msa_build_index(const msa_problem *p, const int32_t *v_idx, int32_t vertical_topk,
                     const int32_t *s_idx, int32_t slash_topk, int32_t block,

@@ -47,7 +47,7 @@ def status_of(lib, fn, *args):
 
 
 def test_problem_validation(lib):
-    for prob, want in [(P(d=64), SHAPE), (P(hq=6, hkv=4), SHAPE), (P(n=100), SHAPE), (P(n=0), SHAPE),
+    for prob, want in [(P(d=64), SHAPE), (P(hq=6, hkv=4), SHAPE), (P(n=0), SHAPE),
                        (P(n=1 << 31), SHAPE), (P(dtype=7), DTYPE), (P(scale=-1.0), RANGE),
                        (P(hkv=0), SHAPE)]:
         assert lib.msa_dense_prefill(prob, FAKE, FAKE, FAKE, FAKE, None, None) == want
@@ -55,6 +55,11 @@ def test_problem_validation(lib):
     assert lib.msa_dense_prefill(None, FAKE, FAKE, FAKE, FAKE, None, None) == NULL
     assert lib.msa_dense_prefill(P(), None, FAKE, FAKE, FAKE, None, None) == NULL
     assert lib.msa_status_str(SHAPE) == b"MSA_ERR_SHAPE"
+    # a length that is not a multiple of 64 passes the shared checks but not the
+    # estimators' (they need whole 64-key tiles)
+    assert lib.msa_estimate_vs(P(n=100), FAKE, FAKE, 64, 8, 8, FAKE, FAKE, None, None, FAKE, 1 << 30,
+                               None) == SHAPE
+    assert lib.msa_estimate_bs(P(n=100), FAKE, FAKE, 64, 2, FAKE, FAKE, 2, FAKE, FAKE, 1 << 30, None) == SHAPE
 
 
 def test_index_caps(lib):
@@ -65,6 +70,9 @@ def test_index_caps(lib):
     assert (cb.value, cc.value) == (64, 64)
     assert lib.msa_index_caps(P(n=4096), 64, 256, 32, ctypes.byref(cb), ctypes.byref(cc)) == RANGE
     assert lib.msa_index_caps(P(n=4096), 5000, 256, 64, ctypes.byref(cb), ctypes.byref(cc)) == RANGE
+    # a short last query block counts as a block
+    assert lib.msa_index_caps(P(n=64 * 3 + 5), 10, 150, 64, ctypes.byref(cb), ctypes.byref(cc)) == OK
+    assert (cb.value, cc.value) == (4, 10)
 
 
 def test_build_index_validation(lib):

@@ -110,6 +110,45 @@ def test_recall_from_lse():
     assert np.abs(got - want).max() <= 3e-4
 
 
+# ------------------------------------------------ lengths not a multiple of 64
+
+@pytest.mark.parametrize("hq,hkv,n,fp32", [(4, 2, 64 * 5 + 23, False), (1, 1, 37, False),
+                                           (2, 1, 64 * 4 + 1, True), (8, 2, 1000, False)])
+def test_dense_prefill_ragged(hq, hkv, n, fp32):
+    w, q, k, v = inputs(hq, hkv, n, seed=n + 3, fp32=fp32)
+    out, lse = msa.dense_prefill(*cuda(q, k, v), lse=True)
+    ref, rlse = oracle.dense_attention(q, k, v)
+    compare_out(out.float().cpu().numpy(), ref, fp32, "dense ragged")
+    compare_lse(lse.cpu().numpy(), rlse, "dense ragged")
+
+
+@pytest.mark.parametrize("hq,n,kv,ks,seed", [(2, 64 * 5 + 23, 7, 40, 0), (3, 1000, 50, 300, 1),
+                                             (1, 37, 5, 20, 2)])
+def test_build_index_ragged(hq, n, kv, ks, seed):
+    vi, si = random_sets(hq, n, kv, ks, seed)
+    ridx = oracle.build_index(vi, si, n)
+    gidx = msa.build_index(*cuda(torch.from_numpy(vi), torch.from_numpy(si)), n)
+    compare_index(gidx, ridx, "build_index ragged")
+
+
+@pytest.mark.parametrize("hq,hkv,n,kv,ks,phase,fp32", [
+    (4, 2, 64 * 7 + 23, 20, 60, 0, False),
+    (2, 1, 64 * 9 + 63, 30, 100, 128, False),     # key phases, short last block
+    (2, 1, 50, 5, 10, 0, False),                  # shorter than one block
+    (2, 1, 64 * 3 + 40, 9, 13, 0, True),
+])
+def test_sparse_prefill_ragged(hq, hkv, n, kv, ks, phase, fp32):
+    w, q, k, v = inputs(hq, hkv, n, seed=n + 5, fp32=fp32)
+    vi, si = random_sets(hq, n, kv, ks, seed=n + 6)
+    ridx = oracle.build_index(vi, si, n)
+    gidx = msa.build_index(*cuda(torch.from_numpy(vi), torch.from_numpy(si)), n)
+    compare_index(gidx, ridx, "index ragged")
+    out, lse = msa.sparse_prefill(*cuda(q, k, v), gidx, lse=True, phase_keys=phase)
+    ref, rlse = oracle.attention_with_mask(q, k, v, oracle.index_mask(ridx, n))
+    compare_out(out.float().cpu().numpy(), ref, fp32, "sparse ragged")
+    compare_lse(lse.cpu().numpy(), rlse, "sparse ragged")
+
+
 def test_sparse_all_selected_equals_dense():
     n = 512
     w, q, k, v = inputs(4, 2, n, seed=3)
