@@ -86,7 +86,7 @@ const char *msa_status_str(int status);
 const char *msa_last_error(void);
 
 /* Capacities of the work lists for one query block (block = 64):
- *   cap_blocks = min(slash_topk, seq_len / 64)   (blocks are disjoint and start
+ *   cap_blocks = min(slash_topk, ceil(seq_len / 64))   (blocks are disjoint and start
  *                at or before the block's last row, so at most b+1 of them)
  *   cap_cols   = min(vertical_topk, seq_len).                               */
 int msa_index_caps(const msa_problem *p, int32_t vertical_topk, int32_t slash_topk, int32_t block,
