@@ -69,6 +69,32 @@ __device__ __forceinline__ void start_tile(unsigned char *buf, const T *kp, int6
     for (int i = 0; i < Gm::kPer; i += 4) dma_x4(tb, off[i], off[i + 1], off[i + 2], off[i + 3], l0 + i * 1024);
 }
 
+// The copy of the frame tile at vbase (frame keys vbase .. vbase+63 are
+// sequence keys vbase - pad ..): a tile reaching before key 0 (the first one
+// when pad > 0) reads key 0 for the missing rows, whose scores are masked.
+template <typename T>
+__device__ __forceinline__ void start_frame_tile(unsigned char *buf, const T *kp, int64_t vbase, int pad,
+                                                 int wave, const uint32_t (&off)[KGeo<T>::kPer], int lane) {
+    using Gm = KGeo<T>;
+    const int64_t rbase = vbase - pad;
+    if (rbase >= 0) {
+        start_tile<T>(buf, kp, rbase, wave, off);
+        return;
+    }
+    const char *rows = reinterpret_cast<const char *>(kp);
+    const int sub = lane / Gm::kChunks;
+    const uint32_t l0 = lds_addr(buf) + wave * 16 * Gm::kRowBytes;
+    const char *ad[Gm::kPer];
+#pragma unroll
+    for (int i = 0; i < Gm::kPer; ++i) {
+        const int r = i * Gm::kRowsPerSlot + sub;                     // row of this wave's 16
+        const int64_t row = max(rbase + wave * 16 + r, (int64_t)0);
+        ad[i] = rows + row * Gm::kRowBytes + (off[i] - (uint32_t)(r * Gm::kRowBytes));
+    }
+#pragma unroll
+    for (int i = 0; i < Gm::kPer; i += 4) dma_x4(ad[i], ad[i + 1], ad[i + 2], ad[i + 3], l0 + i * 1024);
+}
+
 template <typename T>
 __device__ __forceinline__ void copy_offsets(uint32_t (&off)[KGeo<T>::kPer], int lane) {
     using Gm = KGeo<T>;
@@ -106,9 +132,10 @@ void est_pass1_kernel(EstArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int range = blockIdx.x, g = blockIdx.y;
     const int G = a.hq / a.hkv;
-    const int64_t n = a.n;
-    const int64_t k0 = (int64_t)range * a.range_keys;
-    const int64_t k1 = min(n, k0 + a.range_keys);
+    const int64_t n = a.n, nv = a.nv;                   // sequence keys, frame keys
+    const int pad = a.pad;
+    const int64_t k0 = (int64_t)range * a.range_keys;   // frame keys of this range
+    const int64_t k1 = min(nv, k0 + a.range_keys);
     const int ntile = (int)((k1 - k0) / kTK);
     const T *kp = reinterpret_cast<const T *>(a.k) + (int64_t)g * n * kD;
     uint32_t off[Gm::kPer];
@@ -127,15 +154,16 @@ void est_pass1_kernel(EstArgs a) {
         __builtin_amdgcn_s_waitcnt(kVmcnt0);        // Q has landed (compiler-visible wait)
         float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
         __syncthreads();                            // the previous slot is done with both buffers
-        start_tile<T>(sm.k[0], kp, k0, wave, off);
+        start_frame_tile<T>(sm.k[0], kp, k0, pad, wave, off, lane);
         for (int t = 0; t < ntile; ++t) {
             const int64_t base = k0 + (int64_t)t * kTK;
             vm_wait<0>();
             __syncthreads();                        // tile t visible; tile t-1's buffer is free
-            if (t + 1 < ntile) start_tile<T>(sm.k[(t + 1) & 1], kp, base + kTK, wave, off);
+            if (t + 1 < ntile) start_frame_tile<T>(sm.k[(t + 1) & 1], kp, base + kTK, pad, wave, off, lane);
             if (!active) continue;
             const unsigned char *buf = sm.k[t & 1];
-            const bool last = base + kTK > n - kL;  // keys past some p_r
+            const bool last = base + kTK > nv - kL;  // keys past some p_r
+            const bool before = base < pad;         // frame keys before key 0
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 f32x16 s[2];
@@ -146,13 +174,15 @@ void est_pass1_kernel(EstArgs a) {
 #pragma unroll
                     for (int dk = 0; dk < 8; ++dk) E::mma(s[kt], k_frag<T>(buf, kt, dk, l32, hl), qf[half][dk]);
                 }
-                if (last) {
-                    const int64_t prow = n - kL + half * 32 + l32;
+                if (last || before) {
+                    const int64_t prow = nv - kL + half * 32 + l32;
 #pragma unroll
                     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                        for (int i = 0; i < 16; ++i)
-                            if (base + kt * 32 + (i >> 2) * 8 + hl * 4 + (i & 3) > prow) s[kt][i] = -INFINITY;
+                        for (int i = 0; i < 16; ++i) {
+                            const int64_t key = base + kt * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
+                            if (key > prow || key < pad) s[kt][i] = -INFINITY;
+                        }
                 }
                 float mx = -INFINITY;
 #pragma unroll
@@ -243,9 +273,10 @@ __global__ __launch_bounds__(kThreads2) void est_pass2_kernel(EstArgs a) {
     const int hs = wave >> 1, hf = wave & 1;                    // head slot, row half
     const int range = blockIdx.x, g = blockIdx.y;
     const int G = a.hq / a.hkv;
-    const int64_t n = a.n;
-    const int64_t k0 = (int64_t)range * a.range_keys;
-    const int64_t k1 = min(n, k0 + a.range_keys);
+    const int64_t n = a.n, nv = a.nv;                          // sequence keys, frame keys
+    const int pad = a.pad;
+    const int64_t k0 = (int64_t)range * a.range_keys;           // frame keys of this range
+    const int64_t k1 = min(nv, k0 + a.range_keys);
     const int ntile = (int)((k1 - k0) / kTK);
     const T *kp = reinterpret_cast<const T *>(a.k) + (int64_t)g * n * kD;
     const bool loader = wave < 4;                               // waves 0-3 copy the K tiles
@@ -285,8 +316,8 @@ __global__ __launch_bounds__(kThreads2) void est_pass2_kernel(EstArgs a) {
             const float vt = v_own + xs[lane];
             const float dg1 = d1_own + xs[64 + lane], dg2 = d2_own + xs[128 + lane];
             const int64_t base = k0 + (int64_t)t * kTK;
-            vout[base + lane] = vt;
-            const int64_t A = n - kL - base;                     // offset of diagonal D = 0
+            if (base + lane >= pad) vout[base + lane - pad] = vt; // frame key -> sequence key
+            const int64_t A = nv - kL - base;                    // offset of diagonal D = 0
             if (lane == 63) {
                 sout[A] = dg1;                                   // D = 0 lies in this tile only
             } else {
@@ -294,7 +325,8 @@ __global__ __launch_bounds__(kThreads2) void est_pass2_kernel(EstArgs a) {
                 if (t > 0) {
                     sout[o2] = dg2 + carry;
                 } else if (range == 0) {
-                    sout[o2] = dg2;                              // keys below 0 do not exist
+                    // keys below 0 do not exist; offsets from n on reach no key
+                    if (o2 < n) sout[o2] = dg2;
                 } else {
                     a.diag_hi[((int64_t)h * a.nranges + range) * 64 + lane] = dg2;
                 }
@@ -318,7 +350,7 @@ __global__ __launch_bounds__(kThreads2) void est_pass2_kernel(EstArgs a) {
                     const int r = (x >> 2) * 8 + hl * 4 + (x & 3);
                     float p = __builtin_amdgcn_exp2f(fmaf(sc[x], a.scale_log2, -nrm[x]));
                     if constexpr (decltype(masked)::value)
-                        if (base + e > n - kL + hf * 32 + r) p = 0.f;
+                        if (base + e > nv - kL + hf * 32 + r || base + e < pad) p = 0.f;
                     vk[kt] += p;
                     pw[r * kSkew + e - r + 31] = p;
                 }
@@ -337,16 +369,18 @@ __global__ __launch_bounds__(kThreads2) void est_pass2_kernel(EstArgs a) {
             return f32x4{__uint_as_float(sw[0]) + __uint_as_float(sw[1]), d1 * use1, d2 * use2, 0.f};
         };
         __syncthreads();                            // the previous slot is done with every buffer
-        if (loader) start_tile<T>(sm.k[0], kp, k0, wave, off);
+        if (loader) start_frame_tile<T>(sm.k[0], kp, k0, pad, wave, off, lane);
         for (int t = 0; t < ntile; ++t) {
             const int64_t base = k0 + (int64_t)t * kTK;
             vm_wait<0>();
             __syncthreads();                        // tile t visible; half-1 partials of t-1 visible
-            if (Sm::kKBuf == 2 && loader && t + 1 < ntile) start_tile<T>(sm.k[(t + 1) & 1], kp, base + kTK, wave, off);
+            if (Sm::kKBuf == 2 && loader && t + 1 < ntile)
+                start_frame_tile<T>(sm.k[(t + 1) & 1], kp, base + kTK, pad, wave, off, lane);
             if (active && hf == 0 && t > 0) finish(t - 1);
             if (active) {
                 const unsigned char *buf = sm.k[Sm::kKBuf == 2 ? (t & 1) : 0];
-                const f32x4 r = base + kTK > n - kL ? tile(buf, base, std::true_type{}) : tile(buf, base, std::false_type{});
+                const f32x4 r = (base + kTK > nv - kL || base < pad) ? tile(buf, base, std::true_type{})
+                                                                      : tile(buf, base, std::false_type{});
                 if (hf == 0) {
                     v_own = r[0];
                     d1_own = r[1];
@@ -360,7 +394,7 @@ __global__ __launch_bounds__(kThreads2) void est_pass2_kernel(EstArgs a) {
             }
             if (Sm::kKBuf == 1) {
                 __syncthreads();                    // every wave is done with the single tile buffer
-                if (loader && t + 1 < ntile) start_tile<T>(sm.k[0], kp, base + kTK, wave, off);
+                if (loader && t + 1 < ntile) start_frame_tile<T>(sm.k[0], kp, base + kTK, pad, wave, off, lane);
             }
         }
         __syncthreads();                            // half-1 partials of the last tile
@@ -381,8 +415,9 @@ __global__ __launch_bounds__(256) void est_fixup_kernel(EstArgs a) {
     const int64_t rem = t % per_h;
     const int range = 1 + (int)(rem / 63);
     const int lane = (int)(rem % 63);
-    const int64_t A = a.n - kL - (int64_t)range * a.range_keys;
-    const int64_t o = A + lane + 1;
+    const int64_t A = a.nv - kL - (int64_t)range * a.range_keys;
+    const int64_t o = A + lane + 1;                     // below n: range >= 1 starts past frame key 255
+    if (o >= a.n) return;
     a.s_score[(int64_t)h * a.n + o] = a.diag_hi[((int64_t)h * a.nranges + range) * 64 + lane] +
                                       a.diag_lo[((int64_t)h * a.nranges + range - 1) * 64 + lane];
 }

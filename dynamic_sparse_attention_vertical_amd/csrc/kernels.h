@@ -36,7 +36,12 @@ hipError_t launch_dense_prefill(const AttnArgs &a, int dtype, hipStream_t s);
 
 struct EstArgs {
     const void *q, *k;
-    int64_t n;
+    int64_t n;           // keys (and rows of Q, K and the score arrays)
+    // Keys are tiled in a frame shifted by pad = nv - n (nv: n rounded up to
+    // 64), so that tiles end at key n - 1 as the last 64 query rows do; frame
+    // keys 0 .. pad-1 do not exist and score zero.
+    int64_t nv;
+    int32_t pad;
     int32_t hq, hkv;
     float scale_log2;
     int64_t range_keys;  // keys per workgroup range (multiple of 64)

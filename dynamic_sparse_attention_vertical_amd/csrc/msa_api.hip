@@ -67,13 +67,14 @@ struct EstLayout {
 EstLayout est_layout(const msa_problem *p) {
     EstLayout L;
     const int64_t n = p->seq_len;
-    int64_t rk = (n * p->n_kv_heads + 511) / 512;
+    const int64_t nv = (n + 63) / 64 * 64;            // keys tiled in 64s, ending at key n-1
+    int64_t rk = (nv * p->n_kv_heads + 511) / 512;
     rk = ((rk + 63) / 64) * 64;
     if (rk < 256) rk = 256;
     if (rk > 8192) rk = 8192;
-    if (rk > n) rk = n;
+    if (rk > nv) rk = nv;
     L.range_keys = rk;
-    L.nranges = (int32_t)((n + rk - 1) / rk);
+    L.nranges = (int32_t)((nv + rk - 1) / rk);
     L.nslices = (int32_t)((n + msa::kTopkSlice - 1) / msa::kTopkSlice);
     const size_t hq = (size_t)p->n_q_heads;
     size_t o = 0;
@@ -148,9 +149,8 @@ int msa_estimate_vs(const msa_problem *p, const void *q, const void *k, int32_t 
     if (st) return st;
     if (!q || !k || !v_idx || !s_idx || !workspace) return fail(MSA_ERR_NULL, "a required pointer is NULL");
     if (last_q != 64) return fail(MSA_ERR_RANGE, "last_q must be 64 (got %d)", last_q);
-    if (p->seq_len % 64 != 0)
-        return fail(MSA_ERR_SHAPE, "seq_len must be a multiple of 64 for the estimate (got %lld)",
-                    (long long)p->seq_len);
+    if (p->seq_len < 64)
+        return fail(MSA_ERR_SHAPE, "seq_len must be at least last_q = 64 (got %lld)", (long long)p->seq_len);
     if (vertical_topk < 1 || vertical_topk > p->seq_len || slash_topk < 1 || slash_topk > p->seq_len)
         return fail(MSA_ERR_RANGE, "top-k values must lie in [1, seq_len]");
     const EstLayout L = est_layout(p);
@@ -160,6 +160,8 @@ int msa_estimate_vs(const msa_problem *p, const void *q, const void *k, int32_t 
     e.q = q;
     e.k = k;
     e.n = p->seq_len;
+    e.nv = (p->seq_len + 63) / 64 * 64;
+    e.pad = (int32_t)(e.nv - e.n);
     e.hq = p->n_q_heads;
     e.hkv = p->n_kv_heads;
     e.scale_log2 = scale_of(p) * msa::kLog2e;

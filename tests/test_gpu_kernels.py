@@ -214,7 +214,11 @@ def test_build_index_a_shape():
 
 
 @pytest.mark.parametrize("hq,hkv,n,fp32", [(4, 1, 256, False), (4, 2, 1024, False), (8, 2, 4096, False),
-                                           (2, 1, 2048, True), (1, 1, 64, False), (4, 4, 8192, False)])
+                                           (2, 1, 2048, True), (1, 1, 64, False), (4, 4, 8192, False),
+                                           # lengths not a multiple of 64: keys tiled in a shifted frame
+                                           (4, 1, 64 * 4 + 23, False), (2, 1, 64 * 9 + 1, True),
+                                           (4, 2, 100, False), (1, 1, 127, False),
+                                           (8, 2, 64 * 70 + 40, False)])   # 18 key ranges
 def test_estimate_scores(hq, hkv, n, fp32):
     w, q, k, _ = inputs(hq, hkv, n, seed=n + 5, fp32=fp32)
     qs, ks_ = cuda(q, k)
