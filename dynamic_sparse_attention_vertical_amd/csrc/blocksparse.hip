@@ -23,7 +23,7 @@ constexpr int kThreads = 256;
 
 template <typename T>
 __global__ __launch_bounds__(kD) void bs_pool_kernel(BsArgs a) {
-    const int64_t nb = a.n / 64;
+    const int64_t nb = (a.n + 63) / 64;
     const int c = blockIdx.x;
     const int head = blockIdx.y;
     const int d = threadIdx.x;
@@ -36,13 +36,15 @@ __global__ __launch_bounds__(kD) void bs_pool_kernel(BsArgs a) {
         src = reinterpret_cast<const T *>(a.k) + (int64_t)(head - a.hq) * a.n * kD;
         dst = a.km + ((int64_t)(head - a.hq) * nb + c) * kD;
     }
+    // a short last block (length not a multiple of 64) is the mean of its rows
+    const int nrows = (int)min((int64_t)64, a.n - (int64_t)c * 64);
     float acc = 0.f;
-    for (int r = 0; r < 64; ++r) {
+    for (int r = 0; r < nrows; ++r) {
         const T x = src[((int64_t)c * 64 + r) * kD + d];
         if constexpr (sizeof(T) == 2) acc += bf16_to_f32(x.x);
         else acc += x;
     }
-    dst[d] = acc * (1.f / 64.f);
+    dst[d] = nrows == 64 ? acc * (1.f / 64.f) : acc / (float)nrows;
 }
 
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -71,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void bs_select_kernel(BsArgs a) {
     __shared__ uint32_t hist[256];
     __shared__ uint32_t tmp[kThreads];
     __shared__ uint32_t sel_state[2];
-    const int64_t nb = a.n / 64;
+    const int64_t nb = (a.n + 63) / 64;
     const int64_t b = nb - 1 - blockIdx.x;          // heavy rows first
     const int h = blockIdx.y;
     const int G = a.hq / a.hkv;
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void bs_select_kernel(BsArgs a) {
 }
 
 template <typename T> hipError_t launch_t(const BsArgs &a, hipStream_t s) {
-    const int64_t nb = a.n / 64;
+    const int64_t nb = (a.n + 63) / 64;
     hipLaunchKernelGGL(bs_pool_kernel<T>, dim3((unsigned)nb, a.hq + a.hkv), dim3(kD), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -302,7 +302,7 @@ int msa_dense_prefill(const msa_problem *p, const void *q, const void *k, const 
 
 size_t msa_estimate_bs_workspace(const msa_problem *p, int32_t block) {
     if (check_problem(p) != MSA_OK || block != 64) return 0;
-    const size_t nb = (size_t)(p->seq_len / 64);
+    const size_t nb = (size_t)((p->seq_len + 63) / 64);
     return align_up((size_t)p->n_q_heads * nb * 128 * 4) + align_up((size_t)p->n_kv_heads * nb * 128 * 4);
 }
 
@@ -314,10 +314,7 @@ int msa_estimate_bs(const msa_problem *p, const void *q, const void *k, int32_t 
     if (!q || !k || !block_count || !block_offset || !column_count || !workspace)
         return fail(MSA_ERR_NULL, "a required pointer is NULL");
     if (block != 64) return fail(MSA_ERR_RANGE, "block must be 64 (got %d)", block);
-    if (p->seq_len % 64 != 0)
-        return fail(MSA_ERR_SHAPE, "seq_len must be a multiple of 64 for the estimate (got %lld)",
-                    (long long)p->seq_len);
-    const int64_t nb = p->seq_len / 64;
+    const int64_t nb = (p->seq_len + 63) / 64;
     if (nb > kBsMaxBlocks)
         return fail(MSA_ERR_SHAPE, "block-sparse estimation supports at most %lld key blocks",
                     (long long)kBsMaxBlocks);

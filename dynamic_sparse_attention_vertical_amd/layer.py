@@ -100,7 +100,7 @@ class MixedPlan:
 
     def __post_init__(self):
         n, hq = self.seq_len, len(self.patterns)
-        nqb = n // msa.BLOCK
+        nqb = (n + msa.BLOCK - 1) // msa.BLOCK
         caps = [(0, 0)]
         if "vs" in self.patterns:
             caps.append(msa.index_caps(n, self.vertical_topk, self.slash_topk, 1))
@@ -200,7 +200,7 @@ def block_sparse_attention(q, k, v, topk: int, *, stream=None):
     q4, k4, v4, squeeze = _batched(q, k, v)
     out = torch.empty_like(q4)
     hq, hkv, n = q4.shape[1], k4.shape[1], q4.shape[2]
-    idx = msa.alloc_index(hq, n, min(topk, n // msa.BLOCK), 0, q4.device)
+    idx = msa.alloc_index(hq, n, min(topk, (n + msa.BLOCK - 1) // msa.BLOCK), 0, q4.device)
     ws = torch.empty(max(msa.estimate_bs_workspace_bytes(hq, hkv, n, q4.dtype), 1), dtype=torch.uint8,
                      device=q4.device)
     aws_bytes = msa.sparse_prefill_workspace_bytes(hq, hkv, n, q4.dtype)

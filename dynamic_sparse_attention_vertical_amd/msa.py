@@ -285,7 +285,7 @@ def estimate_bs(q: torch.Tensor, k: torch.Tensor, topk_blocks: int, *, cap_block
     lib = load()
     p = _problem_of(q, k, sm_scale)
     hq, n = q.shape[0], q.shape[1]
-    nqb = n // BLOCK
+    nqb = (n + BLOCK - 1) // BLOCK
     if out is None:
         cap = cap_blocks if cap_blocks is not None else min(topk_blocks, nqb)
         out = alloc_index(hq, n, cap, 0, q.device)

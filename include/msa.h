@@ -25,8 +25,8 @@
  *  * Tensors are device memory owned by the caller, batch 1, contiguous
  *    [heads, seq_len, head_dim] row-major.  Q has n_q_heads heads; K and V have
  *    n_kv_heads; q head h reads kv head h / (n_q_heads / n_kv_heads).
- *  * head_dim must be 128; seq_len must be positive and below 2^31 (the two
- *    estimators need a multiple of 64); n_q_heads must be a multiple of
+ *  * head_dim must be 128; seq_len must be positive and below 2^31
+ *    (msa_estimate_vs needs at least 64); n_q_heads must be a multiple of
  *    n_kv_heads.  Query blocks are 64 rows; when seq_len is not a multiple of
  *    64 the last one is shorter (rows 64b .. seq_len-1), and per-block arrays
  *    have ceil(seq_len / 64) entries per head.
@@ -186,11 +186,11 @@ size_t msa_estimate_bs_workspace(const msa_problem *p, int32_t block);
 /* Block-sparse work lists (talk slides "System-Algorithm Co-design", patterns
  * slide: block-sparse heads; "MInference 1.0 README", kernel-only
  * block_sparse_attention(q, k, v, topk)).  Reading: with qm[b] and km[c] the
- * means of 64-row blocks of q and k, u[b, c] = sm_scale <qm[b], km[c]> for
- * c <= b; query block b keeps its min(topk_blocks, b+1) highest-scoring key
- * blocks (exact ties to the lower c), written as ascending key starts 64c.
- * column_count is set to 0.  block must be 64; cap_blocks >= min(topk_blocks,
- * N/64).                                                                    */
+ * means of 64-row blocks of q and k (a short last block: the mean of its
+ * rows), u[b, c] = sm_scale <qm[b], km[c]> for c <= b; query block b keeps its
+ * min(topk_blocks, b+1) highest-scoring key blocks (exact ties to the lower
+ * c), written as ascending key starts 64c.  column_count is set to 0.  block
+ * must be 64; cap_blocks >= min(topk_blocks, ceil(N/64)).                   */
 int msa_estimate_bs(const msa_problem *p, const void *q, const void *k, int32_t block,
                     int32_t topk_blocks, int32_t *block_count, int32_t *block_offset,
                     int32_t cap_blocks, int32_t *column_count, void *workspace,

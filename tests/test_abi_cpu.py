@@ -55,11 +55,9 @@ def test_problem_validation(lib):
     assert lib.msa_dense_prefill(None, FAKE, FAKE, FAKE, FAKE, None, None) == NULL
     assert lib.msa_dense_prefill(P(), None, FAKE, FAKE, FAKE, None, None) == NULL
     assert lib.msa_status_str(SHAPE) == b"MSA_ERR_SHAPE"
-    # the vertical-slash estimate needs last_q = 64 rows; the block-sparse one
-    # whole 64-row blocks
+    # the vertical-slash estimate needs last_q = 64 rows
     assert lib.msa_estimate_vs(P(n=40), FAKE, FAKE, 64, 8, 8, FAKE, FAKE, None, None, FAKE, 1 << 30,
                                None) == SHAPE
-    assert lib.msa_estimate_bs(P(n=100), FAKE, FAKE, 64, 2, FAKE, FAKE, 2, FAKE, FAKE, 1 << 30, None) == SHAPE
 
 
 def test_index_caps(lib):

@@ -63,6 +63,29 @@ def test_streaming_forward_batched(init_num, window):
         compare_out(out[bi].float().cpu().numpy(), ref, False, f"streaming batch {bi}")
 
 
+def test_api_ragged_lengths():
+    """Lengths that are not a multiple of 64 through the whole path: estimate,
+    index, sparse prefill; block-sparse; streaming."""
+    hq, hkv, n = 4, 1, 64 * 11 + 29
+    q, k, v = batch_inputs(1, hq, hkv, n, seed=61)
+    out = msa.vertical_slash_sparse_attention(q.cuda(), k.cuda(), v.cuda(), 30, 90)
+    ref_gpu, plan = msa.vertical_slash_layer(q[0].cuda(), k[0].cuda(), v[0].cuda(), 30, 90)
+    assert torch.equal(out[0], ref_gpu)
+    ref, _ = oracle.attention_with_mask(q[0], k[0], v[0], oracle.index_mask(to_oracle_index(plan.index), n))
+    compare_out(out[0].float().cpu().numpy(), ref, False, "vertical-slash ragged")
+    out = msa.block_sparse_attention(q.cuda(), k.cuda(), v.cuda(), 3)
+    cnt, offs, _ = oracle.block_sparse_select(q[0], k[0], range(hq), topk=3)
+    nb = (n + 63) // 64
+    idx = oracle.IndexArrays(cnt, offs, np.zeros_like(cnt), np.zeros((hq, nb, 0), np.int32))
+    ref, _ = oracle.attention_with_mask(q[0], k[0], v[0], oracle.index_mask(idx, n))
+    compare_out(out[0].float().cpu().numpy(), ref, False, "block-sparse ragged")
+    out = msa.streaming_forward(q.cuda(), k.cuda(), v.cuda(), 64, 200)
+    vs_, ss_ = oracle.a_shape_sets(n, 64, 200)
+    sidx = oracle.build_index(np.tile(vs_, (hq, 1)), np.tile(ss_, (hq, 1)), n)
+    ref, _ = oracle.attention_with_mask(q[0], k[0], v[0], oracle.index_mask(sidx, n))
+    compare_out(out[0].float().cpu().numpy(), ref, False, "streaming ragged")
+
+
 def test_batched_shape_errors():
     q = torch.zeros((2, 4, 256, 128), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(msa.MsaError):

@@ -278,7 +278,8 @@ def test_layer_end_to_end_small(fp32):
     compare_out(out.float().cpu().numpy(), ref, fp32, "layer")
 
 
-@pytest.mark.parametrize("n,topk", [(1024, 3), (2048, 100), (640, 4)])
+@pytest.mark.parametrize("n,topk", [(1024, 3), (2048, 100), (640, 4),
+                                    (64 * 5 + 23, 3), (100, 1), (64 * 10 + 1, 4)])   # short last blocks
 def test_estimate_bs(n, topk):
     hq, hkv = 4, 2
     w, q, k, v = inputs(hq, hkv, n, seed=n)
@@ -288,7 +289,7 @@ def test_estimate_bs(n, topk):
     bo = idx.block_offset.cpu().numpy()
     assert np.array_equal(bc, cnt)
     assert np.all(idx.column_count.cpu().numpy() == 0)
-    nb = n // 64
+    nb = (n + 63) // 64
     for h in range(hq):
         for b in range(nb):
             kk = bc[h, b]
