@@ -159,7 +159,8 @@ void est_pass1_kernel(EstArgs a) {
             const int64_t base = k0 + (int64_t)t * kTK;
             vm_wait<0>();
             __syncthreads();                        // tile t visible; tile t-1's buffer is free
-            if (t + 1 < ntile) start_frame_tile<T>(sm.k[(t + 1) & 1], kp, base + kTK, pad, wave, off, lane);
+            // tiles after a range's first start at frame key 64 or later: all rows exist
+            if (t + 1 < ntile) start_tile<T>(sm.k[(t + 1) & 1], kp, base + kTK - pad, wave, off);
             if (!active) continue;
             const unsigned char *buf = sm.k[t & 1];
             const bool last = base + kTK > nv - kL;  // keys past some p_r
@@ -374,8 +375,8 @@ __global__ __launch_bounds__(kThreads2) void est_pass2_kernel(EstArgs a) {
             const int64_t base = k0 + (int64_t)t * kTK;
             vm_wait<0>();
             __syncthreads();                        // tile t visible; half-1 partials of t-1 visible
-            if (Sm::kKBuf == 2 && loader && t + 1 < ntile)
-                start_frame_tile<T>(sm.k[(t + 1) & 1], kp, base + kTK, pad, wave, off, lane);
+            // tiles after a range's first start at frame key 64 or later: all rows exist
+            if (Sm::kKBuf == 2 && loader && t + 1 < ntile) start_tile<T>(sm.k[(t + 1) & 1], kp, base + kTK - pad, wave, off);
             if (active && hf == 0 && t > 0) finish(t - 1);
             if (active) {
                 const unsigned char *buf = sm.k[Sm::kKBuf == 2 ? (t & 1) : 0];
@@ -394,7 +395,7 @@ __global__ __launch_bounds__(kThreads2) void est_pass2_kernel(EstArgs a) {
             }
             if (Sm::kKBuf == 1) {
                 __syncthreads();                    // every wave is done with the single tile buffer
-                if (loader && t + 1 < ntile) start_frame_tile<T>(sm.k[0], kp, base + kTK, pad, wave, off, lane);
+                if (loader && t + 1 < ntile) start_tile<T>(sm.k[0], kp, base + kTK - pad, wave, off);
             }
         }
         __syncthreads();                            // half-1 partials of the last tile
