@@ -332,9 +332,9 @@ void attn_fwd_kernel(AttnArgs a) {
     const int r0 = (int)b * kBQ;
     const int qrow = r0 + (wave & 1) * 32 + l32;
 
-    const T *qp = reinterpret_cast<const T *>(a.q) + ((int64_t)h * n) * kD;
-    const T *kp = reinterpret_cast<const T *>(a.k) + ((int64_t)g * n) * kD;
-    const T *vp = reinterpret_cast<const T *>(a.v) + ((int64_t)g * n) * kD;
+    const T *qp = reinterpret_cast<const T *>(a.q) + ((int64_t)h * a.stride) * kD;
+    const T *kp = reinterpret_cast<const T *>(a.k) + ((int64_t)g * a.stride) * kD;
+    const T *vp = reinterpret_cast<const T *>(a.v) + ((int64_t)g * a.stride) * kD;
 
     int nblk, ncol;
     const int32_t *blist = nullptr, *clist = nullptr;
@@ -579,7 +579,7 @@ void attn_fwd_kernel(AttnArgs a) {
     const float l_tot = pair32_sum(l_i);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (qrow >= n32) return;                            // rows past the end of a short last block
-    T *op = reinterpret_cast<T *>(a.out) + ((int64_t)h * n + qrow) * kD;
+    T *op = reinterpret_cast<T *>(a.out) + ((int64_t)h * a.stride + qrow) * kD;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -589,7 +589,7 @@ void attn_fwd_kernel(AttnArgs a) {
                          o[dt][jj * 4 + 2] * inv, o[dt][jj * 4 + 3] * inv);
         }
     if (a.lse != nullptr && hl == 0)
-        a.lse[(int64_t)h * n + qrow] = l_tot > 0.f ? (mb_i * kLn2 + logf(l_tot)) : -INFINITY;
+        a.lse[(int64_t)h * a.stride + qrow] = l_tot > 0.f ? (mb_i * kLn2 + logf(l_tot)) : -INFINITY;
 #endif
 }
 

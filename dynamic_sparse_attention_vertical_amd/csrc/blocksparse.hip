@@ -30,10 +30,10 @@ __global__ __launch_bounds__(kD) void bs_pool_kernel(BsArgs a) {
     const T *src;
     float *dst;
     if (head < a.hq) {
-        src = reinterpret_cast<const T *>(a.q) + (int64_t)head * a.n * kD;
+        src = reinterpret_cast<const T *>(a.q) + (int64_t)head * a.stride * kD;
         dst = a.qm + ((int64_t)head * nb + c) * kD;
     } else {
-        src = reinterpret_cast<const T *>(a.k) + (int64_t)(head - a.hq) * a.n * kD;
+        src = reinterpret_cast<const T *>(a.k) + (int64_t)(head - a.hq) * a.stride * kD;
         dst = a.km + ((int64_t)(head - a.hq) * nb + c) * kD;
     }
     // a short last block (length not a multiple of 64) is the mean of its rows

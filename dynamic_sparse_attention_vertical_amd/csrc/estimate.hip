@@ -137,14 +137,14 @@ void est_pass1_kernel(EstArgs a) {
     const int64_t k0 = (int64_t)range * a.range_keys;   // frame keys of this range
     const int64_t k1 = min(nv, k0 + a.range_keys);
     const int ntile = (int)((k1 - k0) / kTK);
-    const T *kp = reinterpret_cast<const T *>(a.k) + (int64_t)g * n * kD;
+    const T *kp = reinterpret_cast<const T *>(a.k) + (int64_t)g * a.stride * kD;
     uint32_t off[Gm::kPer];
     copy_offsets<T>(off, lane);
     for (int slot = 0; slot < n_slots(G); ++slot) {
         const int hw = wave + 4 * slot;
         const bool active = hw < G;
         const int h = g * G + (active ? hw : 0);
-        const T *qp = reinterpret_cast<const T *>(a.q) + ((int64_t)h * n + (n - kL)) * kD;
+        const T *qp = reinterpret_cast<const T *>(a.q) + ((int64_t)h * a.stride + (n - kL)) * kD;
         typename E::frag qf[2][8];
 #pragma unroll
         for (int half = 0; half < 2; ++half)
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(kThreads2) void est_pass2_kernel(EstArgs a) {
     const int64_t k0 = (int64_t)range * a.range_keys;           // frame keys of this range
     const int64_t k1 = min(nv, k0 + a.range_keys);
     const int ntile = (int)((k1 - k0) / kTK);
-    const T *kp = reinterpret_cast<const T *>(a.k) + (int64_t)g * n * kD;
+    const T *kp = reinterpret_cast<const T *>(a.k) + (int64_t)g * a.stride * kD;
     const bool loader = wave < 4;                               // waves 0-3 copy the K tiles
     uint32_t off[Gm::kPer];
     copy_offsets<T>(off, lane);
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(kThreads2) void est_pass2_kernel(EstArgs a) {
         const int hw = hs + 4 * slot;
         const bool active = hw < G;
         const int h = g * G + (active ? hw : 0);
-        const T *qp = reinterpret_cast<const T *>(a.q) + ((int64_t)h * n + (n - kL)) * kD;
+        const T *qp = reinterpret_cast<const T *>(a.q) + ((int64_t)h * a.stride + (n - kL)) * kD;
         // A operand of S = Q K^T: query 32 hf + l32, d = dk*16 + hl*8 + e
         typename E::frag qf[8];
 #pragma unroll

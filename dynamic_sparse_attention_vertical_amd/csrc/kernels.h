@@ -14,6 +14,7 @@ struct AttnArgs {
     float *lse;
     int32_t hq, hkv;
     int64_t n;
+    int64_t stride;      // rows from one head's start to the next (q, k, v, out, lse)
     float scale_log2;    // sm_scale * log2(e)
     float scale;         // sm_scale
     // key phases of the sparse kernel (one launch each): block tiles whose
@@ -37,6 +38,7 @@ hipError_t launch_dense_prefill(const AttnArgs &a, int dtype, hipStream_t s);
 struct EstArgs {
     const void *q, *k;
     int64_t n;           // keys (and rows of Q, K and the score arrays)
+    int64_t stride;      // rows from one head's start to the next in Q and K
     // Keys are tiled in a frame shifted by pad = nv - n (nv: n rounded up to
     // 64), so that tiles end at key n - 1 as the last 64 query rows do; frame
     // keys 0 .. pad-1 do not exist and score zero.
@@ -85,6 +87,7 @@ hipError_t launch_build_index(const IndexArgs &a, hipStream_t s);
 struct BsArgs {
     const void *q, *k;
     int64_t n;
+    int64_t stride;              // rows from one head's start to the next in q and k
     int32_t hq, hkv;
     float scale;
     int32_t topk;

@@ -44,6 +44,9 @@ int check_problem(const msa_problem *p) {
         return fail(MSA_ERR_DTYPE, "unknown dtype %d", p->dtype);
     if (!(p->sm_scale >= 0.f) || isinf(p->sm_scale))
         return fail(MSA_ERR_RANGE, "sm_scale must be finite and >= 0");
+    if (p->seq_stride != 0 && p->seq_stride < p->seq_len)
+        return fail(MSA_ERR_SHAPE, "seq_stride (%lld) must be 0 or at least seq_len (%lld)",
+                    (long long)p->seq_stride, (long long)p->seq_len);
     return MSA_OK;
 }
 
@@ -133,6 +136,9 @@ int msa_index_caps(const msa_problem *p, int32_t vertical_topk, int32_t slash_to
     return ok();
 }
 
+// rows from one head's start to the next
+static int64_t stride_of(const msa_problem *p) { return p->seq_stride ? p->seq_stride : p->seq_len; }
+
 size_t msa_estimate_vs_workspace(const msa_problem *p, int32_t last_q, int32_t vertical_topk,
                                  int32_t slash_topk) {
     (void)vertical_topk;
@@ -160,6 +166,7 @@ int msa_estimate_vs(const msa_problem *p, const void *q, const void *k, int32_t 
     e.q = q;
     e.k = k;
     e.n = p->seq_len;
+    e.stride = stride_of(p);
     e.nv = (p->seq_len + 63) / 64 * 64;
     e.pad = (int32_t)(e.nv - e.n);
     e.hq = p->n_q_heads;
@@ -235,6 +242,7 @@ static int attn_common(const msa_problem *p, const void *q, const void *k, const
     a.hq = p->n_q_heads;
     a.hkv = p->n_kv_heads;
     a.n = p->seq_len;
+    a.stride = stride_of(p);
     a.scale = scale_of(p);
     a.scale_log2 = a.scale * msa::kLog2e;
     a.phase_keys = 0;
@@ -327,6 +335,7 @@ int msa_estimate_bs(const msa_problem *p, const void *q, const void *k, int32_t 
     a.q = q;
     a.k = k;
     a.n = p->seq_len;
+    a.stride = stride_of(p);
     a.hq = p->n_q_heads;
     a.hkv = p->n_kv_heads;
     a.scale = scale_of(p);

@@ -170,8 +170,24 @@ def mixed_layer(q, k, v, plan: MixedPlan, *, out: torch.Tensor | None = None, ls
 # The README's kernel-only calls ("MInference 1.0 README", section "How to use
 # MInference", kernel-only usage: vertical_slash_sparse_attention,
 # block_sparse_attention, streaming_forward), on [batch, heads, seq, dim] or
-# [heads, seq, dim] tensors.  Batch elements run one after another on the
-# stream through the same C-ABI steps, sharing one set of buffers.
+# [heads, seq, dim] tensors, or on a packed batch of sequences of different
+# lengths ([heads, total, dim] with cu_seqlens, sequence i being rows
+# cu_seqlens[i] .. cu_seqlens[i+1]-1).  Sequences run one after another on
+# the stream through the same C-ABI steps; a packed sequence is a view of the
+# packed tensors (the C ABI's seq_stride is the packed length).
+
+
+def _packed(q, k, v, cu_seqlens, fn):
+    """Run fn(q_i, k_i, v_i, out_i) on each packed sequence i."""
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise msa.MsaError("packed q, k, v must be [heads, total, dim]")
+    cu = [int(x) for x in (cu_seqlens.tolist() if hasattr(cu_seqlens, "tolist") else cu_seqlens)]
+    if len(cu) < 2 or cu[0] != 0 or cu[-1] != q.shape[1] or any(b <= a for a, b in zip(cu, cu[1:])):
+        raise msa.MsaError("cu_seqlens must rise strictly from 0 to the packed length")
+    out = torch.empty_like(q)
+    for a, b in zip(cu, cu[1:]):
+        fn(q[:, a:b], k[:, a:b], v[:, a:b], out[:, a:b])
+    return out
 
 def _batched(q, k, v):
     if q.dim() == 3:
@@ -181,10 +197,18 @@ def _batched(q, k, v):
     return q, k, v, False
 
 
-def vertical_slash_sparse_attention(q, k, v, vertical_topk: int, slash_topk: int, *, stream=None):
+def vertical_slash_sparse_attention(q, k, v, vertical_topk: int, slash_topk: int, *, cu_seqlens=None,
+                                    stream=None):
     """Vertical-slash sparse attention: per head, the vertical_topk key columns
     and slash_topk diagonals the online estimate selects, then causal
     attention over their 64-wide block cover.  Returns the attention output."""
+    if cu_seqlens is not None:
+        def one(qi, ki, vi, oi):
+            plan = LayerPlan(qi.shape[0], ki.shape[0], qi.shape[1], min(vertical_topk, qi.shape[1]),
+                             min(slash_topk, qi.shape[1]), str(qi.device), qi.dtype)
+            vertical_slash_layer(qi, ki, vi, plan.vertical_topk, plan.slash_topk, plan=plan, out=oi,
+                                 stream=stream)
+        return _packed(q, k, v, cu_seqlens, one)
     q4, k4, v4, squeeze = _batched(q, k, v)
     out = torch.empty_like(q4)
     plan = LayerPlan(q4.shape[1], k4.shape[1], q4.shape[2], vertical_topk, slash_topk, str(q4.device), q4.dtype)
@@ -194,9 +218,14 @@ def vertical_slash_sparse_attention(q, k, v, vertical_topk: int, slash_topk: int
     return out[0] if squeeze else out
 
 
-def block_sparse_attention(q, k, v, topk: int, *, stream=None):
+def block_sparse_attention(q, k, v, topk: int, *, cu_seqlens=None, stream=None):
     """Block-sparse attention: each 64-row query block attends to its topk
     highest-scoring 64-key blocks (mean-pooled q and k block scores), causally."""
+    if cu_seqlens is not None:
+        def one(qi, ki, vi, oi):
+            idx = msa.estimate_bs(qi, ki, topk, stream=stream)
+            msa.sparse_prefill(qi, ki, vi, idx, out=oi, stream=stream)
+        return _packed(q, k, v, cu_seqlens, one)
     q4, k4, v4, squeeze = _batched(q, k, v)
     out = torch.empty_like(q4)
     hq, hkv, n = q4.shape[1], k4.shape[1], q4.shape[2]
@@ -211,10 +240,15 @@ def block_sparse_attention(q, k, v, topk: int, *, stream=None):
     return out[0] if squeeze else out
 
 
-def streaming_forward(q, k, v, init_num: int, local_window_num: int, *, stream=None):
+def streaming_forward(q, k, v, init_num: int, local_window_num: int, *, cu_seqlens=None, stream=None):
     """A-shape (streaming) attention: every row attends to the first init_num
     keys and to the local_window_num keys ending at itself (diagonal offsets
     0 .. local_window_num - 1), causally, over their 64-wide block cover."""
+    if cu_seqlens is not None:
+        def one(qi, ki, vi, oi):
+            n = qi.shape[1]
+            _streaming_into(qi, ki, vi, min(init_num, n), min(local_window_num, n), oi, stream)
+        return _packed(q, k, v, cu_seqlens, one)
     q4, k4, v4, squeeze = _batched(q, k, v)
     hq, hkv, n = q4.shape[1], k4.shape[1], q4.shape[2]
     if not (1 <= init_num <= n and 1 <= local_window_num <= n):
@@ -229,3 +263,13 @@ def streaming_forward(q, k, v, init_num: int, local_window_num: int, *, stream=N
     for bi in range(q4.shape[0]):
         msa.sparse_prefill(q4[bi], k4[bi], v4[bi], idx, out=out[bi], workspace=aws, stream=stream)
     return out[0] if squeeze else out
+
+
+def _streaming_into(q, k, v, init_num, local_window_num, out, stream):
+    """streaming_forward for one [heads, seq, dim] sequence, written into out."""
+    hq, n = q.shape[0], q.shape[1]
+    i32 = dict(dtype=torch.int32, device=q.device)
+    vi = torch.arange(init_num, **i32).expand(hq, -1).contiguous()
+    si = torch.arange(local_window_num, **i32).expand(hq, -1).contiguous()
+    idx = msa.build_index(vi, si, n, stream=stream)
+    msa.sparse_prefill(q, k, v, idx, out=out, stream=stream)

@@ -31,7 +31,7 @@ class MsaError(RuntimeError):
 class Problem(ctypes.Structure):
     _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("seq_len", ctypes.c_int64), ("head_dim", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("sm_scale", ctypes.c_float)]
+                ("dtype", ctypes.c_int32), ("sm_scale", ctypes.c_float), ("seq_stride", ctypes.c_int64)]
 
 
 _VP = ctypes.c_void_p
@@ -90,14 +90,64 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise MsaError(f"unsupported dtype {t.dtype}")
 
 
-def problem(n_q_heads: int, n_kv_heads: int, seq_len: int, dtype: int, sm_scale: float = 0.0) -> Problem:
-    return Problem(n_q_heads, n_kv_heads, seq_len, HEAD_DIM, dtype, sm_scale)
+def problem(n_q_heads: int, n_kv_heads: int, seq_len: int, dtype: int, sm_scale: float = 0.0,
+            seq_stride: int = 0) -> Problem:
+    return Problem(n_q_heads, n_kv_heads, seq_len, HEAD_DIM, dtype, sm_scale, seq_stride)
 
 
-def _problem_of(q: torch.Tensor, k: torch.Tensor, sm_scale: float) -> Problem:
+def _head_stride(t: torch.Tensor, name: str) -> int:
+    """Rows from one head's start to the next for a [heads, seq, 128] tensor
+    whose rows are contiguous (a whole tensor, or a slice of a packed one)."""
+    if t.dim() != 3 or t.shape[2] != HEAD_DIM or t.stride(2) != 1 or t.stride(1) != HEAD_DIM or \
+            t.stride(0) % HEAD_DIM != 0:
+        raise MsaError(f"{name} must be [heads, seq_len, {HEAD_DIM}] with contiguous rows")
+    return t.stride(0) // HEAD_DIM if t.shape[0] > 1 else t.shape[1]
+
+
+def _problem_of(q: torch.Tensor, k: torch.Tensor, sm_scale: float, v: torch.Tensor | None = None) -> Problem:
     if q.dim() != 3 or k.dim() != 3:
         raise MsaError("q and k must be [heads, seq_len, head_dim]")
-    return problem(q.shape[0], k.shape[0], q.shape[1], _dtype_code(q), sm_scale)
+    n = q.shape[1]
+    sq = _head_stride(q, "q")
+    rows = {sq} | ({_head_stride(k, "k")} if k.shape[0] > 1 else set()) | \
+        ({_head_stride(v, "v")} if v is not None and v.shape[0] > 1 else set())
+    if len(rows) != 1:
+        raise MsaError("q, k and v must have the same head stride")
+    return problem(q.shape[0], k.shape[0], n, _dtype_code(q), sm_scale, 0 if sq == n else sq)
+
+
+def _stride_rows(p: Problem) -> int:
+    return p.seq_stride or p.seq_len
+
+
+def _out_like(q: torch.Tensor, p: Problem) -> torch.Tensor:
+    """An output laid out like q (head stride included)."""
+    if p.seq_stride == 0:
+        return torch.empty_like(q)
+    return torch.empty((q.shape[0], p.seq_stride, HEAD_DIM), dtype=q.dtype, device=q.device)[:, : p.seq_len]
+
+
+def _lse_like(q: torch.Tensor, p: Problem) -> torch.Tensor:
+    return torch.empty((q.shape[0], _stride_rows(p)), dtype=torch.float32, device=q.device)[:, : p.seq_len]
+
+
+def _rows_dev(t: torch.Tensor, name: str, p: Problem, lse: bool = False) -> int:
+    """Pointer of an output that must follow the problem's head stride."""
+    if not t.is_cuda:
+        raise MsaError(f"{name} must be a GPU tensor")
+    r = _stride_rows(p)
+    ok = (t.dim() == 2 and t.stride(1) == 1 and (t.shape[0] == 1 or t.stride(0) == r)) if lse else \
+        (t.dim() == 3 and t.stride(2) == 1 and t.stride(1) == HEAD_DIM and
+         (t.shape[0] == 1 or t.stride(0) == r * HEAD_DIM))
+    if not ok:
+        raise MsaError(f"{name} must have the inputs' head stride ({r} rows)")
+    return t.data_ptr()
+
+
+def _in_dev(t: torch.Tensor, name: str) -> int:
+    if not t.is_cuda:
+        raise MsaError(f"{name} must be a GPU tensor")
+    return t.data_ptr()
 
 
 def _dev(t: torch.Tensor, name: str) -> int:
@@ -177,7 +227,7 @@ def estimate_vs(q: torch.Tensor, k: torch.Tensor, vertical_topk: int, slash_topk
     for t, name in ((v_score, "v_score"), (s_score, "s_score")):
         if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (hq, n)):
             raise MsaError(f"{name} must be float32 [{hq}, {n}]")
-    _check(lib.msa_estimate_vs(ctypes.byref(p), _dev(q, "q"), _dev(k, "k"), last_q, vertical_topk,
+    _check(lib.msa_estimate_vs(ctypes.byref(p), _in_dev(q, "q"), _in_dev(k, "k"), last_q, vertical_topk,
                                slash_topk, _dev(v_idx, "v_idx"), _dev(s_idx, "s_idx"),
                                _dev(v_score, "v_score") if v_score is not None else None,
                                _dev(s_score, "s_score") if s_score is not None else None,
@@ -240,13 +290,13 @@ def sparse_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: Ind
     uint8 buffer of sparse_prefill_workspace_bytes(...) bytes, allocated here
     when None and needed."""
     lib = load()
-    p = _problem_of(q, k, sm_scale)
+    p = _problem_of(q, k, sm_scale, v)
     hq, n = q.shape[0], q.shape[1]
     if out is None:
-        out = torch.empty_like(q)
+        out = _out_like(q, p)
     want_lse = lse is not None and lse is not False
     if lse is True:
-        lse = torch.empty((hq, n), dtype=torch.float32, device=q.device)
+        lse = _lse_like(q, p)
     bc, bo, cb, cc, ci, ccap = _index_ptrs(index, hq, n)
     need = int(lib.msa_sparse_prefill_workspace(ctypes.byref(p), phase_keys))
     ws_ptr, ws_bytes = None, 0
@@ -254,9 +304,10 @@ def sparse_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: Ind
         if workspace is None:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
-    _check(lib.msa_sparse_prefill(ctypes.byref(p), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
-                                  bc, bo, cb, cc, ci, ccap, phase_keys, ws_ptr, ws_bytes, _dev(out, "out"),
-                                  _dev(lse, "lse") if want_lse else None, _stream(stream)),
+    _check(lib.msa_sparse_prefill(ctypes.byref(p), _in_dev(q, "q"), _in_dev(k, "k"), _in_dev(v, "v"),
+                                  bc, bo, cb, cc, ci, ccap, phase_keys, ws_ptr, ws_bytes,
+                                  _rows_dev(out, "out", p), _rows_dev(lse, "lse", p, True) if want_lse else None,
+                                  _stream(stream)),
            "msa_sparse_prefill")
     return (out, lse) if want_lse else out
 
@@ -265,15 +316,15 @@ def dense_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, out: tor
                   lse: torch.Tensor | bool | None = None, sm_scale: float = 0.0, stream=None):
     """Dense causal attention.  Returns out (and lse if requested)."""
     lib = load()
-    p = _problem_of(q, k, sm_scale)
+    p = _problem_of(q, k, sm_scale, v)
     hq, n = q.shape[0], q.shape[1]
     if out is None:
-        out = torch.empty_like(q)
+        out = _out_like(q, p)
     want_lse = lse is not None and lse is not False
     if lse is True:
-        lse = torch.empty((hq, n), dtype=torch.float32, device=q.device)
-    _check(lib.msa_dense_prefill(ctypes.byref(p), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
-                                 _dev(out, "out"), _dev(lse, "lse") if want_lse else None,
+        lse = _lse_like(q, p)
+    _check(lib.msa_dense_prefill(ctypes.byref(p), _in_dev(q, "q"), _in_dev(k, "k"), _in_dev(v, "v"),
+                                 _rows_dev(out, "out", p), _rows_dev(lse, "lse", p, True) if want_lse else None,
                                  _stream(stream)), "msa_dense_prefill")
     return (out, lse) if want_lse else out
 
@@ -292,7 +343,7 @@ def estimate_bs(q: torch.Tensor, k: torch.Tensor, topk_blocks: int, *, cap_block
     ws_bytes = int(lib.msa_estimate_bs_workspace(ctypes.byref(p), BLOCK))
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
-    _check(lib.msa_estimate_bs(ctypes.byref(p), _dev(q, "q"), _dev(k, "k"), BLOCK, topk_blocks,
+    _check(lib.msa_estimate_bs(ctypes.byref(p), _in_dev(q, "q"), _in_dev(k, "k"), BLOCK, topk_blocks,
                                _dev(out.block_count, "block_count"), out.block_offset.data_ptr(),
                                out.cap_blocks, _dev(out.column_count, "column_count"),
                                _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),

@@ -22,8 +22,11 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- *  * Tensors are device memory owned by the caller, batch 1, contiguous
- *    [heads, seq_len, head_dim] row-major.  Q has n_q_heads heads; K and V have
+ *  * Tensors are device memory owned by the caller, batch 1, [heads, seq_len,
+ *    head_dim] row-major with head h starting at row h * seq_stride
+ *    (seq_stride = seq_len: contiguous).  A packed batch of sequences, stored
+ *    as [heads, total, head_dim], is one call per sequence with the pointers
+ *    at its first row and seq_stride = total.  Q has n_q_heads heads; K and V have
  *    n_kv_heads; q head h reads kv head h / (n_q_heads / n_kv_heads).
  *  * head_dim must be 128; seq_len must be positive and below 2^31
  *    (msa_estimate_vs needs at least 64); n_q_heads must be a multiple of
@@ -77,6 +80,8 @@ typedef struct {
     int32_t head_dim;       /* must be 128 */
     int32_t dtype;          /* msa_dtype */
     float sm_scale;         /* softmax scale; 0 selects 1/sqrt(head_dim) */
+    int64_t seq_stride;     /* rows from one head's start to the next in q, k, v,
+                               out and lse; 0 selects seq_len (contiguous) */
 } msa_problem;
 
 /* Human-readable name of a status code (static storage). */

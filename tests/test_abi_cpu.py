@@ -35,8 +35,8 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
-def P(hq=32, hkv=8, n=4096, d=128, dtype=0, scale=0.0):
-    return ctypes.byref(B.Problem(hq, hkv, n, d, dtype, scale))
+def P(hq=32, hkv=8, n=4096, d=128, dtype=0, scale=0.0, stride=0):
+    return ctypes.byref(B.Problem(hq, hkv, n, d, dtype, scale, stride))
 
 
 FAKE = ctypes.c_void_p(0x1000)       # never dereferenced: every case fails validation first
@@ -49,7 +49,7 @@ def status_of(lib, fn, *args):
 def test_problem_validation(lib):
     for prob, want in [(P(d=64), SHAPE), (P(hq=6, hkv=4), SHAPE), (P(n=0), SHAPE),
                        (P(n=1 << 31), SHAPE), (P(dtype=7), DTYPE), (P(scale=-1.0), RANGE),
-                       (P(hkv=0), SHAPE)]:
+                       (P(hkv=0), SHAPE), (P(stride=4095), SHAPE), (P(stride=-1), SHAPE)]:
         assert lib.msa_dense_prefill(prob, FAKE, FAKE, FAKE, FAKE, None, None) == want
         assert lib.msa_last_error()
     assert lib.msa_dense_prefill(None, FAKE, FAKE, FAKE, FAKE, None, None) == NULL

@@ -92,3 +92,55 @@ def test_batched_shape_errors():
         msa.vertical_slash_sparse_attention(q, q[:, :1, :, :][0], q[:, :1], 8, 8)
     with pytest.raises(msa.MsaError):
         msa.streaming_forward(q, q[:, :1], q[:, :1], 0, 64)
+
+
+def _packed_inputs(hq, hkv, lens, seed):
+    parts = [batch_inputs(1, hq, hkv, n, seed=seed + i) for i, n in enumerate(lens)]
+    q = torch.cat([p[0][0] for p in parts], dim=1).cuda()
+    k = torch.cat([p[1][0] for p in parts], dim=1).cuda()
+    v = torch.cat([p[2][0] for p in parts], dim=1).cuda()
+    cu = np.concatenate([[0], np.cumsum(lens)]).tolist()
+    return q, k, v, cu
+
+
+def test_strided_views_match_contiguous():
+    """A sequence that is a slice of packed [heads, total, 128] tensors (head
+    stride = total rows) gives bitwise the same results as a contiguous copy,
+    in every entry point."""
+    hq, hkv, lens = 4, 2, [300, 64 * 5, 777]
+    q, k, v, cu = _packed_inputs(hq, hkv, lens, seed=71)
+    a, b = cu[2], cu[3]
+    qv, kv_, vv = q[:, a:b], k[:, a:b], v[:, a:b]
+    qc, kc, vc = qv.contiguous(), kv_.contiguous(), vv.contiguous()
+    n = b - a
+    o1, l1 = msa.dense_prefill(qv, kv_, vv, lse=True)
+    o2, l2 = msa.dense_prefill(qc, kc, vc, lse=True)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    vi1, si1 = msa.estimate_vs(qv, kv_, 30, 80)
+    vi2, si2 = msa.estimate_vs(qc, kc, 30, 80)
+    assert torch.equal(vi1, vi2) and torch.equal(si1, si2)
+    idx = msa.build_index(vi1, si1, n)
+    o1, l1 = msa.sparse_prefill(qv, kv_, vv, idx, lse=True, phase_keys=128)
+    o2, l2 = msa.sparse_prefill(qc, kc, vc, idx, lse=True, phase_keys=128)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    b1 = msa.estimate_bs(qv, kv_, 3)
+    b2 = msa.estimate_bs(qc, kc, 3)
+    assert torch.equal(b1.block_count, b2.block_count)
+    live = torch.arange(b1.cap_blocks, device="cuda")[None, None, :] < b1.block_count[:, :, None]
+    assert torch.equal(b1.block_offset[live], b2.block_offset[live])       # entries past a count are unspecified
+
+
+def test_packed_batch_calls():
+    """cu_seqlens: each packed sequence equals the same call on that sequence alone."""
+    hq, hkv, lens = 4, 1, [200, 64 * 6, 641]
+    q, k, v, cu = _packed_inputs(hq, hkv, lens, seed=81)
+    for call, args in ((msa.vertical_slash_sparse_attention, (30, 90)), (msa.block_sparse_attention, (3,)),
+                       (msa.streaming_forward, (64, 128))):
+        out = call(q, k, v, *args, cu_seqlens=cu)
+        for i in range(len(lens)):
+            a, b = cu[i], cu[i + 1]
+            one = call(q[:, a:b].contiguous(), k[:, a:b].contiguous(), v[:, a:b].contiguous(),
+                       *[min(x, b - a) for x in args])
+            assert torch.equal(out[:, a:b], one), (call.__name__, i)
+    with pytest.raises(msa.MsaError):
+        msa.streaming_forward(q, k, v, 64, 128, cu_seqlens=[0, 100, 50, q.shape[1]])
