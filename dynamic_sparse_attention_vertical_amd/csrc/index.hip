@@ -108,13 +108,17 @@ __global__ __launch_bounds__(kThreads) void build_index_kernel(IndexArgs a) {
     // unaligned head of the walk, one offset at a time, down to a multiple of 4
     for (; i >= 0 && (i & 3) != 3; --i) step(load_uniform(S + i));
     const bool aligned = ((uintptr_t)S & 15) == 0;
+    auto load4 = [&](int top) {                       // offsets top-3 .. top
+        return aligned ? load_uniform4(S + top - 3)
+                       : make_int4(load_uniform(S + top - 3), load_uniform(S + top - 2), load_uniform(S + top - 1),
+                                   load_uniform(S + top));
+    };
+    // each group of four is loaded one iteration ahead, so the scalar loads
+    // overlap the previous group's steps
+    int4 qn = i >= 3 ? load4(i) : make_int4(0, 0, 0, 0);
     for (; i >= 3; i -= 4) {
-        int4 q;
-        if (aligned) {
-            q = load_uniform4(S + i - 3);
-        } else {
-            q = make_int4(load_uniform(S + i - 3), load_uniform(S + i - 2), load_uniform(S + i - 1), load_uniform(S + i));
-        }
+        const int4 q = qn;
+        if (i >= 7) qn = load4(i - 4);
         step(q.w);
         step(q.z);
         step(q.y);
