@@ -1,4 +1,4 @@
-"""GPU parity at the five named workloads' full sizes, in the launch
+"""GPU parity at the named workloads' full sizes, in the launch
 configuration bench.py times (LayerPlan buffers, one call per step on the
 current stream).  The oracle checks sampled heads and query blocks one by
 one; index counts are checked for every head."""
@@ -156,6 +156,15 @@ def test_llama3_8b_512k():
 
 def test_llama3_8b_1m():
     run_vs_workload("llama3_8b_1m", heads=[5, 31], n_blocks=6, dense=False)
+
+
+def test_llama3_8b_1m_band():
+    """The 1M layer with clustered slashes: long runs of adjacent diagonals, so
+    the index is mostly long contiguous block runs plus the leftover columns."""
+    plan = run_vs_workload("llama3_8b_1m_band", heads=[2, 27], n_blocks=6, dense=False)
+    # the clustering is what this workload is for: far fewer blocks than the
+    # iid 1M layer's (about one per selected diagonal there)
+    assert plan.index.block_count.float().mean().item() < 0.5 * 6096
 
 
 def test_mixed_256k():
