@@ -9,9 +9,13 @@
 // the emitted blocks is listed too, ascending.
 //
 // The offsets of a head are the same for every lane, so a wave walks them in
-// lock step (scalar loads, four at a time) and each lane applies the step to
-// its own cover.  Columns are merged into the same walk: when a block starts at
-// st, the columns in [cov, st) are exactly the ones no block covers.
+// lock step (scalar loads, sixteen at a time, one group ahead) and each lane
+// applies the step to its own cover.  Columns are merged into the same walk:
+// when a block starts at st, the columns in [cov, st) are exactly the ones no
+// block covers.  A lane keeps its next column in a register, so a step that
+// passes no column does no memory access: nearly every step has some lane of
+// the wave emitting a block, and at about one wave per SIMD a load latency per
+// step would set the pace.
 //
 // The pages ask that sparse work come in large contiguous blocks for the
 // matrix units and that the index be built online at small cost ("How to
@@ -21,16 +25,26 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <climits>
+
 namespace msa {
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kStageMax = 4096;      // columns staged in LDS (16 KB)
 
-__device__ __forceinline__ int4 load_uniform4(const int32_t *p) {   // p 16-byte aligned, wave-uniform
-    typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-    const i32x4 v = *(const __attribute__((address_space(4))) i32x4 *)(uintptr_t)p;
-    return make_int4(v.x, v.y, v.z, v.w);
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
+
+// Scalar loads of the offsets.  The address goes through readfirstlane: the
+// walk index is uniform, but the compiler cannot prove it inside a loop with
+// divergent branches and would otherwise issue vector loads, whose waits
+// (vmcnt, in order) would also wait for every store of the walk before them.
+__device__ __forceinline__ int32_t sload(const int32_t *p) {         // p wave-uniform
+    return load_uniform(reinterpret_cast<const int32_t *>(to_sgpr(p)));
+}
+__device__ __forceinline__ i32x4 sload4(const int32_t *p) {          // p 16-byte aligned, wave-uniform
+    return *(const __attribute__((address_space(4))) i32x4 *)(uintptr_t)to_sgpr(p);
 }
 
 constexpr int kRing = 32;            // per-lane LDS ring of block starts (two 16-entry lines)
@@ -61,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void build_index_kernel(IndexArgs a) {
     int lo = 0, hi = a.ks;
     while (lo < hi) {
         const int mid = (lo + hi) >> 1;
-        if (load_uniform(S + mid) <= r1_max) lo = mid + 1; else hi = mid;
+        if (sload(S + mid) <= r1_max) lo = mid + 1; else hi = mid;
     }
 
     // Block starts go to a per-lane LDS ring; a lane writes a completed,
@@ -83,16 +97,16 @@ __global__ __launch_bounds__(kThreads) void build_index_kernel(IndexArgs a) {
         flushed += 16;
     };
     int cov = 0, cnt = 0, vp = 0, cc = 0;
+    int vnext = a.kv > 0 ? V[0] : INT_MAX;           // column vp (INT_MAX past the list)
     // columns below `upto` (exclusive): the ones at or past cov are uncovered
     auto columns_below = [&](int upto) {
-        while (vp < a.kv) {
-            const int j = V[vp];
-            if (j >= upto) break;
-            if (j >= cov) {
-                if (cc < a.cap_c) col[cc] = j;
+        while (vnext < upto) {
+            if (vnext >= cov) {
+                if (cc < a.cap_c) col[cc] = vnext;
                 ++cc;
             }
             ++vp;
+            vnext = vp < a.kv ? V[vp] : INT_MAX;
         }
     };
     auto step = [&](int o) {
@@ -105,32 +119,44 @@ __global__ __launch_bounds__(kThreads) void build_index_kernel(IndexArgs a) {
         cov = st + 64;
     };
     int i = lo - 1;
-    // unaligned head of the walk, one offset at a time, down to a multiple of 4
-    for (; i >= 0 && (i & 3) != 3; --i) step(load_uniform(S + i));
+    // unaligned head of the walk (at most 15 steps), one offset at a time,
+    // down to a group of sixteen
+    for (; i >= 0 && (i & 15) != 15; --i) step(sload(S + i));
     const bool aligned = ((uintptr_t)S & 15) == 0;
-    auto load4 = [&](int top) {                       // offsets top-3 .. top
-        return aligned ? load_uniform4(S + top - 3)
-                       : make_int4(load_uniform(S + top - 3), load_uniform(S + top - 2), load_uniform(S + top - 1),
-                                   load_uniform(S + top));
+    auto load16 = [&](int top) {                      // offsets top-15 .. top
+        i32x16 g;
+#pragma unroll
+        for (int u = 0; u < 16; u += 4) {
+            const i32x4 x = aligned ? sload4(S + top - 15 + u)
+                                    : i32x4{sload(S + top - 15 + u), sload(S + top - 14 + u),
+                                            sload(S + top - 13 + u), sload(S + top - 12 + u)};
+            g[u] = x[0];
+            g[u + 1] = x[1];
+            g[u + 2] = x[2];
+            g[u + 3] = x[3];
+        }
+        return g;
     };
-    // each group of four is loaded one iteration ahead, so the scalar loads
+    // each group of sixteen is loaded one iteration ahead, so the scalar loads
     // overlap the previous group's steps
-    int4 qn = i >= 3 ? load4(i) : make_int4(0, 0, 0, 0);
-    for (; i >= 3; i -= 4) {
-        const int4 q = qn;
-        if (i >= 7) qn = load4(i - 4);
-        step(q.w);
-        step(q.z);
-        step(q.y);
-        step(q.x);
-        if ((i & 15) == 3) {
-            // at most 16 emissions since the last check: at most one line completed
-            if (cnt - flushed >= 16) flush_line();
-            if ((i & 63) == 3 && __builtin_amdgcn_ballot_w64(cov <= r1) == 0) break;   // every lane is done
+    i32x16 qn = {};
+    if (i >= 15) qn = load16(i);
+    bool all_done = false;
+    for (; i >= 15; i -= 16) {
+        const i32x16 q = qn;
+        if (i >= 31) qn = load16(i - 16);
+#pragma unroll
+        for (int u = 15; u >= 0; --u) step(q[u]);
+        // at most 31 unflushed entries (15 left + 16 new): at most one line
+        // is completed and the 32-entry ring has not wrapped onto it
+        if (cnt - flushed >= 16) flush_line();
+        if ((i & 63) == 63 && __builtin_amdgcn_ballot_w64(cov <= r1) == 0) {   // every lane is done
+            all_done = true;
+            break;
         }
     }
-    for (; i >= 0; --i) {
-        step(load_uniform(S + i));
+    for (; !all_done && i >= 0; --i) {
+        step(sload(S + i));
         if (cnt - flushed >= 16) flush_line();
     }
     // the unfinished line
