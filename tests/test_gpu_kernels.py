@@ -36,7 +36,9 @@ def random_sets(h, n, kv, ks, seed=0):
 
 
 @pytest.mark.parametrize("hq,hkv,n,fp32", [(1, 1, 64, False), (4, 1, 256, False), (4, 2, 320, False),
-                                           (8, 2, 1024, False), (2, 1, 320, True), (1, 1, 512, True)])
+                                           (8, 2, 1024, False), (2, 1, 320, True), (1, 1, 512, True),
+                                           # GQA groups of 8, 3 and 6 (four, one and two heads per workgroup)
+                                           (8, 1, 512, False), (6, 2, 384, False), (6, 1, 256, False)])
 def test_dense_prefill(hq, hkv, n, fp32):
     w, q, k, v = inputs(hq, hkv, n, seed=n + hq, fp32=fp32)
     out, lse = msa.dense_prefill(*cuda(q, k, v), lse=True)
@@ -47,7 +49,9 @@ def test_dense_prefill(hq, hkv, n, fp32):
 
 @pytest.mark.parametrize("hq,hkv,n,kv,ks,fp32", [(4, 1, 256, 7, 9, False), (4, 2, 640, 20, 30, False),
                                                  (2, 1, 1024, 100, 40, False), (2, 2, 384, 5, 200, False),
-                                                 (2, 1, 320, 9, 13, True)])
+                                                 (2, 1, 320, 9, 13, True),
+                                                 # GQA groups of 8 and 3
+                                                 (8, 1, 512, 20, 30, False), (6, 2, 448, 15, 25, False)])
 def test_sparse_prefill_given_index(hq, hkv, n, kv, ks, fp32):
     w, q, k, v = inputs(hq, hkv, n, seed=n, fp32=fp32)
     vi, si = random_sets(hq, n, kv, ks, seed=n + 1)
@@ -218,7 +222,11 @@ def test_build_index_a_shape():
                                            # lengths not a multiple of 64: keys tiled in a shifted frame
                                            (4, 1, 64 * 4 + 23, False), (2, 1, 64 * 9 + 1, True),
                                            (4, 2, 100, False), (1, 1, 127, False),
-                                           (8, 2, 64 * 70 + 40, False)])   # 18 key ranges
+                                           (8, 2, 64 * 70 + 40, False),    # 18 key ranges
+                                           # GQA groups above four: each wave serves a second q head
+                                           # in a second pass over the range (8: both passes full;
+                                           # 5: one wave busy in the second); 3: one wave idle
+                                           (8, 1, 1024, False), (5, 1, 512, True), (6, 2, 64 * 6 + 17, False)])
 def test_estimate_scores(hq, hkv, n, fp32):
     w, q, k, _ = inputs(hq, hkv, n, seed=n + 5, fp32=fp32)
     qs, ks_ = cuda(q, k)
