@@ -307,3 +307,29 @@ def test_estimate_bs(n, topk):
             pr = np.exp(u - u.max())
             pr /= pr.sum()
             check_band(c, pr, kk, f"bs head {h} block {b}")
+
+
+@pytest.mark.parametrize("fp32", [False, True])
+def test_explicit_softmax_scale(fp32):
+    """A caller-given sm_scale (here 0.05, not 1/sqrt(128)) reaches every step:
+    estimator scores, sparse and dense attention, against the oracle with the
+    same scale."""
+    hq, hkv, n, scale = 4, 2, 64 * 6 + 9, 0.05
+    w, q, k, v = inputs(hq, hkv, n, seed=77, fp32=fp32)
+    qs, ks_, vs = cuda(q, k, v)
+    vsc = torch.empty((hq, n), dtype=torch.float32, device="cuda")
+    ssc = torch.empty((hq, n), dtype=torch.float32, device="cuda")
+    vi, si = msa.estimate_vs(qs, ks_, 16, 32, v_score=vsc, s_score=ssc, sm_scale=scale)
+    rv, rs = oracle.estimate_vs(q, k, last_q=64, scale=scale)
+    for g, r, name in ((vsc, rv, "v"), (ssc, rs, "s")):
+        g = g.cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(g - r) <= SCORE_RTOL * r + 1e-6), f"{name} scores with sm_scale"
+    ridx = oracle.build_index(vi.cpu().numpy(), si.cpu().numpy(), n)
+    out, lse = msa.sparse_prefill(qs, ks_, vs, msa.build_index(vi, si, n), lse=True, sm_scale=scale)
+    ref, rlse = oracle.attention_with_mask(q, k, v, oracle.index_mask(ridx, n), scale=scale)
+    compare_out(out.float().cpu().numpy(), ref, fp32, "sparse, sm_scale")
+    compare_lse(lse.cpu().numpy(), rlse, "sparse, sm_scale")
+    dout, dlse = msa.dense_prefill(qs, ks_, vs, lse=True, sm_scale=scale)
+    dref, drlse = oracle.dense_attention(q, k, v, scale=scale)
+    compare_out(dout.float().cpu().numpy(), dref, fp32, "dense, sm_scale")
+    compare_lse(dlse.cpu().numpy(), drlse, "dense, sm_scale")
