@@ -151,3 +151,18 @@ def test_binding_rejects_cpu_tensors():
     q = torch.zeros((4, 256, 128), dtype=torch.bfloat16)
     with pytest.raises(m.MsaError):
         m.dense_prefill(q, q[:1], q[:1])
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built HIP library every entry point raises; there is no
+    fallback (CPU or otherwise) to compute anything."""
+    import torch
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "_LIB_PATH", str(tmp_path / "libmsa.so"))
+    q = torch.zeros((1, 64, 128), dtype=torch.bfloat16)
+    with pytest.raises(B.MsaError, match="missing"):
+        B.load()
+    with pytest.raises(B.MsaError, match="missing"):
+        B.dense_prefill(q, q, q)
+    with pytest.raises(B.MsaError, match="missing"):
+        B.sparse_prefill_workspace_bytes(1, 1, 64, phase_keys=16)
