@@ -21,7 +21,7 @@
 // lane, no registers), 16-byte chunks XOR-swizzled per row so that the MFMA
 // operand reads are free of bank conflicts.
 //
-// Long sparse sequences run in key phases, one launch per range of keys (16K
+// Long sparse sequences run in key phases, one launch per range of keys (12K
 // by default): each launch takes the block tiles starting in its range, so the
 // workgroups in flight read K/V from one cache-sized range of a kv head, and a
 // query block's fp32 softmax state (O, row max, row sum) waits in a caller
@@ -293,6 +293,15 @@ __device__ __forceinline__ int lower_bound_wave(const int32_t *list, int cnt, in
     return lo;
 }
 
+// The same for a key whose index is usually among the first 128 entries (the
+// end of a key phase, counted from its start): one lower_bound_wave over
+// those first, so the common case takes two rounds of loads.
+__device__ __forceinline__ int lower_bound_near(const int32_t *list, int cnt, int key, int lane) {
+    const int w = min(cnt, 128);
+    const int i = lower_bound_wave(list, w, key, lane);
+    return (i < w || cnt <= 128) ? i : 128 + lower_bound_wave(list + 128, cnt - 128, key, lane);
+}
+
 // One 64-key tile of K and one of V in LDS (33 KB for bf16: four workgroups
 // and two waves per SIMD), each holding two 32-key chunks; chunk c lives in
 // half c % 2.  Step c of the pipeline (after a wait and a barrier):
@@ -343,7 +352,8 @@ void attn_fwd_kernel(AttnArgs a) {
     // (no later key is visible to it); in between the state lives in ws
     bool first = true, final_ = true, have_state = false;
     float *sw = nullptr;                             // this wave's state: 16 float4 of O per lane, max, sum
-    int *state_flag = nullptr;                       // nonzero: ws holds a state for this query block
+    int2 *phase_rec = nullptr;                       // (state stored, first block of the next phase)
+    int b_next = 0;                                  // first block of the next phase
     if constexpr (kDense) {
         nblk = (int)b + 1;
         ncol = 0;
@@ -361,17 +371,26 @@ void attn_fwd_kernel(AttnArgs a) {
             // splitting for locality.
             first = a.k_lo == INT_MIN;
             final_ = (int64_t)r0 + kBQ - 1 < (int64_t)a.k_hi;
-            const int b0 = first ? 0 : lower_bound_wave(blist, nblk, a.k_lo, lane);
-            const int b1 = a.k_hi == INT_MAX ? nblk : lower_bound_wave(blist, nblk, a.k_hi, lane);
+            // every query block passes the first phase, which writes its
+            // record; each phase with work updates it, so the next one finds
+            // where its blocks start without a search
+            phase_rec = reinterpret_cast<int2 *>(a.ws + (int64_t)a.hq * nqb * 2 * kStateFloats) + item;
+            int2 rec = make_int2(0, 0);
+            if (!first) {
+                rec = *phase_rec;
+                rec.x = __builtin_amdgcn_readfirstlane(rec.x);
+                rec.y = __builtin_amdgcn_readfirstlane(rec.y);
+            }
+            const int b0 = min(max(rec.y, 0), nblk);
+            const int b1 = a.k_hi == INT_MAX ? nblk : b0 + lower_bound_near(blist + b0, nblk - b0, a.k_hi, lane);
+            b_next = b1;
             blist += b0;
-            nblk = max(b1 - b0, 0);
+            nblk = b1 - b0;
             if (!final_) ncol = 0;
             sw = a.ws + item * (2 * kStateFloats) + wave * kStateFloats;
-            // every query block passes the first phase, which sets its flag
-            state_flag = reinterpret_cast<int *>(a.ws + (int64_t)a.hq * nqb * 2 * kStateFloats) + item;
-            have_state = !first && __builtin_amdgcn_readfirstlane(*state_flag) != 0;
+            have_state = rec.x != 0;
             if (!final_ && nblk == 0) {                 // nothing in this phase
-                if (first && tid == 0) *state_flag = 0;
+                if (first && tid == 0) *phase_rec = make_int2(0, 0);
                 return;
             }
         }
@@ -572,7 +591,7 @@ void attn_fwd_kernel(AttnArgs a) {
                             o[v4 >> 2][(v4 & 3) * 4 + 2], o[v4 >> 2][(v4 & 3) * 4 + 3]);
         sw[4096 + lane] = mb_i;
         sw[4096 + 64 + lane] = l_i;
-        if (tid == 0) *state_flag = 1;
+        if (tid == 0) *phase_rec = make_int2(1, b_next);
         return;
     }
     // finalise: lanes l and l^32 hold halves of the same row's sum
@@ -637,7 +656,7 @@ template <typename T, bool kDense> hipError_t launch(AttnArgs a, hipStream_t s) 
 
 size_t sparse_state_bytes(int64_t hq, int64_t n, int64_t phase_keys) {
     if (phase_keys <= 0 || phase_keys >= n) return 0;
-    return (size_t)hq * (size_t)((n + kBQ - 1) / kBQ) * (2 * kStateFloats * sizeof(float) + sizeof(int));
+    return (size_t)hq * (size_t)((n + kBQ - 1) / kBQ) * (2 * kStateFloats * sizeof(float) + sizeof(int2));
 }
 
 hipError_t launch_sparse_prefill(const AttnArgs &a, int dtype, hipStream_t s) {

@@ -20,7 +20,7 @@ _lib = None
 MSA_BF16, MSA_F32 = 0, 1
 HEAD_DIM = 128
 BLOCK = 64
-DEFAULT_PHASE_KEYS = 16384    # MSA_DEFAULT_PHASE_KEYS: keys per sparse-prefill phase when phase_keys is 0
+DEFAULT_PHASE_KEYS = 12288    # MSA_DEFAULT_PHASE_KEYS: keys per sparse-prefill phase when phase_keys is 0
 LAST_Q = 64
 
 

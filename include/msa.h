@@ -173,12 +173,12 @@ int msa_sparse_prefill(const msa_problem *p, const void *q, const void *k, const
                        void *stream);
 
 /* Keys per phase of msa_sparse_prefill when phase_keys is 0 (K+V of one kv
- * head over this many keys: 8 MB in bf16). */
-#define MSA_DEFAULT_PHASE_KEYS 16384
+ * head over this many keys: 6 MB in bf16). */
+#define MSA_DEFAULT_PHASE_KEYS 12288
 
 /* Workspace bytes msa_sparse_prefill needs (0 when one phase covers seq_len;
  * 0 for invalid arguments):
- *   n_q_heads * (seq_len / 64) * (2 * (64 * 64 + 2 * 64) * 4 + 4). */
+ *   n_q_heads * ceil(seq_len / 64) * (2 * (64 * 64 + 2 * 64) * 4 + 8). */
 size_t msa_sparse_prefill_workspace(const msa_problem *p, int32_t phase_keys);
 
 /* Dense causal attention (every j <= i), same layouts as msa_sparse_prefill. */

@@ -87,7 +87,7 @@ def test_sparse_prefill_phases(hq, hkv, n, kv, ks, phase, fp32):
     gidx.column_index.copy_(torch.from_numpy(ridx.column_index))
     dt = torch.float32 if fp32 else torch.bfloat16
     need = msa.sparse_prefill_workspace_bytes(hq, hkv, n, dt, phase_keys=phase)
-    assert need == hq * (n // 64) * (2 * (64 * 64 + 128) * 4 + 4)
+    assert need == hq * (n // 64) * (2 * (64 * 64 + 128) * 4 + 8)
     ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")     # no initial contents assumed
     qs, ks_, vs = cuda(q, k, v)
     out, lse = msa.sparse_prefill(qs, ks_, vs, gidx, lse=True, phase_keys=phase, workspace=ws)
