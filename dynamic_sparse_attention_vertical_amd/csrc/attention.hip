@@ -49,6 +49,12 @@ constexpr int kBQ = 64;          // query rows per work item
 constexpr int kBK = 64;          // keys per tile
 constexpr int kThreads = 128;    // two waves per q head of a workgroup
 constexpr int kStateFloats = 64 * 64 + 2 * 64;   // sparse phase state of one wave: O, max, sum
+// A query block with fewer block tiles than this in a key phase (not its own)
+// leaves them to the next phase: starting a work item (searching, loading Q
+// and the state, filling the copy pipeline) costs about as much as four
+// tiles, and storing the state again as much more, which a handful of tiles
+// would not repay.  The tiles keep their order, so results do not change.
+constexpr int kMinPhaseTiles = 16;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
@@ -389,7 +395,7 @@ void attn_fwd_kernel(AttnArgs a) {
             if (!final_) ncol = 0;
             sw = a.ws + item * (2 * kStateFloats) + wave * kStateFloats;
             have_state = rec.x != 0;
-            if (!final_ && nblk == 0) {                 // nothing in this phase
+            if (!final_ && nblk < kMinPhaseTiles) {     // too little here: leave it to the next phase
                 if (first && tid == 0) *phase_rec = make_int2(0, 0);
                 return;
             }

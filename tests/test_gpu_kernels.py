@@ -73,6 +73,12 @@ def test_sparse_prefill_given_index(hq, hkv, n, kv, ks, fp32):
     (2, 1, 2048, 7, 2048, 512, False),    # every diagonal: blocks in every phase
     (2, 1, 640, 9, 13, 192, True),        # fp32; most phases hold nothing for most blocks
     (1, 1, 256, 1, 1, 64, False),         # a single diagonal and column
+    # (the cases above hold fewer than 16 tiles per block and phase, so every
+    # phase but a block's own leaves its tiles to the next: they check that
+    # path.  Below, phases of 16 tiles carry the softmax state between launches)
+    (2, 1, 4096, 9, 4096, 1024, False),   # every diagonal: 16 tiles in each full phase
+    (1, 1, 4096, 5, 4096, 1024, True),    # the same in fp32
+    (2, 1, 4096, 30, 1200, 1024, False),  # about 16 per phase: some carried, some left over
 ])
 def test_sparse_prefill_phases(hq, hkv, n, kv, ks, phase, fp32):
     """Key phases (one launch per phase, state in the workspace) against the
