@@ -155,7 +155,8 @@ int msa_build_index(const msa_problem *p, const int32_t *v_idx, int32_t vertical
  * seq_len, the work runs as ceil(N / R) launches in order on `stream`; launch
  * j takes the block tiles whose start lies in [jR, (j+1)R) (the first also
  * starts below 0, the last every start from jR on), so the K/V read at any
- * time come from one R-key range of a kv head; each query block's columns go
+ * time come mostly from one R-key range of a kv head; a query block with only
+ * a few tiles in a range leaves them to the next launch, and its columns go
  * to the launch that holds its own rows.  The running softmax state of each
  * query block (fp32) passes between launches through `workspace`.  This path
  * needs every block list ascending, as msa_build_index and msa_estimate_bs
