@@ -10,8 +10,11 @@
 //
 //   pool:   one workgroup per (head, block): 128 threads, one per dimension.
 //   select: one workgroup per (q head, query block): scores into LDS as
-//           order-preserving integer keys, 4 x 8-bit radix select for the
-//           k-th key, then an in-order compaction (ties -> lower c).
+//           order-preserving integer keys (32 lanes per key block, one
+//           coalesced row read each), 4 x 8-bit radix select for the k-th
+//           key (the bin found by a parallel scan), then an in-order
+//           compaction (ties -> lower c).  Every workgroup reads all earlier
+//           key-block means, so the scores are L2-bandwidth bound.
 #include "common.h"
 #include "kernels.h"
 
@@ -69,7 +72,7 @@ __device__ __forceinline__ uint32_t scan256(uint32_t v, uint32_t *tmp) {
 
 __global__ __launch_bounds__(kThreads) void bs_select_kernel(BsArgs a) {
     extern __shared__ uint32_t keys[];              // [b + 1]
-    __shared__ float qrow[kD];
+    __shared__ alignas(16) float qrow[kD];
     __shared__ uint32_t hist[256];
     __shared__ uint32_t tmp[kThreads];
     __shared__ uint32_t sel_state[2];
@@ -92,16 +95,18 @@ __global__ __launch_bounds__(kThreads) void bs_select_kernel(BsArgs a) {
     }
     if (threadIdx.x < kD) qrow[threadIdx.x] = a.qm[item * kD + threadIdx.x];
     __syncthreads();
+    // 32 lanes per candidate key block: lane s holds dimensions 4s .. 4s+3, so
+    // each half-wave reads one 512-byte mean row in a single coalesced load,
+    // and the 32 partial products are summed across the lanes
     const float *kmg = a.km + (int64_t)g * nb * kD;
-    for (int c = threadIdx.x; c < ncand; c += kThreads) {
-        const f32x4 *kr = reinterpret_cast<const f32x4 *>(kmg + (int64_t)c * kD);
-        float acc = 0.f;
-#pragma unroll 8
-        for (int i = 0; i < kD / 4; ++i) {
-            const f32x4 x = kr[i];
-            acc += qrow[4 * i] * x[0] + qrow[4 * i + 1] * x[1] + qrow[4 * i + 2] * x[2] + qrow[4 * i + 3] * x[3];
-        }
-        keys[c] = order_key(acc * a.scale);
+    const int sub = threadIdx.x & 31, grp = threadIdx.x >> 5;
+    const f32x4 qv = *reinterpret_cast<const f32x4 *>(&qrow[4 * sub]);
+    for (int c = grp; c < ncand; c += kThreads / 32) {
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(kmg + (int64_t)c * kD + 4 * sub);
+        float acc = qv[0] * x[0] + qv[1] * x[1] + qv[2] * x[2] + qv[3] * x[3];
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 32);
+        if (sub == 0) keys[c] = order_key(acc * a.scale);
     }
     if (threadIdx.x == 0) { sel_state[0] = 0u; sel_state[1] = (uint32_t)kk; }
     __syncthreads();
@@ -115,16 +120,16 @@ __global__ __launch_bounds__(kThreads) void bs_select_kernel(BsArgs a) {
             if (pass == 0 || (x >> (sh + 8)) == prefix) atomicAdd(&hist[(x >> sh) & 255u], 1u);
         }
         __syncthreads();
-        if (threadIdx.x == 0) {
-            uint32_t krem = sel_state[1], acc = 0;
-            for (int bk = 255; bk >= 0; --bk) {
-                if (acc + hist[bk] >= krem) {
-                    sel_state[0] = (prefix << 8) | (uint32_t)bk;
-                    sel_state[1] = krem - acc;
-                    break;
-                }
-                acc += hist[bk];
-            }
+        // the bin holding the k-th largest key: thread t owns bin 255 - t, and
+        // an exclusive scan over the threads counts the keys in higher bins;
+        // exactly one bin has fewer than krem above it and krem or more with it
+        const uint32_t krem = sel_state[1];
+        const int bk = kThreads - 1 - (int)threadIdx.x;
+        const uint32_t hb = hist[bk];
+        const uint32_t above = scan256(hb, tmp);
+        if (above < krem && above + hb >= krem) {
+            sel_state[0] = (prefix << 8) | (uint32_t)bk;
+            sel_state[1] = krem - above;
         }
         __syncthreads();
     }
