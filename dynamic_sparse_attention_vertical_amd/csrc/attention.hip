@@ -370,11 +370,13 @@ void attn_fwd_kernel(AttnArgs a) {
         blist = a.block_offset + item * a.cap_b;
         clist = a.column_index + item * a.cap_c;
         if (a.ws != nullptr) {
-            // this phase's part: the block tiles starting in [k_lo, k_hi) (the
-            // lists are ascending; the first phase also takes starts below, the
-            // last those above).  The columns all go to the final phase: every
-            // block of a head draws them from the same few keys, so they need no
-            // splitting for locality.
+            // this phase's part: the block tiles from where the previous phase
+            // stopped up to the first start at or past k_hi (the lists are
+            // ascending; that is the tiles starting in [k_lo, k_hi) plus any
+            // left over from earlier phases, and the last phase takes the rest).
+            // The columns all go to the final phase: every block of a head
+            // draws them from the same few keys, so they need no splitting for
+            // locality.
             first = a.k_lo == INT_MIN;
             final_ = (int64_t)r0 + kBQ - 1 < (int64_t)a.k_hi;
             // every query block passes the first phase, which writes its
