@@ -9,12 +9,14 @@
 // ascending key starts 64c with no extra columns.
 //
 //   pool:   one workgroup per (head, block): 128 threads, one per dimension.
-//   select: one workgroup per (q head, query block): scores into LDS as
-//           order-preserving integer keys (32 lanes per key block, one
-//           coalesced row read each), 4 x 8-bit radix select for the k-th
-//           key (the bin found by a parallel scan), then an in-order
-//           compaction (ties -> lower c).  Every workgroup reads all earlier
-//           key-block means, so the scores are L2-bandwidth bound.
+//   score:  the block scores of up to 1024 query blocks at a time, as a
+//           tiled product of the means: one workgroup per (q head, 64 query
+//           blocks, 64 key blocks) below the diagonal, both 64 x 128 tiles of
+//           means in LDS, each thread 4 x 4 scores; written to the workspace
+//           as order-preserving integer keys.
+//   select: one workgroup per (q head, query block): its row of keys into
+//           LDS, 4 x 8-bit radix select for the k-th key (the bin found by a
+//           parallel scan), then an in-order compaction (ties -> lower c).
 #include "common.h"
 #include "kernels.h"
 
@@ -55,6 +57,58 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Scores of query blocks row0 + 64 qt .. (+63) against key blocks 64 kt ..
+// (+63) of q head h, for kt <= qt (blocks above the diagonal are not needed).
+// Thread (ty, tx) computes query blocks 16 i + ty and key blocks 16 j + tx of
+// the tile (i, j = 0..3); rows of 132 floats keep the four-wide LDS reads of
+// the 16 key-block rows of a wave on distinct banks.
+constexpr int kScorePitch = kD + 4;
+__global__ __launch_bounds__(kThreads) void bs_score_kernel(BsArgs a) {
+    __shared__ alignas(16) float qs[64 * kScorePitch];
+    __shared__ alignas(16) float ks[64 * kScorePitch];
+    const int kt = blockIdx.x, qt = blockIdx.y, h = blockIdx.z;
+    const int64_t nb = (a.n + 63) / 64;
+    const int64_t q0 = a.row0 + (int64_t)qt * 64;          // first query block of the tile
+    if ((int64_t)kt * 64 > q0 + 63) return;                 // above the diagonal
+    const int G = a.hq / a.hkv;
+    const float *qm = a.qm + (int64_t)h * nb * kD;
+    const float *km = a.km + (int64_t)(h / G) * nb * kD;
+    // both tiles: 64 rows x 32 float4, eight per thread (rows past nb read row nb-1)
+    for (int i = threadIdx.x; i < 64 * 32; i += kThreads) {
+        const int r = i >> 5, c4 = i & 31;
+        const int64_t qr = min(q0 + r, nb - 1), kr = min((int64_t)kt * 64 + r, nb - 1);
+        *reinterpret_cast<f32x4 *>(&qs[r * kScorePitch + 4 * c4]) = *reinterpret_cast<const f32x4 *>(qm + qr * kD + 4 * c4);
+        *reinterpret_cast<f32x4 *>(&ks[r * kScorePitch + 4 * c4]) = *reinterpret_cast<const f32x4 *>(km + kr * kD + 4 * c4);
+    }
+    __syncthreads();
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    float acc[4][4] = {};
+#pragma unroll 4
+    for (int d = 0; d < kD; d += 4) {
+        f32x4 qv[4], kv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qv[i] = *reinterpret_cast<const f32x4 *>(&qs[(16 * i + ty) * kScorePitch + d]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kv[j] = *reinterpret_cast<const f32x4 *>(&ks[(16 * j + tx) * kScorePitch + d]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] += qv[i][0] * kv[j][0] + qv[i][1] * kv[j][1] + qv[i][2] * kv[j][2] + qv[i][3] * kv[j][3];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t qb = q0 + 16 * i + ty;
+        if (qb >= nb || qb >= a.row0 + a.chunk_rows) continue;
+        uint32_t *row = a.keys + ((int64_t)h * a.chunk_rows + (qb - a.row0)) * nb;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t kb = (int64_t)kt * 64 + 16 * j + tx;
+            if (kb < nb) row[kb] = order_key(acc[i][j] * a.scale);
+        }
+    }
+}
+
 __device__ __forceinline__ uint32_t scan256(uint32_t v, uint32_t *tmp) {
     const int t = threadIdx.x;
     tmp[t] = v;
@@ -72,15 +126,13 @@ __device__ __forceinline__ uint32_t scan256(uint32_t v, uint32_t *tmp) {
 
 __global__ __launch_bounds__(kThreads) void bs_select_kernel(BsArgs a) {
     extern __shared__ uint32_t keys[];              // [b + 1]
-    __shared__ alignas(16) float qrow[kD];
     __shared__ uint32_t hist[256];
     __shared__ uint32_t tmp[kThreads];
     __shared__ uint32_t sel_state[2];
     const int64_t nb = (a.n + 63) / 64;
-    const int64_t b = nb - 1 - blockIdx.x;          // heavy rows first
+    const int64_t rows = min((int64_t)a.chunk_rows, nb - a.row0);
+    const int64_t b = a.row0 + rows - 1 - blockIdx.x;   // heavy rows first
     const int h = blockIdx.y;
-    const int G = a.hq / a.hkv;
-    const int g = h / G;
     const int64_t item = (int64_t)h * nb + b;
     int32_t *out = a.block_offset + item * a.cap_b;
     const int ncand = (int)b + 1;
@@ -93,21 +145,8 @@ __global__ __launch_bounds__(kThreads) void bs_select_kernel(BsArgs a) {
         for (int c = threadIdx.x; c < ncand; c += kThreads) out[c] = c * 64;
         return;
     }
-    if (threadIdx.x < kD) qrow[threadIdx.x] = a.qm[item * kD + threadIdx.x];
-    __syncthreads();
-    // 32 lanes per candidate key block: lane s holds dimensions 4s .. 4s+3, so
-    // each half-wave reads one 512-byte mean row in a single coalesced load,
-    // and the 32 partial products are summed across the lanes
-    const float *kmg = a.km + (int64_t)g * nb * kD;
-    const int sub = threadIdx.x & 31, grp = threadIdx.x >> 5;
-    const f32x4 qv = *reinterpret_cast<const f32x4 *>(&qrow[4 * sub]);
-    for (int c = grp; c < ncand; c += kThreads / 32) {
-        const f32x4 x = *reinterpret_cast<const f32x4 *>(kmg + (int64_t)c * kD + 4 * sub);
-        float acc = qv[0] * x[0] + qv[1] * x[1] + qv[2] * x[2] + qv[3] * x[3];
-#pragma unroll
-        for (int off = 16; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 32);
-        if (sub == 0) keys[c] = order_key(acc * a.scale);
-    }
+    const uint32_t *krow = a.keys + ((int64_t)h * a.chunk_rows + (b - a.row0)) * nb;
+    for (int c = threadIdx.x; c < ncand; c += kThreads) keys[c] = krow[c];
     if (threadIdx.x == 0) { sel_state[0] = 0u; sel_state[1] = (uint32_t)kk; }
     __syncthreads();
     for (int pass = 0; pass < 4; ++pass) {
@@ -154,14 +193,24 @@ __global__ __launch_bounds__(kThreads) void bs_select_kernel(BsArgs a) {
     }
 }
 
-template <typename T> hipError_t launch_t(const BsArgs &a, hipStream_t s) {
+template <typename T> hipError_t launch_t(BsArgs a, hipStream_t s) {
     const int64_t nb = (a.n + 63) / 64;
     hipLaunchKernelGGL(bs_pool_kernel<T>, dim3((unsigned)nb, a.hq + a.hkv), dim3(kD), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t lds = (size_t)nb * sizeof(uint32_t);
-    hipLaunchKernelGGL(bs_select_kernel, dim3((unsigned)nb, a.hq), dim3(kThreads), lds, s, a);
-    return hipGetLastError();
+    // query blocks in chunks of chunk_rows (a multiple of 64): scores of the
+    // chunk into the workspace, then the selection of its rows
+    for (int64_t r0 = 0; r0 < nb; r0 += a.chunk_rows) {
+        a.row0 = r0;
+        const int64_t rows = min((int64_t)a.chunk_rows, nb - r0);
+        const unsigned kts = (unsigned)((r0 + rows + 63) / 64), qts = (unsigned)((rows + 63) / 64);
+        hipLaunchKernelGGL(bs_score_kernel, dim3(kts, qts, a.hq), dim3(kThreads), 0, s, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(bs_select_kernel, dim3((unsigned)rows, a.hq), dim3(kThreads), lds, s, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace

@@ -92,9 +92,16 @@ struct BsArgs {
     float scale;
     int32_t topk;
     float *qm, *km;              // pooled means [hq][nb][128], [hkv][nb][128]
+    uint32_t *keys;              // score keys of one chunk of query blocks [hq][chunk_rows][nb]
+    int32_t chunk_rows;          // query blocks per chunk: min(nb, kBsChunkRows), so a multiple of 64
+                                 // whenever there is more than one chunk
+    int64_t row0;                // first query block of the chunk (set per launch)
     int32_t *block_count, *block_offset, *column_count;
     int32_t cap_b;
 };
+
+// Query blocks per block-sparse scoring chunk.
+constexpr int32_t kBsChunkRows = 1024;
 
 hipError_t launch_estimate_bs(const BsArgs &a, int dtype, hipStream_t s);
 

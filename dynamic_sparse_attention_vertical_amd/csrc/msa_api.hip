@@ -308,10 +308,15 @@ int msa_dense_prefill(const msa_problem *p, const void *q, const void *k, const 
                          "dense_prefill");
 }
 
+// block-sparse workspace: pooled q and k means, then the score keys of one
+// chunk of query blocks
+static size_t bs_chunk_rows(int64_t nb) { return (size_t)(nb < msa::kBsChunkRows ? nb : msa::kBsChunkRows); }
+
 size_t msa_estimate_bs_workspace(const msa_problem *p, int32_t block) {
     if (check_problem(p) != MSA_OK || block != 64) return 0;
     const size_t nb = (size_t)((p->seq_len + 63) / 64);
-    return align_up((size_t)p->n_q_heads * nb * 128 * 4) + align_up((size_t)p->n_kv_heads * nb * 128 * 4);
+    return align_up((size_t)p->n_q_heads * nb * 128 * 4) + align_up((size_t)p->n_kv_heads * nb * 128 * 4) +
+           align_up((size_t)p->n_q_heads * bs_chunk_rows((int64_t)nb) * nb * 4);
 }
 
 int msa_estimate_bs(const msa_problem *p, const void *q, const void *k, int32_t block, int32_t topk_blocks,
@@ -342,6 +347,10 @@ int msa_estimate_bs(const msa_problem *p, const void *q, const void *k, int32_t 
     a.topk = topk_blocks;
     a.qm = at<float>(workspace, 0);
     a.km = at<float>(workspace, align_up((size_t)p->n_q_heads * nb * 128 * 4));
+    a.keys = at<uint32_t>(workspace, align_up((size_t)p->n_q_heads * nb * 128 * 4) +
+                                         align_up((size_t)p->n_kv_heads * nb * 128 * 4));
+    a.chunk_rows = (int32_t)bs_chunk_rows(nb);    // the workspace holds this many rows of keys
+    a.row0 = 0;
     a.block_count = block_count;
     a.block_offset = block_offset;
     a.column_count = column_count;

@@ -98,7 +98,9 @@ def test_estimate_validation(lib):
 def test_estimate_bs_validation(lib):
     prob = P(n=4096)
     ws = lib.msa_estimate_bs_workspace(prob, 64)
-    assert ws == 32 * 64 * 128 * 4 + 8 * 64 * 128 * 4
+    # pooled q and k means, then the score keys of one chunk of query blocks
+    # (all 64 here)
+    assert ws == 32 * 64 * 128 * 4 + 8 * 64 * 128 * 4 + 32 * 64 * 64 * 4
     call = lambda blk, k, cap, wsb: lib.msa_estimate_bs(prob, FAKE, FAKE, blk, k, FAKE, FAKE, cap, FAKE, FAKE,
                                                         wsb, None)
     assert call(32, 10, 10, ws) == RANGE

@@ -293,7 +293,8 @@ def test_layer_end_to_end_small(fp32):
 
 
 @pytest.mark.parametrize("n,topk", [(1024, 3), (2048, 100), (640, 4),
-                                    (64 * 5 + 23, 3), (100, 1), (64 * 10 + 1, 4)])   # short last blocks
+                                    (64 * 5 + 23, 3), (100, 1), (64 * 10 + 1, 4),   # short last blocks
+                                    (64 * 1100 + 5, 7)])   # two scoring chunks of query blocks
 def test_estimate_bs(n, topk):
     hq, hkv = 4, 2
     w, q, k, v = inputs(hq, hkv, n, seed=n)
