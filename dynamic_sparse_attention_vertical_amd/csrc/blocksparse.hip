@@ -8,7 +8,7 @@
 // min(topk, b+1) best key blocks, exact ties to the lower c, listed as
 // ascending key starts 64c with no extra columns.
 //
-//   pool:   one workgroup per (head, block): 128 threads, one per dimension.
+//   pool:   one workgroup per (head, block): 128 threads, 16-byte row reads.
 //   score:  the block scores of up to 1024 query blocks at a time, as a
 //           tiled product of the means: one workgroup per (q head, 64 query
 //           blocks, 64 key blocks) below the diagonal, both 64 x 128 tiles of
@@ -26,12 +26,15 @@ namespace {
 constexpr int kD = 128;
 constexpr int kThreads = 256;
 
+// One workgroup (128 threads) per (head, block): thread t adds up 8
+// consecutive dimensions (one 16-byte load for bf16, two for fp32) of rows
+// t/16, t/16 + 8, ...; the eight row groups are then summed through LDS.
 template <typename T>
 __global__ __launch_bounds__(kD) void bs_pool_kernel(BsArgs a) {
+    __shared__ float part[8][kD];
     const int64_t nb = (a.n + 63) / 64;
     const int c = blockIdx.x;
     const int head = blockIdx.y;
-    const int d = threadIdx.x;
     const T *src;
     float *dst;
     if (head < a.hq) {
@@ -43,13 +46,34 @@ __global__ __launch_bounds__(kD) void bs_pool_kernel(BsArgs a) {
     }
     // a short last block (length not a multiple of 64) is the mean of its rows
     const int nrows = (int)min((int64_t)64, a.n - (int64_t)c * 64);
-    float acc = 0.f;
-    for (int r = 0; r < nrows; ++r) {
-        const T x = src[((int64_t)c * 64 + r) * kD + d];
-        if constexpr (sizeof(T) == 2) acc += bf16_to_f32(x.x);
-        else acc += x;
+    const int d0 = (threadIdx.x & 15) * 8, rg = threadIdx.x >> 4;
+    float acc[8] = {};
+    for (int r = rg; r < nrows; r += 8) {
+        const T *row = src + ((int64_t)c * 64 + r) * kD + d0;
+        if constexpr (sizeof(T) == 2) {
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(row);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] += __uint_as_float(w[e] << 16);
+                acc[2 * e + 1] += __uint_as_float(w[e] & 0xffff0000u);
+            }
+        } else {
+            const f32x4 x0 = *reinterpret_cast<const f32x4 *>(row), x1 = *reinterpret_cast<const f32x4 *>(row + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[e] += x0[e];
+                acc[4 + e] += x1[e];
+            }
+        }
     }
-    dst[d] = nrows == 64 ? acc * (1.f / 64.f) : acc / (float)nrows;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[rg][d0 + e] = acc[e];
+    __syncthreads();
+    const int d = threadIdx.x;
+    float s = 0.f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) s += part[g][d];
+    dst[d] = nrows == 64 ? s * (1.f / 64.f) : s / (float)nrows;
 }
 
 __device__ __forceinline__ uint32_t order_key(float f) {
