@@ -82,7 +82,7 @@ __global__ __launch_bounds__(kThreads) void build_index_kernel(IndexArgs a) {
     // 16-entry-aligned run of its list as one 64-byte line (four 16-byte
     // stores) instead of 16 scattered 4-byte stores.
     int32_t *ring = ring_all + threadIdx.x * kRing;
-    const bool vec = (a.cap_b & 3) == 0;              // rows 16-byte aligned
+    const bool vec = a.vec_rows;                      // rows 16-byte aligned
     int flushed = 0;                                  // entries of blk already written
     auto flush_line = [&]() {                         // entries flushed .. flushed+15, all emitted
         const int32_t *rl = ring + (flushed & (kRing - 1));

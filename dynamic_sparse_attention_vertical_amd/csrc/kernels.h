@@ -80,6 +80,7 @@ struct IndexArgs {
     int32_t hq;
     int32_t *block_count, *block_offset, *column_count, *column_index;
     int32_t cap_b, cap_c;
+    bool vec_rows;               // every block_offset row starts 16-byte aligned (16-byte stores)
 };
 
 hipError_t launch_build_index(const IndexArgs &a, hipStream_t s);

@@ -56,6 +56,16 @@ float scale_of(const msa_problem *p) {
 
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Row data (q, k, v, out) and workspaces are read and written 16 bytes at a
+// time; int32 and float arrays one element at a time.
+bool off_align(const void *ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) != 0; }
+
+int check_rows(const void *q, const void *k, const void *v, const void *out) {
+    if (off_align(q, 16) || off_align(k, 16) || (v && off_align(v, 16)) || (out && off_align(out, 16)))
+        return fail(MSA_ERR_RANGE, "q, k, v and out must be 16-byte aligned");
+    return MSA_OK;
+}
+
 // Estimator work split: contiguous key ranges (256 .. 8192 keys) per workgroup,
 // about 512 workgroups over the kv heads: long enough ranges to amortise each
 // workgroup's set-up, enough workgroups for every CU.
@@ -154,6 +164,10 @@ int msa_estimate_vs(const msa_problem *p, const void *q, const void *k, int32_t 
     int st = check_problem(p);
     if (st) return st;
     if (!q || !k || !v_idx || !s_idx || !workspace) return fail(MSA_ERR_NULL, "a required pointer is NULL");
+    if ((st = check_rows(q, k, nullptr, nullptr))) return st;
+    if (off_align(v_idx, 4) || off_align(s_idx, 4) || off_align(v_score, 4) || off_align(s_score, 4))
+        return fail(MSA_ERR_RANGE, "index and score arrays must be 4-byte aligned");
+    if (off_align(workspace, 16)) return fail(MSA_ERR_RANGE, "workspace is not 16-byte aligned");
     if (last_q != 64) return fail(MSA_ERR_RANGE, "last_q must be 64 (got %d)", last_q);
     if (p->seq_len < 64)
         return fail(MSA_ERR_SHAPE, "seq_len must be at least last_q = 64 (got %lld)", (long long)p->seq_len);
@@ -214,6 +228,9 @@ int msa_build_index(const msa_problem *p, const int32_t *v_idx, int32_t vertical
     if (cap_blocks < need_b || cap_cols < need_c)
         return fail(MSA_ERR_CAPACITY, "capacities (%d, %d) below required (%d, %d)", cap_blocks, cap_cols,
                     need_b, need_c);
+    if (off_align(v_idx, 4) || off_align(s_idx, 4) || off_align(block_count, 4) || off_align(block_offset, 4) ||
+        off_align(column_count, 4) || off_align(column_index, 4))
+        return fail(MSA_ERR_RANGE, "index arrays must be 4-byte aligned");
     msa::IndexArgs a;
     a.v_idx = v_idx;
     a.s_idx = s_idx;
@@ -227,6 +244,7 @@ int msa_build_index(const msa_problem *p, const int32_t *v_idx, int32_t vertical
     a.column_index = column_index;
     a.cap_b = cap_blocks;
     a.cap_c = cap_cols;
+    a.vec_rows = (cap_blocks & 3) == 0 && !off_align(block_offset, 16);
     return launch_status(msa::launch_build_index(a, reinterpret_cast<hipStream_t>(stream)), "build_index");
 }
 
@@ -235,6 +253,7 @@ static int attn_common(const msa_problem *p, const void *q, const void *k, const
     int st = check_problem(p);
     if (st) return st;
     if (!q || !k || !v || !out) return fail(MSA_ERR_NULL, "a required pointer is NULL");
+    if ((st = check_rows(q, k, v, out))) return st;
     a.q = q;
     a.k = k;
     a.v = v;
@@ -273,6 +292,9 @@ int msa_sparse_prefill(const msa_problem *p, const void *q, const void *k, const
     if (!block_count || !column_count || (cap_blocks > 0 && !block_offset) || (cap_cols > 0 && !column_index))
         return fail(MSA_ERR_NULL, "an index pointer is NULL");
     if (cap_blocks < 0 || cap_cols < 0) return fail(MSA_ERR_CAPACITY, "negative capacity");
+    if (off_align(block_count, 4) || off_align(block_offset, 4) || off_align(column_count, 4) ||
+        off_align(column_index, 4) || off_align(lse, 4))
+        return fail(MSA_ERR_RANGE, "index and lse arrays must be 4-byte aligned");
     a.block_count = block_count;
     a.block_offset = block_offset;
     a.column_count = column_count;
@@ -301,6 +323,7 @@ int msa_dense_prefill(const msa_problem *p, const void *q, const void *k, const 
     msa::AttnArgs a;
     int st = attn_common(p, q, k, v, out, a);
     if (st) return st;
+    if (off_align(lse, 4)) return fail(MSA_ERR_RANGE, "lse must be 4-byte aligned");
     a.block_count = a.block_offset = a.column_count = a.column_index = nullptr;
     a.cap_b = a.cap_c = 0;
     a.lse = lse;
@@ -326,6 +349,10 @@ int msa_estimate_bs(const msa_problem *p, const void *q, const void *k, int32_t 
     if (st) return st;
     if (!q || !k || !block_count || !block_offset || !column_count || !workspace)
         return fail(MSA_ERR_NULL, "a required pointer is NULL");
+    if ((st = check_rows(q, k, nullptr, nullptr))) return st;
+    if (off_align(block_count, 4) || off_align(block_offset, 4) || off_align(column_count, 4))
+        return fail(MSA_ERR_RANGE, "index arrays must be 4-byte aligned");
+    if (off_align(workspace, 16)) return fail(MSA_ERR_RANGE, "workspace is not 16-byte aligned");
     if (block != 64) return fail(MSA_ERR_RANGE, "block must be 64 (got %d)", block);
     const int64_t nb = (p->seq_len + 63) / 64;
     if (nb > kBsMaxBlocks)

@@ -35,6 +35,10 @@
  *    have ceil(seq_len / 64) entries per head.
  *  * A subset of heads is selected by offsetting the pointers (q by h0 heads,
  *    k/v by h0/G heads) and passing the subset's head counts.
+ *  * q, k, v, out and every workspace must be 16-byte aligned (any whole
+ *    tensor from a device allocator is; so is a view that starts at a row or
+ *    head boundary), the int32 and float arrays 4-byte aligned.  Anything
+ *    else returns MSA_ERR_RANGE.
  *  * The library never allocates or frees device memory.  Scratch memory comes
  *    from a caller-provided workspace whose size the *_workspace call returns.
  *  * `stream` is a hipStream_t passed as void* (NULL = the default stream).

@@ -168,3 +168,23 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
         B.dense_prefill(q, q, q)
     with pytest.raises(B.MsaError, match="missing"):
         B.sparse_prefill_workspace_bytes(1, 1, 64, phase_keys=16)
+
+
+def test_alignment_validation(lib):
+    odd = ctypes.c_void_p(0x1008)     # 8-byte aligned: not enough for row data or workspaces
+    odd4 = ctypes.c_void_p(0x1002)    # not even 4-byte aligned
+    assert lib.msa_dense_prefill(P(), odd, FAKE, FAKE, FAKE, None, None) == RANGE
+    assert lib.msa_dense_prefill(P(), FAKE, FAKE, FAKE, odd, None, None) == RANGE
+    assert lib.msa_dense_prefill(P(), FAKE, FAKE, FAKE, FAKE, odd4, None) == RANGE
+    assert lib.msa_sparse_prefill(P(), FAKE, FAKE, odd, FAKE, FAKE, 64, FAKE, FAKE, 64, 0, FAKE, 1 << 30,
+                                  FAKE, None, None) == RANGE
+    assert lib.msa_sparse_prefill(P(), FAKE, FAKE, FAKE, odd4, FAKE, 64, FAKE, FAKE, 64, 0, FAKE, 1 << 30,
+                                  FAKE, None, None) == RANGE
+    assert lib.msa_estimate_vs(P(), FAKE, odd, 64, 8, 8, FAKE, FAKE, None, None, FAKE, 1 << 30, None) == RANGE
+    assert lib.msa_estimate_vs(P(), FAKE, FAKE, 64, 8, 8, FAKE, FAKE, None, None, odd, 1 << 30, None) == RANGE
+    assert lib.msa_estimate_vs(P(), FAKE, FAKE, 64, 8, 8, odd4, FAKE, None, None, FAKE, 1 << 30, None) == RANGE
+    assert lib.msa_build_index(P(n=4096), FAKE, 64, FAKE, 256, 64, odd4, FAKE, 64, FAKE, FAKE, 64,
+                               None) == RANGE
+    assert lib.msa_estimate_bs(P(), odd, FAKE, 64, 8, FAKE, FAKE, 64, FAKE, FAKE, 1 << 30, None) == RANGE
+    assert lib.msa_estimate_bs(P(), FAKE, FAKE, 64, 8, FAKE, FAKE, 64, FAKE, odd, 1 << 30, None) == RANGE
+    assert b"aligned" in lib.msa_last_error()
