@@ -105,9 +105,18 @@ def _head_stride(t: torch.Tensor, name: str) -> int:
 
 
 def _problem_of(q: torch.Tensor, k: torch.Tensor, sm_scale: float, v: torch.Tensor | None = None) -> Problem:
-    if q.dim() != 3 or k.dim() != 3:
-        raise MsaError("q and k must be [heads, seq_len, head_dim]")
+    if q.dim() != 3 or k.dim() != 3 or (v is not None and v.dim() != 3):
+        raise MsaError("q, k and v must be [heads, seq_len, head_dim]")
     n = q.shape[1]
+    for t, name in ((k, "k"), (v, "v")):
+        if t is None:
+            continue
+        if t.dtype != q.dtype or t.device != q.device:
+            raise MsaError(f"{name} must have q's dtype and device")
+        if t.shape[1] != n:
+            raise MsaError(f"{name} has {t.shape[1]} rows per head, q has {n}")
+    if v is not None and v.shape[0] != k.shape[0]:
+        raise MsaError("k and v must have the same number of heads")
     sq = _head_stride(q, "q")
     rows = {sq} | ({_head_stride(k, "k")} if k.shape[0] > 1 else set()) | \
         ({_head_stride(v, "v")} if v is not None and v.shape[0] > 1 else set())
@@ -131,10 +140,13 @@ def _lse_like(q: torch.Tensor, p: Problem) -> torch.Tensor:
     return torch.empty((q.shape[0], _stride_rows(p)), dtype=torch.float32, device=q.device)[:, : p.seq_len]
 
 
-def _rows_dev(t: torch.Tensor, name: str, p: Problem, lse: bool = False) -> int:
+def _rows_dev(t: torch.Tensor, name: str, p: Problem, like: torch.Tensor, lse: bool = False) -> int:
     """Pointer of an output that must follow the problem's head stride."""
-    if not t.is_cuda:
-        raise MsaError(f"{name} must be a GPU tensor")
+    if not t.is_cuda or t.device != like.device:
+        raise MsaError(f"{name} must be a GPU tensor on q's device")
+    shape = (p.n_q_heads, p.seq_len) if lse else (p.n_q_heads, p.seq_len, HEAD_DIM)
+    if tuple(t.shape) != shape or t.dtype != (torch.float32 if lse else like.dtype):
+        raise MsaError(f"{name} must be {'float32' if lse else like.dtype} {list(shape)}")
     r = _stride_rows(p)
     ok = (t.dim() == 2 and t.stride(1) == 1 and (t.shape[0] == 1 or t.stride(0) == r)) if lse else \
         (t.dim() == 3 and t.stride(2) == 1 and t.stride(1) == HEAD_DIM and
@@ -227,6 +239,9 @@ def estimate_vs(q: torch.Tensor, k: torch.Tensor, vertical_topk: int, slash_topk
     for t, name in ((v_score, "v_score"), (s_score, "s_score")):
         if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (hq, n)):
             raise MsaError(f"{name} must be float32 [{hq}, {n}]")
+    for t, name, kk in ((v_idx, "v_idx", vertical_topk), (s_idx, "s_idx", slash_topk)):
+        if t.dtype != torch.int32 or tuple(t.shape) != (hq, kk):
+            raise MsaError(f"{name} must be int32 [{hq}, {kk}]")
     _check(lib.msa_estimate_vs(ctypes.byref(p), _in_dev(q, "q"), _in_dev(k, "k"), last_q, vertical_topk,
                                slash_topk, _dev(v_idx, "v_idx"), _dev(s_idx, "s_idx"),
                                _dev(v_score, "v_score") if v_score is not None else None,
@@ -246,19 +261,22 @@ def build_index(v_idx: torch.Tensor, s_idx: torch.Tensor, seq_len: int, *,
         cb, cc = index_caps(seq_len, kv, ks, hq)
         out = alloc_index(hq, seq_len, cb, cc, v_idx.device)
     for t in (v_idx, s_idx):
-        if t.dtype != torch.int32:
-            raise MsaError("index sets must be int32")
+        if t.dtype != torch.int32 or t.dim() != 2 or t.shape[0] != hq:
+            raise MsaError(f"index sets must be int32 [{hq}, k]")
+    bc, bo, cb, cc, ci, ccap = _index_ptrs(out, hq, seq_len)
     _check(lib.msa_build_index(ctypes.byref(p), _dev(v_idx, "v_idx") if kv else None, kv,
-                               _dev(s_idx, "s_idx") if ks else None, ks, BLOCK,
-                               _dev(out.block_count, "block_count"), out.block_offset.data_ptr(),
-                               out.cap_blocks, _dev(out.column_count, "column_count"),
-                               out.column_index.data_ptr(), out.cap_cols, _stream(stream)),
+                               _dev(s_idx, "s_idx") if ks else None, ks, BLOCK, bc, bo, cb, cc, ci, ccap,
+                               _stream(stream)),
            "msa_build_index")
     return out
 
 
 def _index_ptrs(idx: IndexTensors, hq: int, n: int):
+    """Pointers and capacities of work lists shaped for hq heads of n tokens."""
     nqb = (n + BLOCK - 1) // BLOCK
+    for name in ("block_count", "block_offset", "column_count", "column_index"):
+        if not getattr(idx, name).is_cuda:
+            raise MsaError(f"{name} must be a GPU tensor")
     for name in ("block_count", "column_count"):
         t = getattr(idx, name)
         if t.dtype != torch.int32 or tuple(t.shape) != (hq, nqb) or not t.is_contiguous():
@@ -306,7 +324,7 @@ def sparse_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: Ind
         ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
     _check(lib.msa_sparse_prefill(ctypes.byref(p), _in_dev(q, "q"), _in_dev(k, "k"), _in_dev(v, "v"),
                                   bc, bo, cb, cc, ci, ccap, phase_keys, ws_ptr, ws_bytes,
-                                  _rows_dev(out, "out", p), _rows_dev(lse, "lse", p, True) if want_lse else None,
+                                  _rows_dev(out, "out", p, q), _rows_dev(lse, "lse", p, q, True) if want_lse else None,
                                   _stream(stream)),
            "msa_sparse_prefill")
     return (out, lse) if want_lse else out
@@ -324,7 +342,7 @@ def dense_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, out: tor
     if lse is True:
         lse = _lse_like(q, p)
     _check(lib.msa_dense_prefill(ctypes.byref(p), _in_dev(q, "q"), _in_dev(k, "k"), _in_dev(v, "v"),
-                                 _rows_dev(out, "out", p), _rows_dev(lse, "lse", p, True) if want_lse else None,
+                                 _rows_dev(out, "out", p, q), _rows_dev(lse, "lse", p, q, True) if want_lse else None,
                                  _stream(stream)), "msa_dense_prefill")
     return (out, lse) if want_lse else out
 
@@ -343,9 +361,9 @@ def estimate_bs(q: torch.Tensor, k: torch.Tensor, topk_blocks: int, *, cap_block
     ws_bytes = int(lib.msa_estimate_bs_workspace(ctypes.byref(p), BLOCK))
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    bc, bo, cb, cc, _, _ = _index_ptrs(out, hq, n)
     _check(lib.msa_estimate_bs(ctypes.byref(p), _in_dev(q, "q"), _in_dev(k, "k"), BLOCK, topk_blocks,
-                               _dev(out.block_count, "block_count"), out.block_offset.data_ptr(),
-                               out.cap_blocks, _dev(out.column_count, "column_count"),
+                               bc, bo, cb, cc,
                                _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                                _stream(stream)), "msa_estimate_bs")
     return out

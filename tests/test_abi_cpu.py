@@ -188,3 +188,17 @@ def test_alignment_validation(lib):
     assert lib.msa_estimate_bs(P(), odd, FAKE, 64, 8, FAKE, FAKE, 64, FAKE, FAKE, 1 << 30, None) == RANGE
     assert lib.msa_estimate_bs(P(), FAKE, FAKE, 64, 8, FAKE, FAKE, 64, FAKE, odd, 1 << 30, None) == RANGE
     assert b"aligned" in lib.msa_last_error()
+
+
+def test_binding_rejects_mismatched_inputs(lib):
+    """The binding checks shapes, dtypes and devices before any pointer reaches
+    the library (CPU tensors: every case fails before the device check)."""
+    import torch
+    q = torch.zeros(4, 256, 128, dtype=torch.bfloat16)
+    k = torch.zeros(2, 256, 128, dtype=torch.bfloat16)
+    for kk, vv, what in [(k[:, :128], k, "rows per head"), (k.float(), k, "dtype"), (k, k[:1], "heads"),
+                         (k, k[:, :200], "rows per head")]:
+        with pytest.raises(B.MsaError, match=what):
+            B.dense_prefill(q, kk, vv)
+    with pytest.raises(B.MsaError, match="rows per head"):
+        B.estimate_vs(q, k[:, :64], 8, 8)
