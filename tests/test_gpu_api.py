@@ -144,3 +144,27 @@ def test_packed_batch_calls():
             assert torch.equal(out[:, a:b], one), (call.__name__, i)
     with pytest.raises(msa.MsaError):
         msa.streaming_forward(q, k, v, 64, 128, cu_seqlens=[0, 100, 50, q.shape[1]])
+
+
+def test_index_rows_not_16_byte_aligned():
+    """Work lists whose block_offset starts 4 bytes into an allocation (rows
+    4-byte aligned only) take the element-wise stores and hold the same lists."""
+    hq, n, kv, ks = 2, 64 * 40 + 9, 24, 40
+    g = torch.Generator().manual_seed(91)
+    vi = torch.sort(torch.randperm(n, generator=g)[:kv])[0].repeat(hq, 1).int().cuda()
+    si = torch.sort(torch.randperm(n, generator=g)[:ks])[0].repeat(hq, 1).int().cuda()
+    ref = msa.build_index(vi, si, n)
+    cb, cc = ref.cap_blocks, ref.cap_cols
+    assert cb % 4 == 0
+    nqb = ref.block_count.shape[1]
+    buf = torch.full((hq * nqb * cb + 1,), -7, dtype=torch.int32, device="cuda")
+    odd = msa.IndexTensors(torch.empty_like(ref.block_count), buf[1:].view(hq, nqb, cb),
+                           torch.empty_like(ref.column_count), torch.empty_like(ref.column_index))
+    assert odd.block_offset.data_ptr() % 16 == 4
+    msa.build_index(vi, si, n, out=odd)
+    assert torch.equal(odd.block_count, ref.block_count) and torch.equal(odd.column_count, ref.column_count)
+    live = torch.arange(cb, device="cuda")[None, None, :] < ref.block_count[:, :, None]
+    assert torch.equal(odd.block_offset[live], ref.block_offset[live])
+    assert int(buf[0]) == -7                                    # nothing written before the array
+    livec = torch.arange(cc, device="cuda")[None, None, :] < ref.column_count[:, :, None]
+    assert torch.equal(odd.column_index[livec], ref.column_index[livec])
