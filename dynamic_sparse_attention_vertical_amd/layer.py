@@ -48,6 +48,7 @@ class LayerPlan:
         self.s_idx = torch.empty((self.n_q_heads, self.slash_topk), **i32)
 
 
+@msa.on_stream
 def vertical_slash_layer(q, k, v, vertical_topk: int, slash_topk: int, *, plan: LayerPlan | None = None,
                          out: torch.Tensor | None = None, lse=None, stream=None):
     """Estimate + build index + sparse prefill for every head of q.
@@ -129,6 +130,7 @@ class MixedPlan:
         self.attn_workspace = torch.empty(aws, dtype=torch.uint8, device=self.device) if aws else None
 
 
+@msa.on_stream
 def mixed_index(q, k, plan: MixedPlan, *, stream=None) -> msa.IndexTensors:
     """Work lists of every head of a mixed layer: 'a' (static sink + window
     index), 'vs' (online vertical-slash estimate) and 'bs' (online
@@ -158,6 +160,7 @@ def mixed_index(q, k, plan: MixedPlan, *, stream=None) -> msa.IndexTensors:
     return plan.index
 
 
+@msa.on_stream
 def mixed_layer(q, k, v, plan: MixedPlan, *, out: torch.Tensor | None = None, lse=None, stream=None):
     """Per-head patterns in one layer (see mixed_index), then a single sparse
     prefill over all heads."""
@@ -197,6 +200,7 @@ def _batched(q, k, v):
     return q, k, v, False
 
 
+@msa.on_stream
 def vertical_slash_sparse_attention(q, k, v, vertical_topk: int, slash_topk: int, *, cu_seqlens=None,
                                     stream=None):
     """Vertical-slash sparse attention: per head, the vertical_topk key columns
@@ -218,6 +222,7 @@ def vertical_slash_sparse_attention(q, k, v, vertical_topk: int, slash_topk: int
     return out[0] if squeeze else out
 
 
+@msa.on_stream
 def block_sparse_attention(q, k, v, topk: int, *, cu_seqlens=None, stream=None):
     """Block-sparse attention: each 64-row query block attends to its topk
     highest-scoring 64-key blocks (mean-pooled q and k block scores), causally."""
@@ -240,6 +245,7 @@ def block_sparse_attention(q, k, v, topk: int, *, cu_seqlens=None, stream=None):
     return out[0] if squeeze else out
 
 
+@msa.on_stream
 def streaming_forward(q, k, v, init_num: int, local_window_num: int, *, cu_seqlens=None, stream=None):
     """A-shape (streaming) attention: every row attends to the first init_num
     keys and to the local_window_num keys ending at itself (diagonal offsets

@@ -9,6 +9,7 @@ Every step of the computation runs in the HIP kernels; there is no fallback.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from dataclasses import dataclass
 
@@ -176,6 +177,20 @@ def _stream(stream) -> int:
     return stream.cuda_stream
 
 
+def on_stream(fn):
+    """Run a call with its `stream` (if given) as torch's current stream, so
+    that every buffer it allocates belongs to that stream (the caching
+    allocator reuses its memory only after the stream's work on it) and every
+    torch op it issues is ordered with the library's launches."""
+    @functools.wraps(fn)
+    def wrapper(*args, stream=None, **kw):
+        if stream is None:
+            return fn(*args, stream=None, **kw)
+        with torch.cuda.stream(stream):
+            return fn(*args, stream=stream, **kw)
+    return wrapper
+
+
 @dataclass
 class IndexTensors:
     """Per-query-block work lists on the GPU (int32)."""
@@ -220,6 +235,7 @@ def estimate_bs_workspace_bytes(n_q_heads: int, n_kv_heads: int, seq_len: int, d
     return int(load().msa_estimate_bs_workspace(ctypes.byref(p), BLOCK))
 
 
+@on_stream
 def estimate_vs(q: torch.Tensor, k: torch.Tensor, vertical_topk: int, slash_topk: int, *,
                 last_q: int = LAST_Q, v_score: torch.Tensor | None = None,
                 s_score: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
@@ -251,6 +267,7 @@ def estimate_vs(q: torch.Tensor, k: torch.Tensor, vertical_topk: int, slash_topk
     return v_idx, s_idx
 
 
+@on_stream
 def build_index(v_idx: torch.Tensor, s_idx: torch.Tensor, seq_len: int, *,
                 out: IndexTensors | None = None, stream=None) -> IndexTensors:
     lib = load()
@@ -298,6 +315,7 @@ def sparse_prefill_workspace_bytes(n_q_heads: int, n_kv_heads: int, seq_len: int
     return int(load().msa_sparse_prefill_workspace(ctypes.byref(p), phase_keys))
 
 
+@on_stream
 def sparse_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: IndexTensors, *,
                    out: torch.Tensor | None = None, lse: torch.Tensor | bool | None = None,
                    sm_scale: float = 0.0, phase_keys: int = 0, workspace: torch.Tensor | None = None,
@@ -330,6 +348,7 @@ def sparse_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: Ind
     return (out, lse) if want_lse else out
 
 
+@on_stream
 def dense_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, out: torch.Tensor | None = None,
                   lse: torch.Tensor | bool | None = None, sm_scale: float = 0.0, stream=None):
     """Dense causal attention.  Returns out (and lse if requested)."""
@@ -347,6 +366,7 @@ def dense_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, out: tor
     return (out, lse) if want_lse else out
 
 
+@on_stream
 def estimate_bs(q: torch.Tensor, k: torch.Tensor, topk_blocks: int, *, cap_blocks: int | None = None,
                 out: IndexTensors | None = None, workspace: torch.Tensor | None = None,
                 sm_scale: float = 0.0, stream=None) -> IndexTensors:

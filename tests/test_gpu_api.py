@@ -168,3 +168,22 @@ def test_index_rows_not_16_byte_aligned():
     assert int(buf[0]) == -7                                    # nothing written before the array
     livec = torch.arange(cc, device="cuda")[None, None, :] < ref.column_count[:, :, None]
     assert torch.equal(odd.column_index[livec], ref.column_index[livec])
+
+
+def test_side_stream_calls():
+    """Calls on a side stream (their temporaries allocated on it, torch ops
+    ordered with the launches) give the default stream's results."""
+    hq, hkv, n = 4, 2, 1024 + 17
+    x = make_inputs(small_workload(n_q_heads=hq, n_kv_heads=hkv, seq_len=n, seed=97))
+    q, k, v = x["q"].cuda(), x["k"].cuda(), x["v"].cuda()
+    ref = [msa.vertical_slash_sparse_attention(q, k, v, 30, 90), msa.block_sparse_attention(q, k, v, 3),
+           msa.streaming_forward(q, k, v, 64, 128), msa.dense_prefill(q, k, v)]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(torch.cuda.Stream()):     # a third stream current: the calls must not use it
+        got = [msa.vertical_slash_sparse_attention(q, k, v, 30, 90, stream=side),
+               msa.block_sparse_attention(q, k, v, 3, stream=side),
+               msa.streaming_forward(q, k, v, 64, 128, stream=side), msa.dense_prefill(q, k, v, stream=side)]
+    side.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
