@@ -28,6 +28,12 @@
 // workspace between launches; its columns and its output go to the launch that
 // holds its own rows.
 //
+// Before the phases, a query block whose lists leave few keys out for every
+// q head of a kv group (a unit) runs as one walk over the aligned tiles 0..b,
+// as in the dense kernel: one K/V copy per tile serves the group's heads, and
+// each head masks the keys outside its own blocks and columns (its "holes").
+// The walk marks the units it takes; the per-head launches skip them.
+//
 // The pages: causal attention computed only over the selected entries, in
 // FlashAttention style (talk slides "System-Algorithm Co-design", slide
 // "MInference": dynamic sparse attention calculation with PIT and
@@ -55,6 +61,13 @@ constexpr int kStateFloats = 64 * 64 + 2 * 64;   // sparse phase state of one wa
 // tiles, and storing the state again as much more, which a handful of tiles
 // would not repay.  The tiles keep their order, so results do not change.
 constexpr int kMinPhaseTiles = 16;
+// A unit of the grouped walk (the q heads of one kv group sharing a workgroup,
+// one query block) qualifies when every head's blocks and columns leave at
+// most 1/8 of the keys [0, r1] out, in at most kGrpHoles ranges, with at most
+// kGrpCols columns: walking all aligned tiles 0..b with one copy per tile for
+// the group then costs at most an eighth more matrix work than the lists.
+constexpr int kGrpHoles = 192;
+constexpr int kGrpCols = 64;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
@@ -135,6 +148,7 @@ struct ChunkSrc {
     bool masked;    // some score of the tile needs the mask
     int base;
     int c0;
+    uint64_t allow; // grouped walk: bit e set iff key base + e is in this wave's head's lists
 };
 
 // Per-lane constants of the chunk copies.  A chunk (32 rows) is moved by the
@@ -322,7 +336,7 @@ __device__ __forceinline__ int lower_bound_near(const int32_t *list, int cnt, in
 // fp32 (a checking path) uses the same scheme with 64 KB of LDS.
 // kH q heads of one kv group per workgroup (2 kH waves) share every K/V copy;
 // used by the dense kernel, whose heads all walk the same tiles.
-template <typename T, bool kDense, int kH>
+template <typename T, bool kDense, int kH, bool kGrp = false>
 __global__ __launch_bounds__(kThreads * kH) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1, sizeof(T) == 2 ? 2 : 1)))
 void attn_fwd_kernel(AttnArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the body uses gfx950-only LDS builtins
@@ -351,6 +365,63 @@ void attn_fwd_kernel(AttnArgs a) {
     const T *kp = reinterpret_cast<const T *>(a.k) + ((int64_t)g * a.stride) * kD;
     const T *vp = reinterpret_cast<const T *>(a.v) + ((int64_t)g * a.stride) * kD;
 
+    // Grouped walk: each wave lists its head's holes (key ranges in [0, r1]
+    // outside the head's blocks, ascending) and columns in LDS, and the unit
+    // goes ahead only if every head qualifies; the verdict goes to grp.
+    __shared__ int32_t glist[kGrp ? 2 * kH : 1][2 * kGrpHoles + kGrpCols];
+    int nhole = 0, ncl_g = 0;
+    if constexpr (kGrp) {
+        const int lim = min(r0 + kBQ, n32);                // keys [0, r1]
+        const int64_t item = (int64_t)h * nqb + b;
+        const int nbk = min(max(load_uniform(a.block_count + item), 0), a.cap_b);
+        ncl_g = min(max(load_uniform(a.column_count + item), 0), a.cap_c);
+        bool ok = ncl_g <= kGrpCols && (int64_t)kBK * nbk + ncl_g >= lim - lim / 8;
+        int32_t *hw = glist[wave];
+        if (ok) {
+            const int32_t *bl = a.block_offset + item * a.cap_b;
+            int prev = 0;                                  // end of the blocks so far
+            int s_next = lane < nbk ? bl[lane] : lim;      // one round of loads ahead
+            for (int base = 0; base < nbk && nhole <= kGrpHoles; base += 64) {
+                const int i = base + lane;
+                const int s = s_next;
+                s_next = i + 64 < nbk ? bl[i + 64] : lim;
+                const int lo = min(max(s, 0), lim), hi = min(max(s + kBK, 0), lim);
+                int pe = __shfl_up(hi, 1, 64);
+                if (lane == 0) pe = prev;
+                const bool gap = i < nbk && lo > pe;
+                const uint64_t m = __builtin_amdgcn_ballot_w64(gap);
+                const int pos = nhole + __builtin_popcountll(m & ((1ull << lane) - 1));
+                if (gap && pos < kGrpHoles) {
+                    hw[2 * pos] = pe;
+                    hw[2 * pos + 1] = lo;
+                }
+                nhole += __builtin_popcountll(m);
+                prev = __shfl(hi, min(nbk - base, 64) - 1, 64);
+            }
+            if (prev < lim) {
+                if (lane == 0 && nhole < kGrpHoles) {
+                    hw[2 * nhole] = prev;
+                    hw[2 * nhole + 1] = lim;
+                }
+                ++nhole;
+            }
+            ok = nhole <= kGrpHoles;
+            if (ok) {
+                const int32_t *cl = a.column_index + item * a.cap_c;
+                for (int i = lane; i < ncl_g; i += 64) hw[2 * kGrpHoles + i] = cl[i];
+                // uncovered keys: the holes less the columns (which all lie in holes)
+                int len = 0;
+                for (int j = lane; j < nhole; j += 64) len += hw[2 * j + 1] - hw[2 * j];
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) len += __shfl_xor(len, o, 64);
+                ok = len - ncl_g <= lim / 8;
+            }
+        }
+        const bool unit_ok = __syncthreads_and(ok) != 0;
+        if (tid == 0) a.grp[(int64_t)hgrp * nqb + b] = unit_ok ? 1 : 0;
+        if (!unit_ok) return;
+    }
+
     int nblk, ncol;
     const int32_t *blist = nullptr, *clist = nullptr;
     // key phases (sparse, ws set): the first starts from an empty state, and
@@ -364,6 +435,9 @@ void attn_fwd_kernel(AttnArgs a) {
         nblk = (int)b + 1;
         ncol = 0;
     } else {
+        if (a.grp != nullptr &&
+            load_uniform(a.grp + (int64_t)(h / a.grp_kh) * nqb + b) != 0)   // done by the grouped walk
+            return;
         const int64_t item = (int64_t)h * nqb + b;
         nblk = min(max(a.block_count[item], 0), a.cap_b);
         ncol = min(max(a.column_count[item], 0), a.cap_c);
@@ -409,6 +483,14 @@ void attn_fwd_kernel(AttnArgs a) {
 
     // where tile t's keys come from (one scalar load per block tile), and the
     // chunk of it in half hf
+    // grouped walk: the hole at or after the current tile (hx, hy) and the
+    // first column not before it; calls come with t non-decreasing
+    int hp = 0, cp = 0, hx = INT_MAX, hy = INT_MAX;
+    auto hole_at = [&](int j, int &x, int &y) {
+        x = j < nhole ? __builtin_amdgcn_readfirstlane(glist[wave][2 * j]) : INT_MAX;
+        y = j < nhole ? __builtin_amdgcn_readfirstlane(glist[wave][2 * j + 1]) : INT_MAX;
+    };
+    if constexpr (kGrp) hole_at(0, hx, hy);
     auto tile_of = [&](int t) {
         ChunkSrc s;
         s.is_col = t >= nblk;
@@ -416,11 +498,36 @@ void attn_fwd_kernel(AttnArgs a) {
         s.c0 = s.is_col ? (t - nblk) * kBK : 0;
         s.fast = !s.is_col && s.base >= 0 && s.base <= n32 - kBK;
         s.masked = !s.fast || s.base + kBK - 1 > r0;
+        s.allow = ~0ull;
+        if constexpr (kGrp) {
+            const int t0 = t * kBK;
+            while (hy <= t0) hole_at(++hp, hx, hy);
+            if (hx < t0 + kBK) {                            // some hole reaches into the tile
+                uint64_t cut = 0;
+                int j = hp, x = hx, y = hy;
+                while (x < t0 + kBK) {
+                    const int lo = max(x, t0) - t0, len = min(y, t0 + kBK) - t0 - lo;
+                    cut |= len >= 64 ? ~0ull : ((1ull << len) - 1) << lo;
+                    if (y > t0 + kBK) break;
+                    hole_at(++j, x, y);
+                }
+                auto col = [&](int c) { return __builtin_amdgcn_readfirstlane(glist[wave][2 * kGrpHoles + c]); };
+                while (cp < ncl_g && col(cp) < t0) ++cp;
+                for (int c = cp; c < ncl_g; ++c) {
+                    const int key = col(c);
+                    if (key >= t0 + kBK) break;
+                    cut &= ~(1ull << (key - t0));
+                }
+                s.allow = ~cut;
+                s.masked = true;
+            }
+        }
         return s;
     };
     auto half_of = [](ChunkSrc s, int hf) {
         s.base += 32 * hf;
         s.c0 += 32 * hf;
+        s.allow >>= 32 * hf;
         return s;
     };
     // start K of chunk c (and record a column chunk's keys for its mask)
@@ -505,6 +612,17 @@ void attn_fwd_kernel(AttnArgs a) {
                     const int e = jj * 8 + hl * 4 + i;
                     if (e > hi || e < lo) s[jj * 4 + i] = -INFINITY;
                 }
+            if constexpr (kGrp) {
+                const uint32_t al = (uint32_t)cs.allow;     // keys base .. base+31 of the chunk
+                if (al != ~0u) {
+                    const uint32_t am = al >> (hl * 4);
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (!((am >> (jj * 8 + i)) & 1u)) s[jj * 4 + i] = -INFINITY;
+                }
+            }
         }
     };
     // online softmax of S(c) -> P(c); returns the factor for O (1 if no row
@@ -620,10 +738,10 @@ void attn_fwd_kernel(AttnArgs a) {
 #endif
 }
 
-template <typename T, bool kDense, int kH> hipError_t launch_h(const AttnArgs &a, hipStream_t s) {
+template <typename T, bool kDense, int kH, bool kGrp = false> hipError_t launch_h(const AttnArgs &a, hipStream_t s) {
     const int64_t total = (int64_t)(a.hq / kH) * ((a.n + kBQ - 1) / kBQ - (kDense ? 0 : a.qb_lo));
     if (total == 0) return hipSuccess;
-    hipLaunchKernelGGL((attn_fwd_kernel<T, kDense, kH>), dim3((unsigned)total), dim3(kThreads * kH), 0, s, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, kDense, kH, kGrp>), dim3((unsigned)total), dim3(kThreads * kH), 0, s, a);
     return hipGetLastError();
 }
 
@@ -648,6 +766,19 @@ template <typename T, bool kDense> hipError_t launch(AttnArgs a, hipStream_t s) 
             a.qb_lo = 0;
             return launch_h<T, false, 1>(a, s);
         }
+        // first the grouped walk over the units that qualify (it marks them),
+        // then the key phases of the per-head kernel over the rest
+        const int64_t nqb = (a.n + kBQ - 1) / kBQ;
+        a.grp = reinterpret_cast<int32_t *>(reinterpret_cast<int2 *>(a.ws + (int64_t)a.hq * nqb * 2 * kStateFloats) +
+                                            (int64_t)a.hq * nqb);
+        const int G = a.hq / a.hkv;
+        a.grp_kh = G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1);
+        {
+            const hipError_t e = a.grp_kh == 4   ? launch_h<T, true, 4, true>(a, s)
+                                 : a.grp_kh == 2 ? launch_h<T, true, 2, true>(a, s)
+                                                 : launch_h<T, true, 1, true>(a, s);
+            if (e != hipSuccess) return e;
+        }
         const int64_t np = (a.n + R - 1) / R;
         for (int64_t j = 0; j < np; ++j) {
             a.k_lo = j == 0 ? INT_MIN : (int32_t)(j * R);
@@ -664,7 +795,7 @@ template <typename T, bool kDense> hipError_t launch(AttnArgs a, hipStream_t s) 
 
 size_t sparse_state_bytes(int64_t hq, int64_t n, int64_t phase_keys) {
     if (phase_keys <= 0 || phase_keys >= n) return 0;
-    return (size_t)hq * (size_t)((n + kBQ - 1) / kBQ) * (2 * kStateFloats * sizeof(float) + sizeof(int2));
+    return (size_t)hq * (size_t)((n + kBQ - 1) / kBQ) * (2 * kStateFloats * sizeof(float) + sizeof(int2) + sizeof(int32_t));
 }
 
 hipError_t launch_sparse_prefill(const AttnArgs &a, int dtype, hipStream_t s) {

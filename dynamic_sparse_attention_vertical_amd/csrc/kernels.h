@@ -25,6 +25,12 @@ struct AttnArgs {
     int32_t k_lo, k_hi;
     int64_t qb_lo;
     float *ws;
+    // units of grp_kh q heads of one kv group and one query block whose lists
+    // leave few keys out run first as one aligned-tile walk with a shared
+    // copy per tile; grp[(h / grp_kh) * nblocks + b] = 1 marks them for the
+    // per-head launches to skip (NULL: no such walk)
+    int32_t *grp;
+    int32_t grp_kh;
 };
 
 // Bytes of sparse-prefill state for hq heads and n keys in phases of

@@ -269,6 +269,8 @@ static int attn_common(const msa_problem *p, const void *q, const void *k, const
     a.k_hi = INT32_MAX;
     a.qb_lo = 0;
     a.ws = nullptr;
+    a.grp = nullptr;
+    a.grp_kh = 1;
     return MSA_OK;
 }
 

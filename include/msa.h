@@ -162,7 +162,11 @@ int msa_build_index(const msa_problem *p, const int32_t *v_idx, int32_t vertical
  * time come mostly from one R-key range of a kv head; a query block with only
  * a few tiles in a range leaves them to the next launch, and its columns go
  * to the launch that holds its own rows.  The running softmax state of each
- * query block (fp32) passes between launches through `workspace`.  This path
+ * query block (fp32) passes between launches through `workspace`.  Before
+ * them, one launch takes the query blocks whose lists, for every q head of a
+ * kv group (up to four heads), leave at most 1/8 of the keys [0, r1] out: it
+ * walks all 64-key tiles 0..b once for those heads together and masks each
+ * head to its own blocks and columns.  This path
  * needs every block list ascending, as msa_build_index and msa_estimate_bs
  * write them; the result is then the same up to fp32 rounding order.  With
  * R >= seq_len there is one launch over the lists in their given order and no
@@ -183,7 +187,7 @@ int msa_sparse_prefill(const msa_problem *p, const void *q, const void *k, const
 
 /* Workspace bytes msa_sparse_prefill needs (0 when one phase covers seq_len;
  * 0 for invalid arguments):
- *   n_q_heads * ceil(seq_len / 64) * (2 * (64 * 64 + 2 * 64) * 4 + 8). */
+ *   n_q_heads * ceil(seq_len / 64) * (2 * (64 * 64 + 2 * 64) * 4 + 12). */
 size_t msa_sparse_prefill_workspace(const msa_problem *p, int32_t phase_keys);
 
 /* Dense causal attention (every j <= i), same layouts as msa_sparse_prefill. */

@@ -140,8 +140,9 @@ def test_sparse_prefill_workspace_size(lib):
     assert lib.msa_sparse_prefill_workspace(P(), 4096) == 0
     assert lib.msa_sparse_prefill_workspace(P(n=1 << 17), 1 << 17) == 0
     # per q head and query block: two waves x (64 x 64 O + 64 max + 64 sum) fp32,
-    # and an 8-byte record (state stored, where the next phase's blocks start)
-    per_item = 2 * (64 * 64 + 2 * 64) * 4 + 8
+    # an 8-byte record (state stored, where the next phase's blocks start) and
+    # a 4-byte mark of the query blocks the grouped walk takes
+    per_item = 2 * (64 * 64 + 2 * 64) * 4 + 12
     assert lib.msa_sparse_prefill_workspace(P(), 1024) == 32 * 64 * per_item
     assert lib.msa_sparse_prefill_workspace(P(n=1 << 17), 0) == 32 * 2048 * per_item
     assert lib.msa_sparse_prefill_workspace(P(), 100) == 0          # invalid: not a multiple of 64

@@ -93,7 +93,7 @@ def test_sparse_prefill_phases(hq, hkv, n, kv, ks, phase, fp32):
     gidx.column_index.copy_(torch.from_numpy(ridx.column_index))
     dt = torch.float32 if fp32 else torch.bfloat16
     need = msa.sparse_prefill_workspace_bytes(hq, hkv, n, dt, phase_keys=phase)
-    assert need == hq * (n // 64) * (2 * (64 * 64 + 128) * 4 + 8)
+    assert need == hq * (n // 64) * (2 * (64 * 64 + 128) * 4 + 12)
     ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")     # no initial contents assumed
     qs, ks_, vs = cuda(q, k, v)
     out, lse = msa.sparse_prefill(qs, ks_, vs, gidx, lse=True, phase_keys=phase, workspace=ws)
@@ -340,3 +340,40 @@ def test_explicit_softmax_scale(fp32):
     dref, drlse = oracle.dense_attention(q, k, v, scale=scale)
     compare_out(dout.float().cpu().numpy(), dref, fp32, "dense, sm_scale")
     compare_lse(dlse.cpu().numpy(), drlse, "dense, sm_scale")
+
+
+@pytest.mark.parametrize("hq,hkv,n,fp32", [(8, 2, 64 * 40 + 17, False), (4, 2, 64 * 24, False),
+                                           (3, 3, 64 * 20 + 1, False), (4, 1, 64 * 16 + 33, True)])
+def test_sparse_grouped_walk(hq, hkv, n, fp32):
+    """Lists that leave few keys out: every diagonal but two runs of 200 (so
+    query blocks far enough down have two holes, partly filled by columns).
+    The last head instead keeps the diagonals below n - 400, which leaves too
+    much out for the late query blocks.  The q heads of a kv group whose lists
+    all qualify run as one aligned-tile walk, the rest per head: against the
+    oracle, and against the per-head kernel alone (one phase, no workspace)."""
+    w, q, k, v = inputs(hq, hkv, n, seed=n + hq, fp32=fp32)
+    rng = np.random.default_rng(n + 7)
+    vi = np.sort(np.stack([rng.choice(n, 12, replace=False) for _ in range(hq)]), axis=1).astype(np.int32)
+    rows = []
+    for h in range(hq):
+        if h == hq - 1:
+            rows.append(np.arange(n - 400))
+        else:
+            a = 200 + 37 * h
+            drop = np.r_[np.arange(a, a + 200), np.arange(a + 400, a + 600)]
+            rows.append(np.setdiff1d(np.arange(n), drop))
+    si = np.stack(rows).astype(np.int32)
+    ridx = oracle.build_index(vi, si, n)
+    gidx = msa.alloc_index(hq, n, ridx.block_offset.shape[2], ridx.column_index.shape[2])
+    gidx.block_count.copy_(torch.from_numpy(ridx.block_count))
+    gidx.block_offset.copy_(torch.from_numpy(ridx.block_offset))
+    gidx.column_count.copy_(torch.from_numpy(ridx.column_count))
+    gidx.column_index.copy_(torch.from_numpy(ridx.column_index))
+    qs, ks_, vs = cuda(q, k, v)
+    out, lse = msa.sparse_prefill(qs, ks_, vs, gidx, lse=True, phase_keys=512)
+    ref, rlse = oracle.attention_with_mask(q, k, v, oracle.index_mask(ridx, n))
+    compare_out(out.float().cpu().numpy(), ref, fp32, "grouped walk")
+    compare_lse(lse.cpu().numpy(), rlse, "grouped walk")
+    one, one_lse = msa.sparse_prefill(qs, ks_, vs, gidx, lse=True, phase_keys=-(-n // 64) * 64)
+    compare_out(out.float().cpu().numpy(), one.float().cpu().numpy(), fp32, "grouped vs per-head")
+    compare_lse(lse.cpu().numpy(), one_lse.cpu().numpy(), "grouped vs per-head")
