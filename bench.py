@@ -4,9 +4,10 @@ A step is one pass of the whole hot path over one layer's synthetic input
 already resident in HBM: online estimation (scores + top-k), index build, and
 the sparse prefill kernel.  Prints one JSON line:
 
-  value      = executed sparse-attention TFLOP per layer / layer time
-               (effective TFLOP/s; executed FLOP counts every issued 64x64
-               tile: 4 * 128 * 64 * 64 per block and per 64-column chunk)
+  value      = listed sparse-attention TFLOP per layer / layer time
+               (effective TFLOP/s; every 64x64 tile of the work lists counts
+               4 * 128 * 64 * 64 FLOP, per block and per 64-column chunk; the
+               masked tiles that the grouped walk also runs are not counted)
   roofline   = the sparse prefill kernel against the bf16 MFMA peak, timed
                with HIP events on its own stream over the timed steps
   cpu_baseline = the float64 CPU oracle on a bounded sample, extrapolated to
@@ -62,9 +63,11 @@ def measured_traffic(workload):
 
 
 def phase_launches(n):
-    """Launches of one sparse prefill at the default phase length."""
+    """Launches of one sparse prefill at the default phase length: the
+    grouped walk, then one per key phase (a single launch when one phase
+    covers the sequence)."""
     from dynamic_sparse_attention_vertical_amd.msa import DEFAULT_PHASE_KEYS
-    return max(1, -(-n // DEFAULT_PHASE_KEYS))
+    return 1 + -(-n // DEFAULT_PHASE_KEYS) if n > DEFAULT_PHASE_KEYS else 1
 
 
 def copy_calibration(gib):
@@ -314,8 +317,8 @@ def main():
         "config": {"workload": w.name, "seq_len": n, "q_heads": hq, "kv_heads": hkv, "head_dim": 128,
                    "vertical_topk": w.vertical_topk, "slash_topk": w.slash_topk, "last_q": 64, "block": 64},
         "breakdown": breakdown,
-        # the step's sparse prefill is n / phase_keys launches of one kernel
-        # (key phases): achieved = the step's executed FLOPs over their summed time
+        # the step's sparse prefill is one grouped-walk launch and n / phase_keys
+        # key-phase launches: achieved = the step's listed FLOPs over their summed time
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel<bf16, sparse>",
                      "launches_per_step": phase_launches(n),
                      "achieved": round(att_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

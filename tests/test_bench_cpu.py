@@ -15,11 +15,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def test_phase_launches():
     from dynamic_sparse_attention_vertical_amd.msa import DEFAULT_PHASE_KEYS as R
+    # one launch when one phase covers the sequence; else the grouped walk
+    # and one launch per phase
     assert bench.phase_launches(R) == 1
-    assert bench.phase_launches(R + 64) == 2
-    assert bench.phase_launches(1 << 17) == -(-(1 << 17) // R)     # a short last phase counts
-    assert bench.phase_launches(1 << 20) == -(-(1 << 20) // R)
-    assert bench.phase_launches(3 * R) == 3
+    assert bench.phase_launches(R + 64) == 3
+    assert bench.phase_launches(1 << 17) == 1 + -(-(1 << 17) // R)     # a short last phase counts
+    assert bench.phase_launches(1 << 20) == 1 + -(-(1 << 20) // R)
+    assert bench.phase_launches(3 * R) == 4
 
 
 def test_traffic_record_follows_the_kernel_source(tmp_path, monkeypatch):
