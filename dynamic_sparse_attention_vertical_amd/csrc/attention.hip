@@ -149,6 +149,7 @@ struct ChunkSrc {
     int base;
     int c0;
     uint64_t allow; // grouped walk: bit e set iff key base + e is in this wave's head's lists
+    bool causal;    // some key of the tile is past a row or outside the sequence
 };
 
 // Per-lane constants of the chunk copies.  A chunk (32 rows) is moved by the
@@ -498,6 +499,7 @@ void attn_fwd_kernel(AttnArgs a) {
         s.c0 = s.is_col ? (t - nblk) * kBK : 0;
         s.fast = !s.is_col && s.base >= 0 && s.base <= n32 - kBK;
         s.masked = !s.fast || s.base + kBK - 1 > r0;
+        s.causal = s.masked;
         s.allow = ~0ull;
         if constexpr (kGrp) {
             const int t0 = t * kBK;
@@ -603,6 +605,7 @@ void attn_fwd_kernel(AttnArgs a) {
             }
         } else {
             // e allowed iff 0 <= base + e <= qrow
+            if (cs.causal) {
             const int hi = min(max(qrow - cs.base, -1), 32);
             const int lo = min(max(-cs.base, 0), 32);
 #pragma unroll
@@ -612,15 +615,17 @@ void attn_fwd_kernel(AttnArgs a) {
                     const int e = jj * 8 + hl * 4 + i;
                     if (e > hi || e < lo) s[jj * 4 + i] = -INFINITY;
                 }
+            }
             if constexpr (kGrp) {
                 const uint32_t al = (uint32_t)cs.allow;     // keys base .. base+31 of the chunk
                 if (al != ~0u) {
-                    const uint32_t am = al >> (hl * 4);
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            if (!((am >> (jj * 8 + i)) & 1u)) s[jj * 4 + i] = -INFINITY;
+                        for (int i = 0; i < 4; ++i) {
+                            const bool k0 = (al >> (jj * 8 + i)) & 1u, k1 = (al >> (jj * 8 + 4 + i)) & 1u;
+                            if (!(hl ? k1 : k0)) s[jj * 4 + i] = -INFINITY;
+                        }
                 }
             }
         }
