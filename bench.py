@@ -8,10 +8,16 @@ the sparse prefill kernel.  Prints one JSON line:
                (effective TFLOP/s; every 64x64 tile of the work lists counts
                4 * 128 * 64 * 64 FLOP, per block and per 64-column chunk; the
                masked tiles that the grouped walk also runs are not counted)
-  roofline   = the sparse prefill kernel against the bf16 MFMA peak, timed
-               with HIP events on its own stream over the timed steps
+  roofline   = the sparse prefill kernel against the bf16 MFMA peak on the
+               tiles it executed (listed tiles, plus every aligned tile 0..b
+               of the query blocks the grouped walk ran), timed with HIP events
+               on its own stream over the timed steps
   cpu_baseline = the float64 CPU oracle on a bounded sample, extrapolated to
                the layer
+
+The default workload is the 1M-token LLaMA-3-8B-shaped layer (32 q / 8 kv
+heads, vertical top-k 1000, slash top-k 6096), with the dense causal kernel
+timed at the same shape for the speedup.
 
 usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
 """
@@ -82,11 +88,37 @@ def copy_calibration(gib):
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4}), flush=True)
 
 
-def executed_tiles(idx):
+def listed_tiles(idx):
+    """64-key tiles of the work lists: every block, and the columns in
+    chunks of 64 per query block."""
     import torch
     bc = idx.block_count.to(torch.int64)
     cc = idx.column_count.to(torch.int64)
     return int(bc.sum().item() + ((cc + 63) // 64).sum().item())
+
+
+def executed_tiles(idx, marks):
+    """Tiles the sparse prefill ran: the listed ones, except that a query
+    block b the grouped walk took ran every aligned tile 0..b (masked to its
+    lists).  marks: [Hq, nQB] from msa.sparse_walk_marks, or None."""
+    import torch
+    bc = idx.block_count.to(torch.int64)
+    per = bc + (idx.column_count.to(torch.int64) + 63) // 64
+    if marks is not None:
+        b = torch.arange(per.shape[1], device=per.device, dtype=torch.int64)[None, :] + 1
+        per = torch.where(marks.to(per.device) != 0, b.expand_as(per), per)
+    return int(per.sum().item()), (0 if marks is None else int((marks != 0).sum().item()))
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def useful_pairs(idx, n):
@@ -149,6 +181,7 @@ def cpu_baseline(x, plan, w, target_s=20.0):
         "value": round(tiles * TILE_FLOP / t_layer / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": threads,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"float64 oracle: estimator on 1 of {hq} heads, index build on all heads, masked "
                    f"attention on {len(done)} of {nqb} query blocks of head 0; layer time extrapolated "
@@ -162,7 +195,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="llama3_8b_128k")
+    ap.add_argument("--workload", default="llama3_8b_1m")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
@@ -240,10 +273,15 @@ def main():
     log(f"[bench] timed {args.steps} steps: {ms_step:.2f} ms/layer (estimate {ms_est:.3f}, index {ms_idx:.3f}, "
         f"sparse prefill {ms_att:.3f})")
 
-    tiles = executed_tiles(plan.index)
+    tiles = listed_tiles(plan.index)
     nqb = n // 64
     causal_tiles = hq * nqb * (nqb + 1) // 2
-    exec_flop = tiles * TILE_FLOP
+    listed_flop = tiles * TILE_FLOP
+    marks = None
+    if plan.attn_workspace is not None:
+        marks = msa.sparse_walk_marks(plan.attn_workspace, hq, hkv, n, q.dtype)
+    run_tiles, walk_blocks = executed_tiles(plan.index, marks)
+    exec_flop = run_tiles * TILE_FLOP
     pairs = useful_pairs(plan.index, n)
     causal_pairs = hq * n * (n + 1) // 2
     att_tflops = exec_flop / (ms_att * 1e-3) / 1e12
@@ -266,11 +304,15 @@ def main():
             "build_index_gbs": round(idx_gbs, 1), "build_index_hbm_frac": round(idx_gbs / PEAK_HBM_GBS, 4)}
     breakdown.update({
         "ms_sparse_prefill": round(ms_att, 4),
-        "executed_tiles": tiles, "causal_tiles": causal_tiles,
-        "executed_density": round(tiles / causal_tiles, 5),
+        "listed_tiles": tiles, "executed_tiles": run_tiles, "causal_tiles": causal_tiles,
+        "grouped_walk_blocks": walk_blocks,
+        "listed_density": round(tiles / causal_tiles, 5),
+        "executed_density": round(run_tiles / causal_tiles, 5),
         "useful_density": round(pairs / causal_pairs, 5),
+        "listed_tflop": round(listed_flop / 1e12, 4),
         "executed_tflop": round(exec_flop / 1e12, 4),
         "sparse_prefill_tflops": round(att_tflops, 2),
+        "sparse_prefill_listed_tflops": round(listed_flop / (ms_att * 1e-3) / 1e12, 2),
     })
     if not args.no_dense:
         dense_out = torch.empty_like(q)
@@ -303,7 +345,7 @@ def main():
 
     res = {
         "metric": METRIC,
-        "value": round(exec_flop / (ms_step * 1e-3) / 1e12, 3),
+        "value": round(listed_flop / (ms_step * 1e-3) / 1e12, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -318,12 +360,17 @@ def main():
                    "vertical_topk": w.vertical_topk, "slash_topk": w.slash_topk, "last_q": 64, "block": 64},
         "breakdown": breakdown,
         # the step's sparse prefill is one grouped-walk launch and n / phase_keys
-        # key-phase launches: achieved = the step's listed FLOPs over their summed time
-        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel<bf16, sparse>",
+        # key-phase launches (one kernel template, attention.hip): achieved =
+        # the FLOPs of the tiles they executed over their summed time
+        "roofline": {"bound": "mfma",
+                     "kernel": "attn_fwd_kernel<bf16> sparse: grouped walk + per-head key phases",
                      "launches_per_step": phase_launches(n),
                      "achieved": round(att_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(w.name)},
+                     "traffic": measured_traffic(w.name),
+                     "traffic_source": ("rocprofv3 FETCH_SIZE + WRITE_SIZE of the same source, committed in "
+                                        "profiles/attn_sparse_traffic.json (null when the kernel source "
+                                        "has changed since)")},
     }
     if mixed:
         log("[bench] the CPU oracle baseline is sampled on vertical-slash layers only")

@@ -381,6 +381,8 @@ void attn_fwd_kernel(AttnArgs a) {
         if (ok) {
             const int32_t *bl = a.block_offset + item * a.cap_b;
             int prev = 0;                                  // end of the blocks so far
+            int prev_s = 0;                                // start of the last block so far
+            bool bad = false;                              // blocks not ascending and disjoint
             int s_next = lane < nbk ? bl[lane] : lim;      // one round of loads ahead
             for (int base = 0; base < nbk && nhole <= kGrpHoles; base += 64) {
                 const int i = base + lane;
@@ -388,7 +390,12 @@ void attn_fwd_kernel(AttnArgs a) {
                 s_next = i + 64 < nbk ? bl[i + 64] : lim;
                 const int lo = min(max(s, 0), lim), hi = min(max(s + kBK, 0), lim);
                 int pe = __shfl_up(hi, 1, 64);
-                if (lane == 0) pe = prev;
+                int ps = __shfl_up(s, 1, 64);
+                if (lane == 0) {
+                    pe = prev;
+                    ps = prev_s;
+                }
+                bad |= i < nbk && i > 0 && (int64_t)s < (int64_t)ps + kBK;
                 const bool gap = i < nbk && lo > pe;
                 const uint64_t m = __builtin_amdgcn_ballot_w64(gap);
                 const int pos = nhole + __builtin_popcountll(m & ((1ull << lane) - 1));
@@ -398,7 +405,9 @@ void attn_fwd_kernel(AttnArgs a) {
                 }
                 nhole += __builtin_popcountll(m);
                 prev = __shfl(hi, min(nbk - base, 64) - 1, 64);
+                prev_s = __shfl(s, min(nbk - base, 64) - 1, 64);
             }
+            ok = __builtin_amdgcn_ballot_w64(bad) == 0;
             if (prev < lim) {
                 if (lane == 0 && nhole < kGrpHoles) {
                     hw[2 * nhole] = prev;
@@ -406,16 +415,24 @@ void attn_fwd_kernel(AttnArgs a) {
                 }
                 ++nhole;
             }
-            ok = nhole <= kGrpHoles;
+            ok = ok && nhole <= kGrpHoles;
             if (ok) {
+                // the walk below reads the columns in ascending order; a list
+                // in any other order runs per head instead
                 const int32_t *cl = a.column_index + item * a.cap_c;
-                for (int i = lane; i < ncl_g; i += 64) hw[2 * kGrpHoles + i] = cl[i];
+                bool unsorted = false;
+                for (int i = lane; i < ncl_g; i += 64) {
+                    const int c = cl[i];
+                    hw[2 * kGrpHoles + i] = c;
+                    unsorted |= i > 0 && c <= cl[i - 1];
+                }
+                ok = __builtin_amdgcn_ballot_w64(unsorted) == 0;
                 // uncovered keys: the holes less the columns (which all lie in holes)
                 int len = 0;
                 for (int j = lane; j < nhole; j += 64) len += hw[2 * j + 1] - hw[2 * j];
 #pragma unroll
                 for (int o = 32; o > 0; o >>= 1) len += __shfl_xor(len, o, 64);
-                ok = len - ncl_g <= lim / 8;
+                ok = ok && len - ncl_g <= lim / 8;
             }
         }
         const bool unit_ok = __syncthreads_and(ok) != 0;
@@ -773,11 +790,8 @@ template <typename T, bool kDense> hipError_t launch(AttnArgs a, hipStream_t s) 
         }
         // first the grouped walk over the units that qualify (it marks them),
         // then the key phases of the per-head kernel over the rest
-        const int64_t nqb = (a.n + kBQ - 1) / kBQ;
-        a.grp = reinterpret_cast<int32_t *>(reinterpret_cast<int2 *>(a.ws + (int64_t)a.hq * nqb * 2 * kStateFloats) +
-                                            (int64_t)a.hq * nqb);
-        const int G = a.hq / a.hkv;
-        a.grp_kh = G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1);
+        a.grp = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(a.ws) + sparse_walk_marks_offset(a.hq, a.n));
+        a.grp_kh = walk_heads_per_unit(a.hq, a.hkv);
         {
             const hipError_t e = a.grp_kh == 4   ? launch_h<T, true, 4, true>(a, s)
                                  : a.grp_kh == 2 ? launch_h<T, true, 2, true>(a, s)
@@ -797,6 +811,15 @@ template <typename T, bool kDense> hipError_t launch(AttnArgs a, hipStream_t s) 
 }
 
 }  // namespace
+
+size_t sparse_walk_marks_offset(int64_t hq, int64_t n) {
+    return (size_t)hq * (size_t)((n + kBQ - 1) / kBQ) * (2 * kStateFloats * sizeof(float) + sizeof(int2));
+}
+
+int walk_heads_per_unit(int hq, int hkv) {
+    const int G = hq / hkv;
+    return G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1);
+}
 
 size_t sparse_state_bytes(int64_t hq, int64_t n, int64_t phase_keys) {
     if (phase_keys <= 0 || phase_keys >= n) return 0;

@@ -15,8 +15,9 @@
 //           means in LDS, each thread 4 x 4 scores; written to the workspace
 //           as order-preserving integer keys.
 //   select: one workgroup per (q head, query block): its row of keys into
-//           LDS, 4 x 8-bit radix select for the k-th key (the bin found by a
-//           parallel scan), then an in-order compaction (ties -> lower c).
+//           LDS (rows past 15360 key blocks stay in the workspace), 4 x 8-bit
+//           radix select for the k-th key (the bin found by a parallel scan),
+//           then an in-order compaction (ties -> lower c).
 #include "common.h"
 #include "kernels.h"
 
@@ -25,6 +26,10 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kThreads = 256;
+// Keys of a query block's row held in LDS for its selection (60 KB, within
+// the 64 KB of dynamic LDS a launch gets by default); longer rows (query
+// blocks past 15360, i.e. keys past 983,040) are read from the workspace.
+constexpr int kBsLdsKeys = 15360;
 
 // One workgroup (128 threads) per (head, block): thread t adds up 8
 // consecutive dimensions (one 16-byte load for bf16, two for fp32) of rows
@@ -148,29 +153,12 @@ __device__ __forceinline__ uint32_t scan256(uint32_t v, uint32_t *tmp) {
     return r;
 }
 
-__global__ __launch_bounds__(kThreads) void bs_select_kernel(BsArgs a) {
-    extern __shared__ uint32_t keys[];              // [b + 1]
-    __shared__ uint32_t hist[256];
-    __shared__ uint32_t tmp[kThreads];
-    __shared__ uint32_t sel_state[2];
-    const int64_t nb = (a.n + 63) / 64;
-    const int64_t rows = min((int64_t)a.chunk_rows, nb - a.row0);
-    const int64_t b = a.row0 + rows - 1 - blockIdx.x;   // heavy rows first
-    const int h = blockIdx.y;
-    const int64_t item = (int64_t)h * nb + b;
-    int32_t *out = a.block_offset + item * a.cap_b;
-    const int ncand = (int)b + 1;
-    const int kk = min(a.topk, ncand);
-    if (threadIdx.x == 0) {
-        a.block_count[item] = kk;
-        a.column_count[item] = 0;
-    }
-    if (ncand <= a.topk) {
-        for (int c = threadIdx.x; c < ncand; c += kThreads) out[c] = c * 64;
-        return;
-    }
-    const uint32_t *krow = a.keys + ((int64_t)h * a.chunk_rows + (b - a.row0)) * nb;
-    for (int c = threadIdx.x; c < ncand; c += kThreads) keys[c] = krow[c];
+// Selection over one row of keys held at `keys`: the workgroup's LDS copy of
+// the row when it fits (kLds), else the row in the workspace itself (read
+// through the caches once per radix pass).
+template <bool kLds>
+__device__ __forceinline__ void select_row(const uint32_t *keys, int ncand, int kk, int32_t *out, int32_t cap_b,
+                                           uint32_t *hist, uint32_t *tmp, uint32_t *sel_state) {
     if (threadIdx.x == 0) { sel_state[0] = 0u; sel_state[1] = (uint32_t)kk; }
     __syncthreads();
     for (int pass = 0; pass < 4; ++pass) {
@@ -211,9 +199,39 @@ __global__ __launch_bounds__(kThreads) void bs_select_kernel(BsArgs a) {
         bool take = x > T;
         if (x == T) { take = seen < need_eq; ++seen; }
         if (take) {
-            if (pos < (uint32_t)a.cap_b) out[pos] = c * 64;
+            if (pos < (uint32_t)cap_b) out[pos] = c * 64;
             ++pos;
         }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void bs_select_kernel(BsArgs a) {
+    extern __shared__ uint32_t keys[];              // [min(b + 1, kBsLdsKeys)]
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t tmp[kThreads];
+    __shared__ uint32_t sel_state[2];
+    const int64_t nb = (a.n + 63) / 64;
+    const int64_t rows = min((int64_t)a.chunk_rows, nb - a.row0);
+    const int64_t b = a.row0 + rows - 1 - blockIdx.x;   // heavy rows first
+    const int h = blockIdx.y;
+    const int64_t item = (int64_t)h * nb + b;
+    int32_t *out = a.block_offset + item * a.cap_b;
+    const int ncand = (int)b + 1;
+    const int kk = min(a.topk, ncand);
+    if (threadIdx.x == 0) {
+        a.block_count[item] = kk;
+        a.column_count[item] = 0;
+    }
+    if (ncand <= a.topk) {
+        for (int c = threadIdx.x; c < ncand; c += kThreads) out[c] = c * 64;
+        return;
+    }
+    const uint32_t *krow = a.keys + ((int64_t)h * a.chunk_rows + (b - a.row0)) * nb;
+    if (ncand <= kBsLdsKeys) {
+        for (int c = threadIdx.x; c < ncand; c += kThreads) keys[c] = krow[c];
+        select_row<true>(keys, ncand, kk, out, a.cap_b, hist, tmp, sel_state);
+    } else {
+        select_row<false>(krow, ncand, kk, out, a.cap_b, hist, tmp, sel_state);
     }
 }
 
@@ -222,7 +240,7 @@ template <typename T> hipError_t launch_t(BsArgs a, hipStream_t s) {
     hipLaunchKernelGGL(bs_pool_kernel<T>, dim3((unsigned)nb, a.hq + a.hkv), dim3(kD), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t lds = (size_t)nb * sizeof(uint32_t);
+    const size_t lds = (size_t)min(nb, (int64_t)kBsLdsKeys) * sizeof(uint32_t);
     // query blocks in chunks of chunk_rows (a multiple of 64): scores of the
     // chunk into the workspace, then the selection of its rows
     for (int64_t r0 = 0; r0 < nb; r0 += a.chunk_rows) {

@@ -151,46 +151,70 @@ __device__ __forceinline__ const void *to_sgpr(const void *p) {   // p is wave-u
 // them on its own (it would otherwise wait for all of them before any LDS read
 // it cannot prove disjoint).  Completion is awaited with vm_wait<N>() (every
 // copy but the last N issued has landed), then a barrier.
+// M0 holds the LDS destination while a copy issues (the hardware reads it at
+// issue).  M0 is a reserved register the compiler may keep values in, so each
+// block saves it into a scratch SGPR first and puts it back before it ends:
+// the compiler sees M0 unchanged, as it assumes.
 // Uniform 64-bit base in SGPRs plus a per-lane 32-bit offset per copy:
 __device__ __forceinline__ void dma_x4(const void *sbase, uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3,
                                        uint32_t lds) {
+    uint32_t saved;
     asm volatile(
-        "s_mov_b32 m0, %5\n\t"
-        "global_load_lds_dwordx4 %0, %4\n\t"
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %6\n\t"
+        "global_load_lds_dwordx4 %1, %5\n\t"
         "s_add_u32 m0, m0, 0x400\n\t"
-        "global_load_lds_dwordx4 %1, %4\n\t"
+        "global_load_lds_dwordx4 %2, %5\n\t"
         "s_add_u32 m0, m0, 0x400\n\t"
-        "global_load_lds_dwordx4 %2, %4\n\t"
+        "global_load_lds_dwordx4 %3, %5\n\t"
         "s_add_u32 m0, m0, 0x400\n\t"
-        "global_load_lds_dwordx4 %3, %4" ::"v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(to_sgpr(sbase)), "s"(lds)
-        : "memory", "m0", "scc");
+        "global_load_lds_dwordx4 %4, %5\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(to_sgpr(sbase)), "s"(lds)
+        : "memory", "scc");
 }
 // One 1 KB copy (uniform base in SGPRs plus a per-lane offset):
 __device__ __forceinline__ void dma_x1(const void *sbase, uint32_t v0, uint32_t lds) {
+    uint32_t saved;
     asm volatile(
-        "s_mov_b32 m0, %2\n\t"
-        "global_load_lds_dwordx4 %0, %1" ::"v"(v0), "s"(to_sgpr(sbase)), "s"(lds)
-        : "memory", "m0");
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(v0), "s"(to_sgpr(sbase)), "s"(lds)
+        : "memory");
 }
 // One 1 KB copy from per-lane 64-bit addresses:
 __device__ __forceinline__ void dma_x1(const void *a0, uint32_t lds) {
+    uint32_t saved;
     asm volatile(
-        "s_mov_b32 m0, %1\n\t"
-        "global_load_lds_dwordx4 %0, off" ::"v"(a0), "s"(lds)
-        : "memory", "m0");
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(a0), "s"(lds)
+        : "memory");
 }
 // Per-lane 64-bit addresses:
 __device__ __forceinline__ void dma_x4(const void *a0, const void *a1, const void *a2, const void *a3, uint32_t lds) {
+    uint32_t saved;
     asm volatile(
-        "s_mov_b32 m0, %4\n\t"
-        "global_load_lds_dwordx4 %0, off\n\t"
-        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %5\n\t"
         "global_load_lds_dwordx4 %1, off\n\t"
         "s_add_u32 m0, m0, 0x400\n\t"
         "global_load_lds_dwordx4 %2, off\n\t"
         "s_add_u32 m0, m0, 0x400\n\t"
-        "global_load_lds_dwordx4 %3, off" ::"v"(a0), "v"(a1), "v"(a2), "v"(a3), "s"(lds)
-        : "memory", "m0", "scc");
+        "global_load_lds_dwordx4 %3, off\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "global_load_lds_dwordx4 %4, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "s"(lds)
+        : "memory", "scc");
 }
 
 // Number of XCDs on MI355X; consecutive workgroup ids are spread round-robin

@@ -36,6 +36,10 @@ struct AttnArgs {
 // Bytes of sparse-prefill state for hq heads and n keys in phases of
 // phase_keys keys (0 when one phase covers all keys).
 size_t sparse_state_bytes(int64_t hq, int64_t n, int64_t phase_keys);
+// Where the grouped walk's per-unit marks start in that workspace, and how
+// many q heads of a kv group one unit holds.
+size_t sparse_walk_marks_offset(int64_t hq, int64_t n);
+int walk_heads_per_unit(int hq, int hkv);
 
 // dtype: 0 = bf16, 1 = fp32
 hipError_t launch_sparse_prefill(const AttnArgs &a, int dtype, hipStream_t s);

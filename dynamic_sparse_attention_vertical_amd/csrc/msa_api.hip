@@ -110,8 +110,6 @@ template <typename T> T *at(void *ws, size_t off) {
     return reinterpret_cast<T *>(reinterpret_cast<char *>(ws) + off);
 }
 
-constexpr int64_t kBsMaxBlocks = 15360;   // LDS holds one score key per key block
-
 }  // namespace
 
 extern "C" {
@@ -320,6 +318,23 @@ int msa_sparse_prefill(const msa_problem *p, const void *q, const void *k, const
                          "sparse_prefill");
 }
 
+int msa_sparse_prefill_walk_marks(const msa_problem *p, int32_t phase_keys, size_t *offset,
+                                  int32_t *heads_per_unit) {
+    int st = check_problem(p);
+    if (st) return st;
+    if (!offset || !heads_per_unit) return fail(MSA_ERR_NULL, "outputs are NULL");
+    if (phase_keys < 0 || phase_keys % 64 != 0)
+        return fail(MSA_ERR_RANGE, "phase_keys %d is not a non-negative multiple of 64", phase_keys);
+    if (msa::sparse_state_bytes(p->n_q_heads, p->seq_len, phase_keys_of(phase_keys)) == 0) {
+        *offset = 0;
+        *heads_per_unit = 0;
+    } else {
+        *offset = msa::sparse_walk_marks_offset(p->n_q_heads, p->seq_len);
+        *heads_per_unit = msa::walk_heads_per_unit(p->n_q_heads, p->n_kv_heads);
+    }
+    return ok();
+}
+
 int msa_dense_prefill(const msa_problem *p, const void *q, const void *k, const void *v, void *out,
                       float *lse, void *stream) {
     msa::AttnArgs a;
@@ -357,9 +372,6 @@ int msa_estimate_bs(const msa_problem *p, const void *q, const void *k, int32_t 
     if (off_align(workspace, 16)) return fail(MSA_ERR_RANGE, "workspace is not 16-byte aligned");
     if (block != 64) return fail(MSA_ERR_RANGE, "block must be 64 (got %d)", block);
     const int64_t nb = (p->seq_len + 63) / 64;
-    if (nb > kBsMaxBlocks)
-        return fail(MSA_ERR_SHAPE, "block-sparse estimation supports at most %lld key blocks",
-                    (long long)kBsMaxBlocks);
     if (topk_blocks < 1) return fail(MSA_ERR_RANGE, "topk_blocks must be >= 1");
     const int64_t need = topk_blocks < nb ? topk_blocks : nb;
     if (cap_blocks < need) return fail(MSA_ERR_CAPACITY, "cap_blocks %d below %lld", cap_blocks, (long long)need);

@@ -49,6 +49,7 @@ _SIGS = {
     "msa_sparse_prefill": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32,
                                           _VP, ctypes.c_size_t, _VP, _VP, _VP]),
     "msa_sparse_prefill_workspace": (ctypes.c_size_t, [_VP, _I32]),
+    "msa_sparse_prefill_walk_marks": (ctypes.c_int, [_VP, _I32, _VP, _VP]),
     "msa_dense_prefill": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "msa_estimate_bs_workspace": (ctypes.c_size_t, [_VP, _I32]),
     "msa_estimate_bs": (ctypes.c_int, [_VP, _VP, _VP, _I32, _I32, _VP, _VP, _I32, _VP, _VP,
@@ -313,6 +314,24 @@ def sparse_prefill_workspace_bytes(n_q_heads: int, n_kv_heads: int, seq_len: int
     """Workspace bytes of sparse_prefill (0: one key phase, none needed)."""
     p = problem(n_q_heads, n_kv_heads, seq_len, MSA_BF16 if dtype == torch.bfloat16 else MSA_F32)
     return int(load().msa_sparse_prefill_workspace(ctypes.byref(p), phase_keys))
+
+
+def sparse_walk_marks(workspace: torch.Tensor, n_q_heads: int, n_kv_heads: int, seq_len: int,
+                      dtype=torch.bfloat16, phase_keys: int = 0) -> torch.Tensor | None:
+    """The grouped walk's marks from a sparse_prefill workspace, expanded to
+    one int32 per (q head, query block): 1 where the walk ran the block (all
+    aligned tiles 0..b, masked), else 0.  None when the call used no
+    workspace.  Reads the workspace as the last call on it left it."""
+    p = problem(n_q_heads, n_kv_heads, seq_len, MSA_BF16 if dtype == torch.bfloat16 else MSA_F32)
+    off, kh = ctypes.c_size_t(), ctypes.c_int32()
+    _check(load().msa_sparse_prefill_walk_marks(ctypes.byref(p), phase_keys, ctypes.byref(off),
+                                                 ctypes.byref(kh)), "msa_sparse_prefill_walk_marks")
+    if kh.value == 0:
+        return None
+    nqb = (seq_len + BLOCK - 1) // BLOCK
+    units = n_q_heads // kh.value
+    m = workspace[off.value: off.value + units * nqb * 4].view(torch.int32).reshape(units, nqb)
+    return m.repeat_interleave(kh.value, dim=0)
 
 
 @on_stream

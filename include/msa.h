@@ -155,6 +155,17 @@ int msa_build_index(const msa_problem *p, const int32_t *v_idx, int32_t vertical
  * A row with no allowed key gives out = 0 and lse = -inf.  Counts above the
  * capacities are clamped; keys outside [0, N) are ignored.
  *
+ * Preconditions on the lists of each query block (msa_build_index and
+ * msa_estimate_bs write lists that meet them):
+ *   - block starts ascending and pairwise disjoint: each start at least 64
+ *     past the one before;
+ *   - column keys distinct and outside every block of the same query block,
+ *     in any order.
+ * The sum above runs over the listed keys, so a key listed twice (a column
+ * inside a block, overlapping blocks, a repeated column) would be counted
+ * twice; such lists give unspecified (finite) results, never an access
+ * outside q, k, v, out, lse or the workspace.
+ *
  * Key phases.  With R = phase_keys (0 selects MSA_DEFAULT_PHASE_KEYS) below
  * seq_len, the work runs as ceil(N / R) launches in order on `stream`; launch
  * j takes the block tiles whose start lies in [jR, (j+1)R) (the first also
@@ -166,9 +177,10 @@ int msa_build_index(const msa_problem *p, const int32_t *v_idx, int32_t vertical
  * them, one launch takes the query blocks whose lists, for every q head of a
  * kv group (up to four heads), leave at most 1/8 of the keys [0, r1] out: it
  * walks all 64-key tiles 0..b once for those heads together and masks each
- * head to its own blocks and columns.  This path
- * needs every block list ascending, as msa_build_index and msa_estimate_bs
- * write them; the result is then the same up to fp32 rounding order.  With
+ * head to its own blocks and columns.  It takes a query block only if every
+ * such head's blocks are ascending and disjoint and its columns strictly
+ * ascending (others run per head); the result is the same up to fp32
+ * rounding order.  With
  * R >= seq_len there is one launch over the lists in their given order and no
  * workspace is used (it may be NULL).
  *   phase_keys: 0 or a positive multiple of 64, else MSA_ERR_RANGE.
@@ -190,7 +202,27 @@ int msa_sparse_prefill(const msa_problem *p, const void *q, const void *k, const
  *   n_q_heads * ceil(seq_len / 64) * (2 * (64 * 64 + 2 * 64) * 4 + 12). */
 size_t msa_sparse_prefill_workspace(const msa_problem *p, int32_t phase_keys);
 
-/* Dense causal attention (every j <= i), same layouts as msa_sparse_prefill. */
+/* Where msa_sparse_prefill records which query blocks the grouped walk took
+ * (a diagnostic: the walk executes every aligned tile 0..b of such a block for
+ * each of its heads, masked to the head's lists, so its executed tiles are
+ * not the listed ones).  After a msa_sparse_prefill call with the same
+ * problem and phase_keys, the int32 at byte
+ *     offset + 4 * ((h / heads_per_unit) * ceil(N/64) + b)
+ * of its workspace is 1 if query block b of q head h ran in the walk, else 0.
+ * heads_per_unit = 0 (and offset = 0) when the call uses no workspace (one
+ * phase), and then no block runs in the walk.  Errors as for
+ * msa_sparse_prefill_workspace's arguments. */
+int msa_sparse_prefill_walk_marks(const msa_problem *p, int32_t phase_keys, size_t *offset,
+                                  int32_t *heads_per_unit);
+
+/* Dense causal attention (every j <= i), same layouts as msa_sparse_prefill:
+ * out[h, i] = sum_{j <= i} softmax_j(sm_scale <q_i, k_j>) v_j, lse as above.
+ * This is the FlashAttention baseline the pages measure the sparse method
+ * against ("How to optimise the TTFT of an 8B LLM with 1M tokens to 20
+ * seconds", section on the speedup needed relative to FlashAttention; talk
+ * slides "System-Algorithm Co-design", slide "MInference": FlashAttn vs
+ * MInference latency at 1M tokens on one A100), computed here on the same
+ * GPU as the speedup denominator.  No workspace; errors as for every call. */
 int msa_dense_prefill(const msa_problem *p, const void *q, const void *k, const void *v,
                       void *out, float *lse, void *stream);
 
@@ -204,7 +236,9 @@ size_t msa_estimate_bs_workspace(const msa_problem *p, int32_t block);
  * rows), u[b, c] = sm_scale <qm[b], km[c]> for c <= b; query block b keeps its
  * min(topk_blocks, b+1) highest-scoring key blocks (exact ties to the lower
  * c), written as ascending key starts 64c.  column_count is set to 0.  block
- * must be 64; cap_blocks >= min(topk_blocks, ceil(N/64)).                   */
+ * must be 64; cap_blocks >= min(topk_blocks, ceil(N/64)).  Any seq_len below
+ * 2^31 is accepted (the workspace grows as n_q_heads * ceil(N/64) *
+ * min(ceil(N/64), 1024) * 4 bytes plus the pooled means).                   */
 int msa_estimate_bs(const msa_problem *p, const void *q, const void *k, int32_t block,
                     int32_t topk_blocks, int32_t *block_count, int32_t *block_offset,
                     int32_t cap_blocks, int32_t *column_count, void *workspace,

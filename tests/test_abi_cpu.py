@@ -30,7 +30,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -107,6 +107,14 @@ def test_estimate_bs_validation(lib):
     assert call(64, 0, 10, ws) == RANGE
     assert call(64, 10, 9, ws) == CAP
     assert call(64, 10, 10, ws - 1) == WS
+    # no length limit beyond seq_len < 2^31: at 1M tokens (16384 key blocks,
+    # more than one query-block chunk of 1024) the workspace follows the same
+    # formula and a call gets as far as the workspace check
+    big = P(hq=8, hkv=2, n=1 << 20)
+    nb = (1 << 20) // 64
+    wsb = lib.msa_estimate_bs_workspace(big, 64)
+    assert wsb == 8 * nb * 128 * 4 + 2 * nb * 128 * 4 + 8 * 1024 * nb * 4
+    assert lib.msa_estimate_bs(big, FAKE, FAKE, 64, 100, FAKE, FAKE, 100, FAKE, FAKE, wsb - 1, None) == WS
 
 
 def test_sparse_prefill_validation(lib):
@@ -123,6 +131,22 @@ def test_sparse_prefill_validation(lib):
     assert phased(1024, None, need) == NULL
     assert phased(1024, FAKE, need - 1) == WS
     assert phased(1024, ctypes.c_void_p(0x1004), need) == RANGE      # not 16-byte aligned
+
+
+def test_walk_marks_query(lib):
+    off, kh = ctypes.c_size_t(), ctypes.c_int32()
+    # one phase covers the sequence: no workspace, no walk
+    assert lib.msa_sparse_prefill_walk_marks(P(n=4096), 0, ctypes.byref(off), ctypes.byref(kh)) == OK
+    assert (off.value, kh.value) == (0, 0)
+    # phases: the marks follow the per-block states and records; GQA 4 -> units of 4 heads
+    n = 1 << 17
+    assert lib.msa_sparse_prefill_walk_marks(P(n=n), 0, ctypes.byref(off), ctypes.byref(kh)) == OK
+    assert kh.value == 4 and off.value == 32 * (n // 64) * (2 * (64 * 64 + 2 * 64) * 4 + 8)
+    assert off.value + 32 * (n // 64) * 4 <= lib.msa_sparse_prefill_workspace(P(n=n), 0)
+    assert lib.msa_sparse_prefill_walk_marks(P(hq=6, hkv=2, n=n), 0, ctypes.byref(off), ctypes.byref(kh)) == OK
+    assert kh.value == 1
+    assert lib.msa_sparse_prefill_walk_marks(P(n=n), 100, ctypes.byref(off), ctypes.byref(kh)) == RANGE
+    assert lib.msa_sparse_prefill_walk_marks(P(n=n), 0, None, ctypes.byref(kh)) == NULL
 
 
 def test_default_phase_keys_matches_header(lib):

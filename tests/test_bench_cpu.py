@@ -54,3 +54,18 @@ def test_band_workload_gathers_slashes():
     y = make_inputs(small_workload(seq_len=256, n_q_heads=1, n_kv_heads=1, n_planted=0, rope_base=1e30))
     z0 = (y["q"][0].double() @ y["k"][0].double().T).diagonal().mean()
     assert z > z0 + 100
+
+
+def test_listed_and_executed_tiles():
+    """Listed tiles count blocks and 64-column chunks; a query block the
+    grouped walk took counts all aligned tiles 0..b instead."""
+    import torch
+    from dynamic_sparse_attention_vertical_amd.msa import IndexTensors
+    bc = torch.tensor([[1, 2, 1], [0, 1, 3]], dtype=torch.int32)
+    cc = torch.tensor([[0, 65, 3], [1, 0, 64]], dtype=torch.int32)
+    idx = IndexTensors(bc, torch.zeros((2, 3, 3), dtype=torch.int32), cc, torch.zeros((2, 3, 65), dtype=torch.int32))
+    assert bench.listed_tiles(idx) == (1 + 2 + 1 + 0 + 1 + 3) + (0 + 2 + 1 + 1 + 0 + 1)
+    assert bench.executed_tiles(idx, None) == (bench.listed_tiles(idx), 0)
+    marks = torch.tensor([[0, 0, 1], [1, 0, 1]], dtype=torch.int32)
+    # walked: (h0, b2) -> 3 tiles, (h1, b0) -> 1, (h1, b2) -> 3; the rest as listed
+    assert bench.executed_tiles(idx, marks) == ((1) + (2 + 2) + 3 + 1 + (1 + 0) + 3, 3)

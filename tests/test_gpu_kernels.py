@@ -342,6 +342,34 @@ def test_explicit_softmax_scale(fp32):
     compare_lse(dlse.cpu().numpy(), drlse, "dense, sm_scale")
 
 
+def test_estimate_bs_long_rows():
+    """Block-sparse selection for query blocks past 15360 (rows of block
+    scores longer than the LDS copy the selection keeps): 10^6 tokens, so
+    15625 key blocks and a short last one.  Chosen blocks within the tie band
+    of the oracle's row softmax, on rows both below and past 15360."""
+    n, topk = 1_000_000, 100
+    w = small_workload(n_q_heads=2, n_kv_heads=1, seq_len=n, seed=99, n_planted=3)
+    x = make_inputs(w, device="cuda")
+    q, k = x["q"], x["k"]
+    idx = msa.estimate_bs(q, k, topk)
+    torch.cuda.synchronize()
+    nb = -(-n // 64)
+    rows = [0, 99, 100, 5000, 15359, 15360, 15361, 15500, nb - 2, nb - 1]
+    qc, kc = q.cpu(), k.cpu()
+    for h in range(2):
+        u = oracle.block_scores(qc, kc, h)
+        bc = idx.block_count[h].cpu().numpy()
+        bo = idx.block_offset[h].cpu().numpy()
+        assert np.all(idx.column_count[h].cpu().numpy() == 0)
+        for b in rows:
+            kk = min(topk, b + 1)
+            assert bc[b] == kk
+            row = u[b, : b + 1]
+            pr = np.exp(row - row.max())
+            check_band(bo[b, :kk] // 64, pr / pr.sum(), kk, f"head {h} block {b}")
+            assert np.all(bo[b, :kk] % 64 == 0)
+
+
 @pytest.mark.parametrize("hq,hkv,n,fp32", [(8, 2, 64 * 40 + 17, False), (4, 2, 64 * 24, False),
                                            (3, 3, 64 * 20 + 1, False), (4, 1, 64 * 16 + 33, True)])
 def test_sparse_grouped_walk(hq, hkv, n, fp32):
@@ -370,10 +398,84 @@ def test_sparse_grouped_walk(hq, hkv, n, fp32):
     gidx.column_count.copy_(torch.from_numpy(ridx.column_count))
     gidx.column_index.copy_(torch.from_numpy(ridx.column_index))
     qs, ks_, vs = cuda(q, k, v)
-    out, lse = msa.sparse_prefill(qs, ks_, vs, gidx, lse=True, phase_keys=512)
+    ws = walk_workspace(hq, hkv, n, qs.dtype)
+    out, lse = msa.sparse_prefill(qs, ks_, vs, gidx, lse=True, phase_keys=512, workspace=ws)
     ref, rlse = oracle.attention_with_mask(q, k, v, oracle.index_mask(ridx, n))
     compare_out(out.float().cpu().numpy(), ref, fp32, "grouped walk")
     compare_lse(lse.cpu().numpy(), rlse, "grouped walk")
     one, one_lse = msa.sparse_prefill(qs, ks_, vs, gidx, lse=True, phase_keys=-(-n // 64) * 64)
     compare_out(out.float().cpu().numpy(), one.float().cpu().numpy(), fp32, "grouped vs per-head")
     compare_lse(lse.cpu().numpy(), one_lse.cpu().numpy(), "grouped vs per-head")
+    # which units the walk took: the first query blocks (rows below 200, where
+    # every head keeps all diagonals up to its last row) for every kv group;
+    # never the last query block of the group holding the last head, whose
+    # diagonals stop at n - 400 and leave hundreds of keys out
+    marks = walk_marks(ws, hq, hkv, n)
+    assert np.all(marks[:, :3] == 1), marks[:, :3]
+    assert marks[-1, -1] == 0
+
+
+def walk_workspace(hq, hkv, n, dtype, phase_keys=512):
+    nbytes = msa.sparse_prefill_workspace_bytes(hq, hkv, n, dtype, phase_keys=phase_keys)
+    assert nbytes > 0
+    return torch.full((nbytes,), 0x7f, dtype=torch.uint8, device="cuda")
+
+
+def walk_marks(ws, hq, hkv, n):
+    """The grouped walk's marks, one per group of q heads sharing a unit and
+    query block (1: the unit ran as one aligned-tile walk)."""
+    torch.cuda.synchronize()
+    m = msa.sparse_walk_marks(ws, hq, hkv, n, phase_keys=512).cpu().numpy()
+    G = hq // hkv
+    kh = 4 if G % 4 == 0 else (2 if G % 2 == 0 else 1)
+    assert np.array_equal(m, np.repeat(m[::kh], kh, axis=0))      # one mark per unit
+    return m[::kh]
+
+
+@pytest.mark.parametrize("hq,hkv,fp32", [(4, 1, False), (4, 2, False), (4, 2, True)])
+def test_sparse_columns_in_any_order(hq, hkv, fp32):
+    """Column lists are sets: any order gives the same attention.  Per query
+    block b >= 1 every head lists the aligned tiles 0..b except one, plus 10
+    columns inside that tile; the even heads list them in descending order on
+    odd query blocks.  The grouped walk reads columns in ascending order, so it
+    must leave every unit holding such a list to the per-head kernel; it takes
+    the others whose uncovered keys (64 - 10) are at most 1/8 of [0, r1], i.e.
+    b = 0 and b >= 6."""
+    n = 64 * 24
+    nqb = n // 64
+    w, q, k, v = inputs(hq, hkv, n, seed=77 + hq + hkv, fp32=fp32)
+    rng = np.random.default_rng(5)
+    bc = np.zeros((hq, nqb), np.int32)
+    bo = np.full((hq, nqb, nqb), -1, np.int32)
+    cc = np.zeros((hq, nqb), np.int32)
+    ci = np.full((hq, nqb, 10), -1, np.int32)
+    for h in range(hq):
+        for b in range(nqb):
+            hole = (7 * b + h) % (b + 1) if b > 0 else -1
+            starts = [64 * t for t in range(b + 1) if t != hole]
+            bc[h, b] = len(starts)
+            bo[h, b, : len(starts)] = starts
+            if hole >= 0:
+                cols = np.sort(rng.choice(64, 10, replace=False)) + 64 * hole
+                if h % 2 == 0 and b % 2 == 1:
+                    cols = cols[::-1]
+                cc[h, b] = 10
+                ci[h, b] = cols
+    ridx = oracle.IndexArrays(bc, bo, cc, ci)
+    gidx = msa.alloc_index(hq, n, nqb, 10)
+    for name in ("block_count", "block_offset", "column_count", "column_index"):
+        getattr(gidx, name).copy_(torch.from_numpy(getattr(ridx, name)))
+    qs, ks_, vs = cuda(q, k, v)
+    ws = walk_workspace(hq, hkv, n, qs.dtype)
+    out, lse = msa.sparse_prefill(qs, ks_, vs, gidx, lse=True, phase_keys=512, workspace=ws)
+    ref, rlse = oracle.attention_with_mask(q, k, v, oracle.index_mask(ridx, n))
+    compare_out(out.float().cpu().numpy(), ref, fp32, "columns in any order")
+    compare_lse(lse.cpu().numpy(), rlse, "columns in any order")
+    marks = walk_marks(ws, hq, hkv, n)
+    b = np.arange(nqb)
+    want = ((b == 0) | (b >= 6)) & (b % 2 == 0)
+    np.testing.assert_array_equal(marks, np.broadcast_to(want.astype(np.int32), marks.shape))
+    # the same lists in one phase (no walk, no workspace) agree
+    one, one_lse = msa.sparse_prefill(qs, ks_, vs, gidx, lse=True, phase_keys=n)
+    compare_out(one.float().cpu().numpy(), ref, fp32, "columns in any order, one phase")
+    compare_lse(one_lse.cpu().numpy(), rlse, "columns in any order, one phase")

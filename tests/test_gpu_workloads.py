@@ -1,7 +1,18 @@
 """GPU parity at the named workloads' full sizes, in the launch
 configuration bench.py times (LayerPlan buffers, one call per step on the
-current stream).  The oracle checks sampled heads and query blocks one by
-one; index counts are checked for every head."""
+current stream).  What each workload checks against the oracle:
+
+  * index arrays (block and column counts, block starts, column keys) of
+    every q head, bit for bit, against oracle.build_index run on the GPU's
+    own top-k sets (head by head, compared on the GPU);
+  * estimator scores (element by element) and top-k sets (tie band) of
+    sampled heads: three at 128K, one per kv head at 512K and 1M;
+  * sparse attention outputs and lse on sampled query blocks (0, 1, the
+    last, and seeded random ones) of the sampled heads;
+  * dense attention on sampled query blocks, 1M included;
+  * mixed 256K: every A-shape and vertical-slash head's arrays exact, every
+    row of every block-sparse head within the tie band, attention sampled.
+"""
 
 import numpy as np
 import pytest
@@ -54,7 +65,9 @@ def check_vs_heads(x, w, plan, heads):
         log(f"  head {h}: scores and sets within tolerance")
 
 
-def check_index_heads(plan_idx, v_idx, s_idx, n, heads, full_arrays=True):
+def check_index_heads(plan_idx, v_idx, s_idx, n, heads):
+    """Index arrays of the sampled heads against the oracle (CPU compare);
+    returns the oracle's index of those heads."""
     vi = v_idx.cpu().numpy()
     si = s_idx.cpu().numpy()
     ridx = oracle.build_index(vi[heads], si[heads], n)
@@ -62,6 +75,35 @@ def check_index_heads(plan_idx, v_idx, s_idx, n, heads, full_arrays=True):
                            plan_idx.column_count[heads], plan_idx.column_index[heads])
     compare_index(sub, ridx, "index")
     return ridx
+
+
+def compare_head_arrays_gpu(gidx, h, ridx, r, what):
+    """Row r of an oracle index against head h of a GPU index, exactly, up
+    to each count (the compare runs on the GPU: a 1M head is 400 MB)."""
+    dev = gidx.block_count.device
+    rbc = torch.from_numpy(ridx.block_count[r]).to(dev)
+    rcc = torch.from_numpy(ridx.column_count[r]).to(dev)
+    assert torch.equal(gidx.block_count[h], rbc), f"{what}: block counts differ"
+    assert torch.equal(gidx.column_count[h], rcc), f"{what}: column counts differ"
+    for cnt, garr, rarr, name in ((rbc, gidx.block_offset[h], ridx.block_offset[r], "block starts"),
+                                  (rcc, gidx.column_index[h], ridx.column_index[r], "columns")):
+        wd = int(cnt.max().item()) if cnt.numel() else 0
+        if wd == 0:
+            continue
+        ref = torch.from_numpy(np.ascontiguousarray(rarr[:, :wd])).to(dev)
+        valid = torch.arange(wd, device=dev)[None, :] < cnt[:, None]
+        diff = (garr[:, :wd] != ref) & valid
+        assert not bool(diff.any()), f"{what}: {int(diff.sum())} {name} differ"
+
+
+def check_index_all_heads(plan_idx, v_idx, s_idx, n, what):
+    """Every head's arrays against oracle.build_index on that head's sets."""
+    vi = v_idx.cpu().numpy()
+    si = s_idx.cpu().numpy()
+    for h in range(vi.shape[0]):
+        ridx = oracle.build_index(vi[h:h + 1], si[h:h + 1], n)
+        compare_head_arrays_gpu(plan_idx, h, ridx, 0, f"{what} head {h}")
+    log(f"  {what}: index arrays of all {vi.shape[0]} heads exact")
 
 
 def check_attention(x, out, lse, idx_rows, items, what):
@@ -84,7 +126,11 @@ def check_dense(x, n, items):
     log(f"  dense: {len(items)} sampled query blocks within tolerance")
 
 
-def run_vs_workload(name, heads, n_blocks, dense=True):
+def run_vs_workload(name, heads, n_blocks, dense_blocks=6, attn_heads=None):
+    """The layer as bench.py runs it, then: estimator scores and sets of
+    `heads`; every head's index arrays; sparse attention on n_blocks sampled
+    query blocks of `attn_heads` (default: the first two of `heads`); dense
+    attention on dense_blocks of them for the first head."""
     w = WORKLOADS[name]
     n, hq = w.seq_len, w.n_q_heads
     log(f"[{name}] generating inputs")
@@ -97,17 +143,15 @@ def run_vs_workload(name, heads, n_blocks, dense=True):
     torch.cuda.synchronize()
     log(f"[{name}] layer done")
     check_vs_heads(x, w, plan, heads)
-    # counts: every head; arrays: sampled heads
-    bc = plan.index.block_count.cpu().numpy()
-    assert bc.min() >= 0 and bc.max() <= plan.index.cap_blocks
-    ridx = check_index_heads(plan.index, plan.v_idx, plan.s_idx, n, heads)
-    log(f"[{name}] index arrays of heads {heads} exact")
+    check_index_all_heads(plan.index, plan.v_idx, plan.s_idx, n, name)
+    attn_heads = heads[:2] if attn_heads is None else attn_heads
+    ridx = check_index_heads(plan.index, plan.v_idx, plan.s_idx, n, attn_heads)
     nqb = n // 64
     blocks = sample_blocks(nqb, n_blocks, seed=n)
-    items = [(h, b) for h in heads for b in blocks]
-    check_attention(x, out, lse, (ridx, {h: i for i, h in enumerate(heads)}), items, "sparse")
-    if dense:
-        check_dense(x, n, [(heads[0], b) for b in blocks[:6]])
+    items = [(h, b) for h in attn_heads for b in blocks]
+    check_attention(x, out, lse, (ridx, {h: i for i, h in enumerate(attn_heads)}), items, "sparse")
+    if dense_blocks:
+        check_dense(x, n, [(attn_heads[0], b) for b in blocks[:dense_blocks]])
     return plan
 
 
@@ -144,24 +188,25 @@ def test_single_head_4k_full_parity():
 
 
 def test_llama3_8b_128k():
-    plan = run_vs_workload("llama3_8b_128k", heads=[0, 13, 31], n_blocks=10)
-    # whole index arrays of every head at this size
-    ridx = oracle.build_index(plan.v_idx.cpu().numpy(), plan.s_idx.cpu().numpy(), 131072)
-    compare_index(plan.index, ridx, "index (all heads)")
+    run_vs_workload("llama3_8b_128k", heads=[0, 13, 31], n_blocks=10, attn_heads=[0, 13, 31])
+
+
+# one q head per kv head (G = 4), the first of each group but for two groups
+ONE_PER_KV = [0, 5, 10, 15, 16, 22, 26, 31]
 
 
 def test_llama3_8b_512k():
-    run_vs_workload("llama3_8b_512k", heads=[0, 22], n_blocks=8)
+    run_vs_workload("llama3_8b_512k", heads=ONE_PER_KV, n_blocks=8, attn_heads=[0, 22])
 
 
 def test_llama3_8b_1m():
-    run_vs_workload("llama3_8b_1m", heads=[5, 31], n_blocks=6, dense=False)
+    run_vs_workload("llama3_8b_1m", heads=ONE_PER_KV, n_blocks=6, attn_heads=[5, 31])
 
 
 def test_llama3_8b_1m_band():
     """The 1M layer with clustered slashes: long runs of adjacent diagonals, so
     the index is mostly long contiguous block runs plus the leftover columns."""
-    plan = run_vs_workload("llama3_8b_1m_band", heads=[2, 27], n_blocks=6, dense=False)
+    plan = run_vs_workload("llama3_8b_1m_band", heads=[2, 27], n_blocks=6, dense_blocks=0)
     # the clustering is what this workload is for: far fewer blocks than the
     # iid 1M layer's (about one per selected diagonal there)
     assert plan.index.block_count.float().mean().item() < 0.5 * 6096
@@ -180,15 +225,18 @@ def test_mixed_256k():
     log("[mixed_256k] layer done")
     nqb = n // 64
     a_heads, vs_heads, bs_heads = w.heads_with("a"), w.heads_with("vs"), w.heads_with("bs")
-    # A-shape heads: static index, exact
+    # A-shape heads: static index, exact, every head
     av, as_ = oracle.a_shape_sets(n, w.sink, w.window)
     ra = oracle.build_index(av[None], as_[None], n)
-    for h in (a_heads[0], a_heads[-1]):
-        compare_index(msa.IndexTensors(plan.index.block_count[h:h + 1], plan.index.block_offset[h:h + 1],
-                                       plan.index.column_count[h:h + 1], plan.index.column_index[h:h + 1]),
-                      ra, f"a-shape head {h}")
-    # vertical-slash heads: sets within the band, arrays exact
+    for h in a_heads:
+        compare_head_arrays_gpu(plan.index, h, ra, 0, f"a-shape head {h}")
+    # vertical-slash heads: arrays exact for every head (given its sets), sets
+    # within the band for two of them
     vs_rows = {h: i for i, h in enumerate(vs_heads)}
+    for h in vs_heads:
+        r = vs_rows[h]
+        ridx = oracle.build_index(plan.v_idx[r:r + 1].cpu().numpy(), plan.s_idx[r:r + 1].cpu().numpy(), n)
+        compare_head_arrays_gpu(plan.index, h, ridx, 0, f"vs head {h}")
     sample_vs = [vs_heads[0], vs_heads[-1]]
     for h in sample_vs:
         r = vs_rows[h]
@@ -197,22 +245,22 @@ def test_mixed_256k():
         rv, rs = oracle.estimate_vs(qfull, k[h // w.group: h // w.group + 1].cpu(), last_q=64)
         check_band(plan.v_idx[r].cpu().numpy(), rv[0], w.vertical_topk, f"vs head {h} v")
         check_band(plan.s_idx[r].cpu().numpy(), rs[0], w.slash_topk, f"vs head {h} s")
-        ridx = oracle.build_index(plan.v_idx[r:r + 1].cpu().numpy(), plan.s_idx[r:r + 1].cpu().numpy(), n)
-        compare_index(msa.IndexTensors(plan.index.block_count[h:h + 1], plan.index.block_offset[h:h + 1],
-                                       plan.index.column_count[h:h + 1], plan.index.column_index[h:h + 1]),
-                      ridx, f"vs head {h}")
-    # block-sparse heads: chosen blocks within the band of the row softmax of the block scores
-    for h in (bs_heads[0], bs_heads[-1]):
-        u = oracle.block_scores(q.cpu(), k.cpu(), h)
+    # block-sparse heads: every query block's chosen key blocks within the band
+    # of the row softmax of the oracle's block scores, every head
+    qc, kc = q.cpu(), k.cpu()
+    for h in bs_heads:
+        u = oracle.block_scores(qc, kc, h)
         bc = plan.index.block_count[h].cpu().numpy()
         bo = plan.index.block_offset[h].cpu().numpy()
         assert np.all(plan.index.column_count[h].cpu().numpy() == 0)
-        for b in sample_blocks(nqb, 40, seed=h):
+        for b in range(nqb):
             kk = min(w.bs_topk, b + 1)
             assert bc[b] == kk
             row = u[b, : b + 1]
             pr = np.exp(row - row.max())
             check_band(bo[b, :kk] // 64, pr / pr.sum(), kk, f"bs head {h} block {b}")
+            assert np.all(bo[b, :kk] % 64 == 0)
+        log(f"  bs head {h}: all {nqb} query blocks within the band")
     log("[mixed_256k] index checks passed")
     # attention on sampled blocks of every pattern, with the GPU's (validated) index
     heads = [a_heads[0], sample_vs[0], bs_heads[-1]]

@@ -206,6 +206,44 @@ def test_index_mask_contains_exact_union():
     assert np.all(~np.triu(np.ones((n, n), bool), 1)[None] | ~M)   # causal
 
 
+def brute_exact_union(v_idx, s_idx, n):
+    """M_x straight from the lists, one entry at a time: row i sees key j iff
+    j <= i and (j is a selected column or i - j a selected diagonal)."""
+    H = len(v_idx)
+    M = np.zeros((H, n, n), dtype=bool)
+    for h in range(H):
+        cols = set(int(x) for x in v_idx[h])
+        diags = set(int(x) for x in s_idx[h])
+        for i in range(n):
+            for j in range(i + 1):
+                M[h, i, j] = (j in cols) or ((i - j) in diags)
+    return M
+
+
+@pytest.mark.parametrize("n,kv,ks,seed", [(40, 3, 5, 1), (97, 7, 11, 2), (130, 1, 30, 3), (64, 20, 1, 4)])
+def test_exact_union_mask_brute_force(n, kv, ks, seed):
+    v_idx, s_idx = random_sets(3, n, kv, ks, seed=seed)
+    np.testing.assert_array_equal(oracle.exact_union_mask(v_idx, s_idx, n), brute_exact_union(v_idx, s_idx, n))
+
+
+def test_exact_union_mask_closed_forms():
+    """Each term alone, by its closed form: the main diagonal only is the
+    identity; one column c is the column below row c; diagonal o alone is the
+    sub-diagonal i - j = o; every diagonal is the causal mask."""
+    n = 50
+    none = np.zeros((1, 0), np.int32)
+    np.testing.assert_array_equal(oracle.exact_union_mask(none, np.array([[0]]), n)[0], np.eye(n, dtype=bool))
+    c = 17
+    want = np.zeros((n, n), bool)
+    want[c:, c] = True
+    np.testing.assert_array_equal(oracle.exact_union_mask(np.array([[c]]), none, n)[0], want)
+    o = 9
+    np.testing.assert_array_equal(oracle.exact_union_mask(none, np.array([[o]]), n)[0],
+                                  np.eye(n, k=-o, dtype=bool))
+    np.testing.assert_array_equal(oracle.exact_union_mask(none, np.arange(n)[None], n)[0],
+                                  np.tril(np.ones((n, n), bool)))
+
+
 def test_index_all_selected_is_causal():
     n = 320
     all_ = np.arange(n, dtype=np.int32)[None]
