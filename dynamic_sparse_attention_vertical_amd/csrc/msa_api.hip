@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "msa.h"
 #include "common.h"
 #include "kernels.h"
@@ -49,6 +51,9 @@ int check_problem(const msa_problem *p) {
                     (long long)p->seq_stride, (long long)p->seq_len);
     return MSA_OK;
 }
+
+// rows from one head's start to the next
+int64_t stride_of(const msa_problem *p) { return p->seq_stride ? p->seq_stride : p->seq_len; }
 
 float scale_of(const msa_problem *p) {
     return p->sm_scale > 0.f ? p->sm_scale : 1.0f / sqrtf((float)p->head_dim);
@@ -110,70 +115,31 @@ template <typename T> T *at(void *ws, size_t off) {
     return reinterpret_cast<T *>(reinterpret_cast<char *>(ws) + off);
 }
 
-}  // namespace
-
-extern "C" {
-
-const char *msa_status_str(int status) {
-    switch (status) {
-        case MSA_OK: return "MSA_OK";
-        case MSA_ERR_NULL: return "MSA_ERR_NULL";
-        case MSA_ERR_SHAPE: return "MSA_ERR_SHAPE";
-        case MSA_ERR_DTYPE: return "MSA_ERR_DTYPE";
-        case MSA_ERR_RANGE: return "MSA_ERR_RANGE";
-        case MSA_ERR_CAPACITY: return "MSA_ERR_CAPACITY";
-        case MSA_ERR_WORKSPACE: return "MSA_ERR_WORKSPACE";
-        case MSA_ERR_LAUNCH: return "MSA_ERR_LAUNCH";
-        default: return "MSA_ERR_UNKNOWN";
-    }
-}
-
-const char *msa_last_error(void) { return g_err; }
-
-int msa_index_caps(const msa_problem *p, int32_t vertical_topk, int32_t slash_topk, int32_t block,
-                   int32_t *cap_blocks, int32_t *cap_cols) {
+// Argument checks of msa_estimate_vs other than the workspace.
+int check_estimate_vs(const msa_problem *p, const void *q, const void *k, int32_t last_q, int32_t vertical_topk,
+                      int32_t slash_topk, const int32_t *v_idx, const int32_t *s_idx, const float *v_score,
+                      const float *s_score) {
     int st = check_problem(p);
     if (st) return st;
-    if (!cap_blocks || !cap_cols) return fail(MSA_ERR_NULL, "cap outputs are NULL");
-    if (block != 64) return fail(MSA_ERR_RANGE, "block must be 64 (got %d)", block);
-    if (vertical_topk < 0 || vertical_topk > p->seq_len || slash_topk < 0 || slash_topk > p->seq_len)
-        return fail(MSA_ERR_RANGE, "top-k values must lie in [0, seq_len]");
-    const int64_t nqb = (p->seq_len + 63) / 64;
-    *cap_blocks = (int32_t)(slash_topk < nqb ? slash_topk : nqb);
-    *cap_cols = vertical_topk;
-    return ok();
-}
-
-// rows from one head's start to the next
-static int64_t stride_of(const msa_problem *p) { return p->seq_stride ? p->seq_stride : p->seq_len; }
-
-size_t msa_estimate_vs_workspace(const msa_problem *p, int32_t last_q, int32_t vertical_topk,
-                                 int32_t slash_topk) {
-    (void)vertical_topk;
-    (void)slash_topk;
-    if (check_problem(p) != MSA_OK || last_q != 64) return 0;
-    return est_layout(p).total;
-}
-
-int msa_estimate_vs(const msa_problem *p, const void *q, const void *k, int32_t last_q,
-                    int32_t vertical_topk, int32_t slash_topk, int32_t *v_idx, int32_t *s_idx,
-                    float *v_score, float *s_score, void *workspace, size_t workspace_bytes,
-                    void *stream) {
-    int st = check_problem(p);
-    if (st) return st;
-    if (!q || !k || !v_idx || !s_idx || !workspace) return fail(MSA_ERR_NULL, "a required pointer is NULL");
+    if (!q || !k || !v_idx || !s_idx) return fail(MSA_ERR_NULL, "a required pointer is NULL");
     if ((st = check_rows(q, k, nullptr, nullptr))) return st;
     if (off_align(v_idx, 4) || off_align(s_idx, 4) || off_align(v_score, 4) || off_align(s_score, 4))
         return fail(MSA_ERR_RANGE, "index and score arrays must be 4-byte aligned");
-    if (off_align(workspace, 16)) return fail(MSA_ERR_RANGE, "workspace is not 16-byte aligned");
     if (last_q != 64) return fail(MSA_ERR_RANGE, "last_q must be 64 (got %d)", last_q);
     if (p->seq_len < 64)
         return fail(MSA_ERR_SHAPE, "seq_len must be at least last_q = 64 (got %lld)", (long long)p->seq_len);
     if (vertical_topk < 1 || vertical_topk > p->seq_len || slash_topk < 1 || slash_topk > p->seq_len)
         return fail(MSA_ERR_RANGE, "top-k values must lie in [1, seq_len]");
+    return MSA_OK;
+}
+
+// The estimate's launches on a checked problem and a workspace of at least
+// est_layout(p).total bytes.
+int run_estimate_vs(const msa_problem *p, const void *q, const void *k, int32_t vertical_topk, int32_t slash_topk,
+                    int32_t *v_idx, int32_t *s_idx, float *v_score, float *s_score, void *workspace,
+                    void *stream) {
     const EstLayout L = est_layout(p);
-    if (workspace_bytes < L.total)
-        return fail(MSA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, L.total);
+    int st;
     msa::EstArgs e;
     e.q = q;
     e.k = k;
@@ -211,6 +177,114 @@ int msa_estimate_vs(const msa_problem *p, const void *q, const void *k, int32_t 
     t.cnt = at<uint32_t>(workspace, L.off_cnt);
     t.off = at<uint32_t>(workspace, L.off_off);
     return launch_status(msa::launch_topk(t, s), "top-k");
+}
+
+// Scratch of msa_estimate_vs_noalloc: device memory of the library itself, one
+// copy per GPU, held until the process ends, so that the call allocates
+// nothing.  Host code reaches it only through the per-device address that
+// hipGetSymbolAddress returns (the array's own name is a host-side stand-in).
+constexpr size_t kNoAllocScratchBytes = size_t(80) << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+// This device's scratch address, looked up once per device (with the device
+// current) and kept.
+int scratch_of_current_device(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MSA_ERR_LAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(MSA_ERR_LAUNCH, "device %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        void *addr = nullptr;
+        e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || addr == nullptr)
+            return fail(MSA_ERR_LAUNCH, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch[dev] = addr;
+    }
+    *ptr = g_scratch[dev];
+    return MSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *msa_status_str(int status) {
+    switch (status) {
+        case MSA_OK: return "MSA_OK";
+        case MSA_ERR_NULL: return "MSA_ERR_NULL";
+        case MSA_ERR_SHAPE: return "MSA_ERR_SHAPE";
+        case MSA_ERR_DTYPE: return "MSA_ERR_DTYPE";
+        case MSA_ERR_RANGE: return "MSA_ERR_RANGE";
+        case MSA_ERR_CAPACITY: return "MSA_ERR_CAPACITY";
+        case MSA_ERR_WORKSPACE: return "MSA_ERR_WORKSPACE";
+        case MSA_ERR_LAUNCH: return "MSA_ERR_LAUNCH";
+        default: return "MSA_ERR_UNKNOWN";
+    }
+}
+
+const char *msa_last_error(void) { return g_err; }
+
+int msa_index_caps(const msa_problem *p, int32_t vertical_topk, int32_t slash_topk, int32_t block,
+                   int32_t *cap_blocks, int32_t *cap_cols) {
+    int st = check_problem(p);
+    if (st) return st;
+    if (!cap_blocks || !cap_cols) return fail(MSA_ERR_NULL, "cap outputs are NULL");
+    if (block != 64) return fail(MSA_ERR_RANGE, "block must be 64 (got %d)", block);
+    if (vertical_topk < 0 || vertical_topk > p->seq_len || slash_topk < 0 || slash_topk > p->seq_len)
+        return fail(MSA_ERR_RANGE, "top-k values must lie in [0, seq_len]");
+    const int64_t nqb = (p->seq_len + 63) / 64;
+    *cap_blocks = (int32_t)(slash_topk < nqb ? slash_topk : nqb);
+    *cap_cols = vertical_topk;
+    return ok();
+}
+
+
+size_t msa_estimate_vs_workspace(const msa_problem *p, int32_t last_q, int32_t vertical_topk,
+                                 int32_t slash_topk) {
+    (void)vertical_topk;
+    (void)slash_topk;
+    if (check_problem(p) != MSA_OK || last_q != 64) return 0;
+    return est_layout(p).total;
+}
+
+int msa_estimate_vs(const msa_problem *p, const void *q, const void *k, int32_t last_q,
+                    int32_t vertical_topk, int32_t slash_topk, int32_t *v_idx, int32_t *s_idx,
+                    float *v_score, float *s_score, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+    int st = check_estimate_vs(p, q, k, last_q, vertical_topk, slash_topk, v_idx, s_idx, v_score, s_score);
+    if (st) return st;
+    if (!workspace) return fail(MSA_ERR_NULL, "a required pointer is NULL");
+    if (off_align(workspace, 16)) return fail(MSA_ERR_RANGE, "workspace is not 16-byte aligned");
+    const size_t need = est_layout(p).total;
+    if (workspace_bytes < need)
+        return fail(MSA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    return run_estimate_vs(p, q, k, vertical_topk, slash_topk, v_idx, s_idx, v_score, s_score, workspace, stream);
+}
+
+int msa_estimate_vs_noalloc(const msa_problem *p, const void *q, const void *k, int32_t last_q,
+                            int32_t vertical_topk, int32_t slash_topk, int32_t *v_idx, int32_t *s_idx,
+                            float *v_score, float *s_score, void *stream) {
+    int st = check_estimate_vs(p, q, k, last_q, vertical_topk, slash_topk, v_idx, s_idx, v_score, s_score);
+    if (st) return st;
+    const size_t need = est_layout(p).total;
+    if (need > kNoAllocScratchBytes)
+        return fail(MSA_ERR_WORKSPACE,
+                    "msa_estimate_vs_noalloc: this problem needs %zu bytes of scratch, above the %zu bytes the "
+                    "library holds per GPU; split the heads over several calls or use msa_estimate_vs",
+                    need, kNoAllocScratchBytes);
+    void *ws = nullptr;
+    if ((st = scratch_of_current_device(&ws))) return st;
+    return run_estimate_vs(p, q, k, vertical_topk, slash_topk, v_idx, s_idx, v_score, s_score, ws, stream);
 }
 
 int msa_build_index(const msa_problem *p, const int32_t *v_idx, int32_t vertical_topk,

@@ -44,6 +44,7 @@ _SIGS = {
     "msa_estimate_vs_workspace": (ctypes.c_size_t, [_VP, _I32, _I32, _I32]),
     "msa_estimate_vs": (ctypes.c_int, [_VP, _VP, _VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP,
                                        ctypes.c_size_t, _VP]),
+    "msa_estimate_vs_noalloc": (ctypes.c_int, [_VP, _VP, _VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP]),
     "msa_build_index": (ctypes.c_int, [_VP, _VP, _I32, _VP, _I32, _I32, _VP, _VP, _I32, _VP, _VP,
                                        _I32, _VP]),
     "msa_sparse_prefill": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32,
@@ -265,6 +266,36 @@ def estimate_vs(q: torch.Tensor, k: torch.Tensor, vertical_topk: int, slash_topk
                                _dev(s_score, "s_score") if s_score is not None else None,
                                _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                                _stream(stream)), "msa_estimate_vs")
+    return v_idx, s_idx
+
+
+@on_stream
+def estimate_vs_noalloc(q: torch.Tensor, k: torch.Tensor, vertical_topk: int, slash_topk: int, *,
+                        last_q: int = LAST_Q, v_score: torch.Tensor | None = None,
+                        s_score: torch.Tensor | None = None, v_idx: torch.Tensor | None = None,
+                        s_idx: torch.Tensor | None = None, sm_scale: float = 0.0, stream=None):
+    """estimate_vs through msa_estimate_vs_noalloc: the library's own
+    per-GPU scratch instead of a workspace (the C call allocates nothing;
+    pass v_idx and s_idx to keep this wrapper from allocating them)."""
+    lib = load()
+    p = _problem_of(q, k, sm_scale)
+    hq, n = q.shape[0], q.shape[1]
+    if v_idx is None:
+        v_idx = torch.empty((hq, vertical_topk), dtype=torch.int32, device=q.device)
+    if s_idx is None:
+        s_idx = torch.empty((hq, slash_topk), dtype=torch.int32, device=q.device)
+    for t, name in ((v_score, "v_score"), (s_score, "s_score")):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (hq, n)):
+            raise MsaError(f"{name} must be float32 [{hq}, {n}]")
+    for t, name, kk in ((v_idx, "v_idx", vertical_topk), (s_idx, "s_idx", slash_topk)):
+        if t.dtype != torch.int32 or tuple(t.shape) != (hq, kk):
+            raise MsaError(f"{name} must be int32 [{hq}, {kk}]")
+    with torch.cuda.device(q.device):
+        _check(lib.msa_estimate_vs_noalloc(ctypes.byref(p), _in_dev(q, "q"), _in_dev(k, "k"), last_q,
+                                           vertical_topk, slash_topk, _dev(v_idx, "v_idx"), _dev(s_idx, "s_idx"),
+                                           _dev(v_score, "v_score") if v_score is not None else None,
+                                           _dev(s_score, "s_score") if s_score is not None else None,
+                                           _stream(stream)), "msa_estimate_vs_noalloc")
     return v_idx, s_idx
 
 

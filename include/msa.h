@@ -126,6 +126,22 @@ int msa_estimate_vs(const msa_problem *p, const void *q, const void *k, int32_t 
                     float *v_score, float *s_score, void *workspace, size_t workspace_bytes,
                     void *stream);
 
+/* msa_estimate_vs without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, results and errors as
+ * msa_estimate_vs, minus the workspace: its scratch is a fixed array of
+ * 80 MiB that the library holds on each GPU it runs on until the process
+ * ends (32 q heads up to 262,144 tokens; 8 q heads up to 1M).  A problem
+ * needing more (msa_estimate_vs_workspace) returns MSA_ERR_WORKSPACE;
+ * splitting the heads over several calls (head subsets, see above) fits it.
+ * The call works on the GPU current on the calling thread, which must be
+ * `stream`'s; it allocates and frees nothing.  Every call on one GPU shares
+ * that GPU's array (each call initialises what it reads): calls that overlap
+ * in time on one GPU, on any streams, race and give undefined results. */
+int msa_estimate_vs_noalloc(const msa_problem *p, const void *q, const void *k, int32_t last_q,
+                            int32_t vertical_topk, int32_t slash_topk, int32_t *v_idx, int32_t *s_idx,
+                            float *v_score, float *s_score, void *stream);
+
 /* Work lists from index sets (block = 64).  For query block b (rows r0 = 64b to
  * r1 = min(64b+63, N-1)), each selected offset o <= r1 needs keys [max(0, r0-o), r1-o];
  * visiting those ranges by descending o, a range not yet covered emits a

@@ -30,7 +30,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -93,6 +93,26 @@ def test_estimate_validation(lib):
     assert call(64, 0, 256, ws) == RANGE
     assert call(64, 64, 5000, ws) == RANGE
     assert call(64, 64, 256, ws - 1) == WS
+
+
+def test_estimate_noalloc_validation(lib):
+    """Checked on the host before any device call: the arguments as for
+    msa_estimate_vs, and the scratch the problem needs against the 80 MiB the
+    library holds per GPU."""
+    call = lambda prob, lq=64, kv=64, ks=256: lib.msa_estimate_vs_noalloc(prob, FAKE, FAKE, lq, kv, ks, FAKE, FAKE,
+                                                                           None, None, None)
+    assert call(P(n=4096), lq=32) == RANGE
+    assert call(P(n=4096), kv=0) == RANGE
+    assert call(P(n=40)) == SHAPE
+    assert lib.msa_estimate_vs_noalloc(P(n=4096), None, FAKE, 64, 64, 256, FAKE, FAKE, None, None, None) == NULL
+    # 32 q heads at 1M need ~260 MiB of scratch (the workspace size of msa_estimate_vs)
+    big = P(n=1 << 20)
+    assert lib.msa_estimate_vs_workspace(big, 64, 1000, 6096) > 80 << 20
+    assert call(big, kv=1000, ks=6096) == WS
+    assert b"80" in lib.msa_last_error() or b"83886080" in lib.msa_last_error()
+    # 8 q heads at 1M and 32 at 256K fit
+    assert lib.msa_estimate_vs_workspace(P(hq=8, hkv=2, n=1 << 20), 64, 1000, 6096) <= 80 << 20
+    assert lib.msa_estimate_vs_workspace(P(n=1 << 18), 64, 1000, 6096) <= 80 << 20
 
 
 def test_estimate_bs_validation(lib):
