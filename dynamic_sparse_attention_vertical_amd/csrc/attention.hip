@@ -291,6 +291,14 @@ __device__ __forceinline__ typename Elem<T>::frag v_frag(const AttnStage<T> &st,
 }
 
 
+// Per-lane choice under a wave-uniform 64-bit lane mask: lane l gets `b`
+// where bit l of `mask` is set, else `a` (one v_cndmask with an SGPR pair).
+__device__ __forceinline__ float lane_select(float a, float b, uint64_t mask) {
+    float r;
+    asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(mask));
+    return r;
+}
+
 // First index i in [0, cnt) with list[i] >= key (cnt if none) in an ascending
 // list.  The 64 lanes of the wave probe 64 evenly spaced entries per round and
 // the ballot of the comparisons narrows the range 64-fold, so a list of up to
@@ -636,12 +644,17 @@ void attn_fwd_kernel(AttnArgs a) {
             if constexpr (kGrp) {
                 const uint32_t al = (uint32_t)cs.allow;     // keys base .. base+31 of the chunk
                 if (al != ~0u) {
+                    // score jj*4+i is key jj*8+i in lanes 0-31 and key
+                    // jj*8+4+i in lanes 32-63: one select per score under a
+                    // 64-bit lane mask built from the two bits on the scalar unit
+                    const float ninf = -INFINITY;
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            const bool k0 = (al >> (jj * 8 + i)) & 1u, k1 = (al >> (jj * 8 + 4 + i)) & 1u;
-                            if (!(hl ? k1 : k0)) s[jj * 4 + i] = -INFINITY;
+                            const uint32_t lo = __builtin_amdgcn_readfirstlane(0u - ((al >> (jj * 8 + i)) & 1u));
+                            const uint32_t hi = __builtin_amdgcn_readfirstlane(0u - ((al >> (jj * 8 + 4 + i)) & 1u));
+                            s[jj * 4 + i] = lane_select(ninf, s[jj * 4 + i], ((uint64_t)hi << 32) | lo);
                         }
                 }
             }
