@@ -48,11 +48,15 @@ __device__ __forceinline__ i32x4 sload4(const int32_t *p) {          // p 16-byt
 }
 
 constexpr int kRing = 32;            // per-lane LDS ring of block starts (two 16-entry lines)
+// Lane rings lie kRing + 1 words apart: lanes writing the same ring position
+// then hit 64 different banks (a pitch of 32 words would put every lane of a
+// parity on one bank).
+constexpr int kRingPitch = kRing + 1;
 
 template <bool kStaged>
 __global__ __launch_bounds__(kThreads) void build_index_kernel(IndexArgs a) {
     __shared__ int32_t stage[kStaged ? kStageMax : 1];
-    __shared__ int32_t ring_all[kThreads * kRing];
+    __shared__ int32_t ring_all[kThreads * kRingPitch];
     const int h = blockIdx.y;
     const int nqb = (int)((a.n + 63) / 64);          // sequence lengths are below 2^31
     const int b = blockIdx.x * kThreads + threadIdx.x;
@@ -81,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void build_index_kernel(IndexArgs a) {
     // Block starts go to a per-lane LDS ring; a lane writes a completed,
     // 16-entry-aligned run of its list as one 64-byte line (four 16-byte
     // stores) instead of 16 scattered 4-byte stores.
-    int32_t *ring = ring_all + threadIdx.x * kRing;
+    int32_t *ring = ring_all + threadIdx.x * kRingPitch;
     const bool vec = a.vec_rows;                      // rows 16-byte aligned
     int flushed = 0;                                  // entries of blk already written
     auto flush_line = [&]() {                         // entries flushed .. flushed+15, all emitted
