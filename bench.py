@@ -199,6 +199,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--fused", action="store_true",
+                    help="time estimate + msa_sparse_prefill_fused (work lists walked inside the attention "
+                         "kernel) as the step instead of estimate + build_index + sparse_prefill")
     ap.add_argument("--copy-calib", type=float, default=0.0,
                     help="only run a plain copy of this many GiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -233,6 +236,14 @@ def main():
         plan = LayerPlan(hq, hkv, n, w.vertical_topk, w.slash_topk, "cuda", q.dtype)
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
+    fused = args.fused
+    if fused and mixed:
+        print("--fused applies to vertical-slash layers only", file=sys.stderr)
+        sys.exit(2)
+    fused_ws = None
+    if fused:
+        nbytes = msa.sparse_prefill_fused_workspace_bytes(hq, hkv, n, w.vertical_topk, q.dtype)
+        fused_ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
 
     def step(ev=None):
         if ev is not None:
@@ -247,10 +258,14 @@ def main():
                             s_idx=plan.s_idx, stream=stream)
             if ev is not None:
                 ev[1].record(stream)
-            msa.build_index(plan.v_idx, plan.s_idx, n, out=plan.index, stream=stream)
+            if not fused:
+                msa.build_index(plan.v_idx, plan.s_idx, n, out=plan.index, stream=stream)
             if ev is not None:
                 ev[2].record(stream)
-        msa.sparse_prefill(q, k, v, plan.index, out=out, workspace=plan.attn_workspace, stream=stream)
+        if fused:
+            msa.sparse_prefill_fused(q, k, v, plan.v_idx, plan.s_idx, out=out, workspace=fused_ws, stream=stream)
+        else:
+            msa.sparse_prefill(q, k, v, plan.index, out=out, workspace=plan.attn_workspace, stream=stream)
         if ev is not None:
             ev[3].record(stream)
 
@@ -273,12 +288,15 @@ def main():
     log(f"[bench] timed {args.steps} steps: {ms_step:.2f} ms/layer (estimate {ms_est:.3f}, index {ms_idx:.3f}, "
         f"sparse prefill {ms_att:.3f})")
 
+    if fused:       # the lists the fused kernel walked, built once (untimed) to count their tiles
+        msa.build_index(plan.v_idx, plan.s_idx, n, out=plan.index, stream=stream)
+        torch.cuda.synchronize()
     tiles = listed_tiles(plan.index)
     nqb = n // 64
     causal_tiles = hq * nqb * (nqb + 1) // 2
     listed_flop = tiles * TILE_FLOP
     marks = None
-    if plan.attn_workspace is not None:
+    if plan.attn_workspace is not None and not fused:
         marks = msa.sparse_walk_marks(plan.attn_workspace, hq, hkv, n, q.dtype)
     run_tiles, walk_blocks = executed_tiles(plan.index, marks)
     exec_flop = run_tiles * TILE_FLOP
@@ -297,11 +315,16 @@ def main():
         est_bytes = 2 * hkv * n * 128 * 2 + 2 * hq * n * 4
         idx_bytes = 4 * (int(plan.index.block_count.sum()) + int(plan.index.column_count.sum())) + 8 * hq * nqb
         est_gbs = est_bytes / (ms_est * 1e-3) / 1e9
-        idx_gbs = idx_bytes / (ms_idx * 1e-3) / 1e9
         breakdown = {
-            "ms_estimate": round(ms_est, 4), "ms_build_index": round(ms_idx, 4),
-            "estimate_gbs": round(est_gbs, 1), "estimate_hbm_frac": round(est_gbs / PEAK_HBM_GBS, 4),
-            "build_index_gbs": round(idx_gbs, 1), "build_index_hbm_frac": round(idx_gbs / PEAK_HBM_GBS, 4)}
+            "ms_estimate": round(ms_est, 4),
+            "estimate_gbs": round(est_gbs, 1), "estimate_hbm_frac": round(est_gbs / PEAK_HBM_GBS, 4)}
+        if fused:
+            breakdown["work_lists"] = ("walked inside the attention kernel (msa_sparse_prefill_fused); "
+                                       f"{idx_bytes / 1e9:.2f} GB of lists not written")
+        else:
+            idx_gbs = idx_bytes / (ms_idx * 1e-3) / 1e9
+            breakdown.update({"ms_build_index": round(ms_idx, 4), "build_index_gbs": round(idx_gbs, 1),
+                              "build_index_hbm_frac": round(idx_gbs / PEAK_HBM_GBS, 4)})
     breakdown.update({
         "ms_sparse_prefill": round(ms_att, 4),
         "listed_tiles": tiles, "executed_tiles": run_tiles, "causal_tiles": causal_tiles,
@@ -356,18 +379,19 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "seq_len": n, "q_heads": hq, "kv_heads": hkv, "head_dim": 128,
+        "config": {"workload": w.name, "step": "fused" if fused else "lists", "seq_len": n, "q_heads": hq, "kv_heads": hkv, "head_dim": 128,
                    "vertical_topk": w.vertical_topk, "slash_topk": w.slash_topk, "last_q": 64, "block": 64},
         "breakdown": breakdown,
         # the step's sparse prefill is one grouped-walk launch and n / phase_keys
         # key-phase launches (one kernel template, attention.hip): achieved =
         # the FLOPs of the tiles they executed over their summed time
         "roofline": {"bound": "mfma",
-                     "kernel": "attn_fwd_kernel<bf16> sparse: grouped walk + per-head key phases",
-                     "launches_per_step": phase_launches(n),
+                     "kernel": ("attn_fwd_kernel<bf16> fused: per-head key phases walking the cover" if fused
+                                else "attn_fwd_kernel<bf16> sparse: grouped walk + per-head key phases"),
+                     "launches_per_step": phase_launches(n) - (1 if fused and phase_launches(n) > 1 else 0),
                      "achieved": round(att_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(w.name),
+                     "traffic": None if fused else measured_traffic(w.name),
                      "traffic_source": ("rocprofv3 FETCH_SIZE + WRITE_SIZE of the same source, committed in "
                                         "profiles/attn_sparse_traffic.json (null when the kernel source "
                                         "has changed since)")},

@@ -68,6 +68,14 @@ constexpr int kMinPhaseTiles = 16;
 // the group then costs at most an eighth more matrix work than the lists.
 constexpr int kGrpHoles = 192;
 constexpr int kGrpCols = 64;
+// Fused mode (work lists built inside the kernel): the block starts of one
+// item and key phase, and the item's leftover columns, held in LDS.  Blocks
+// starting in one phase are disjoint and start inside its keys, so a phase of
+// at most kFusedMaxPhase keys has at most kFusedMaxPhase / 64 of them, plus
+// fewer than kMinPhaseTiles left over from earlier phases.
+constexpr int kFusedMaxPhase = 16384;
+constexpr int kFusedBlocks = kFusedMaxPhase / 64 + 32;
+constexpr int kFusedCols = 1024;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
@@ -345,7 +353,7 @@ __device__ __forceinline__ int lower_bound_near(const int32_t *list, int cnt, in
 // fp32 (a checking path) uses the same scheme with 64 KB of LDS.
 // kH q heads of one kv group per workgroup (2 kH waves) share every K/V copy;
 // used by the dense kernel, whose heads all walk the same tiles.
-template <typename T, bool kDense, int kH, bool kGrp = false>
+template <typename T, bool kDense, int kH, bool kGrp = false, bool kFused = false>
 __global__ __launch_bounds__(kThreads * kH) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1, sizeof(T) == 2 ? 2 : 1)))
 void attn_fwd_kernel(AttnArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the body uses gfx950-only LDS builtins
@@ -373,6 +381,37 @@ void attn_fwd_kernel(AttnArgs a) {
     const T *qp = reinterpret_cast<const T *>(a.q) + ((int64_t)h * a.stride) * kD;
     const T *kp = reinterpret_cast<const T *>(a.k) + ((int64_t)g * a.stride) * kD;
     const T *vp = reinterpret_cast<const T *>(a.v) + ((int64_t)g * a.stride) * kD;
+
+    // Q fragments (B operand of S^T = K Q^T): query qrow, d = dk*16 + hl*8 + e.
+    // The per-head sparse kernels load them before reading their work lists
+    // (and the softmax state as soon as they know it exists), so those
+    // latencies overlap; the dense and grouped kernels after qualifying.
+    frag qf[8];
+    auto load_q = [&]() {
+#pragma unroll
+        for (int dk = 0; dk < 8; ++dk)
+            qf[dk] = E::load_frag(qp + (int64_t)min(qrow, n32 - 1) * kD + dk * 16 + hl * 8);
+    };
+    f32x16 o[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+    // running row max kept in scaled log2 units as a stored fp32 value, so an
+    // unchanged max gives a rescale factor of exactly 1
+    float mb_i = -INFINITY, l_i = 0.f;
+    auto load_state = [&](const float *sw) {         // this wave's state: 16 float4 of O per lane, max, sum
+#pragma unroll
+        for (int v4 = 0; v4 < 16; ++v4) {
+            const float4 x = *reinterpret_cast<const float4 *>(sw + (v4 * 64 + lane) * 4);
+            o[v4 >> 2][(v4 & 3) * 4 + 0] = x.x;
+            o[v4 >> 2][(v4 & 3) * 4 + 1] = x.y;
+            o[v4 >> 2][(v4 & 3) * 4 + 2] = x.z;
+            o[v4 >> 2][(v4 & 3) * 4 + 3] = x.w;
+        }
+        mb_i = sw[4096 + lane];
+        l_i = sw[4096 + 64 + lane];
+    };
 
     // Grouped walk: each wave lists its head's holes (key ranges in [0, r1]
     // outside the head's blocks, ascending) and columns in LDS, and the unit
@@ -450,6 +489,11 @@ void attn_fwd_kernel(AttnArgs a) {
 
     int nblk, ncol;
     const int32_t *blist = nullptr, *clist = nullptr;
+    __shared__ int32_t fblk[kFused ? kFusedBlocks : 1];
+    __shared__ int32_t fcol[kFused ? kFusedCols : 1];
+    __shared__ int32_t fwalk[5];                     // fused walk: blocks, columns, offset index, cover end, column index
+    int fcov_next = 0, fcol_next = 0;
+    if constexpr (kFused) clist = fcol;
     // key phases (sparse, ws set): the first starts from an empty state, and
     // the query block's output is written in the phase holding its own rows
     // (no later key is visible to it); in between the state lives in ws
@@ -460,10 +504,224 @@ void attn_fwd_kernel(AttnArgs a) {
     if constexpr (kDense) {
         nblk = (int)b + 1;
         ncol = 0;
+    } else if constexpr (kFused) {
+        // Fused mode: this phase's blocks are the part of the greedy cover
+        // (the one msa_build_index writes) that starts before k_hi, walked
+        // here over the head's ascending diagonal offsets from where the
+        // previous phase stopped; its columns are the selected ones in
+        // [cover end before, cover end after) that its blocks leave out (the
+        // final phase: up to r1), so every uncovered column falls in exactly
+        // one phase.  Carried between phases: the offset index (record .y),
+        // the column index (record .x >> 1, next to the state flag in bit 0)
+        // and the cover end (fused_cov).
+        load_q();
+        const int64_t item = (int64_t)h * nqb + b;
+        const int32_t *S = a.s_idx + (int64_t)h * a.ks;
+        const int32_t *V = a.v_idx + (int64_t)h * a.kv;
+        const int r1 = min(r0 + kBQ - 1, n32 - 1);
+        first = a.ws == nullptr || a.k_lo == INT_MIN;
+        final_ = a.ws == nullptr || (int64_t)r0 + kBQ - 1 < (int64_t)a.k_hi;
+        const int k_hi = final_ ? INT_MAX : a.k_hi;
+        int i_in, cov_in = 0, ci_in = 0;
+        if (a.ws != nullptr) {
+            phase_rec = reinterpret_cast<int2 *>(a.ws + (int64_t)a.hq * nqb * 2 * kStateFloats) + item;
+            sw = a.ws + item * (2 * kStateFloats) + wave * kStateFloats;
+        }
+        if (first) {
+            i_in = lower_bound_wave(S, a.ks, r1 + 1, lane) - 1;       // offsets <= r1 are S[0 .. i_in]
+        } else {
+            const int2 rec = *phase_rec;
+            const int rx = __builtin_amdgcn_readfirstlane(rec.x);
+            have_state = (rx & 1) != 0;
+            if (have_state) load_state(sw);
+            ci_in = min(max(rx >> 1, 0), a.kv);
+            i_in = min(__builtin_amdgcn_readfirstlane(rec.y), a.ks - 1);
+            cov_in = max(__builtin_amdgcn_readfirstlane(load_uniform(a.fused_cov + item)), 0);
+        }
+        if (wave == 0) {                                // one wave walks, both read the lists after the barrier
+            // the first two windows of columns, loaded now so that they land during the walk
+            int cw = ci_in + lane < a.kv ? V[ci_in + lane] : INT_MAX;
+            int cw_n = ci_in + 64 + lane < a.kv ? V[ci_in + 64 + lane] : INT_MAX;
+            // Blocks, 64 offsets per step, one per lane in walk order (lane L:
+            // offset index i - L, so range starts a = r0 - o ascend over the
+            // lanes).  Ranges [a, a + d] that touch or overlap their
+            // predecessor form a run whose union is one interval [L, R]; the
+            // greedy cover tiles a run with consecutive blocks from its first
+            // uncovered key, so a run m emits ceil((len - e) / 64) blocks from
+            // L + e, e = max(s - g, 0), where g is the gap from the previous
+            // run's end and s that run's overhang past its end, s' = (e - len)
+            // mod 64 (len = R - L + 1).  The overhangs form a short chain,
+            // solved by iterating to the fixed point (exact after as many
+            // rounds as the longest chain of runs closer than 64 keys); a
+            // prefix sum places the blocks.  The offsets come through LDS
+            // (the tile stage is free until the pipeline starts), 1024 per
+            // memory round trip.
+            constexpr int kRound = 1024;
+            int32_t *stage = reinterpret_cast<int32_t *>(st.k);
+            const int d = r1 - r0;                      // a range covers keys [a, a + d]
+            int i = i_in, cov = cov_in, nb = 0;
+            int rhi = -1, rlo = 0;                      // staged: indices rlo .. rhi in slots rhi - index
+            while (i >= 0 && cov <= r1) {
+                if (i > rhi || (i - 63 < rlo && rlo > 0)) {
+                    rhi = i;
+                    rlo = max(i - (kRound - 1), 0);
+                    int v[kRound / 64];
+#pragma unroll
+                    for (int k = 0; k < kRound / 64; ++k) {
+                        const int idx = rhi - (k * 64 + lane);
+                        v[k] = idx >= rlo ? S[idx] : -1;
+                    }
+#pragma unroll
+                    for (int k = 0; k < kRound / 64; ++k) stage[k * 64 + lane] = v[k];
+                }
+                const int o = i - lane >= 0 ? stage[rhi - i + lane] : -1;
+                // offsets below 0 (and indices below 0) select nothing and end the walk
+                const uint64_t vmask = __builtin_amdgcn_ballot_w64(o >= 0);
+                const int nvalid = vmask == ~0ull ? 64 : __builtin_ctzll(~vmask);
+                const int a_ = r0 - o;
+                // ranges the cover already holds
+                const uint64_t cmask = __builtin_amdgcn_ballot_w64(lane < nvalid && a_ + d < cov);
+                const int nskip = cmask == ~0ull ? 64 : __builtin_ctzll(~cmask);
+                const bool live = lane >= nskip && lane < nvalid;
+                const int a_prev = __shfl_up(a_, 1, 64);
+                const bool head = live && (lane == nskip || a_ > a_prev + d + 1);
+                const uint64_t heads = __builtin_amdgcn_ballot_w64(head);
+                bool stopped = false;
+                if (heads != 0) {
+                    const uint64_t after = lane == 63 ? 0ull : heads & (~0ull << (lane + 1));
+                    const int next_h = after != 0 ? __builtin_ctzll(after) : nvalid;
+                    const int R = __shfl(a_, max(next_h - 1, 0), 64) + d;
+                    const int len = R - a_ + 1;
+                    const int g = lane == nskip ? a_ - cov : a_ - (a_prev + d) - 1;
+                    const uint64_t before = heads & ((1ull << lane) - 1);
+                    const int prev_h = before != 0 ? 63 - __builtin_clzll(before) : -1;
+                    int sv = (-len) & 63, e = 0;
+                    while (true) {
+                        const int sp_ = __shfl(sv, max(prev_h, 0), 64);
+                        e = max((prev_h >= 0 ? sp_ : 0) - g, 0);
+                        const int s_new = (e - len) & 63;
+                        const bool changed = __builtin_amdgcn_ballot_w64(head && s_new != sv) != 0;
+                        sv = s_new;
+                        if (!changed) break;
+                    }
+                    const int start = a_ + e;
+                    const int cnt = head && e < len ? (len - e + kBK - 1) / kBK : 0;
+                    int cnt2 = cnt;
+                    if (k_hi != INT_MAX)
+                        cnt2 = (int)min((int64_t)cnt, max((int64_t)0, ((int64_t)k_hi - start + kBK - 1) / kBK));
+                    const uint64_t cut = __builtin_amdgcn_ballot_w64(cnt2 < cnt);
+                    if (cut != 0) {                     // a later phase's block: this phase ends there
+                        stopped = true;
+                        if (lane > __builtin_ctzll(cut)) cnt2 = 0;
+                    }
+                    int incl = cnt2;                    // inclusive prefix sum over the lanes
+#pragma unroll
+                    for (int off = 1; off < 64; off <<= 1) {
+                        const int t = __shfl_up(incl, off, 64);
+                        if (lane >= off) incl += t;
+                    }
+                    const int pos = nb + incl - cnt2;
+                    for (int j = 0; j < cnt2 && pos + j < kFusedBlocks; ++j) fblk[pos + j] = start + kBK * j;
+                    nb += __shfl(incl, 63, 64);
+                    const uint64_t emitted = __builtin_amdgcn_ballot_w64(cnt2 > 0);
+                    if (emitted != 0) cov = __shfl(start + kBK * cnt2, 63 - __builtin_clzll(emitted), 64);
+                }
+                if (stopped) {                          // resume at the first range the cover does not hold
+                    const uint64_t unc = __builtin_amdgcn_ballot_w64(lane < nvalid && a_ + d >= cov);
+                    i -= unc != 0 ? __builtin_ctzll(unc) : nvalid;
+                    break;
+                }
+                i = nvalid < 64 ? -1 : i - 64;
+            }
+            if (cov > r1) i = -1;                       // every remaining range is covered
+            const int nbl = min(nb, kFusedBlocks);
+            // Columns, lane-parallel: this phase takes the selected columns in
+            // [cov_in, x_end) that none of its blocks covers (the blocks of
+            // earlier phases end by cov_in, those of later phases start at or
+            // past x_end); the final phase takes the rest up to r1.
+            const int x_end = final_ ? r1 + 1 : cov;
+            const uint64_t below = (1ull << lane) - 1;
+            int ci = ci_in, nc = 0;
+            if (final_ && a.fused_cols != nullptr && ci_in > 0) {
+                // the columns earlier phases took: set bits of the bitmap,
+                // all below ci_in, in index (so key) order
+                const uint32_t *bm = a.fused_cols + item * a.fused_cw;
+                const uint32_t word = lane < a.fused_cw ? bm[lane] : 0u;
+                int vwin = lane < ci_in ? V[lane] : INT_MAX;
+                for (int base = 0; base < ci_in; base += 64) {
+                    const int vnext = base + 64 + lane < ci_in ? V[base + 64 + lane] : INT_MAX;
+                    const uint32_t lo = __builtin_amdgcn_readlane(word, base >> 5);
+                    const uint32_t hi = (base >> 5) + 1 < a.fused_cw ? __builtin_amdgcn_readlane(word, (base >> 5) + 1) : 0u;
+                    const uint64_t bits = ((uint64_t)hi << 32 | lo);
+                    const bool take = base + lane < ci_in && ((bits >> lane) & 1) != 0;
+                    const uint64_t m = __builtin_amdgcn_ballot_w64(take);
+                    const int at = nc + __builtin_popcountll(m & below);
+                    if (take && at < kFusedCols) fcol[at] = vwin;
+                    nc += __builtin_popcountll(m);
+                    vwin = vnext;
+                }
+            }
+            int top_bit = 1;                            // the largest power of two <= nbl
+            while (top_bit * 2 <= nbl) top_bit *= 2;
+            while (true) {
+                const bool in = cw >= cov_in && cw < x_end;
+                if (__builtin_amdgcn_ballot_w64(in) != 0) {
+                    int pos = 0;                        // blocks starting at or before cw
+                    if (nbl > 0)
+                        for (int bit = top_bit; bit > 0; bit >>= 1)
+                            if (pos + bit <= nbl && fblk[pos + bit - 1] <= cw) pos += bit;
+                    const bool take = in && !(pos > 0 && cw < fblk[pos - 1] + kBK);
+                    const uint64_t m = __builtin_amdgcn_ballot_w64(take);
+                    const int at = nc + __builtin_popcountll(m & below);
+                    // the final phase lists the keys; an earlier one their
+                    // indices in v_idx, for the bitmap the final phase reads
+                    if (take && at < kFusedCols) fcol[at] = final_ ? cw : ci + lane;
+                    nc += __builtin_popcountll(m);
+                }
+                const uint64_t lower = __builtin_amdgcn_ballot_w64(cw < x_end);
+                if (lower != ~0ull) {                   // the first column at or past x_end is here
+                    ci += __builtin_popcountll(lower);
+                    break;
+                }
+                ci += 64;
+                cw = cw_n;
+                cw_n = ci + 64 + lane < a.kv ? V[ci + 64 + lane] : INT_MAX;
+            }
+            if (lane == 0) {
+                fwalk[0] = nbl;
+                fwalk[1] = min(nc, kFusedCols);
+                fwalk[2] = i;
+                fwalk[3] = cov;
+                fwalk[4] = ci;
+            }
+        }
+        __syncthreads();
+        nblk = __builtin_amdgcn_readfirstlane(fwalk[0]);
+        ncol = __builtin_amdgcn_readfirstlane(fwalk[1]);
+        b_next = __builtin_amdgcn_readfirstlane(fwalk[2]);
+        fcov_next = __builtin_amdgcn_readfirstlane(fwalk[3]);
+        fcol_next = __builtin_amdgcn_readfirstlane(fwalk[4]);
+        if (a.ws != nullptr && !final_ && nblk < kMinPhaseTiles) {
+            // too little here: leave it to the next phase, which starts from the same place
+            if (first && tid == 0) {
+                *phase_rec = make_int2(0, i_in);
+                a.fused_cov[item] = 0;
+            }
+            return;
+        }
+        if (!final_) {                                  // this phase's columns run in the final phase
+            if (wave == 0)
+                for (int t = lane; t < ncol; t += 64) {
+                    const int idx = fcol[t];
+                    atomicOr(a.fused_cols + item * a.fused_cw + (idx >> 5), 1u << (idx & 31));
+                }
+            ncol = 0;
+        }
     } else {
         if (a.grp != nullptr &&
             load_uniform(a.grp + (int64_t)(h / a.grp_kh) * nqb + b) != 0)   // done by the grouped walk
             return;
+        load_q();
         const int64_t item = (int64_t)h * nqb + b;
         nblk = min(max(a.block_count[item], 0), a.cap_b);
         ncol = min(max(a.column_count[item], 0), a.cap_c);
@@ -484,10 +742,13 @@ void attn_fwd_kernel(AttnArgs a) {
             // where its blocks start without a search
             phase_rec = reinterpret_cast<int2 *>(a.ws + (int64_t)a.hq * nqb * 2 * kStateFloats) + item;
             int2 rec = make_int2(0, 0);
+            sw = a.ws + item * (2 * kStateFloats) + wave * kStateFloats;
             if (!first) {
                 rec = *phase_rec;
                 rec.x = __builtin_amdgcn_readfirstlane(rec.x);
                 rec.y = __builtin_amdgcn_readfirstlane(rec.y);
+                have_state = rec.x != 0;
+                if (have_state) load_state(sw);
             }
             const int b0 = min(max(rec.y, 0), nblk);
             const int b1 = a.k_hi == INT_MAX ? nblk : b0 + lower_bound_near(blist + b0, nblk - b0, a.k_hi, lane);
@@ -495,8 +756,6 @@ void attn_fwd_kernel(AttnArgs a) {
             blist += b0;
             nblk = b1 - b0;
             if (!final_) ncol = 0;
-            sw = a.ws + item * (2 * kStateFloats) + wave * kStateFloats;
-            have_state = rec.x != 0;
             if (!final_ && nblk < kMinPhaseTiles) {     // too little here: leave it to the next phase
                 if (first && tid == 0) *phase_rec = make_int2(0, 0);
                 return;
@@ -520,7 +779,8 @@ void attn_fwd_kernel(AttnArgs a) {
     auto tile_of = [&](int t) {
         ChunkSrc s;
         s.is_col = t >= nblk;
-        s.base = s.is_col ? 0 : (kDense ? t * kBK : load_uniform(blist + t));
+        if constexpr (kFused) s.base = s.is_col ? 0 : __builtin_amdgcn_readfirstlane(fblk[t]);
+        else s.base = s.is_col ? 0 : (kDense ? t * kBK : load_uniform(blist + t));
         s.c0 = s.is_col ? (t - nblk) * kBK : 0;
         s.fast = !s.is_col && s.base >= 0 && s.base <= n32 - kBK;
         s.masked = !s.fast || s.base + kBK - 1 > r0;
@@ -570,31 +830,7 @@ void attn_fwd_kernel(AttnArgs a) {
         load_chunk<T, kH, true>(cl, lds_v, vp, s, c & 1, wave, n32, clist, ncol, st.kidx[c & 3]);
     };
 
-    // Q fragments (B operand of S^T = K Q^T): query qrow, d = dk*16 + hl*8 + e
-    frag qf[8];
-#pragma unroll
-    for (int dk = 0; dk < 8; ++dk) qf[dk] = E::load_frag(qp + (int64_t)min(qrow, n32 - 1) * kD + dk * 16 + hl * 8);
-
-    f32x16 o[4];
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
-    // running row max kept in scaled log2 units as a stored fp32 value, so an
-    // unchanged max gives a rescale factor of exactly 1
-    float mb_i = -INFINITY, l_i = 0.f;
-    if (have_state) {
-#pragma unroll
-        for (int v4 = 0; v4 < 16; ++v4) {
-            const float4 x = *reinterpret_cast<const float4 *>(sw + (v4 * 64 + lane) * 4);
-            o[v4 >> 2][(v4 & 3) * 4 + 0] = x.x;
-            o[v4 >> 2][(v4 & 3) * 4 + 1] = x.y;
-            o[v4 >> 2][(v4 & 3) * 4 + 2] = x.z;
-            o[v4 >> 2][(v4 & 3) * 4 + 3] = x.w;
-        }
-        mb_i = sw[4096 + lane];
-        l_i = sw[4096 + 64 + lane];
-    }
+    if constexpr (kDense) load_q();
     // Q has landed.  A compiler-visible wait: otherwise the compiler places its
     // waits for these loads inside the chunk loop, where they would also wait
     // for the K/V copies in flight.
@@ -752,7 +988,14 @@ void attn_fwd_kernel(AttnArgs a) {
                             o[v4 >> 2][(v4 & 3) * 4 + 2], o[v4 >> 2][(v4 & 3) * 4 + 3]);
         sw[4096 + lane] = mb_i;
         sw[4096 + 64 + lane] = l_i;
-        if (tid == 0) *phase_rec = make_int2(1, b_next);
+        if (tid == 0) {
+            if constexpr (kFused) {
+                *phase_rec = make_int2(1 | (fcol_next << 1), b_next);
+                a.fused_cov[(int64_t)h * nqb + b] = fcov_next;
+            } else {
+                *phase_rec = make_int2(1, b_next);
+            }
+        }
         return;
     }
     // finalise: lanes l and l^32 hold halves of the same row's sum
@@ -773,11 +1016,51 @@ void attn_fwd_kernel(AttnArgs a) {
 #endif
 }
 
-template <typename T, bool kDense, int kH, bool kGrp = false> hipError_t launch_h(const AttnArgs &a, hipStream_t s) {
+template <typename T, bool kDense, int kH, bool kGrp = false, bool kFused = false>
+hipError_t launch_h(const AttnArgs &a, hipStream_t s) {
     const int64_t total = (int64_t)(a.hq / kH) * ((a.n + kBQ - 1) / kBQ - (kDense ? 0 : a.qb_lo));
     if (total == 0) return hipSuccess;
-    hipLaunchKernelGGL((attn_fwd_kernel<T, kDense, kH, kGrp>), dim3((unsigned)total), dim3(kThreads * kH), 0, s, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, kDense, kH, kGrp, kFused>), dim3((unsigned)total), dim3(kThreads * kH), 0,
+                       s, a);
     return hipGetLastError();
+}
+
+__global__ void clear_words_kernel(uint32_t *p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+// Fused mode: no grouped walk (there are no lists to qualify), the key phases
+// of the per-head kernel each walking its part of the cover.
+template <typename T> hipError_t launch_fused(AttnArgs a, hipStream_t s) {
+    const int64_t R = a.phase_keys;
+    a.grp = nullptr;
+    if (a.ws == nullptr || R <= 0 || R >= a.n) {
+        a.ws = nullptr;
+        a.k_lo = INT_MIN;
+        a.k_hi = INT_MAX;
+        a.qb_lo = 0;
+        return launch_h<T, false, 1, false, true>(a, s);
+    }
+    a.fused_cov = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(a.ws) + sparse_walk_marks_offset(a.hq, a.n));
+    a.fused_cw = (a.kv + 31) / 32;
+    a.fused_cols = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(a.ws) + sparse_state_bytes(a.hq, a.n, R));
+    const int64_t words = (int64_t)a.hq * ((a.n + kBQ - 1) / kBQ) * a.fused_cw;
+    if (words > 0) {
+        const int64_t blocks = (words + 255) / 256 < 65536 ? (words + 255) / 256 : 65536;
+        hipLaunchKernelGGL(clear_words_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a.fused_cols, words);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int64_t np = (a.n + R - 1) / R;
+    for (int64_t j = 0; j < np; ++j) {
+        a.k_lo = j == 0 ? INT_MIN : (int32_t)(j * R);
+        a.k_hi = j == np - 1 ? INT_MAX : (int32_t)((j + 1) * R);
+        a.qb_lo = j * R / kBQ;
+        const hipError_t e = launch_h<T, false, 1, false, true>(a, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 // Sparse: one q head per workgroup (each head has its own work lists).  Dense:
@@ -839,9 +1122,22 @@ size_t sparse_state_bytes(int64_t hq, int64_t n, int64_t phase_keys) {
     return (size_t)hq * (size_t)((n + kBQ - 1) / kBQ) * (2 * kStateFloats * sizeof(float) + sizeof(int2) + sizeof(int32_t));
 }
 
+size_t fused_state_bytes(int64_t hq, int64_t n, int64_t phase_keys, int64_t kv) {
+    const size_t state = sparse_state_bytes(hq, n, phase_keys);
+    if (state == 0) return 0;
+    return state + (size_t)hq * (size_t)((n + kBQ - 1) / kBQ) * (size_t)((kv + 31) / 32) * sizeof(uint32_t);
+}
+
 hipError_t launch_sparse_prefill(const AttnArgs &a, int dtype, hipStream_t s) {
     return dtype == 0 ? launch<bf16, false>(a, s) : launch<float, false>(a, s);
 }
+
+hipError_t launch_sparse_prefill_fused(const AttnArgs &a, int dtype, hipStream_t s) {
+    return dtype == 0 ? launch_fused<bf16>(a, s) : launch_fused<float>(a, s);
+}
+
+int fused_max_phase_keys() { return kFusedMaxPhase; }
+int fused_max_columns() { return kFusedCols; }
 
 hipError_t launch_dense_prefill(const AttnArgs &a, int dtype, hipStream_t s) {
     return dtype == 0 ? launch<bf16, true>(a, s) : launch<float, true>(a, s);

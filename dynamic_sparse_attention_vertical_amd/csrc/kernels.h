@@ -31,6 +31,16 @@ struct AttnArgs {
     // per-head launches to skip (NULL: no such walk)
     int32_t *grp;
     int32_t grp_kh;
+    // fused mode: the index sets themselves instead of work lists, and the
+    // cover end each query block's walk has reached (in the workspace)
+    const int32_t *v_idx, *s_idx;
+    int32_t kv, ks;
+    int32_t *fused_cov;
+    // fused mode in key phases: per (q head, query block) a bitmap over
+    // v_idx of the columns that earlier phases passed and left uncovered,
+    // fused_cw 32-bit words each (all of them run in the final phase)
+    uint32_t *fused_cols;
+    int32_t fused_cw;
 };
 
 // Bytes of sparse-prefill state for hq heads and n keys in phases of
@@ -39,11 +49,18 @@ size_t sparse_state_bytes(int64_t hq, int64_t n, int64_t phase_keys);
 // Where the grouped walk's per-unit marks start in that workspace, and how
 // many q heads of a kv group one unit holds.
 size_t sparse_walk_marks_offset(int64_t hq, int64_t n);
+// Bytes of fused-mode workspace: that state, then (when phases are used) one
+// bitmap of kv bits, rounded up to 32-bit words, per (q head, query block).
+size_t fused_state_bytes(int64_t hq, int64_t n, int64_t phase_keys, int64_t kv);
 int walk_heads_per_unit(int hq, int hkv);
 
 // dtype: 0 = bf16, 1 = fp32
 hipError_t launch_sparse_prefill(const AttnArgs &a, int dtype, hipStream_t s);
 hipError_t launch_dense_prefill(const AttnArgs &a, int dtype, hipStream_t s);
+// Sparse prefill that walks the cover of s_idx / v_idx itself (no work lists).
+hipError_t launch_sparse_prefill_fused(const AttnArgs &a, int dtype, hipStream_t s);
+int fused_max_phase_keys();
+int fused_max_columns();
 
 struct EstArgs {
     const void *q, *k;

@@ -343,6 +343,11 @@ static int attn_common(const msa_problem *p, const void *q, const void *k, const
     a.ws = nullptr;
     a.grp = nullptr;
     a.grp_kh = 1;
+    a.v_idx = a.s_idx = nullptr;
+    a.kv = a.ks = 0;
+    a.fused_cov = nullptr;
+    a.fused_cols = nullptr;
+    a.fused_cw = 0;
     return MSA_OK;
 }
 
@@ -390,6 +395,55 @@ int msa_sparse_prefill(const msa_problem *p, const void *q, const void *k, const
     }
     return launch_status(msa::launch_sparse_prefill(a, p->dtype, reinterpret_cast<hipStream_t>(stream)),
                          "sparse_prefill");
+}
+
+size_t msa_sparse_prefill_fused_workspace(const msa_problem *p, int32_t vertical_topk, int32_t phase_keys) {
+    if (check_problem(p) != MSA_OK || phase_keys < 0 || phase_keys % 64 != 0 || vertical_topk < 0 ||
+        vertical_topk > msa::fused_max_columns())
+        return 0;
+    return msa::fused_state_bytes(p->n_q_heads, p->seq_len, phase_keys_of(phase_keys), vertical_topk);
+}
+
+int msa_sparse_prefill_fused(const msa_problem *p, const void *q, const void *k, const void *v,
+                             const int32_t *v_idx, int32_t vertical_topk, const int32_t *s_idx, int32_t slash_topk,
+                             int32_t phase_keys, void *workspace, size_t workspace_bytes, void *out, float *lse,
+                             void *stream) {
+    msa::AttnArgs a;
+    int st = attn_common(p, q, k, v, out, a);
+    if (st) return st;
+    if ((vertical_topk > 0 && !v_idx) || (slash_topk > 0 && !s_idx))
+        return fail(MSA_ERR_NULL, "an index set pointer is NULL");
+    if (vertical_topk < 0 || slash_topk < 0 || vertical_topk > p->seq_len || slash_topk > p->seq_len)
+        return fail(MSA_ERR_RANGE, "top-k values must lie in [0, seq_len]");
+    if (vertical_topk > msa::fused_max_columns())
+        return fail(MSA_ERR_RANGE, "the fused mode holds at most %d columns per head (got %d)",
+                    msa::fused_max_columns(), vertical_topk);
+    if (off_align(v_idx, 4) || off_align(s_idx, 4) || off_align(lse, 4))
+        return fail(MSA_ERR_RANGE, "index sets and lse must be 4-byte aligned");
+    if (phase_keys < 0 || phase_keys % 64 != 0)
+        return fail(MSA_ERR_RANGE, "phase_keys %d is not a non-negative multiple of 64", phase_keys);
+    a.phase_keys = (int32_t)phase_keys_of(phase_keys);
+    if (a.phase_keys > msa::fused_max_phase_keys())
+        return fail(MSA_ERR_RANGE, "the fused mode takes phases of at most %d keys (got %d)",
+                    msa::fused_max_phase_keys(), a.phase_keys);
+    a.block_count = a.block_offset = a.column_count = a.column_index = nullptr;
+    a.cap_b = a.cap_c = 0;
+    a.lse = lse;
+    a.v_idx = v_idx;
+    a.s_idx = s_idx;
+    a.kv = vertical_topk;
+    a.ks = slash_topk;
+    const size_t need = msa::fused_state_bytes(p->n_q_heads, p->seq_len, a.phase_keys, vertical_topk);
+    if (need > 0) {
+        if (!workspace) return fail(MSA_ERR_NULL, "workspace is NULL (%zu bytes needed)", need);
+        if (workspace_bytes < need)
+            return fail(MSA_ERR_WORKSPACE, "workspace %zu bytes, %zu needed", workspace_bytes, need);
+        if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+            return fail(MSA_ERR_RANGE, "workspace is not 16-byte aligned");
+        a.ws = static_cast<float *>(workspace);
+    }
+    return launch_status(msa::launch_sparse_prefill_fused(a, p->dtype, reinterpret_cast<hipStream_t>(stream)),
+                         "sparse_prefill_fused");
 }
 
 int msa_sparse_prefill_walk_marks(const msa_problem *p, int32_t phase_keys, size_t *offset,

@@ -50,7 +50,10 @@ _SIGS = {
     "msa_sparse_prefill": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32,
                                           _VP, ctypes.c_size_t, _VP, _VP, _VP]),
     "msa_sparse_prefill_workspace": (ctypes.c_size_t, [_VP, _I32]),
+    "msa_sparse_prefill_fused_workspace": (ctypes.c_size_t, [_VP, _I32, _I32]),
     "msa_sparse_prefill_walk_marks": (ctypes.c_int, [_VP, _I32, _VP, _VP]),
+    "msa_sparse_prefill_fused": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I32, _VP, _I32, _I32, _VP,
+                                                ctypes.c_size_t, _VP, _VP, _VP]),
     "msa_dense_prefill": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "msa_estimate_bs_workspace": (ctypes.c_size_t, [_VP, _I32]),
     "msa_estimate_bs": (ctypes.c_int, [_VP, _VP, _VP, _I32, _I32, _VP, _VP, _I32, _VP, _VP,
@@ -347,6 +350,13 @@ def sparse_prefill_workspace_bytes(n_q_heads: int, n_kv_heads: int, seq_len: int
     return int(load().msa_sparse_prefill_workspace(ctypes.byref(p), phase_keys))
 
 
+def sparse_prefill_fused_workspace_bytes(n_q_heads: int, n_kv_heads: int, seq_len: int, vertical_topk: int,
+                                         dtype=torch.bfloat16, phase_keys: int = 0) -> int:
+    """Workspace bytes of sparse_prefill_fused (0: one key phase, none needed)."""
+    p = problem(n_q_heads, n_kv_heads, seq_len, MSA_BF16 if dtype == torch.bfloat16 else MSA_F32)
+    return int(load().msa_sparse_prefill_fused_workspace(ctypes.byref(p), vertical_topk, phase_keys))
+
+
 def sparse_walk_marks(workspace: torch.Tensor, n_q_heads: int, n_kv_heads: int, seq_len: int,
                       dtype=torch.bfloat16, phase_keys: int = 0) -> torch.Tensor | None:
     """The grouped walk's marks from a sparse_prefill workspace, expanded to
@@ -395,6 +405,44 @@ def sparse_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: Ind
                                   _rows_dev(out, "out", p, q), _rows_dev(lse, "lse", p, q, True) if want_lse else None,
                                   _stream(stream)),
            "msa_sparse_prefill")
+    return (out, lse) if want_lse else out
+
+
+@on_stream
+def sparse_prefill_fused(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, v_idx: torch.Tensor,
+                         s_idx: torch.Tensor, *, out: torch.Tensor | None = None,
+                         lse: torch.Tensor | bool | None = None, sm_scale: float = 0.0, phase_keys: int = 0,
+                         workspace: torch.Tensor | None = None, stream=None):
+    """Causal attention over the greedy block cover of s_idx plus the leftover
+    columns of v_idx, the work lists walked inside the kernel (no index
+    arrays).  The same tiles in the same order as sparse_prefill(q, k, v,
+    build_index(v_idx, s_idx, seq_len)) without its grouped walk; workspace:
+    sparse_prefill_fused_workspace_bytes(...) bytes, allocated here when None
+    and needed."""
+    lib = load()
+    p = _problem_of(q, k, sm_scale, v)
+    hq, n = q.shape[0], q.shape[1]
+    for t, name in ((v_idx, "v_idx"), (s_idx, "s_idx")):
+        if t.dtype != torch.int32 or t.dim() != 2 or t.shape[0] != hq:
+            raise MsaError(f"{name} must be int32 [{hq}, k]")
+    if out is None:
+        out = _out_like(q, p)
+    want_lse = lse is not None and lse is not False
+    if lse is True:
+        lse = _lse_like(q, p)
+    kv, ks = v_idx.shape[1], s_idx.shape[1]
+    need = int(lib.msa_sparse_prefill_fused_workspace(ctypes.byref(p), kv, phase_keys))
+    ws_ptr, ws_bytes = None, 0
+    if need > 0:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    _check(lib.msa_sparse_prefill_fused(ctypes.byref(p), _in_dev(q, "q"), _in_dev(k, "k"), _in_dev(v, "v"),
+                                        _dev(v_idx, "v_idx") if kv else None, kv,
+                                        _dev(s_idx, "s_idx") if ks else None, ks, phase_keys, ws_ptr, ws_bytes,
+                                        _rows_dev(out, "out", p, q),
+                                        _rows_dev(lse, "lse", p, q, True) if want_lse else None, _stream(stream)),
+           "msa_sparse_prefill_fused")
     return (out, lse) if want_lse else out
 
 

@@ -218,6 +218,37 @@ int msa_sparse_prefill(const msa_problem *p, const void *q, const void *k, const
  *   n_q_heads * ceil(seq_len / 64) * (2 * (64 * 64 + 2 * 64) * 4 + 12). */
 size_t msa_sparse_prefill_workspace(const msa_problem *p, int32_t phase_keys);
 
+/* msa_build_index followed by msa_sparse_prefill in one call that builds no
+ * work lists: each query block's 64-wide key blocks are the same greedy cover
+ * of its selected diagonals (msa_build_index above), walked inside the
+ * attention kernel over the sorted s_idx, one key phase at a time, and its
+ * leftover columns are found from v_idx in the phases that pass them; no
+ * block_offset / column_index arrays exist (12.8 + 2.1 GB at 1M tokens and 32
+ * heads).  The pages ask for an index built online at minimal overhead ("How
+ * to optimise the TTFT of an 8B LLM with 1M tokens to 20 seconds", section on
+ * co-designing algorithm and system, principle 2).  Same attention and key
+ * phases as msa_sparse_prefill over msa_build_index's lists, the same tiles
+ * in the same order (blocks per phase, every column in the query block's
+ * final phase), but without the grouped walk, so where that walk runs the
+ * results agree up to fp32 rounding order and elsewhere bit for bit.  Same
+ * errors, and:
+ *   v_idx [n_q_heads, vertical_topk], s_idx [n_q_heads, slash_topk] int32,
+ *     ascending and distinct, as msa_estimate_vs writes them; entries outside
+ *     [0, N) select nothing (other orders give unspecified but finite
+ *     results, never an access out of bounds);
+ *   vertical_topk <= 1024 and phase keys (phase_keys, 0 = the default) at most
+ *     16384, else MSA_ERR_RANGE (the kernel holds a block's columns and a
+ *     phase's block starts in LDS);
+ *   workspace: msa_sparse_prefill_fused_workspace(p, vertical_topk,
+ *     phase_keys) bytes, 16-byte aligned (the key-phase state of
+ *     msa_sparse_prefill_workspace, then one bitmap of vertical_topk bits per
+ *     q head and query block); no initial contents assumed.               */
+size_t msa_sparse_prefill_fused_workspace(const msa_problem *p, int32_t vertical_topk, int32_t phase_keys);
+int msa_sparse_prefill_fused(const msa_problem *p, const void *q, const void *k, const void *v,
+                             const int32_t *v_idx, int32_t vertical_topk, const int32_t *s_idx, int32_t slash_topk,
+                             int32_t phase_keys, void *workspace, size_t workspace_bytes, void *out, float *lse,
+                             void *stream);
+
 /* Where msa_sparse_prefill records which query blocks the grouped walk took
  * (a diagnostic: the walk executes every aligned tile 0..b of such a block for
  * each of its heads, masked to the head's lists, so its executed tiles are

@@ -30,7 +30,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -151,6 +151,41 @@ def test_sparse_prefill_validation(lib):
     assert phased(1024, None, need) == NULL
     assert phased(1024, FAKE, need - 1) == WS
     assert phased(1024, ctypes.c_void_p(0x1004), need) == RANGE      # not 16-byte aligned
+
+
+def test_sparse_prefill_fused_validation(lib):
+    call = lambda prob, vi, kv, si, ks, pk=0, ws=None, wsb=0, lse=None: lib.msa_sparse_prefill_fused(
+        prob, FAKE, FAKE, FAKE, vi, kv, si, ks, pk, ws, wsb, FAKE, lse, None)
+    assert call(P(), None, 4, FAKE, 4) == NULL
+    assert call(P(), FAKE, 4, None, 4) == NULL
+    assert call(P(), FAKE, -1, FAKE, 4) == RANGE
+    assert call(P(), FAKE, 4, FAKE, 4097) == RANGE                  # more than seq_len
+    assert call(P(), FAKE, 1025, FAKE, 4) == RANGE                  # the kernel holds 1024 columns
+    assert call(P(), ctypes.c_void_p(0x1002), 4, FAKE, 4) == RANGE  # not 4-byte aligned
+    assert call(P(), FAKE, 4, FAKE, 4, pk=100) == RANGE
+    assert call(P(n=1 << 17), FAKE, 4, FAKE, 4, pk=32768) == RANGE  # phases of at most 16384 keys
+    n = 1 << 15
+    need = lib.msa_sparse_prefill_fused_workspace(P(n=n), 4, 0)
+    assert need > 0
+    assert call(P(n=n), FAKE, 4, FAKE, 4, ws=None, wsb=need) == NULL
+    assert call(P(n=n), FAKE, 4, FAKE, 4, ws=FAKE, wsb=need - 1) == WS
+    assert call(P(n=n), FAKE, 4, FAKE, 4, ws=ctypes.c_void_p(0x1004), wsb=need) == RANGE
+    assert call(P(d=64), FAKE, 4, FAKE, 4) == SHAPE
+    assert lib.msa_last_error()
+
+
+def test_sparse_prefill_fused_workspace_size(lib):
+    # one phase: none; phases: the list path's state, then kv bits (rounded
+    # up to 32-bit words) per q head and query block
+    assert lib.msa_sparse_prefill_fused_workspace(P(), 1000, 0) == 0
+    for kv in (0, 1, 32, 33, 1000, 1024):
+        n = 1 << 17
+        words = (kv + 31) // 32
+        assert lib.msa_sparse_prefill_fused_workspace(P(n=n), kv, 0) == \
+            lib.msa_sparse_prefill_workspace(P(n=n), 0) + 32 * (n // 64) * words * 4
+    assert lib.msa_sparse_prefill_fused_workspace(P(n=1 << 17), 1025, 0) == 0     # invalid: too many columns
+    assert lib.msa_sparse_prefill_fused_workspace(P(n=1 << 17), -1, 0) == 0
+    assert lib.msa_sparse_prefill_fused_workspace(P(n=1 << 17), 8, 100) == 0      # invalid phase length
 
 
 def test_walk_marks_query(lib):
