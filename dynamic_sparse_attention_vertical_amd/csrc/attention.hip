@@ -383,14 +383,22 @@ void attn_fwd_kernel(AttnArgs a) {
     const T *vp = reinterpret_cast<const T *>(a.v) + ((int64_t)g * a.stride) * kD;
 
     // Q fragments (B operand of S^T = K Q^T): query qrow, d = dk*16 + hl*8 + e.
-    // The per-head sparse kernels load them before reading their work lists
-    // (and the softmax state as soon as they know it exists), so those
-    // latencies overlap; the dense and grouped kernels after qualifying.
+    // A per-head sparse item in a key phase that surely runs (its own rows'
+    // phase) or likely runs (it holds a state from an earlier phase) loads
+    // them, and its state, before finding its part of the lists, so those
+    // latencies overlap; other items, which often leave a phase with few
+    // tiles to the next one, load Q once they know they run.  The dense and
+    // grouped kernels load Q after qualifying.
     frag qf[8];
+    bool q_loaded = false;
     auto load_q = [&]() {
 #pragma unroll
         for (int dk = 0; dk < 8; ++dk)
             qf[dk] = E::load_frag(qp + (int64_t)min(qrow, n32 - 1) * kD + dk * 16 + hl * 8);
+        q_loaded = true;
+    };
+    auto load_q_early = [&]() {
+        if (!q_loaded) load_q();
     };
     f32x16 o[4];
 #pragma unroll
@@ -514,7 +522,6 @@ void attn_fwd_kernel(AttnArgs a) {
         // one phase.  Carried between phases: the offset index (record .y),
         // the column index (record .x >> 1, next to the state flag in bit 0)
         // and the cover end (fused_cov).
-        load_q();
         const int64_t item = (int64_t)h * nqb + b;
         const int32_t *S = a.s_idx + (int64_t)h * a.ks;
         const int32_t *V = a.v_idx + (int64_t)h * a.kv;
@@ -522,6 +529,7 @@ void attn_fwd_kernel(AttnArgs a) {
         first = a.ws == nullptr || a.k_lo == INT_MIN;
         final_ = a.ws == nullptr || (int64_t)r0 + kBQ - 1 < (int64_t)a.k_hi;
         const int k_hi = final_ ? INT_MAX : a.k_hi;
+        if (final_) load_q_early();
         int i_in, cov_in = 0, ci_in = 0;
         if (a.ws != nullptr) {
             phase_rec = reinterpret_cast<int2 *>(a.ws + (int64_t)a.hq * nqb * 2 * kStateFloats) + item;
@@ -533,10 +541,27 @@ void attn_fwd_kernel(AttnArgs a) {
             const int2 rec = *phase_rec;
             const int rx = __builtin_amdgcn_readfirstlane(rec.x);
             have_state = (rx & 1) != 0;
-            if (have_state) load_state(sw);
+            if (have_state) {
+                load_q_early();
+                load_state(sw);
+            }
             ci_in = min(max(rx >> 1, 0), a.kv);
             i_in = min(__builtin_amdgcn_readfirstlane(rec.y), a.ks - 1);
             cov_in = max(__builtin_amdgcn_readfirstlane(load_uniform(a.fused_cov + item)), 0);
+        }
+        // A phase emits at most as many blocks as it has offsets whose ranges
+        // start before k_hi (a run of k ranges takes at most k blocks): when
+        // the 16th offset from i_in on already starts at or past k_hi, the
+        // phase cannot reach kMinPhaseTiles and is left to the next one
+        // without a walk.
+        if (a.ws != nullptr && !final_ &&
+            (i_in < kMinPhaseTiles - 1 ||
+             (int64_t)r0 - load_uniform(S + (i_in - (kMinPhaseTiles - 1))) >= (int64_t)k_hi)) {
+            if (first && tid == 0) {
+                *phase_rec = make_int2(0, i_in);
+                a.fused_cov[item] = 0;
+            }
+            return;
         }
         if (wave == 0) {                                // one wave walks, both read the lists after the barrier
             // the first two windows of columns, loaded now so that they land during the walk
@@ -709,6 +734,7 @@ void attn_fwd_kernel(AttnArgs a) {
             }
             return;
         }
+        if (!q_loaded) load_q();
         if (!final_) {                                  // this phase's columns run in the final phase
             if (wave == 0)
                 for (int t = lane; t < ncol; t += 64) {
@@ -721,7 +747,6 @@ void attn_fwd_kernel(AttnArgs a) {
         if (a.grp != nullptr &&
             load_uniform(a.grp + (int64_t)(h / a.grp_kh) * nqb + b) != 0)   // done by the grouped walk
             return;
-        load_q();
         const int64_t item = (int64_t)h * nqb + b;
         nblk = min(max(a.block_count[item], 0), a.cap_b);
         ncol = min(max(a.column_count[item], 0), a.cap_c);
@@ -737,6 +762,7 @@ void attn_fwd_kernel(AttnArgs a) {
             // locality.
             first = a.k_lo == INT_MIN;
             final_ = (int64_t)r0 + kBQ - 1 < (int64_t)a.k_hi;
+            if (final_) load_q_early();
             // every query block passes the first phase, which writes its
             // record; each phase with work updates it, so the next one finds
             // where its blocks start without a search
@@ -748,7 +774,10 @@ void attn_fwd_kernel(AttnArgs a) {
                 rec.x = __builtin_amdgcn_readfirstlane(rec.x);
                 rec.y = __builtin_amdgcn_readfirstlane(rec.y);
                 have_state = rec.x != 0;
-                if (have_state) load_state(sw);
+                if (have_state) {
+                    load_q_early();
+                    load_state(sw);
+                }
             }
             const int b0 = min(max(rec.y, 0), nblk);
             const int b1 = a.k_hi == INT_MAX ? nblk : b0 + lower_bound_near(blist + b0, nblk - b0, a.k_hi, lane);
@@ -761,6 +790,7 @@ void attn_fwd_kernel(AttnArgs a) {
                 return;
             }
         }
+        if (!q_loaded) load_q();
     }
     // an even number of chunks (column chunks padded with an empty one), so
     // that the steps come in pairs

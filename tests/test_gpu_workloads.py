@@ -10,6 +10,10 @@ current stream).  What each workload checks against the oracle:
   * sparse attention outputs and lse on sampled query blocks (0, 1, the
     last, and seeded random ones) of the sampled heads;
   * dense attention on sampled query blocks, 1M included;
+  * the fused sparse prefill (work lists walked inside the kernel) on the
+    layer's own sets: bitwise equal to the list path on every (q head,
+    query block) the grouped walk did not take, graded tolerances on the
+    rest (128K, 1M, 1M-band);
   * mixed 256K: every A-shape and vertical-slash head's arrays exact, every
     row of every block-sparse head within the tie band, attention sampled.
 """
@@ -126,7 +130,36 @@ def check_dense(x, n, items):
     log(f"  dense: {len(items)} sampled query blocks within tolerance")
 
 
-def run_vs_workload(name, heads, n_blocks, dense_blocks=6, attn_heads=None):
+def check_fused(x, w, plan, out, lse):
+    """msa_sparse_prefill_fused on the layer's sets against the list path's
+    output: the same tiles in the same order except where the grouped walk
+    ran."""
+    q, k, v = x["q"], x["k"], x["v"]
+    hq, n = q.shape[0], q.shape[1]
+    nbytes = msa.sparse_prefill_fused_workspace_bytes(hq, w.n_kv_heads, n, w.vertical_topk, q.dtype)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda") if nbytes else None
+    fout = torch.empty_like(out)
+    flse = torch.empty_like(lse)
+    msa.sparse_prefill_fused(q, k, v, plan.v_idx, plan.s_idx, out=fout, lse=flse, workspace=ws)
+    torch.cuda.synchronize()
+    del ws
+    marks = msa.sparse_walk_marks(plan.attn_workspace, hq, w.n_kv_heads, n, q.dtype) \
+        if plan.attn_workspace is not None else None
+    rows = torch.ones((hq, n), dtype=torch.bool, device="cuda") if marks is None else \
+        (marks == 0).repeat_interleave(64, dim=1)[:, :n]
+    for h in range(hq):
+        r = rows[h]
+        assert torch.equal(fout[h][r], out[h][r]), f"fused head {h}: outputs differ where the walk did not run"
+        assert torch.equal(flse[h][r], lse[h][r]), f"fused head {h}: lse differs where the walk did not run"
+        if not bool(r.all()):
+            compare_out(fout[h][~r].float().cpu().numpy(), out[h][~r].float().cpu().numpy(), False, f"fused h{h}")
+            compare_lse(flse[h][~r].cpu().numpy(), lse[h][~r].cpu().numpy(), f"fused h{h}")
+    walked = 0 if marks is None else int((marks != 0).sum())
+    log(f"  fused: bitwise equal on {hq * (n // 64) - walked} of {hq * (n // 64)} (head, query block) items, "
+        f"the rest within tolerance")
+
+
+def run_vs_workload(name, heads, n_blocks, dense_blocks=6, attn_heads=None, fused=False):
     """The layer as bench.py runs it, then: estimator scores and sets of
     `heads`; every head's index arrays; sparse attention on n_blocks sampled
     query blocks of `attn_heads` (default: the first two of `heads`); dense
@@ -152,6 +185,8 @@ def run_vs_workload(name, heads, n_blocks, dense_blocks=6, attn_heads=None):
     check_attention(x, out, lse, (ridx, {h: i for i, h in enumerate(attn_heads)}), items, "sparse")
     if dense_blocks:
         check_dense(x, n, [(attn_heads[0], b) for b in blocks[:dense_blocks]])
+    if fused:
+        check_fused(x, w, plan, out, lse)
     return plan
 
 
@@ -188,7 +223,7 @@ def test_single_head_4k_full_parity():
 
 
 def test_llama3_8b_128k():
-    run_vs_workload("llama3_8b_128k", heads=[0, 13, 31], n_blocks=10, attn_heads=[0, 13, 31])
+    run_vs_workload("llama3_8b_128k", heads=[0, 13, 31], n_blocks=10, attn_heads=[0, 13, 31], fused=True)
 
 
 # one q head per kv head (G = 4), the first of each group but for two groups
@@ -200,13 +235,13 @@ def test_llama3_8b_512k():
 
 
 def test_llama3_8b_1m():
-    run_vs_workload("llama3_8b_1m", heads=ONE_PER_KV, n_blocks=6, attn_heads=[5, 31])
+    run_vs_workload("llama3_8b_1m", heads=ONE_PER_KV, n_blocks=6, attn_heads=[5, 31], fused=True)
 
 
 def test_llama3_8b_1m_band():
     """The 1M layer with clustered slashes: long runs of adjacent diagonals, so
     the index is mostly long contiguous block runs plus the leftover columns."""
-    plan = run_vs_workload("llama3_8b_1m_band", heads=[2, 27], n_blocks=6, dense_blocks=0)
+    plan = run_vs_workload("llama3_8b_1m_band", heads=[2, 27], n_blocks=6, dense_blocks=0, fused=True)
     # the clustering is what this workload is for: far fewer blocks than the
     # iid 1M layer's (about one per selected diagonal there)
     assert plan.index.block_count.float().mean().item() < 0.5 * 6096
