@@ -199,6 +199,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--exact", action="store_true",
+                    help="with --fused: the exact union mask (selected columns and diagonals only, "
+                         "same tiles masked)")
     ap.add_argument("--fused", action="store_true",
                     help="time estimate + msa_sparse_prefill_fused (work lists walked inside the attention "
                          "kernel) as the step instead of estimate + build_index + sparse_prefill")
@@ -237,12 +240,16 @@ def main():
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
     fused = args.fused
+    exact = args.exact
+    if exact and not fused:
+        print("--exact needs --fused", file=sys.stderr)
+        sys.exit(2)
     if fused and mixed:
         print("--fused applies to vertical-slash layers only", file=sys.stderr)
         sys.exit(2)
     fused_ws = None
     if fused:
-        nbytes = msa.sparse_prefill_fused_workspace_bytes(hq, hkv, n, w.vertical_topk, q.dtype)
+        nbytes = msa.sparse_prefill_fused_workspace_bytes(hq, hkv, n, w.vertical_topk, q.dtype, exact=exact)
         fused_ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
 
     def step(ev=None):
@@ -263,7 +270,8 @@ def main():
             if ev is not None:
                 ev[2].record(stream)
         if fused:
-            msa.sparse_prefill_fused(q, k, v, plan.v_idx, plan.s_idx, out=out, workspace=fused_ws, stream=stream)
+            msa.sparse_prefill_fused(q, k, v, plan.v_idx, plan.s_idx, out=out, exact=exact, workspace=fused_ws,
+                                     stream=stream)
         else:
             msa.sparse_prefill(q, k, v, plan.index, out=out, workspace=plan.attn_workspace, stream=stream)
         if ev is not None:
@@ -379,7 +387,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "step": "fused" if fused else "lists", "seq_len": n, "q_heads": hq, "kv_heads": hkv, "head_dim": 128,
+        "config": {"workload": w.name, "step": ("fused-exact" if exact else "fused") if fused else "lists",
+                   "seq_len": n, "q_heads": hq, "kv_heads": hkv, "head_dim": 128,
                    "vertical_topk": w.vertical_topk, "slash_topk": w.slash_topk, "last_q": 64, "block": 64},
         "breakdown": breakdown,
         # the step's sparse prefill is one grouped-walk launch and n / phase_keys

@@ -159,6 +159,13 @@ struct ChunkSrc {
     uint64_t allow; // grouped walk: bit e set iff key base + e is in this wave's head's lists
     bool causal;    // some key of the tile is past a row or outside the sequence
 };
+// The exact union mask also carries words of the selected-offset bitmap from
+// bit sbase on (the tile's offsets) and of the selected-column bitmap from bit
+// vbase on (the tile's keys).
+struct ExactSrc : ChunkSrc {
+    uint32_t sx[5], vx[3];
+    int sbase, vbase;
+};
 
 // Per-lane constants of the chunk copies.  A chunk (32 rows) is moved by the
 // 2 kH waves of the workgroup, kRpw = 16 / kH rows each (wave w: chunk rows
@@ -353,7 +360,7 @@ __device__ __forceinline__ int lower_bound_near(const int32_t *list, int cnt, in
 // fp32 (a checking path) uses the same scheme with 64 KB of LDS.
 // kH q heads of one kv group per workgroup (2 kH waves) share every K/V copy;
 // used by the dense kernel, whose heads all walk the same tiles.
-template <typename T, bool kDense, int kH, bool kGrp = false, bool kFused = false>
+template <typename T, bool kDense, int kH, bool kGrp = false, bool kFused = false, bool kExact = false>
 __global__ __launch_bounds__(kThreads * kH) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1, sizeof(T) == 2 ? 2 : 1)))
 void attn_fwd_kernel(AttnArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the body uses gfx950-only LDS builtins
@@ -806,8 +813,9 @@ void attn_fwd_kernel(AttnArgs a) {
         y = j < nhole ? __builtin_amdgcn_readfirstlane(glist[wave][2 * j + 1]) : INT_MAX;
     };
     if constexpr (kGrp) hole_at(0, hx, hy);
+    using Src = typename std::conditional<kExact, ExactSrc, ChunkSrc>::type;
     auto tile_of = [&](int t) {
-        ChunkSrc s;
+        Src s;
         s.is_col = t >= nblk;
         if constexpr (kFused) s.base = s.is_col ? 0 : __builtin_amdgcn_readfirstlane(fblk[t]);
         else s.base = s.is_col ? 0 : (kDense ? t * kBK : load_uniform(blist + t));
@@ -816,6 +824,28 @@ void attn_fwd_kernel(AttnArgs a) {
         s.masked = !s.fast || s.base + kBK - 1 > r0;
         s.causal = s.masked;
         s.allow = ~0ull;
+        if constexpr (kExact) {
+            if (!s.is_col) {
+                // the tile's offsets qrow - key span [r0 - base - 63, r0 + 63 - base]:
+                // five words from the one holding the lowest; its keys: three words
+                const uint32_t *sb = a.ex_s + (int64_t)h * a.ex_words;
+                const uint32_t *vb = a.ex_v + (int64_t)h * a.ex_words;
+                const int lo = r0 - s.base - 63;
+                const int w0 = lo >= 0 ? lo >> 5 : -((31 - lo) >> 5);          // floor(lo / 32)
+                s.sbase = 32 * w0;
+#pragma unroll
+                for (int k = 0; k < 5; ++k)
+                    s.sx[k] = w0 + k >= 0 && w0 + k < a.ex_words ? (uint32_t)load_uniform(
+                                  reinterpret_cast<const int32_t *>(sb + w0 + k)) : 0u;
+                const int v0 = s.base >> 5;                                       // base >= 0
+                s.vbase = 32 * v0;
+#pragma unroll
+                for (int k = 0; k < 3; ++k)
+                    s.vx[k] = v0 + k < a.ex_words ? (uint32_t)load_uniform(reinterpret_cast<const int32_t *>(vb + v0 + k))
+                                                   : 0u;
+                s.masked = true;
+            }
+        }
         if constexpr (kGrp) {
             const int t0 = t * kBK;
             while (hy <= t0) hole_at(++hp, hx, hy);
@@ -841,7 +871,7 @@ void attn_fwd_kernel(AttnArgs a) {
         }
         return s;
     };
-    auto half_of = [](ChunkSrc s, int hf) {
+    auto half_of = [](Src s, int hf) {
         s.base += 32 * hf;
         s.c0 += 32 * hf;
         s.allow >>= 32 * hf;
@@ -883,7 +913,7 @@ void attn_fwd_kernel(AttnArgs a) {
     // mask: the key must exist and satisfy j <= i (keys past the end of the
     // sequence are > i, column padding is -1).  Lane value jj*4+i of S^T is
     // chunk key jj*8 + hl*4 + i.
-    auto mask = [&](int c, const ChunkSrc &cs, f32x16 &s) {
+    auto mask = [&](int c, const Src &cs, f32x16 &s) {
         if (!cs.masked) return;
         if (cs.is_col) {
 #pragma unroll
@@ -906,6 +936,26 @@ void attn_fwd_kernel(AttnArgs a) {
                     const int e = jj * 8 + hl * 4 + i;
                     if (e > hi || e < lo) s[jj * 4 + i] = -INFINITY;
                 }
+            }
+            if constexpr (kExact) {
+                // key base + e is allowed iff its offset from the row is a
+                // selected diagonal or it is a selected column.  x: the
+                // offset bits from qrow - base - 31 up, bit 31 - e for key e
+                const int rel = qrow - cs.base - 31 - cs.sbase;                 // 0 .. 126
+                const int w = rel >> 5;
+                const uint32_t lo = w == 0 ? cs.sx[0] : w == 1 ? cs.sx[1] : w == 2 ? cs.sx[2] : cs.sx[3];
+                const uint32_t hi = w == 0 ? cs.sx[1] : w == 1 ? cs.sx[2] : w == 2 ? cs.sx[3] : cs.sx[4];
+                const uint32_t x = __builtin_amdgcn_alignbit(hi, lo, (uint32_t)(rel & 31));
+                const int vr = cs.base - cs.vbase;                              // 0 .. 63, uniform
+                const uint32_t vlo = vr < 32 ? cs.vx[0] : cs.vx[1], vhi = vr < 32 ? cs.vx[1] : cs.vx[2];
+                const uint32_t cols = __builtin_amdgcn_alignbit(vhi, vlo, (uint32_t)(vr & 31));
+                // lane value jj*4+i is key jj*8 + hl*4 + i: bit jj*8+i of m
+                const uint32_t m = (__builtin_bitreverse32(x) | cols) >> (4 * hl);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (((m >> (jj * 8 + i)) & 1u) == 0) s[jj * 4 + i] = -INFINITY;
             }
             if constexpr (kGrp) {
                 const uint32_t al = (uint32_t)cs.allow;     // keys base .. base+31 of the chunk
@@ -955,7 +1005,7 @@ void attn_fwd_kernel(AttnArgs a) {
         }
     };
     // one pipeline step for chunk c (source cs); kn is the source of chunk c+2
-    auto step = [&](int c, const ChunkSrc &cs, const ChunkSrc &kn, f32x16 &s_cur, f32x16 &s_next,
+    auto step = [&](int c, const Src &cs, const Src &kn, f32x16 &s_cur, f32x16 &s_next,
                     frag (&p_cur)[2], const frag (&p_prev)[2], auto with_pv) {
         vm_wait<0>();                                   // K(c+1), V(c-1) have landed (this wave's part)
         __syncthreads();                                // ... all parts; K(c) and V(c-2) are free
@@ -983,8 +1033,8 @@ void attn_fwd_kernel(AttnArgs a) {
         const int ntile = nchunk / 2;
         f32x16 sa, sb;
         frag pa[2], pb[2];
-        ChunkSrc cur = tile_of(0);
-        ChunkSrc nxt = tile_of(min(1, ntile - 1));
+        Src cur = tile_of(0);
+        Src nxt = tile_of(min(1, ntile - 1));
         start_k(0, half_of(cur, 0));
         start_k(1, half_of(cur, 1));
         vm_wait<0>();
@@ -992,14 +1042,14 @@ void attn_fwd_kernel(AttnArgs a) {
         qk(0, sa);
         // tile 0: no PV yet in its first step
         {
-            const ChunkSrc after = tile_of(min(2, ntile - 1));
+            const Src after = tile_of(min(2, ntile - 1));
             step(0, half_of(cur, 0), half_of(nxt, 0), sa, sb, pa, pb, std::false_type{});
             step(1, half_of(cur, 1), half_of(nxt, 1), sb, sa, pb, pa, std::true_type{});
             cur = nxt;
             nxt = after;
         }
         for (int t = 1; t < ntile; ++t) {
-            const ChunkSrc after = tile_of(min(t + 2, ntile - 1));     // needed one pair later
+            const Src after = tile_of(min(t + 2, ntile - 1));          // needed one pair later
             step(2 * t, half_of(cur, 0), half_of(nxt, 0), sa, sb, pa, pb, std::true_type{});
             step(2 * t + 1, half_of(cur, 1), half_of(nxt, 1), sb, sa, pb, pa, std::true_type{});
             cur = nxt;
@@ -1046,12 +1096,12 @@ void attn_fwd_kernel(AttnArgs a) {
 #endif
 }
 
-template <typename T, bool kDense, int kH, bool kGrp = false, bool kFused = false>
+template <typename T, bool kDense, int kH, bool kGrp = false, bool kFused = false, bool kExact = false>
 hipError_t launch_h(const AttnArgs &a, hipStream_t s) {
     const int64_t total = (int64_t)(a.hq / kH) * ((a.n + kBQ - 1) / kBQ - (kDense ? 0 : a.qb_lo));
     if (total == 0) return hipSuccess;
-    hipLaunchKernelGGL((attn_fwd_kernel<T, kDense, kH, kGrp, kFused>), dim3((unsigned)total), dim3(kThreads * kH), 0,
-                       s, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, kDense, kH, kGrp, kFused, kExact>), dim3((unsigned)total),
+                       dim3(kThreads * kH), 0, s, a);
     return hipGetLastError();
 }
 
@@ -1060,26 +1110,63 @@ __global__ void clear_words_kernel(uint32_t *p, int64_t n) {
         p[i] = 0u;
 }
 
+// The exact union mask's bitmaps: selected offsets and selected column keys
+// of each q head (entries outside [0, n) select nothing), set on cleared words.
+__global__ void exact_bits_kernel(const int32_t *v_idx, int32_t kv, const int32_t *s_idx, int32_t ks, int32_t hq,
+                                  int64_t n, int32_t words, uint32_t *ex_s, uint32_t *ex_v) {
+    const int64_t per = (int64_t)kv + ks, total = per * hq;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t h = e / per, r = e % per;
+        const int32_t x = r < kv ? v_idx[h * kv + r] : s_idx[h * ks + (r - kv)];
+        if (x < 0 || x >= n) continue;
+        uint32_t *bits = (r < kv ? ex_v : ex_s) + h * words;
+        atomicOr(bits + (x >> 5), 1u << (x & 31));
+    }
+}
+
+hipError_t clear_words(uint32_t *p, int64_t words, hipStream_t s) {
+    if (words <= 0) return hipSuccess;
+    const int64_t blocks = (words + 255) / 256 < 65536 ? (words + 255) / 256 : 65536;
+    hipLaunchKernelGGL(clear_words_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, words);
+    return hipGetLastError();
+}
+
 // Fused mode: no grouped walk (there are no lists to qualify), the key phases
-// of the per-head kernel each walking its part of the cover.
-template <typename T> hipError_t launch_fused(AttnArgs a, hipStream_t s) {
+// of the per-head kernel each walking its part of the cover.  The exact
+// union mask's bitmaps follow the phase state and column bitmaps in ws.
+template <typename T, bool kExact> hipError_t launch_fused(AttnArgs a, hipStream_t s) {
     const int64_t R = a.phase_keys;
+    const bool phases = a.ws != nullptr && R > 0 && R < a.n;
     a.grp = nullptr;
-    if (a.ws == nullptr || R <= 0 || R >= a.n) {
+    if constexpr (kExact) {
+        a.ex_words = (int32_t)((a.n + 31) / 32);
+        uint32_t *bits = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(a.ws) +
+                                                      (phases ? fused_state_bytes(a.hq, a.n, R, a.kv, false) : 0));
+        a.ex_s = bits;
+        a.ex_v = bits + (int64_t)a.hq * a.ex_words;
+        hipError_t e = clear_words(bits, 2 * (int64_t)a.hq * a.ex_words, s);
+        if (e != hipSuccess) return e;
+        const int64_t total = ((int64_t)a.kv + a.ks) * a.hq;
+        if (total > 0) {
+            const int64_t blocks = (total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096;
+            hipLaunchKernelGGL(exact_bits_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a.v_idx, a.kv, a.s_idx,
+                               a.ks, a.hq, a.n, a.ex_words, bits, bits + (int64_t)a.hq * a.ex_words);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    }
+    if (!phases) {
         a.ws = nullptr;
         a.k_lo = INT_MIN;
         a.k_hi = INT_MAX;
         a.qb_lo = 0;
-        return launch_h<T, false, 1, false, true>(a, s);
+        return launch_h<T, false, 1, false, true, kExact>(a, s);
     }
     a.fused_cov = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(a.ws) + sparse_walk_marks_offset(a.hq, a.n));
     a.fused_cw = (a.kv + 31) / 32;
     a.fused_cols = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(a.ws) + sparse_state_bytes(a.hq, a.n, R));
-    const int64_t words = (int64_t)a.hq * ((a.n + kBQ - 1) / kBQ) * a.fused_cw;
-    if (words > 0) {
-        const int64_t blocks = (words + 255) / 256 < 65536 ? (words + 255) / 256 : 65536;
-        hipLaunchKernelGGL(clear_words_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a.fused_cols, words);
-        const hipError_t e = hipGetLastError();
+    {
+        const hipError_t e = clear_words(a.fused_cols, (int64_t)a.hq * ((a.n + kBQ - 1) / kBQ) * a.fused_cw, s);
         if (e != hipSuccess) return e;
     }
     const int64_t np = (a.n + R - 1) / R;
@@ -1087,7 +1174,7 @@ template <typename T> hipError_t launch_fused(AttnArgs a, hipStream_t s) {
         a.k_lo = j == 0 ? INT_MIN : (int32_t)(j * R);
         a.k_hi = j == np - 1 ? INT_MAX : (int32_t)((j + 1) * R);
         a.qb_lo = j * R / kBQ;
-        const hipError_t e = launch_h<T, false, 1, false, true>(a, s);
+        const hipError_t e = launch_h<T, false, 1, false, true, kExact>(a, s);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -1152,18 +1239,21 @@ size_t sparse_state_bytes(int64_t hq, int64_t n, int64_t phase_keys) {
     return (size_t)hq * (size_t)((n + kBQ - 1) / kBQ) * (2 * kStateFloats * sizeof(float) + sizeof(int2) + sizeof(int32_t));
 }
 
-size_t fused_state_bytes(int64_t hq, int64_t n, int64_t phase_keys, int64_t kv) {
+size_t fused_state_bytes(int64_t hq, int64_t n, int64_t phase_keys, int64_t kv, bool exact) {
     const size_t state = sparse_state_bytes(hq, n, phase_keys);
-    if (state == 0) return 0;
-    return state + (size_t)hq * (size_t)((n + kBQ - 1) / kBQ) * (size_t)((kv + 31) / 32) * sizeof(uint32_t);
+    size_t bytes = 0;
+    if (state != 0) bytes = state + (size_t)hq * (size_t)((n + kBQ - 1) / kBQ) * (size_t)((kv + 31) / 32) * sizeof(uint32_t);
+    if (exact) bytes += 2 * (size_t)hq * (size_t)((n + 31) / 32) * sizeof(uint32_t);
+    return bytes;
 }
 
 hipError_t launch_sparse_prefill(const AttnArgs &a, int dtype, hipStream_t s) {
     return dtype == 0 ? launch<bf16, false>(a, s) : launch<float, false>(a, s);
 }
 
-hipError_t launch_sparse_prefill_fused(const AttnArgs &a, int dtype, hipStream_t s) {
-    return dtype == 0 ? launch_fused<bf16>(a, s) : launch_fused<float>(a, s);
+hipError_t launch_sparse_prefill_fused(const AttnArgs &a, int dtype, bool exact, hipStream_t s) {
+    if (exact) return dtype == 0 ? launch_fused<bf16, true>(a, s) : launch_fused<float, true>(a, s);
+    return dtype == 0 ? launch_fused<bf16, false>(a, s) : launch_fused<float, false>(a, s);
 }
 
 int fused_max_phase_keys() { return kFusedMaxPhase; }

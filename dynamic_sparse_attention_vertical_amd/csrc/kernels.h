@@ -41,6 +41,11 @@ struct AttnArgs {
     // fused_cw 32-bit words each (all of them run in the final phase)
     uint32_t *fused_cols;
     int32_t fused_cw;
+    // fused mode with the exact union mask: per q head, a bitmap of the
+    // selected diagonal offsets over [0, n) and one of the selected column
+    // keys, ex_words 32-bit words each (unused otherwise)
+    const uint32_t *ex_s, *ex_v;
+    int32_t ex_words;
 };
 
 // Bytes of sparse-prefill state for hq heads and n keys in phases of
@@ -51,14 +56,16 @@ size_t sparse_state_bytes(int64_t hq, int64_t n, int64_t phase_keys);
 size_t sparse_walk_marks_offset(int64_t hq, int64_t n);
 // Bytes of fused-mode workspace: that state, then (when phases are used) one
 // bitmap of kv bits, rounded up to 32-bit words, per (q head, query block).
-size_t fused_state_bytes(int64_t hq, int64_t n, int64_t phase_keys, int64_t kv);
+// With exact, two bitmaps of n bits per q head follow (the exact union mask
+// needs them even when one phase covers all keys).
+size_t fused_state_bytes(int64_t hq, int64_t n, int64_t phase_keys, int64_t kv, bool exact);
 int walk_heads_per_unit(int hq, int hkv);
 
 // dtype: 0 = bf16, 1 = fp32
 hipError_t launch_sparse_prefill(const AttnArgs &a, int dtype, hipStream_t s);
 hipError_t launch_dense_prefill(const AttnArgs &a, int dtype, hipStream_t s);
 // Sparse prefill that walks the cover of s_idx / v_idx itself (no work lists).
-hipError_t launch_sparse_prefill_fused(const AttnArgs &a, int dtype, hipStream_t s);
+hipError_t launch_sparse_prefill_fused(const AttnArgs &a, int dtype, bool exact, hipStream_t s);
 int fused_max_phase_keys();
 int fused_max_columns();
 

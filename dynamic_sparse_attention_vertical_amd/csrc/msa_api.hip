@@ -348,6 +348,8 @@ static int attn_common(const msa_problem *p, const void *q, const void *k, const
     a.fused_cov = nullptr;
     a.fused_cols = nullptr;
     a.fused_cw = 0;
+    a.ex_s = a.ex_v = nullptr;
+    a.ex_words = 0;
     return MSA_OK;
 }
 
@@ -397,17 +399,19 @@ int msa_sparse_prefill(const msa_problem *p, const void *q, const void *k, const
                          "sparse_prefill");
 }
 
-size_t msa_sparse_prefill_fused_workspace(const msa_problem *p, int32_t vertical_topk, int32_t phase_keys) {
+size_t msa_sparse_prefill_fused_workspace(const msa_problem *p, int32_t vertical_topk, int32_t phase_keys,
+                                          int32_t flags) {
     if (check_problem(p) != MSA_OK || phase_keys < 0 || phase_keys % 64 != 0 || vertical_topk < 0 ||
-        vertical_topk > msa::fused_max_columns())
+        vertical_topk > msa::fused_max_columns() || (flags & ~MSA_FUSED_EXACT) != 0)
         return 0;
-    return msa::fused_state_bytes(p->n_q_heads, p->seq_len, phase_keys_of(phase_keys), vertical_topk);
+    return msa::fused_state_bytes(p->n_q_heads, p->seq_len, phase_keys_of(phase_keys), vertical_topk,
+                                  (flags & MSA_FUSED_EXACT) != 0);
 }
 
 int msa_sparse_prefill_fused(const msa_problem *p, const void *q, const void *k, const void *v,
                              const int32_t *v_idx, int32_t vertical_topk, const int32_t *s_idx, int32_t slash_topk,
-                             int32_t phase_keys, void *workspace, size_t workspace_bytes, void *out, float *lse,
-                             void *stream) {
+                             int32_t phase_keys, int32_t flags, void *workspace, size_t workspace_bytes, void *out,
+                             float *lse, void *stream) {
     msa::AttnArgs a;
     int st = attn_common(p, q, k, v, out, a);
     if (st) return st;
@@ -422,6 +426,8 @@ int msa_sparse_prefill_fused(const msa_problem *p, const void *q, const void *k,
         return fail(MSA_ERR_RANGE, "index sets and lse must be 4-byte aligned");
     if (phase_keys < 0 || phase_keys % 64 != 0)
         return fail(MSA_ERR_RANGE, "phase_keys %d is not a non-negative multiple of 64", phase_keys);
+    if ((flags & ~MSA_FUSED_EXACT) != 0) return fail(MSA_ERR_RANGE, "unknown flags 0x%x", (unsigned)flags);
+    const bool exact = (flags & MSA_FUSED_EXACT) != 0;
     a.phase_keys = (int32_t)phase_keys_of(phase_keys);
     if (a.phase_keys > msa::fused_max_phase_keys())
         return fail(MSA_ERR_RANGE, "the fused mode takes phases of at most %d keys (got %d)",
@@ -433,7 +439,7 @@ int msa_sparse_prefill_fused(const msa_problem *p, const void *q, const void *k,
     a.s_idx = s_idx;
     a.kv = vertical_topk;
     a.ks = slash_topk;
-    const size_t need = msa::fused_state_bytes(p->n_q_heads, p->seq_len, a.phase_keys, vertical_topk);
+    const size_t need = msa::fused_state_bytes(p->n_q_heads, p->seq_len, a.phase_keys, vertical_topk, exact);
     if (need > 0) {
         if (!workspace) return fail(MSA_ERR_NULL, "workspace is NULL (%zu bytes needed)", need);
         if (workspace_bytes < need)
@@ -442,7 +448,7 @@ int msa_sparse_prefill_fused(const msa_problem *p, const void *q, const void *k,
             return fail(MSA_ERR_RANGE, "workspace is not 16-byte aligned");
         a.ws = static_cast<float *>(workspace);
     }
-    return launch_status(msa::launch_sparse_prefill_fused(a, p->dtype, reinterpret_cast<hipStream_t>(stream)),
+    return launch_status(msa::launch_sparse_prefill_fused(a, p->dtype, exact, reinterpret_cast<hipStream_t>(stream)),
                          "sparse_prefill_fused");
 }
 

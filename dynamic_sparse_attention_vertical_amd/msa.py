@@ -50,9 +50,9 @@ _SIGS = {
     "msa_sparse_prefill": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32,
                                           _VP, ctypes.c_size_t, _VP, _VP, _VP]),
     "msa_sparse_prefill_workspace": (ctypes.c_size_t, [_VP, _I32]),
-    "msa_sparse_prefill_fused_workspace": (ctypes.c_size_t, [_VP, _I32, _I32]),
+    "msa_sparse_prefill_fused_workspace": (ctypes.c_size_t, [_VP, _I32, _I32, _I32]),
     "msa_sparse_prefill_walk_marks": (ctypes.c_int, [_VP, _I32, _VP, _VP]),
-    "msa_sparse_prefill_fused": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I32, _VP, _I32, _I32, _VP,
+    "msa_sparse_prefill_fused": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I32, _VP, _I32, _I32, _I32, _VP,
                                                 ctypes.c_size_t, _VP, _VP, _VP]),
     "msa_dense_prefill": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "msa_estimate_bs_workspace": (ctypes.c_size_t, [_VP, _I32]),
@@ -350,11 +350,15 @@ def sparse_prefill_workspace_bytes(n_q_heads: int, n_kv_heads: int, seq_len: int
     return int(load().msa_sparse_prefill_workspace(ctypes.byref(p), phase_keys))
 
 
+FUSED_EXACT = 1
+
+
 def sparse_prefill_fused_workspace_bytes(n_q_heads: int, n_kv_heads: int, seq_len: int, vertical_topk: int,
-                                         dtype=torch.bfloat16, phase_keys: int = 0) -> int:
-    """Workspace bytes of sparse_prefill_fused (0: one key phase, none needed)."""
+                                         dtype=torch.bfloat16, phase_keys: int = 0, exact: bool = False) -> int:
+    """Workspace bytes of sparse_prefill_fused (0: none needed)."""
     p = problem(n_q_heads, n_kv_heads, seq_len, MSA_BF16 if dtype == torch.bfloat16 else MSA_F32)
-    return int(load().msa_sparse_prefill_fused_workspace(ctypes.byref(p), vertical_topk, phase_keys))
+    return int(load().msa_sparse_prefill_fused_workspace(ctypes.byref(p), vertical_topk, phase_keys,
+                                                         FUSED_EXACT if exact else 0))
 
 
 def sparse_walk_marks(workspace: torch.Tensor, n_q_heads: int, n_kv_heads: int, seq_len: int,
@@ -412,13 +416,14 @@ def sparse_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: Ind
 def sparse_prefill_fused(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, v_idx: torch.Tensor,
                          s_idx: torch.Tensor, *, out: torch.Tensor | None = None,
                          lse: torch.Tensor | bool | None = None, sm_scale: float = 0.0, phase_keys: int = 0,
-                         workspace: torch.Tensor | None = None, stream=None):
+                         exact: bool = False, workspace: torch.Tensor | None = None, stream=None):
     """Causal attention over the greedy block cover of s_idx plus the leftover
     columns of v_idx, the work lists walked inside the kernel (no index
     arrays).  The same tiles in the same order as sparse_prefill(q, k, v,
-    build_index(v_idx, s_idx, seq_len)) without its grouped walk; workspace:
-    sparse_prefill_fused_workspace_bytes(...) bytes, allocated here when None
-    and needed."""
+    build_index(v_idx, s_idx, seq_len)) without its grouped walk; exact: attend
+    only to the selected columns and diagonals themselves (the same tiles,
+    masked); workspace: sparse_prefill_fused_workspace_bytes(...) bytes,
+    allocated here when None and needed."""
     lib = load()
     p = _problem_of(q, k, sm_scale, v)
     hq, n = q.shape[0], q.shape[1]
@@ -431,7 +436,8 @@ def sparse_prefill_fused(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, v_id
     if lse is True:
         lse = _lse_like(q, p)
     kv, ks = v_idx.shape[1], s_idx.shape[1]
-    need = int(lib.msa_sparse_prefill_fused_workspace(ctypes.byref(p), kv, phase_keys))
+    flags = FUSED_EXACT if exact else 0
+    need = int(lib.msa_sparse_prefill_fused_workspace(ctypes.byref(p), kv, phase_keys, flags))
     ws_ptr, ws_bytes = None, 0
     if need > 0:
         if workspace is None:
@@ -439,7 +445,7 @@ def sparse_prefill_fused(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, v_id
         ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
     _check(lib.msa_sparse_prefill_fused(ctypes.byref(p), _in_dev(q, "q"), _in_dev(k, "k"), _in_dev(v, "v"),
                                         _dev(v_idx, "v_idx") if kv else None, kv,
-                                        _dev(s_idx, "s_idx") if ks else None, ks, phase_keys, ws_ptr, ws_bytes,
+                                        _dev(s_idx, "s_idx") if ks else None, ks, phase_keys, flags, ws_ptr, ws_bytes,
                                         _rows_dev(out, "out", p, q),
                                         _rows_dev(lse, "lse", p, q, True) if want_lse else None, _stream(stream)),
            "msa_sparse_prefill_fused")

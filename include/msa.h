@@ -239,15 +239,25 @@ size_t msa_sparse_prefill_workspace(const msa_problem *p, int32_t phase_keys);
  *   vertical_topk <= 1024 and phase keys (phase_keys, 0 = the default) at most
  *     16384, else MSA_ERR_RANGE (the kernel holds a block's columns and a
  *     phase's block starts in LDS);
+ *   flags: 0, or MSA_FUSED_EXACT for the exact union mask: entry (i, j) is
+ *     attended iff j <= i and (j is a selected column or i - j a selected
+ *     diagonal) -- the selected lines themselves, as the talk slides draw
+ *     the vertical-slash pattern (slide "Dynamic sparsity in attention"),
+ *     instead of the 64-key blocks that cover them; the same tiles are
+ *     visited, with the entries off those lines masked; other bits:
+ *     MSA_ERR_RANGE;
  *   workspace: msa_sparse_prefill_fused_workspace(p, vertical_topk,
- *     phase_keys) bytes, 16-byte aligned (the key-phase state of
+ *     phase_keys, flags) bytes, 16-byte aligned (the key-phase state of
  *     msa_sparse_prefill_workspace, then one bitmap of vertical_topk bits per
- *     q head and query block); no initial contents assumed.               */
-size_t msa_sparse_prefill_fused_workspace(const msa_problem *p, int32_t vertical_topk, int32_t phase_keys);
+ *     q head and query block, then with MSA_FUSED_EXACT two bitmaps of N bits
+ *     per q head; 0 bytes: none needed); no initial contents assumed.      */
+#define MSA_FUSED_EXACT 1
+size_t msa_sparse_prefill_fused_workspace(const msa_problem *p, int32_t vertical_topk, int32_t phase_keys,
+                                          int32_t flags);
 int msa_sparse_prefill_fused(const msa_problem *p, const void *q, const void *k, const void *v,
                              const int32_t *v_idx, int32_t vertical_topk, const int32_t *s_idx, int32_t slash_topk,
-                             int32_t phase_keys, void *workspace, size_t workspace_bytes, void *out, float *lse,
-                             void *stream);
+                             int32_t phase_keys, int32_t flags, void *workspace, size_t workspace_bytes, void *out,
+                             float *lse, void *stream);
 
 /* Where msa_sparse_prefill records which query blocks the grouped walk took
  * (a diagnostic: the walk executes every aligned tile 0..b of such a block for

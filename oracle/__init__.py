@@ -25,6 +25,10 @@ state):
   index.build_index        selected diagonals -> per-query-block lists of
                            64-wide key blocks plus leftover vertical columns
                            (plain C helper, see csrc/index_ref.c).
+  index.exact_union_mask   M_x: the selected columns and diagonals themselves
+  index.exact_union_rows   (the vertical-slash pattern as the talk slides
+                           draw it, slide "Dynamic sparsity in attention");
+                           the second gives given rows only.
   attention.*              softmax attention restricted to an explicit boolean
                            mask (dense causal when every column and diagonal is
                            selected); attention_recall, the share of each
@@ -35,14 +39,15 @@ tests/test_oracle_pins.py.
 """
 
 from .estimate import estimate_vs, top_k_indices, block_sparse_select, block_scores
-from .index import (build_index, a_shape_sets, index_mask, exact_union_mask, block_key_sets,
-                    IndexArrays)
-from .attention import (attention_with_mask, masked_attention_blocks, dense_attention_blocks,
-                        dense_attention, attention_recall)
+from .index import (build_index, a_shape_sets, index_mask, exact_union_mask, exact_union_rows,
+                    block_key_sets, IndexArrays)
+from .attention import (attention_with_mask, masked_attention_blocks, exact_attention_blocks,
+                        dense_attention_blocks, dense_attention, attention_recall)
 
 __all__ = [
     "estimate_vs", "top_k_indices", "block_sparse_select", "block_scores",
-    "build_index", "a_shape_sets", "index_mask", "exact_union_mask", "block_key_sets",
+    "build_index", "a_shape_sets", "index_mask", "exact_union_mask", "exact_union_rows", "block_key_sets",
     "IndexArrays",
-    "attention_with_mask", "masked_attention_blocks", "dense_attention_blocks", "dense_attention",
+    "attention_with_mask", "masked_attention_blocks", "exact_attention_blocks", "dense_attention_blocks",
+    "dense_attention",
 ]

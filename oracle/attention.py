@@ -98,6 +98,27 @@ def masked_attention_blocks(q, k, v, idx: IndexArrays, items, head_rows=None, bl
     return out
 
 
+def exact_attention_blocks(q, k, v, v_idx, s_idx, items, block: int = 64, scale: float | None = None):
+    """Attention under the exact union mask M_x for sampled (head, query
+    block) pairs: {(h, b): (O [rows, D], lse [rows])}, row by row as
+    exact_union_mask defines it."""
+    from .index import exact_union_rows
+    Hq, N, D = q.shape
+    G = Hq // k.shape[0]
+    scale = (1.0 / np.sqrt(D)) if scale is None else scale
+    out = {}
+    for g, its in _grouped(items, G).items():
+        kg = as_f64(k[g])
+        vg = as_f64(v[g])
+        for (h, b) in its:
+            r0, r1 = b * block, min(b * block + block - 1, N - 1)
+            mask = exact_union_rows(v_idx[h], s_idx[h], r0, r1, N)
+            o, lse, _ = _masked_softmax_rows(as_f64(q[h, r0: r1 + 1]), kg[: r1 + 1], vg[: r1 + 1],
+                                             mask, scale)
+            out[(h, b)] = (o, lse)
+    return out
+
+
 def dense_attention_blocks(q, k, v, items, block: int = 64, scale: float | None = None):
     """Dense causal attention for sampled (head, query block) pairs."""
     Hq, N, D = q.shape

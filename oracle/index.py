@@ -116,6 +116,21 @@ def block_key_sets(idx: IndexArrays, h: int, b: int, n: int, block: int = 64) ->
     return keys
 
 
+def exact_union_rows(v_set, s_set, r0: int, r1: int, n: int) -> np.ndarray:
+    """Rows r0..r1 of one head's M_x over keys 0..r1: (j <= i) and (j in V or
+    i - j in S), V and S that head's column and diagonal sets (entries outside
+    [0, n) select nothing)."""
+    col = np.zeros(n, dtype=bool)
+    diag = np.zeros(n, dtype=bool)
+    v_set = np.asarray(v_set, dtype=np.int64)
+    s_set = np.asarray(s_set, dtype=np.int64)
+    col[v_set[(v_set >= 0) & (v_set < n)]] = True
+    diag[s_set[(s_set >= 0) & (s_set < n)]] = True
+    i = np.arange(r0, r1 + 1)[:, None]
+    j = np.arange(r1 + 1)[None, :]
+    return (j <= i) & (col[None, : r1 + 1] | diag[np.clip(i - j, 0, n - 1)])
+
+
 def index_mask(idx: IndexArrays, n: int, block: int = 64) -> np.ndarray:
     """Explicit boolean mask M [H, N, N] of the index (causal cut applied)."""
     H = idx.n_heads

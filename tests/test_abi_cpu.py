@@ -154,8 +154,8 @@ def test_sparse_prefill_validation(lib):
 
 
 def test_sparse_prefill_fused_validation(lib):
-    call = lambda prob, vi, kv, si, ks, pk=0, ws=None, wsb=0, lse=None: lib.msa_sparse_prefill_fused(
-        prob, FAKE, FAKE, FAKE, vi, kv, si, ks, pk, ws, wsb, FAKE, lse, None)
+    call = lambda prob, vi, kv, si, ks, pk=0, ws=None, wsb=0, lse=None, flags=0: lib.msa_sparse_prefill_fused(
+        prob, FAKE, FAKE, FAKE, vi, kv, si, ks, pk, flags, ws, wsb, FAKE, lse, None)
     assert call(P(), None, 4, FAKE, 4) == NULL
     assert call(P(), FAKE, 4, None, 4) == NULL
     assert call(P(), FAKE, -1, FAKE, 4) == RANGE
@@ -164,8 +164,14 @@ def test_sparse_prefill_fused_validation(lib):
     assert call(P(), ctypes.c_void_p(0x1002), 4, FAKE, 4) == RANGE  # not 4-byte aligned
     assert call(P(), FAKE, 4, FAKE, 4, pk=100) == RANGE
     assert call(P(n=1 << 17), FAKE, 4, FAKE, 4, pk=32768) == RANGE  # phases of at most 16384 keys
+    assert call(P(), FAKE, 4, FAKE, 4, flags=2) == RANGE            # unknown flag
+    # the exact mask needs its bitmaps even in one phase
+    need_x = lib.msa_sparse_prefill_fused_workspace(P(), 4, 0, 1)
+    assert need_x > 0
+    assert call(P(), FAKE, 4, FAKE, 4, flags=1) == NULL
+    assert call(P(), FAKE, 4, FAKE, 4, flags=1, ws=FAKE, wsb=need_x - 1) == WS
     n = 1 << 15
-    need = lib.msa_sparse_prefill_fused_workspace(P(n=n), 4, 0)
+    need = lib.msa_sparse_prefill_fused_workspace(P(n=n), 4, 0, 0)
     assert need > 0
     assert call(P(n=n), FAKE, 4, FAKE, 4, ws=None, wsb=need) == NULL
     assert call(P(n=n), FAKE, 4, FAKE, 4, ws=FAKE, wsb=need - 1) == WS
@@ -177,15 +183,19 @@ def test_sparse_prefill_fused_validation(lib):
 def test_sparse_prefill_fused_workspace_size(lib):
     # one phase: none; phases: the list path's state, then kv bits (rounded
     # up to 32-bit words) per q head and query block
-    assert lib.msa_sparse_prefill_fused_workspace(P(), 1000, 0) == 0
+    assert lib.msa_sparse_prefill_fused_workspace(P(), 1000, 0, 0) == 0
     for kv in (0, 1, 32, 33, 1000, 1024):
         n = 1 << 17
         words = (kv + 31) // 32
-        assert lib.msa_sparse_prefill_fused_workspace(P(n=n), kv, 0) == \
-            lib.msa_sparse_prefill_workspace(P(n=n), 0) + 32 * (n // 64) * words * 4
-    assert lib.msa_sparse_prefill_fused_workspace(P(n=1 << 17), 1025, 0) == 0     # invalid: too many columns
-    assert lib.msa_sparse_prefill_fused_workspace(P(n=1 << 17), -1, 0) == 0
-    assert lib.msa_sparse_prefill_fused_workspace(P(n=1 << 17), 8, 100) == 0      # invalid phase length
+        base = lib.msa_sparse_prefill_workspace(P(n=n), 0) + 32 * (n // 64) * words * 4
+        assert lib.msa_sparse_prefill_fused_workspace(P(n=n), kv, 0, 0) == base
+        # exact union mask: two bitmaps of n bits per q head after that
+        assert lib.msa_sparse_prefill_fused_workspace(P(n=n), kv, 0, 1) == base + 2 * 32 * (n // 32) * 4
+    assert lib.msa_sparse_prefill_fused_workspace(P(n=4096 + 5), 8, 0, 1) == 2 * 32 * (4096 // 32 + 1) * 4
+    assert lib.msa_sparse_prefill_fused_workspace(P(n=1 << 17), 1025, 0, 0) == 0     # invalid: too many columns
+    assert lib.msa_sparse_prefill_fused_workspace(P(n=1 << 17), -1, 0, 0) == 0
+    assert lib.msa_sparse_prefill_fused_workspace(P(n=1 << 17), 8, 100, 0) == 0      # invalid phase length
+    assert lib.msa_sparse_prefill_fused_workspace(P(n=1 << 17), 8, 0, 4) == 0        # unknown flag
 
 
 def test_walk_marks_query(lib):

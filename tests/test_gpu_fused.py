@@ -206,3 +206,53 @@ def test_fused_layer_sets():
     idx = msa.build_index(vi, si, n)
     ref, rlse = msa.sparse_prefill(qs, ks_, vs, idx, lse=True, phase_keys=one_phase(n))
     assert torch.equal(out, ref) and torch.equal(lse, rlse)
+
+
+@pytest.mark.parametrize("hq,hkv,n,kv,ks,phase,fp32", [
+    (4, 2, 640, 20, 60, 0, False),          # one launch
+    (2, 1, 64 * 9 + 23, 30, 200, 0, False),  # ragged last query block
+    (2, 1, 1216, 40, 300, 256, False),      # key phases, state carried
+    (2, 1, 640, 9, 13, 192, True),          # fp32, phases
+    (8, 2, 1024, 64, 500, 0, False),        # GQA group of 4, dense-ish diagonals
+])
+def test_fused_exact_union_mask(hq, hkv, n, kv, ks, phase, fp32):
+    """MSA_FUSED_EXACT: attention over exactly (j <= i) and (j in V or i - j in
+    S), against the oracle's exact_union_mask."""
+    q, k, v = inputs(hq, hkv, n, seed=n + ks, fp32=fp32)
+    vi, si = random_sets(hq, n, kv, ks, seed=n + kv)
+    qs, ks_, vs = dev(q, k, v)
+    vt, st = dev(torch.from_numpy(vi), torch.from_numpy(si))
+    dt = torch.float32 if fp32 else torch.bfloat16
+    need = msa.sparse_prefill_fused_workspace_bytes(hq, hkv, n, kv, dt, phase_keys=phase, exact=True)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    out, lse = msa.sparse_prefill_fused(qs, ks_, vs, vt, st, lse=True, phase_keys=phase, exact=True, workspace=ws)
+    ref, rlse = oracle.attention_with_mask(q, k, v, oracle.exact_union_mask(vi, si, n))
+    compare_out(out.float().cpu().numpy(), ref, fp32, "exact union")
+    compare_lse(lse.cpu().numpy(), rlse, "exact union")
+    # the exact mask is a subset of the block cover: no row keeps more mass
+    _, blse = msa.sparse_prefill_fused(qs, ks_, vs, vt, st, lse=True, phase_keys=phase)
+    fin = torch.isfinite(lse)
+    assert torch.all(lse[fin] <= blse[fin] + 1e-5)
+
+
+def test_fused_exact_special_cases():
+    """Closed forms: only the main diagonal -> each row attends to itself
+    (out = v of that row); every diagonal -> dense causal attention; only
+    columns -> the column keys below each row."""
+    n, hq = 448, 2
+    q, k, v = inputs(hq, 1, n, seed=5)
+    qs, ks_, vs = dev(q, k, v)
+    none = torch.empty((hq, 0), dtype=torch.int32, device="cuda")
+    main = torch.zeros((hq, 1), dtype=torch.int32, device="cuda")
+    out = msa.sparse_prefill_fused(qs, ks_, vs, none, main, exact=True)
+    assert torch.equal(out[0], vs[0]) and torch.equal(out[1], vs[0])
+    every = torch.arange(n, dtype=torch.int32, device="cuda").expand(hq, -1).contiguous()
+    out, lse = msa.sparse_prefill_fused(qs, ks_, vs, none, every, lse=True, exact=True)
+    ref, rlse = oracle.dense_attention(q, k, v)
+    compare_out(out.float().cpu().numpy(), ref, False, "exact, every diagonal")
+    compare_lse(lse.cpu().numpy(), rlse, "exact, every diagonal")
+    cols = np.array([[3, 70, 200, 201, 447]] * hq, np.int32)
+    out, lse = msa.sparse_prefill_fused(qs, ks_, vs, dev(torch.from_numpy(cols))[0], none, lse=True, exact=True)
+    ref, rlse = oracle.attention_with_mask(q, k, v, oracle.exact_union_mask(cols, np.zeros((hq, 0), np.int64), n))
+    compare_out(out.float().cpu().numpy(), ref, False, "exact, columns only")
+    compare_lse(lse.cpu().numpy(), rlse, "exact, columns only")

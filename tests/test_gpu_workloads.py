@@ -13,7 +13,8 @@ current stream).  What each workload checks against the oracle:
   * the fused sparse prefill (work lists walked inside the kernel) on the
     layer's own sets: bitwise equal to the list path on every (q head,
     query block) the grouped walk did not take, graded tolerances on the
-    rest (128K, 1M, 1M-band);
+    rest; and its exact union mask (MSA_FUSED_EXACT) against the oracle's
+    exact_attention_blocks on sampled query blocks (128K, 1M, 1M-band);
   * mixed 256K: every A-shape and vertical-slash head's arrays exact, every
     row of every block-sparse head within the tie band, attention sampled.
 """
@@ -130,7 +131,7 @@ def check_dense(x, n, items):
     log(f"  dense: {len(items)} sampled query blocks within tolerance")
 
 
-def check_fused(x, w, plan, out, lse):
+def check_fused(x, w, plan, out, lse, items):
     """msa_sparse_prefill_fused on the layer's sets against the list path's
     output: the same tiles in the same order except where the grouped walk
     ran."""
@@ -157,6 +158,18 @@ def check_fused(x, w, plan, out, lse):
     walked = 0 if marks is None else int((marks != 0).sum())
     log(f"  fused: bitwise equal on {hq * (n // 64) - walked} of {hq * (n // 64)} (head, query block) items, "
         f"the rest within tolerance")
+    # the exact union mask on the same sets, sampled against the oracle
+    nbytes = msa.sparse_prefill_fused_workspace_bytes(hq, w.n_kv_heads, n, w.vertical_topk, q.dtype, exact=True)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    msa.sparse_prefill_fused(q, k, v, plan.v_idx, plan.s_idx, out=fout, lse=flse, exact=True, workspace=ws)
+    torch.cuda.synchronize()
+    del ws
+    vi, si = plan.v_idx.cpu().numpy(), plan.s_idx.cpu().numpy()
+    ref = oracle.exact_attention_blocks(q.cpu(), k.cpu(), v.cpu(), vi, si, items)
+    for (h, b), (o, l) in ref.items():
+        compare_out(fout[h, 64 * b: 64 * b + 64].float().cpu().numpy(), o, False, f"exact h{h} b{b}")
+        compare_lse(flse[h, 64 * b: 64 * b + 64].cpu().numpy(), l, f"exact h{h} b{b}")
+    log(f"  fused exact union mask: {len(items)} sampled query blocks within tolerance")
 
 
 def run_vs_workload(name, heads, n_blocks, dense_blocks=6, attn_heads=None, fused=False):
@@ -186,7 +199,7 @@ def run_vs_workload(name, heads, n_blocks, dense_blocks=6, attn_heads=None, fuse
     if dense_blocks:
         check_dense(x, n, [(attn_heads[0], b) for b in blocks[:dense_blocks]])
     if fused:
-        check_fused(x, w, plan, out, lse)
+        check_fused(x, w, plan, out, lse, [(h, b) for h in attn_heads for b in blocks[:4]])
     return plan
 
 

@@ -244,6 +244,35 @@ def test_exact_union_mask_closed_forms():
                                   np.tril(np.ones((n, n), bool)))
 
 
+@pytest.mark.parametrize("n,kv,ks,seed", [(200, 7, 30, 0), (130, 0, 50, 1), (257, 20, 0, 2)])
+def test_exact_union_rows_and_blocks(n, kv, ks, seed):
+    """Row slices of exact_union_mask (brute-force pinned above) from
+    exact_union_rows, ragged last block included, plus entries outside [0, n)
+    selecting nothing; exact_attention_blocks against attention_with_mask
+    under the full mask on the same rows."""
+    rng = np.random.default_rng(seed)
+    vi = np.sort(rng.choice(n, kv, replace=False))[None].astype(np.int64)
+    si = np.sort(rng.choice(n, ks, replace=False))[None].astype(np.int64)
+    full = oracle.exact_union_mask(vi, si, n)[0]
+    for b in range((n + 63) // 64):
+        r0, r1 = 64 * b, min(64 * b + 63, n - 1)
+        np.testing.assert_array_equal(oracle.exact_union_rows(vi[0], si[0], r0, r1, n), full[r0:r1 + 1, :r1 + 1])
+        padded_v = np.r_[-5, vi[0], n, n + 7]
+        padded_s = np.r_[-1, si[0], n + 2]
+        np.testing.assert_array_equal(oracle.exact_union_rows(padded_v, padded_s, r0, r1, n),
+                                      full[r0:r1 + 1, :r1 + 1])
+    q = rng.standard_normal((1, n, 32))
+    k = rng.standard_normal((1, n, 32))
+    v = rng.standard_normal((1, n, 32))
+    ref, rlse = oracle.attention_with_mask(q, k, v, full[None])
+    items = [(0, b) for b in range((n + 63) // 64)]
+    got = oracle.exact_attention_blocks(q, k, v, vi, si, items)
+    for (h, b), (o, l) in got.items():
+        r0, r1 = 64 * b, min(64 * b + 63, n - 1)
+        np.testing.assert_allclose(o, ref[0, r0:r1 + 1], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(l, rlse[0, r0:r1 + 1], rtol=0, atol=1e-12)
+
+
 def test_index_all_selected_is_causal():
     n = 320
     all_ = np.arange(n, dtype=np.int32)[None]
