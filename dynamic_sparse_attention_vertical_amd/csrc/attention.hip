@@ -163,7 +163,7 @@ struct ChunkSrc {
 // bit sbase on (the tile's offsets) and of the selected-column bitmap from bit
 // vbase on (the tile's keys).
 struct ExactSrc : ChunkSrc {
-    uint32_t sx[5], vx[3];
+    uint32_t sx0, sx1, sx2, sx3, sx4, vx0, vx1, vx2;
     int sbase, vbase;
 };
 
@@ -833,16 +833,20 @@ void attn_fwd_kernel(AttnArgs a) {
                 const int lo = r0 - s.base - 63;
                 const int w0 = lo >= 0 ? lo >> 5 : -((31 - lo) >> 5);          // floor(lo / 32)
                 s.sbase = 32 * w0;
-#pragma unroll
-                for (int k = 0; k < 5; ++k)
-                    s.sx[k] = w0 + k >= 0 && w0 + k < a.ex_words ? (uint32_t)load_uniform(
-                                  reinterpret_cast<const int32_t *>(sb + w0 + k)) : 0u;
+                auto word = [&](const uint32_t *bits, int i) {
+                    return i >= 0 && i < a.ex_words ? (uint32_t)load_uniform(reinterpret_cast<const int32_t *>(bits + i))
+                                                    : 0u;
+                };
+                s.sx0 = word(sb, w0);
+                s.sx1 = word(sb, w0 + 1);
+                s.sx2 = word(sb, w0 + 2);
+                s.sx3 = word(sb, w0 + 3);
+                s.sx4 = word(sb, w0 + 4);
                 const int v0 = s.base >> 5;                                       // base >= 0
                 s.vbase = 32 * v0;
-#pragma unroll
-                for (int k = 0; k < 3; ++k)
-                    s.vx[k] = v0 + k < a.ex_words ? (uint32_t)load_uniform(reinterpret_cast<const int32_t *>(vb + v0 + k))
-                                                   : 0u;
+                s.vx0 = word(vb, v0);
+                s.vx1 = word(vb, v0 + 1);
+                s.vx2 = word(vb, v0 + 2);
                 s.masked = true;
             }
         }
@@ -943,11 +947,17 @@ void attn_fwd_kernel(AttnArgs a) {
                 // offset bits from qrow - base - 31 up, bit 31 - e for key e
                 const int rel = qrow - cs.base - 31 - cs.sbase;                 // 0 .. 126
                 const int w = rel >> 5;
-                const uint32_t lo = w == 0 ? cs.sx[0] : w == 1 ? cs.sx[1] : w == 2 ? cs.sx[2] : cs.sx[3];
-                const uint32_t hi = w == 0 ? cs.sx[1] : w == 1 ? cs.sx[2] : w == 2 ? cs.sx[3] : cs.sx[4];
+                // the words as scalar values first (a select between fields
+                // of one struct would otherwise become an indexed load from
+                // scratch memory)
+                const uint32_t x0 = __builtin_amdgcn_readfirstlane(cs.sx0), x1 = __builtin_amdgcn_readfirstlane(cs.sx1),
+                               x2 = __builtin_amdgcn_readfirstlane(cs.sx2), x3 = __builtin_amdgcn_readfirstlane(cs.sx3),
+                               x4 = __builtin_amdgcn_readfirstlane(cs.sx4);
+                const uint32_t lo = w == 0 ? x0 : w == 1 ? x1 : w == 2 ? x2 : x3;
+                const uint32_t hi = w == 0 ? x1 : w == 1 ? x2 : w == 2 ? x3 : x4;
                 const uint32_t x = __builtin_amdgcn_alignbit(hi, lo, (uint32_t)(rel & 31));
                 const int vr = cs.base - cs.vbase;                              // 0 .. 63, uniform
-                const uint32_t vlo = vr < 32 ? cs.vx[0] : cs.vx[1], vhi = vr < 32 ? cs.vx[1] : cs.vx[2];
+                const uint32_t vlo = vr < 32 ? cs.vx0 : cs.vx1, vhi = vr < 32 ? cs.vx1 : cs.vx2;
                 const uint32_t cols = __builtin_amdgcn_alignbit(vhi, vlo, (uint32_t)(vr & 31));
                 // lane value jj*4+i is key jj*8 + hl*4 + i: bit jj*8+i of m
                 const uint32_t m = (__builtin_bitreverse32(x) | cols) >> (4 * hl);
