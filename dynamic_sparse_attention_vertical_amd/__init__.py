@@ -5,7 +5,8 @@ the C ABI declared in include/msa.h); this package is a thin ctypes binding
 over it.  PyTorch provides device memory and streams only.
 """
 
-from .msa import (MsaError, IndexTensors, Problem, alloc_index, build_index, dense_prefill,
+from .msa import (MsaError, IndexTensors, Problem, alloc_index, build_index, decode_sparse,
+                  decode_sparse_workspace_bytes, dense_prefill,
                   estimate_bs, estimate_vs, estimate_vs_noalloc, estimate_vs_workspace_bytes, index_caps, lib_path, load,
                   problem, sparse_prefill, sparse_prefill_fused, sparse_prefill_fused_workspace_bytes,
                   sparse_prefill_workspace_bytes,
@@ -13,7 +14,8 @@ from .msa import (MsaError, IndexTensors, Problem, alloc_index, build_index, den
 from .layer import (vertical_slash_layer, mixed_layer, vertical_slash_sparse_attention, block_sparse_attention,
                     streaming_forward)
 
-__all__ = ["MsaError", "IndexTensors", "Problem", "alloc_index", "build_index", "dense_prefill",
+__all__ = ["MsaError", "IndexTensors", "Problem", "alloc_index", "build_index", "decode_sparse",
+           "decode_sparse_workspace_bytes", "dense_prefill",
            "estimate_bs", "estimate_vs", "estimate_vs_noalloc", "estimate_vs_workspace_bytes", "index_caps", "lib_path",
            "load", "problem", "sparse_prefill", "sparse_prefill_fused", "sparse_prefill_fused_workspace_bytes",
            "sparse_prefill_workspace_bytes",

@@ -1,0 +1,348 @@
+// Decode-side dynamic sparsity for gfx950: one new query row per q head
+// attends only to the top-k cached keys by attention score.
+//
+// The talk slides "System-Algorithm Co-design" (slide "Dynamic sparsity in
+// attention", decoding panel) show that the keys a decode step needs change
+// from step to step: choosing the top-1000 keys anew at each step keeps far
+// more of the attention mass than a fixed choice.  The step here:
+//   scores   s[h, j] = scale * <q_h, k_{g(h), j}> in log2 units, for every
+//            cached key (K streamed once per kv head, shared by its q heads),
+//            written as order-preserving 32-bit keys, with each chunk's
+//            running max and sum of 2^s (the dense softmax denominator);
+//   stats    the dense log-sum-exp of every q head from those partials;
+//   select   exact top-k of the keys per head (the radix select of topk.hip,
+//            ties to the lower index, indices ascending), or a given set;
+//   attend   softmax over the selected scores and the weighted sum of their V
+//            rows; the retrieved share of the dense attention mass is
+//            2^(lse_selected - lse_dense).
+// Layout: q [hq, 128], K and V [hkv, stride, 128], out [hq, 128], one query
+// per head (a batch of sequences is folded into the heads).
+#include "common.h"
+#include "kernels.h"
+
+#include <climits>
+
+namespace msa {
+namespace {
+
+constexpr int kD = 128;           // head_dim
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+constexpr int kThreads = 256;
+constexpr int kMaxG = 8;          // q heads scored together per K pass
+constexpr int kU = 4;             // rows per 16-lane group in flight
+
+// float score -> 32-bit key that orders like the score (and back)
+__device__ __forceinline__ uint32_t order_key(float s) {
+    const uint32_t b = __float_as_uint(s);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key_score(uint32_t u) {
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+
+// 8 consecutive elements of a row as floats (16 lanes cover a 128-wide row)
+template <typename T> __device__ __forceinline__ void load8(const T *p, float (&x)[8]);
+template <> __device__ __forceinline__ void load8<bf16>(const bf16 *p, float (&x)[8]) {
+    const u32x4 w = *reinterpret_cast<const u32x4 *>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+template <> __device__ __forceinline__ void load8<float>(const float *p, float (&x)[8]) {
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[i] = a[i];
+        x[4 + i] = b[i];
+    }
+}
+
+__device__ __forceinline__ float sum16(float v) {          // over the 16 lanes of a row group
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, 16);
+    return v;
+}
+
+// The kG dot products of a 16-lane row group (one partial per lane each),
+// reduce-scattered: afterwards lane pairs (kG = 8) or quads (kG = 4) hold
+// one head's full sum each, head_of(lane) -- kG - 1 + 4 shuffles instead of
+// 4 per head.
+template <int kG> __device__ __forceinline__ float reduce_scatter16(const float (&v)[kG], int lane) {
+    float w[kG];
+#pragma unroll
+    for (int i = 0; i < kG; ++i) w[i] = v[i];
+    int live = kG;
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) {
+        if (live > 1) {
+            const bool upper = (lane & o) != 0;
+            const int half = live / 2;
+#pragma unroll
+            for (int i = 0; i < kG / 2; ++i) {
+                if (i < half) {
+                    const float send = upper ? w[i] : w[i + half];
+                    const float keep = upper ? w[i + half] : w[i];
+                    w[i] = keep + __shfl_xor(send, o, 16);
+                }
+            }
+            live = half;
+        } else {
+            w[0] += __shfl_xor(w[0], o, 16);
+        }
+    }
+    return w[0];
+}
+template <int kG> __device__ __forceinline__ int head_of(int lane) {
+    return kG == 8 ? ((lane >> 3) & 1) * 4 + ((lane >> 2) & 1) * 2 + ((lane >> 1) & 1)
+                   : ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1);
+}
+
+// Grid (chunk, kv head): heads g0 .. g0 + gcount - 1 (gcount <= kG) of the kv
+// head's group, keys [chunk * chunk_keys, ...).  A wave scores 4 keys per
+// step (16 lanes per key, 8 elements each, kU keys per row group in flight);
+// after the reduce-scatter each lane owns one head of its key and keeps that
+// head's running max and sum.
+template <typename T, int kG>
+__global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a, int g0) {
+    const int kvh = blockIdx.y;
+    const int G = a.hq / a.hkv;
+    const int gcount = min(G - g0, kG);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = (lane & 15) * 8, sub = lane >> 4;
+    const int hl = head_of<kG>(lane);                        // this lane's head after the reduction
+    const bool owner = hl < gcount && (lane & (kG == 8 ? 1 : 3)) == 0;
+    // bf16: q and K stay bf16 pairs, multiplied by v_dot2 (two products
+    // summed into an fp32 accumulator); fp32: fused multiply-adds
+    constexpr bool kPairs = sizeof(T) == 2;
+    float qv[kG][8];
+    bf16x2_t qp[kG][4];
+#pragma unroll
+    for (int g = 0; g < kG; ++g) {
+        const T *src = reinterpret_cast<const T *>(a.q) + (int64_t)(kvh * G + g0 + min(g, gcount - 1)) * kD + col;
+        if constexpr (kPairs) {
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(src);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) qp[g][i] = __builtin_bit_cast(bf16x2_t, g < gcount ? w[i] : 0u);
+        } else {
+            load8<T>(src, qv[g]);
+            if (g >= gcount)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qv[g][e] = 0.f;
+        }
+    }
+    const T *kp = reinterpret_cast<const T *>(a.k) + (int64_t)kvh * a.stride * kD;
+    uint32_t *krow = a.keys + (int64_t)(kvh * G + g0 + min(hl, gcount - 1)) * a.n;
+    const int64_t j0 = (int64_t)blockIdx.x * a.chunk_keys;
+    const int64_t j1 = min(j0 + a.chunk_keys, a.n);
+    float m = -INFINITY, l = 0.f;
+    constexpr int kUs = kPairs ? 2 * kU : kU;               // bf16 rows are half the registers
+    for (int64_t jb = j0 + wave * 4 + sub; jb < j1; jb += 16 * kUs) {
+        float kx[kUs][8];
+        u32x4 kw[kUs];
+#pragma unroll
+        for (int u = 0; u < kUs; ++u) {
+            const int64_t j = jb + 16 * u;
+            if constexpr (kPairs) {
+                // non-temporal: each K row is read once per pass (8% faster at 100K x 64 kv heads)
+                kw[u] = j < j1 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kp + j * kD + col))
+                               : u32x4{0u, 0u, 0u, 0u};
+            } else if (j < j1) {
+                load8<T>(kp + j * kD + col, kx[u]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) kx[u][e] = 0.f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUs; ++u) {
+            const int64_t j = jb + 16 * u;
+            if (j >= j1) break;
+            float d[kG];
+#pragma unroll
+            for (int g = 0; g < kG; ++g) {
+                d[g] = 0.f;
+                if constexpr (kPairs) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        // the element into a scalar first: a bit cast of a
+                        // vector element in place reads element 0
+                        const uint32_t kpair = kw[u][i];
+                        d[g] = __builtin_amdgcn_fdot2_f32_bf16(qp[g][i], __builtin_bit_cast(bf16x2_t, kpair), d[g],
+                                                               false);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) d[g] = fmaf(qv[g][e], kx[u][e], d[g]);
+                }
+            }
+            const float sc = reduce_scatter16<kG>(d, lane) * a.scale_log2;
+            if (owner) {
+                krow[j] = order_key(sc);
+                const float mn = fmaxf(m, sc);
+                l = l * __builtin_amdgcn_exp2f(m - mn) + __builtin_amdgcn_exp2f(sc - mn);
+                m = mn;
+            }
+        }
+    }
+    // the chunk's (max, sum) per head: owners of one head sit at the same
+    // position in each row group; combine the 4 row groups, then the waves
+    auto comb = [](float &mg, float &lg, float mo, float lo) {
+        const float mn = fmaxf(mg, mo);
+        lg = (mn == -INFINITY) ? 0.f : lg * __builtin_amdgcn_exp2f(mg - mn) + lo * __builtin_amdgcn_exp2f(mo - mn);
+        mg = mn;
+    };
+#pragma unroll
+    for (int o = 16; o < 64; o <<= 1) comb(m, l, __shfl_xor(m, o, 64), __shfl_xor(l, o, 64));
+    __shared__ float pm[4][kG], pl[4][kG];
+    if (owner && lane < 16) {
+        pm[wave][hl] = m;
+        pl[wave][hl] = l;
+    }
+    __syncthreads();
+    if (threadIdx.x < gcount) {
+        const int g = threadIdx.x;
+        float mg = -INFINITY, lg = 0.f;
+        for (int w = 0; w < 4; ++w) comb(mg, lg, pm[w][g], pl[w][g]);
+        const int64_t h = kvh * G + g0 + g;
+        a.part[(h * a.nchunks + blockIdx.x) * 2 + 0] = mg;
+        a.part[(h * a.nchunks + blockIdx.x) * 2 + 1] = lg;
+    }
+}
+
+// Dense log2-sum-exp of each q head from its chunks' partials (one wave per head).
+__global__ __launch_bounds__(64) void decode_stats_kernel(DecodeArgs a) {
+    const int h = blockIdx.x, lane = threadIdx.x;
+    float m = -INFINITY, l = 0.f;
+    for (int c = lane; c < a.nchunks; c += 64) {
+        const float mc = a.part[((int64_t)h * a.nchunks + c) * 2], lc = a.part[((int64_t)h * a.nchunks + c) * 2 + 1];
+        const float mn = fmaxf(m, mc);
+        l = (mn == -INFINITY) ? 0.f : l * __builtin_amdgcn_exp2f(m - mn) + lc * __builtin_amdgcn_exp2f(mc - mn);
+        m = mn;
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const float mo = __shfl_xor(m, o, 64), lo = __shfl_xor(l, o, 64);
+        const float mn = fmaxf(m, mo);
+        l = (mn == -INFINITY) ? 0.f : l * __builtin_amdgcn_exp2f(m - mn) + lo * __builtin_amdgcn_exp2f(mo - mn);
+        m = mn;
+    }
+    if (lane == 0) a.lse2_all[h] = l > 0.f ? m + __log2f(l) : -INFINITY;
+}
+
+// One workgroup per q head: softmax over the selected keys' scores and the
+// weighted sum of their V rows (16 lanes per row, 16 rows per step).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void decode_attend_kernel(DecodeArgs a) {
+    const int h = blockIdx.x;
+    const int G = a.hq / a.hkv;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = (lane & 15) * 8, slot = wave * 4 + (lane >> 4);   // 16 row slots
+    const int32_t *idx = a.idx + (int64_t)h * a.topk;
+    const uint32_t *keys = a.keys + (int64_t)h * a.n;
+    __shared__ float red[kThreads / 64];
+    // the selected scores' maximum
+    float mx = -INFINITY;
+    for (int t = threadIdx.x; t < a.topk; t += kThreads) {
+        const int64_t j = min(max((int64_t)idx[t], (int64_t)0), a.n - 1);
+        mx = fmaxf(mx, key_score(keys[j]));
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    const T *vp = reinterpret_cast<const T *>(a.v) + (int64_t)(h / G) * a.stride * kD;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float lsum = 0.f;
+    for (int tb = slot; tb < a.topk; tb += 16 * kU) {
+        // kU rows per slot per step, their loads issued together
+        float vx[kU][8], p[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int t = tb + 16 * u;
+            p[u] = 0.f;
+            if (t < a.topk) {
+                const int64_t j = min(max((int64_t)idx[t], (int64_t)0), a.n - 1);
+                p[u] = __builtin_amdgcn_exp2f(key_score(keys[j]) - mx);
+                load8<T>(vp + j * kD + col, vx[u]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vx[u][e] = 0.f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = fmaf(p[u], vx[u][e], acc[e]);
+            lsum += p[u];                             // the same p in all 16 lanes of the slot
+        }
+    }
+    // sum the 16 slots: rows of each column slice in LDS, then one thread per column
+    __shared__ float part[16][kD];
+    __shared__ float lpart[16];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[slot][col + e] = acc[e];
+    if ((lane & 15) == 0) lpart[slot] = lsum;
+    __syncthreads();
+    if (threadIdx.x < kD) {
+        float o = 0.f, ls = 0.f;
+        for (int r = 0; r < 16; ++r) {
+            o += part[r][threadIdx.x];
+            ls += lpart[r];
+        }
+        const float inv = ls > 0.f ? 1.f / ls : 0.f;
+        T *op = reinterpret_cast<T *>(a.out) + (int64_t)h * kD + threadIdx.x;
+        if constexpr (sizeof(T) == 2) {
+            reinterpret_cast<uint16_t *>(op)[0] = f32_to_bf16(o * inv);
+        } else {
+            *reinterpret_cast<float *>(op) = o * inv;
+        }
+        if (threadIdx.x == 0) {
+            const float lse2 = ls > 0.f ? mx + __log2f(ls) : -INFINITY;
+            if (a.lse != nullptr) a.lse[h] = lse2 * kLn2;
+            if (a.recovery != nullptr) {
+                const float all = a.lse2_all[h];
+                a.recovery[h] = (ls > 0.f && all != -INFINITY) ? __builtin_amdgcn_exp2f(lse2 - all) : 0.f;
+            }
+        }
+    }
+}
+
+}  // namespace
+
+template <typename T> void launch_scores_group(const DecodeArgs &a, int g0, int gcount, hipStream_t s) {
+    const dim3 grid((unsigned)a.nchunks, (unsigned)a.hkv);
+    if (gcount <= 4)
+        hipLaunchKernelGGL((decode_scores_kernel<T, 4>), grid, dim3(kThreads), 0, s, a, g0);
+    else
+        hipLaunchKernelGGL((decode_scores_kernel<T, 8>), grid, dim3(kThreads), 0, s, a, g0);
+}
+
+hipError_t launch_decode_scores(const DecodeArgs &a, int dtype, hipStream_t s) {
+    const int G = a.hq / a.hkv;
+    for (int g0 = 0; g0 < G; g0 += kMaxG) {
+        const int gcount = G - g0 < kMaxG ? G - g0 : kMaxG;
+        if (dtype == 0)
+            launch_scores_group<bf16>(a, g0, gcount, s);
+        else
+            launch_scores_group<float>(a, g0, gcount, s);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(decode_stats_kernel, dim3((unsigned)a.hq), dim3(64), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_attend(const DecodeArgs &a, int dtype, hipStream_t s) {
+    if (dtype == 0)
+        hipLaunchKernelGGL(decode_attend_kernel<bf16>, dim3((unsigned)a.hq), dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL(decode_attend_kernel<float>, dim3((unsigned)a.hq), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace msa

@@ -101,11 +101,34 @@ struct TopkArgs {
     uint32_t *state;             // [2*hq][4]
     uint32_t *cnt;               // [2*hq][nslices][2]
     uint32_t *off;               // [2*hq][nslices][2]
+    int32_t rows;                // rows selected: 0 = 2*hq (both sets); else the first rows, all from src0
 };
 
 constexpr int kTopkSlice = 4096;   // elements per top-k workgroup slice
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
+
+// Decode-side top-k attention: one query row per q head over a cache of n keys.
+struct DecodeArgs {
+    const void *q;               // [hq][128]
+    const void *k, *v;           // [hkv][stride][128]
+    void *out;                   // [hq][128]
+    float *lse;                  // [hq] natural log over the selected keys (NULL: not written)
+    float *recovery;             // [hq] share of the dense attention mass selected (NULL: not written)
+    int32_t hq, hkv;
+    int64_t n, stride;
+    float scale_log2;
+    int32_t topk;
+    const int32_t *idx;          // [hq][topk] the selected keys
+    uint32_t *keys;              // [hq][n] order-preserving keys of the scores (log2 units)
+    float *part;                 // [hq][nchunks][2] running max and sum of 2^s per key chunk
+    float *lse2_all;             // [hq] dense log2-sum-exp
+    int64_t chunk_keys;
+    int32_t nchunks;
+};
+
+hipError_t launch_decode_scores(const DecodeArgs &a, int dtype, hipStream_t s);
+hipError_t launch_decode_attend(const DecodeArgs &a, int dtype, hipStream_t s);
 
 struct IndexArgs {
     const int32_t *v_idx, *s_idx;

@@ -176,7 +176,39 @@ int run_estimate_vs(const msa_problem *p, const void *q, const void *k, int32_t 
     t.state = at<uint32_t>(workspace, L.off_state);
     t.cnt = at<uint32_t>(workspace, L.off_cnt);
     t.off = at<uint32_t>(workspace, L.off_off);
+    t.rows = 0;
     return launch_status(msa::launch_topk(t, s), "top-k");
+}
+
+// Workspace of msa_decode_sparse: score keys, chunk partials, dense lse, and
+// the top-k select's histograms and counters.
+struct DecodeLayout {
+    int64_t chunk_keys;
+    int32_t nchunks, nslices;
+    size_t off_keys, off_part, off_lse, off_hist, off_state, off_cnt, off_off, total;
+};
+
+DecodeLayout decode_layout(const msa_problem *p) {
+    DecodeLayout L;
+    const int64_t n = p->seq_len;
+    // about 2048 workgroups per pass over the caches, at least 1024 keys each
+    int64_t ck = (n * p->n_kv_heads + 2047) / 2048;
+    ck = ((ck + 1023) / 1024) * 1024;
+    if (ck < 1024) ck = 1024;
+    L.chunk_keys = ck;
+    L.nchunks = (int32_t)((n + ck - 1) / ck);
+    L.nslices = (int32_t)((n + msa::kTopkSlice - 1) / msa::kTopkSlice);
+    const size_t hq = (size_t)p->n_q_heads;
+    size_t o = 0;
+    L.off_keys = o;  o = align_up(o + hq * (size_t)n * 4);
+    L.off_part = o;  o = align_up(o + hq * (size_t)L.nchunks * 2 * 4);
+    L.off_lse = o;   o = align_up(o + hq * 4);
+    L.off_hist = o;  o = align_up(o + hq * 2048 * 4);
+    L.off_state = o; o = align_up(o + hq * 4 * 4);
+    L.off_cnt = o;   o = align_up(o + hq * (size_t)L.nslices * 2 * 4);
+    L.off_off = o;   o = align_up(o + hq * (size_t)L.nslices * 2 * 4);
+    L.total = o;
+    return L;
 }
 
 // Scratch of msa_estimate_vs_noalloc: device memory of the library itself, one
@@ -450,6 +482,65 @@ int msa_sparse_prefill_fused(const msa_problem *p, const void *q, const void *k,
     }
     return launch_status(msa::launch_sparse_prefill_fused(a, p->dtype, exact, reinterpret_cast<hipStream_t>(stream)),
                          "sparse_prefill_fused");
+}
+
+size_t msa_decode_sparse_workspace(const msa_problem *p) {
+    if (check_problem(p) != MSA_OK) return 0;
+    return decode_layout(p).total;
+}
+
+int msa_decode_sparse(const msa_problem *p, const void *q, const void *k, const void *v, int32_t topk,
+                      int32_t *idx, int32_t flags, void *workspace, size_t workspace_bytes, void *out, float *lse,
+                      float *recovery, void *stream) {
+    int st = check_problem(p);
+    if (st) return st;
+    if (!q || !k || !v || !out || !idx) return fail(MSA_ERR_NULL, "a required pointer is NULL");
+    if ((st = check_rows(q, k, v, out))) return st;
+    if ((flags & ~MSA_DECODE_GIVEN_KEYS) != 0) return fail(MSA_ERR_RANGE, "unknown flags 0x%x", (unsigned)flags);
+    if (topk < 1 || topk > p->seq_len) return fail(MSA_ERR_RANGE, "topk must lie in [1, seq_len] (got %d)", topk);
+    if (off_align(idx, 4) || off_align(lse, 4) || off_align(recovery, 4))
+        return fail(MSA_ERR_RANGE, "idx, lse and recovery must be 4-byte aligned");
+    const DecodeLayout L = decode_layout(p);
+    if (!workspace) return fail(MSA_ERR_NULL, "workspace is NULL (%zu bytes needed)", L.total);
+    if (workspace_bytes < L.total) return fail(MSA_ERR_WORKSPACE, "workspace %zu bytes, %zu needed", workspace_bytes, L.total);
+    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return fail(MSA_ERR_RANGE, "workspace is not 16-byte aligned");
+    msa::DecodeArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.lse = lse;
+    a.recovery = recovery;
+    a.hq = p->n_q_heads;
+    a.hkv = p->n_kv_heads;
+    a.n = p->seq_len;
+    a.stride = stride_of(p);
+    a.scale_log2 = scale_of(p) * msa::kLog2e;
+    a.topk = topk;
+    a.idx = idx;
+    a.keys = at<uint32_t>(workspace, L.off_keys);
+    a.part = at<float>(workspace, L.off_part);
+    a.lse2_all = at<float>(workspace, L.off_lse);
+    a.chunk_keys = L.chunk_keys;
+    a.nchunks = L.nchunks;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if ((st = launch_status(msa::launch_decode_scores(a, p->dtype, s), "decode scores"))) return st;
+    if ((flags & MSA_DECODE_GIVEN_KEYS) == 0) {
+        msa::TopkArgs t;
+        t.src0 = t.src1 = reinterpret_cast<const float *>(a.keys);
+        t.dst0 = t.dst1 = idx;
+        t.k0 = t.k1 = topk;
+        t.hq = p->n_q_heads;
+        t.rows = p->n_q_heads;
+        t.n = p->seq_len;
+        t.nslices = L.nslices;
+        t.hist = at<uint32_t>(workspace, L.off_hist);
+        t.state = at<uint32_t>(workspace, L.off_state);
+        t.cnt = at<uint32_t>(workspace, L.off_cnt);
+        t.off = at<uint32_t>(workspace, L.off_off);
+        if ((st = launch_status(msa::launch_topk(t, s), "decode top-k"))) return st;
+    }
+    return launch_status(msa::launch_decode_attend(a, p->dtype, s), "decode attend");
 }
 
 int msa_sparse_prefill_walk_marks(const msa_problem *p, int32_t phase_keys, size_t *offset,

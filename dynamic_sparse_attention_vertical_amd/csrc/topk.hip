@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void topk_write_kernel(TopkArgs a) {
 }  // namespace
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
-    const int rows = 2 * a.hq;
+    const int rows = a.rows > 0 ? a.rows : 2 * a.hq;
     hipError_t e;
     hipLaunchKernelGGL(topk_init_kernel, dim3(rows), dim3(kThreads), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -51,6 +51,9 @@ _SIGS = {
                                           _VP, ctypes.c_size_t, _VP, _VP, _VP]),
     "msa_sparse_prefill_workspace": (ctypes.c_size_t, [_VP, _I32]),
     "msa_sparse_prefill_fused_workspace": (ctypes.c_size_t, [_VP, _I32, _I32, _I32]),
+    "msa_decode_sparse_workspace": (ctypes.c_size_t, [_VP]),
+    "msa_decode_sparse": (ctypes.c_int, [_VP, _VP, _VP, _VP, _I32, _VP, _I32, _VP, ctypes.c_size_t, _VP, _VP, _VP,
+                                         _VP]),
     "msa_sparse_prefill_walk_marks": (ctypes.c_int, [_VP, _I32, _VP, _VP]),
     "msa_sparse_prefill_fused": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I32, _VP, _I32, _I32, _I32, _VP,
                                                 ctypes.c_size_t, _VP, _VP, _VP]),
@@ -450,6 +453,73 @@ def sparse_prefill_fused(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, v_id
                                         _rows_dev(lse, "lse", p, q, True) if want_lse else None, _stream(stream)),
            "msa_sparse_prefill_fused")
     return (out, lse) if want_lse else out
+
+
+DECODE_GIVEN_KEYS = 1
+
+
+def decode_sparse_workspace_bytes(n_q_heads: int, n_kv_heads: int, cache_len: int, dtype=torch.bfloat16) -> int:
+    """Workspace bytes of decode_sparse."""
+    p = problem(n_q_heads, n_kv_heads, cache_len, MSA_BF16 if dtype == torch.bfloat16 else MSA_F32)
+    return int(load().msa_decode_sparse_workspace(ctypes.byref(p)))
+
+
+@on_stream
+def decode_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, topk: int, *, idx: torch.Tensor | None = None,
+                  given: bool = False, out: torch.Tensor | None = None, lse: torch.Tensor | bool | None = None,
+                  recovery: torch.Tensor | bool | None = None, sm_scale: float = 0.0,
+                  workspace: torch.Tensor | None = None, stream=None):
+    """One decode step: q [Hq, 128] (one row per head) against the caches k, v
+    [Hkv, N, 128] (rows may be strided), attending only to the top-k keys of
+    each head by score (idx receives them, ascending) or, with given=True, to
+    the keys in idx.  Returns out [Hq, 128] and idx, plus lse and recovery (the
+    selected share of the dense attention mass) when asked for (True or a
+    tensor)."""
+    lib = load()
+    if q.dim() != 2 or q.shape[1] != HEAD_DIM or not q.is_contiguous():
+        raise MsaError(f"q must be contiguous [heads, {HEAD_DIM}]")
+    if k.dim() != 3 or v.dim() != 3 or k.shape != v.shape:
+        raise MsaError("k and v must be caches of the same shape [kv heads, cache_len, head_dim]")
+    for t, name in ((k, "k"), (v, "v")):
+        if t.dtype != q.dtype or t.device != q.device:
+            raise MsaError(f"{name} must have q's dtype and device")
+    hq, hk, n = q.shape[0], k.shape[0], k.shape[1]
+    sk, sv = _head_stride(k, "k"), _head_stride(v, "v")
+    if hk > 1 and sk != sv:
+        raise MsaError("k and v must have the same head stride")
+    p = problem(hq, hk, n, _dtype_code(q), sm_scale, 0 if sk == n else sk)
+    if idx is None:
+        if given:
+            raise MsaError("given=True needs idx")
+        idx = torch.empty((hq, topk), dtype=torch.int32, device=q.device)
+    if idx.dtype != torch.int32 or tuple(idx.shape) != (hq, topk) or not idx.is_contiguous():
+        raise MsaError(f"idx must be contiguous int32 [{hq}, {topk}]")
+    if out is None:
+        out = torch.empty((hq, HEAD_DIM), dtype=q.dtype, device=q.device)
+    if tuple(out.shape) != (hq, HEAD_DIM) or out.dtype != q.dtype or not out.is_contiguous():
+        raise MsaError(f"out must be contiguous {q.dtype} [{hq}, {HEAD_DIM}]")
+    extra = []
+    for t, name in ((lse, "lse"), (recovery, "recovery")):
+        if t is True:
+            t = torch.empty(hq, dtype=torch.float32, device=q.device)
+        if t is not None and t is not False:
+            if t.dtype != torch.float32 or tuple(t.shape) != (hq,) or not t.is_contiguous():
+                raise MsaError(f"{name} must be contiguous float32 [{hq}]")
+            extra.append(t)
+        else:
+            extra.append(None)
+    need = int(lib.msa_decode_sparse_workspace(ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(lib.msa_decode_sparse(ctypes.byref(p), _dev(q, "q"), _in_dev(k, "k"), _in_dev(v, "v"), topk,
+                                 _dev(idx, "idx"), DECODE_GIVEN_KEYS if given else 0, _dev(workspace, "workspace"),
+                                 workspace.numel() * workspace.element_size(), _dev(out, "out"),
+                                 _dev(extra[0], "lse") if extra[0] is not None else None,
+                                 _dev(extra[1], "recovery") if extra[1] is not None else None, _stream(stream)),
+           "msa_decode_sparse")
+    res = [out, idx]
+    res += [t for t, want in zip(extra, (lse, recovery)) if want is not None and want is not False]
+    return tuple(res)
 
 
 @on_stream

@@ -301,6 +301,35 @@ int msa_estimate_bs(const msa_problem *p, const void *q, const void *k, int32_t 
                     int32_t cap_blocks, int32_t *column_count, void *workspace,
                     size_t workspace_bytes, void *stream);
 
+/* Decode-side dynamic sparsity: one new query row per q head attends only to
+ * the top-k cached keys by attention score, chosen anew at every call (talk
+ * slides "System-Algorithm Co-design", slide "Dynamic sparsity in
+ * attention", decoding panel: choosing the top-1000 keys of a 100K-token
+ * cache dynamically keeps more of the attention mass than a static choice).
+ *   p: seq_len = N cached keys; n_q_heads, n_kv_heads, dtype, sm_scale and
+ *      seq_stride (rows between cache heads) as for prefill.  A batch of
+ *      sequences is folded into the heads (n_q_heads = batch * Hq with the
+ *      caches as batch * Hkv heads, Hq / Hkv per group as always).
+ *   q [n_q_heads, 128] (one row per head, 16-byte aligned); k, v caches
+ *      [n_kv_heads, stride, 128]; out [n_q_heads, 128] (dtype).
+ *   topk in [1, N]; idx [n_q_heads, topk] int32: written with the selected
+ *      keys, ascending, exact top-k of s[h, j] = sm_scale <q_h, k_j> (ties to
+ *      the lower index) -- or, with flags = MSA_DECODE_GIVEN_KEYS, read as the
+ *      caller's own selection (a static pattern, say; entries are clamped into
+ *      [0, N), a key given twice counts twice).
+ *   lse [n_q_heads] (optional): natural log-sum-exp of the selected scores;
+ *   recovery [n_q_heads] (optional): the selected keys' share of the dense
+ *      attention mass, sum over selected e^s / sum over all e^s.
+ *   workspace: msa_decode_sparse_workspace(p) bytes, 16-byte aligned, no
+ *      initial contents assumed.
+ * Errors as for every call; topk out of range or unknown flags:
+ * MSA_ERR_RANGE.                                                           */
+#define MSA_DECODE_GIVEN_KEYS 1
+size_t msa_decode_sparse_workspace(const msa_problem *p);
+int msa_decode_sparse(const msa_problem *p, const void *q, const void *k, const void *v, int32_t topk,
+                      int32_t *idx, int32_t flags, void *workspace, size_t workspace_bytes, void *out, float *lse,
+                      float *recovery, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,6 +29,11 @@ state):
   index.exact_union_rows   (the vertical-slash pattern as the talk slides
                            draw it, slide "Dynamic sparsity in attention");
                            the second gives given rows only.
+  decode.*                 one decode query row per head over a key cache:
+                           scores, attention over the top-k keys (or a given
+                           set) and the kept share of the dense attention mass
+                           (talk slides, slide "Dynamic sparsity in attention",
+                           decoding panel).
   attention.*              softmax attention restricted to an explicit boolean
                            mask (dense causal when every column and diagonal is
                            selected); attention_recall, the share of each
@@ -43,11 +48,12 @@ from .index import (build_index, a_shape_sets, index_mask, exact_union_mask, exa
                     block_key_sets, IndexArrays)
 from .attention import (attention_with_mask, masked_attention_blocks, exact_attention_blocks,
                         dense_attention_blocks, dense_attention, attention_recall)
+from .decode import decode_scores, decode_sparse_attention
 
 __all__ = [
     "estimate_vs", "top_k_indices", "block_sparse_select", "block_scores",
     "build_index", "a_shape_sets", "index_mask", "exact_union_mask", "exact_union_rows", "block_key_sets",
     "IndexArrays",
     "attention_with_mask", "masked_attention_blocks", "exact_attention_blocks", "dense_attention_blocks",
-    "dense_attention",
+    "dense_attention", "attention_recall", "decode_scores", "decode_sparse_attention",
 ]

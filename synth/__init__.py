@@ -6,6 +6,7 @@ the method's arithmetic, so both the CPU oracle and the GPU path can consume the
 same tensors without sharing any code.
 """
 
-from .gen import WORKLOADS, Workload, make_inputs, small_workload, rope_tables
+from .gen import (WORKLOADS, DECODE_WORKLOADS, DecodeWorkload, Workload, make_decode_inputs, make_inputs,
+                  small_workload, rope_tables)
 
 __all__ = ["WORKLOADS", "Workload", "make_inputs", "small_workload", "rope_tables"]

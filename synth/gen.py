@@ -92,6 +92,43 @@ WORKLOADS = {
 }
 
 
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """One decode step over a batch of key caches: batch sequences of
+    cache_len cached tokens, each with the layer's q / kv heads; the decode
+    query of a sequence is the last query row of its synthetic prefill."""
+    name: str
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    cache_len: int
+    topk: int
+    seed: int = 0
+
+    def prefill(self, b: int) -> Workload:
+        return Workload(f"{self.name}_{b}", self.n_q_heads, self.n_kv_heads, self.cache_len, seed=self.seed + b)
+
+
+DECODE_WORKLOADS = {
+    # LLaMA-3-8B attention shape decoding over 100K cached tokens, top-1000
+    # keys per head (the talk slides' decoding panel), 8 sequences at once
+    "llama3_8b_decode_100k": DecodeWorkload("llama3_8b_decode_100k", 8, 32, 8, 100000, 1000, seed=2001),
+}
+
+
+def make_decode_inputs(dw: DecodeWorkload, device: str = "cpu") -> dict:
+    """q [batch * Hq, D] (each sequence's last query row), k and v caches
+    [batch * Hkv, cache_len, D], bfloat16; sequences folded into the heads."""
+    qs, ks, vs = [], [], []
+    for b in range(dw.batch):
+        x = make_inputs(dw.prefill(b), device=device)
+        qs.append(x["q"][:, -1].clone())
+        ks.append(x["k"])
+        vs.append(x["v"])
+        del x
+    return {"q": torch.cat(qs).contiguous(), "k": torch.cat(ks), "v": torch.cat(vs)}
+
+
 def small_workload(name: str = "small", **kw) -> Workload:
     """A test-sized workload (same recipe, smaller shapes)."""
     base = dict(n_q_heads=4, n_kv_heads=1, seq_len=1024, vertical_topk=64, slash_topk=128,

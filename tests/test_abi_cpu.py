@@ -30,7 +30,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -196,6 +196,24 @@ def test_sparse_prefill_fused_workspace_size(lib):
     assert lib.msa_sparse_prefill_fused_workspace(P(n=1 << 17), -1, 0, 0) == 0
     assert lib.msa_sparse_prefill_fused_workspace(P(n=1 << 17), 8, 100, 0) == 0      # invalid phase length
     assert lib.msa_sparse_prefill_fused_workspace(P(n=1 << 17), 8, 0, 4) == 0        # unknown flag
+
+
+def test_decode_sparse_validation(lib):
+    call = lambda prob, topk=8, idx=FAKE, flags=0, ws=FAKE, wsb=1 << 30, lse=None, rec=None: lib.msa_decode_sparse(
+        prob, FAKE, FAKE, FAKE, topk, idx, flags, ws, wsb, FAKE, lse, rec, None)
+    need = lib.msa_decode_sparse_workspace(P())
+    # scores as 32-bit keys for every (q head, cached key), top-k histograms
+    assert need >= 32 * 4096 * 4 + 32 * 2048 * 4
+    assert call(P(), topk=0) == RANGE
+    assert call(P(), topk=4097) == RANGE
+    assert call(P(), flags=2) == RANGE
+    assert call(P(), idx=None) == NULL
+    assert call(P(), ws=None) == NULL
+    assert call(P(), wsb=need - 1) == WS
+    assert call(P(), ws=ctypes.c_void_p(0x1004), wsb=need) == RANGE
+    assert call(P(), idx=ctypes.c_void_p(0x1002)) == RANGE
+    assert call(P(hq=6, hkv=4)) == SHAPE
+    assert lib.msa_decode_sparse_workspace(P(d=64)) == 0
 
 
 def test_walk_marks_query(lib):

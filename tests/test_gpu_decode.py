@@ -1,0 +1,134 @@
+"""GPU parity of the decode-side top-k attention (msa_decode_sparse) against
+the float64 oracle (oracle.decode_sparse_attention): the selected key sets
+exactly, except keys whose oracle score lies within 1e-4 of the k-th largest
+(the fp32 / fp64 tie band); outputs, lse and the kept share of the attention
+mass on the GPU's own sets at the graded tolerances.  Every call goes through
+the C ABI."""
+
+import numpy as np
+import pytest
+import torch
+
+import dynamic_sparse_attention_vertical_amd as msa
+import oracle
+from parity import compare_out
+from synth import WORKLOADS, make_inputs, small_workload
+
+pytestmark = pytest.mark.gpu
+
+SCORE_BAND = 1e-4     # absolute, on sm_scale * <q, k>
+LSE_ATOL = 1e-4
+REC_ATOL = 1e-5
+
+
+def cache(hq, hkv, n, seed, fp32=False):
+    """Decode inputs of the synthetic recipe: the caches are a prefill's K and
+    V, the decode queries its last query row."""
+    w = small_workload(n_q_heads=hq, n_kv_heads=hkv, seq_len=n, seed=seed,
+                       dtypes=("fp32", "bf16") if fp32 else ("bf16",))
+    x = make_inputs(w)
+    sfx = "32" if fp32 else ""
+    return x["q" + sfx][:, -1].contiguous(), x["k" + sfx], x["v" + sfx]
+
+
+def check_sets(idx, s, topk, what):
+    """idx [Hq, topk] ascending; every key scoring above the k-th largest
+    (by more than the band) chosen, none scoring below it by more."""
+    for h in range(s.shape[0]):
+        got = idx[h]
+        assert len(np.unique(got)) == topk and np.all(np.diff(got) > 0), f"{what} h{h}: not ascending distinct"
+        kth = np.sort(s[h])[::-1][topk - 1]
+        must = np.nonzero(s[h] > kth + SCORE_BAND)[0]
+        assert np.isin(must, got).all(), f"{what} h{h}: a key above the band is missing"
+        assert np.all(s[h][got] >= kth - SCORE_BAND), f"{what} h{h}: a key below the band was chosen"
+
+
+def check_decode(q, k, v, topk, fp32, what, given=None):
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    if given is None:
+        out, idx, lse, rec = msa.decode_sparse(qd, kd, vd, topk, lse=True, recovery=True)
+    else:
+        out, idx, lse, rec = msa.decode_sparse(qd, kd, vd, topk, idx=given.cuda(), given=True, lse=True,
+                                               recovery=True)
+    idx = idx.cpu().numpy()
+    s = oracle.decode_scores(q, k)
+    if given is None:
+        check_sets(idx, s, topk, what)
+    else:
+        np.testing.assert_array_equal(idx, given.numpy())
+    ro, rl, rr, _ = oracle.decode_sparse_attention(q, k, v, topk, idx=idx)
+    compare_out(out.float().cpu().numpy(), ro, fp32, what)
+    np.testing.assert_allclose(lse.cpu().numpy(), rl, rtol=0, atol=LSE_ATOL, err_msg=what)
+    np.testing.assert_allclose(rec.cpu().numpy(), rr, rtol=0, atol=REC_ATOL, err_msg=what)
+    return out, idx, rec.cpu().numpy()
+
+
+@pytest.mark.parametrize("hq,hkv,n,topk,fp32", [
+    (4, 1, 1000, 100, False),
+    (8, 2, 4096 + 37, 300, False),     # ragged: the last score chunk and top-k slice are partial
+    (6, 2, 2500, 64, False),           # GQA group of 3
+    (16, 1, 2048, 128, False),         # group of 16: two scoring passes over K
+    (2, 2, 777, 1, False),             # one key
+    (2, 1, 513, 513, False),           # every key: dense decode attention
+    (4, 2, 1500, 200, True),           # fp32
+])
+def test_decode_topk(hq, hkv, n, topk, fp32):
+    q, k, v = cache(hq, hkv, n, seed=n + topk, fp32=fp32)
+    _, _, rec = check_decode(q, k, v, topk, fp32, f"decode {hq}/{hkv} n={n} k={topk}")
+    if topk == n:
+        np.testing.assert_allclose(rec, 1.0, atol=REC_ATOL)
+
+
+def test_decode_static_set_keeps_less():
+    """A static choice (the first 16 keys and the last topk - 16) against the
+    dynamic top-k of the same size: the dynamic set keeps at least as much of
+    every head's attention mass (the top-k maximise the kept share), and both
+    match the oracle."""
+    hq, hkv, n, topk = 8, 2, 3000, 200
+    q, k, v = cache(hq, hkv, n, seed=9)
+    _, _, rec_dyn = check_decode(q, k, v, topk, False, "dynamic")
+    static = np.r_[np.arange(16), np.arange(n - (topk - 16), n)].astype(np.int32)
+    given = torch.from_numpy(np.tile(static, (hq, 1)))
+    _, _, rec_st = check_decode(q, k, v, topk, False, "static", given=given)
+    assert np.all(rec_dyn >= rec_st - REC_ATOL)
+
+
+def test_decode_strided_cache_and_batch():
+    """Caches inside a longer buffer (rows between heads = the buffer's
+    length), and a batch of two sequences folded into the heads."""
+    hq, hkv, n, cap, topk = 4, 2, 900, 1200, 50
+    qa, ka, va = cache(hq, hkv, n, seed=21)
+    qb, kb, vb = cache(hq, hkv, n, seed=22)
+    kbuf = torch.zeros((2 * hkv, cap, 128), dtype=ka.dtype)
+    vbuf = torch.zeros((2 * hkv, cap, 128), dtype=va.dtype)
+    kbuf[:hkv, :n], kbuf[hkv:, :n] = ka, kb
+    vbuf[:hkv, :n], vbuf[hkv:, :n] = va, vb
+    q = torch.cat([qa, qb])
+    out, idx, lse, rec = msa.decode_sparse(q.cuda(), kbuf.cuda()[:, :n], vbuf.cuda()[:, :n], topk, lse=True,
+                                           recovery=True)
+    for part, (qq, kk, vv) in enumerate(((qa, ka, va), (qb, kb, vb))):
+        rows = slice(part * hq, (part + 1) * hq)
+        i = idx[rows].cpu().numpy()
+        check_sets(i, oracle.decode_scores(qq, kk), topk, f"batch {part}")
+        ro, rl, rr, _ = oracle.decode_sparse_attention(qq, kk, vv, topk, idx=i)
+        compare_out(out[rows].float().cpu().numpy(), ro, False, f"batch {part}")
+        np.testing.assert_allclose(lse[rows].cpu().numpy(), rl, atol=LSE_ATOL)
+        np.testing.assert_allclose(rec[rows].cpu().numpy(), rr, atol=REC_ATOL)
+
+
+def test_decode_128k_cache():
+    """The 128K workload's caches (32 q heads, 8 kv heads, 131,072 keys), the
+    top-1000 keys per head, every head against the oracle."""
+    w = WORKLOADS["llama3_8b_128k"]
+    x = make_inputs(w, device="cuda")
+    q = x["q"][:, -1].contiguous()
+    out, idx, lse, rec = msa.decode_sparse(q, x["k"], x["v"], 1000, lse=True, recovery=True)
+    torch.cuda.synchronize()
+    qc, kc, vc = q.cpu(), x["k"].cpu(), x["v"].cpu()
+    i = idx.cpu().numpy()
+    check_sets(i, oracle.decode_scores(qc, kc), 1000, "128K")
+    ro, rl, rr, _ = oracle.decode_sparse_attention(qc, kc, vc, 1000, idx=i)
+    compare_out(out.float().cpu().numpy(), ro, False, "128K")
+    np.testing.assert_allclose(lse.cpu().numpy(), rl, atol=LSE_ATOL)
+    np.testing.assert_allclose(rec.cpu().numpy(), rr, atol=REC_ATOL)
+    print(f"128K decode: kept share of the attention mass, top-1000: mean {rr.mean():.3f}, min {rr.min():.3f}")

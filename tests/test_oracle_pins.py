@@ -525,3 +525,95 @@ def test_block_sparse_topk_picks_best_blocks():
 def test_index_caps():
     assert index_caps(1 << 20, 1000, 6096) == (6096, 1000)
     assert index_caps(4096, 64, 256) == (64, 64)
+
+
+def _brute_decode(q, k, v, topk, scale):
+    """Plain loops: scores, the top-k by score (ties to the lower index),
+    softmax over them, the weighted V sum and the kept share of e^s."""
+    Hq, D = q.shape
+    G = Hq // k.shape[0]
+    N = k.shape[1]
+    outs, lses, recs, idxs = [], [], [], []
+    for h in range(Hq):
+        g = h // G
+        s = [scale * sum(float(q[h, d]) * float(k[g, j, d]) for d in range(D)) for j in range(N)]
+        order = sorted(range(N), key=lambda j: (-s[j], j))[:topk]
+        sel = sorted(order)
+        m = max(s[j] for j in sel)
+        w = [math.exp(s[j] - m) for j in sel]
+        tot = sum(w)
+        outs.append([sum(w[t] * float(v[g, sel[t], d]) for t in range(len(sel))) / tot for d in range(D)])
+        lses.append(m + math.log(tot))
+        m_all = max(s)
+        recs.append(tot * math.exp(m - m_all) / sum(math.exp(x - m_all) for x in s))
+        idxs.append(sel)
+    return np.array(outs), np.array(lses), np.array(recs), np.array(idxs)
+
+
+@pytest.mark.parametrize("hq,hkv,n,d,topk,seed", [(2, 1, 9, 4, 3, 0), (4, 2, 13, 3, 5, 1), (3, 3, 7, 5, 7, 2)])
+def test_decode_sparse_brute_force(hq, hkv, n, d, topk, seed):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((hq, d))
+    k = rng.standard_normal((hkv, n, d))
+    v = rng.standard_normal((hkv, n, d))
+    k[:, 2] = k[:, 5]                                  # equal scores: the tie goes to the lower index
+    out, lse, rec, idx = oracle.decode_sparse_attention(q, k, v, topk, scale=0.7)
+    bo, bl, br, bi = _brute_decode(q, k, v, topk, 0.7)
+    np.testing.assert_array_equal(idx, bi)
+    np.testing.assert_allclose(out, bo, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, bl, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(rec, br, rtol=1e-12, atol=1e-12)
+
+
+def test_decode_sparse_closed_forms():
+    """All keys: the dense attention of the last row of a causal prefill whose
+    last query is q, recovery 1.  One key: V at the highest score, lse = that
+    score, recovery = its softmax weight.  A zero query: every score 0, so the
+    first k keys (ties to the lower index), their mean V, recovery k / N."""
+    rng = np.random.default_rng(3)
+    hq, hkv, n, d = 4, 2, 40, 16
+    q = rng.standard_normal((hq, d))
+    k = rng.standard_normal((hkv, n, d))
+    v = rng.standard_normal((hkv, n, d))
+    out, lse, rec, idx = oracle.decode_sparse_attention(q, k, v, n)
+    qf = np.zeros((hq, n, d))
+    qf[:, -1] = q
+    dense, dlse = oracle.dense_attention(qf, k, v)
+    np.testing.assert_allclose(out, dense[:, -1], atol=1e-12)
+    np.testing.assert_allclose(lse, dlse[:, -1], atol=1e-12)
+    np.testing.assert_allclose(rec, 1.0, atol=1e-12)
+    s = oracle.decode_scores(q, k)
+    out, lse, rec, idx = oracle.decode_sparse_attention(q, k, v, 1)
+    G = hq // hkv
+    for h in range(hq):
+        j = int(np.argmax(s[h]))
+        assert idx[h, 0] == j
+        np.testing.assert_allclose(out[h], v[h // G, j], atol=1e-12)
+        np.testing.assert_allclose(lse[h], s[h, j], atol=1e-12)
+        np.testing.assert_allclose(rec[h], np.exp(s[h, j]) / np.exp(s[h]).sum(), atol=1e-12)
+    out, lse, rec, idx = oracle.decode_sparse_attention(np.zeros((hq, d)), k, v, 7)
+    np.testing.assert_array_equal(idx, np.tile(np.arange(7), (hq, 1)))
+    for h in range(hq):
+        np.testing.assert_allclose(out[h], v[h // G, :7].mean(axis=0), atol=1e-12)
+    np.testing.assert_allclose(rec, 7 / n, atol=1e-12)
+
+
+def test_decode_scores_gqa_and_given_keys():
+    """q head h reads kv head h // (Hq / Hkv): swapping the two kv heads swaps
+    the scores of their q heads.  A given key set is used as is."""
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((4, 8))
+    k = rng.standard_normal((2, 30, 8))
+    v = rng.standard_normal((2, 30, 8))
+    s = oracle.decode_scores(q, k)
+    s2 = oracle.decode_scores(q, k[::-1].copy())
+    scale = 1 / np.sqrt(8)
+    for h in range(4):
+        np.testing.assert_allclose(s[h], scale * k[h // 2] @ q[h], atol=1e-12)
+        np.testing.assert_allclose(s2[h], scale * k[1 - h // 2] @ q[h], atol=1e-12)
+    given = np.array([[0, 5, 29]] * 4)
+    out, lse, rec, idx = oracle.decode_sparse_attention(q, k, v, 3, idx=given)
+    np.testing.assert_array_equal(idx, given)
+    for h in range(4):
+        w = np.exp(s[h, given[h]] - s[h, given[h]].max())
+        np.testing.assert_allclose(out[h], (w[:, None] * v[h // 2, given[h]]).sum(0) / w.sum(), atol=1e-12)
