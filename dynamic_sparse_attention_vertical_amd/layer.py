@@ -175,9 +175,12 @@ def mixed_layer(q, k, v, plan: MixedPlan, *, out: torch.Tensor | None = None, ls
 # block_sparse_attention, streaming_forward), on [batch, heads, seq, dim] or
 # [heads, seq, dim] tensors, or on a packed batch of sequences of different
 # lengths ([heads, total, dim] with cu_seqlens, sequence i being rows
-# cu_seqlens[i] .. cu_seqlens[i+1]-1).  Sequences run one after another on
-# the stream through the same C-ABI steps; a packed sequence is a view of the
-# packed tensors (the C ABI's seq_stride is the packed length).
+# cu_seqlens[i] .. cu_seqlens[i+1]-1).  A batch whose batch stride is heads x
+# the head stride (a contiguous [B, H, N, D] tensor, or a slice of one along
+# the sequence) runs as one problem of B*H heads: one launch chain for the
+# whole batch.  Other batch layouts, and packed sequences, run one after
+# another on the stream through the same C-ABI steps; a packed sequence is a
+# view of the packed tensors (the C ABI's seq_stride is the packed length).
 
 
 def _packed(q, k, v, cu_seqlens, fn):
@@ -200,6 +203,30 @@ def _batched(q, k, v):
     return q, k, v, False
 
 
+def _fold(q4, k4, v4):
+    """[B, H, N, D] inputs as [B*H, N, D] views of the same memory, or None
+    when a tensor's batch stride is not H head strides.  Head h of batch
+    element b becomes head b*H + h; with H = G*Hkv its kv head under the C
+    ABI's mapping (q head // G) is b*Hkv + h // G, the same element's."""
+    if any(t.shape[1] > 1 and t.stride(0) != t.shape[1] * t.stride(1) for t in (q4, k4, v4)):
+        return None
+    if q4.shape[1] % k4.shape[1]:
+        return None                     # leave the head-count error to the per-element call
+    try:
+        return tuple(t.view(t.shape[0] * t.shape[1], t.shape[2], t.shape[3]) for t in (q4, k4, v4))
+    except RuntimeError:
+        return None
+
+
+def _rows(t):
+    """Rows between heads of a [heads, seq, dim] view."""
+    return t.stride(0) // t.shape[2] if t.shape[0] > 1 else t.shape[1]
+
+
+def _unfold(out, q4):
+    return out.view(q4.shape[0], q4.shape[1], out.shape[1], out.shape[2])
+
+
 @msa.on_stream
 def vertical_slash_sparse_attention(q, k, v, vertical_topk: int, slash_topk: int, *, cu_seqlens=None,
                                     stream=None):
@@ -207,13 +234,23 @@ def vertical_slash_sparse_attention(q, k, v, vertical_topk: int, slash_topk: int
     and slash_topk diagonals the online estimate selects, then causal
     attention over their 64-wide block cover.  Returns the attention output."""
     if cu_seqlens is not None:
+        plans = {}                      # one set of buffers per distinct length
+
         def one(qi, ki, vi, oi):
-            plan = LayerPlan(qi.shape[0], ki.shape[0], qi.shape[1], min(vertical_topk, qi.shape[1]),
-                             min(slash_topk, qi.shape[1]), str(qi.device), qi.dtype)
+            n = qi.shape[1]
+            plan = plans.get(n)
+            if plan is None:
+                plan = plans[n] = LayerPlan(qi.shape[0], ki.shape[0], n, min(vertical_topk, n),
+                                            min(slash_topk, n), str(qi.device), qi.dtype)
             vertical_slash_layer(qi, ki, vi, plan.vertical_topk, plan.slash_topk, plan=plan, out=oi,
                                  stream=stream)
         return _packed(q, k, v, cu_seqlens, one)
     q4, k4, v4, squeeze = _batched(q, k, v)
+    f = _fold(q4, k4, v4)
+    if f is not None:
+        out, _ = vertical_slash_layer(*f, vertical_topk, slash_topk, stream=stream)
+        out = _unfold(out, q4)
+        return out[0] if squeeze else out
     out = torch.empty_like(q4)
     plan = LayerPlan(q4.shape[1], k4.shape[1], q4.shape[2], vertical_topk, slash_topk, str(q4.device), q4.dtype)
     for bi in range(q4.shape[0]):
@@ -232,6 +269,11 @@ def block_sparse_attention(q, k, v, topk: int, *, cu_seqlens=None, stream=None):
             msa.sparse_prefill(qi, ki, vi, idx, out=oi, stream=stream)
         return _packed(q, k, v, cu_seqlens, one)
     q4, k4, v4, squeeze = _batched(q, k, v)
+    f = _fold(q4, k4, v4)
+    if f is not None:
+        idx = msa.estimate_bs(f[0], f[1], topk, stream=stream)
+        out = _unfold(msa.sparse_prefill(*f, idx, stream=stream), q4)
+        return out[0] if squeeze else out
     out = torch.empty_like(q4)
     hq, hkv, n = q4.shape[1], k4.shape[1], q4.shape[2]
     idx = msa.alloc_index(hq, n, min(topk, (n + msa.BLOCK - 1) // msa.BLOCK), 0, q4.device)
@@ -259,6 +301,13 @@ def streaming_forward(q, k, v, init_num: int, local_window_num: int, *, cu_seqle
     hq, hkv, n = q4.shape[1], k4.shape[1], q4.shape[2]
     if not (1 <= init_num <= n and 1 <= local_window_num <= n):
         raise msa.MsaError("init_num and local_window_num must be in [1, seq_len]")
+    f = _fold(q4, k4, v4)
+    if f is not None:
+        out = torch.empty((f[0].shape[0], _rows(f[0]), f[0].shape[2]), dtype=q4.dtype,
+                          device=q4.device)[:, :n]
+        _streaming_into(*f, init_num, local_window_num, out, stream)
+        out = _unfold(out, q4)
+        return out[0] if squeeze else out
     i32 = dict(dtype=torch.int32, device=q4.device)
     vi = torch.arange(init_num, **i32).expand(hq, -1).contiguous()
     si = torch.arange(local_window_num, **i32).expand(hq, -1).contiguous()

@@ -310,3 +310,28 @@ def test_binding_rejects_mismatched_inputs(lib):
             B.dense_prefill(q, kk, vv)
     with pytest.raises(B.MsaError, match="rows per head"):
         B.estimate_vs(q, k[:, :64], 8, 8)
+
+
+def test_batch_fold_views():
+    """Host logic of the batched calls: a contiguous [B, H, N, D] batch (or a
+    slice of one along the sequence) folds into [B*H, N, D] views of the same
+    memory in which q head b*H + h reads kv head (b*H + h) // G = b*Hkv + h // G;
+    other layouts do not fold."""
+    import torch
+    from dynamic_sparse_attention_vertical_amd import layer as L
+    Bn, H, Hkv, N, D = 3, 8, 2, 10, 128
+    q = torch.arange(Bn * H * 16 * D, dtype=torch.float32).view(Bn, H, 16, D)[:, :, :N]
+    k = torch.arange(Bn * Hkv * 16 * D, dtype=torch.float32).view(Bn, Hkv, 16, D)[:, :, :N]
+    f = L._fold(q, k, k)
+    assert f is not None
+    qf, kf, _ = f
+    assert qf.data_ptr() == q.data_ptr() and kf.data_ptr() == k.data_ptr()
+    assert qf.stride(0) == 16 * D and kf.stride(0) == 16 * D       # head stride unchanged
+    G = H // Hkv
+    for b in range(Bn):
+        for h in range(H):
+            assert torch.equal(qf[b * H + h], q[b, h])
+            assert torch.equal(kf[(b * H + h) // G], k[b, h // G])
+    perm = q.transpose(0, 1).contiguous().transpose(0, 1)
+    assert L._fold(perm, k, k) is None
+    assert L._fold(q, k[:, :1].expand(Bn, 3, N, D), k) is None      # 8 q heads over 3 kv heads

@@ -63,6 +63,28 @@ def test_streaming_forward_batched(init_num, window):
         compare_out(out[bi].float().cpu().numpy(), ref, False, f"streaming batch {bi}")
 
 
+def test_batch_layouts_fold_or_loop():
+    """A contiguous batch runs as one problem of B*H heads; a batch whose
+    heads are not evenly spaced across elements (here [H, B, N, D] memory
+    seen as [B, H, N, D]) runs element by element.  Both give bitwise the
+    same outputs as the per-element calls (at this length every element's
+    estimate uses the same key ranges either way)."""
+    B, hq, hkv, n = 3, 4, 2, 768
+    q, k, v = batch_inputs(B, hq, hkv, n, seed=91)
+    qp, kp, vp = (t.transpose(0, 1).contiguous().cuda().transpose(0, 1) for t in (q, k, v))
+    assert qp.stride(0) != qp.shape[1] * qp.stride(1)           # not foldable
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    for call, args in ((msa.vertical_slash_sparse_attention, (24, 70)), (msa.block_sparse_attention, (3,)),
+                       (msa.streaming_forward, (64, 128))):
+        folded = call(qc, kc, vc, *args)
+        looped = call(qp, kp, vp, *args)
+        assert folded.shape == looped.shape == q.shape
+        for bi in range(B):
+            one = call(qc[bi], kc[bi], vc[bi], *args)
+            assert torch.equal(folded[bi], one), (call.__name__, "folded", bi)
+            assert torch.equal(looped[bi], one), (call.__name__, "looped", bi)
+
+
 def test_api_ragged_lengths():
     """Lengths that are not a multiple of 64 through the whole path: estimate,
     index, sparse prefill; block-sparse; streaming."""
