@@ -60,40 +60,36 @@ template <> __device__ __forceinline__ void load8<float>(const float *p, float (
     }
 }
 
-__device__ __forceinline__ float sum16(float v) {          // over the 16 lanes of a row group
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, 16);
-    return v;
+// Lane moves inside a row of 16 lanes (DPP, no LDS): the lane 15 - i of the
+// row, the lane 7 - i of its half, and the lanes i ^ 2, i ^ 1 of its quad.
+template <int kCtrl> __device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
 }
+constexpr int kDppRowMirror = 0x140, kDppHalfMirror = 0x141, kDppQuadXor2 = 0x4e, kDppQuadXor1 = 0xb1;
 
 // The kG dot products of a 16-lane row group (one partial per lane each),
-// reduce-scattered: afterwards lane pairs (kG = 8) or quads (kG = 4) hold
-// one head's full sum each, head_of(lane) -- kG - 1 + 4 shuffles instead of
-// 4 per head.
-template <int kG> __device__ __forceinline__ float reduce_scatter16(const float (&v)[kG], int lane) {
-    float w[kG];
+// reduce-scattered: at each step the lower and upper halves of a group of
+// lanes pair up (mirror images), each keeps half of the heads and adds the
+// partner's partials of them.  Afterwards lane pairs (kG = 8) or quads
+// (kG = 4) hold one head's full sum each, head_of(lane).
+template <int kG> __device__ __forceinline__ float reduce_scatter16(const float (&v)[kG], int lane);
+template <> __device__ __forceinline__ float reduce_scatter16<4>(const float (&v)[4], int lane) {
+    const bool u8 = (lane & 8) != 0, u4 = (lane & 4) != 0;
+    const float k0 = (u8 ? v[2] : v[0]) + dpp<kDppRowMirror>(u8 ? v[0] : v[2]);
+    const float k1 = (u8 ? v[3] : v[1]) + dpp<kDppRowMirror>(u8 ? v[1] : v[3]);
+    float k = (u4 ? k1 : k0) + dpp<kDppHalfMirror>(u4 ? k0 : k1);
+    k += dpp<kDppQuadXor2>(k);
+    return k + dpp<kDppQuadXor1>(k);
+}
+template <> __device__ __forceinline__ float reduce_scatter16<8>(const float (&v)[8], int lane) {
+    const bool u8 = (lane & 8) != 0, u4 = (lane & 4) != 0, u2 = (lane & 2) != 0;
+    float k[4];
 #pragma unroll
-    for (int i = 0; i < kG; ++i) w[i] = v[i];
-    int live = kG;
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) {
-        if (live > 1) {
-            const bool upper = (lane & o) != 0;
-            const int half = live / 2;
-#pragma unroll
-            for (int i = 0; i < kG / 2; ++i) {
-                if (i < half) {
-                    const float send = upper ? w[i] : w[i + half];
-                    const float keep = upper ? w[i + half] : w[i];
-                    w[i] = keep + __shfl_xor(send, o, 16);
-                }
-            }
-            live = half;
-        } else {
-            w[0] += __shfl_xor(w[0], o, 16);
-        }
-    }
-    return w[0];
+    for (int i = 0; i < 4; ++i) k[i] = (u8 ? v[i + 4] : v[i]) + dpp<kDppRowMirror>(u8 ? v[i] : v[i + 4]);
+    const float m0 = (u4 ? k[2] : k[0]) + dpp<kDppHalfMirror>(u4 ? k[0] : k[2]);
+    const float m1 = (u4 ? k[3] : k[1]) + dpp<kDppHalfMirror>(u4 ? k[1] : k[3]);
+    const float r = (u2 ? m1 : m0) + dpp<kDppQuadXor2>(u2 ? m0 : m1);
+    return r + dpp<kDppQuadXor1>(r);
 }
 template <int kG> __device__ __forceinline__ int head_of(int lane) {
     return kG == 8 ? ((lane >> 3) & 1) * 4 + ((lane >> 2) & 1) * 2 + ((lane >> 1) & 1)

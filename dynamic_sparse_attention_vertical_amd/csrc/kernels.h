@@ -107,6 +107,9 @@ struct TopkArgs {
 constexpr int kTopkSlice = 4096;   // elements per top-k workgroup slice
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
+// The same selection with one 1024-thread workgroup per row, in one launch
+// (uses none of hist / state / cnt / off).
+hipError_t launch_topk_rows(const TopkArgs &a, hipStream_t s);
 
 // Decode-side top-k attention: one query row per q head over a cache of n keys.
 struct DecodeArgs {

@@ -191,10 +191,13 @@ struct DecodeLayout {
 DecodeLayout decode_layout(const msa_problem *p) {
     DecodeLayout L;
     const int64_t n = p->seq_len;
-    // about 2048 workgroups per pass over the caches, at least 1024 keys each
-    int64_t ck = (n * p->n_kv_heads + 2047) / 2048;
-    ck = ((ck + 1023) / 1024) * 1024;
-    if (ck < 1024) ck = 1024;
+    // about 24576 workgroups per pass over the caches (16 rounds of the ~1536
+    // that fit on the chip at once), at least 256 keys each: with a few large
+    // chunks per kv head the last round runs a handful of workgroups alone
+    // (1600 chunks of 4096 keys: 0.558 ms per 100K-key step against 0.484
+    // with 24576 chunks of 261)
+    int64_t ck = (n * p->n_kv_heads + 24575) / 24576;
+    if (ck < 256) ck = 256;
     L.chunk_keys = ck;
     L.nchunks = (int32_t)((n + ck - 1) / ck);
     L.nslices = (int32_t)((n + msa::kTopkSlice - 1) / msa::kTopkSlice);
@@ -538,7 +541,10 @@ int msa_decode_sparse(const msa_problem *p, const void *q, const void *k, const 
         t.state = at<uint32_t>(workspace, L.off_state);
         t.cnt = at<uint32_t>(workspace, L.off_cnt);
         t.off = at<uint32_t>(workspace, L.off_off);
-        if ((st = launch_status(msa::launch_topk(t, s), "decode top-k"))) return st;
+        // one workgroup per row once there are rows for half the chip; fewer
+        // rows are split into slices across the chip
+        const hipError_t e = t.rows >= 128 ? msa::launch_topk_rows(t, s) : msa::launch_topk(t, s);
+        if ((st = launch_status(e, "decode top-k"))) return st;
     }
     return launch_status(msa::launch_decode_attend(a, p->dtype, s), "decode attend");
 }

@@ -245,7 +245,147 @@ __global__ __launch_bounds__(kThreads) void topk_write_kernel(TopkArgs a) {
     }
 }
 
+// ---- One workgroup per row ----
+// The same selection in a single launch: a 1024-thread workgroup takes one
+// row through the three histogram passes and the ordered write, reading the
+// row once per pass (after the first pass from the caches).  For many rows
+// at once (the decode step's one row per q head) this replaces the ten
+// launches above, most of whose time is the fixed cost of a launch.
+constexpr int kRowThreads = 1024;
+constexpr int kRowPer = 16;                             // consecutive elements per thread and tile
+constexpr int kRowTile = kRowThreads * kRowPer;
+
+__device__ __forceinline__ void row_load(const uint32_t *src, int64_t n, int64_t e, uint32_t (&x)[kRowPer],
+                                         int &cnt) {
+    if (e + kRowPer <= n) {
+#pragma unroll
+        for (int c = 0; c < kRowPer / 4; ++c) {
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(src + e + 4 * c);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[4 * c + i] = w[i];
+        }
+        cnt = kRowPer;
+    } else {
+        cnt = e < n ? (int)(n - e) : 0;
+#pragma unroll
+        for (int i = 0; i < kRowPer; ++i) x[i] = i < cnt ? src[e + i] : 0u;
+    }
+}
+
+// exclusive prefix sum over the workgroup's 1024 threads, and the total
+__device__ __forceinline__ uint32_t row_scan(uint32_t v, uint32_t *wsum, uint32_t &total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    uint32_t before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kRowThreads / 64; ++w) {
+        const uint32_t sw = wsum[w];
+        before += w < wave ? sw : 0u;
+        tot += sw;
+    }
+    __syncthreads();                                    // wsum is free again
+    total = tot;
+    return before + incl - v;
+}
+
+__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
+    __shared__ uint32_t hist[2048];
+    __shared__ uint32_t wsum[kRowThreads / 64];
+    __shared__ uint32_t sel[2];
+    const int row = blockIdx.x, tid = threadIdx.x;
+    const RowView r = row_view(a, row);
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(r.src);
+    const int64_t n = a.n;
+    uint32_t prefix = 0, krem = (uint32_t)r.k;
+    uint32_t xa[kRowPer], xb[kRowPer];
+    int ca, cb;
+    for (int p = 0; p < 3; ++p) {
+        const int sh = pass_shift(p), bits = pass_bits(p), nb = 1 << bits, hi_sh = sh + bits;
+        for (int i = tid; i < 2048; i += kRowThreads) hist[i] = 0u;
+        __syncthreads();
+        row_load(src, n, (int64_t)tid * kRowPer, xa, ca);
+        for (int64_t e0 = 0; e0 < n; e0 += kRowTile) {
+            if (e0 + kRowTile < n) row_load(src, n, e0 + kRowTile + (int64_t)tid * kRowPer, xb, cb);
+#pragma unroll
+            for (int i = 0; i < kRowPer; ++i)
+                if (i < ca && (hi_sh >= 32 || (xa[i] >> hi_sh) == prefix))
+                    atomicAdd(&hist[(xa[i] >> sh) & (uint32_t)(nb - 1)], 1u);
+#pragma unroll
+            for (int i = 0; i < kRowPer; ++i) xa[i] = xb[i];
+            ca = cb;
+        }
+        __syncthreads();
+        // buckets top down: thread t owns nb-1-t*per .. nb-per-t*per
+        const int per = nb / kRowThreads;
+        const uint32_t c0 = hist[nb - 1 - tid * per], c1 = per == 2 ? hist[nb - 2 - tid * per] : 0u;
+        uint32_t tot;
+        const uint32_t above = row_scan(c0 + c1, wsum, tot);
+        if (above < krem && krem <= above + c0 + c1) {
+            const bool first = krem <= above + c0;
+            const uint32_t bucket = (uint32_t)(nb - 1 - tid * per - (first ? 0 : 1));
+            sel[0] = (prefix << bits) | bucket;
+            sel[1] = krem - (first ? above : above + c0);
+        }
+        __syncthreads();
+        prefix = sel[0];
+        krem = sel[1];
+    }
+    // every entry above T, and the krem lowest-index entries equal to T, in
+    // ascending index order; the tile's scan carries both counts (above in
+    // the high half, equal in the low half: at most 16384 each)
+    const uint32_t T = prefix;
+    uint32_t need = krem, base = 0;
+    row_load(src, n, (int64_t)tid * kRowPer, xa, ca);
+    for (int64_t e0 = 0; e0 < n && base < (uint32_t)r.k; e0 += kRowTile) {
+        if (e0 + kRowTile < n) row_load(src, n, e0 + kRowTile + (int64_t)tid * kRowPer, xb, cb);
+        uint32_t gt = 0, eq = 0;
+#pragma unroll
+        for (int i = 0; i < kRowPer; ++i) {
+            gt += (i < ca && xa[i] > T) ? 1u : 0u;
+            eq += (i < ca && xa[i] == T) ? 1u : 0u;
+        }
+        uint32_t tot;
+        const uint32_t ex = row_scan((gt << 16) | eq, wsum, tot);
+        const uint32_t eq_before = ex & 0xffffu;
+        uint32_t pos = base + (ex >> 16) + min(eq_before, need);
+        uint32_t eq_seen = eq_before;
+        const int64_t e = e0 + (int64_t)tid * kRowPer;
+#pragma unroll
+        for (int i = 0; i < kRowPer; ++i) {
+            if (i >= ca) continue;
+            bool take = xa[i] > T;
+            if (xa[i] == T) {
+                take = eq_seen < need;
+                ++eq_seen;
+            }
+            if (take) {
+                if (pos < (uint32_t)r.k) r.dst[pos] = (int32_t)(e + i);
+                ++pos;
+            }
+        }
+        const uint32_t teq = min(tot & 0xffffu, need);
+        base += (tot >> 16) + teq;
+        need -= teq;
+#pragma unroll
+        for (int i = 0; i < kRowPer; ++i) xa[i] = xb[i];
+        ca = cb;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_topk_rows(const TopkArgs &a, hipStream_t s) {
+    const int rows = a.rows > 0 ? a.rows : 2 * a.hq;
+    hipLaunchKernelGGL(topk_row_kernel, dim3(rows), dim3(kRowThreads), 0, s, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
     const int rows = a.rows > 0 ? a.rows : 2 * a.hq;

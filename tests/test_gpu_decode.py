@@ -71,6 +71,8 @@ def check_decode(q, k, v, topk, fp32, what, given=None):
     (2, 2, 777, 1, False),             # one key
     (2, 1, 513, 513, False),           # every key: dense decode attention
     (4, 2, 1500, 200, True),           # fp32
+    (128, 32, 3000 + 5, 200, False),   # 128 rows: one top-k workgroup per row
+    (256, 64, 1100, 1100, False),      # every key, one workgroup per row
 ])
 def test_decode_topk(hq, hkv, n, topk, fp32):
     q, k, v = cache(hq, hkv, n, seed=n + topk, fp32=fp32)
@@ -132,3 +134,33 @@ def test_decode_128k_cache():
     np.testing.assert_allclose(lse.cpu().numpy(), rl, atol=LSE_ATOL)
     np.testing.assert_allclose(rec.cpu().numpy(), rr, atol=REC_ATOL)
     print(f"128K decode: kept share of the attention mass, top-1000: mean {rr.mean():.3f}, min {rr.min():.3f}")
+
+
+def tie_cache(hq, hkv, n, seed):
+    """Keys at seven score levels, key j at level j % 7, every q head equal
+    to the direction of its kv head's keys: keys of one level score exactly
+    alike (identical rows), levels lie far apart."""
+    g = torch.Generator().manual_seed(seed)
+    w = torch.randn(hkv, 128, generator=g)
+    levels = torch.tensor([-1.5, -1.0, -0.5, 0.0, 0.5, 1.0, 1.5])
+    c = levels[torch.arange(n) % 7]
+    k = (c[None, :, None] * w[:, None, :]).to(torch.bfloat16)
+    q = w.repeat_interleave(hq // hkv, 0).to(torch.bfloat16)
+    v = torch.randn(hkv, n, 128, generator=g).to(torch.bfloat16)
+    return q, k, v
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (128, 32)])      # slices across the chip; one workgroup per row
+def test_decode_topk_exact_ties(hq, hkv):
+    """The top level's 300 keys, then the 17 lowest-index keys of the next
+    level, whose 300 keys all tie: the selected sets equal the oracle's
+    exactly (ties go to the lower index)."""
+    n, topk = 2100, 300 + 17
+    q, k, v = tie_cache(hq, hkv, n, seed=5)
+    out, idx, lse, rec = msa.decode_sparse(q.cuda(), k.cuda(), v.cuda(), topk, lse=True, recovery=True)
+    ro, rl, rr, ref_idx = oracle.decode_sparse_attention(q, k, v, topk)
+    expect = np.sort(np.r_[np.arange(6, n, 7), np.arange(5, 5 + 7 * 17, 7)])
+    assert np.array_equal(ref_idx[0], expect)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx)
+    compare_out(out.float().cpu().numpy(), ro, False, "ties")
+    np.testing.assert_allclose(lse.cpu().numpy(), rl, rtol=0, atol=LSE_ATOL)
