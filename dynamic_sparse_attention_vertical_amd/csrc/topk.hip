@@ -255,20 +255,40 @@ constexpr int kRowThreads = 1024;
 constexpr int kRowPer = 16;                             // consecutive elements per thread and tile
 constexpr int kRowTile = kRowThreads * kRowPer;
 
-__device__ __forceinline__ void row_load(const uint32_t *src, int64_t n, int64_t e, uint32_t (&x)[kRowPer],
-                                         int &cnt) {
-    if (e + kRowPer <= n) {
+// Tiles of kRowTile elements, thread t holding elements e0 + 16t .. e0 + 16t + 15.
+// Full tiles stream with one tile loaded ahead and exactly four 16-byte loads
+// per thread per tile (so the compiler can wait for the older tile only); the
+// partial last tile is read element by element afterwards.  visit(x, cnt, e0)
+// sees a tile (cnt valid elements in this thread) and returns false to stop
+// (a workgroup-uniform decision).
+__device__ __forceinline__ void row_load_full(const uint32_t *src, int64_t e, uint32_t (&x)[kRowPer]) {
 #pragma unroll
-        for (int c = 0; c < kRowPer / 4; ++c) {
-            const u32x4 w = *reinterpret_cast<const u32x4 *>(src + e + 4 * c);
+    for (int c = 0; c < kRowPer / 4; ++c) {
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(src + e + 4 * c);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x[4 * c + i] = w[i];
-        }
-        cnt = kRowPer;
-    } else {
-        cnt = e < n ? (int)(n - e) : 0;
+        for (int i = 0; i < 4; ++i) x[4 * c + i] = w[i];
+    }
+}
+template <typename F>
+__device__ __forceinline__ void row_tiles(const uint32_t *src, int64_t n, F &&visit) {
+    const int64_t mine = (int64_t)threadIdx.x * kRowPer;
+    const int64_t nfull = n / kRowTile * kRowTile;
+    uint32_t xa[kRowPer], xb[kRowPer];
+    if (nfull > 0) row_load_full(src, mine, xa);
+    for (int64_t e0 = 0; e0 < nfull; e0 += kRowTile) {
+        // the tile after this one (after the last full tile: that tile again, unused)
+        const int64_t nx = e0 + kRowTile < nfull ? e0 + kRowTile : e0;
+        row_load_full(src, nx + mine, xb);
+        if (!visit(xa, kRowPer, e0)) return;
 #pragma unroll
-        for (int i = 0; i < kRowPer; ++i) x[i] = i < cnt ? src[e + i] : 0u;
+        for (int i = 0; i < kRowPer; ++i) xa[i] = xb[i];
+    }
+    if (nfull < n) {
+        const int64_t e = nfull + mine;
+        const int cnt = e < n ? (n - e < kRowPer ? (int)(n - e) : kRowPer) : 0;
+#pragma unroll
+        for (int i = 0; i < kRowPer; ++i) xa[i] = i < cnt ? src[e + i] : 0u;
+        visit(xa, cnt, nfull);
     }
 }
 
@@ -304,23 +324,17 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
     const uint32_t *src = reinterpret_cast<const uint32_t *>(r.src);
     const int64_t n = a.n;
     uint32_t prefix = 0, krem = (uint32_t)r.k;
-    uint32_t xa[kRowPer], xb[kRowPer];
-    int ca, cb;
     for (int p = 0; p < 3; ++p) {
         const int sh = pass_shift(p), bits = pass_bits(p), nb = 1 << bits, hi_sh = sh + bits;
         for (int i = tid; i < 2048; i += kRowThreads) hist[i] = 0u;
         __syncthreads();
-        row_load(src, n, (int64_t)tid * kRowPer, xa, ca);
-        for (int64_t e0 = 0; e0 < n; e0 += kRowTile) {
-            if (e0 + kRowTile < n) row_load(src, n, e0 + kRowTile + (int64_t)tid * kRowPer, xb, cb);
+        row_tiles(src, n, [&](const uint32_t (&x)[kRowPer], int cnt, int64_t) {
 #pragma unroll
             for (int i = 0; i < kRowPer; ++i)
-                if (i < ca && (hi_sh >= 32 || (xa[i] >> hi_sh) == prefix))
-                    atomicAdd(&hist[(xa[i] >> sh) & (uint32_t)(nb - 1)], 1u);
-#pragma unroll
-            for (int i = 0; i < kRowPer; ++i) xa[i] = xb[i];
-            ca = cb;
-        }
+                if (i < cnt && (hi_sh >= 32 || (x[i] >> hi_sh) == prefix))
+                    atomicAdd(&hist[(x[i] >> sh) & (uint32_t)(nb - 1)], 1u);
+            return true;
+        });
         __syncthreads();
         // buckets top down: thread t owns nb-1-t*per .. nb-per-t*per
         const int per = nb / kRowThreads;
@@ -342,14 +356,12 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
     // the high half, equal in the low half: at most 16384 each)
     const uint32_t T = prefix;
     uint32_t need = krem, base = 0;
-    row_load(src, n, (int64_t)tid * kRowPer, xa, ca);
-    for (int64_t e0 = 0; e0 < n && base < (uint32_t)r.k; e0 += kRowTile) {
-        if (e0 + kRowTile < n) row_load(src, n, e0 + kRowTile + (int64_t)tid * kRowPer, xb, cb);
+    row_tiles(src, n, [&](const uint32_t (&x)[kRowPer], int cnt, int64_t e0) {
         uint32_t gt = 0, eq = 0;
 #pragma unroll
         for (int i = 0; i < kRowPer; ++i) {
-            gt += (i < ca && xa[i] > T) ? 1u : 0u;
-            eq += (i < ca && xa[i] == T) ? 1u : 0u;
+            gt += (i < cnt && x[i] > T) ? 1u : 0u;
+            eq += (i < cnt && x[i] == T) ? 1u : 0u;
         }
         uint32_t tot;
         const uint32_t ex = row_scan((gt << 16) | eq, wsum, tot);
@@ -359,9 +371,9 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
         const int64_t e = e0 + (int64_t)tid * kRowPer;
 #pragma unroll
         for (int i = 0; i < kRowPer; ++i) {
-            if (i >= ca) continue;
-            bool take = xa[i] > T;
-            if (xa[i] == T) {
+            if (i >= cnt) continue;
+            bool take = x[i] > T;
+            if (x[i] == T) {
                 take = eq_seen < need;
                 ++eq_seen;
             }
@@ -373,10 +385,8 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
         const uint32_t teq = min(tot & 0xffffu, need);
         base += (tot >> 16) + teq;
         need -= teq;
-#pragma unroll
-        for (int i = 0; i < kRowPer; ++i) xa[i] = xb[i];
-        ca = cb;
-    }
+        return base < (uint32_t)r.k;                   // every selected entry written
+    });
 }
 
 }  // namespace
