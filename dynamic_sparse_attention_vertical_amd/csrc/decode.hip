@@ -21,6 +21,7 @@
 #include "kernels.h"
 
 #include <climits>
+#include <type_traits>
 
 namespace msa {
 namespace {
@@ -135,7 +136,11 @@ __global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a, i
     const int64_t j1 = min(j0 + a.chunk_keys, a.n);
     float m = -INFINITY, l = 0.f;
     constexpr int kUs = kPairs ? 2 * kU : kU;               // bf16 rows are half the registers
-    for (int64_t jb = j0 + wave * 4 + sub; jb < j1; jb += 16 * kUs) {
+    // one step: rows jb + 16 u, u < kUs, of this 16-lane row group; all of
+    // them inside the chunk (kFull: loads without conditions, so that the
+    // compiler waits for each row's load alone), or some past its end
+    auto step = [&](int64_t jb, auto full) {
+        constexpr bool kFull = decltype(full)::value;
         float kx[kUs][8];
         u32x4 kw[kUs];
 #pragma unroll
@@ -143,9 +148,9 @@ __global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a, i
             const int64_t j = jb + 16 * u;
             if constexpr (kPairs) {
                 // non-temporal: each K row is read once per pass (8% faster at 100K x 64 kv heads)
-                kw[u] = j < j1 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kp + j * kD + col))
-                               : u32x4{0u, 0u, 0u, 0u};
-            } else if (j < j1) {
+                kw[u] = (kFull || j < j1) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kp + j * kD + col))
+                                          : u32x4{0u, 0u, 0u, 0u};
+            } else if (kFull || j < j1) {
                 load8<T>(kp + j * kD + col, kx[u]);
             } else {
 #pragma unroll
@@ -155,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a, i
 #pragma unroll
         for (int u = 0; u < kUs; ++u) {
             const int64_t j = jb + 16 * u;
-            if (j >= j1) break;
+            if (!kFull && j >= j1) break;
             float d[kG];
 #pragma unroll
             for (int g = 0; g < kG; ++g) {
@@ -182,7 +187,10 @@ __global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a, i
                 m = mn;
             }
         }
-    }
+    };
+    int64_t jb = j0 + wave * 4 + sub;
+    for (; jb + 16 * (kUs - 1) < j1; jb += 16 * kUs) step(jb, std::true_type{});
+    if (jb < j1) step(jb, std::false_type{});
     // the chunk's (max, sum) per head: owners of one head sit at the same
     // position in each row group; combine the 4 row groups, then the waves
     auto comb = [](float &mg, float &lg, float mo, float lo) {
