@@ -237,19 +237,21 @@ __global__ __launch_bounds__(64) void decode_stats_kernel(DecodeArgs a) {
 }
 
 // One workgroup per q head: softmax over the selected keys' scores and the
-// weighted sum of their V rows (16 lanes per row, 16 rows per step).
+// weighted sum of their V rows (16 lanes per row, 64 row slots of kU rows per
+// step: the gathers of one head spread over 16 waves).
+constexpr int kAttThreads = 1024, kSlots = kAttThreads / 16;
 template <typename T>
-__global__ __launch_bounds__(kThreads) void decode_attend_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kAttThreads) void decode_attend_kernel(DecodeArgs a) {
     const int h = blockIdx.x;
     const int G = a.hq / a.hkv;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int col = (lane & 15) * 8, slot = wave * 4 + (lane >> 4);   // 16 row slots
+    const int col = (lane & 15) * 8, slot = wave * 4 + (lane >> 4);   // kSlots row slots
     const int32_t *idx = a.idx + (int64_t)h * a.topk;
     const uint32_t *keys = a.keys + (int64_t)h * a.n;
-    __shared__ float red[kThreads / 64];
+    __shared__ float red[kAttThreads / 64];
     // the selected scores' maximum
     float mx = -INFINITY;
-    for (int t = threadIdx.x; t < a.topk; t += kThreads) {
+    for (int t = threadIdx.x; t < a.topk; t += kAttThreads) {
         const int64_t j = min(max((int64_t)idx[t], (int64_t)0), a.n - 1);
         mx = fmaxf(mx, key_score(keys[j]));
     }
@@ -257,17 +259,19 @@ __global__ __launch_bounds__(kThreads) void decode_attend_kernel(DecodeArgs a) {
     for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
     if (lane == 0) red[wave] = mx;
     __syncthreads();
-    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    mx = red[0];
+#pragma unroll
+    for (int w = 1; w < kAttThreads / 64; ++w) mx = fmaxf(mx, red[w]);
     __syncthreads();
     const T *vp = reinterpret_cast<const T *>(a.v) + (int64_t)(h / G) * a.stride * kD;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float lsum = 0.f;
-    for (int tb = slot; tb < a.topk; tb += 16 * kU) {
+    for (int tb = slot; tb < a.topk; tb += kSlots * kU) {
         // kU rows per slot per step, their loads issued together
         float vx[kU][8], p[kU];
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            const int t = tb + 16 * u;
+            const int t = tb + kSlots * u;
             p[u] = 0.f;
             if (t < a.topk) {
                 const int64_t j = min(max((int64_t)idx[t], (int64_t)0), a.n - 1);
@@ -286,15 +290,15 @@ __global__ __launch_bounds__(kThreads) void decode_attend_kernel(DecodeArgs a) {
         }
     }
     // sum the 16 slots: rows of each column slice in LDS, then one thread per column
-    __shared__ float part[16][kD];
-    __shared__ float lpart[16];
+    __shared__ float part[kSlots][kD];
+    __shared__ float lpart[kSlots];
 #pragma unroll
     for (int e = 0; e < 8; ++e) part[slot][col + e] = acc[e];
     if ((lane & 15) == 0) lpart[slot] = lsum;
     __syncthreads();
     if (threadIdx.x < kD) {
         float o = 0.f, ls = 0.f;
-        for (int r = 0; r < 16; ++r) {
+        for (int r = 0; r < kSlots; ++r) {
             o += part[r][threadIdx.x];
             ls += lpart[r];
         }
@@ -343,9 +347,9 @@ hipError_t launch_decode_scores(const DecodeArgs &a, int dtype, hipStream_t s) {
 
 hipError_t launch_decode_attend(const DecodeArgs &a, int dtype, hipStream_t s) {
     if (dtype == 0)
-        hipLaunchKernelGGL(decode_attend_kernel<bf16>, dim3((unsigned)a.hq), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL(decode_attend_kernel<bf16>, dim3((unsigned)a.hq), dim3(kAttThreads), 0, s, a);
     else
-        hipLaunchKernelGGL(decode_attend_kernel<float>, dim3((unsigned)a.hq), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL(decode_attend_kernel<float>, dim3((unsigned)a.hq), dim3(kAttThreads), 0, s, a);
     return hipGetLastError();
 }
 
