@@ -315,41 +315,126 @@ __device__ __forceinline__ uint32_t row_scan(uint32_t v, uint32_t *wsum, uint32_
     return before + incl - v;
 }
 
+// Entries staged in LDS after the first pass (index and key, 8 bytes each).
+constexpr int kStage = 6144;
+
 __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
     __shared__ uint32_t hist[2048];
     __shared__ uint32_t wsum[kRowThreads / 64];
-    __shared__ uint32_t sel[2];
+    __shared__ uint32_t sel[3];
+    __shared__ uint32_t st_key[kStage];
+    __shared__ int32_t st_idx[kStage];
     const int row = blockIdx.x, tid = threadIdx.x;
     const RowView r = row_view(a, row);
     const uint32_t *src = reinterpret_cast<const uint32_t *>(r.src);
     const int64_t n = a.n;
-    uint32_t prefix = 0, krem = (uint32_t)r.k;
-    for (int p = 0; p < 3; ++p) {
-        const int sh = pass_shift(p), bits = pass_bits(p), nb = 1 << bits, hi_sh = sh + bits;
+    const uint32_t k = (uint32_t)r.k;
+    uint32_t prefix = 0, krem = k, in_bucket = 0;
+
+    auto clear = [&]() {
         for (int i = tid; i < 2048; i += kRowThreads) hist[i] = 0u;
         __syncthreads();
-        row_tiles(src, n, [&](const uint32_t (&x)[kRowPer], int cnt, int64_t) {
-#pragma unroll
-            for (int i = 0; i < kRowPer; ++i)
-                if (i < cnt && (hi_sh >= 32 || (x[i] >> hi_sh) == prefix))
-                    atomicAdd(&hist[(x[i] >> sh) & (uint32_t)(nb - 1)], 1u);
-            return true;
-        });
-        __syncthreads();
-        // buckets top down: thread t owns nb-1-t*per .. nb-per-t*per
-        const int per = nb / kRowThreads;
+    };
+    // pass p's bucket of x, counted if x matches the prefix found so far
+    auto count = [&](int p, uint32_t x) {
+        const int sh = pass_shift(p), hi_sh = sh + pass_bits(p);
+        if (hi_sh >= 32 || (x >> hi_sh) == prefix) atomicAdd(&hist[(x >> sh) & ((1u << pass_bits(p)) - 1u)], 1u);
+    };
+    // the bucket holding the krem-th largest counted entry (buckets top down,
+    // thread t owning nb-1-t*per .. nb-per-t*per); krem becomes its rank
+    // inside the bucket, in_bucket the bucket's count
+    auto pick = [&](int p) {
+        const int bits = pass_bits(p), nb = 1 << bits, per = nb / kRowThreads;
         const uint32_t c0 = hist[nb - 1 - tid * per], c1 = per == 2 ? hist[nb - 2 - tid * per] : 0u;
         uint32_t tot;
         const uint32_t above = row_scan(c0 + c1, wsum, tot);
         if (above < krem && krem <= above + c0 + c1) {
             const bool first = krem <= above + c0;
-            const uint32_t bucket = (uint32_t)(nb - 1 - tid * per - (first ? 0 : 1));
-            sel[0] = (prefix << bits) | bucket;
+            sel[0] = (prefix << bits) | (uint32_t)(nb - 1 - tid * per - (first ? 0 : 1));
             sel[1] = krem - (first ? above : above + c0);
+            sel[2] = first ? c0 : c1;
         }
         __syncthreads();
         prefix = sel[0];
         krem = sel[1];
+        in_bucket = sel[2];
+    };
+
+    clear();
+    row_tiles(src, n, [&](const uint32_t (&x)[kRowPer], int cnt, int64_t) {
+#pragma unroll
+        for (int i = 0; i < kRowPer; ++i)
+            if (i < cnt) count(0, x[i]);
+        return true;
+    });
+    __syncthreads();
+    pick(0);
+    // entries whose top 11 bits reach the chosen bucket: k - krem above it
+    // (all selected) and in_bucket inside it
+    const uint32_t staged = k - krem + in_bucket;
+    if (staged <= (uint32_t)kStage) {
+        // the second and last pass over the row stages them in index order;
+        // the other two radix steps and the ordered write then run in LDS
+        const uint32_t b0 = prefix;
+        uint32_t base = 0;
+        row_tiles(src, n, [&](const uint32_t (&x)[kRowPer], int cnt, int64_t e0) {
+            uint32_t c = 0;
+#pragma unroll
+            for (int i = 0; i < kRowPer; ++i) c += (i < cnt && (x[i] >> 21) >= b0) ? 1u : 0u;
+            uint32_t tot;
+            uint32_t pos = base + row_scan(c, wsum, tot);
+            const int64_t e = e0 + (int64_t)tid * kRowPer;
+#pragma unroll
+            for (int i = 0; i < kRowPer; ++i) {
+                if (i < cnt && (x[i] >> 21) >= b0) {
+                    if (pos < (uint32_t)kStage) {
+                        st_key[pos] = x[i];
+                        st_idx[pos] = (int32_t)(e + i);
+                    }
+                    ++pos;
+                }
+            }
+            base += tot;
+            return true;
+        });
+        __syncthreads();
+        for (int p = 1; p < 3; ++p) {
+            clear();
+            for (uint32_t i = tid; i < staged; i += kRowThreads) count(p, st_key[i]);
+            __syncthreads();
+            pick(p);
+        }
+        const uint32_t T = prefix;
+        uint32_t need = krem, out = 0;
+        for (uint32_t i0 = 0; i0 < staged; i0 += kRowThreads) {
+            const uint32_t i = i0 + tid;
+            const uint32_t x = i < staged ? st_key[i] : 0u;
+            const uint32_t gt = (i < staged && x > T) ? 1u : 0u, eq = (i < staged && x == T) ? 1u : 0u;
+            uint32_t tot;
+            const uint32_t ex = row_scan((gt << 16) | eq, wsum, tot);
+            const uint32_t eq_before = ex & 0xffffu;
+            if (gt || (eq && eq_before < need)) {
+                const uint32_t pos = out + (ex >> 16) + min(eq_before, need);
+                if (pos < k) r.dst[pos] = st_idx[i];
+            }
+            const uint32_t teq = min(tot & 0xffffu, need);
+            out += (tot >> 16) + teq;
+            need -= teq;
+        }
+        return;
+    }
+    // too many entries share the top bits: the other two radix steps and the
+    // ordered write each take a pass over the row
+    for (int p = 1; p < 3; ++p) {
+        clear();
+        row_tiles(src, n, [&](const uint32_t (&x)[kRowPer], int cnt, int64_t) {
+#pragma unroll
+            for (int i = 0; i < kRowPer; ++i)
+                if (i < cnt) count(p, x[i]);
+            return true;
+        });
+        __syncthreads();
+        pick(p);
     }
     // every entry above T, and the krem lowest-index entries equal to T, in
     // ascending index order; the tile's scan carries both counts (above in
@@ -378,14 +463,14 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
                 ++eq_seen;
             }
             if (take) {
-                if (pos < (uint32_t)r.k) r.dst[pos] = (int32_t)(e + i);
+                if (pos < k) r.dst[pos] = (int32_t)(e + i);
                 ++pos;
             }
         }
         const uint32_t teq = min(tot & 0xffffu, need);
         base += (tot >> 16) + teq;
         need -= teq;
-        return base < (uint32_t)r.k;                   // every selected entry written
+        return base < k;                              // every selected entry written
     });
 }
 
