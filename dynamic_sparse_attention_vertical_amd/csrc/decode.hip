@@ -30,7 +30,7 @@ constexpr int kD = 128;           // head_dim
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 256;
 constexpr int kMaxG = 8;          // q heads scored together per K pass
-constexpr int kU = 4;             // rows per 16-lane group in flight
+constexpr int kU = 8;             // rows per 16-lane group in flight
 
 // float score -> 32-bit key that orders like the score (and back)
 __device__ __forceinline__ uint32_t order_key(float s) {

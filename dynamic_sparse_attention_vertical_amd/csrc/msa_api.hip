@@ -195,10 +195,10 @@ DecodeLayout decode_layout(const msa_problem *p) {
     // that fit on the chip at once): with a few large chunks per kv head the
     // last round runs a handful of workgroups alone (1600 chunks of 4096 keys:
     // 0.558 ms per 100K-key step against 0.484 with 24576 chunks of 261).
-    // Chunks are whole multiples of the 128 rows a workgroup loads per step.
+    // Chunks are whole multiples of the 256 rows a workgroup loads per step.
     int64_t ck = (n * p->n_kv_heads + 24575) / 24576;
-    ck = (ck + 64) / 128 * 128;
-    if (ck < 128) ck = 128;
+    ck = (ck + 128) / 256 * 256;
+    if (ck < 256) ck = 256;
     L.chunk_keys = ck;
     L.nchunks = (int32_t)((n + ck - 1) / ck);
     L.nslices = (int32_t)((n + msa::kTopkSlice - 1) / msa::kTopkSlice);
