@@ -68,6 +68,29 @@ def measured_traffic(workload):
         entry["write_kib_per_step"] * 1024 * rec["write_calib"]
 
 
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+
+
+def measured_decode_traffic(workload):
+    """HBM bytes of one decode step (scores, stats, top-k and attend kernels)
+    from the committed rocprofv3 counter runs, scaled like measured_traffic,
+    or None if absent or taken on a different source of those kernels."""
+    import hashlib
+    try:
+        rec = json.load(open(DECODE_TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    csrc = os.path.dirname(ATTN_SRC)
+    for name, sha in rec.get("src_sha", {}).items():
+        if hashlib.sha256(open(os.path.join(csrc, name), "rb").read()).hexdigest()[:16] != sha:
+            return None
+    entry = rec.get("workloads", {}).get(workload)
+    if not entry:
+        return None
+    return entry["fetch_kib_per_step"] * 1024 * rec["fetch_calib"] + \
+        entry["write_kib_per_step"] * 1024 * rec["write_calib"]
+
+
 def phase_launches(n):
     """Launches of one sparse prefill at the default phase length: the
     grouped walk, then one per key phase (a single launch when one phase
@@ -256,8 +279,10 @@ def bench_decode(args, dw):
         },
         "roofline": {"bound": "hbm", "kernel": "decode_scores_kernel + top-k + decode_attend_kernel (one step)",
                      "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                     "traffic_source": "no counter run of the decode step is committed"},
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": measured_decode_traffic(dw.name),
+                     "traffic_source": ("rocprofv3 FETCH_SIZE + WRITE_SIZE of the same source, committed in "
+                                        "profiles/decode_traffic.json (null when the decode, top-k or layout "
+                                        "source has changed since)")},
     }
     print(json.dumps(res), flush=True)
 
