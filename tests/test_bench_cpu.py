@@ -1,5 +1,5 @@
 """bench.py logic that needs no GPU: the phase-launch count, the counter
-traffic record's source-hash guard, the refusal of more than one GPU, and the
+traffic records' source-hash guards (prefill and decode), the refusal of more than one GPU, and the
 band workload's shape."""
 
 import json
@@ -35,6 +35,23 @@ def test_traffic_record_follows_the_kernel_source(tmp_path, monkeypatch):
     rec["attention_src_sha"] = "0" * 16                     # taken on another kernel source
     f.write_text(json.dumps(rec))
     assert bench.measured_traffic("w") is None
+
+
+def test_decode_traffic_record_follows_the_sources(tmp_path, monkeypatch):
+    import hashlib
+    csrc = os.path.join(ROOT, "dynamic_sparse_attention_vertical_amd", "csrc")
+    sha = {n: hashlib.sha256(open(os.path.join(csrc, n), "rb").read()).hexdigest()[:16]
+           for n in ("decode.hip", "topk.hip", "msa_api.hip")}
+    rec = {"workloads": {"d": {"fetch_kib_per_step": 4.0, "write_kib_per_step": 1.0}},
+           "src_sha": sha, "fetch_calib": 2.0, "write_calib": 1.0}
+    f = tmp_path / "d.json"
+    f.write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "DECODE_TRAFFIC_FILE", str(f))
+    assert bench.measured_decode_traffic("d") == 4.0 * 1024 * 2.0 + 1.0 * 1024
+    assert bench.measured_decode_traffic("other") is None
+    rec["src_sha"]["topk.hip"] = "0" * 16                   # taken on another top-k source
+    f.write_text(json.dumps(rec))
+    assert bench.measured_decode_traffic("d") is None
 
 
 def test_more_than_one_gpu_is_refused():
