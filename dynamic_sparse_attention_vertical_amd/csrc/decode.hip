@@ -131,16 +131,20 @@ __global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a, i
         }
     }
     const T *kp = reinterpret_cast<const T *>(a.k) + (int64_t)kvh * a.stride * kD;
-    uint32_t *krow = a.keys + (int64_t)(kvh * G + g0 + min(hl, gcount - 1)) * a.n;
     const int64_t j0 = (int64_t)blockIdx.x * a.chunk_keys;
     const int64_t j1 = min(j0 + a.chunk_keys, a.n);
     float m = -INFINITY, l = 0.f;
     constexpr int kUs = kPairs ? 2 * kU : kU;               // bf16 rows are half the registers
-    // one step: rows jb + 16 u, u < kUs, of this 16-lane row group; all of
-    // them inside the chunk (kFull: loads without conditions, so that the
-    // compiler waits for each row's load alone), or some past its end
-    auto step = [&](int64_t jb, auto full) {
+    // One step: the workgroup's 16 kUs consecutive keys from sb, rows sb +
+    // 4 wave + sub + 16 u (u < kUs) in this 16-lane row group; all of them
+    // inside the chunk (kFull: loads without conditions, so that the compiler
+    // waits for each row's load alone), or some past its end.  The step's
+    // score keys are gathered in LDS and leave as 16-byte row stores.
+    constexpr int kStep = 16 * kUs;
+    __shared__ uint32_t sk[kG][kStep];
+    auto step = [&](int64_t sb, auto full) {
         constexpr bool kFull = decltype(full)::value;
+        const int64_t jb = sb + wave * 4 + sub;
         float kx[kUs][8];
         u32x4 kw[kUs];
 #pragma unroll
@@ -181,16 +185,36 @@ __global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a, i
             }
             const float sc = reduce_scatter16<kG>(d, lane) * a.scale_log2;
             if (owner) {
-                krow[j] = order_key(sc);
+                sk[hl][wave * 4 + sub + 16 * u] = order_key(sc);
                 const float mn = fmaxf(m, sc);
                 l = l * __builtin_amdgcn_exp2f(m - mn) + __builtin_amdgcn_exp2f(sc - mn);
                 m = mn;
             }
         }
+        __syncthreads();
+        // the step's keys of every head: 16 bytes per thread and store
+        const bool vec = (a.n & 3) == 0;                   // key rows start 16-byte aligned
+        for (int c = threadIdx.x; c < gcount * (kStep / 4); c += kThreads) {
+            const int hh = c / (kStep / 4), q4 = c % (kStep / 4);
+            const int64_t key = sb + 4 * q4;
+            uint32_t *dst = a.keys + (int64_t)(kvh * G + g0 + hh) * a.n + key;
+            const uint32_t *srcw = &sk[hh][4 * q4];
+            if (vec && (kFull || key + 3 < j1)) {
+                *reinterpret_cast<u32x4 *>(dst) = u32x4{srcw[0], srcw[1], srcw[2], srcw[3]};
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (key + e < j1) dst[e] = srcw[e];
+            }
+        }
+        __syncthreads();                                   // sk is free for the next step
     };
-    int64_t jb = j0 + wave * 4 + sub;
-    for (; jb + 16 * (kUs - 1) < j1; jb += 16 * kUs) step(jb, std::true_type{});
-    if (jb < j1) step(jb, std::false_type{});
+    for (int64_t sb = j0; sb < j1; sb += kStep) {
+        if (sb + kStep <= j1)
+            step(sb, std::true_type{});
+        else
+            step(sb, std::false_type{});
+    }
     // the chunk's (max, sum) per head: owners of one head sit at the same
     // position in each row group; combine the 4 row groups, then the waves
     auto comb = [](float &mg, float &lg, float mo, float lo) {
