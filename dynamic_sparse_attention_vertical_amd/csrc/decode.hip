@@ -141,8 +141,10 @@ __global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a, i
     // waits for each row's load alone), or some past its end.  The step's
     // score keys are gathered in LDS and leave as 16-byte row stores.
     constexpr int kStep = 16 * kUs;
-    __shared__ uint32_t sk[kG][kStep];
+    __shared__ uint32_t skb[2][kG][kStep];
+    int sbuf = 0;
     auto step = [&](int64_t sb, auto full) {
+        uint32_t (&sk)[kG][kStep] = skb[sbuf];
         constexpr bool kFull = decltype(full)::value;
         const int64_t jb = sb + wave * 4 + sub;
         float kx[kUs][8];
@@ -207,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a, i
                     if (key + e < j1) dst[e] = srcw[e];
             }
         }
-        __syncthreads();                                   // sk is free for the next step
+        sbuf ^= 1;                                         // the next step fills the other buffer
     };
     for (int64_t sb = j0; sb < j1; sb += kStep) {
         if (sb + kStep <= j1)
