@@ -805,14 +805,30 @@ void attn_fwd_kernel(AttnArgs a) {
 
     // where tile t's keys come from (one scalar load per block tile), and the
     // chunk of it in half hf
-    // grouped walk: the hole at or after the current tile (hx, hy) and the
-    // first column not before it; calls come with t non-decreasing
-    int hp = 0, cp = 0, hx = INT_MAX, hy = INT_MAX;
+    // grouped walk: the hole at or after the current tile (hx, hy), the hole
+    // after it (nx, ny) and the first column not before the tile (cv, at
+    // index cp), each read from LDS one use ahead so that a tile touching a
+    // hole rarely waits for a read; calls come with t non-decreasing
+    // (The prefetched values stay as loaded, in vector registers, and become
+    // uniform only where they are used, so the LDS read is waited for there.)
+    int hp = 0, cp = 0, hx = INT_MAX, hy = INT_MAX, nxv = INT_MAX, nyv = INT_MAX, cvv = INT_MAX;
     auto hole_at = [&](int j, int &x, int &y) {
         x = j < nhole ? __builtin_amdgcn_readfirstlane(glist[wave][2 * j]) : INT_MAX;
         y = j < nhole ? __builtin_amdgcn_readfirstlane(glist[wave][2 * j + 1]) : INT_MAX;
     };
-    if constexpr (kGrp) hole_at(0, hx, hy);
+    auto hole_ahead = [&](int j) {
+        nxv = j < nhole ? glist[wave][2 * j] : INT_MAX;
+        nyv = j < nhole ? glist[wave][2 * j + 1] : INT_MAX;
+    };
+    auto col_ahead = [&](int c) { cvv = c < ncl_g ? glist[wave][2 * kGrpHoles + c] : INT_MAX; };
+    auto col_at = [&](int c) {
+        return c < ncl_g ? __builtin_amdgcn_readfirstlane(glist[wave][2 * kGrpHoles + c]) : INT_MAX;
+    };
+    if constexpr (kGrp) {
+        hole_at(0, hx, hy);
+        hole_ahead(1);
+        col_ahead(0);
+    }
     using Src = typename std::conditional<kExact, ExactSrc, ChunkSrc>::type;
     auto tile_of = [&](int t) {
         Src s;
@@ -852,7 +868,12 @@ void attn_fwd_kernel(AttnArgs a) {
         }
         if constexpr (kGrp) {
             const int t0 = t * kBK;
-            while (hy <= t0) hole_at(++hp, hx, hy);
+            while (hy <= t0) {
+                ++hp;
+                hx = __builtin_amdgcn_readfirstlane(nxv);
+                hy = __builtin_amdgcn_readfirstlane(nyv);
+                hole_ahead(hp + 1);
+            }
             if (hx < t0 + kBK) {                            // some hole reaches into the tile
                 uint64_t cut = 0;
                 int j = hp, x = hx, y = hy;
@@ -860,15 +881,21 @@ void attn_fwd_kernel(AttnArgs a) {
                     const int lo = max(x, t0) - t0, len = min(y, t0 + kBK) - t0 - lo;
                     cut |= len >= 64 ? ~0ull : ((1ull << len) - 1) << lo;
                     if (y > t0 + kBK) break;
-                    hole_at(++j, x, y);
+                    ++j;
+                    if (j == hp + 1) {
+                        x = __builtin_amdgcn_readfirstlane(nxv);
+                        y = __builtin_amdgcn_readfirstlane(nyv);
+                    } else {
+                        hole_at(j, x, y);
+                    }
                 }
-                auto col = [&](int c) { return __builtin_amdgcn_readfirstlane(glist[wave][2 * kGrpHoles + c]); };
-                while (cp < ncl_g && col(cp) < t0) ++cp;
-                for (int c = cp; c < ncl_g; ++c) {
-                    const int key = col(c);
-                    if (key >= t0 + kBK) break;
-                    cut &= ~(1ull << (key - t0));
+                int cv = __builtin_amdgcn_readfirstlane(cvv);
+                if (cv < t0) {
+                    do cv = col_at(++cp);
+                    while (cv < t0);
+                    col_ahead(cp);
                 }
+                for (int c = cp, key = cv; key < t0 + kBK; key = col_at(++c)) cut &= ~(1ull << (key - t0));
                 s.allow = ~cut;
                 s.masked = true;
             }
