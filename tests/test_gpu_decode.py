@@ -74,6 +74,8 @@ def check_decode(q, k, v, topk, fp32, what, given=None):
     (128, 32, 3000 + 5, 200, False),   # 128 rows: one top-k workgroup per row
     (256, 64, 1100, 1100, False),      # every key, one workgroup per row
     (128, 32, 20000, 15000, False),    # one workgroup per row, more entries than it stages in LDS
+    (8, 2, 70, 9, False),              # a cache shorter than one scoring chunk
+    (128, 32, 101, 17, False),         # the same with one workgroup per row
 ])
 def test_decode_topk(hq, hkv, n, topk, fp32):
     q, k, v = cache(hq, hkv, n, seed=n + topk, fp32=fp32)
