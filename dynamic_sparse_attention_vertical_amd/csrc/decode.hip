@@ -10,8 +10,9 @@
 //            written as order-preserving 32-bit keys, with each chunk's
 //            running max and sum of 2^s (the dense softmax denominator);
 //   stats    the dense log-sum-exp of every q head from those partials;
-//   select   exact top-k of the keys per head (the radix select of topk.hip,
-//            ties to the lower index, indices ascending), or a given set;
+//   select   exact top-k of the keys per head (ties to the lower index,
+//            indices ascending; topk.hip: one workgroup per row when there are
+//            many rows, else the sliced radix select), or a given set;
 //   attend   softmax over the selected scores and the weighted sum of their V
 //            rows; the retrieved share of the dense attention mass is
 //            2^(lse_selected - lse_dense).
@@ -98,10 +99,10 @@ template <int kG> __device__ __forceinline__ int head_of(int lane) {
 }
 
 // Grid (chunk, kv head): heads g0 .. g0 + gcount - 1 (gcount <= kG) of the kv
-// head's group, keys [chunk * chunk_keys, ...).  A wave scores 4 keys per
-// step (16 lanes per key, 8 elements each, kU keys per row group in flight);
-// after the reduce-scatter each lane owns one head of its key and keeps that
-// head's running max and sum.
+// head's group, keys [chunk * chunk_keys, ...).  A wave scores 4 keys at a
+// time (16 lanes per key, 8 elements each, 2 kU keys per row group in flight
+// for bf16); after the reduce-scatter each lane owns one head of its key and
+// keeps that head's running max and sum.
 template <typename T, int kG>
 __global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a, int g0) {
     const int kvh = blockIdx.y;
