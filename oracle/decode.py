@@ -32,27 +32,43 @@ def _logsumexp(x: np.ndarray) -> float:
     return float(m + np.log(np.exp(x - m).sum()))
 
 
-def decode_sparse_attention(q, k, v, topk: int, idx=None, scale: float | None = None):
+def decode_sparse_attention(q, k, v, topk: int, idx=None, scale: float | None = None, cache_len=None):
     """Attention of each query row over a subset of the cache: the exact
     top-k keys by score (ties to the lower index, ascending), or the given
     idx [Hq, k].  Returns out [Hq, D], lse [Hq] (natural log over the chosen
     keys), recovery [Hq] = sum over chosen e^s / sum over all e^s, and the
-    chosen indices."""
+    chosen indices.
+
+    cache_len [Hkv] (optional): kv head g holds keys 0 .. cache_len[g] - 1
+    only; the rows past them are capacity, not keys.  Reading: a key that is
+    not in the cache takes no part in the attention, so it scores -inf: it
+    gets no weight and is outside the dense sum.  The top-k is then taken over
+    those scores as before, so a head whose cache holds fewer than topk keys
+    selects all of them and, by the tie rule, the lowest positions past its
+    end (with no weight).  A head with no key at all: out 0, lse -inf,
+    recovery 0."""
     s = decode_scores(q, k, scale)
     v = as_f64(v)
-    Hq = s.shape[0]
+    Hq, N = s.shape
     G = Hq // v.shape[0]
+    if cache_len is not None:
+        for h in range(Hq):
+            s[h, int(cache_len[h // G]):] = -np.inf
     if idx is None:
         idx = np.stack([top_k_indices(s[h], topk) for h in range(Hq)])
     idx = np.asarray(idx, dtype=np.int64)
     out = np.zeros((Hq, v.shape[2]))
-    lse = np.zeros(Hq)
+    lse = np.full(Hq, -np.inf)
     rec = np.zeros(Hq)
     for h in range(Hq):
         sel = s[h, idx[h]]
-        m = sel.max()
-        p = np.exp(sel - m)
-        out[h] = (p[:, None] * v[h // G][idx[h]]).sum(axis=0) / p.sum()
+        keep = sel > -np.inf
+        if not keep.any():
+            continue
+        m = sel[keep].max()
+        p = np.where(keep, np.exp(sel - m), 0.0)
+        rows = np.where(keep[:, None], v[h // G][idx[h]], 0.0)
+        out[h] = (p[:, None] * rows).sum(axis=0) / p.sum()
         lse[h] = m + np.log(p.sum())
-        rec[h] = np.exp(lse[h] - _logsumexp(s[h]))
+        rec[h] = np.exp(lse[h] - _logsumexp(s[h][s[h] > -np.inf]))
     return out, lse, rec, idx

@@ -598,6 +598,91 @@ def test_decode_sparse_closed_forms():
     np.testing.assert_allclose(rec, 7 / n, atol=1e-12)
 
 
+def _brute_decode_varlen(q, k, v, topk, scale, lens):
+    """Plain loops over caches of different lengths: kv head g has the keys
+    j < lens[g] only.  The top-k of those by score (ties to the lower index);
+    when fewer than topk exist, the selection is filled with the positions
+    lens[g], lens[g] + 1, ... (no weight).  Softmax, V sum and kept share over
+    the keys that exist; no key: out 0, lse -inf, kept share 0."""
+    Hq, D = q.shape
+    G = Hq // k.shape[0]
+    outs, lses, recs, idxs = [], [], [], []
+    for h in range(Hq):
+        g = h // G
+        L = int(lens[g])
+        s = [scale * sum(float(q[h, d]) * float(k[g, j, d]) for d in range(D)) for j in range(L)]
+        sel = sorted(sorted(range(L), key=lambda j: (-s[j], j))[:topk])
+        idxs.append(sel + list(range(L, L + topk - len(sel))))
+        if not sel:
+            outs.append([0.0] * D)
+            lses.append(-math.inf)
+            recs.append(0.0)
+            continue
+        m = max(s[j] for j in sel)
+        w = [math.exp(s[j] - m) for j in sel]
+        tot = sum(w)
+        outs.append([sum(w[t] * float(v[g, sel[t], d]) for t in range(len(sel))) / tot for d in range(D)])
+        lses.append(m + math.log(tot))
+        m_all = max(s)
+        recs.append(tot * math.exp(m - m_all) / sum(math.exp(x - m_all) for x in s))
+    return np.array(outs), np.array(lses), np.array(recs), np.array(idxs)
+
+
+@pytest.mark.parametrize("hq,hkv,n,d,topk,lens,seed", [
+    (4, 2, 12, 4, 5, (7, 12), 0),        # one short cache, one full
+    (6, 3, 10, 3, 4, (0, 3, 4), 1),      # empty, shorter than topk, exactly topk
+    (2, 2, 9, 5, 9, (9, 1), 2),          # topk = capacity; a single key
+])
+def test_decode_varlen_brute_force(hq, hkv, n, d, topk, lens, seed):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((hq, d))
+    k = rng.standard_normal((hkv, n, d))
+    v = rng.standard_normal((hkv, n, d))
+    for g, L in enumerate(lens):                       # rows past a cache's end are not keys
+        k[g, L:] = np.nan
+        v[g, L:] = np.nan
+    if lens[0] > 5:
+        k[0, 2] = k[0, 5]                              # equal scores inside the cache
+    out, lse, rec, idx = oracle.decode_sparse_attention(q, k, v, topk, scale=0.6, cache_len=np.array(lens))
+    bo, bl, br, bi = _brute_decode_varlen(q, k, v, topk, 0.6, lens)
+    np.testing.assert_array_equal(idx, bi)
+    np.testing.assert_allclose(out, bo, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(np.isneginf(lse), np.isneginf(bl))
+    fin = np.isfinite(bl)
+    np.testing.assert_allclose(lse[fin], bl[fin], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(rec, br, rtol=1e-12, atol=1e-12)
+
+
+def test_decode_varlen_reduces_to_shorter_caches():
+    """A cache of length L inside a larger capacity gives what a cache of
+    exactly L keys gives (L >= topk); with L < topk, the dense attention of
+    the last row of a causal prefill over those L keys, recovery 1."""
+    rng = np.random.default_rng(5)
+    hq, hkv, n, d = 6, 3, 50, 16
+    q = rng.standard_normal((hq, d))
+    k = rng.standard_normal((hkv, n, d))
+    v = rng.standard_normal((hkv, n, d))
+    lens = np.array([31, 50, 12])
+    out, lse, rec, idx = oracle.decode_sparse_attention(q, k, v, 20, cache_len=lens)
+    for g in range(hkv):
+        L = int(lens[g])
+        hs = slice(2 * g, 2 * g + 2)
+        if L >= 20:
+            o2, l2, r2, i2 = oracle.decode_sparse_attention(q[hs], k[g:g + 1, :L], v[g:g + 1, :L], 20)
+            np.testing.assert_array_equal(idx[hs], i2)
+            np.testing.assert_allclose(out[hs], o2, atol=1e-12)
+            np.testing.assert_allclose(lse[hs], l2, atol=1e-12)
+            np.testing.assert_allclose(rec[hs], r2, atol=1e-12)
+        else:
+            qf = np.zeros((2, L, d))
+            qf[:, -1] = q[hs]
+            dense, dlse = oracle.dense_attention(qf, k[g:g + 1, :L], v[g:g + 1, :L])
+            np.testing.assert_allclose(out[hs], dense[:, -1], atol=1e-12)
+            np.testing.assert_allclose(lse[hs], dlse[:, -1], atol=1e-12)
+            np.testing.assert_allclose(rec[hs], 1.0, atol=1e-12)
+            np.testing.assert_array_equal(idx[hs], np.tile(np.arange(20), (2, 1)))
+
+
 def test_decode_scores_gqa_and_given_keys():
     """q head h reads kv head h // (Hq / Hkv): swapping the two kv heads swaps
     the scores of their q heads.  A given key set is used as is."""
