@@ -227,6 +227,7 @@ def bench_decode(args, dw):
         f"cache {dw.cache_len}, top-{dw.topk}")
     x = make_decode_inputs(dw, device="cuda")
     q, k, v = x["q"], x["k"], x["v"]
+    lens = x.get("cache_lens")                # sequences of different lengths: msa_decode_sparse_varlen
     hq, hkv, n = q.shape[0], k.shape[0], dw.cache_len
     stream = torch.cuda.current_stream()
     ws = torch.empty(msa.decode_sparse_workspace_bytes(hq, hkv, n, q.dtype), dtype=torch.uint8, device="cuda")
@@ -235,7 +236,8 @@ def bench_decode(args, dw):
     rec = torch.empty(hq, dtype=torch.float32, device="cuda")
 
     def step():
-        msa.decode_sparse(q, k, v, dw.topk, idx=idx, out=out, recovery=rec, workspace=ws, stream=stream)
+        msa.decode_sparse(q, k, v, dw.topk, idx=idx, out=out, recovery=rec, cache_lens=lens, workspace=ws,
+                          stream=stream)
 
     for i in range(args.warmup):
         step()
@@ -249,7 +251,7 @@ def bench_decode(args, dw):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
     recovery = rec.clone()
-    k_bytes = hkv * n * 128 * 2
+    k_bytes = sum(dw.length(b) for b in range(dw.batch)) * dw.n_kv_heads * 128 * 2   # the keys that exist
     v_bytes = hq * dw.topk * 128 * 2
     alg = k_bytes + v_bytes
     gbs = alg / (ms * 1e-3) / 1e9
@@ -268,7 +270,8 @@ def bench_decode(args, dw):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": dw.name, "batch": dw.batch, "q_heads": dw.n_q_heads, "kv_heads": dw.n_kv_heads,
-                   "cache_len": n, "topk": dw.topk, "head_dim": 128},
+                   "cache_len": n, "topk": dw.topk, "head_dim": 128,
+                   **({"cache_lens": list(dw.lengths)} if dw.lengths else {})},
         "breakdown": {
             "ms_floor_sparse_step": round(alg / PEAK_HBM_GBS / 1e6, 4),
             "ms_floor_dense_decode": round(2 * k_bytes / PEAK_HBM_GBS / 1e6, 4),

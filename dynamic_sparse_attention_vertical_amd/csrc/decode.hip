@@ -17,7 +17,12 @@
 //            rows; the retrieved share of the dense attention mass is
 //            2^(lse_selected - lse_dense).
 // Layout: q [hq, 128], K and V [hkv, stride, 128], out [hq, 128], one query
-// per head (a batch of sequences is folded into the heads).
+// per head (a batch of sequences is folded into the heads).  Caches may be
+// shorter than the capacity n (a length per kv head): a position past a
+// cache's length holds no key (score -inf), so no kernel reads its K or V
+// row or a score for it: the dense sum and the top-k run over the positions
+// before it, and a selection longer than the cache is completed with the
+// lowest positions past its end, which get no weight.
 #include "common.h"
 #include "kernels.h"
 
@@ -40,6 +45,12 @@ __device__ __forceinline__ uint32_t order_key(float s) {
 }
 __device__ __forceinline__ float key_score(uint32_t u) {
     return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+// keys in kv head g's cache (the capacity n unless lengths are given)
+__device__ __forceinline__ int64_t cache_keys(const DecodeArgs &a, int g) {
+    if (a.lens == nullptr) return a.n;
+    const int64_t len = a.lens[g];
+    return len < 0 ? 0 : (len > a.n ? a.n : len);
 }
 
 // 8 consecutive elements of a row as floats (16 lanes cover a 128-wide row)
@@ -134,13 +145,15 @@ __global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a, i
     const T *kp = reinterpret_cast<const T *>(a.k) + (int64_t)kvh * a.stride * kD;
     const int64_t j0 = (int64_t)blockIdx.x * a.chunk_keys;
     const int64_t j1 = min(j0 + a.chunk_keys, a.n);
+    const int64_t jv = min(j1, max(j0, cache_keys(a, kvh)));   // keys [j0, jv) are in the cache
     float m = -INFINITY, l = 0.f;
     constexpr int kUs = kPairs ? 2 * kU : kU;               // bf16 rows are half the registers
     // One step: the workgroup's 16 kUs consecutive keys from sb, rows sb +
     // 4 wave + sub + 16 u (u < kUs) in this 16-lane row group; all of them
-    // inside the chunk (kFull: loads without conditions, so that the compiler
-    // waits for each row's load alone), or some past its end.  The step's
-    // score keys are gathered in LDS and leave as 16-byte row stores.
+    // inside the chunk and the cache (kFull: loads without conditions, so
+    // that the compiler waits for each row's load alone), or some past the
+    // end of either, which are neither read nor given a score key.  The
+    // step's score keys are gathered in LDS and leave as 16-byte row stores.
     constexpr int kStep = 16 * kUs;
     __shared__ uint32_t skb[2][kG][kStep];
     int sbuf = 0;
@@ -155,9 +168,9 @@ __global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a, i
             const int64_t j = jb + 16 * u;
             if constexpr (kPairs) {
                 // non-temporal: each K row is read once per pass (8% faster at 100K x 64 kv heads)
-                kw[u] = (kFull || j < j1) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kp + j * kD + col))
+                kw[u] = (kFull || j < jv) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kp + j * kD + col))
                                           : u32x4{0u, 0u, 0u, 0u};
-            } else if (kFull || j < j1) {
+            } else if (kFull || j < jv) {
                 load8<T>(kp + j * kD + col, kx[u]);
             } else {
 #pragma unroll
@@ -167,7 +180,7 @@ __global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a, i
 #pragma unroll
         for (int u = 0; u < kUs; ++u) {
             const int64_t j = jb + 16 * u;
-            if (!kFull && j >= j1) break;
+            if (!kFull && j >= jv) break;
             float d[kG];
 #pragma unroll
             for (int g = 0; g < kG; ++g) {
@@ -202,18 +215,18 @@ __global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a, i
             const int64_t key = sb + 4 * q4;
             uint32_t *dst = a.keys + (int64_t)(kvh * G + g0 + hh) * a.n + key;
             const uint32_t *srcw = &sk[hh][4 * q4];
-            if (vec && (kFull || key + 3 < j1)) {
+            if (vec && (kFull || key + 3 < jv)) {
                 *reinterpret_cast<u32x4 *>(dst) = u32x4{srcw[0], srcw[1], srcw[2], srcw[3]};
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (key + e < j1) dst[e] = srcw[e];
+                    if (key + e < jv) dst[e] = srcw[e];
             }
         }
         sbuf ^= 1;                                         // the next step fills the other buffer
     };
-    for (int64_t sb = j0; sb < j1; sb += kStep) {
-        if (sb + kStep <= j1)
+    for (int64_t sb = j0; sb < jv; sb += kStep) {
+        if (sb + kStep <= jv)
             step(sb, std::true_type{});
         else
             step(sb, std::false_type{});
@@ -275,12 +288,13 @@ __global__ __launch_bounds__(kAttThreads) void decode_attend_kernel(DecodeArgs a
     const int col = (lane & 15) * 8, slot = wave * 4 + (lane >> 4);   // kSlots row slots
     const int32_t *idx = a.idx + (int64_t)h * a.topk;
     const uint32_t *keys = a.keys + (int64_t)h * a.n;
+    const int64_t nv = cache_keys(a, h / G);   // selected positions at or past it hold no key: no score, no V
     __shared__ float red[kAttThreads / 64];
     // the selected scores' maximum
     float mx = -INFINITY;
     for (int t = threadIdx.x; t < a.topk; t += kAttThreads) {
         const int64_t j = min(max((int64_t)idx[t], (int64_t)0), a.n - 1);
-        mx = fmaxf(mx, key_score(keys[j]));
+        if (j < nv) mx = fmaxf(mx, key_score(keys[j]));
     }
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
@@ -300,8 +314,8 @@ __global__ __launch_bounds__(kAttThreads) void decode_attend_kernel(DecodeArgs a
         for (int u = 0; u < kU; ++u) {
             const int t = tb + kSlots * u;
             p[u] = 0.f;
-            if (t < a.topk) {
-                const int64_t j = min(max((int64_t)idx[t], (int64_t)0), a.n - 1);
+            const int64_t j = t < a.topk ? min(max((int64_t)idx[t], (int64_t)0), a.n - 1) : a.n;
+            if (j < nv) {
                 p[u] = __builtin_amdgcn_exp2f(key_score(keys[j]) - mx);
                 load8<T>(vp + j * kD + col, vx[u]);
             } else {

@@ -102,6 +102,9 @@ struct TopkArgs {
     uint32_t *cnt;               // [2*hq][nslices][2]
     uint32_t *off;               // [2*hq][nslices][2]
     int32_t rows;                // rows selected: 0 = 2*hq (both sets); else the first rows, all from src0
+    const int32_t *row_len = nullptr;   // NULL: every row has n entries; else row r has
+    int32_t row_len_div = 1;            //   row_len[r / row_len_div], clamped into [0, n]; a row with
+                                        //   at most k of them selects 0 .. k - 1
 };
 
 constexpr int kTopkSlice = 4096;   // elements per top-k workgroup slice
@@ -128,6 +131,7 @@ struct DecodeArgs {
     float *lse2_all;             // [hq] dense log2-sum-exp
     int64_t chunk_keys;
     int32_t nchunks;
+    const int32_t *lens;         // [hkv] keys in each kv head's cache, clamped into [0, n] (NULL: n)
 };
 
 hipError_t launch_decode_scores(const DecodeArgs &a, int dtype, hipStream_t s);

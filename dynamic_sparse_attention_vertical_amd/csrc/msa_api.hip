@@ -493,17 +493,17 @@ size_t msa_decode_sparse_workspace(const msa_problem *p) {
     return decode_layout(p).total;
 }
 
-int msa_decode_sparse(const msa_problem *p, const void *q, const void *k, const void *v, int32_t topk,
-                      int32_t *idx, int32_t flags, void *workspace, size_t workspace_bytes, void *out, float *lse,
-                      float *recovery, void *stream) {
+static int run_decode_sparse(const msa_problem *p, const void *q, const void *k, const void *v,
+                             const int32_t *cache_lens, int32_t topk, int32_t *idx, int32_t flags, void *workspace,
+                             size_t workspace_bytes, void *out, float *lse, float *recovery, void *stream) {
     int st = check_problem(p);
     if (st) return st;
     if (!q || !k || !v || !out || !idx) return fail(MSA_ERR_NULL, "a required pointer is NULL");
     if ((st = check_rows(q, k, v, out))) return st;
     if ((flags & ~MSA_DECODE_GIVEN_KEYS) != 0) return fail(MSA_ERR_RANGE, "unknown flags 0x%x", (unsigned)flags);
     if (topk < 1 || topk > p->seq_len) return fail(MSA_ERR_RANGE, "topk must lie in [1, seq_len] (got %d)", topk);
-    if (off_align(idx, 4) || off_align(lse, 4) || off_align(recovery, 4))
-        return fail(MSA_ERR_RANGE, "idx, lse and recovery must be 4-byte aligned");
+    if (off_align(idx, 4) || off_align(lse, 4) || off_align(recovery, 4) || off_align(cache_lens, 4))
+        return fail(MSA_ERR_RANGE, "idx, lse, recovery and cache_lens must be 4-byte aligned");
     const DecodeLayout L = decode_layout(p);
     if (!workspace) return fail(MSA_ERR_NULL, "workspace is NULL (%zu bytes needed)", L.total);
     if (workspace_bytes < L.total) return fail(MSA_ERR_WORKSPACE, "workspace %zu bytes, %zu needed", workspace_bytes, L.total);
@@ -527,6 +527,7 @@ int msa_decode_sparse(const msa_problem *p, const void *q, const void *k, const 
     a.lse2_all = at<float>(workspace, L.off_lse);
     a.chunk_keys = L.chunk_keys;
     a.nchunks = L.nchunks;
+    a.lens = cache_lens;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if ((st = launch_status(msa::launch_decode_scores(a, p->dtype, s), "decode scores"))) return st;
     if ((flags & MSA_DECODE_GIVEN_KEYS) == 0) {
@@ -542,12 +543,29 @@ int msa_decode_sparse(const msa_problem *p, const void *q, const void *k, const 
         t.state = at<uint32_t>(workspace, L.off_state);
         t.cnt = at<uint32_t>(workspace, L.off_cnt);
         t.off = at<uint32_t>(workspace, L.off_off);
+        t.row_len = cache_lens;                      // q head h reads kv head h / G's cache
+        t.row_len_div = p->n_q_heads / p->n_kv_heads;
         // one workgroup per row once there are rows for half the chip; fewer
         // rows are split into slices across the chip
         const hipError_t e = t.rows >= 128 ? msa::launch_topk_rows(t, s) : msa::launch_topk(t, s);
         if ((st = launch_status(e, "decode top-k"))) return st;
     }
     return launch_status(msa::launch_decode_attend(a, p->dtype, s), "decode attend");
+}
+
+int msa_decode_sparse(const msa_problem *p, const void *q, const void *k, const void *v, int32_t topk,
+                      int32_t *idx, int32_t flags, void *workspace, size_t workspace_bytes, void *out, float *lse,
+                      float *recovery, void *stream) {
+    return run_decode_sparse(p, q, k, v, nullptr, topk, idx, flags, workspace, workspace_bytes, out, lse, recovery,
+                             stream);
+}
+
+int msa_decode_sparse_varlen(const msa_problem *p, const void *q, const void *k, const void *v,
+                             const int32_t *cache_lens, int32_t topk, int32_t *idx, int32_t flags, void *workspace,
+                             size_t workspace_bytes, void *out, float *lse, float *recovery, void *stream) {
+    if (!cache_lens) return fail(MSA_ERR_NULL, "cache_lens is NULL");
+    return run_decode_sparse(p, q, k, v, cache_lens, topk, idx, flags, workspace, workspace_bytes, out, lse,
+                             recovery, stream);
 }
 
 int msa_sparse_prefill_walk_marks(const msa_problem *p, int32_t phase_keys, size_t *offset,

@@ -42,6 +42,13 @@ __device__ __forceinline__ RowView row_view(const TopkArgs &a, int row) {
     return r;
 }
 
+// entries of a row: n, or the row's own length (clamped into [0, n])
+__device__ __forceinline__ int64_t row_n(const TopkArgs &a, int row) {
+    if (a.row_len == nullptr) return a.n;
+    const int64_t len = a.row_len[row / a.row_len_div];
+    return len < 0 ? 0 : (len > a.n ? a.n : len);
+}
+
 // pass p: bucket bits and the prefix the element must match
 __device__ __forceinline__ int pass_shift(int p) { return p == 0 ? 21 : (p == 1 ? 10 : 0); }
 __device__ __forceinline__ int pass_bits(int p) { return p == 2 ? 10 : 11; }
@@ -86,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(TopkArgs a) {
     const uint32_t prefix = a.state[row * 4 + 0];
     uint32_t x[kPer];
     bool valid[kPer];
-    load_slice(r.src, a.n, e0, x, valid);
+    load_slice(r.src, row_n(a, row), e0, x, valid);
     const int sh = pass_shift(P);
     const int hi_sh = sh + pass_bits(P);         // bits above the bucket must equal prefix
 #pragma unroll
@@ -160,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void topk_count_kernel(TopkArgs a) {
     const uint32_t T = a.state[row * 4 + 0];
     uint32_t x[kPer];
     bool valid[kPer];
-    load_slice(r.src, a.n, e0, x, valid);
+    load_slice(r.src, row_n(a, row), e0, x, valid);
     uint32_t gt = 0, eq = 0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -219,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void topk_write_kernel(TopkArgs a) {
     const uint32_t slice_off = a.off[o], slice_eq = a.off[o + 1];
     uint32_t x[kPer];
     bool valid[kPer];
-    load_slice(r.src, a.n, e0, x, valid);
+    load_slice(r.src, row_n(a, row), e0, x, valid);
     uint32_t gt = 0, eq = 0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -243,6 +250,11 @@ __global__ __launch_bounds__(kThreads) void topk_write_kernel(TopkArgs a) {
             ++pos;
         }
     }
+    // a row with fewer than k entries: every entry is taken (positions
+    // 0 .. len - 1 above), and the selection goes on with the positions after
+    const int64_t len = row_n(a, row);
+    if (blockIdx.x == 0)
+        for (int64_t i = len + threadIdx.x; i < r.k; i += kThreads) r.dst[i] = (int32_t)i;
 }
 
 // ---- One workgroup per row ----
@@ -327,9 +339,13 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
     const int row = blockIdx.x, tid = threadIdx.x;
     const RowView r = row_view(a, row);
     const uint32_t *src = reinterpret_cast<const uint32_t *>(r.src);
-    const int64_t n = a.n;
+    const int64_t n = row_n(a, row);
     const uint32_t k = (uint32_t)r.k;
     uint32_t prefix = 0, krem = k, in_bucket = 0;
+    if (n <= (int64_t)k) {                              // every entry, then the positions after the row's end
+        for (int i = tid; i < (int)k; i += kRowThreads) r.dst[i] = i;
+        return;
+    }
 
     auto clear = [&]() {
         for (int i = tid; i < 2048; i += kRowThreads) hist[i] = 0u;

@@ -54,6 +54,8 @@ _SIGS = {
     "msa_decode_sparse_workspace": (ctypes.c_size_t, [_VP]),
     "msa_decode_sparse": (ctypes.c_int, [_VP, _VP, _VP, _VP, _I32, _VP, _I32, _VP, ctypes.c_size_t, _VP, _VP, _VP,
                                          _VP]),
+    "msa_decode_sparse_varlen": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I32, _VP, _I32, _VP, ctypes.c_size_t, _VP,
+                                                _VP, _VP, _VP]),
     "msa_sparse_prefill_walk_marks": (ctypes.c_int, [_VP, _I32, _VP, _VP]),
     "msa_sparse_prefill_fused": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I32, _VP, _I32, _I32, _I32, _VP,
                                                 ctypes.c_size_t, _VP, _VP, _VP]),
@@ -468,13 +470,18 @@ def decode_sparse_workspace_bytes(n_q_heads: int, n_kv_heads: int, cache_len: in
 def decode_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, topk: int, *, idx: torch.Tensor | None = None,
                   given: bool = False, out: torch.Tensor | None = None, lse: torch.Tensor | bool | None = None,
                   recovery: torch.Tensor | bool | None = None, sm_scale: float = 0.0,
-                  workspace: torch.Tensor | None = None, stream=None):
+                  cache_lens: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
     """One decode step: q [Hq, 128] (one row per head) against the caches k, v
     [Hkv, N, 128] (rows may be strided), attending only to the top-k keys of
     each head by score (idx receives them, ascending) or, with given=True, to
     the keys in idx.  Returns out [Hq, 128] and idx, plus lse and recovery (the
     selected share of the dense attention mass) when asked for (True or a
-    tensor)."""
+    tensor).
+
+    cache_lens: int32 on q's device, [Hkv] (keys in each kv head's cache) or
+    [B] for a batch of B sequences folded into the heads (each length then
+    serves the sequence's Hkv / B kv heads); N is then the capacity and the
+    rows past a length are never read (msa_decode_sparse_varlen)."""
     lib = load()
     if q.dim() != 2 or q.shape[1] != HEAD_DIM or not q.is_contiguous():
         raise MsaError(f"q must be contiguous [heads, {HEAD_DIM}]")
@@ -511,12 +518,22 @@ def decode_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, topk: int, 
     need = int(lib.msa_decode_sparse_workspace(ctypes.byref(p)))
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    _check(lib.msa_decode_sparse(ctypes.byref(p), _dev(q, "q"), _in_dev(k, "k"), _in_dev(v, "v"), topk,
-                                 _dev(idx, "idx"), DECODE_GIVEN_KEYS if given else 0, _dev(workspace, "workspace"),
-                                 workspace.numel() * workspace.element_size(), _dev(out, "out"),
-                                 _dev(extra[0], "lse") if extra[0] is not None else None,
-                                 _dev(extra[1], "recovery") if extra[1] is not None else None, _stream(stream)),
-           "msa_decode_sparse")
+    tail = (topk, _dev(idx, "idx"), DECODE_GIVEN_KEYS if given else 0, _dev(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), _dev(out, "out"),
+            _dev(extra[0], "lse") if extra[0] is not None else None,
+            _dev(extra[1], "recovery") if extra[1] is not None else None, _stream(stream))
+    if cache_lens is None:
+        _check(lib.msa_decode_sparse(ctypes.byref(p), _dev(q, "q"), _in_dev(k, "k"), _in_dev(v, "v"), *tail),
+               "msa_decode_sparse")
+    else:
+        if cache_lens.dtype != torch.int32 or cache_lens.dim() != 1 or cache_lens.device != q.device:
+            raise MsaError("cache_lens must be int32 [kv heads] or [batch] on q's device")
+        nb = cache_lens.shape[0]
+        if nb == 0 or hk % nb != 0:
+            raise MsaError(f"cache_lens has {nb} entries; it needs one per kv head ({hk}) or per sequence")
+        lens = cache_lens.repeat_interleave(hk // nb) if nb != hk else cache_lens.contiguous()
+        _check(lib.msa_decode_sparse_varlen(ctypes.byref(p), _dev(q, "q"), _in_dev(k, "k"), _in_dev(v, "v"),
+                                            _dev(lens, "cache_lens"), *tail), "msa_decode_sparse_varlen")
     res = [out, idx]
     res += [t for t, want in zip(extra, (lse, recovery)) if want is not None and want is not False]
     return tuple(res)

@@ -330,6 +330,25 @@ int msa_decode_sparse(const msa_problem *p, const void *q, const void *k, const 
                       int32_t *idx, int32_t flags, void *workspace, size_t workspace_bytes, void *out, float *lse,
                       float *recovery, void *stream);
 
+/* msa_decode_sparse over caches of different lengths (a batch of sequences at
+ * different positions, folded into the heads as above): kv head g holds the
+ * keys 0 .. cache_lens[g] - 1 of its rows; seq_len is the capacity.  A
+ * position past a cache's length holds no key and scores -inf (the same
+ * slide: the decode step attends over the keys that exist): it is never read,
+ * gets no weight and is outside the dense sum behind recovery.
+ *   cache_lens [n_kv_heads] int32, device memory, 4-byte aligned; each value
+ *     is clamped into [0, seq_len] on the device.
+ *   idx: the top-k as above over those scores, so a cache holding fewer than
+ *     topk keys gives all of them followed by the lowest positions past its
+ *     end (no weight); given keys (MSA_DECODE_GIVEN_KEYS) at or past the end
+ *     get no weight.
+ *   A head whose cache is empty: out 0, lse -inf, recovery 0.
+ * Workspace: msa_decode_sparse_workspace(p).  Errors as msa_decode_sparse;
+ * cache_lens NULL: MSA_ERR_NULL.                                            */
+int msa_decode_sparse_varlen(const msa_problem *p, const void *q, const void *k, const void *v,
+                             const int32_t *cache_lens, int32_t topk, int32_t *idx, int32_t flags, void *workspace,
+                             size_t workspace_bytes, void *out, float *lse, float *recovery, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -96,7 +96,9 @@ WORKLOADS = {
 class DecodeWorkload:
     """One decode step over a batch of key caches: batch sequences of
     cache_len cached tokens, each with the layer's q / kv heads; the decode
-    query of a sequence is the last query row of its synthetic prefill."""
+    query of a sequence is the last query row of its synthetic prefill.  With
+    lengths, sequence b holds lengths[b] tokens in a cache of capacity
+    cache_len."""
     name: str
     batch: int
     n_q_heads: int
@@ -104,29 +106,49 @@ class DecodeWorkload:
     cache_len: int
     topk: int
     seed: int = 0
+    lengths: tuple = ()
+
+    def length(self, b: int) -> int:
+        return self.lengths[b] if self.lengths else self.cache_len
 
     def prefill(self, b: int) -> Workload:
-        return Workload(f"{self.name}_{b}", self.n_q_heads, self.n_kv_heads, self.cache_len, seed=self.seed + b)
+        return Workload(f"{self.name}_{b}", self.n_q_heads, self.n_kv_heads, self.length(b), seed=self.seed + b)
 
 
 DECODE_WORKLOADS = {
     # LLaMA-3-8B attention shape decoding over 100K cached tokens, top-1000
     # keys per head (the talk slides' decoding panel), 8 sequences at once
     "llama3_8b_decode_100k": DecodeWorkload("llama3_8b_decode_100k", 8, 32, 8, 100000, 1000, seed=2001),
+    # the same shape with the sequences at different positions: caches of
+    # capacity 128K holding 4K to 128K tokens (485,584 in all)
+    "llama3_8b_decode_varlen": DecodeWorkload("llama3_8b_decode_varlen", 8, 32, 8, 131072, 1000, seed=2101,
+                                              lengths=(131072, 98304, 65536, 40000, 24576, 12000, 110000, 4096)),
 }
 
 
 def make_decode_inputs(dw: DecodeWorkload, device: str = "cpu") -> dict:
     """q [batch * Hq, D] (each sequence's last query row), k and v caches
-    [batch * Hkv, cache_len, D], bfloat16; sequences folded into the heads."""
+    [batch * Hkv, cache_len, D], bfloat16; sequences folded into the heads.
+    With lengths, sequence b's keys fill the first lengths[b] rows of its
+    caches (the rest zero) and cache_lens [batch] int32 is returned too."""
     qs, ks, vs = [], [], []
     for b in range(dw.batch):
         x = make_inputs(dw.prefill(b), device=device)
         qs.append(x["q"][:, -1].clone())
-        ks.append(x["k"])
-        vs.append(x["v"])
+        L = dw.length(b)
+        if L == dw.cache_len:
+            ks.append(x["k"])
+            vs.append(x["v"])
+        else:
+            for src, dst in ((x["k"], ks), (x["v"], vs)):
+                buf = torch.zeros((src.shape[0], dw.cache_len, src.shape[2]), dtype=src.dtype, device=device)
+                buf[:, :L] = src
+                dst.append(buf)
         del x
-    return {"q": torch.cat(qs).contiguous(), "k": torch.cat(ks), "v": torch.cat(vs)}
+    res = {"q": torch.cat(qs).contiguous(), "k": torch.cat(ks), "v": torch.cat(vs)}
+    if dw.lengths:
+        res["cache_lens"] = torch.tensor([dw.length(b) for b in range(dw.batch)], dtype=torch.int32, device=device)
+    return res
 
 
 def small_workload(name: str = "small", **kw) -> Workload:

@@ -30,7 +30,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -214,6 +214,14 @@ def test_decode_sparse_validation(lib):
     assert call(P(), idx=ctypes.c_void_p(0x1002)) == RANGE
     assert call(P(hq=6, hkv=4)) == SHAPE
     assert lib.msa_decode_sparse_workspace(P(d=64)) == 0
+    # the per-cache lengths: the same checks, plus the lengths pointer itself
+    vl = lambda prob, lens=FAKE, topk=8, wsb=1 << 30: lib.msa_decode_sparse_varlen(
+        prob, FAKE, FAKE, FAKE, lens, topk, FAKE, 0, FAKE, wsb, FAKE, None, None, None)
+    assert vl(P(), lens=None) == NULL
+    assert vl(P(), lens=ctypes.c_void_p(0x1002)) == RANGE
+    assert vl(P(), topk=4097) == RANGE
+    assert vl(P(), wsb=need - 1) == WS
+    assert vl(P(hq=6, hkv=4)) == SHAPE
 
 
 def test_walk_marks_query(lib):
