@@ -371,23 +371,31 @@ void attn_fwd_kernel(AttnArgs a) {
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
-    const int64_t n = a.n;
-    const int n32 = (int)n;                          // below 2^31
-    const int64_t nqb = (n + kBQ - 1) / kBQ;        // the last query block may be short
+    // query blocks per head in the per-head arrays (those of the longest
+    // sequence of a packed batch)
+    const int64_t nqb = (a.n + kBQ - 1) / kBQ;
+    const int64_t heads = (int64_t)a.hq * a.vl.nseq;  // heads in the per-head arrays
     const int G = a.hq / a.hkv;
     int hgrp;
     int64_t b;
     const int64_t qb0 = kDense ? 0 : a.qb_lo;         // first query block of this launch
     item_of_block(blockIdx.x, nqb - qb0, G / kH, hgrp, b);
     b += qb0;
-    const int h = hgrp * kH + (wave >> 1);           // this wave's q head
-    const int g = h / G;
+    const int h = hgrp * kH + (wave >> 1);           // this wave's q head (in the per-head arrays)
+    // its sequence (the workgroup's heads share it) and the head within it
+    const int seq = (hgrp * kH) / a.hq;
+    const SeqSpan span = seq_span(a.vl.cu, seq, a.vl.rows, a.n);
+    const int64_t n = span.n;
+    const int n32 = (int)n;                          // below 2^31
+    if (b * kBQ >= n) return;                        // past the end of a shorter packed sequence
+    const int hs = h - seq * a.hq;
+    const int g = hs / G;
     const int r0 = (int)b * kBQ;
     const int qrow = r0 + (wave & 1) * 32 + l32;
 
-    const T *qp = reinterpret_cast<const T *>(a.q) + ((int64_t)h * a.stride) * kD;
-    const T *kp = reinterpret_cast<const T *>(a.k) + ((int64_t)g * a.stride) * kD;
-    const T *vp = reinterpret_cast<const T *>(a.v) + ((int64_t)g * a.stride) * kD;
+    const T *qp = reinterpret_cast<const T *>(a.q) + ((int64_t)hs * a.stride + span.row0) * kD;
+    const T *kp = reinterpret_cast<const T *>(a.k) + ((int64_t)g * a.stride + span.row0) * kD;
+    const T *vp = reinterpret_cast<const T *>(a.v) + ((int64_t)g * a.stride + span.row0) * kD;
 
     // Q fragments (B operand of S^T = K Q^T): query qrow, d = dk*16 + hl*8 + e.
     // A per-head sparse item in a key phase that surely runs (its own rows'
@@ -539,7 +547,7 @@ void attn_fwd_kernel(AttnArgs a) {
         if (final_) load_q_early();
         int i_in, cov_in = 0, ci_in = 0;
         if (a.ws != nullptr) {
-            phase_rec = reinterpret_cast<int2 *>(a.ws + (int64_t)a.hq * nqb * 2 * kStateFloats) + item;
+            phase_rec = reinterpret_cast<int2 *>(a.ws + heads * nqb * 2 * kStateFloats) + item;
             sw = a.ws + item * (2 * kStateFloats) + wave * kStateFloats;
         }
         if (first) {
@@ -773,7 +781,7 @@ void attn_fwd_kernel(AttnArgs a) {
             // every query block passes the first phase, which writes its
             // record; each phase with work updates it, so the next one finds
             // where its blocks start without a search
-            phase_rec = reinterpret_cast<int2 *>(a.ws + (int64_t)a.hq * nqb * 2 * kStateFloats) + item;
+            phase_rec = reinterpret_cast<int2 *>(a.ws + heads * nqb * 2 * kStateFloats) + item;
             int2 rec = make_int2(0, 0);
             sw = a.ws + item * (2 * kStateFloats) + wave * kStateFloats;
             if (!first) {
@@ -1119,7 +1127,7 @@ void attn_fwd_kernel(AttnArgs a) {
     const float l_tot = pair32_sum(l_i);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (qrow >= n32) return;                            // rows past the end of a short last block
-    T *op = reinterpret_cast<T *>(a.out) + ((int64_t)h * a.stride + qrow) * kD;
+    T *op = reinterpret_cast<T *>(a.out) + ((int64_t)hs * a.stride + span.row0 + qrow) * kD;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -1129,13 +1137,13 @@ void attn_fwd_kernel(AttnArgs a) {
                          o[dt][jj * 4 + 2] * inv, o[dt][jj * 4 + 3] * inv);
         }
     if (a.lse != nullptr && hl == 0)
-        a.lse[(int64_t)h * a.stride + qrow] = l_tot > 0.f ? (mb_i * kLn2 + logf(l_tot)) : -INFINITY;
+        a.lse[(int64_t)hs * a.stride + span.row0 + qrow] = l_tot > 0.f ? (mb_i * kLn2 + logf(l_tot)) : -INFINITY;
 #endif
 }
 
 template <typename T, bool kDense, int kH, bool kGrp = false, bool kFused = false, bool kExact = false>
 hipError_t launch_h(const AttnArgs &a, hipStream_t s) {
-    const int64_t total = (int64_t)(a.hq / kH) * ((a.n + kBQ - 1) / kBQ - (kDense ? 0 : a.qb_lo));
+    const int64_t total = (int64_t)a.hq * a.vl.nseq / kH * ((a.n + kBQ - 1) / kBQ - (kDense ? 0 : a.qb_lo));
     if (total == 0) return hipSuccess;
     hipLaunchKernelGGL((attn_fwd_kernel<T, kDense, kH, kGrp, kFused, kExact>), dim3((unsigned)total),
                        dim3(kThreads * kH), 0, s, a);
@@ -1240,7 +1248,8 @@ template <typename T, bool kDense> hipError_t launch(AttnArgs a, hipStream_t s) 
         }
         // first the grouped walk over the units that qualify (it marks them),
         // then the key phases of the per-head kernel over the rest
-        a.grp = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(a.ws) + sparse_walk_marks_offset(a.hq, a.n));
+        a.grp = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(a.ws) +
+                                            sparse_walk_marks_offset((int64_t)a.hq * a.vl.nseq, a.n));
         a.grp_kh = walk_heads_per_unit(a.hq, a.hkv);
         {
             const hipError_t e = a.grp_kh == 4   ? launch_h<T, true, 4, true>(a, s)

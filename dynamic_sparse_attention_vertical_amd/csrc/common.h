@@ -135,6 +135,20 @@ __device__ __forceinline__ int32_t load_uniform(const int32_t *p) {
     return *(const __attribute__((address_space(4))) int32_t *)(uintptr_t)p;
 }
 
+// Rows of sequence `seq` of a packed batch (cu: device int32 offsets, read
+// as scalars; seq wave-uniform): the first row and the length, clamped into
+// the rows of a head and to at most nmax.  cu NULL: one sequence of nmax rows.
+struct SeqSpan {
+    int64_t row0, n;
+};
+__device__ __forceinline__ SeqSpan seq_span(const int32_t *cu, int seq, int64_t rows, int64_t nmax) {
+    if (cu == nullptr) return SeqSpan{0, nmax};
+    int64_t a = load_uniform(cu + seq), b = load_uniform(cu + seq + 1);
+    a = a < 0 ? 0 : (a > rows ? rows : a);
+    b = b < a ? a : (b > rows ? rows : b);
+    return SeqSpan{a, b - a < nmax ? b - a : nmax};
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)(LDS_AS const unsigned char *)p;
 }

@@ -122,6 +122,25 @@ __device__ __forceinline__ typename Elem<T>::frag k_frag(const unsigned char *bu
 // Number of q heads waves serve per pass over the key range.
 __device__ __forceinline__ int n_slots(int G) { return (G + 3) / 4; }
 
+// One sequence's frame: its first row, keys, frame keys (keys rounded up to
+// 64), frame shift and key ranges.  A packed batch shares the range length;
+// its per-head arrays hold the longest sequence's nranges and n per head.
+struct EstGeom {
+    int64_t row0, n, nv;
+    int pad, nranges;
+};
+__device__ __forceinline__ EstGeom est_geom(const EstArgs &a, int seq) {
+    if (a.vl.cu == nullptr) return EstGeom{0, a.n, a.nv, a.pad, a.nranges};
+    const SeqSpan sp = seq_span(a.vl.cu, seq, a.vl.rows, a.n);
+    EstGeom e;
+    e.row0 = sp.row0;
+    e.n = sp.n;
+    e.nv = (sp.n + kTK - 1) / kTK * kTK;
+    e.pad = (int)(e.nv - e.n);
+    e.nranges = (int)((e.nv + a.range_keys - 1) / a.range_keys);
+    return e;
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void est_pass1_kernel(EstArgs a) {
@@ -130,27 +149,34 @@ void est_pass1_kernel(EstArgs a) {
     __shared__ EstSmem<T> sm;
     const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int range = blockIdx.x, g = blockIdx.y;
+    const int range = blockIdx.x, seq = blockIdx.y / a.hkv, g = blockIdx.y % a.hkv;
     const int G = a.hq / a.hkv;
-    const int64_t n = a.n, nv = a.nv;                   // sequence keys, frame keys
-    const int pad = a.pad;
+    const EstGeom gm = est_geom(a, seq);
+    if (gm.n == 0 || range >= gm.nranges) return;      // an empty packed sequence, or past its keys
+    const int64_t n = gm.n, nv = gm.nv;                 // sequence keys, frame keys
+    const int pad = gm.pad;
     const int64_t k0 = (int64_t)range * a.range_keys;   // frame keys of this range
     const int64_t k1 = min(nv, k0 + a.range_keys);
     const int ntile = (int)((k1 - k0) / kTK);
-    const T *kp = reinterpret_cast<const T *>(a.k) + (int64_t)g * a.stride * kD;
+    const T *kp = reinterpret_cast<const T *>(a.k) + ((int64_t)g * a.stride + gm.row0) * kD;
     uint32_t off[Gm::kPer];
     copy_offsets<T>(off, lane);
     for (int slot = 0; slot < n_slots(G); ++slot) {
         const int hw = wave + 4 * slot;
         const bool active = hw < G;
         const int h = g * G + (active ? hw : 0);
-        const T *qp = reinterpret_cast<const T *>(a.q) + ((int64_t)h * a.stride + (n - kL)) * kD;
+        const int64_t vh = (int64_t)seq * a.hq + h;     // the head in the per-head arrays
+        const T *qp = reinterpret_cast<const T *>(a.q) + ((int64_t)h * a.stride + gm.row0) * kD;
         typename E::frag qf[2][8];
 #pragma unroll
-        for (int half = 0; half < 2; ++half)
+        for (int half = 0; half < 2; ++half) {
+            // window row half*32 + l32 is sequence row n - 64 + that; in a
+            // sequence shorter than the window the rows before its start read
+            // row 0, and every key of theirs is masked
+            const int64_t qr = max(n - kL + half * 32 + l32, (int64_t)0);
 #pragma unroll
-            for (int dk = 0; dk < 8; ++dk)
-                qf[half][dk] = E::load_frag(qp + (half * 32 + l32) * kD + dk * 16 + hl * 8);
+            for (int dk = 0; dk < 8; ++dk) qf[half][dk] = E::load_frag(qp + qr * kD + dk * 16 + hl * 8);
+        }
         __builtin_amdgcn_s_waitcnt(kVmcnt0);        // Q has landed (compiler-visible wait)
         float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
         __syncthreads();                            // the previous slot is done with both buffers
@@ -211,7 +237,7 @@ void est_pass1_kernel(EstArgs a) {
                 const float ref = (mn == -INFINITY) ? 0.f : mn;
                 const float lt = l[half] * __builtin_amdgcn_exp2f(m[half] - ref) + lo * __builtin_amdgcn_exp2f(mo - ref);
                 if (hl == 0) {
-                    const int64_t o = ((int64_t)h * kL + half * 32 + l32) * a.nranges + range;
+                    const int64_t o = (vh * kL + half * 32 + l32) * a.nranges + range;
                     a.part_m[o] = mn;
                     a.part_l[o] = lt;
                 }
@@ -226,11 +252,13 @@ void est_pass1_kernel(EstArgs a) {
 __global__ __launch_bounds__(256) void est_combine_kernel(EstArgs a) {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= (int64_t)a.hq * kL) return;
+    if (row >= (int64_t)a.vl.nseq * a.hq * kL) return;
+    const EstGeom gm = est_geom(a, (int)(row / kL / a.hq));
+    if (gm.n == 0) return;
     const float *pm = a.part_m + row * a.nranges;
     const float *pl = a.part_l + row * a.nranges;
     float m = -INFINITY, l = 0.f;
-    for (int i = lane; i < a.nranges; i += 64) {
+    for (int i = lane; i < gm.nranges; i += 64) {
         const float mi = pm[i], li = pl[i];
         const float mn = fmaxf(m, mi);
         const float base = (mn == -INFINITY) ? 0.f : mn;
@@ -245,7 +273,8 @@ __global__ __launch_bounds__(256) void est_combine_kernel(EstArgs a) {
         l = l * exp2f(m - base) + lo * exp2f(mo - base);
         m = mn;
     }
-    // every last-window row has at least one key, so l > 0
+    // a window row has at least one key (l > 0) unless it lies before the
+    // start of a sequence shorter than the window: -inf, and its p is masked
     if (lane == 0) a.row_norm[row] = m + log2f(l);
 }
 
@@ -272,14 +301,16 @@ __global__ __launch_bounds__(kThreads2) void est_pass2_kernel(EstArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hs = wave >> 1, hf = wave & 1;                    // head slot, row half
-    const int range = blockIdx.x, g = blockIdx.y;
+    const int range = blockIdx.x, seq = blockIdx.y / a.hkv, g = blockIdx.y % a.hkv;
     const int G = a.hq / a.hkv;
-    const int64_t n = a.n, nv = a.nv;                          // sequence keys, frame keys
-    const int pad = a.pad;
+    const EstGeom gm = est_geom(a, seq);
+    if (gm.n == 0 || range >= gm.nranges) return;              // as in pass 1
+    const int64_t n = gm.n, nv = gm.nv;                        // sequence keys, frame keys
+    const int pad = gm.pad;
     const int64_t k0 = (int64_t)range * a.range_keys;           // frame keys of this range
     const int64_t k1 = min(nv, k0 + a.range_keys);
     const int ntile = (int)((k1 - k0) / kTK);
-    const T *kp = reinterpret_cast<const T *>(a.k) + (int64_t)g * a.stride * kD;
+    const T *kp = reinterpret_cast<const T *>(a.k) + ((int64_t)g * a.stride + gm.row0) * kD;
     const bool loader = wave < 4;                               // waves 0-3 copy the K tiles
     uint32_t off[Gm::kPer];
     copy_offsets<T>(off, lane);
@@ -297,18 +328,21 @@ __global__ __launch_bounds__(kThreads2) void est_pass2_kernel(EstArgs a) {
         const int hw = hs + 4 * slot;
         const bool active = hw < G;
         const int h = g * G + (active ? hw : 0);
-        const T *qp = reinterpret_cast<const T *>(a.q) + ((int64_t)h * a.stride + (n - kL)) * kD;
+        const int64_t vh = (int64_t)seq * a.hq + h;             // the head in the per-head arrays
+        const T *qp = reinterpret_cast<const T *>(a.q) + ((int64_t)h * a.stride + gm.row0) * kD;
         // A operand of S = Q K^T: query 32 hf + l32, d = dk*16 + hl*8 + e
+        // (rows before the start of a short sequence read row 0, as in pass 1)
+        const int64_t qr = max(n - kL + hf * 32 + l32, (int64_t)0);
         typename E::frag qf[8];
 #pragma unroll
-        for (int dk = 0; dk < 8; ++dk) qf[dk] = E::load_frag(qp + (hf * 32 + l32) * kD + dk * 16 + hl * 8);
+        for (int dk = 0; dk < 8; ++dk) qf[dk] = E::load_frag(qp + qr * kD + dk * 16 + hl * 8);
         // normaliser of the 16 rows this lane holds: row 32 hf + jj*8 + hl*4 + i at jj*4 + i
         float nrm[16];
 #pragma unroll
-        for (int x = 0; x < 16; ++x) nrm[x] = a.row_norm[(int64_t)h * kL + hf * 32 + (x >> 2) * 8 + hl * 4 + (x & 3)];
+        for (int x = 0; x < 16; ++x) nrm[x] = a.row_norm[vh * kL + hf * 32 + (x >> 2) * 8 + hl * 4 + (x & 3)];
         __builtin_amdgcn_s_waitcnt(kVmcnt0);        // Q and the normalisers have landed
-        float *vout = a.v_score + (int64_t)h * n;
-        float *sout = a.s_score + (int64_t)h * n;
+        float *vout = a.v_score + vh * a.n;                     // rows of the longest sequence's length
+        float *sout = a.s_score + vh * a.n;
         float carry = 0.f;
         float v_own = 0.f, d1_own = 0.f, d2_own = 0.f;          // half-0 partials of the pending tile
         // tile t's scores (half-0 wave): add the half-1 partials, write, carry
@@ -329,7 +363,7 @@ __global__ __launch_bounds__(kThreads2) void est_pass2_kernel(EstArgs a) {
                     // keys below 0 do not exist; offsets from n on reach no key
                     if (o2 < n) sout[o2] = dg2;
                 } else {
-                    a.diag_hi[((int64_t)h * a.nranges + range) * 64 + lane] = dg2;
+                    a.diag_hi[(vh * a.nranges + range) * 64 + lane] = dg2;
                 }
                 carry = dg1;                                     // D = lane - 63, finished by the next tile
             }
@@ -401,8 +435,8 @@ __global__ __launch_bounds__(kThreads2) void est_pass2_kernel(EstArgs a) {
         __syncthreads();                            // half-1 partials of the last tile
         if (active && hf == 0 && ntile > 0) {
             finish(ntile - 1);
-            if (lane < 63 && range != a.nranges - 1)
-                a.diag_lo[((int64_t)h * a.nranges + range) * 64 + lane] = carry;
+            if (lane < 63 && range != gm.nranges - 1)
+                a.diag_lo[(vh * a.nranges + range) * 64 + lane] = carry;
         }
     }
 }
@@ -411,29 +445,31 @@ __global__ __launch_bounds__(kThreads2) void est_pass2_kernel(EstArgs a) {
 __global__ __launch_bounds__(256) void est_fixup_kernel(EstArgs a) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t per_h = (int64_t)(a.nranges - 1) * 63;
-    if (t >= per_h * a.hq) return;
-    const int h = (int)(t / per_h);
+    if (t >= per_h * a.hq * a.vl.nseq) return;
+    const int64_t vh = t / per_h;
     const int64_t rem = t % per_h;
     const int range = 1 + (int)(rem / 63);
     const int lane = (int)(rem % 63);
-    const int64_t A = a.nv - kL - (int64_t)range * a.range_keys;
+    const EstGeom gm = est_geom(a, (int)(vh / a.hq));
+    if (gm.n == 0 || range >= gm.nranges) return;
+    const int64_t A = gm.nv - kL - (int64_t)range * a.range_keys;
     const int64_t o = A + lane + 1;                     // below n: range >= 1 starts past frame key 255
-    if (o >= a.n) return;
-    a.s_score[(int64_t)h * a.n + o] = a.diag_hi[((int64_t)h * a.nranges + range) * 64 + lane] +
-                                      a.diag_lo[((int64_t)h * a.nranges + range - 1) * 64 + lane];
+    if (o >= gm.n) return;
+    a.s_score[vh * a.n + o] = a.diag_hi[(vh * a.nranges + range) * 64 + lane] +
+                              a.diag_lo[(vh * a.nranges + range - 1) * 64 + lane];
 }
 
 template <typename T> hipError_t launch_t(const EstArgs &a, hipStream_t s) {
-    dim3 grid(a.nranges, a.hkv);
+    dim3 grid(a.nranges, a.hkv * a.vl.nseq);
     hipLaunchKernelGGL(est_pass1_kernel<T>, grid, dim3(kThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t rows = (int64_t)a.hq * kL;
+    const int64_t rows = (int64_t)a.hq * a.vl.nseq * kL;
     hipLaunchKernelGGL(est_combine_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(est_pass2_kernel<T>, grid, dim3(kThreads2), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int64_t fix = (int64_t)(a.nranges - 1) * 63 * a.hq;
+    const int64_t fix = (int64_t)(a.nranges - 1) * 63 * a.hq * a.vl.nseq;
     if (fix > 0) {
         hipLaunchKernelGGL(est_fixup_kernel, dim3((unsigned)((fix + 255) / 256)), dim3(256), 0, s, a);
         e = hipGetLastError();

@@ -57,8 +57,11 @@ template <bool kStaged>
 __global__ __launch_bounds__(kThreads) void build_index_kernel(IndexArgs a) {
     __shared__ int32_t stage[kStaged ? kStageMax : 1];
     __shared__ int32_t ring_all[kThreads * kRingPitch];
-    const int h = blockIdx.y;
-    const int nqb = (int)((a.n + 63) / 64);          // sequence lengths are below 2^31
+    const int h = blockIdx.y;                        // head (of its sequence, in a packed batch)
+    const SeqSpan sp = seq_span(a.vl.cu, h / a.hq, a.vl.rows, a.n);
+    const int n = (int)sp.n;                         // sequence lengths are below 2^31
+    const int nqb = (n + 63) / 64;
+    const int64_t nqb_rows = (a.n + 63) / 64;        // query blocks per head in the arrays
     const int b = blockIdx.x * kThreads + threadIdx.x;
     const int32_t *S = a.s_idx + (int64_t)h * a.ks;
     const int32_t *V = a.v_idx + (int64_t)h * a.kv;
@@ -68,14 +71,14 @@ __global__ __launch_bounds__(kThreads) void build_index_kernel(IndexArgs a) {
         V = stage;
     }
     if (b >= nqb) return;
-    const int r0 = b * 64, r1 = min(r0 + 63, (int)a.n - 1);   // the last block may be short
-    const int64_t item = (int64_t)h * nqb + b;
+    const int r0 = b * 64, r1 = min(r0 + 63, n - 1);          // the last block may be short
+    const int64_t item = (int64_t)h * nqb_rows + b;
     int32_t *blk = a.block_offset + item * a.cap_b;
     int32_t *col = a.column_index + item * a.cap_c;
 
     // offsets that matter to some lane of the wave: those <= r1 of its last item
     const int wave_first = b - (int)(threadIdx.x & 63);
-    const int r1_max = min(min(wave_first + 63, nqb - 1) * 64 + 63, (int)a.n - 1);
+    const int r1_max = min(min(wave_first + 63, nqb - 1) * 64 + 63, n - 1);
     int lo = 0, hi = a.ks;
     while (lo < hi) {
         const int mid = (lo + hi) >> 1;
@@ -175,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void build_index_kernel(IndexArgs a) {
 
 hipError_t launch_build_index(const IndexArgs &a, hipStream_t s) {
     const int64_t nqb = (a.n + 63) / 64;
-    dim3 grid((unsigned)((nqb + kThreads - 1) / kThreads), a.hq);
+    dim3 grid((unsigned)((nqb + kThreads - 1) / kThreads), a.hq * a.vl.nseq);
     if (a.kv <= kStageMax)
         hipLaunchKernelGGL(build_index_kernel<true>, grid, dim3(kThreads), 0, s, a);
     else

@@ -6,6 +6,19 @@
 
 namespace msa {
 
+// A packed batch of sequences of different lengths (cu NULL: one sequence of
+// the problem's length).  Sequence s holds rows cu[s] .. cu[s+1]-1 of every
+// head of q, k, v, out and lse (device int32 [nseq + 1]); in the per-head
+// arrays (scores, index sets, work lists, state) head h of sequence s is the
+// head s * heads + h, with room for the longest sequence (the problem's n).
+// Entries are clamped into [0, rows] and lengths to n, so that any contents
+// keep every access inside the buffers.
+struct Varlen {
+    const int32_t *cu = nullptr;
+    int32_t nseq = 1;
+    int64_t rows = 0;            // rows of each head of q, k, v (and out, lse)
+};
+
 struct AttnArgs {
     const void *q, *k, *v;
     const int32_t *block_count, *block_offset, *column_count, *column_index;
@@ -41,6 +54,7 @@ struct AttnArgs {
     // fused_cw 32-bit words each (all of them run in the final phase)
     uint32_t *fused_cols;
     int32_t fused_cw;
+    Varlen vl;           // hq, hkv: heads per sequence; n: the longest sequence
     // fused mode with the exact union mask: per q head, a bitmap of the
     // selected diagonal offsets over [0, n) and one of the selected column
     // keys, ex_words 32-bit words each (unused otherwise)
@@ -86,6 +100,7 @@ struct EstArgs {
     float *row_norm;             // [hq][64] per-row log2 normaliser (scaled max + log2 sum)
     float *v_score, *s_score;    // [hq][n]
     float *diag_hi, *diag_lo;    // [hq][nranges][64]
+    Varlen vl;                   // hq, hkv: heads per sequence; n, nv, pad, nranges: the longest
 };
 
 hipError_t launch_estimate_scores(const EstArgs &a, int dtype, hipStream_t s);
@@ -103,8 +118,8 @@ struct TopkArgs {
     uint32_t *off;               // [2*hq][nslices][2]
     int32_t rows;                // rows selected: 0 = 2*hq (both sets); else the first rows, all from src0
     const int32_t *row_len = nullptr;   // NULL: every row has n entries; else row r has
-    int32_t row_len_div = 1;            //   row_len[r / row_len_div], clamped into [0, n]; a row with
-                                        //   at most k of them selects 0 .. k - 1
+    int32_t row_len_div = 1;            //   row_len[(r % hq) / row_len_div], clamped into [0, n]; a row
+                                        //   with at most k of them selects 0 .. k - 1
 };
 
 constexpr int kTopkSlice = 4096;   // elements per top-k workgroup slice
@@ -113,6 +128,9 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
 // The same selection with one 1024-thread workgroup per row, in one launch
 // (uses none of hist / state / cnt / off).
 hipError_t launch_topk_rows(const TopkArgs &a, hipStream_t s);
+// The lengths of a packed batch's sequences (as the kernels clamp them), for
+// TopkArgs.row_len: len [vl.nseq].
+hipError_t launch_seq_lengths(const Varlen &vl, int64_t nmax, int32_t *len, hipStream_t s);
 
 // Decode-side top-k attention: one query row per q head over a cache of n keys.
 struct DecodeArgs {
@@ -145,6 +163,7 @@ struct IndexArgs {
     int32_t *block_count, *block_offset, *column_count, *column_index;
     int32_t cap_b, cap_c;
     bool vec_rows;               // every block_offset row starts 16-byte aligned (16-byte stores)
+    Varlen vl;                   // hq: heads per sequence; n: the longest sequence
 };
 
 hipError_t launch_build_index(const IndexArgs &a, hipStream_t s);

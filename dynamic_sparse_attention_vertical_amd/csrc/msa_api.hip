@@ -79,14 +79,16 @@ struct EstLayout {
     int32_t nranges;
     int32_t nslices;
     size_t off_part_m, off_part_l, off_row_norm, off_hi, off_lo, off_v, off_s;
-    size_t off_hist, off_state, off_cnt, off_off, total;
+    size_t off_hist, off_state, off_cnt, off_off, off_lens, total;
 };
 
-EstLayout est_layout(const msa_problem *p) {
+// hq_all, hkv_all: the heads of all sequences; n: keys of the longest one;
+// nlens: sequences of a packed batch (their lengths for the top-k go to
+// off_lens), 0 for one sequence
+EstLayout est_layout_for(int64_t hq_all, int64_t hkv_all, int64_t n, int64_t nlens) {
     EstLayout L;
-    const int64_t n = p->seq_len;
     const int64_t nv = (n + 63) / 64 * 64;            // keys tiled in 64s, ending at key n-1
-    int64_t rk = (nv * p->n_kv_heads + 511) / 512;
+    int64_t rk = (nv * hkv_all + 511) / 512;
     rk = ((rk + 63) / 64) * 64;
     if (rk < 256) rk = 256;
     if (rk > 8192) rk = 8192;
@@ -94,7 +96,7 @@ EstLayout est_layout(const msa_problem *p) {
     L.range_keys = rk;
     L.nranges = (int32_t)((nv + rk - 1) / rk);
     L.nslices = (int32_t)((n + msa::kTopkSlice - 1) / msa::kTopkSlice);
-    const size_t hq = (size_t)p->n_q_heads;
+    const size_t hq = (size_t)hq_all;
     size_t o = 0;
     L.off_part_m = o; o = align_up(o + hq * 64 * L.nranges * 4);
     L.off_part_l = o; o = align_up(o + hq * 64 * L.nranges * 4);
@@ -107,9 +109,12 @@ EstLayout est_layout(const msa_problem *p) {
     L.off_state = o;  o = align_up(o + 2 * hq * 4 * 4);
     L.off_cnt = o;    o = align_up(o + 2 * hq * (size_t)L.nslices * 2 * 4);
     L.off_off = o;    o = align_up(o + 2 * hq * (size_t)L.nslices * 2 * 4);
+    L.off_lens = o;   o = align_up(o + (size_t)nlens * 4);
     L.total = o;
     return L;
 }
+
+EstLayout est_layout(const msa_problem *p) { return est_layout_for(p->n_q_heads, p->n_kv_heads, p->seq_len, 0); }
 
 template <typename T> T *at(void *ws, size_t off) {
     return reinterpret_cast<T *>(reinterpret_cast<char *>(ws) + off);
@@ -137,15 +142,16 @@ int check_estimate_vs(const msa_problem *p, const void *q, const void *k, int32_
 // est_layout(p).total bytes.
 int run_estimate_vs(const msa_problem *p, const void *q, const void *k, int32_t vertical_topk, int32_t slash_topk,
                     int32_t *v_idx, int32_t *s_idx, float *v_score, float *s_score, void *workspace,
-                    void *stream) {
-    const EstLayout L = est_layout(p);
+                    void *stream, const msa::Varlen *vl = nullptr, int64_t max_len = 0) {
+    const int64_t nseq = vl ? vl->nseq : 1, n = vl ? max_len : p->seq_len;
+    const EstLayout L = est_layout_for(p->n_q_heads * nseq, p->n_kv_heads * nseq, n, vl ? nseq : 0);
     int st;
     msa::EstArgs e;
     e.q = q;
     e.k = k;
-    e.n = p->seq_len;
+    e.n = n;
     e.stride = stride_of(p);
-    e.nv = (p->seq_len + 63) / 64 * 64;
+    e.nv = (n + 63) / 64 * 64;
     e.pad = (int32_t)(e.nv - e.n);
     e.hq = p->n_q_heads;
     e.hkv = p->n_kv_heads;
@@ -159,6 +165,7 @@ int run_estimate_vs(const msa_problem *p, const void *q, const void *k, int32_t 
     e.diag_lo = at<float>(workspace, L.off_lo);
     e.v_score = v_score ? v_score : at<float>(workspace, L.off_v);
     e.s_score = s_score ? s_score : at<float>(workspace, L.off_s);
+    if (vl) e.vl = *vl;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     st = launch_status(msa::launch_estimate_scores(e, p->dtype, s), "estimate");
     if (st) return st;
@@ -169,15 +176,23 @@ int run_estimate_vs(const msa_problem *p, const void *q, const void *k, int32_t 
     t.dst1 = s_idx;
     t.k0 = vertical_topk;
     t.k1 = slash_topk;
-    t.hq = p->n_q_heads;
-    t.n = p->seq_len;
+    t.hq = (int32_t)(p->n_q_heads * nseq);
+    t.n = n;
     t.nslices = L.nslices;
     t.hist = at<uint32_t>(workspace, L.off_hist);
     t.state = at<uint32_t>(workspace, L.off_state);
     t.cnt = at<uint32_t>(workspace, L.off_cnt);
     t.off = at<uint32_t>(workspace, L.off_off);
     t.rows = 0;
-    return launch_status(msa::launch_topk(t, s), "top-k");
+    if (!vl) return launch_status(msa::launch_topk(t, s), "top-k");
+    // a packed batch: each row selects among its own sequence's keys (a row
+    // with at most k of them takes 0 .. k-1, the ones past its end ignored by
+    // the index builder), one workgroup per row
+    int32_t *lens = at<int32_t>(workspace, L.off_lens);
+    if ((st = launch_status(msa::launch_seq_lengths(*vl, n, lens, s), "sequence lengths"))) return st;
+    t.row_len = lens;
+    t.row_len_div = p->n_q_heads;
+    return launch_status(msa::launch_topk_rows(t, s), "top-k");
 }
 
 // Workspace of msa_decode_sparse: score keys, chunk partials, dense lse, and
@@ -596,6 +611,158 @@ int msa_dense_prefill(const msa_problem *p, const void *q, const void *k, const 
     a.lse = lse;
     return launch_status(msa::launch_dense_prefill(a, p->dtype, reinterpret_cast<hipStream_t>(stream)),
                          "dense_prefill");
+}
+
+// ---- Packed batches of sequences of different lengths ----
+
+// heads of all sequences together: the kernels' grids index them in their
+// second dimension (the top-k's rows are twice this many)
+constexpr int64_t kMaxVarlenHeads = 32767;
+
+static int check_varlen(const msa_problem *p, const msa_varlen *vl, msa::Varlen &out) {
+    int st = check_problem(p);
+    if (st) return st;
+    if (!vl || !vl->cu_seqlens) return fail(MSA_ERR_NULL, "the varlen descriptor or its cu_seqlens is NULL");
+    if (off_align(vl->cu_seqlens, 4)) return fail(MSA_ERR_RANGE, "cu_seqlens must be 4-byte aligned");
+    if (vl->n_seqs < 1) return fail(MSA_ERR_SHAPE, "n_seqs must be at least 1 (got %d)", vl->n_seqs);
+    if ((int64_t)vl->n_seqs * p->n_q_heads > kMaxVarlenHeads)
+        return fail(MSA_ERR_SHAPE, "n_seqs * n_q_heads must be at most %lld (got %lld)", (long long)kMaxVarlenHeads,
+                    (long long)vl->n_seqs * p->n_q_heads);
+    if (vl->max_seqlen < 1 || vl->max_seqlen > p->seq_len)
+        return fail(MSA_ERR_SHAPE, "max_seqlen must lie in [1, seq_len] (got %d)", vl->max_seqlen);
+    out.cu = vl->cu_seqlens;
+    out.nseq = vl->n_seqs;
+    out.rows = p->seq_len;
+    return MSA_OK;
+}
+
+size_t msa_estimate_vs_varlen_workspace(const msa_problem *p, const msa_varlen *vl, int32_t last_q) {
+    msa::Varlen V;
+    if (check_varlen(p, vl, V) != MSA_OK || last_q != 64) return 0;
+    return est_layout_for((int64_t)p->n_q_heads * V.nseq, (int64_t)p->n_kv_heads * V.nseq, vl->max_seqlen, V.nseq)
+        .total;
+}
+
+int msa_estimate_vs_varlen(const msa_problem *p, const msa_varlen *vl, const void *q, const void *k, int32_t last_q,
+                           int32_t vertical_topk, int32_t slash_topk, int32_t *v_idx, int32_t *s_idx, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+    msa::Varlen V;
+    int st = check_varlen(p, vl, V);
+    if (st) return st;
+    if (!q || !k || !v_idx || !s_idx || !workspace) return fail(MSA_ERR_NULL, "a required pointer is NULL");
+    if ((st = check_rows(q, k, nullptr, nullptr))) return st;
+    if (off_align(v_idx, 4) || off_align(s_idx, 4)) return fail(MSA_ERR_RANGE, "index arrays must be 4-byte aligned");
+    if (off_align(workspace, 16)) return fail(MSA_ERR_RANGE, "workspace is not 16-byte aligned");
+    if (last_q != 64) return fail(MSA_ERR_RANGE, "last_q must be 64 (got %d)", last_q);
+    if (vertical_topk < 1 || vertical_topk > vl->max_seqlen || slash_topk < 1 || slash_topk > vl->max_seqlen)
+        return fail(MSA_ERR_RANGE, "top-k values must lie in [1, max_seqlen]");
+    const size_t need = msa_estimate_vs_varlen_workspace(p, vl, last_q);
+    if (workspace_bytes < need)
+        return fail(MSA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    return run_estimate_vs(p, q, k, vertical_topk, slash_topk, v_idx, s_idx, nullptr, nullptr, workspace, stream, &V,
+                           vl->max_seqlen);
+}
+
+int msa_build_index_varlen(const msa_problem *p, const msa_varlen *vl, const int32_t *v_idx, int32_t vertical_topk,
+                           const int32_t *s_idx, int32_t slash_topk, int32_t block, int32_t *block_count,
+                           int32_t *block_offset, int32_t cap_blocks, int32_t *column_count, int32_t *column_index,
+                           int32_t cap_cols, void *stream) {
+    msa::Varlen V;
+    int st = check_varlen(p, vl, V);
+    if (st) return st;
+    msa_problem one = *p;                          // the per-head arrays' geometry: the longest sequence
+    one.seq_len = vl->max_seqlen;
+    one.seq_stride = 0;
+    int32_t need_b, need_c;
+    if ((st = msa_index_caps(&one, vertical_topk, slash_topk, block, &need_b, &need_c))) return st;
+    if ((vertical_topk > 0 && !v_idx) || (slash_topk > 0 && !s_idx) || !block_count || !column_count ||
+        (cap_blocks > 0 && !block_offset) || (cap_cols > 0 && !column_index))
+        return fail(MSA_ERR_NULL, "a required pointer is NULL");
+    if (cap_blocks < need_b || cap_cols < need_c)
+        return fail(MSA_ERR_CAPACITY, "capacities (%d, %d) below required (%d, %d)", cap_blocks, cap_cols,
+                    need_b, need_c);
+    if (off_align(v_idx, 4) || off_align(s_idx, 4) || off_align(block_count, 4) || off_align(block_offset, 4) ||
+        off_align(column_count, 4) || off_align(column_index, 4))
+        return fail(MSA_ERR_RANGE, "index arrays must be 4-byte aligned");
+    msa::IndexArgs a;
+    a.v_idx = v_idx;
+    a.s_idx = s_idx;
+    a.kv = vertical_topk;
+    a.ks = slash_topk;
+    a.n = vl->max_seqlen;
+    a.hq = p->n_q_heads;
+    a.block_count = block_count;
+    a.block_offset = block_offset;
+    a.column_count = column_count;
+    a.column_index = column_index;
+    a.cap_b = cap_blocks;
+    a.cap_c = cap_cols;
+    a.vec_rows = (cap_blocks & 3) == 0 && !off_align(block_offset, 16);
+    a.vl = V;
+    return launch_status(msa::launch_build_index(a, reinterpret_cast<hipStream_t>(stream)), "build_index_varlen");
+}
+
+size_t msa_sparse_prefill_varlen_workspace(const msa_problem *p, const msa_varlen *vl, int32_t phase_keys) {
+    msa::Varlen V;
+    if (check_varlen(p, vl, V) != MSA_OK || phase_keys < 0 || phase_keys % 64 != 0) return 0;
+    return msa::sparse_state_bytes((int64_t)p->n_q_heads * V.nseq, vl->max_seqlen, phase_keys_of(phase_keys));
+}
+
+int msa_sparse_prefill_varlen(const msa_problem *p, const msa_varlen *vl, const void *q, const void *k, const void *v,
+                              const int32_t *block_count, const int32_t *block_offset, int32_t cap_blocks,
+                              const int32_t *column_count, const int32_t *column_index, int32_t cap_cols,
+                              int32_t phase_keys, void *workspace, size_t workspace_bytes, void *out, float *lse,
+                              void *stream) {
+    msa::Varlen V;
+    int st = check_varlen(p, vl, V);
+    if (st) return st;
+    msa::AttnArgs a;
+    if ((st = attn_common(p, q, k, v, out, a))) return st;
+    if (!block_count || !column_count || (cap_blocks > 0 && !block_offset) || (cap_cols > 0 && !column_index))
+        return fail(MSA_ERR_NULL, "an index pointer is NULL");
+    if (cap_blocks < 0 || cap_cols < 0) return fail(MSA_ERR_CAPACITY, "negative capacity");
+    if (off_align(block_count, 4) || off_align(block_offset, 4) || off_align(column_count, 4) ||
+        off_align(column_index, 4) || off_align(lse, 4))
+        return fail(MSA_ERR_RANGE, "index and lse arrays must be 4-byte aligned");
+    if (phase_keys < 0 || phase_keys % 64 != 0)
+        return fail(MSA_ERR_RANGE, "phase_keys %d is not a non-negative multiple of 64", phase_keys);
+    a.n = vl->max_seqlen;
+    a.vl = V;
+    a.block_count = block_count;
+    a.block_offset = block_offset;
+    a.column_count = column_count;
+    a.column_index = column_index;
+    a.cap_b = cap_blocks;
+    a.cap_c = cap_cols;
+    a.lse = lse;
+    a.phase_keys = (int32_t)phase_keys_of(phase_keys);
+    const size_t need = msa::sparse_state_bytes((int64_t)p->n_q_heads * V.nseq, a.n, a.phase_keys);
+    if (need > 0) {
+        if (!workspace) return fail(MSA_ERR_NULL, "workspace is NULL (%zu bytes needed)", need);
+        if (workspace_bytes < need)
+            return fail(MSA_ERR_WORKSPACE, "workspace %zu bytes, %zu needed", workspace_bytes, need);
+        if (off_align(workspace, 16)) return fail(MSA_ERR_RANGE, "workspace is not 16-byte aligned");
+        a.ws = static_cast<float *>(workspace);
+    }
+    return launch_status(msa::launch_sparse_prefill(a, p->dtype, reinterpret_cast<hipStream_t>(stream)),
+                         "sparse_prefill_varlen");
+}
+
+int msa_dense_prefill_varlen(const msa_problem *p, const msa_varlen *vl, const void *q, const void *k, const void *v,
+                             void *out, float *lse, void *stream) {
+    msa::Varlen V;
+    int st = check_varlen(p, vl, V);
+    if (st) return st;
+    msa::AttnArgs a;
+    if ((st = attn_common(p, q, k, v, out, a))) return st;
+    if (off_align(lse, 4)) return fail(MSA_ERR_RANGE, "lse must be 4-byte aligned");
+    a.n = vl->max_seqlen;
+    a.vl = V;
+    a.block_count = a.block_offset = a.column_count = a.column_index = nullptr;
+    a.cap_b = a.cap_c = 0;
+    a.lse = lse;
+    return launch_status(msa::launch_dense_prefill(a, p->dtype, reinterpret_cast<hipStream_t>(stream)),
+                         "dense_prefill_varlen");
 }
 
 // block-sparse workspace: pooled q and k means, then the score keys of one

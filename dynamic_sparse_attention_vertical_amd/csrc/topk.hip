@@ -45,7 +45,7 @@ __device__ __forceinline__ RowView row_view(const TopkArgs &a, int row) {
 // entries of a row: n, or the row's own length (clamped into [0, n])
 __device__ __forceinline__ int64_t row_n(const TopkArgs &a, int row) {
     if (a.row_len == nullptr) return a.n;
-    const int64_t len = a.row_len[row / a.row_len_div];
+    const int64_t len = a.row_len[(row % a.hq) / a.row_len_div];   // the two sets of a row share it
     return len < 0 ? 0 : (len > a.n ? a.n : len);
 }
 
@@ -491,6 +491,21 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
 }
 
 }  // namespace
+
+namespace {
+__global__ __launch_bounds__(256) void seq_lengths_kernel(Varlen vl, int64_t nmax, int32_t *len) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= vl.nseq) return;
+    const int64_t a = min(max((int64_t)vl.cu[i], (int64_t)0), vl.rows);
+    const int64_t b = min(max((int64_t)vl.cu[i + 1], a), vl.rows);
+    len[i] = (int32_t)min(b - a, nmax);
+}
+}  // namespace
+
+hipError_t launch_seq_lengths(const Varlen &vl, int64_t nmax, int32_t *len, hipStream_t s) {
+    hipLaunchKernelGGL(seq_lengths_kernel, dim3((unsigned)((vl.nseq + 255) / 256)), dim3(256), 0, s, vl, nmax, len);
+    return hipGetLastError();
+}
 
 hipError_t launch_topk_rows(const TopkArgs &a, hipStream_t s) {
     const int rows = a.rows > 0 ? a.rows : 2 * a.hq;

@@ -178,22 +178,44 @@ def mixed_layer(q, k, v, plan: MixedPlan, *, out: torch.Tensor | None = None, ls
 # cu_seqlens[i] .. cu_seqlens[i+1]-1).  A batch whose batch stride is heads x
 # the head stride (a contiguous [B, H, N, D] tensor, or a slice of one along
 # the sequence) runs as one problem of B*H heads: one launch chain for the
-# whole batch.  Other batch layouts, and packed sequences, run one after
-# another on the stream through the same C-ABI steps; a packed sequence is a
-# view of the packed tensors (the C ABI's seq_stride is the packed length).
+# whole batch.  A packed batch of the vertical-slash or A-shape kind runs as
+# one problem too, through the C ABI's variable-length calls (one launch
+# chain for all sequences).  Other batch layouts, and packed block-sparse
+# batches, run one sequence after another on the stream through the same
+# C-ABI steps; a packed sequence is then a view of the packed tensors (the C
+# ABI's seq_stride is the packed length).
 
 
-def _packed(q, k, v, cu_seqlens, fn):
-    """Run fn(q_i, k_i, v_i, out_i) on each packed sequence i."""
+def _cu_list(q, k, v, cu_seqlens):
+    """cu_seqlens checked on the host: a list rising strictly from 0 to the
+    packed length."""
     if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
         raise msa.MsaError("packed q, k, v must be [heads, total, dim]")
     cu = [int(x) for x in (cu_seqlens.tolist() if hasattr(cu_seqlens, "tolist") else cu_seqlens)]
     if len(cu) < 2 or cu[0] != 0 or cu[-1] != q.shape[1] or any(b <= a for a, b in zip(cu, cu[1:])):
         raise msa.MsaError("cu_seqlens must rise strictly from 0 to the packed length")
+    return cu
+
+
+def _packed(q, k, v, cu_seqlens, fn):
+    """Run fn(q_i, k_i, v_i, out_i) on each packed sequence i."""
+    cu = _cu_list(q, k, v, cu_seqlens)
     out = torch.empty_like(q)
     for a, b in zip(cu, cu[1:]):
         fn(q[:, a:b], k[:, a:b], v[:, a:b], out[:, a:b])
     return out
+
+
+def _packed_varlen(q, k, v, cu_seqlens, sets, stream):
+    """Attention of a packed batch over the cover of per-head index sets in
+    one launch chain: sets(cu_dev, max_len) gives v_idx, s_idx for the
+    n_seqs * heads heads."""
+    cu = _cu_list(q, k, v, cu_seqlens)
+    max_len = max(b - a for a, b in zip(cu, cu[1:]))
+    cu_dev = torch.tensor(cu, dtype=torch.int32, device=q.device)
+    v_idx, s_idx = sets(cu_dev, max_len)
+    idx = msa.build_index_varlen(v_idx, s_idx, cu_dev, max_len, q.shape[0], rows=q.shape[1], stream=stream)
+    return msa.sparse_prefill_varlen(q, k, v, idx, cu_dev, max_len, stream=stream)
 
 def _batched(q, k, v):
     if q.dim() == 3:
@@ -234,17 +256,12 @@ def vertical_slash_sparse_attention(q, k, v, vertical_topk: int, slash_topk: int
     and slash_topk diagonals the online estimate selects, then causal
     attention over their 64-wide block cover.  Returns the attention output."""
     if cu_seqlens is not None:
-        plans = {}                      # one set of buffers per distinct length
-
-        def one(qi, ki, vi, oi):
-            n = qi.shape[1]
-            plan = plans.get(n)
-            if plan is None:
-                plan = plans[n] = LayerPlan(qi.shape[0], ki.shape[0], n, min(vertical_topk, n),
-                                            min(slash_topk, n), str(qi.device), qi.dtype)
-            vertical_slash_layer(qi, ki, vi, plan.vertical_topk, plan.slash_topk, plan=plan, out=oi,
-                                 stream=stream)
-        return _packed(q, k, v, cu_seqlens, one)
+        # each sequence estimated, indexed and attended as on its own (a
+        # sequence of at most k tokens selects all of them); one launch chain
+        def sets(cu_dev, max_len):
+            return msa.estimate_vs_varlen(q, k, cu_dev, max_len, min(vertical_topk, max_len),
+                                          min(slash_topk, max_len), stream=stream)
+        return _packed_varlen(q, k, v, cu_seqlens, sets, stream)
     q4, k4, v4, squeeze = _batched(q, k, v)
     f = _fold(q4, k4, v4)
     if f is not None:
@@ -293,10 +310,16 @@ def streaming_forward(q, k, v, init_num: int, local_window_num: int, *, cu_seqle
     keys and to the local_window_num keys ending at itself (diagonal offsets
     0 .. local_window_num - 1), causally, over their 64-wide block cover."""
     if cu_seqlens is not None:
-        def one(qi, ki, vi, oi):
-            n = qi.shape[1]
-            _streaming_into(qi, ki, vi, min(init_num, n), min(local_window_num, n), oi, stream)
-        return _packed(q, k, v, cu_seqlens, one)
+        if init_num < 1 or local_window_num < 1:
+            raise msa.MsaError("init_num and local_window_num must be at least 1")
+
+        def sets(cu_dev, max_len):
+            # the same sets for every head; entries past a sequence's end select nothing
+            heads = (cu_dev.shape[0] - 1) * q.shape[0]
+            i32 = dict(dtype=torch.int32, device=q.device)
+            return (torch.arange(min(init_num, max_len), **i32).expand(heads, -1).contiguous(),
+                    torch.arange(min(local_window_num, max_len), **i32).expand(heads, -1).contiguous())
+        return _packed_varlen(q, k, v, cu_seqlens, sets, stream)
     q4, k4, v4, squeeze = _batched(q, k, v)
     hq, hkv, n = q4.shape[1], k4.shape[1], q4.shape[2]
     if not (1 <= init_num <= n and 1 <= local_window_num <= n):

@@ -61,6 +61,15 @@ _SIGS = {
                                                 ctypes.c_size_t, _VP, _VP, _VP]),
     "msa_dense_prefill": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "msa_estimate_bs_workspace": (ctypes.c_size_t, [_VP, _I32]),
+    "msa_estimate_vs_varlen_workspace": (ctypes.c_size_t, [_VP, _VP, _I32]),
+    "msa_estimate_vs_varlen": (ctypes.c_int, [_VP, _VP, _VP, _VP, _I32, _I32, _I32, _VP, _VP, _VP, ctypes.c_size_t,
+                                              _VP]),
+    "msa_build_index_varlen": (ctypes.c_int, [_VP, _VP, _VP, _I32, _VP, _I32, _I32, _VP, _VP, _I32, _VP, _VP, _I32,
+                                              _VP]),
+    "msa_sparse_prefill_varlen_workspace": (ctypes.c_size_t, [_VP, _VP, _I32]),
+    "msa_sparse_prefill_varlen": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32, _VP,
+                                                 ctypes.c_size_t, _VP, _VP, _VP]),
+    "msa_dense_prefill_varlen": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "msa_estimate_bs": (ctypes.c_int, [_VP, _VP, _VP, _I32, _I32, _VP, _VP, _I32, _VP, _VP,
                                        ctypes.c_size_t, _VP]),
 }
@@ -454,6 +463,141 @@ def sparse_prefill_fused(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, v_id
                                         _rows_dev(out, "out", p, q),
                                         _rows_dev(lse, "lse", p, q, True) if want_lse else None, _stream(stream)),
            "msa_sparse_prefill_fused")
+    return (out, lse) if want_lse else out
+
+
+class Varlen(ctypes.Structure):
+    """msa_varlen: a packed batch of sequences of different lengths."""
+    _fields_ = [("cu_seqlens", ctypes.c_void_p), ("n_seqs", ctypes.c_int32), ("max_seqlen", ctypes.c_int32)]
+
+
+def varlen(cu_seqlens: torch.Tensor, max_seqlen: int) -> Varlen:
+    """The descriptor of a packed batch: cu_seqlens int32 [n_seqs + 1] on the
+    GPU (rows cu[s] .. cu[s+1]-1 of every head are sequence s), max_seqlen
+    at least every length."""
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.shape[0] < 2:
+        raise MsaError("cu_seqlens must be int32 [n_seqs + 1]")
+    return Varlen(_dev(cu_seqlens, "cu_seqlens"), cu_seqlens.shape[0] - 1, int(max_seqlen))
+
+
+def estimate_vs_varlen_workspace_bytes(n_q_heads: int, n_kv_heads: int, rows: int, cu_seqlens: torch.Tensor,
+                                       max_seqlen: int, dtype=torch.bfloat16) -> int:
+    p = problem(n_q_heads, n_kv_heads, rows, MSA_BF16 if dtype == torch.bfloat16 else MSA_F32)
+    vl = varlen(cu_seqlens, max_seqlen)
+    return int(load().msa_estimate_vs_varlen_workspace(ctypes.byref(p), ctypes.byref(vl), LAST_Q))
+
+
+@on_stream
+def estimate_vs_varlen(q: torch.Tensor, k: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int,
+                       vertical_topk: int, slash_topk: int, *, workspace: torch.Tensor | None = None,
+                       v_idx: torch.Tensor | None = None, s_idx: torch.Tensor | None = None,
+                       sm_scale: float = 0.0, stream=None):
+    """estimate_vs of every sequence of a packed batch (q [Hq, total, 128], k
+    [Hkv, total, 128]) in one launch chain: v_idx [n_seqs * Hq, vertical_topk]
+    and s_idx [n_seqs * Hq, slash_topk], head h of sequence s at row
+    s * Hq + h."""
+    lib = load()
+    p = _problem_of(q, k, sm_scale)
+    vl = varlen(cu_seqlens, max_seqlen)
+    heads = vl.n_seqs * q.shape[0]
+    need = int(lib.msa_estimate_vs_varlen_workspace(ctypes.byref(p), ctypes.byref(vl), LAST_Q))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if v_idx is None:
+        v_idx = torch.empty((heads, vertical_topk), dtype=torch.int32, device=q.device)
+    if s_idx is None:
+        s_idx = torch.empty((heads, slash_topk), dtype=torch.int32, device=q.device)
+    for t, name, kk in ((v_idx, "v_idx", vertical_topk), (s_idx, "s_idx", slash_topk)):
+        if t.dtype != torch.int32 or tuple(t.shape) != (heads, kk):
+            raise MsaError(f"{name} must be int32 [{heads}, {kk}]")
+    _check(lib.msa_estimate_vs_varlen(ctypes.byref(p), ctypes.byref(vl), _in_dev(q, "q"), _in_dev(k, "k"), LAST_Q,
+                                      vertical_topk, slash_topk, _dev(v_idx, "v_idx"), _dev(s_idx, "s_idx"),
+                                      _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                      _stream(stream)), "msa_estimate_vs_varlen")
+    return v_idx, s_idx
+
+
+@on_stream
+def build_index_varlen(v_idx: torch.Tensor, s_idx: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int,
+                       n_q_heads: int, *, rows: int | None = None, out: IndexTensors | None = None,
+                       stream=None) -> IndexTensors:
+    """build_index of every sequence of a packed batch: work lists of
+    n_seqs * n_q_heads heads, each for max_seqlen tokens (rows: the packed
+    length, which bounds cu_seqlens; default max_seqlen * n_seqs)."""
+    lib = load()
+    vl = varlen(cu_seqlens, max_seqlen)
+    heads, kv = v_idx.shape
+    ks = s_idx.shape[1]
+    if heads != vl.n_seqs * n_q_heads:
+        raise MsaError(f"index sets must have n_seqs * n_q_heads = {vl.n_seqs * n_q_heads} rows")
+    p = problem(n_q_heads, 1, rows if rows is not None else max_seqlen * vl.n_seqs, MSA_BF16)
+    if out is None:
+        cb, cc = index_caps(max_seqlen, kv, ks, heads)
+        out = alloc_index(heads, max_seqlen, cb, cc, v_idx.device)
+    for t in (v_idx, s_idx):
+        if t.dtype != torch.int32 or t.dim() != 2 or t.shape[0] != heads:
+            raise MsaError(f"index sets must be int32 [{heads}, k]")
+    bc, bo, cb, cc, ci, ccap = _index_ptrs(out, heads, max_seqlen)
+    _check(lib.msa_build_index_varlen(ctypes.byref(p), ctypes.byref(vl), _dev(v_idx, "v_idx") if kv else None, kv,
+                                      _dev(s_idx, "s_idx") if ks else None, ks, BLOCK, bc, bo, cb, cc, ci, ccap,
+                                      _stream(stream)), "msa_build_index_varlen")
+    return out
+
+
+def sparse_prefill_varlen_workspace_bytes(n_q_heads: int, n_kv_heads: int, rows: int, cu_seqlens: torch.Tensor,
+                                          max_seqlen: int, dtype=torch.bfloat16, phase_keys: int = 0) -> int:
+    p = problem(n_q_heads, n_kv_heads, rows, MSA_BF16 if dtype == torch.bfloat16 else MSA_F32)
+    vl = varlen(cu_seqlens, max_seqlen)
+    return int(load().msa_sparse_prefill_varlen_workspace(ctypes.byref(p), ctypes.byref(vl), phase_keys))
+
+
+@on_stream
+def sparse_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: IndexTensors,
+                          cu_seqlens: torch.Tensor, max_seqlen: int, *, out: torch.Tensor | None = None,
+                          lse: torch.Tensor | bool | None = None, sm_scale: float = 0.0, phase_keys: int = 0,
+                          workspace: torch.Tensor | None = None, stream=None):
+    """sparse_prefill of every sequence of a packed batch over the work lists
+    of build_index_varlen; out (and lse) packed like q."""
+    lib = load()
+    p = _problem_of(q, k, sm_scale, v)
+    vl = varlen(cu_seqlens, max_seqlen)
+    if out is None:
+        out = _out_like(q, p)
+    want_lse = lse is not None and lse is not False
+    if lse is True:
+        lse = _lse_like(q, p)
+    bc, bo, cb, cc, ci, ccap = _index_ptrs(index, vl.n_seqs * q.shape[0], max_seqlen)
+    need = int(lib.msa_sparse_prefill_varlen_workspace(ctypes.byref(p), ctypes.byref(vl), phase_keys))
+    ws_ptr, ws_bytes = None, 0
+    if need > 0:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    _check(lib.msa_sparse_prefill_varlen(ctypes.byref(p), ctypes.byref(vl), _in_dev(q, "q"), _in_dev(k, "k"),
+                                         _in_dev(v, "v"), bc, bo, cb, cc, ci, ccap, phase_keys, ws_ptr, ws_bytes,
+                                         _rows_dev(out, "out", p, q),
+                                         _rows_dev(lse, "lse", p, q, True) if want_lse else None, _stream(stream)),
+           "msa_sparse_prefill_varlen")
+    return (out, lse) if want_lse else out
+
+
+@on_stream
+def dense_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                         max_seqlen: int, *, out: torch.Tensor | None = None, lse: torch.Tensor | bool | None = None,
+                         sm_scale: float = 0.0, stream=None):
+    """Dense causal attention of every sequence of a packed batch."""
+    lib = load()
+    p = _problem_of(q, k, sm_scale, v)
+    vl = varlen(cu_seqlens, max_seqlen)
+    if out is None:
+        out = _out_like(q, p)
+    want_lse = lse is not None and lse is not False
+    if lse is True:
+        lse = _lse_like(q, p)
+    _check(lib.msa_dense_prefill_varlen(ctypes.byref(p), ctypes.byref(vl), _in_dev(q, "q"), _in_dev(k, "k"),
+                                        _in_dev(v, "v"), _rows_dev(out, "out", p, q),
+                                        _rows_dev(lse, "lse", p, q, True) if want_lse else None, _stream(stream)),
+           "msa_dense_prefill_varlen")
     return (out, lse) if want_lse else out
 
 

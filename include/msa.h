@@ -349,6 +349,61 @@ int msa_decode_sparse_varlen(const msa_problem *p, const void *q, const void *k,
                              const int32_t *cache_lens, int32_t topk, int32_t *idx, int32_t flags, void *workspace,
                              size_t workspace_bytes, void *out, float *lse, float *recovery, void *stream);
 
+/* ---- Packed batches of sequences of different lengths ----
+ * The pages' kernel-only interface takes a batch dimension ("MInference 1.0
+ * README", kernel-only usage); these forms take a batch whose sequences have
+ * different lengths as one problem (one launch chain instead of one per
+ * sequence).  Sequence s holds rows cu_seqlens[s] .. cu_seqlens[s+1] - 1 of
+ * every head of q, k, v, out and lse, which hold p->seq_len rows per head
+ * (p->seq_stride apart; 0: seq_len).  Each sequence is computed exactly as the
+ * one-sequence call on its own rows would compute it, except that a sequence
+ * shorter than last_q = 64 takes all its rows as the estimate's window (the
+ * one-sequence estimate refuses such a length).
+ *   cu_seqlens: device int32 [n_seqs + 1], ascending from 0, at most seq_len,
+ *     4-byte aligned; max_seqlen: a host value at least every length, at
+ *     most seq_len.  The device clamps entries into [0, seq_len] and lengths
+ *     to max_seqlen, so contents that break these rules give unspecified
+ *     results but no access outside the buffers.
+ *   n_seqs * n_q_heads at most 32767.
+ *   Per-head arrays (index sets, work lists) hold n_seqs * n_q_heads heads:
+ *     head h of sequence s is s * n_q_heads + h; each is sized for max_seqlen
+ *     (index sets [heads, topk]; block_count [heads, ceil(max_seqlen / 64)],
+ *     caps from msa_index_caps with seq_len = max_seqlen).  A sequence whose
+ *     length is at most a top-k selects all its keys and then the positions
+ *     past its end, which msa_build_index_varlen ignores.
+ * Errors as for the one-sequence calls; a NULL descriptor or cu_seqlens:
+ * MSA_ERR_NULL; n_seqs, max_seqlen or the head count out of range:
+ * MSA_ERR_SHAPE.                                                            */
+typedef struct {
+    const int32_t *cu_seqlens;
+    int32_t n_seqs;
+    int32_t max_seqlen;
+} msa_varlen;
+
+size_t msa_estimate_vs_varlen_workspace(const msa_problem *p, const msa_varlen *vl, int32_t last_q);
+/* msa_estimate_vs per sequence (the same online estimate); top-k values in
+ * [1, max_seqlen]. */
+int msa_estimate_vs_varlen(const msa_problem *p, const msa_varlen *vl, const void *q, const void *k, int32_t last_q,
+                           int32_t vertical_topk, int32_t slash_topk, int32_t *v_idx, int32_t *s_idx, void *workspace,
+                           size_t workspace_bytes, void *stream);
+/* msa_build_index per sequence (the same cover rule). */
+int msa_build_index_varlen(const msa_problem *p, const msa_varlen *vl, const int32_t *v_idx, int32_t vertical_topk,
+                           const int32_t *s_idx, int32_t slash_topk, int32_t block, int32_t *block_count,
+                           int32_t *block_offset, int32_t cap_blocks, int32_t *column_count, int32_t *column_index,
+                           int32_t cap_cols, void *stream);
+size_t msa_sparse_prefill_varlen_workspace(const msa_problem *p, const msa_varlen *vl, int32_t phase_keys);
+/* msa_sparse_prefill per sequence (the same attention over the lists, key
+ * phases of the longest sequence's geometry). */
+int msa_sparse_prefill_varlen(const msa_problem *p, const msa_varlen *vl, const void *q, const void *k, const void *v,
+                              const int32_t *block_count, const int32_t *block_offset, int32_t cap_blocks,
+                              const int32_t *column_count, const int32_t *column_index, int32_t cap_cols,
+                              int32_t phase_keys, void *workspace, size_t workspace_bytes, void *out, float *lse,
+                              void *stream);
+/* msa_dense_prefill per sequence (the FlashAttention baseline the speedups
+ * of the pages are quoted against, on a packed batch). */
+int msa_dense_prefill_varlen(const msa_problem *p, const msa_varlen *vl, const void *q, const void *k, const void *v,
+                             void *out, float *lse, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

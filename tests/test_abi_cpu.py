@@ -30,7 +30,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 24, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -222,6 +222,41 @@ def test_decode_sparse_validation(lib):
     assert vl(P(), topk=4097) == RANGE
     assert vl(P(), wsb=need - 1) == WS
     assert vl(P(hq=6, hkv=4)) == SHAPE
+
+
+def test_varlen_validation(lib):
+    """The packed-batch calls check their descriptor on the host."""
+    VL = lambda cu=FAKE, n=3, mx=1000: ctypes.byref(B.Varlen(cu, n, mx))
+    est = lambda prob, vl, kv=8, ks=8, ws=FAKE, wsb=1 << 30: lib.msa_estimate_vs_varlen(
+        prob, vl, FAKE, FAKE, 64, kv, ks, FAKE, FAKE, ws, wsb, None)
+    assert est(P(), None) == NULL
+    assert est(P(), VL(cu=None)) == NULL
+    assert est(P(), VL(cu=ctypes.c_void_p(0x1002))) == RANGE
+    assert est(P(), VL(n=0)) == SHAPE
+    assert est(P(), VL(mx=0)) == SHAPE
+    assert est(P(), VL(mx=4097)) == SHAPE                       # longer than the rows of a head
+    assert est(P(), VL(n=1024)) == SHAPE                        # 1024 sequences x 32 heads > 32767
+    assert est(P(), VL(), kv=1001) == RANGE                     # top-k above max_seqlen
+    assert est(P(hq=6, hkv=4), VL()) == SHAPE
+    need = lib.msa_estimate_vs_varlen_workspace(P(), VL(), 64)
+    assert need > 0 and lib.msa_estimate_vs_varlen_workspace(P(), VL(), 32) == 0
+    assert est(P(), VL(), wsb=need - 1) == WS
+    # the work lists are sized for max_seqlen per head
+    cb, cc = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.msa_index_caps(P(n=1000), 8, 30, 64, ctypes.byref(cb), ctypes.byref(cc)) == OK
+    bi = lambda vl, cap_b=cb.value, cap_c=cc.value: lib.msa_build_index_varlen(
+        P(), vl, FAKE, 8, FAKE, 30, 64, FAKE, FAKE, cap_b, FAKE, FAKE, cap_c, None)
+    assert bi(None) == NULL
+    assert bi(VL(), cap_b=cb.value - 1) == CAP
+    assert bi(VL(mx=5000)) == SHAPE
+    sp = lambda vl, wsb=1 << 30: lib.msa_sparse_prefill_varlen(
+        P(n=1 << 17), vl, FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, FAKE, 8, 0, FAKE, wsb, FAKE, None, None)
+    assert sp(None) == NULL
+    assert sp(VL(n=4, mx=1 << 17), wsb=1) == WS                 # phases of the longest sequence need state
+    assert lib.msa_sparse_prefill_varlen_workspace(P(n=1 << 17), VL(n=4, mx=1 << 17), 0) > \
+        lib.msa_sparse_prefill_varlen_workspace(P(n=1 << 17), VL(n=2, mx=1 << 17), 0) > 0
+    assert lib.msa_sparse_prefill_varlen_workspace(P(n=1 << 17), VL(n=4, mx=1000), 0) == 0   # one phase
+    assert lib.msa_dense_prefill_varlen(P(), VL(cu=None), FAKE, FAKE, FAKE, FAKE, None, None) == NULL
 
 
 def test_walk_marks_query(lib):
