@@ -37,20 +37,23 @@ constexpr int kBsLdsKeys = 15360;
 template <typename T>
 __global__ __launch_bounds__(kD) void bs_pool_kernel(BsArgs a) {
     __shared__ float part[8][kD];
-    const int64_t nb = (a.n + 63) / 64;
+    const int64_t nb = (a.n + 63) / 64;              // blocks per head in the pooled arrays
     const int c = blockIdx.x;
-    const int head = blockIdx.y;
+    // q heads, then kv heads, of each sequence of a packed batch in turn
+    const int seq = blockIdx.y / (a.hq + a.hkv), head = blockIdx.y % (a.hq + a.hkv);
+    const SeqSpan sp = seq_span(a.vl.cu, seq, a.vl.rows, a.n);
+    if ((int64_t)c * 64 >= sp.n) return;             // past the end of a shorter packed sequence
     const T *src;
     float *dst;
     if (head < a.hq) {
-        src = reinterpret_cast<const T *>(a.q) + (int64_t)head * a.stride * kD;
-        dst = a.qm + ((int64_t)head * nb + c) * kD;
+        src = reinterpret_cast<const T *>(a.q) + ((int64_t)head * a.stride + sp.row0) * kD;
+        dst = a.qm + (((int64_t)seq * a.hq + head) * nb + c) * kD;
     } else {
-        src = reinterpret_cast<const T *>(a.k) + (int64_t)(head - a.hq) * a.stride * kD;
-        dst = a.km + ((int64_t)(head - a.hq) * nb + c) * kD;
+        src = reinterpret_cast<const T *>(a.k) + ((int64_t)(head - a.hq) * a.stride + sp.row0) * kD;
+        dst = a.km + (((int64_t)seq * a.hkv + head - a.hq) * nb + c) * kD;
     }
     // a short last block (length not a multiple of 64) is the mean of its rows
-    const int nrows = (int)min((int64_t)64, a.n - (int64_t)c * 64);
+    const int nrows = (int)min((int64_t)64, sp.n - (int64_t)c * 64);
     const int d0 = (threadIdx.x & 15) * 8, rg = threadIdx.x >> 4;
     float acc[8] = {};
     for (int r = rg; r < nrows; r += 8) {
@@ -95,13 +98,14 @@ constexpr int kScorePitch = kD + 4;
 __global__ __launch_bounds__(kThreads) void bs_score_kernel(BsArgs a) {
     __shared__ alignas(16) float qs[64 * kScorePitch];
     __shared__ alignas(16) float ks[64 * kScorePitch];
-    const int kt = blockIdx.x, qt = blockIdx.y, h = blockIdx.z;
-    const int64_t nb = (a.n + 63) / 64;
+    const int kt = blockIdx.x, qt = blockIdx.y, h = blockIdx.z;   // h: head s * hq + h' of sequence s
+    const int64_t nbr = (a.n + 63) / 64;                    // blocks per head in the arrays
+    const int64_t nb = (seq_span(a.vl.cu, h / a.hq, a.vl.rows, a.n).n + 63) / 64;   // this sequence's
     const int64_t q0 = a.row0 + (int64_t)qt * 64;          // first query block of the tile
-    if ((int64_t)kt * 64 > q0 + 63) return;                 // above the diagonal
+    if ((int64_t)kt * 64 > q0 + 63 || q0 >= nb) return;    // above the diagonal, or past the sequence
     const int G = a.hq / a.hkv;
-    const float *qm = a.qm + (int64_t)h * nb * kD;
-    const float *km = a.km + (int64_t)(h / G) * nb * kD;
+    const float *qm = a.qm + (int64_t)h * nbr * kD;
+    const float *km = a.km + (int64_t)(h / G) * nbr * kD;  // h / G: kv head s * hkv + h' / G
     // both tiles: 64 rows x 32 float4, eight per thread (rows past nb read row nb-1)
     for (int i = threadIdx.x; i < 64 * 32; i += kThreads) {
         const int r = i >> 5, c4 = i & 31;
@@ -129,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void bs_score_kernel(BsArgs a) {
     for (int i = 0; i < 4; ++i) {
         const int64_t qb = q0 + 16 * i + ty;
         if (qb >= nb || qb >= a.row0 + a.chunk_rows) continue;
-        uint32_t *row = a.keys + ((int64_t)h * a.chunk_rows + (qb - a.row0)) * nb;
+        uint32_t *row = a.keys + ((int64_t)h * a.chunk_rows + (qb - a.row0)) * nbr;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int64_t kb = (int64_t)kt * 64 + 16 * j + tx;
@@ -210,11 +214,12 @@ __global__ __launch_bounds__(kThreads) void bs_select_kernel(BsArgs a) {
     __shared__ uint32_t hist[256];
     __shared__ uint32_t tmp[kThreads];
     __shared__ uint32_t sel_state[2];
-    const int64_t nb = (a.n + 63) / 64;
-    const int64_t rows = min((int64_t)a.chunk_rows, nb - a.row0);
+    const int64_t nbr = (a.n + 63) / 64;                 // blocks per head in the arrays
+    const int64_t rows = min((int64_t)a.chunk_rows, nbr - a.row0);
     const int64_t b = a.row0 + rows - 1 - blockIdx.x;   // heavy rows first
-    const int h = blockIdx.y;
-    const int64_t item = (int64_t)h * nb + b;
+    const int h = blockIdx.y;                            // head s * hq + h' of sequence s
+    if (b * 64 >= seq_span(a.vl.cu, h / a.hq, a.vl.rows, a.n).n) return;   // past the sequence's end
+    const int64_t item = (int64_t)h * nbr + b;
     int32_t *out = a.block_offset + item * a.cap_b;
     const int ncand = (int)b + 1;
     const int kk = min(a.topk, ncand);
@@ -226,7 +231,7 @@ __global__ __launch_bounds__(kThreads) void bs_select_kernel(BsArgs a) {
         for (int c = threadIdx.x; c < ncand; c += kThreads) out[c] = c * 64;
         return;
     }
-    const uint32_t *krow = a.keys + ((int64_t)h * a.chunk_rows + (b - a.row0)) * nb;
+    const uint32_t *krow = a.keys + ((int64_t)h * a.chunk_rows + (b - a.row0)) * nbr;
     if (ncand <= kBsLdsKeys) {
         for (int c = threadIdx.x; c < ncand; c += kThreads) keys[c] = krow[c];
         select_row<true>(keys, ncand, kk, out, a.cap_b, hist, tmp, sel_state);
@@ -237,7 +242,7 @@ __global__ __launch_bounds__(kThreads) void bs_select_kernel(BsArgs a) {
 
 template <typename T> hipError_t launch_t(BsArgs a, hipStream_t s) {
     const int64_t nb = (a.n + 63) / 64;
-    hipLaunchKernelGGL(bs_pool_kernel<T>, dim3((unsigned)nb, a.hq + a.hkv), dim3(kD), 0, s, a);
+    hipLaunchKernelGGL(bs_pool_kernel<T>, dim3((unsigned)nb, (a.hq + a.hkv) * a.vl.nseq), dim3(kD), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t lds = (size_t)min(nb, (int64_t)kBsLdsKeys) * sizeof(uint32_t);
@@ -247,9 +252,9 @@ template <typename T> hipError_t launch_t(BsArgs a, hipStream_t s) {
         a.row0 = r0;
         const int64_t rows = min((int64_t)a.chunk_rows, nb - r0);
         const unsigned kts = (unsigned)((r0 + rows + 63) / 64), qts = (unsigned)((rows + 63) / 64);
-        hipLaunchKernelGGL(bs_score_kernel, dim3(kts, qts, a.hq), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL(bs_score_kernel, dim3(kts, qts, a.hq * a.vl.nseq), dim3(kThreads), 0, s, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(bs_select_kernel, dim3((unsigned)rows, a.hq), dim3(kThreads), lds, s, a);
+        hipLaunchKernelGGL(bs_select_kernel, dim3((unsigned)rows, a.hq * a.vl.nseq), dim3(kThreads), lds, s, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;

@@ -182,6 +182,7 @@ struct BsArgs {
     int64_t row0;                // first query block of the chunk (set per launch)
     int32_t *block_count, *block_offset, *column_count;
     int32_t cap_b;
+    Varlen vl;                   // hq, hkv: heads per sequence; n: the longest sequence
 };
 
 // Query blocks per block-sparse scoring chunk.

@@ -769,18 +769,23 @@ int msa_dense_prefill_varlen(const msa_problem *p, const msa_varlen *vl, const v
 // chunk of query blocks
 static size_t bs_chunk_rows(int64_t nb) { return (size_t)(nb < msa::kBsChunkRows ? nb : msa::kBsChunkRows); }
 
-size_t msa_estimate_bs_workspace(const msa_problem *p, int32_t block) {
-    if (check_problem(p) != MSA_OK || block != 64) return 0;
-    const size_t nb = (size_t)((p->seq_len + 63) / 64);
-    return align_up((size_t)p->n_q_heads * nb * 128 * 4) + align_up((size_t)p->n_kv_heads * nb * 128 * 4) +
-           align_up((size_t)p->n_q_heads * bs_chunk_rows((int64_t)nb) * nb * 4);
+// hq, hkv: heads of all sequences; n: the longest sequence
+static size_t bs_workspace(int64_t hq, int64_t hkv, int64_t n) {
+    const size_t nb = (size_t)((n + 63) / 64);
+    return align_up((size_t)hq * nb * 128 * 4) + align_up((size_t)hkv * nb * 128 * 4) +
+           align_up((size_t)hq * bs_chunk_rows((int64_t)nb) * nb * 4);
 }
 
-int msa_estimate_bs(const msa_problem *p, const void *q, const void *k, int32_t block, int32_t topk_blocks,
-                    int32_t *block_count, int32_t *block_offset, int32_t cap_blocks, int32_t *column_count,
-                    void *workspace, size_t workspace_bytes, void *stream) {
-    int st = check_problem(p);
-    if (st) return st;
+size_t msa_estimate_bs_workspace(const msa_problem *p, int32_t block) {
+    if (check_problem(p) != MSA_OK || block != 64) return 0;
+    return bs_workspace(p->n_q_heads, p->n_kv_heads, p->seq_len);
+}
+
+static int run_estimate_bs(const msa_problem *p, const msa::Varlen *vl, int64_t n, const void *q, const void *k,
+                           int32_t block, int32_t topk_blocks, int32_t *block_count, int32_t *block_offset,
+                           int32_t cap_blocks, int32_t *column_count, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+    int st;
     if (!q || !k || !block_count || !block_offset || !column_count || !workspace)
         return fail(MSA_ERR_NULL, "a required pointer is NULL");
     if ((st = check_rows(q, k, nullptr, nullptr))) return st;
@@ -788,25 +793,27 @@ int msa_estimate_bs(const msa_problem *p, const void *q, const void *k, int32_t 
         return fail(MSA_ERR_RANGE, "index arrays must be 4-byte aligned");
     if (off_align(workspace, 16)) return fail(MSA_ERR_RANGE, "workspace is not 16-byte aligned");
     if (block != 64) return fail(MSA_ERR_RANGE, "block must be 64 (got %d)", block);
-    const int64_t nb = (p->seq_len + 63) / 64;
+    const int64_t nb = (n + 63) / 64;
     if (topk_blocks < 1) return fail(MSA_ERR_RANGE, "topk_blocks must be >= 1");
     const int64_t need = topk_blocks < nb ? topk_blocks : nb;
     if (cap_blocks < need) return fail(MSA_ERR_CAPACITY, "cap_blocks %d below %lld", cap_blocks, (long long)need);
-    const size_t ws = msa_estimate_bs_workspace(p, block);
+    const int64_t nseq = vl ? vl->nseq : 1;
+    const size_t ws = bs_workspace(p->n_q_heads * nseq, p->n_kv_heads * nseq, n);
     if (workspace_bytes < ws) return fail(MSA_ERR_WORKSPACE, "workspace too small: %zu < %zu", workspace_bytes, ws);
     msa::BsArgs a;
     a.q = q;
     a.k = k;
-    a.n = p->seq_len;
+    a.n = n;
     a.stride = stride_of(p);
     a.hq = p->n_q_heads;
     a.hkv = p->n_kv_heads;
+    if (vl) a.vl = *vl;
     a.scale = scale_of(p);
     a.topk = topk_blocks;
     a.qm = at<float>(workspace, 0);
-    a.km = at<float>(workspace, align_up((size_t)p->n_q_heads * nb * 128 * 4));
-    a.keys = at<uint32_t>(workspace, align_up((size_t)p->n_q_heads * nb * 128 * 4) +
-                                         align_up((size_t)p->n_kv_heads * nb * 128 * 4));
+    a.km = at<float>(workspace, align_up((size_t)(p->n_q_heads * nseq) * nb * 128 * 4));
+    a.keys = at<uint32_t>(workspace, align_up((size_t)(p->n_q_heads * nseq) * nb * 128 * 4) +
+                                         align_up((size_t)(p->n_kv_heads * nseq) * nb * 128 * 4));
     a.chunk_rows = (int32_t)bs_chunk_rows(nb);    // the workspace holds this many rows of keys
     a.row0 = 0;
     a.block_count = block_count;
@@ -815,6 +822,31 @@ int msa_estimate_bs(const msa_problem *p, const void *q, const void *k, int32_t 
     a.cap_b = cap_blocks;
     return launch_status(msa::launch_estimate_bs(a, p->dtype, reinterpret_cast<hipStream_t>(stream)),
                          "estimate_bs");
+}
+
+int msa_estimate_bs(const msa_problem *p, const void *q, const void *k, int32_t block, int32_t topk_blocks,
+                    int32_t *block_count, int32_t *block_offset, int32_t cap_blocks, int32_t *column_count,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+    const int st = check_problem(p);
+    if (st) return st;
+    return run_estimate_bs(p, nullptr, p->seq_len, q, k, block, topk_blocks, block_count, block_offset, cap_blocks,
+                           column_count, workspace, workspace_bytes, stream);
+}
+
+size_t msa_estimate_bs_varlen_workspace(const msa_problem *p, const msa_varlen *vl, int32_t block) {
+    msa::Varlen V;
+    if (check_varlen(p, vl, V) != MSA_OK || block != 64) return 0;
+    return bs_workspace((int64_t)p->n_q_heads * V.nseq, (int64_t)p->n_kv_heads * V.nseq, vl->max_seqlen);
+}
+
+int msa_estimate_bs_varlen(const msa_problem *p, const msa_varlen *vl, const void *q, const void *k, int32_t block,
+                           int32_t topk_blocks, int32_t *block_count, int32_t *block_offset, int32_t cap_blocks,
+                           int32_t *column_count, void *workspace, size_t workspace_bytes, void *stream) {
+    msa::Varlen V;
+    const int st = check_varlen(p, vl, V);
+    if (st) return st;
+    return run_estimate_bs(p, &V, vl->max_seqlen, q, k, block, topk_blocks, block_count, block_offset, cap_blocks,
+                           column_count, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -178,12 +178,10 @@ def mixed_layer(q, k, v, plan: MixedPlan, *, out: torch.Tensor | None = None, ls
 # cu_seqlens[i] .. cu_seqlens[i+1]-1).  A batch whose batch stride is heads x
 # the head stride (a contiguous [B, H, N, D] tensor, or a slice of one along
 # the sequence) runs as one problem of B*H heads: one launch chain for the
-# whole batch.  A packed batch of the vertical-slash or A-shape kind runs as
-# one problem too, through the C ABI's variable-length calls (one launch
-# chain for all sequences).  Other batch layouts, and packed block-sparse
-# batches, run one sequence after another on the stream through the same
-# C-ABI steps; a packed sequence is then a view of the packed tensors (the C
-# ABI's seq_stride is the packed length).
+# whole batch.  A packed batch runs as one problem too, through the C ABI's
+# variable-length calls (one launch chain for all sequences).  Other batch
+# layouts run one element after another on the stream through the same C-ABI
+# steps.
 
 
 def _cu_list(q, k, v, cu_seqlens):
@@ -195,15 +193,6 @@ def _cu_list(q, k, v, cu_seqlens):
     if len(cu) < 2 or cu[0] != 0 or cu[-1] != q.shape[1] or any(b <= a for a, b in zip(cu, cu[1:])):
         raise msa.MsaError("cu_seqlens must rise strictly from 0 to the packed length")
     return cu
-
-
-def _packed(q, k, v, cu_seqlens, fn):
-    """Run fn(q_i, k_i, v_i, out_i) on each packed sequence i."""
-    cu = _cu_list(q, k, v, cu_seqlens)
-    out = torch.empty_like(q)
-    for a, b in zip(cu, cu[1:]):
-        fn(q[:, a:b], k[:, a:b], v[:, a:b], out[:, a:b])
-    return out
 
 
 def _packed_varlen(q, k, v, cu_seqlens, sets, stream):
@@ -281,10 +270,11 @@ def block_sparse_attention(q, k, v, topk: int, *, cu_seqlens=None, stream=None):
     """Block-sparse attention: each 64-row query block attends to its topk
     highest-scoring 64-key blocks (mean-pooled q and k block scores), causally."""
     if cu_seqlens is not None:
-        def one(qi, ki, vi, oi):
-            idx = msa.estimate_bs(qi, ki, topk, stream=stream)
-            msa.sparse_prefill(qi, ki, vi, idx, out=oi, stream=stream)
-        return _packed(q, k, v, cu_seqlens, one)
+        cu = _cu_list(q, k, v, cu_seqlens)
+        max_len = max(b - a for a, b in zip(cu, cu[1:]))
+        cu_dev = torch.tensor(cu, dtype=torch.int32, device=q.device)
+        idx = msa.estimate_bs_varlen(q, k, cu_dev, max_len, topk, stream=stream)
+        return msa.sparse_prefill_varlen(q, k, v, idx, cu_dev, max_len, stream=stream)
     q4, k4, v4, squeeze = _batched(q, k, v)
     f = _fold(q4, k4, v4)
     if f is not None:

@@ -70,6 +70,9 @@ _SIGS = {
     "msa_sparse_prefill_varlen": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32, _VP,
                                                  ctypes.c_size_t, _VP, _VP, _VP]),
     "msa_dense_prefill_varlen": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "msa_estimate_bs_varlen_workspace": (ctypes.c_size_t, [_VP, _VP, _I32]),
+    "msa_estimate_bs_varlen": (ctypes.c_int, [_VP, _VP, _VP, _VP, _I32, _I32, _VP, _VP, _I32, _VP, _VP,
+                                              ctypes.c_size_t, _VP]),
     "msa_estimate_bs": (ctypes.c_int, [_VP, _VP, _VP, _I32, _I32, _VP, _VP, _I32, _VP, _VP,
                                        ctypes.c_size_t, _VP]),
 }
@@ -721,4 +724,28 @@ def estimate_bs(q: torch.Tensor, k: torch.Tensor, topk_blocks: int, *, cap_block
                                bc, bo, cb, cc,
                                _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                                _stream(stream)), "msa_estimate_bs")
+    return out
+
+
+@on_stream
+def estimate_bs_varlen(q: torch.Tensor, k: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int,
+                       topk_blocks: int, *, out: IndexTensors | None = None, workspace: torch.Tensor | None = None,
+                       sm_scale: float = 0.0, stream=None) -> IndexTensors:
+    """estimate_bs of every sequence of a packed batch: work lists of
+    n_seqs * Hq heads, each for max_seqlen tokens."""
+    lib = load()
+    p = _problem_of(q, k, sm_scale)
+    vl = varlen(cu_seqlens, max_seqlen)
+    heads = vl.n_seqs * q.shape[0]
+    nqb = (max_seqlen + BLOCK - 1) // BLOCK
+    if out is None:
+        out = alloc_index(heads, max_seqlen, min(topk_blocks, nqb), 0, q.device)
+    ws_bytes = int(lib.msa_estimate_bs_varlen_workspace(ctypes.byref(p), ctypes.byref(vl), BLOCK))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    bc, bo, cb, cc, _, _ = _index_ptrs(out, heads, max_seqlen)
+    _check(lib.msa_estimate_bs_varlen(ctypes.byref(p), ctypes.byref(vl), _in_dev(q, "q"), _in_dev(k, "k"), BLOCK,
+                                      topk_blocks, bc, bo, cb, cc, _dev(workspace, "workspace"),
+                                      workspace.numel() * workspace.element_size(), _stream(stream)),
+           "msa_estimate_bs_varlen")
     return out

@@ -368,9 +368,12 @@ int msa_decode_sparse_varlen(const msa_problem *p, const void *q, const void *k,
  *   Per-head arrays (index sets, work lists) hold n_seqs * n_q_heads heads:
  *     head h of sequence s is s * n_q_heads + h; each is sized for max_seqlen
  *     (index sets [heads, topk]; block_count [heads, ceil(max_seqlen / 64)],
- *     caps from msa_index_caps with seq_len = max_seqlen).  A sequence whose
+ *     caps from msa_index_caps with seq_len = max_seqlen); the entries of
+ *     query blocks past a sequence's end are not written.  A sequence whose
  *     length is at most a top-k selects all its keys and then the positions
  *     past its end, which msa_build_index_varlen ignores.
+ *   Rows of q, k, v, out and lse outside every sequence are neither read nor
+ *     written.
  * Errors as for the one-sequence calls; a NULL descriptor or cu_seqlens:
  * MSA_ERR_NULL; n_seqs, max_seqlen or the head count out of range:
  * MSA_ERR_SHAPE.                                                            */
@@ -399,6 +402,13 @@ int msa_sparse_prefill_varlen(const msa_problem *p, const msa_varlen *vl, const 
                               const int32_t *column_count, const int32_t *column_index, int32_t cap_cols,
                               int32_t phase_keys, void *workspace, size_t workspace_bytes, void *out, float *lse,
                               void *stream);
+size_t msa_estimate_bs_varlen_workspace(const msa_problem *p, const msa_varlen *vl, int32_t block);
+/* msa_estimate_bs per sequence (the same block scores and selection): work
+ * lists of n_seqs * n_q_heads heads, ceil(max_seqlen / 64) query blocks each;
+ * cap_blocks at least min(topk_blocks, ceil(max_seqlen / 64)). */
+int msa_estimate_bs_varlen(const msa_problem *p, const msa_varlen *vl, const void *q, const void *k, int32_t block,
+                           int32_t topk_blocks, int32_t *block_count, int32_t *block_offset, int32_t cap_blocks,
+                           int32_t *column_count, void *workspace, size_t workspace_bytes, void *stream);
 /* msa_dense_prefill per sequence (the FlashAttention baseline the speedups
  * of the pages are quoted against, on a packed batch). */
 int msa_dense_prefill_varlen(const msa_problem *p, const msa_varlen *vl, const void *q, const void *k, const void *v,

@@ -30,7 +30,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 24, names
+    assert len(names) == 26, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -257,6 +257,14 @@ def test_varlen_validation(lib):
         lib.msa_sparse_prefill_varlen_workspace(P(n=1 << 17), VL(n=2, mx=1 << 17), 0) > 0
     assert lib.msa_sparse_prefill_varlen_workspace(P(n=1 << 17), VL(n=4, mx=1000), 0) == 0   # one phase
     assert lib.msa_dense_prefill_varlen(P(), VL(cu=None), FAKE, FAKE, FAKE, FAKE, None, None) == NULL
+    bs = lambda vl, cap=8, wsb=1 << 30: lib.msa_estimate_bs_varlen(P(), vl, FAKE, FAKE, 64, 8, FAKE, FAKE, cap,
+                                                                   FAKE, FAKE, wsb, None)
+    assert bs(None) == NULL
+    assert bs(VL(), cap=7) == CAP
+    assert bs(VL(mx=5000)) == SHAPE
+    need_bs = lib.msa_estimate_bs_varlen_workspace(P(), VL(), 64)
+    assert need_bs > lib.msa_estimate_bs_varlen_workspace(P(), VL(n=2), 64) > 0
+    assert bs(VL(), wsb=need_bs - 1) == WS
 
 
 def test_walk_marks_query(lib):

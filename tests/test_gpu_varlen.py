@@ -165,6 +165,43 @@ def test_packed_varlen_equals_single_calls():
         assert torch.equal(msa.dense_prefill(qs, ks_, vs), r["dout"][:, a:b]), f"sequence {s} dense"
 
 
+def test_packed_block_sparse_varlen():
+    """The block-sparse estimate of a packed batch: each sequence's lists
+    against the oracle's selection on its own rows (top-3 and top-100 key
+    blocks of the mean-pooled scores, ties in a band), and its attention over
+    them."""
+    hq, hkv, lens = 4, 2, [150, 64 * 7, 2000, 30, 64 * 40 + 5]
+    q, k, v, cu = packed_inputs(hq, hkv, lens, seed=801)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    cu_d = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    max_len = max(lens)
+    for topk in (3, 100):
+        idx = msa.estimate_bs_varlen(qd, kd, cu_d, max_len, topk)
+        out = msa.sparse_prefill_varlen(qd, kd, vd, idx, cu_d, max_len)
+        bc, bo, cc = (t.cpu().numpy() for t in (idx.block_count, idx.block_offset, idx.column_count))
+        for s_, (a, b) in enumerate(zip(cu, cu[1:])):
+            n = b - a
+            nqb = (n + 63) // 64                      # entries past a sequence's blocks are not written
+            qs, ks_, vs = q[:, a:b], k[:, a:b], v[:, a:b]
+            rows = slice(s_ * hq, (s_ + 1) * hq)
+            what = f"block-sparse top-{topk} sequence {s_} ({n} tokens)"
+            assert (cc[rows][:, :nqb] == 0).all(), what
+            cnt, _, scores = oracle.block_sparse_select(qs, ks_, range(hq), topk=topk)
+            assert np.array_equal(bc[rows][:, :nqb], cnt), what
+            for h in range(hq):
+                for qb in range(nqb):
+                    kk = cnt[h, qb]
+                    starts = bo[rows][h, qb, :kk]
+                    assert np.all(starts % 64 == 0) and np.all(np.diff(starts) > 0), what
+                    u = scores[h, qb, : qb + 1]          # the band on the row's softmax (scores may be negative)
+                    pr = np.exp(u - u.max())
+                    check_band(starts // 64, pr / pr.sum(), kk, f"{what} h{h} b{qb}")
+            ref_idx = oracle.IndexArrays(bc[rows][:, :nqb], bo[rows][:, :nqb],
+                                         np.zeros((hq, nqb), np.int32), np.zeros((hq, nqb, 0), np.int32))
+            ro, _ = oracle.attention_with_mask(qs, ks_, vs, oracle.index_mask(ref_idx, n))
+            compare_out(out[:, a:b].float().cpu().numpy(), ro, False, what)
+
+
 def test_packed_streaming_and_block_sparse():
     """streaming_forward and block_sparse_attention with cu_seqlens: each
     sequence as the one-sequence call computes it."""
