@@ -360,7 +360,10 @@ __device__ __forceinline__ int lower_bound_near(const int32_t *list, int cnt, in
 // fp32 (a checking path) uses the same scheme with 64 KB of LDS.
 // kH q heads of one kv group per workgroup (2 kH waves) share every K/V copy;
 // used by the dense kernel, whose heads all walk the same tiles.
-template <typename T, bool kDense, int kH, bool kGrp = false, bool kFused = false, bool kExact = false>
+// kVar: a packed batch of sequences of different lengths (AttnArgs.vl), each
+// workgroup's heads belonging to one of them; otherwise one sequence.
+template <typename T, bool kDense, int kH, bool kGrp = false, bool kFused = false, bool kExact = false,
+          bool kVar = false>
 __global__ __launch_bounds__(kThreads * kH) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1, sizeof(T) == 2 ? 2 : 1)))
 void attn_fwd_kernel(AttnArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the body uses gfx950-only LDS builtins
@@ -374,7 +377,7 @@ void attn_fwd_kernel(AttnArgs a) {
     // query blocks per head in the per-head arrays (those of the longest
     // sequence of a packed batch)
     const int64_t nqb = (a.n + kBQ - 1) / kBQ;
-    const int64_t heads = (int64_t)a.hq * a.vl.nseq;  // heads in the per-head arrays
+    const int64_t heads = kVar ? (int64_t)a.hq * a.vl.nseq : a.hq;   // heads in the per-head arrays
     const int G = a.hq / a.hkv;
     int hgrp;
     int64_t b;
@@ -383,11 +386,15 @@ void attn_fwd_kernel(AttnArgs a) {
     b += qb0;
     const int h = hgrp * kH + (wave >> 1);           // this wave's q head (in the per-head arrays)
     // its sequence (the workgroup's heads share it) and the head within it
-    const int seq = (hgrp * kH) / a.hq;
-    const SeqSpan span = seq_span(a.vl.cu, seq, a.vl.rows, a.n);
+    int seq = 0;
+    SeqSpan span{0, a.n};
+    if constexpr (kVar) {
+        seq = (hgrp * kH) / a.hq;
+        span = seq_span(a.vl.cu, seq, a.vl.rows, a.n);
+        if (b * kBQ >= span.n) return;               // past the end of a shorter sequence
+    }
     const int64_t n = span.n;
     const int n32 = (int)n;                          // below 2^31
-    if (b * kBQ >= n) return;                        // past the end of a shorter packed sequence
     const int hs = h - seq * a.hq;
     const int g = hs / G;
     const int r0 = (int)b * kBQ;
@@ -1141,11 +1148,12 @@ void attn_fwd_kernel(AttnArgs a) {
 #endif
 }
 
-template <typename T, bool kDense, int kH, bool kGrp = false, bool kFused = false, bool kExact = false>
+template <typename T, bool kDense, int kH, bool kGrp = false, bool kFused = false, bool kExact = false,
+          bool kVar = false>
 hipError_t launch_h(const AttnArgs &a, hipStream_t s) {
     const int64_t total = (int64_t)a.hq * a.vl.nseq / kH * ((a.n + kBQ - 1) / kBQ - (kDense ? 0 : a.qb_lo));
     if (total == 0) return hipSuccess;
-    hipLaunchKernelGGL((attn_fwd_kernel<T, kDense, kH, kGrp, kFused, kExact>), dim3((unsigned)total),
+    hipLaunchKernelGGL((attn_fwd_kernel<T, kDense, kH, kGrp, kFused, kExact, kVar>), dim3((unsigned)total),
                        dim3(kThreads * kH), 0, s, a);
     return hipGetLastError();
 }
@@ -1231,12 +1239,12 @@ template <typename T, bool kExact> hipError_t launch_fused(AttnArgs a, hipStream
 // blocks from j R / 64 on, so the workgroups in flight read K/V from one
 // R-key range of a kv head (a working set the last-level cache holds) rather
 // than from the whole sequence.
-template <typename T, bool kDense> hipError_t launch(AttnArgs a, hipStream_t s) {
+template <typename T, bool kDense, bool kVar = false> hipError_t launch(AttnArgs a, hipStream_t s) {
     if constexpr (kDense) {
         const int G = a.hq / a.hkv;
-        if (G % 4 == 0) return launch_h<T, true, 4>(a, s);
-        if (G % 2 == 0) return launch_h<T, true, 2>(a, s);
-        return launch_h<T, true, 1>(a, s);
+        if (G % 4 == 0) return launch_h<T, true, 4, false, false, false, kVar>(a, s);
+        if (G % 2 == 0) return launch_h<T, true, 2, false, false, false, kVar>(a, s);
+        return launch_h<T, true, 1, false, false, false, kVar>(a, s);
     } else {
         const int64_t R = a.phase_keys;
         if (a.ws == nullptr || R <= 0 || R >= a.n) {
@@ -1244,7 +1252,7 @@ template <typename T, bool kDense> hipError_t launch(AttnArgs a, hipStream_t s) 
             a.k_lo = INT_MIN;
             a.k_hi = INT_MAX;
             a.qb_lo = 0;
-            return launch_h<T, false, 1>(a, s);
+            return launch_h<T, false, 1, false, false, false, kVar>(a, s);
         }
         // first the grouped walk over the units that qualify (it marks them),
         // then the key phases of the per-head kernel over the rest
@@ -1252,9 +1260,9 @@ template <typename T, bool kDense> hipError_t launch(AttnArgs a, hipStream_t s) 
                                             sparse_walk_marks_offset((int64_t)a.hq * a.vl.nseq, a.n));
         a.grp_kh = walk_heads_per_unit(a.hq, a.hkv);
         {
-            const hipError_t e = a.grp_kh == 4   ? launch_h<T, true, 4, true>(a, s)
-                                 : a.grp_kh == 2 ? launch_h<T, true, 2, true>(a, s)
-                                                 : launch_h<T, true, 1, true>(a, s);
+            const hipError_t e = a.grp_kh == 4   ? launch_h<T, true, 4, true, false, false, kVar>(a, s)
+                                 : a.grp_kh == 2 ? launch_h<T, true, 2, true, false, false, kVar>(a, s)
+                                                 : launch_h<T, true, 1, true, false, false, kVar>(a, s);
             if (e != hipSuccess) return e;
         }
         const int64_t np = (a.n + R - 1) / R;
@@ -1262,7 +1270,7 @@ template <typename T, bool kDense> hipError_t launch(AttnArgs a, hipStream_t s) 
             a.k_lo = j == 0 ? INT_MIN : (int32_t)(j * R);
             a.k_hi = j == np - 1 ? INT_MAX : (int32_t)((j + 1) * R);
             a.qb_lo = j * R / kBQ;
-            const hipError_t e = launch_h<T, false, 1>(a, s);
+            const hipError_t e = launch_h<T, false, 1, false, false, false, kVar>(a, s);
             if (e != hipSuccess) return e;
         }
         return hipSuccess;
@@ -1294,6 +1302,7 @@ size_t fused_state_bytes(int64_t hq, int64_t n, int64_t phase_keys, int64_t kv, 
 }
 
 hipError_t launch_sparse_prefill(const AttnArgs &a, int dtype, hipStream_t s) {
+    if (a.vl.cu != nullptr) return dtype == 0 ? launch<bf16, false, true>(a, s) : launch<float, false, true>(a, s);
     return dtype == 0 ? launch<bf16, false>(a, s) : launch<float, false>(a, s);
 }
 
@@ -1306,6 +1315,7 @@ int fused_max_phase_keys() { return kFusedMaxPhase; }
 int fused_max_columns() { return kFusedCols; }
 
 hipError_t launch_dense_prefill(const AttnArgs &a, int dtype, hipStream_t s) {
+    if (a.vl.cu != nullptr) return dtype == 0 ? launch<bf16, true, true>(a, s) : launch<float, true, true>(a, s);
     return dtype == 0 ? launch<bf16, true>(a, s) : launch<float, true>(a, s);
 }
 
