@@ -290,6 +290,153 @@ def bench_decode(args, dw):
     print(json.dumps(res), flush=True)
 
 
+def bench_packed(args, pw):
+    """One packed prefill layer: sequences of different lengths packed along
+    the rows, each estimated, indexed and attended as on its own, in one
+    launch chain (the msa_*_varlen calls); the dense causal kernel over the
+    same packed batch for the speedup; and, for reference, the same sequences
+    as one call chain each (what a packed batch cost before the variable-length
+    calls).  TFLOP/s on the work lists' tiles, as for one sequence."""
+    import torch
+    import dynamic_sparse_attention_vertical_amd as msa
+    from dynamic_sparse_attention_vertical_amd.layer import LayerPlan, vertical_slash_layer
+    from synth import make_packed_inputs
+
+    lens = list(pw.lengths)
+    hq, hkv, nseq = pw.n_q_heads, pw.n_kv_heads, len(lens)
+    rows, max_len = sum(lens), max(lens)
+    log(f"[bench] packed workload {pw.name}: {nseq} sequences of {min(lens)}..{max_len} tokens ({rows} in all), "
+        f"{hq}q/{hkv}kv heads")
+    x = make_packed_inputs(pw, device="cuda")
+    q, k, v, cu = x["q"], x["k"], x["v"], x["cu_seqlens"]
+    cu_d = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    kv, ks = min(pw.vertical_topk, max_len), min(pw.slash_topk, max_len)
+    heads = nseq * hq
+    stream = torch.cuda.current_stream()
+    est_ws = torch.empty(msa.estimate_vs_varlen_workspace_bytes(hq, hkv, rows, cu_d, max_len, q.dtype),
+                         dtype=torch.uint8, device="cuda")
+    v_idx = torch.empty((heads, kv), dtype=torch.int32, device="cuda")
+    s_idx = torch.empty((heads, ks), dtype=torch.int32, device="cuda")
+    cb, cc = msa.index_caps(max_len, kv, ks, heads)
+    idx = msa.alloc_index(heads, max_len, cb, cc, "cuda")
+    att_bytes = msa.sparse_prefill_varlen_workspace_bytes(hq, hkv, rows, cu_d, max_len, q.dtype)
+    att_ws = torch.empty(max(att_bytes, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        msa.estimate_vs_varlen(q, k, cu_d, max_len, kv, ks, workspace=est_ws, v_idx=v_idx, s_idx=s_idx,
+                               stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        msa.build_index_varlen(v_idx, s_idx, cu_d, max_len, hq, rows=rows, out=idx, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        msa.sparse_prefill_varlen(q, k, v, idx, cu_d, max_len, out=out, workspace=att_ws, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    per = [[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in events]
+    ms_est, ms_idx, ms_att = (sum(p[j] for p in per) / len(per) for j in range(3))
+    log(f"[bench] timed {args.steps} steps: {ms_step:.2f} ms/layer (estimate {ms_est:.3f}, index {ms_idx:.3f}, "
+        f"sparse prefill {ms_att:.3f})")
+
+    # tiles of the query blocks each sequence has (entries past its end are unwritten)
+    nqb_max = (max_len + 63) // 64
+    seq_nqb = torch.tensor([(n + 63) // 64 for n in lens], device="cuda").repeat_interleave(hq)
+    live = torch.arange(nqb_max, device="cuda")[None, :] < seq_nqb[:, None]
+    bc = idx.block_count.to(torch.int64) * live
+    per_blk = bc + ((idx.column_count.to(torch.int64) + 63) // 64) * live
+    tiles = int(per_blk.sum().item())
+    marks = msa.sparse_walk_marks(att_ws, heads, hkv * nseq, max_len, q.dtype) if att_bytes else None
+    run_per = per_blk
+    walk_blocks = 0
+    if marks is not None:
+        marks = (marks != 0) & live
+        b1 = torch.arange(nqb_max, device="cuda", dtype=torch.int64)[None, :] + 1
+        run_per = torch.where(marks, b1.expand_as(per_blk), per_blk)
+        walk_blocks = int(marks.sum().item())
+    run_tiles = int(run_per.sum().item())
+    causal_tiles = hq * sum(((n + 63) // 64) * ((n + 63) // 64 + 1) // 2 for n in lens)
+    att_tflops = run_tiles * TILE_FLOP / (ms_att * 1e-3) / 1e12
+
+    # dense over the same packed batch, and the per-sequence loop
+    dense_out = torch.empty_like(q)
+    msa.dense_prefill_varlen(q, k, v, cu_d, max_len, out=dense_out, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    msa.dense_prefill_varlen(q, k, v, cu_d, max_len, out=dense_out, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_dense = e0.elapsed_time(e1)
+    plans = {}
+
+    def loop():
+        for a, b in zip(cu, cu[1:]):
+            n = b - a
+            if n not in plans:
+                plans[n] = LayerPlan(hq, hkv, n, min(kv, n), min(ks, n), "cuda", q.dtype)
+            pl = plans[n]
+            vertical_slash_layer(q[:, a:b], k[:, a:b], v[:, a:b], pl.vertical_topk, pl.slash_topk, plan=pl,
+                                 out=dense_out[:, a:b], stream=stream)
+    loop()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    loop()
+    torch.cuda.synchronize()
+    ms_loop = (time.perf_counter() - t0) * 1e3
+    log(f"[bench] dense over the packed batch {ms_dense:.2f} ms; one call chain per sequence {ms_loop:.2f} ms")
+    res = {
+        "metric": METRIC,
+        "value": round(tiles * TILE_FLOP / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": pw.name, "step": "packed lists", "sequences": nseq, "total_tokens": rows,
+                   "max_seqlen": max_len, "min_seqlen": min(lens), "q_heads": hq, "kv_heads": hkv, "head_dim": 128,
+                   "vertical_topk": pw.vertical_topk, "slash_topk": pw.slash_topk, "last_q": 64, "block": 64},
+        "breakdown": {
+            "ms_estimate": round(ms_est, 4), "ms_build_index": round(ms_idx, 4),
+            "ms_sparse_prefill": round(ms_att, 4),
+            "listed_tiles": tiles, "executed_tiles": run_tiles, "causal_tiles": causal_tiles,
+            "grouped_walk_blocks": walk_blocks,
+            "listed_density": round(tiles / causal_tiles, 5), "executed_density": round(run_tiles / causal_tiles, 5),
+            "sparse_prefill_tflops": round(att_tflops, 2),
+            "ms_dense_prefill": round(ms_dense, 3),
+            "dense_prefill_tflops": round(causal_tiles * TILE_FLOP / (ms_dense * 1e-3) / 1e12, 2),
+            "speedup_vs_dense": round(ms_dense / ms_step, 3),
+            "ms_one_chain_per_sequence": round(ms_loop, 3),
+            "speedup_vs_one_chain_per_sequence": round(ms_loop / ms_step, 3),
+        },
+        "roofline": {"bound": "mfma",
+                     "kernel": "attn_fwd_kernel<bf16, packed> sparse: grouped walk + per-head key phases",
+                     "launches_per_step": phase_launches(max_len),
+                     "achieved": round(att_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "traffic_source": "no counter run committed for this workload"},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -319,10 +466,13 @@ def main():
     import torch
     import dynamic_sparse_attention_vertical_amd as msa
     from dynamic_sparse_attention_vertical_amd.layer import LayerPlan, MixedPlan, mixed_index
-    from synth import DECODE_WORKLOADS, WORKLOADS, make_inputs
+    from synth import DECODE_WORKLOADS, PACKED_WORKLOADS, WORKLOADS, make_inputs
 
     if args.workload in DECODE_WORKLOADS:
         bench_decode(args, DECODE_WORKLOADS[args.workload])
+        return
+    if args.workload in PACKED_WORKLOADS:
+        bench_packed(args, PACKED_WORKLOADS[args.workload])
         return
     w = WORKLOADS[args.workload]
     mixed = bool(w.head_patterns)

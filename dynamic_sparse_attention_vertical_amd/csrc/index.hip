@@ -75,6 +75,20 @@ __global__ __launch_bounds__(kThreads) void build_index_kernel(IndexArgs a) {
     const int64_t item = (int64_t)h * nqb_rows + b;
     int32_t *blk = a.block_offset + item * a.cap_b;
     int32_t *col = a.column_index + item * a.cap_c;
+    // Every offset 0 .. r1 selected (the offsets ascend and are distinct, so
+    // S[r1] == r1 says so; a sequence of at most ks tokens has all of them):
+    // the walk would emit the aligned blocks 0, 64, .., 64 b, which cover
+    // every key of the block and so every column.  Write them directly.
+    if (r1 < a.ks && S[r1] == r1) {
+        const int cnt = min(b + 1, a.cap_b);
+        int j = 0;
+        if (a.vec_rows)
+            for (; j + 4 <= cnt; j += 4) *reinterpret_cast<int4 *>(blk + j) = make_int4(64 * j, 64 * j + 64, 64 * j + 128, 64 * j + 192);
+        for (; j < cnt; ++j) blk[j] = 64 * j;
+        a.block_count[item] = cnt;
+        a.column_count[item] = 0;
+        return;
+    }
 
     // offsets that matter to some lane of the wave: those <= r1 of its last item
     const int wave_first = b - (int)(threadIdx.x & 63);

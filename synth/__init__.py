@@ -6,7 +6,8 @@ the method's arithmetic, so both the CPU oracle and the GPU path can consume the
 same tensors without sharing any code.
 """
 
-from .gen import (WORKLOADS, DECODE_WORKLOADS, DecodeWorkload, Workload, make_decode_inputs, make_inputs,
-                  small_workload, rope_tables)
+from .gen import (WORKLOADS, DECODE_WORKLOADS, PACKED_WORKLOADS, DecodeWorkload, PackedWorkload, Workload,
+                  make_decode_inputs, make_inputs, make_packed_inputs, small_workload, rope_tables)
 
-__all__ = ["WORKLOADS", "Workload", "make_inputs", "small_workload", "rope_tables"]
+__all__ = ["WORKLOADS", "DECODE_WORKLOADS", "PACKED_WORKLOADS", "Workload", "DecodeWorkload", "PackedWorkload",
+           "make_inputs", "make_decode_inputs", "make_packed_inputs", "small_workload", "rope_tables"]

@@ -151,6 +151,51 @@ def make_decode_inputs(dw: DecodeWorkload, device: str = "cpu") -> dict:
     return res
 
 
+@dataclass(frozen=True)
+class PackedWorkload:
+    """A prefill batch of sequences of different lengths packed along the
+    rows ([heads, total, D], sequence i at rows cu[i] .. cu[i+1]-1), each of
+    the single-sequence recipe with its own seed."""
+    name: str
+    n_q_heads: int
+    n_kv_heads: int
+    lengths: tuple
+    vertical_topk: int = 1000
+    slash_topk: int = 6096
+    seed: int = 0
+
+    def sequence(self, i: int) -> Workload:
+        return Workload(f"{self.name}_{i}", self.n_q_heads, self.n_kv_heads, self.lengths[i],
+                        vertical_topk=self.vertical_topk, slash_topk=self.slash_topk, seed=self.seed + i)
+
+
+PACKED_WORKLOADS = {
+    # LLaMA-3-8B attention shape, 64 prompts of 1,062 to 32,444 tokens
+    # (516,245 in all; lengths drawn once, log-uniform over 1K..32K, seed 2201)
+    "llama3_8b_packed_64": PackedWorkload("llama3_8b_packed_64", 32, 8, (
+        13039, 1674, 12436, 11505, 11600, 22901, 1363, 17329, 22318, 5504, 3218, 16594, 3164, 1512, 3054, 32444,
+        6841, 8179, 2492, 2748, 4455, 5982, 3093, 9549, 1461, 3920, 2841, 3023, 4602, 2838, 20765, 15880, 4435,
+        2140, 8080, 3913, 3511, 2809, 1974, 9432, 4318, 10344, 6202, 1717, 1454, 2281, 5094, 14056, 1165, 1561,
+        9677, 1679, 21155, 12621, 1858, 27981, 14001, 1481, 1062, 2025, 19360, 25824, 4118, 10593), seed=2301),
+}
+
+
+def make_packed_inputs(pw: PackedWorkload, device: str = "cpu") -> dict:
+    """q [Hq, total, D], k and v [Hkv, total, D] (bfloat16) with the
+    sequences one after another, and cu_seqlens (a list)."""
+    qs, ks, vs = [], [], []
+    for i in range(len(pw.lengths)):
+        x = make_inputs(pw.sequence(i), device=device)
+        qs.append(x["q"])
+        ks.append(x["k"])
+        vs.append(x["v"])
+        del x
+    cu = [0]
+    for n in pw.lengths:
+        cu.append(cu[-1] + n)
+    return {"q": torch.cat(qs, dim=1), "k": torch.cat(ks, dim=1), "v": torch.cat(vs, dim=1), "cu_seqlens": cu}
+
+
 def small_workload(name: str = "small", **kw) -> Workload:
     """A test-sized workload (same recipe, smaller shapes)."""
     base = dict(n_q_heads=4, n_kv_heads=1, seq_len=1024, vertical_topk=64, slash_topk=128,

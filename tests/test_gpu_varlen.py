@@ -215,3 +215,46 @@ def test_packed_streaming_and_block_sparse():
             one = call(qd[:, a:b].contiguous(), kd[:, a:b].contiguous(), vd[:, a:b].contiguous(),
                        *[min(x, b - a) for x in args])
             assert torch.equal(out[:, a:b], one), (call.__name__, i)
+
+
+def test_packed_workload_sampled():
+    """The benchmark's packed batch as the benchmark runs it (64 prompts of
+    1,062 to 32,444 tokens, 32 q / 8 kv heads, vertical 1000 / slash 6096):
+    the shortest, a middle and the longest sequence against the oracle
+    (sets of four heads within the tie band, their work lists bit-exact,
+    sampled query blocks of the sparse output)."""
+    from synth import PACKED_WORKLOADS, make_packed_inputs
+    pw = PACKED_WORKLOADS["llama3_8b_packed_64"]
+    x = make_packed_inputs(pw, device="cuda")
+    q, k, v, cu = x["q"], x["k"], x["v"], x["cu_seqlens"]
+    lens = list(pw.lengths)
+    hq, max_len = pw.n_q_heads, max(lens)
+    cu_d = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    v_idx, s_idx = msa.estimate_vs_varlen(q, k, cu_d, max_len, pw.vertical_topk, pw.slash_topk)
+    idx = msa.build_index_varlen(v_idx, s_idx, cu_d, max_len, hq, rows=q.shape[1])
+    out = msa.sparse_prefill_varlen(q, k, v, idx, cu_d, max_len)
+    torch.cuda.synchronize()
+    heads = [0, 5, 17, 31]
+    for s in (int(np.argmin(lens)), 9, int(np.argmax(lens))):
+        a, b = cu[s], cu[s + 1]
+        n = b - a
+        what = f"packed sequence {s} ({n} tokens)"
+        qs, ks_, vs = q[:, a:b].cpu(), k[:, a:b].cpu(), v[:, a:b].cpu()
+        vsc, ssc = oracle.estimate_vs(qs, ks_, heads=heads)
+        vi = v_idx[s * hq:(s + 1) * hq].cpu().numpy()[heads]
+        si = s_idx[s * hq:(s + 1) * hq].cpu().numpy()[heads]
+        for j, h in enumerate(heads):
+            check_sets(vi[j], vsc[j], pw.vertical_topk, n, f"{what} vertical h{h}")
+            check_sets(si[j], ssc[j], pw.slash_topk, n, f"{what} slash h{h}")
+        nqb = (n + 63) // 64
+        ref_idx = oracle.build_index(vi, si, n)
+        rows = [s * hq + h for h in heads]
+        mine = msa.IndexTensors(idx.block_count[rows, :nqb], idx.block_offset[rows, :nqb],
+                                idx.column_count[rows, :nqb], idx.column_index[rows, :nqb])
+        compare_index(mine, ref_idx, what)
+        blocks = sorted({0, nqb // 3, nqb // 2, nqb - 1})
+        items = [(h, bb) for h in heads for bb in blocks]
+        ref = oracle.masked_attention_blocks(qs, ks_, vs, ref_idx, items, head_rows={h: j for j, h in enumerate(heads)})
+        o = out[:, a:b].float().cpu().numpy()
+        for (h, bb), (ro, _) in ref.items():
+            compare_out(o[h, bb * 64:min(bb * 64 + 64, n)], ro, False, f"{what} h{h} b{bb}")
