@@ -363,7 +363,8 @@ int msa_decode_sparse_varlen(const msa_problem *p, const void *q, const void *k,
  *     4-byte aligned; max_seqlen: a host value at least every length, at
  *     most seq_len.  The device clamps entries into [0, seq_len] and lengths
  *     to max_seqlen, so contents that break these rules give unspecified
- *     results but no access outside the buffers.
+ *     results (overlapping sequences overwrite each other's rows) but no
+ *     access outside the buffers.
  *   n_seqs * n_q_heads at most 32767.
  *   Per-head arrays (index sets, work lists) hold n_seqs * n_q_heads heads:
  *     head h of sequence s is s * n_q_heads + h; each is sized for max_seqlen

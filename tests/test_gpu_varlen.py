@@ -258,3 +258,27 @@ def test_packed_workload_sampled():
         o = out[:, a:b].float().cpu().numpy()
         for (h, bb), (ro, _) in ref.items():
             compare_out(o[h, bb * 64:min(bb * 64 + 64, n)], ro, False, f"{what} h{h} b{bb}")
+
+
+def test_packed_bad_offsets_stay_in_bounds():
+    """cu_seqlens contents that break the rules (falling, past the packed
+    length) are clamped on the device: the calls complete and every output
+    is finite.  Here sequence 1 clamps to empty and sequence 2 to rows
+    100..599, overlapping sequence 0, so only rows 0..99 are sequence 0's
+    alone and must equal the well-formed batch's."""
+    hq, hkv, lens = 4, 2, [300, 200, 500]
+    q, k, v, cu = packed_inputs(hq, hkv, lens, seed=901)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    good = run_varlen(q, k, v, cu, 30, 90)
+    total = q.shape[1]
+    bad = torch.tensor([0, 300, 100, 1 << 30], dtype=torch.int32, device="cuda")   # falling, then past the end
+    v_idx, s_idx = msa.estimate_vs_varlen(qd, kd, bad, 500, 30, 90)
+    idx = msa.build_index_varlen(v_idx, s_idx, bad, 500, hq, rows=total)
+    out = torch.zeros_like(qd)
+    msa.sparse_prefill_varlen(qd, kd, vd, idx, bad, 500, out=out)
+    dout = torch.zeros_like(qd)
+    msa.dense_prefill_varlen(qd, kd, vd, bad, 500, out=dout)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(dout.float()).all()
+    assert torch.equal(out[:, :100], good["out"][:, :100])
+    assert torch.equal(dout[:, :100], good["dout"][:, :100])
