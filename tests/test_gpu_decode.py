@@ -298,3 +298,22 @@ def test_decode_varlen_workload_sampled():
         compare_out(out[hs].float().cpu().numpy(), ro, False, what)
         np.testing.assert_allclose(lse[hs].cpu().numpy(), rl, atol=LSE_ATOL, err_msg=what)
         np.testing.assert_allclose(rec[hs].cpu().numpy(), rr, atol=REC_ATOL, err_msg=what)
+
+
+def test_decode_varlen_lengths_clamped():
+    """Cache lengths outside [0, capacity] are clamped on the device: a
+    negative length is an empty cache, one past the capacity the full one."""
+    hq, hkv, n, topk = 8, 2, 900, 50
+    q, k, v = cache(hq, hkv, n, seed=51)
+    lens_dev = torch.tensor([-3, 1 << 30], dtype=torch.int32).cuda()
+    out, idx, lse, rec = msa.decode_sparse(q.cuda(), k.cuda(), v.cuda(), topk, lse=True, recovery=True,
+                                           cache_lens=lens_dev)
+    i = idx.cpu().numpy()
+    ro, rl, rr, _ = oracle.decode_sparse_attention(q, k, v, topk, idx=i, cache_len=np.array([0, n]))
+    np.testing.assert_array_equal(i[:4], np.tile(np.arange(topk), (4, 1)))     # empty: the first positions
+    check_sets(i[4:], oracle.decode_scores(q[4:], k[1:]), topk, "full cache")
+    compare_out(out.float().cpu().numpy(), ro, False, "clamped lengths")
+    lg = lse.cpu().numpy()
+    assert np.isneginf(lg[:4]).all() and np.isfinite(lg[4:]).all()
+    np.testing.assert_allclose(lg[4:], rl[4:], atol=LSE_ATOL)
+    np.testing.assert_allclose(rec.cpu().numpy(), rr, atol=REC_ATOL)
