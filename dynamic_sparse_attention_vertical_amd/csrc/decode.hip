@@ -123,6 +123,17 @@ __global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a, i
     const int col = (lane & 15) * 8, sub = lane >> 4;
     const int hl = head_of<kG>(lane);                        // this lane's head after the reduction
     const bool owner = hl < gcount && (lane & (kG == 8 ? 1 : 3)) == 0;
+    const int64_t j0 = (int64_t)blockIdx.x * a.chunk_keys;
+    const int64_t j1 = min(j0 + a.chunk_keys, a.n);
+    const int64_t jv = min(j1, max(j0, cache_keys(a, kvh)));   // keys [j0, jv) are in the cache
+    if (jv == j0) {                                            // a chunk past the cache's end: an empty partial
+        if (threadIdx.x < gcount) {
+            const int64_t h = kvh * G + g0 + threadIdx.x;
+            a.part[(h * a.nchunks + blockIdx.x) * 2 + 0] = -INFINITY;
+            a.part[(h * a.nchunks + blockIdx.x) * 2 + 1] = 0.f;
+        }
+        return;
+    }
     // bf16: q and K stay bf16 pairs, multiplied by v_dot2 (two products
     // summed into an fp32 accumulator); fp32: fused multiply-adds
     constexpr bool kPairs = sizeof(T) == 2;
@@ -143,9 +154,6 @@ __global__ __launch_bounds__(kThreads) void decode_scores_kernel(DecodeArgs a, i
         }
     }
     const T *kp = reinterpret_cast<const T *>(a.k) + (int64_t)kvh * a.stride * kD;
-    const int64_t j0 = (int64_t)blockIdx.x * a.chunk_keys;
-    const int64_t j1 = min(j0 + a.chunk_keys, a.n);
-    const int64_t jv = min(j1, max(j0, cache_keys(a, kvh)));   // keys [j0, jv) are in the cache
     float m = -INFINITY, l = 0.f;
     constexpr int kUs = kPairs ? 2 * kU : kU;               // bf16 rows are half the registers
     // One step: the workgroup's 16 kUs consecutive keys from sb, rows sb +
