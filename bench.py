@@ -431,8 +431,10 @@ def bench_packed(args, pw):
                      "kernel": "attn_fwd_kernel<bf16, packed> sparse: grouped walk + per-head key phases",
                      "launches_per_step": phase_launches(max_len),
                      "achieved": round(att_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "traffic_source": "no counter run committed for this workload"},
+                     "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(pw.name),
+                     "traffic_source": ("rocprofv3 FETCH_SIZE + WRITE_SIZE of the same source, committed in "
+                                        "profiles/attn_sparse_traffic.json (null when the kernel source "
+                                        "has changed since)")},
     }
     print(json.dumps(res), flush=True)
 
