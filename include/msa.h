@@ -375,6 +375,10 @@ int msa_decode_sparse_varlen(const msa_problem *p, const void *q, const void *k,
  *     past its end, which msa_build_index_varlen ignores.
  *   Rows of q, k, v, out and lse outside every sequence are neither read nor
  *     written.
+ *   The grouped walk's marks in a msa_sparse_prefill_varlen workspace are
+ *     where msa_sparse_prefill_walk_marks puts them for a problem of
+ *     n_seqs * n_q_heads q heads, n_seqs * n_kv_heads kv heads and seq_len =
+ *     max_seqlen.
  * Errors as for the one-sequence calls; a NULL descriptor or cu_seqlens:
  * MSA_ERR_NULL; n_seqs, max_seqlen or the head count out of range:
  * MSA_ERR_SHAPE.                                                            */
