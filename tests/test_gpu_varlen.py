@@ -45,11 +45,15 @@ def run_varlen(q, k, v, cu, kv, ks):
     kv, ks = min(kv, max_len), min(ks, max_len)
     v_idx, s_idx = msa.estimate_vs_varlen(qd, kd, cu_d, max_len, kv, ks)
     idx = msa.build_index_varlen(v_idx, s_idx, cu_d, max_len, q.shape[0], rows=q.shape[1])
-    out, lse = msa.sparse_prefill_varlen(qd, kd, vd, idx, cu_d, max_len, lse=True)
+    nb = msa.sparse_prefill_varlen_workspace_bytes(q.shape[0], k.shape[0], q.shape[1], cu_d, max_len, q.dtype)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+    out, lse = msa.sparse_prefill_varlen(qd, kd, vd, idx, cu_d, max_len, lse=True, workspace=ws)
     dout, dlse = msa.dense_prefill_varlen(qd, kd, vd, cu_d, max_len, lse=True)
     torch.cuda.synchronize()
+    nseq = len(cu) - 1
+    marks = msa.sparse_walk_marks(ws, nseq * q.shape[0], nseq * k.shape[0], max_len, q.dtype) if nb else None
     return dict(v_idx=v_idx.cpu().numpy(), s_idx=s_idx.cpu().numpy(), idx=idx, out=out, lse=lse, dout=dout,
-                dlse=dlse, kv=kv, ks=ks)
+                dlse=dlse, kv=kv, ks=ks, marks=marks)
 
 
 def sequence_index(idx, rows, nqb):
@@ -124,6 +128,10 @@ def test_packed_varlen_key_phases():
     hq, hkv, lens = 4, 1, [700, 13000, 5000]
     q, k, v, cu = packed_inputs(hq, hkv, lens, seed=501)
     r = run_varlen(q, k, v, cu, 300, 1000)
+    # the grouped walk ran in the packed batch: every sequence has units it took
+    marks = r["marks"].cpu().numpy()
+    for s_, n in enumerate(lens):
+        assert marks[s_ * hq:(s_ + 1) * hq, :(n + 63) // 64].any(), f"sequence {s_}: no unit in the grouped walk"
     check_sequence(q, k, v, cu, r, 0, False)
     check_sequence(q, k, v, cu, r, 1, False, sample=[0, 1, 95, 191, 192, 200, 203])
     check_sequence(q, k, v, cu, r, 2, False, sample=[0, 40, 77, 78])
