@@ -38,20 +38,23 @@ def packed_inputs(hq, hkv, lens, seed, fp32=False):
     return q, k, v, cu
 
 
-def run_varlen(q, k, v, cu, kv, ks):
+def run_varlen(q, k, v, cu, kv, ks, phase_keys=0):
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     cu_d = torch.tensor(cu, dtype=torch.int32, device="cuda")
     max_len = max(b - a for a, b in zip(cu, cu[1:]))
     kv, ks = min(kv, max_len), min(ks, max_len)
     v_idx, s_idx = msa.estimate_vs_varlen(qd, kd, cu_d, max_len, kv, ks)
     idx = msa.build_index_varlen(v_idx, s_idx, cu_d, max_len, q.shape[0], rows=q.shape[1])
-    nb = msa.sparse_prefill_varlen_workspace_bytes(q.shape[0], k.shape[0], q.shape[1], cu_d, max_len, q.dtype)
+    nb = msa.sparse_prefill_varlen_workspace_bytes(q.shape[0], k.shape[0], q.shape[1], cu_d, max_len, q.dtype,
+                                                   phase_keys=phase_keys)
     ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
-    out, lse = msa.sparse_prefill_varlen(qd, kd, vd, idx, cu_d, max_len, lse=True, workspace=ws)
+    out, lse = msa.sparse_prefill_varlen(qd, kd, vd, idx, cu_d, max_len, lse=True, workspace=ws,
+                                         phase_keys=phase_keys)
     dout, dlse = msa.dense_prefill_varlen(qd, kd, vd, cu_d, max_len, lse=True)
     torch.cuda.synchronize()
     nseq = len(cu) - 1
-    marks = msa.sparse_walk_marks(ws, nseq * q.shape[0], nseq * k.shape[0], max_len, q.dtype) if nb else None
+    marks = msa.sparse_walk_marks(ws, nseq * q.shape[0], nseq * k.shape[0], max_len, q.dtype,
+                                  phase_keys=phase_keys) if nb else None
     return dict(v_idx=v_idx.cpu().numpy(), s_idx=s_idx.cpu().numpy(), idx=idx, out=out, lse=lse, dout=dout,
                 dlse=dlse, kv=kv, ks=ks, marks=marks)
 
@@ -119,6 +122,20 @@ def test_packed_varlen(hq, hkv, lens, kv, ks, fp32):
     r = run_varlen(q, k, v, cu, kv, ks)
     for s in range(len(lens)):
         check_sequence(q, k, v, cu, r, s, fp32)
+
+
+@pytest.mark.parametrize("fp32", [False, True])
+def test_packed_varlen_short_phases(fp32):
+    """Key phases of 256 keys over a packed batch (so every sequence longer
+    than that crosses phases, with its state carried in the workspace, and
+    the grouped walk takes the units it qualifies), bf16 and fp32, every
+    sequence against the oracle."""
+    hq, hkv, lens = 4, 1, [700, 130, 1000, 257]
+    q, k, v, cu = packed_inputs(hq, hkv, lens, seed=1001, fp32=fp32)
+    r = run_varlen(q, k, v, cu, 40, 150, phase_keys=256)
+    assert r["marks"] is not None
+    for s_ in range(len(lens)):
+        check_sequence(q, k, v, cu, r, s_, fp32)
 
 
 def test_packed_varlen_key_phases():
