@@ -307,3 +307,27 @@ def test_packed_bad_offsets_stay_in_bounds():
     assert torch.isfinite(out.float()).all() and torch.isfinite(dout.float()).all()
     assert torch.equal(out[:, :100], good["out"][:, :100])
     assert torch.equal(dout[:, :100], good["dout"][:, :100])
+
+
+def test_packed_block_sparse_chunks():
+    """The block-sparse scores of a packed batch go through the workspace in
+    chunks of 1024 query blocks: a 70,000-token sequence (1,094 blocks, two
+    chunks) packed with short ones, fp32, its lists and the short ones'
+    against the oracle's selection (two heads each)."""
+    hq, hkv, lens = 2, 1, [70000, 300, 1500]
+    q, k, v, cu = packed_inputs(hq, hkv, lens, seed=1101, fp32=True)
+    cu_d = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    idx = msa.estimate_bs_varlen(q.cuda(), k.cuda(), cu_d, max(lens), 100)
+    bc, bo = idx.block_count.cpu().numpy(), idx.block_offset.cpu().numpy()
+    for s_, (a, b) in enumerate(zip(cu, cu[1:])):
+        n = b - a
+        nqb = (n + 63) // 64
+        cnt, _, scores = oracle.block_sparse_select(q[:, a:b], k[:, a:b], range(hq), topk=100)
+        rows = slice(s_ * hq, (s_ + 1) * hq)
+        assert np.array_equal(bc[rows][:, :nqb], cnt), f"sequence {s_}"
+        for h in range(hq):
+            for qb in sorted({0, nqb // 2, 1023 % nqb, 1024 % nqb, nqb - 1}):
+                kk = cnt[h, qb]
+                u = scores[h, qb, : qb + 1]
+                pr = np.exp(u - u.max())
+                check_band(bo[rows][h, qb, :kk] // 64, pr / pr.sum(), kk, f"sequence {s_} h{h} b{qb}")
