@@ -213,6 +213,34 @@ def cpu_baseline(x, plan, w, target_s=20.0):
     }
 
 
+def time_graph(step, outs, steps, warmup):
+    """Capture step() once as a HIP graph (graphs.StepGraph) and time `steps`
+    replays back to back with events on the stream they run on; also whether
+    the replays left outs (the eager step's results on the same inputs)
+    bit-identical."""
+    import torch
+    from dynamic_sparse_attention_vertical_amd.graphs import StepGraph
+
+    before = [t.clone() for t in outs]
+    g = StepGraph(step)
+    for t in outs:      # so that equal results after the replays show that the replays computed them
+        t.fill_(float("nan") if t.is_floating_point() else -1)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    same = all(torch.equal(a, b) for a, b in zip(before, outs))
+    del before, g
+    return {"ms_per_step": round(ms, 4), "replays": steps, "replay_equals_eager": same}
+
+
 def bench_decode(args, dw):
     """One decode step over a batch of key caches (msa_decode_sparse): scores
     for every cached key, the top-k per head, attention over them.  Bound by
@@ -235,9 +263,9 @@ def bench_decode(args, dw):
     idx = torch.empty((hq, dw.topk), dtype=torch.int32, device="cuda")
     rec = torch.empty(hq, dtype=torch.float32, device="cuda")
 
-    def step():
+    def step():     # on torch's current stream (a graph capture makes its own stream current)
         msa.decode_sparse(q, k, v, dw.topk, idx=idx, out=out, recovery=rec, cache_lens=lens, workspace=ws,
-                          stream=stream)
+                          stream=torch.cuda.current_stream())
 
     for i in range(args.warmup):
         step()
@@ -250,6 +278,10 @@ def bench_decode(args, dw):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
+    graph = None
+    if args.graph:
+        graph = time_graph(step, [out, idx, rec], reps, args.warmup)
+        log(f"[bench] decode step as one HIP graph {graph['ms_per_step']:.4f} ms")
     recovery = rec.clone()
     k_bytes = sum(dw.length(b) for b in range(dw.batch)) * dw.n_kv_heads * 128 * 2   # the keys that exist
     v_bytes = hq * dw.topk * 128 * 2
@@ -279,6 +311,7 @@ def bench_decode(args, dw):
                                      "min": round(float(recovery.min()), 4),
                                      "note": "synthetic iid queries and keys: near-flat attention"},
             "k_cache_bytes": k_bytes, "selected_v_bytes": v_bytes,
+            **({"graph": {**graph, "speedup_vs_eager": round(ms / graph["ms_per_step"], 3)}} if graph else {}),
         },
         "roofline": {"bound": "hbm", "kernel": "decode_scores_kernel + top-k + decode_attend_kernel (one step)",
                      "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -454,6 +487,9 @@ def main():
     ap.add_argument("--fused", action="store_true",
                     help="time estimate + msa_sparse_prefill_fused (work lists walked inside the attention "
                          "kernel) as the step instead of estimate + build_index + sparse_prefill")
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture the step as one HIP graph and time its replays (layer and decode "
+                         "workloads; breakdown.graph)")
     ap.add_argument("--copy-calib", type=float, default=0.0,
                     help="only run a plain copy of this many GiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -508,6 +544,9 @@ def main():
         fused_ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
 
     def step(ev=None):
+        # torch's current stream at call time: the timed loop's stream, or the
+        # capture stream when the step is recorded as a graph
+        stream = torch.cuda.current_stream()
         if ev is not None:
             ev[0].record(stream)
         if mixed:
@@ -550,6 +589,12 @@ def main():
     ms_step = wall * 1e3 / args.steps
     log(f"[bench] timed {args.steps} steps: {ms_step:.2f} ms/layer (estimate {ms_est:.3f}, index {ms_idx:.3f}, "
         f"sparse prefill {ms_att:.3f})")
+    graph = None
+    if args.graph and mixed:
+        log("[bench] --graph: timed for vertical-slash layers only")
+    elif args.graph:
+        graph = time_graph(step, [out], args.steps, args.warmup)
+        log(f"[bench] the step as one HIP graph: {graph['ms_per_step']:.3f} ms/layer")
 
     if fused:       # the lists the fused kernel walked, built once (untimed) to count their tiles
         msa.build_index(plan.v_idx, plan.s_idx, n, out=plan.index, stream=stream)
@@ -600,6 +645,8 @@ def main():
         "sparse_prefill_tflops": round(att_tflops, 2),
         "sparse_prefill_listed_tflops": round(listed_flop / (ms_att * 1e-3) / 1e12, 2),
     })
+    if graph:
+        breakdown["graph"] = {**graph, "speedup_vs_eager": round(ms_step / graph["ms_per_step"], 3)}
     if not args.no_dense:
         dense_out = torch.empty_like(q)
         lse_d = torch.empty((hq, n), dtype=torch.float32, device=q.device)

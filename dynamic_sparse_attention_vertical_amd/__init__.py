@@ -15,6 +15,7 @@ from .msa import (MsaError, IndexTensors, Problem, alloc_index, build_index, dec
                   sparse_walk_marks)
 from .layer import (vertical_slash_layer, mixed_layer, vertical_slash_sparse_attention, block_sparse_attention,
                     streaming_forward)
+from .graphs import StepGraph, decode_graph, layer_graph
 
 __all__ = ["MsaError", "IndexTensors", "Problem", "alloc_index", "build_index", "decode_sparse",
            "decode_sparse_workspace_bytes", "dense_prefill", "build_index_varlen", "dense_prefill_varlen",
@@ -24,4 +25,5 @@ __all__ = ["MsaError", "IndexTensors", "Problem", "alloc_index", "build_index", 
            "load", "problem", "sparse_prefill", "sparse_prefill_fused", "sparse_prefill_fused_workspace_bytes",
            "sparse_prefill_workspace_bytes",
            "sparse_walk_marks", "vertical_slash_layer", "mixed_layer",
-           "vertical_slash_sparse_attention", "block_sparse_attention", "streaming_forward"]
+           "vertical_slash_sparse_attention", "block_sparse_attention", "streaming_forward",
+           "StepGraph", "decode_graph", "layer_graph"]
