@@ -386,3 +386,10 @@ def test_batch_fold_views():
     perm = q.transpose(0, 1).contiguous().transpose(0, 1)
     assert L._fold(perm, k, k) is None
     assert L._fold(q, k[:, :1].expand(Bn, 3, N, D), k) is None      # 8 q heads over 3 kv heads
+
+
+@pytest.mark.skipif(__import__("torch").cuda.is_available(), reason="checks the refusal on a host without a GPU")
+def test_graph_capture_refused_without_gpu():
+    from dynamic_sparse_attention_vertical_amd.graphs import StepGraph
+    with pytest.raises(m.MsaError):
+        StepGraph(lambda: None)
