@@ -1,7 +1,9 @@
 """HIP-graph replay of whole call chains (graphs.StepGraph, layer_graph,
 decode_graph): a vertical-slash layer (estimate, index, sparse prefill in
 several key phases) and decode steps (one cache length, and per-sequence
-lengths read from the device), each captured once and replayed three times
+lengths read from the device) and a packed batch (device cu_seqlens, host
+max_seqlen, sequence boundaries changed between replays), each captured once
+and replayed three times
 with new inputs copied into the captured buffers, eager torch work and
 synchronisations between the replays.  Every replay must equal, bit for bit,
 the eager chain on the same inputs in buffers of its own (the kernels are
@@ -114,3 +116,43 @@ def test_decode_graph_replays_like_eager(varlen):
         torch.cuda.synchronize()
         for i, (a, b) in enumerate(zip(got, ref)):
             assert torch.equal(a, b), f"replay {r}: output {i} differs"
+
+
+def test_packed_chain_replays_like_eager():
+    """estimate_vs_varlen + build_index_varlen + sparse_prefill_varlen (512-key
+    phases) as one graph over a fixed capacity of rows and a host max_seqlen;
+    the device cu_seqlens change between replays."""
+    hq, hkv, rows, max_len, kv, ks, phase = 4, 1, 3000, 2000, 40, 120, 512
+    splits = [[1000, 1200, 800], [2000, 500, 500], [700, 700, 1600]]
+
+    def packed(lens, seed):
+        parts = [inputs(hq, hkv, n, seed + i) for i, n in enumerate(lens)]
+        return [torch.cat([p[j] for p in parts], dim=1).cuda() for j in range(3)]
+
+    def offsets(lens):
+        return torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+
+    q, k, v = packed(splits[0], 960)
+    cu = offsets(splits[0]).cuda()
+    nb = msa.sparse_prefill_varlen_workspace_bytes(hq, hkv, rows, cu, max_len, q.dtype, phase_keys=phase)
+
+    def chain(ws):
+        v_idx, s_idx = msa.estimate_vs_varlen(q, k, cu, max_len, kv, ks)
+        idx = msa.build_index_varlen(v_idx, s_idx, cu, max_len, hq, rows=rows)
+        out, lse = msa.sparse_prefill_varlen(q, k, v, idx, cu, max_len, lse=True, workspace=ws,
+                                             phase_keys=phase)
+        return out, lse, v_idx, s_idx
+
+    ws_graph = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+    ws_eager = torch.empty_like(ws_graph)
+    g = StepGraph(lambda: chain(ws_graph))
+    for r, lens in enumerate(splits):
+        qr, kr, vr = packed(lens, 970 + 10 * r)
+        q.copy_(qr), k.copy_(kr), v.copy_(vr), cu.copy_(offsets(lens))
+        torch.cuda.synchronize()
+        got = [t.clone() for t in g.replay()]
+        torch.cuda.synchronize()
+        ref = chain(ws_eager)
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(got, ref)):
+            assert torch.equal(a, b), f"replay {r} (lengths {lens}): output {i} differs from the eager chain"
